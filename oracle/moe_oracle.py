@@ -1,0 +1,407 @@
+"""Oracle functions, one per step of the routed-expert layer.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): not imported by the
+product path.
+
+Sources, cited by page title and section:
+  [RapidMoE]  "RapidMoE: Exploiting Cross-Asymmetry via Adaptive Residual
+              Offloading for Large-Scale MoE Inference", Sec. 2.1 (gating,
+              top-k, weighted sum), Algorithm 1 (weighted sum over the routed
+              experts), Sec. 4.4-4.5 and Eq. (7) (SwiGLU expert).
+  [CAP]       "Communication-Aware Placement and Pruning for Efficient
+              Mixture-of-Experts Inference", Sec. II-A, Eq. (1) (normalised
+              routing weights).
+  [SeqMoE]    SeqMoE summary page (graph-compatible MoE offload), Mechanism:
+              one slot pool at a fixed base, expert_id -> slot_id table,
+              pinned host pool, per-slot tags.
+  [HybriMoE]  HybriMoE summary page (hybrid CPU-GPU scheduling), Mechanism:
+              misses = routed set minus cached set; only routed experts cached;
+              LRU as the baseline replacement.
+  [MoE-CORE]  MoE-CORE summary page (coordinated expert offload), Mechanism:
+              routed experts in a fixed-budget device cache.
+
+Readings of points the pages leave open (each also listed in the design notes):
+  * selection is on the logits (same set as on softmax probabilities), ties go
+    to the lower expert id, selected ids are ordered by descending logit;
+  * the bias is part of the logit (added before selection and softmax);
+  * gate weights are the softmax probabilities of the selected experts divided
+    by their sum (renormalised); with renorm off they are the plain softmax
+    probabilities;
+  * SiLU is applied to the gate projection only: h = SiLU(x W_gate) * (x W_up)
+    (Eq. (7) in [RapidMoE]; its Sec. 4.4 text is garbled on this point);
+  * int4 weights are symmetric with one bf16 scale per 128 input values;
+    int8 activations use one fp32 scale per row, absmax / 127;
+  * a term whose gate weight is exactly zero is skipped in the weighted sum.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+try:  # torch tensors are accepted as inputs; the oracle computes in numpy.
+    import torch
+except ImportError:  # pragma: no cover
+    torch = None
+
+__all__ = [
+    "as_f64", "as_f32", "router_logits", "select_topk", "topk_margin", "gate_weights",
+    "permute", "silu", "swiglu_expert", "decode_int4", "dequant_int4g128",
+    "quantize_rows_int8", "swiglu_expert_w4a8", "expert_forward", "combine",
+    "SlotPool", "LruSlotPlanner", "Wave", "route", "moe_layer",
+]
+
+
+# ------------------------------------------------------------ conversions ---
+def as_f64(a) -> np.ndarray:
+    """Exact float64 copy of a float32/bf16 array (torch bf16 -> fp32 is exact)."""
+    if torch is not None and isinstance(a, torch.Tensor):
+        a = a.detach().to("cpu")
+        if a.dtype == torch.bfloat16:
+            a = a.to(torch.float32)
+        a = a.numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def as_f32(a) -> np.ndarray:
+    if torch is not None and isinstance(a, torch.Tensor):
+        a = a.detach().to("cpu")
+        if a.dtype == torch.bfloat16:
+            a = a.to(torch.float32)
+        a = a.numpy()
+    return np.asarray(a, dtype=np.float32)
+
+
+def _np(a) -> np.ndarray:
+    if torch is not None and isinstance(a, torch.Tensor):
+        return a.detach().to("cpu").numpy()
+    return np.asarray(a)
+
+
+# ---------------------------------------------------------------- routing ---
+def router_logits(x, w_router, bias=None) -> np.ndarray:
+    """Router logits l[t, e] = sum_h x[t, h] * w_r[e, h] + b[e], float64.
+
+    [RapidMoE] Sec. 2.1: the gating function is a linear projection of the
+    token followed by softmax; the bias carries the synthetic routing skew.
+    """
+    x64, w64 = as_f64(x), as_f64(w_router)
+    logits = x64 @ w64.T
+    if bias is not None:
+        logits = logits + as_f64(bias)[None, :]
+    return logits
+
+
+def select_topk(scores, k: int) -> np.ndarray:
+    """ids[t, :] = the first k experts in the order (score descending, id ascending).
+
+    [RapidMoE] Sec. 2.1: the k experts with the highest logits are activated.
+    The comparison is exact on whatever precision ``scores`` holds; callers
+    pass float32 scores so that the decision is taken in the kernels'
+    precision.
+    """
+    s = np.asarray(scores)
+    T, E = s.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    expert = np.arange(E)
+    for t in range(T):
+        # lexsort: last key is primary -> descending score, then ascending id.
+        order = np.lexsort((expert, -s[t]))
+        ids[t] = order[:k]
+    return ids
+
+
+def topk_margin(scores, k: int) -> np.ndarray:
+    """Gap between the k-th and (k+1)-th largest score of each token (inf if k == E)."""
+    s = np.sort(np.asarray(scores, dtype=np.float64), axis=1)[:, ::-1]
+    if k >= s.shape[1]:
+        return np.full(s.shape[0], np.inf)
+    return s[:, k - 1] - s[:, k]
+
+
+def gate_weights(logits, ids, renorm: bool = True) -> np.ndarray:
+    """Routing weights of the selected experts, float64.
+
+    p = softmax over all experts (max-subtracted); w[t, j] = p[t, ids[t, j]],
+    divided by the sum over the k selected when ``renorm`` ([CAP] Eq. (1):
+    normalised routing weight of each selected expert).
+    """
+    l64 = as_f64(logits)
+    m = l64.max(axis=1, keepdims=True)
+    p = np.exp(l64 - m)
+    p = p / p.sum(axis=1, keepdims=True)
+    w = np.take_along_axis(p, np.asarray(ids, dtype=np.int64), axis=1)
+    if renorm:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w
+
+
+def route(x, w_router, bias, k: int, renorm: bool = True) -> dict:
+    """Logits (float64), their float32 rounding, selection on the float32 values, weights."""
+    logits = router_logits(x, w_router, bias)
+    logits32 = logits.astype(np.float32)
+    ids = select_topk(logits32, k)
+    return dict(logits=logits, logits32=logits32, ids=ids,
+                weights=gate_weights(logits, ids, renorm), margin=topk_margin(logits32, k))
+
+
+# ------------------------------------------------------------ permutation ---
+def permute(ids, E: int) -> dict:
+    """Counting sort of the T*k assignments by expert, stable in token order.
+
+    Flat assignment index f = t*k + j. For each expert in ascending id, the
+    flat indices routed to it in ascending order; counts, exclusive offsets,
+    perm (sorted position -> f), inv (f -> sorted position) and the distinct
+    routed experts (count > 0, ascending).
+    """
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    counts = np.zeros(E, dtype=np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    perm: list[int] = []
+    for e in range(E):
+        rows = np.flatnonzero(flat == e)
+        counts[e] = rows.size
+        offsets[e + 1] = offsets[e] + rows.size
+        perm.extend(int(r) for r in rows)
+    perm_a = np.asarray(perm, dtype=np.int32)
+    inv = np.empty(flat.size, dtype=np.int32)
+    for pos, f in enumerate(perm_a):
+        inv[f] = pos
+    distinct = np.asarray([e for e in range(E) if counts[e] > 0], dtype=np.int32)
+    return dict(counts=counts, offsets=offsets, perm=perm_a, inv=inv, distinct=distinct)
+
+
+# -------------------------------------------------------------- expert FFN ---
+def silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu_expert(x_rows, gate, up, down) -> np.ndarray:
+    """One expert on a block of rows: y = (SiLU(x W_gate) * (x W_up)) W_down.
+
+    [RapidMoE] Eq. (7): SiLU acts on the gate projection, the product with the
+    up projection feeds the down projection. Weights are in nn.Linear
+    orientation: gate, up [F, H]; down [H, F].
+    """
+    x64 = as_f64(x_rows)
+    g = x64 @ as_f64(gate).T
+    u = x64 @ as_f64(up).T
+    with np.errstate(over="ignore"):
+        h = silu(g) * u
+    return h @ as_f64(down).T
+
+
+def decode_int4(codes) -> np.ndarray:
+    """Packed signed 4-bit codes [rows, K/2] (even K in the low nibble) -> int8 [rows, K]."""
+    b = _np(codes).astype(np.uint8)
+    lo = (b & 0x0F).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty((b.shape[0], b.shape[1] * 2), dtype=np.int8)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def dequant_int4g128(codes, scales) -> np.ndarray:
+    """W_hat[n, c] = q[n, c] * s[n, c // 128] (exact in float64)."""
+    q = decode_int4(codes).astype(np.float64)
+    s = as_f64(scales)
+    return q * np.repeat(s, 128, axis=1)
+
+
+def quantize_rows_int8(a) -> tuple[np.ndarray, np.ndarray]:
+    """Symmetric per-row int8: s = max|a_row| / 127, q = clip(rint(a / s), -127, 127).
+
+    Taken in float32 (the kernels' precision), since the float result decides
+    an integer code; a zero row gets s = 1 and q = 0.
+    """
+    a32 = as_f32(a)
+    amax = np.max(np.abs(a32), axis=1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+    q = np.clip(np.rint(a32 / s[:, None]), -127, 127).astype(np.int8)
+    return q, s
+
+
+def swiglu_expert_w4a8(x_rows, w: dict) -> np.ndarray:
+    """SwiGLU expert with int4 group-128 weights and int8 per-row activations.
+
+    x rows and the SwiGLU intermediate are each quantised per row to int8
+    (float32 decision), dequantised exactly, and multiplied in float64 by the
+    exactly dequantised int4 weights.
+    """
+    qx, sx = quantize_rows_int8(x_rows)
+    xh = qx.astype(np.float64) * sx.astype(np.float64)[:, None]
+    g = xh @ dequant_int4g128(w["gate_q"], w["gate_s"]).T
+    u = xh @ dequant_int4g128(w["up_q"], w["up_s"]).T
+    with np.errstate(over="ignore"):
+        h = silu(g) * u
+    qh, sh = quantize_rows_int8(h.astype(np.float32))
+    hh = qh.astype(np.float64) * sh.astype(np.float64)[:, None]
+    return hh @ dequant_int4g128(w["down_q"], w["down_s"]).T
+
+
+def expert_forward(x_rows, w: dict) -> np.ndarray:
+    if "gate_q" in w:
+        return swiglu_expert_w4a8(x_rows, w)
+    return swiglu_expert(x_rows, w["gate"], w["up"], w["down"])
+
+
+# ---------------------------------------------------------------- combine ---
+def combine(y_assign, weights, shared=None) -> np.ndarray:
+    """out[t] = sum_j [w[t,j] != 0] w[t,j] * y[t,j] + sum_s y_shared[s, t].
+
+    [RapidMoE] Sec. 2.1 and Algorithm 1: weighted sum of the routed experts'
+    outputs; [CAP] Eq. (1). y_assign is [T, k, H]: the output of the expert
+    routed at (t, j) for token t. Shared experts enter with weight 1.
+    """
+    y = as_f64(y_assign)
+    w = as_f64(weights)
+    T, k, H = y.shape
+    out = np.zeros((T, H), dtype=np.float64)
+    for j in range(k):
+        nz = w[:, j] != 0.0
+        out[nz] += w[nz, j, None] * y[nz, j]
+    if shared is not None:
+        for ys in shared:
+            out += as_f64(ys)
+    return out
+
+
+# -------------------------------------------------------------- slot pool ---
+class SlotPool:
+    """The fixed-base pool of expert slots and the expert_id -> slot_id table.
+
+    [SeqMoE] Mechanism: one pool of slots shared by every MoE layer; a lookup
+    table rewrites expert ids to slot ids, so the expert computation reads an
+    expert's weights through its slot. Here a slot holds a reference to the
+    weights last copied into it.
+    """
+
+    def __init__(self, num_slots: int, layers: int, E: int):
+        self.content: list[dict | None] = [None] * num_slots
+        self.lut = np.full((layers, E), -1, dtype=np.int32)
+
+    def fill(self, slot: int, weights: dict) -> None:
+        self.content[slot] = weights
+
+    def weights_of(self, layer: int, expert: int) -> dict:
+        slot = int(self.lut[layer, expert])
+        if slot < 0:
+            raise KeyError(f"expert {expert} of layer {layer} is not resident")
+        return self.content[slot]
+
+
+@dataclass
+class Wave:
+    compute: list[int]                                           # experts computed
+    fills: list[tuple[int, int]] = field(default_factory=list)   # (expert, slot)
+
+
+class LruSlotPlanner:
+    """Residency plan for one layer call: hits, misses, victims, fill waves.
+
+    The pages give the vocabulary ([HybriMoE] Mechanism: misses are the routed
+    set minus the cached set, only routed experts are cached, LRU is the
+    baseline replacement; [SeqMoE] Mechanism: one shared pool and a per-layer
+    table) but no hot-path victim rule, so this is plain least-recently-used:
+
+      U = distinct routed experts (ascending), H = resident ones, M = the rest.
+      Victims: empty slots by ascending id, then slots not holding a member of
+      H, by (last use, slot id) ascending.
+      If |M| <= |victims|: one wave, M[i] goes to victim i.
+      Otherwise: wave 1 computes H and the first (S - |H|) misses (into the
+      victims); every later wave takes up to S further misses into slots
+      0, 1, ... in order (the earlier waves' experts are already consumed).
+      A clock advances once per call; every slot used in the call gets it as
+      its last use. The table keeps the state after the last wave.
+    """
+
+    def __init__(self, num_slots: int, layers: int, E: int,
+                 residency: list[tuple[int, int] | None] | None = None):
+        if num_slots < 1:
+            raise ValueError("need at least one slot")
+        self.S, self.L, self.E = num_slots, layers, E
+        self.lut = np.full((layers, E), -1, dtype=np.int32)
+        self.owner: list[tuple[int, int] | None] = [None] * num_slots
+        self.last_use = [0] * num_slots
+        self.clock = 0
+        for s, o in enumerate(residency or []):
+            if o is not None:
+                self.lut[o] = s
+                self.owner[s] = o
+
+    def _assign(self, layer: int, expert: int, slot: int) -> None:
+        old = self.owner[slot]
+        if old is not None:
+            self.lut[old] = -1
+        self.lut[layer, expert] = slot
+        self.owner[slot] = (layer, expert)
+
+    def plan(self, layer: int, distinct) -> list[Wave]:
+        self.clock += 1
+        U = sorted(int(e) for e in distinct)
+        hits = [e for e in U if self.lut[layer, e] >= 0]
+        misses = [e for e in U if self.lut[layer, e] < 0]
+        kept = {int(self.lut[layer, e]) for e in hits}
+        empty = [s for s in range(self.S) if self.owner[s] is None]
+        reusable = sorted((s for s in range(self.S) if self.owner[s] is not None and s not in kept),
+                          key=lambda s: (self.last_use[s], s))
+        victims = empty + reusable
+        used = set(kept)
+        waves: list[Wave] = []
+        if len(misses) <= len(victims):
+            fills = list(zip(misses, victims))
+            waves.append(Wave(compute=list(U), fills=fills))
+        else:
+            first = misses[:len(victims)]
+            waves.append(Wave(compute=hits + first, fills=list(zip(first, victims))))
+            rest = misses[len(first):]
+            for i in range(0, len(rest), self.S):
+                chunk = rest[i:i + self.S]
+                waves.append(Wave(compute=list(chunk), fills=list(zip(chunk, range(len(chunk))))))
+        for wave in waves:
+            for e, s in wave.fills:
+                self._assign(layer, e, s)
+                used.add(s)
+        for s in used:
+            self.last_use[s] = self.clock
+        return waves
+
+
+# ------------------------------------------------------------- full layer ---
+def moe_layer(x, w_router, bias, k: int, *, layer: int, pool: SlotPool,
+              planner: LruSlotPlanner | None, weights_of_expert,
+              shared: list[dict] | None = None, renorm: bool = True) -> dict:
+    """One routed-expert layer over the slot pool.
+
+    route -> permute -> residency plan (fills copy the expert's weights into
+    its slot) -> each routed (t, j) runs expert ids[t, j] with the weights
+    read through pool.lut -> weighted combine (+ shared experts, weight 1).
+    ``weights_of_expert(e)`` returns the host-store weights of expert e of
+    this layer (what a fill copies).
+    """
+    r = route(x, w_router, bias, k, renorm)
+    ids = r["ids"]
+    p = permute(ids, w_router.shape[0])
+    waves = []
+    if planner is not None:
+        waves = planner.plan(layer, p["distinct"])
+        for wave in waves:
+            for e, s in wave.fills:
+                pool.fill(s, weights_of_expert(e))
+        pool.lut[layer] = planner.lut[layer]
+    x_rows = as_f32(x)  # exact for fp32 and bf16 tokens; each expert form converts further
+    T = ids.shape[0]
+    H = as_f64(w_router).shape[1]
+    y = np.zeros((T, k, H), dtype=np.float64)
+    for e in p["distinct"]:
+        e = int(e)
+        f = p["perm"][p["offsets"][e]:p["offsets"][e + 1]]
+        t_rows, j_rows = f // k, f % k
+        y[t_rows, j_rows] = expert_forward(x_rows[t_rows], pool.weights_of(layer, e))
+    y_sh = [expert_forward(x_rows, w) for w in (shared or [])]
+    out = combine(y, r["weights"], y_sh)
+    return dict(route=r, perm=p, waves=waves, y=y, y_shared=y_sh, out=out)

@@ -1,0 +1,335 @@
+"""Pins of the oracle to things other than itself (CPU only).
+
+Every check goes through a different route than the oracle's own code: brute
+force on tiny inputs, closed forms worked out by hand, an independent library
+routine (scipy, torch.nn.functional, numpy's stable argsort), a textbook
+algorithm the policy reduces to, or an invariant the definition implies.
+"""
+import math
+from collections import OrderedDict
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as Fnn
+
+import oracle as O
+from expert_offload_routed_amd import workloads as W
+
+
+# ------------------------------------------------------------ router logits --
+def test_router_logits_closed_form():
+    # x = [1, 2]; rows of w_r are expert vectors; bias shifts each logit.
+    x = np.array([[1.0, 2.0], [0.0, -1.0]])
+    w_r = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    b = np.array([0.5, -0.5, 0.0])
+    got = O.router_logits(x, w_r, b)
+    assert got.tolist() == [[1.5, 1.5, 3.0], [0.5, -1.5, -1.0]]
+
+
+def test_router_logits_matches_torch_linear_nonsquare():
+    g = torch.Generator().manual_seed(1)
+    x = torch.randn(5, 37, generator=g, dtype=torch.float64)
+    w = torch.randn(11, 37, generator=g, dtype=torch.float64)
+    b = torch.randn(11, generator=g, dtype=torch.float64)
+    ref = Fnn.linear(x, w, b).numpy()
+    np.testing.assert_allclose(O.router_logits(x.numpy(), w.numpy(), b.numpy()), ref, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- selection --
+def _brute_topk(row, k):
+    return sorted(range(len(row)), key=lambda e: (-float(row[e]), e))[:k]
+
+
+@pytest.mark.parametrize("E,k", [(4, 1), (8, 2), (16, 6), (9, 9), (33, 8)])
+def test_select_topk_equals_full_sort_with_ties(E, k):
+    rng = np.random.default_rng(E * 100 + k)
+    scores = rng.integers(-3, 4, size=(40, E)).astype(np.float32)  # many exact ties
+    ids = O.select_topk(scores, k)
+    for t in range(scores.shape[0]):
+        assert ids[t].tolist() == _brute_topk(scores[t], k)
+
+
+def test_select_topk_hand_ties():
+    s = np.array([[1.0, 3.0, 3.0, 2.0], [0.0, 0.0, 0.0, 0.0], [-1.0, -0.0, 0.0, 5.0]], np.float32)
+    assert O.select_topk(s, 2).tolist() == [[1, 2], [0, 1], [3, 1]]
+
+
+def test_topk_margin_brute():
+    rng = np.random.default_rng(3)
+    s = rng.normal(size=(10, 12))
+    m = O.topk_margin(s, 3)
+    for t in range(10):
+        v = sorted(s[t], reverse=True)
+        assert m[t] == v[2] - v[3]
+    assert np.all(np.isinf(O.topk_margin(s, 12)))
+
+
+# ------------------------------------------------------------------ gating --
+def test_gate_weights_two_experts_closed_form():
+    l = np.array([[2.0, -1.0, 0.5]])
+    ids = np.array([[0, 2]])
+    w = O.gate_weights(l, ids, renorm=True)
+    w0 = 1.0 / (1.0 + math.exp(0.5 - 2.0))  # softmax of two logits = logistic of the gap
+    assert w[0, 0] == pytest.approx(w0, rel=1e-15)
+    assert w[0, 1] == pytest.approx(1.0 - w0, rel=1e-14)
+
+
+def test_gate_weights_against_scipy_softmax():
+    rng = np.random.default_rng(4)
+    l = rng.normal(size=(20, 16)) * 3
+    ids = O.select_topk(l.astype(np.float32), 5)
+    w = O.gate_weights(l, ids, renorm=True)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    sel = np.take_along_axis(l, ids, axis=1)
+    np.testing.assert_allclose(w, scipy.special.softmax(sel, axis=1), rtol=1e-13)
+    w_raw = O.gate_weights(l, ids, renorm=False)
+    np.testing.assert_allclose(w_raw, np.take_along_axis(scipy.special.softmax(l, axis=1), ids, axis=1),
+                               rtol=1e-13)
+
+
+def test_gate_weights_k_equals_e_is_plain_softmax_and_k1_is_one():
+    rng = np.random.default_rng(5)
+    l = rng.normal(size=(7, 6))
+    ids = O.select_topk(l.astype(np.float32), 6)
+    w = O.gate_weights(l, ids)
+    np.testing.assert_allclose(w, np.take_along_axis(scipy.special.softmax(l, axis=1), ids, axis=1),
+                               rtol=1e-13)
+    w1 = O.gate_weights(l, O.select_topk(l.astype(np.float32), 1))
+    assert np.all(w1 == 1.0)
+
+
+def test_route_orders_by_descending_weight():
+    s = W.shape_of("tiny_e8k2_h256_f512_fp32")
+    r = O.route(W.tokens(s, 16), *W.router(s), k=2)
+    assert np.all(np.diff(r["weights"], axis=1) <= 0)
+
+
+# ------------------------------------------------------------- permutation --
+@pytest.mark.parametrize("T,E,k", [(0, 8, 2), (1, 8, 2), (16, 8, 2), (37, 64, 6), (200, 256, 8)])
+def test_permute_against_stable_argsort(T, E, k):
+    rng = np.random.default_rng(T + E)
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32).reshape(T, k)
+    p = O.permute(ids, E)
+    flat = ids.reshape(-1)
+    assert p["perm"].tolist() == np.argsort(flat, kind="stable").tolist()
+    bc = np.bincount(flat, minlength=E)
+    assert p["counts"].tolist() == bc.tolist()
+    assert p["offsets"].tolist() == [0] + np.cumsum(bc).tolist()
+    assert int(p["counts"].sum()) == T * k
+    if T:
+        assert np.array_equal(p["inv"][p["perm"]], np.arange(T * k))
+    assert p["distinct"].tolist() == [e for e in range(E) if bc[e] > 0]
+    # inside an expert's segment, tokens rise strictly (each token picks an expert once)
+    for e in range(E):
+        seg = p["perm"][p["offsets"][e]:p["offsets"][e + 1]] // k
+        assert np.all(np.diff(seg) > 0)
+
+
+# ------------------------------------------------------------- expert FFN ---
+def test_swiglu_closed_form():
+    x = np.array([[1.0, 2.0]])
+    gate = np.array([[1.0, 0.0]])   # g = x0 = 1
+    up = np.array([[0.0, 1.0]])     # u = x1 = 2
+    down = np.array([[1.0], [-1.0]])
+    s1 = 1.0 / (1.0 + math.exp(-1.0))  # SiLU(1) = 1 * sigmoid(1)
+    y = O.swiglu_expert(x, gate, up, down)
+    assert y[0, 0] == pytest.approx(2 * s1, rel=1e-15)
+    assert y[0, 1] == pytest.approx(-2 * s1, rel=1e-15)
+
+
+def test_swiglu_matches_torch_nonsquare():
+    g = torch.Generator().manual_seed(7)
+    H, F, n = 24, 40, 5
+    x = torch.randn(n, H, generator=g, dtype=torch.float64)
+    gate = torch.randn(F, H, generator=g, dtype=torch.float64)
+    up = torch.randn(F, H, generator=g, dtype=torch.float64)
+    down = torch.randn(H, F, generator=g, dtype=torch.float64)
+    ref = Fnn.linear(Fnn.silu(Fnn.linear(x, gate)) * Fnn.linear(x, up), down).numpy()
+    got = O.swiglu_expert(x.numpy(), gate.numpy(), up.numpy(), down.numpy())
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------- int4 and int8 ---
+def _pack_int4(q):
+    """Reference packer: two's-complement nibbles, even column in the low nibble."""
+    q = np.asarray(q, dtype=np.int64)
+    lo = q[:, 0::2] & 0xF
+    hi = q[:, 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def test_int4_decode_roundtrip_all_codes():
+    rng = np.random.default_rng(8)
+    q = rng.integers(-8, 8, size=(6, 256))
+    q[0, :16] = np.arange(-8, 8)
+    assert np.array_equal(O.decode_int4(_pack_int4(q)), q.astype(np.int8))
+
+
+def test_int4_dequant_group_boundaries():
+    rows, K = 3, 384
+    q = np.ones((rows, K), dtype=np.int64)
+    q[:, 1::2] = -2
+    scales = torch.tensor([[0.5, 0.25, 2.0], [1.0, 3.0, -0.125], [4.0, 0.0, 1.5]], dtype=torch.bfloat16)
+    w = O.dequant_int4g128(_pack_int4(q), scales)
+    s = scales.float().numpy().astype(np.float64)
+    for r in range(rows):
+        for c in (0, 1, 126, 127, 128, 129, 255, 256, 383):
+            assert w[r, c] == q[r, c] * s[r, c // 128]
+
+
+def test_int8_rows_error_bound_and_extremes():
+    rng = np.random.default_rng(9)
+    a = (rng.normal(size=(8, 300)) * rng.uniform(0.01, 50, size=(8, 1))).astype(np.float32)
+    a[3] = 0.0
+    q, s = O.quantize_rows_int8(a)
+    assert q[3].tolist() == [0] * 300 and s[3] == 1.0
+    for r in range(8):
+        if r == 3:
+            continue
+        amax = np.abs(a[r]).max()
+        assert s[r] == np.float32(amax / np.float32(127))
+        assert np.abs(q[r]).max() == 127
+        err = np.abs(a[r].astype(np.float64) - q[r].astype(np.float64) * float(s[r]))
+        assert err.max() <= float(s[r]) * 0.5 * (1 + 1e-6)
+    qn, sn = O.quantize_rows_int8(-a)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+
+
+def test_w4a8_expert_close_to_dense_on_dequantised_weights():
+    sh = W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), H=256, F=128)
+    w = W.expert_weights(sh, 0)
+    x = W.tokens(sh, 4).float().numpy()
+    dense = O.swiglu_expert(x, O.dequant_int4g128(w["gate_q"], w["gate_s"]),
+                            O.dequant_int4g128(w["up_q"], w["up_s"]),
+                            O.dequant_int4g128(w["down_q"], w["down_s"]))
+    q = O.swiglu_expert_w4a8(x, w)
+    rel = np.linalg.norm(q - dense) / np.linalg.norm(dense)
+    assert 0 < rel < 0.03  # only the two int8 activation roundings differ
+
+
+# ---------------------------------------------------------------- combine ---
+def test_combine_linearity_and_zero_weight_poison():
+    rng = np.random.default_rng(10)
+    y = rng.normal(size=(4, 3, 8))
+    w = np.zeros((4, 3))
+    w[:, 1] = 1.0
+    np.testing.assert_array_equal(O.combine(y, w), y[:, 1])
+    y[:, 2] = np.nan
+    w2 = np.array([[0.6, 0.4, 0.0]] * 4)
+    out = O.combine(y, w2)
+    assert np.all(np.isfinite(out))
+    np.testing.assert_allclose(out, 0.6 * y[:, 0] + 0.4 * y[:, 1], rtol=1e-15)
+    sh = rng.normal(size=(2, 4, 8))
+    np.testing.assert_allclose(O.combine(y, w2, sh), out + sh[0] + sh[1], rtol=1e-15)
+
+
+# ---------------------------------------------------------- full layer ------
+def _tiny_layer(lut_perm, E=8, k=2, H=64, F=96, T=12):
+    sh = W.reduced(W.shape_of("tiny_e8k2_h256_f512_fp32"), E=E, k=k, H=H, F=F)
+    x = W.tokens(sh, T)
+    wr, b = W.router(sh)
+    experts = [W.expert_weights(sh, e) for e in range(E)]
+    pool = O.SlotPool(E, 1, E)
+    for e in range(E):
+        pool.fill(lut_perm[e], experts[e])
+        pool.lut[0, e] = lut_perm[e]
+    return O.moe_layer(x, wr, b, k, layer=0, pool=pool, planner=None,
+                       weights_of_expert=lambda e: experts[e]), experts, x, wr, b
+
+
+def test_slot_relabel_invariance():
+    a, *_ = _tiny_layer(list(range(8)))
+    b, *_ = _tiny_layer([5, 2, 7, 0, 3, 6, 1, 4])
+    assert np.array_equal(a["out"], b["out"])
+
+
+def test_layer_e1_k1_is_dense_swiglu():
+    res, experts, x, wr, b = _tiny_layer([0], E=1, k=1)
+    w = {n: torch.tensor(t.numpy(), dtype=torch.float64) for n, t in experts[0].items()}
+    xt = torch.tensor(x.numpy(), dtype=torch.float64)
+    ref = Fnn.linear(Fnn.silu(Fnn.linear(xt, w["gate"])) * Fnn.linear(xt, w["up"]), w["down"]).numpy()
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_weighted_sum_by_hand():
+    res, experts, x, wr, b = _tiny_layer(list(range(8)), T=3)
+    ids, w = res["route"]["ids"], res["route"]["weights"]
+    for t in range(3):
+        acc = 0
+        for j in range(2):
+            e = experts[ids[t, j]]
+            acc = acc + w[t, j] * O.swiglu_expert(x[t:t + 1].numpy(), e["gate"], e["up"], e["down"])[0]
+        np.testing.assert_allclose(res["out"][t], acc, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------- LRU slot planner ---
+def test_planner_reduces_to_textbook_lru_for_single_expert_requests():
+    rng = np.random.default_rng(11)
+    E, S = 12, 4
+    planner = O.LruSlotPlanner(S, 1, E)
+    lru = OrderedDict()
+    for step in range(400):
+        e = int(rng.zipf(1.3) - 1) % E
+        before = planner.lut[0, e] >= 0
+        waves = planner.plan(0, [e])
+        # textbook LRU cache of capacity S
+        hit = e in lru
+        if hit:
+            lru.move_to_end(e)
+        else:
+            if len(lru) == S:
+                lru.popitem(last=False)
+            lru[e] = True
+        assert before == hit, step
+        assert sorted(int(v) for v in np.flatnonzero(planner.lut[0] >= 0)) == sorted(lru)
+        assert len(waves) == 1 and len(waves[0].fills) == (0 if hit else 1)
+
+
+def test_planner_hand_trace():
+    # 3 slots, one layer of 6 experts; slot 2 starts empty.
+    p = O.LruSlotPlanner(3, 1, 6, residency=[(0, 4), (0, 1), None])
+    w = p.plan(0, [1, 3])          # hit 1 (slot 1); miss 3 -> empty slot 2
+    assert [(x.compute, x.fills) for x in w] == [([1, 3], [(3, 2)])]
+    w = p.plan(0, [0, 3])          # hit 3; miss 0 -> LRU among {0 (last 0), 1 (last 1)} = slot 0
+    assert [(x.compute, x.fills) for x in w] == [([0, 3], [(0, 0)])]
+    assert p.lut[0].tolist() == [0, 1, -1, 2, -1, -1]
+    w = p.plan(0, [1, 2, 4, 5])    # |U| = 4 > S = 3: hit 1 stays; misses 2, 4, 5
+    # wave 1: hit 1 + first two misses into victims by LRU: slot 0 (last 2) vs 2 (last 2) -> id order 0, 2
+    assert [(x.compute, x.fills) for x in w] == [([1, 2, 4], [(2, 0), (4, 2)]), ([5], [(5, 0)])]
+    assert p.lut[0].tolist() == [-1, 1, -1, -1, 2, 0]
+    assert p.last_use == [3, 3, 3]
+
+
+def test_planner_invariants_random_multilayer():
+    rng = np.random.default_rng(12)
+    L, E, S, k = 3, 10, 7, 3
+    p = O.LruSlotPlanner(S, L, E)
+    for step in range(300):
+        layer = step % L
+        T = int(rng.integers(1, 5))
+        U = sorted({int(e) for e in rng.choice(E, size=(T * k), replace=True)})
+        lut_before = p.lut.copy()
+        hits = [e for e in U if lut_before[layer, e] >= 0]
+        waves = p.plan(layer, U)
+        computed = [e for wv in waves for e in wv.compute]
+        assert sorted(computed) == U
+        fills = [f for wv in waves for f in wv.fills]
+        assert sorted(e for e, _ in fills) == sorted(set(U) - set(hits))
+        # wave 1's fills never land on a slot holding a hit of this call
+        kept = {int(lut_before[layer, e]) for e in hits}
+        assert not kept & {s for _, s in waves[0].fills}
+        # no slot is filled twice within one wave
+        for wv in waves:
+            assert len({s for _, s in wv.fills}) == len(wv.fills)
+        # table is injective and the owner list is its inverse
+        own = {}
+        for (l_, e_), s in np.ndenumerate(p.lut):
+            if s >= 0:
+                assert s not in own
+                own[int(s)] = (l_, e_)
+        for s in range(S):
+            assert p.owner[s] == own.get(s)
+        if len(U) <= S:
+            assert all(p.lut[layer, e] >= 0 for e in U)
