@@ -1,0 +1,236 @@
+"""Thin ctypes binding of libmoe_offload (same names as the C ABI in include/moe_offload.h).
+
+Argument marshalling only: tensors become device pointers, streams become HIP
+stream handles, missing outputs are allocated with torch, and a non-zero
+status raises ``MoeError``. Every step of the layer runs in the library's
+kernels; there is no fallback path, and loading fails loudly when the library
+has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import torch
+
+from .build import LIB_PATH
+
+MOE_F32, MOE_BF16, MOE_INT4G128 = 0, 1, 2
+MOE_ERR_ABSENT, MOE_ERR_STALE_TAG = 1, 2
+_STATUS = {-1: "invalid argument", -2: "unsupported dtype or shape", -3: "HIP runtime error"}
+
+_vp, _i32, _i64, _u64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_route": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "moe_permute": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_slot_layout": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "moe_pack_expert_host": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
+    "moe_ffn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "moe_expert_ffn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _i32, _i32, _i32, _i32,
+                              _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_combine": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _vp]),
+    "slot_fill": (_i32, [_vp, _sz, _i32, _vp, _sz, _vp, _i32, _vp, _vp, _u64, _vp, _vp, _vp]),
+    "slot_commit": (_i32, [_vp, _i32, _vp, _i32, _vp, _u64, _vp, _vp]),
+    "moe_plan_fills": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp,
+                              _vp, _vp, _vp, _vp]),
+    "moe_version": (ctypes.c_char_p, []),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, rc: int):
+        super().__init__(f"{fn} failed: {rc} ({_STATUS.get(rc, 'unknown status')})")
+        self.rc = rc
+
+
+_LIB: ctypes.CDLL | None = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python __graft_entry__.py` "
+                               "or expert_offload_routed_amd.build.build()")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            if hasattr(handle, name):
+                fn = getattr(handle, name)
+                fn.restype, fn.argtypes = res, args
+        _LIB = handle
+    return _LIB
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/*.h."""
+    inc = os.path.join(os.path.dirname(os.path.dirname(LIB_PATH)), "include")
+    names = []
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            src = open(os.path.join(inc, f)).read()
+            names += re.findall(r"^(?:const\s+)?\w+\s*\*?\s+(\w+)\s*\(", src, flags=re.M)
+    return names
+
+
+def _call(name: str, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != 0:
+        raise MoeError(name, rc)
+
+
+# ------------------------------------------------------------- marshalling --
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _host(a):
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("expected a contiguous array")
+        return a.ctypes.data
+    if a.is_cuda or not a.is_contiguous():
+        raise ValueError("expected a contiguous host tensor")
+    return a.data_ptr()
+
+
+def _stream(s) -> int:
+    if s is None:
+        s = torch.cuda.current_stream()
+    return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+
+
+# ----------------------------------------------------------------- gating --
+def moe_route(x, w_router, bias, k: int, renorm: bool = True, logits=None, topk_ids=None,
+              topk_w=None, stream=None):
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    logits = torch.empty(T, E, device=dev, dtype=torch.float32) if logits is None else logits
+    topk_ids = torch.empty(T, k, device=dev, dtype=torch.int32) if topk_ids is None else topk_ids
+    topk_w = torch.empty(T, k, device=dev, dtype=torch.float32) if topk_w is None else topk_w
+    if w_router.dtype != x.dtype:
+        raise TypeError("x and w_router must share a dtype")
+    _call("moe_route", _dev(x), dtype_code(x), _dev(w_router), _dev(bias), T, H, E, k, int(renorm),
+          _dev(logits), _dev(topk_ids), _dev(topk_w), _stream(stream))
+    return logits, topk_ids, topk_w
+
+
+def moe_permute(topk_ids, E: int, out: dict | None = None, stream=None) -> dict:
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    o = out or {}
+    o.setdefault("counts", torch.empty(E, device=dev, dtype=torch.int32))
+    o.setdefault("offsets", torch.empty(E + 1, device=dev, dtype=torch.int32))
+    o.setdefault("perm", torch.empty(max(T * k, 1), device=dev, dtype=torch.int32))
+    o.setdefault("inv", torch.empty(max(T * k, 1), device=dev, dtype=torch.int32))
+    o.setdefault("distinct", torch.empty(E, device=dev, dtype=torch.int32))
+    o.setdefault("n_distinct", torch.empty(1, device=dev, dtype=torch.int32))
+    _call("moe_permute", _dev(topk_ids), T, k, E, _dev(o["counts"]), _dev(o["offsets"]),
+          _dev(o["perm"]), _dev(o["inv"]), _dev(o["distinct"]), _dev(o["n_distinct"]),
+          _stream(stream))
+    return o
+
+
+# ------------------------------------------------------------ slot layout --
+def moe_slot_layout(H: int, F: int, w_dtype: int) -> dict:
+    vals = [ctypes.c_size_t() for _ in range(5)]
+    _call("moe_slot_layout", H, F, w_dtype, *[ctypes.addressof(v) for v in vals])
+    return dict(zip(("slot_bytes", "off_w13", "off_w2", "off_s13", "off_s2"), (v.value for v in vals)))
+
+
+def moe_pack_expert_host(weights: dict, H: int, F: int, w_dtype: int, dst) -> None:
+    """Pack one expert (host tensors, nn.Linear orientation) into dst (host uint8, slot bytes)."""
+    def h(name):
+        t = weights.get(name)
+        if t is None:
+            return None
+        t = t.contiguous()
+        weights[name] = t
+        return _host(t)
+    if w_dtype == MOE_INT4G128:
+        args = [h("gate_q"), h("up_q"), h("down_q"), h("gate_s"), h("up_s"), h("down_s")]
+    else:
+        args = [h("gate"), h("up"), h("down"), None, None, None]
+    _call("moe_pack_expert_host", *args, H, F, w_dtype, _host(dst))
+
+
+# ------------------------------------------------------------- expert FFN --
+def moe_ffn_workspace_bytes(T, H, F, E, k, w_dtype) -> int:
+    return int(lib().moe_ffn_workspace_bytes(T, H, F, E, k, w_dtype))
+
+
+def moe_expert_ffn(x, perm, offsets, lut_row, group_mask, pool, slot_stride: int, w_dtype: int,
+                   T: int, H: int, F: int, E: int, k: int, y_perm, err_word, workspace, stream=None):
+    num_slots = pool.numel() // slot_stride
+    _call("moe_expert_ffn", _dev(x), dtype_code(x), _dev(perm), _dev(offsets), _dev(lut_row),
+          _dev(group_mask), _dev(pool), slot_stride, num_slots, w_dtype, T, H, F, E, k, _dev(y_perm),
+          _dev(err_word), _dev(workspace), workspace.numel() * workspace.element_size(),
+          _stream(stream))
+
+
+# ---------------------------------------------------------------- combine --
+def moe_combine(y_perm, inv, topk_w, T: int, k: int, H: int, shared_y=None, out=None,
+                out_dtype=torch.bfloat16, stream=None):
+    if out is None:
+        out = torch.empty(T, H, device=topk_w.device, dtype=out_dtype)
+    n_sh = 0 if shared_y is None else shared_y.shape[0]
+    _call("moe_combine", _dev(y_perm), _dev(inv), _dev(topk_w), T, k, H, _dev(shared_y), n_sh,
+          _dev(out), dtype_code(out), _stream(stream))
+    return out
+
+
+# -------------------------------------------------------------- slot fill --
+def slot_fill(pool, slot_stride: int, slot: int, host_src, nbytes: int, lut, lut_index: int, owner,
+              slot_tags, tag: int, err_word, fill_stream=None, compute_stream=None):
+    src = host_src if isinstance(host_src, int) else host_src.data_ptr()
+    _call("slot_fill", _dev(pool), slot_stride, slot, src, nbytes, _dev(lut), lut_index, _dev(owner),
+          _dev(slot_tags), tag, _dev(err_word), _stream(fill_stream), _stream(compute_stream))
+
+
+def slot_commit(lut, lut_index: int, owner, slot: int, slot_tags, tag: int, err_word, stream=None):
+    _call("slot_commit", _dev(lut), lut_index, _dev(owner), slot, _dev(slot_tags), tag,
+          _dev(err_word), _stream(stream))
+
+
+# --------------------------------------------------------- host residency --
+def moe_plan_fills(lut: np.ndarray, owner: np.ndarray, last_use: np.ndarray, clock: np.ndarray,
+                   S: int, L: int, E: int, layer: int, distinct: np.ndarray) -> dict:
+    """Run the host LRU plan on numpy state arrays (updated in place)."""
+    assert lut.dtype == np.int32 and owner.dtype == np.int32
+    assert last_use.dtype == np.int64 and clock.dtype == np.int64
+    d = np.ascontiguousarray(distinct, dtype=np.int32)
+    n = d.size
+    wave_of = np.empty(E, np.int32)
+    is_hit = np.empty(E, np.int32)
+    fe, fs, fw = (np.empty(max(n, 1), np.int32) for _ in range(3))
+    nf, nw = np.zeros(1, np.int32), np.zeros(1, np.int32)
+    _call("moe_plan_fills", _host(lut), _host(owner), _host(last_use), _host(clock), S, L, E, layer,
+          _host(d) if n else None, n, _host(wave_of), _host(is_hit), _host(fe), _host(fs), _host(fw),
+          _host(nf), _host(nw))
+    k = int(nf[0])
+    return dict(wave_of=wave_of, is_hit=is_hit, fill_expert=fe[:k].copy(), fill_slot=fs[:k].copy(),
+                fill_wave=fw[:k].copy(), n_waves=int(nw[0]))
+
+
+def moe_version() -> str:
+    return lib().moe_version().decode()

@@ -1,0 +1,203 @@
+// Router logits, top-k selection and routing weights (moe_route).
+//
+// Gating as defined in "RapidMoE: Exploiting Cross-Asymmetry via Adaptive
+// Residual Offloading for Large-Scale MoE Inference", Sec. 2.1: a linear
+// projection of the token, softmax, and the k experts with the highest
+// logits; the weights are normalised over the selected experts ("Communication-
+// Aware Placement and Pruning for Efficient Mixture-of-Experts Inference",
+// Sec. II-A, Eq. (1)).
+//
+// Two kernels:
+//   route_logits_kernel: each wave computes EW experts x TT tokens of dot
+//     products over H; lanes stride H with 8-element vectors (16-byte bf16 /
+//     2x16-byte fp32 loads), fp32 FMA, then a wave reduction. Spread over
+//     ceil(E/EW) x ceil(T/TT) waves so a decode step pulls w_router from HBM
+//     with many CUs at once.
+//   topk_softmax_kernel: one wave per token; lane l holds logits l, l+64, ...
+//     Each of the k rounds takes the wave-wide (value desc, id asc) maximum
+//     through xor shuffles; then softmax over the selected values.
+#include <float.h>
+#include <limits.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kRouteEW = 4;   // experts per wave
+constexpr int kRouteTT = 4;   // tokens per wave
+constexpr int kTopkMaxV = 16; // logits per lane (E <= 1024)
+
+template <int FMT>
+__device__ __forceinline__ void load8(const void* base, size_t elem, float out[8]) {
+  if constexpr (FMT == MOE_BF16) {
+    u32x4 v = ld16(static_cast<const uint16_t*>(base) + elem);
+    out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
+    out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+    out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
+    out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+  } else {
+    const float* p = static_cast<const float*>(base) + elem;
+    u32x4 a = ld16(p), b = ld16(p + 4);
+    out[0] = __uint_as_float(a.x); out[1] = __uint_as_float(a.y);
+    out[2] = __uint_as_float(a.z); out[3] = __uint_as_float(a.w);
+    out[4] = __uint_as_float(b.x); out[5] = __uint_as_float(b.y);
+    out[6] = __uint_as_float(b.z); out[7] = __uint_as_float(b.w);
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void route_logits_kernel(const void* __restrict__ x,
+                                                           const void* __restrict__ w,
+                                                           const float* __restrict__ bias, int T,
+                                                           int H, int E, float* __restrict__ logits) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int e0 = (blockIdx.x * 4 + wave) * kRouteEW;
+  const int t0 = blockIdx.y * kRouteTT;
+  if (e0 >= E) return;
+  const int ne = min(kRouteEW, E - e0);
+  const int nt = min(kRouteTT, T - t0);
+
+  float acc[kRouteEW][kRouteTT];
+#pragma unroll
+  for (int e = 0; e < kRouteEW; ++e)
+#pragma unroll
+    for (int t = 0; t < kRouteTT; ++t) acc[e][t] = 0.f;
+
+  for (int c = lane * 8; c < H; c += 64 * 8) {
+    float wv[kRouteEW][8];
+#pragma unroll
+    for (int e = 0; e < kRouteEW; ++e) {
+      if (e < ne) {
+        load8<FMT>(w, (size_t)(e0 + e) * H + c, wv[e]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) wv[e][q] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kRouteTT; ++t) {
+      if (t < nt) {
+        float xv[8];
+        load8<FMT>(x, (size_t)(t0 + t) * H + c, xv);
+#pragma unroll
+        for (int e = 0; e < kRouteEW; ++e)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[e][t] = fmaf(wv[e][q], xv[q], acc[e][t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kRouteEW; ++e) {
+#pragma unroll
+    for (int t = 0; t < kRouteTT; ++t) {
+      if (e < ne && t < nt) {
+        float s = wave_sum(acc[e][t]);
+        if (lane == 0) logits[(size_t)(t0 + t) * E + e0 + e] = s + (bias ? bias[e0 + e] : 0.f);
+      }
+    }
+  }
+}
+
+// (value, id) order used for selection: larger value first, then smaller id.
+__device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
+  return v > bv || (v == bv && id < bid);
+}
+
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int T,
+                                                           int E, int k, int renorm,
+                                                           int32_t* __restrict__ ids,
+                                                           float* __restrict__ weights) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+
+  float v[kTopkMaxV];
+  uint32_t avail = 0;  // bit i: logit of expert lane + 64 i still selectable
+#pragma unroll
+  for (int i = 0; i < kTopkMaxV; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = -INFINITY;
+    if (e < E) {
+      v[i] = logits[(size_t)t * E + e];
+      avail |= 1u << i;
+    }
+  }
+  float sel[kTopkMaxV];  // selected value r is held by lane r % 64 in sel[r / 64]
+#pragma unroll
+  for (int i = 0; i < kTopkMaxV; ++i) sel[i] = 0.f;
+  float vmax = 0.f;
+
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bid = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < kTopkMaxV; ++i) {
+      if ((avail >> i) & 1u) {
+        if (better(v[i], lane + 64 * i, bv, bid)) {
+          bv = v[i];
+          bid = lane + 64 * i;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(bv, m, 64);
+      const int oid = __shfl_xor(bid, m, 64);
+      if (better(ov, oid, bv, bid)) {
+        bv = ov;
+        bid = oid;
+      }
+    }
+    if (bid != INT_MAX && (bid & 63) == lane) avail &= ~(1u << (bid >> 6));
+#pragma unroll
+    for (int i = 0; i < kTopkMaxV; ++i)
+      if (i == (r >> 6) && lane == (r & 63)) sel[i] = bv;
+    if (r == 0) vmax = bv;
+    if (lane == 0) ids[(size_t)t * k + r] = (bid == INT_MAX) ? -1 : bid;
+  }
+
+  float denom = 0.f;
+  if (renorm) {
+#pragma unroll
+    for (int i = 0; i < kTopkMaxV; ++i)
+      if (lane + 64 * i < k) denom += expf(sel[i] - vmax);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kTopkMaxV; ++i)
+      if (lane + 64 * i < E) denom += expf(v[i] - vmax);
+  }
+  denom = wave_sum(denom);
+#pragma unroll
+  for (int i = 0; i < kTopkMaxV; ++i) {
+    const int r = lane + 64 * i;
+    if (r < k) weights[(size_t)t * k + r] = expf(sel[i] - vmax) / denom;
+  }
+}
+
+}  // namespace
+
+extern "C" int moe_route(const void* x, int x_dtype, const void* w_router, const float* bias,
+                         int T, int H, int E, int k, int renorm, float* logits,
+                         int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && H > 0 && H % 8 == 0);
+  MOE_CHECK_ARG(k >= 1 && k <= E && E <= 64 * kTopkMaxV);
+  MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(x && w_router && logits && topk_ids && topk_w);
+  MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)w_router % 16) == 0);
+
+  const int eblocks = (E + kRouteEW - 1) / kRouteEW;
+  dim3 g1((eblocks + 3) / 4, (T + kRouteTT - 1) / kRouteTT);
+  if (g1.y > 65535u) return MOE_EUNSUPPORTED;
+  if (x_dtype == MOE_BF16)
+    hipLaunchKernelGGL(route_logits_kernel<MOE_BF16>, g1, dim3(256), 0, stream, x, w_router, bias,
+                       T, H, E, logits);
+  else
+    hipLaunchKernelGGL(route_logits_kernel<MOE_F32>, g1, dim3(256), 0, stream, x, w_router, bias,
+                       T, H, E, logits);
+  hipLaunchKernelGGL(topk_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E,
+                     k, renorm, topk_ids, topk_w);
+  return moe_launch_status();
+}

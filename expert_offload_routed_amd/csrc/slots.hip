@@ -1,0 +1,250 @@
+// Slot pool layout, host packing, tagged slot fills and the host LRU plan.
+//
+// The SeqMoE summary page (Mechanism) gives the residency design: one pool of
+// slots at a fixed base address shared by every MoE layer, a table rewriting
+// expert_id to slot_id so the expert kernel's layout never changes, misses
+// copied from a pinned host pool on a separate stream, and a monotonically
+// increasing per-slot tag that the copy writes back; a copied expert is
+// committed into the table only when the written-back tag equals the tag the
+// commit expects, so a superseded copy never lands in the table.
+//
+// The HybriMoE summary page (Mechanism) defines misses as the routed set minus
+// the cached set and uses LRU as the baseline replacement; moe_plan_fills is
+// that baseline made precise (the pages give no hot-path victim rule).
+#include <string.h>
+
+#include <vector>
+
+#include "common.h"
+#include "ffn_internal.h"
+
+#ifndef MOE_VERSION_STRING
+#define MOE_VERSION_STRING "moe_offload 0.1 gfx950"
+#endif
+
+// ------------------------------------------------------------------ layout --
+int slot_layout(int H, int F, int w_dtype, SlotLayout* out) {
+  if (H <= 0 || F <= 0 || H % 16 != 0 || F % 16 != 0) return MOE_EINVAL;
+  SlotLayout l{};
+  if (w_dtype == MOE_F32 || w_dtype == MOE_BF16) {
+    const size_t es = (w_dtype == MOE_F32) ? 4 : 2;
+    l.off_w13 = 0;
+    l.off_w2 = align_up((size_t)2 * F * H * es, 256);
+    l.off_s13 = l.off_s2 = 0;
+    l.slot_bytes = align_up(l.off_w2 + (size_t)H * F * es, 4096);
+  } else if (w_dtype == MOE_INT4G128) {
+    if (H % 128 != 0 || F % 128 != 0) return MOE_EINVAL;
+    l.off_w13 = 0;
+    l.off_w2 = align_up((size_t)2 * F * (H / 2), 256);
+    l.off_s13 = align_up(l.off_w2 + (size_t)H * (F / 2), 256);
+    l.off_s2 = align_up(l.off_s13 + (size_t)2 * F * (H / 128) * 2, 256);
+    l.slot_bytes = align_up(l.off_s2 + (size_t)H * (F / 128) * 2, 4096);
+  } else {
+    return MOE_EINVAL;
+  }
+  *out = l;
+  return MOE_OK;
+}
+
+extern "C" int moe_slot_layout(int H, int F, int w_dtype, size_t* slot_bytes, size_t* off_w13,
+                               size_t* off_w2, size_t* off_s13, size_t* off_s2) {
+  SlotLayout l;
+  const int rc = slot_layout(H, F, w_dtype, &l);
+  if (rc != MOE_OK) return rc;
+  if (slot_bytes) *slot_bytes = l.slot_bytes;
+  if (off_w13) *off_w13 = l.off_w13;
+  if (off_w2) *off_w2 = l.off_w2;
+  if (off_s13) *off_s13 = l.off_s13;
+  if (off_s2) *off_s2 = l.off_s2;
+  return MOE_OK;
+}
+
+extern "C" int moe_pack_expert_host(const void* gate, const void* up, const void* down,
+                                    const void* gate_s, const void* up_s, const void* down_s,
+                                    int H, int F, int w_dtype, void* dst) {
+  SlotLayout l;
+  if (slot_layout(H, F, w_dtype, &l) != MOE_OK) return MOE_EINVAL;
+  MOE_CHECK_ARG(gate && up && down && dst);
+  char* d = static_cast<char*>(dst);
+  memset(d, 0, l.slot_bytes);
+  // bytes of one gate/up row (H inputs) and one down row (F inputs)
+  size_t rb13, rb2;
+  if (w_dtype == MOE_INT4G128) {
+    MOE_CHECK_ARG(gate_s && up_s && down_s);
+    rb13 = H / 2;
+    rb2 = F / 2;
+  } else {
+    const size_t es = (w_dtype == MOE_F32) ? 4 : 2;
+    rb13 = H * es;
+    rb2 = F * es;
+  }
+  const char* g = static_cast<const char*>(gate);
+  const char* u = static_cast<const char*>(up);
+  for (int n = 0; n < F; ++n) {
+    memcpy(d + l.off_w13 + (size_t)(2 * n) * rb13, g + (size_t)n * rb13, rb13);
+    memcpy(d + l.off_w13 + (size_t)(2 * n + 1) * rb13, u + (size_t)n * rb13, rb13);
+  }
+  memcpy(d + l.off_w2, down, (size_t)H * rb2);
+  if (w_dtype == MOE_INT4G128) {
+    const size_t sb13 = (size_t)(H / 128) * 2, sb2 = (size_t)(F / 128) * 2;
+    const char* gs = static_cast<const char*>(gate_s);
+    const char* us = static_cast<const char*>(up_s);
+    for (int n = 0; n < F; ++n) {
+      memcpy(d + l.off_s13 + (size_t)(2 * n) * sb13, gs + (size_t)n * sb13, sb13);
+      memcpy(d + l.off_s13 + (size_t)(2 * n + 1) * sb13, us + (size_t)n * sb13, sb13);
+    }
+    memcpy(d + l.off_s2, down_s, (size_t)H * sb2);
+  }
+  return MOE_OK;
+}
+
+// -------------------------------------------------------- tags and commits --
+namespace {
+
+__global__ void tag_writeback_kernel(uint64_t* tags, int slot, uint64_t tag) {
+  if (threadIdx.x == 0) tags[slot] = tag;
+}
+
+__global__ void slot_commit_kernel(int32_t* lut, int32_t idx, int32_t* owner, int32_t slot,
+                                   const uint64_t* tags, uint64_t tag, int32_t* err_word) {
+  if (threadIdx.x != 0) return;
+  if (tags[slot] != tag) {
+    atomicOr(err_word, MOE_ERR_STALE_TAG);
+    return;
+  }
+  const int32_t old = owner[slot];
+  if (old >= 0 && lut[old] == slot) lut[old] = -1;
+  lut[idx] = slot;
+  owner[slot] = idx;
+}
+
+}  // namespace
+
+extern "C" int slot_commit(int32_t* lut, int32_t lut_index, int32_t* owner, int32_t slot,
+                           const uint64_t* slot_tags, uint64_t tag, int32_t* err_word,
+                           hipStream_t stream) {
+  MOE_CHECK_ARG(lut && owner && slot_tags && err_word && slot >= 0 && lut_index >= 0);
+  hipLaunchKernelGGL(slot_commit_kernel, dim3(1), dim3(64), 0, stream, lut, lut_index, owner, slot,
+                     slot_tags, tag, err_word);
+  return moe_launch_status();
+}
+
+extern "C" int slot_fill(void* pool_base, size_t slot_stride, int32_t slot, const void* host_src,
+                         size_t bytes, int32_t* lut, int32_t lut_index, int32_t* owner,
+                         uint64_t* slot_tags, uint64_t tag, int32_t* err_word,
+                         hipStream_t fill_stream, hipStream_t compute_stream) {
+  MOE_CHECK_ARG(pool_base && host_src && lut && owner && slot_tags && err_word);
+  MOE_CHECK_ARG(slot >= 0 && lut_index >= 0 && bytes <= slot_stride);
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host_src) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_EINVAL;  // not memory the runtime knows: pageable host memory
+  }
+  if (attr.type != hipMemoryTypeHost) return MOE_EINVAL;
+
+  char* dst = static_cast<char*>(pool_base) + (size_t)slot * slot_stride;
+  hipError_t e = hipMemcpyAsync(dst, host_src, bytes, hipMemcpyHostToDevice, fill_stream);
+  if (e != hipSuccess) return moe_hip_status(e);
+  hipLaunchKernelGGL(tag_writeback_kernel, dim3(1), dim3(64), 0, fill_stream, slot_tags, slot, tag);
+  if (fill_stream != compute_stream) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return moe_hip_status(e);
+    e = hipEventRecord(ev, fill_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(compute_stream, ev, 0);
+    (void)hipEventDestroy(ev);
+    if (e != hipSuccess) return moe_hip_status(e);
+  }
+  hipLaunchKernelGGL(slot_commit_kernel, dim3(1), dim3(64), 0, compute_stream, lut, lut_index,
+                     owner, slot, slot_tags, tag, err_word);
+  return moe_launch_status();
+}
+
+// ------------------------------------------------------- host LRU planning --
+extern "C" int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock,
+                              int S, int L, int E, int layer, const int32_t* distinct,
+                              int n_distinct, int32_t* wave_of, int32_t* is_hit,
+                              int32_t* fill_expert, int32_t* fill_slot, int32_t* fill_wave,
+                              int32_t* n_fills, int32_t* n_waves) {
+  MOE_CHECK_ARG(lut && owner && last_use && clock && wave_of && is_hit && n_fills && n_waves);
+  MOE_CHECK_ARG(S >= 1 && L >= 1 && E >= 1 && layer >= 0 && layer < L);
+  MOE_CHECK_ARG(n_distinct >= 0 && n_distinct <= E);
+  MOE_CHECK_ARG(n_distinct == 0 || (distinct && fill_expert && fill_slot && fill_wave));
+  // The routed set must be strictly ascending ids in range.
+  for (int i = 0; i < n_distinct; ++i) {
+    if (distinct[i] < 0 || distinct[i] >= E) return MOE_EINVAL;
+    if (i > 0 && distinct[i] <= distinct[i - 1]) return MOE_EINVAL;
+  }
+  int32_t* row = lut + (size_t)layer * E;
+  for (int e = 0; e < E; ++e) {
+    wave_of[e] = -1;
+    is_hit[e] = 0;
+  }
+  std::vector<int> hits, misses;
+  std::vector<char> kept(S, 0);
+  for (int i = 0; i < n_distinct; ++i) {
+    const int e = distinct[i];
+    if (row[e] >= 0) {
+      hits.push_back(e);
+      kept[row[e]] = 1;
+      is_hit[e] = 1;
+    } else {
+      misses.push_back(e);
+    }
+  }
+  // Victims: empty slots by id, then the other slots by (last use, id).
+  std::vector<int> victims, used;
+  for (int s = 0; s < S; ++s)
+    if (owner[s] < 0) victims.push_back(s);
+  std::vector<int> reuse;
+  for (int s = 0; s < S; ++s)
+    if (owner[s] >= 0 && !kept[s]) reuse.push_back(s);
+  // insertion sort by (last_use, slot): small S per call, no allocation churn
+  for (size_t i = 1; i < reuse.size(); ++i) {
+    const int s = reuse[i];
+    size_t j = i;
+    while (j > 0 && (last_use[reuse[j - 1]] > last_use[s] ||
+                     (last_use[reuse[j - 1]] == last_use[s] && reuse[j - 1] > s))) {
+      reuse[j] = reuse[j - 1];
+      --j;
+    }
+    reuse[j] = s;
+  }
+  victims.insert(victims.end(), reuse.begin(), reuse.end());
+
+  *clock += 1;
+  int nf = 0, nw = 1;
+  auto assign = [&](int e, int s, int wave) {
+    const int32_t old = owner[s];
+    if (old >= 0) lut[old] = -1;
+    row[e] = s;
+    owner[s] = layer * E + e;
+    fill_expert[nf] = e;
+    fill_slot[nf] = s;
+    fill_wave[nf] = wave;
+    ++nf;
+    wave_of[e] = wave;
+    used.push_back(s);
+  };
+  for (int e : hits) {
+    wave_of[e] = 0;
+    used.push_back(row[e]);
+  }
+  if (misses.size() <= victims.size()) {
+    for (size_t i = 0; i < misses.size(); ++i) assign(misses[i], victims[i], 0);
+  } else {
+    const size_t first = victims.size();
+    for (size_t i = 0; i < first; ++i) assign(misses[i], victims[i], 0);
+    int wave = 1;
+    for (size_t i = first; i < misses.size(); i += S, ++wave) {
+      for (size_t j = i; j < misses.size() && j < i + S; ++j) assign(misses[j], (int)(j - i), wave);
+      nw = wave + 1;
+    }
+  }
+  for (int s : used) last_use[s] = *clock;
+  *n_fills = nf;
+  *n_waves = (n_distinct == 0) ? 0 : nw;
+  return MOE_OK;
+}
+
+extern "C" const char* moe_version(void) { return MOE_VERSION_STRING; }

@@ -1,0 +1,247 @@
+/*
+ * moe_offload.h - C ABI of the routed-expert MoE layer over a device-resident
+ * expert slot cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the source pages define it:
+ *   - gating: a linear projection of the token, softmax, and the top-k experts
+ *     by logit ("RapidMoE: Exploiting Cross-Asymmetry via Adaptive Residual
+ *     Offloading for Large-Scale MoE Inference", Sec. 2.1);
+ *   - output: the sum over the selected experts of the normalised routing
+ *     weight times the expert's output ("Communication-Aware Placement and
+ *     Pruning for Efficient Mixture-of-Experts Inference", Sec. II-A, Eq. (1);
+ *     RapidMoE Algorithm 1);
+ *   - expert: a SwiGLU FFN, down(SiLU(gate x) * up x) (RapidMoE Eq. (7));
+ *   - residency: one pool of expert slots at a fixed base address, shared by
+ *     every MoE layer, and a table that rewrites expert_id to slot_id so the
+ *     expert kernel always sees the same layout; misses are copied from a
+ *     pinned host pool, and a per-slot monotonically increasing tag decides
+ *     whether a copied expert may be committed (SeqMoE summary page,
+ *     Mechanism); only routed experts are cached, shared experts stay
+ *     resident (SeqMoE and HybriMoE summary pages, Mechanism).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless the comment says "host".
+ *   - The caller owns all memory passed in; the library keeps no pointer after
+ *     the call returns (except that enqueued work reads/writes them later).
+ *   - Calls only enqueue work on the given stream(s) and return; they never
+ *     synchronise the device, except the host-only helpers.
+ *   - Return value: MOE_OK (0), MOE_EINVAL (-1) invalid argument (nothing was
+ *     enqueued), MOE_EUNSUPPORTED (-2) dtype/shape this build does not
+ *     support, MOE_EHIP (-3) a HIP runtime error (the HIP error is consumed).
+ *   - Faults found on the device are OR-ed into a caller-owned int32 error
+ *     word (MOE_ERR_* bits); kernels never trap.
+ *   - No mutable global state: calls on different streams may run
+ *     concurrently as long as their buffers do not overlap.
+ *   - Row-major layouts; T tokens, H hidden size, F expert FFN size, E routed
+ *     experts per layer, k experts per token, S pool slots, L layers.
+ */
+#ifndef MOE_OFFLOAD_H
+#define MOE_OFFLOAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element formats */
+enum {
+  MOE_F32 = 0,      /* IEEE binary32 */
+  MOE_BF16 = 1,     /* bfloat16 (upper half of binary32, round-to-nearest-even) */
+  MOE_INT4G128 = 2  /* expert weights only: signed 4-bit codes, one bf16 scale per
+                       128 consecutive input values of an output row; with these
+                       weights the activations are quantised per row to int8 */
+};
+
+/* status codes */
+enum { MOE_OK = 0, MOE_EINVAL = -1, MOE_EUNSUPPORTED = -2, MOE_EHIP = -3 };
+
+/* device error-word bits */
+#define MOE_ERR_ABSENT 1    /* a routed expert had no slot (table entry -1); its rows were skipped */
+#define MOE_ERR_STALE_TAG 2 /* a commit found another tag in the slot; table left unchanged */
+
+/* ------------------------------------------------------------------ gating -
+ * moe_route: router logits, top-k selection and routing weights.
+ *   logits[t,e] = sum_h x[t,h] * w_router[e,h] + bias[e]        (fp32 accumulate)
+ *   topk_ids[t,:] = the k experts with the largest logits, ordered by
+ *                   (logit descending, expert id ascending)
+ *   topk_w[t,j]   = softmax(logits[t,:])[ids[t,j]], divided by the sum over
+ *                   the k selected when renorm != 0
+ * (RapidMoE Sec. 2.1; CAP Eq. (1).) Selection is on the logits; the bias is
+ * part of the logit.
+ *   x         [T,H] in x_dtype (MOE_F32 or MOE_BF16)
+ *   w_router  [E,H] in x_dtype; row e is expert e's projection vector
+ *   bias      [E] fp32, may be NULL (no bias)
+ *   logits    [T,E] fp32 out (required: it is the hand-off between the
+ *             projection and the selection kernels)
+ *   topk_ids  [T,k] int32 out; topk_w [T,k] fp32 out
+ * Requires 1 <= k <= E <= 1024, H % 8 == 0, T >= 0 (T == 0 is a no-op).
+ */
+int moe_route(const void* x, int x_dtype, const void* w_router, const float* bias,
+              int T, int H, int E, int k, int renorm,
+              float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* ------------------------------------------------------------- permutation -
+ * moe_permute: counting sort of the T*k assignments by expert, stable in token
+ * order, so each expert's rows form one contiguous block (the grouped layout
+ * the expert kernel reads; SeqMoE Mechanism: the expert kernel sees a fixed,
+ * contiguous layout).
+ *   topk_ids   [T,k] int32, each row k distinct ids in [0,E)
+ *   counts     [E] int32 out: assignments per expert
+ *   offsets    [E+1] int32 out: exclusive prefix sum of counts
+ *   perm       [T*k] int32 out: sorted position -> flat assignment t*k+j
+ *   inv        [T*k] int32 out: flat assignment -> sorted position
+ *   distinct   [E] int32 out: experts with count > 0, ascending (first n_distinct valid)
+ *   n_distinct [1] int32 out
+ * Requires 1 <= k <= E <= 1024, T*k < 2^31. Ids outside [0,E) are not
+ * counted and leave their perm/inv entries unwritten.
+ */
+int moe_permute(const int32_t* topk_ids, int T, int k, int E,
+                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                int32_t* distinct, int32_t* n_distinct, hipStream_t stream);
+
+/* ------------------------------------------------------------- slot layout -
+ * The byte layout of one expert inside a slot (and inside the pinned host
+ * store, which holds the same bytes so a fill is one contiguous copy). The
+ * slot pool is one allocation: slot s starts at pool_base + s * slot_stride
+ * (the fixed-base [num_slots, dim0, dim1] pool of the SeqMoE page).
+ *   w13 at off_w13: 2F rows of H values, row 2n = gate row n, row 2n+1 = up
+ *                   row n (fp32/bf16 values, or int4 codes packed two per
+ *                   byte along H, even index in the low nibble)
+ *   w2  at off_w2:  H rows of F values (down projection, same packing)
+ *   int4 only: s13 at off_s13: [2F, H/128] bf16 scales (rows as w13);
+ *              s2 at off_s2: [H, F/128] bf16 scales.
+ * Every section starts on a 256-byte boundary; slot_bytes is a multiple of 4096.
+ * Returns MOE_EINVAL for a bad format or sizes (H, F multiples of 16; of 128
+ * for int4).
+ */
+int moe_slot_layout(int H, int F, int w_dtype, size_t* slot_bytes,
+                    size_t* off_w13, size_t* off_w2, size_t* off_s13, size_t* off_s2);
+
+/* moe_pack_expert_host (host only, not on the hot path): write one expert in
+ * the slot layout into dst (host, slot_bytes). Inputs are host arrays in
+ * nn.Linear orientation: gate, up [F,H], down [H,F] as fp32/bf16 values, or
+ * for int4 packed codes gate, up [F,H/2], down [H,F/2] bytes plus bf16 scales
+ * gate_s, up_s [F,H/128], down_s [H,F/128] (NULL for dense formats). */
+int moe_pack_expert_host(const void* gate, const void* up, const void* down,
+                         const void* gate_s, const void* up_s, const void* down_s,
+                         int H, int F, int w_dtype, void* dst);
+
+/* --------------------------------------------------------------- expert FFN -
+ * moe_ffn_workspace_bytes: device workspace moe_expert_ffn needs for these
+ * sizes (work list, SwiGLU intermediate, int8 activations).
+ */
+size_t moe_ffn_workspace_bytes(int T, int H, int F, int E, int k, int w_dtype);
+
+/* moe_expert_ffn: grouped SwiGLU FFN of every routed expert group, reading the
+ * expert's weights through the slot table (SeqMoE Mechanism; RapidMoE Eq. (7)):
+ *   for each expert e with offsets[e] < offsets[e+1] and group_mask[e] != 0:
+ *     slot = lut[e]; W = pool_base + slot * slot_stride (moe_slot_layout)
+ *     for each sorted position p in [offsets[e], offsets[e+1]):
+ *       x_p = x[perm[p] / k]
+ *       y_perm[p] = down(SiLU(gate x_p) * up x_p)            (fp32)
+ *   x         [T,H] tokens in x_dtype (MOE_F32 or MOE_BF16)
+ *   perm, offsets from moe_permute
+ *   lut       [E] int32: this layer's row of the expert->slot table (-1 = absent)
+ *   group_mask [E] int32 or NULL (NULL = every routed expert); lets a caller
+ *             run resident experts while misses are still being copied
+ *   pool_base, slot_stride, num_slots: the slot pool; w_dtype the weight format
+ *   y_perm    [T*k,H] fp32 out: rows of skipped groups are left untouched
+ *   err_word  [1] int32: MOE_ERR_ABSENT is OR-ed in when a selected group's
+ *             lut entry is -1 or not below num_slots (that group is skipped)
+ *   workspace device buffer of ws_bytes >= moe_ffn_workspace_bytes(...)
+ * With MOE_INT4G128 the tokens and the SwiGLU intermediate are quantised per
+ * row to int8 (scale = max|row| / 127, IEEE fp32 division, round to nearest
+ * even) before the int4 x int8 products (int32 accumulation per 128 values,
+ * scaled by the group scales in fp32).
+ */
+int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* offsets,
+                   const int32_t* lut, const int32_t* group_mask,
+                   const void* pool_base, size_t slot_stride, int num_slots, int w_dtype,
+                   int T, int H, int F, int E, int k,
+                   float* y_perm, int32_t* err_word, void* workspace, size_t ws_bytes,
+                   hipStream_t stream);
+
+/* ------------------------------------------------------------------ combine -
+ * moe_combine: weighted sum of the routed experts' outputs (RapidMoE Sec. 2.1,
+ * Algorithm 1; CAP Eq. (1)) plus the always-on shared experts (weight 1):
+ *   out[t,:] = sum_{j<k, topk_w[t,j] != 0} topk_w[t,j] * y_perm[inv[t*k+j],:]
+ *            + sum_{s<n_shared} shared_y[s,t,:]
+ * accumulated in fp32 in this fixed order (deterministic; a zero weight
+ * skips its term, so a NaN in an unused row cannot reach the output).
+ *   shared_y  [n_shared,T,H] fp32 or NULL (n_shared ignored when NULL)
+ *   out       [T,H] in out_dtype (MOE_F32, or MOE_BF16 rounded to nearest even)
+ */
+int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w,
+                int T, int k, int H, const float* shared_y, int n_shared,
+                void* out, int out_dtype, hipStream_t stream);
+
+/* ---------------------------------------------------------------- slot fill -
+ * slot_fill: copy one expert from the pinned host store into a slot and
+ * commit it into the table (SeqMoE Mechanism: pinned host pool, copy on a
+ * separate stream, commit only when the slot's tag matches):
+ *   fill_stream:    copy bytes host_src -> pool_base + slot*slot_stride;
+ *                   then slot_tags[slot] = tag (the tag written back by this copy)
+ *   compute_stream: waits for the copy, then commits:
+ *                   if slot_tags[slot] == tag:
+ *                      old = owner[slot]; if old >= 0 and lut[old] == slot: lut[old] = -1
+ *                      lut[lut_index] = slot; owner[slot] = lut_index
+ *                   else: table unchanged, MOE_ERR_STALE_TAG OR-ed into err_word
+ *   host_src   host pointer into page-locked memory (hipHostMalloc or torch
+ *              pin_memory); pageable memory is rejected with MOE_EINVAL
+ *   lut        the whole table [L*E] int32; lut_index = layer*E + expert
+ *   owner      [S] int32: lut index held by each slot, -1 = empty
+ *   slot_tags  [S] uint64 (device)
+ * The copy is ordered after earlier work on fill_stream only: the caller must
+ * make fill_stream wait for any kernel that may still read this slot.
+ * fill_stream may equal compute_stream.
+ */
+int slot_fill(void* pool_base, size_t slot_stride, int32_t slot,
+              const void* host_src, size_t bytes,
+              int32_t* lut, int32_t lut_index, int32_t* owner,
+              uint64_t* slot_tags, uint64_t tag, int32_t* err_word,
+              hipStream_t fill_stream, hipStream_t compute_stream);
+
+/* slot_commit: the commit step of slot_fill alone, on one stream, for a copy
+ * whose tag was written back by other means (e.g. a prefetcher). Same rule
+ * and same error bit as above. */
+int slot_commit(int32_t* lut, int32_t lut_index, int32_t* owner, int32_t slot,
+                const uint64_t* slot_tags, uint64_t tag, int32_t* err_word,
+                hipStream_t stream);
+
+/* ------------------------------------------------------- residency (host) -
+ * moe_plan_fills (host only): least-recently-used residency plan for one
+ * layer call. The pages name misses as the routed set minus the cached set
+ * and LRU as the baseline replacement (HybriMoE summary page, Mechanism) but
+ * give no hot-path victim rule; this is the plain one:
+ *   U = distinct[0..n_distinct) (ascending), hits = U with lut[layer*E+e] >= 0,
+ *   misses = the rest (ascending). Victims: empty slots (ascending id), then
+ *   slots not holding a hit, by (last_use, slot id) ascending.
+ *   |misses| <= |victims|: one wave, misses[i] -> victims[i].
+ *   else: wave 0 = hits + the first S-|hits| misses (into the victims); each
+ *   later wave takes up to S more misses into slots 0,1,2,...
+ *   clock[0] += 1 once per call; every slot used gets last_use = clock.
+ * State (host arrays, updated in place to the state after the last wave):
+ *   lut [L*E] int32, owner [S] int32 (lut index or -1), last_use [S] int64,
+ *   clock [1] int64.
+ * Outputs (host): wave_of [E] int32 = wave in which expert e is computed, -1
+ *   if not routed; is_hit [E] int32 = 1 for hits; fill_expert, fill_slot,
+ *   fill_wave [n_distinct] int32 and n_fills; n_waves.
+ * Returns MOE_EINVAL for bad sizes or ids (state untouched).
+ */
+int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock,
+                   int S, int L, int E, int layer,
+                   const int32_t* distinct, int n_distinct,
+                   int32_t* wave_of, int32_t* is_hit,
+                   int32_t* fill_expert, int32_t* fill_slot, int32_t* fill_wave,
+                   int32_t* n_fills, int32_t* n_waves);
+
+/* Library version string and the gfx target it was built for (host). */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_OFFLOAD_H */

@@ -1,0 +1,126 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and its host-only logic (slot layout, packing, LRU plan) behaves as defined.
+
+No kernel is launched here. The LRU plan is compared with the oracle's
+planner on random traces (bit-exact tables, fills and waves).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from expert_offload_routed_amd import binding as B
+from expert_offload_routed_amd import workloads as W
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe_offload.so is not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = B.header_functions()
+    assert {"moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "slot_fill"} <= set(names)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version(lib):
+    assert "gfx950" in B.moe_version()
+
+
+@pytest.mark.parametrize("H,F,fmt,expect", [
+    (256, 512, B.MOE_F32, (3 * 256 * 512 * 4)),
+    (4096, 14336, B.MOE_BF16, 352_321_536),
+    (2048, 768, B.MOE_BF16, 3 * 2048 * 768 * 2),
+    (7168, 2048, B.MOE_INT4G128, 3 * 7168 * 2048 // 2 + 3 * 7168 * 2048 // 128 * 2),
+])
+def test_slot_layout_sizes(lib, H, F, fmt, expect):
+    lay = B.moe_slot_layout(H, F, fmt)
+    assert lay["slot_bytes"] % 4096 == 0
+    assert expect <= lay["slot_bytes"] < expect + 4096 + 3 * 256
+    for key in ("off_w13", "off_w2", "off_s13", "off_s2"):
+        assert lay[key] % 256 == 0
+
+
+def test_slot_layout_rejects_bad_sizes(lib):
+    with pytest.raises(B.MoeError):
+        B.moe_slot_layout(100, 512, B.MOE_BF16)
+    with pytest.raises(B.MoeError):
+        B.moe_slot_layout(7168 + 16, 2048, B.MOE_INT4G128)
+    with pytest.raises(B.MoeError):
+        B.moe_slot_layout(256, 256, 7)
+
+
+def test_pack_dense_interleaves_gate_and_up(lib):
+    sh = W.reduced(W.shape_of("mixtral_e8k2_h4096_f14336_bf16"), H=64, F=32)
+    w = W.expert_weights(sh, 3)
+    lay = B.moe_slot_layout(64, 32, B.MOE_BF16)
+    dst = torch.zeros(lay["slot_bytes"], dtype=torch.uint8)
+    B.moe_pack_expert_host(dict(w), 64, 32, B.MOE_BF16, dst)
+    w13 = dst[lay["off_w13"]:lay["off_w13"] + 2 * 32 * 64 * 2].view(torch.bfloat16).view(64, 64)
+    assert torch.equal(w13[0::2], w["gate"]) and torch.equal(w13[1::2], w["up"])
+    w2 = dst[lay["off_w2"]:lay["off_w2"] + 64 * 32 * 2].view(torch.bfloat16).view(64, 32)
+    assert torch.equal(w2, w["down"])
+
+
+def test_pack_int4_keeps_codes_and_scales(lib):
+    sh = W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), H=256, F=128)
+    w = W.expert_weights(sh, 1)
+    lay = B.moe_slot_layout(256, 128, B.MOE_INT4G128)
+    dst = torch.zeros(lay["slot_bytes"], dtype=torch.uint8)
+    B.moe_pack_expert_host(dict(w), 256, 128, B.MOE_INT4G128, dst)
+    w13 = dst[lay["off_w13"]:lay["off_w13"] + 256 * 128].view(256, 128)
+    assert torch.equal(w13[0::2], w["gate_q"]) and torch.equal(w13[1::2], w["up_q"])
+    s13 = dst[lay["off_s13"]:lay["off_s13"] + 256 * 2 * 2].view(torch.bfloat16).view(256, 2)
+    assert torch.equal(s13[0::2], w["gate_s"]) and torch.equal(s13[1::2], w["up_s"])
+    s2 = dst[lay["off_s2"]:lay["off_s2"] + 256 * 1 * 2].view(torch.bfloat16).view(256, 1)
+    assert torch.equal(s2, w["down_s"])
+
+
+def _lib_state(S, L, E, residency):
+    lut = np.full(L * E, -1, np.int32)
+    owner = np.full(S, -1, np.int32)
+    for s, o in enumerate(residency):
+        if o is not None:
+            lut[o[0] * E + o[1]] = s
+            owner[s] = o[0] * E + o[1]
+    return lut, owner, np.zeros(S, np.int64), np.zeros(1, np.int64)
+
+
+@pytest.mark.parametrize("S,L,E,kmax,seed", [(4, 1, 8, 2, 0), (3, 2, 6, 4, 1), (16, 1, 64, 6, 2),
+                                             (7, 3, 10, 3, 3), (1, 1, 5, 2, 4)])
+def test_plan_fills_matches_oracle_planner(lib, S, L, E, kmax, seed):
+    rng = np.random.default_rng(seed)
+    init = [(int(rng.integers(L)), int(e)) for e in rng.choice(E, size=min(S, E) - 1, replace=False)]
+    init = list(dict.fromkeys(init)) + [None]
+    residency = (init + [None] * S)[:S]
+    ref = O.LruSlotPlanner(S, L, E, residency)
+    lut, owner, last_use, clock = _lib_state(S, L, E, residency)
+    for step in range(200):
+        layer = int(rng.integers(L))
+        U = sorted({int(e) for e in rng.choice(E, size=int(rng.integers(1, kmax * 3 + 1)))})
+        waves = ref.plan(layer, U)
+        got = B.moe_plan_fills(lut, owner, last_use, clock, S, L, E, layer, np.array(U))
+        assert got["n_waves"] == len(waves)
+        exp_fills = [(e, s, wi) for wi, wv in enumerate(waves) for e, s in wv.fills]
+        assert list(zip(got["fill_expert"], got["fill_slot"], got["fill_wave"])) == exp_fills
+        exp_wave = np.full(E, -1)
+        for wi, wv in enumerate(waves):
+            exp_wave[wv.compute] = wi
+        assert got["wave_of"].tolist() == exp_wave.tolist()
+        assert lut.reshape(L, E).tolist() == ref.lut.tolist()
+        assert owner.tolist() == [-1 if o is None else o[0] * E + o[1] for o in ref.owner]
+        assert last_use.tolist() == ref.last_use and int(clock[0]) == ref.clock
+
+
+def test_plan_fills_rejects_unsorted_or_out_of_range(lib):
+    lut, owner, last_use, clock = _lib_state(2, 1, 4, [None, None])
+    for bad in ([2, 1], [0, 4], [-1], [1, 1]):
+        with pytest.raises(B.MoeError):
+            B.moe_plan_fills(lut, owner, last_use, clock, 2, 1, 4, 0, np.array(bad))
+    assert lut.tolist() == [-1] * 4 and int(clock[0]) == 0
