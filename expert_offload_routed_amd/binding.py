@@ -128,6 +128,10 @@ def moe_route(x, w_router, bias, k: int, renorm: bool = True, logits=None, topk_
     logits = torch.empty(T, E, device=dev, dtype=torch.float32) if logits is None else logits
     topk_ids = torch.empty(T, k, device=dev, dtype=torch.int32) if topk_ids is None else topk_ids
     topk_w = torch.empty(T, k, device=dev, dtype=torch.float32) if topk_w is None else topk_w
+    if tuple(w_router.shape) != (E, H) or (bias is not None and bias.numel() != E):
+        raise ValueError("moe_route: w_router must be [E, H] and bias [E]")
+    if logits.numel() < T * E or topk_ids.numel() < T * k or topk_w.numel() < T * k:
+        raise ValueError("moe_route: output buffers too small")
     if w_router.dtype != x.dtype:
         raise TypeError("x and w_router must share a dtype")
     _call("moe_route", _dev(x), dtype_code(x), _dev(w_router), _dev(bias), T, H, E, k, int(renorm),
@@ -145,6 +149,10 @@ def moe_permute(topk_ids, E: int, out: dict | None = None, stream=None) -> dict:
     o.setdefault("inv", torch.empty(max(T * k, 1), device=dev, dtype=torch.int32))
     o.setdefault("distinct", torch.empty(E, device=dev, dtype=torch.int32))
     o.setdefault("n_distinct", torch.empty(1, device=dev, dtype=torch.int32))
+    need = {"counts": E, "offsets": E + 1, "perm": T * k, "inv": T * k, "distinct": E, "n_distinct": 1}
+    for name, n in need.items():
+        if o[name].numel() < n or o[name].dtype != torch.int32:
+            raise ValueError(f"moe_permute: output '{name}' needs {n} int32 elements")
     _call("moe_permute", _dev(topk_ids), T, k, E, _dev(o["counts"]), _dev(o["offsets"]),
           _dev(o["perm"]), _dev(o["inv"]), _dev(o["distinct"]), _dev(o["n_distinct"]),
           _stream(stream))
@@ -182,6 +190,9 @@ def moe_ffn_workspace_bytes(T, H, F, E, k, w_dtype) -> int:
 def moe_expert_ffn(x, perm, offsets, lut_row, group_mask, pool, slot_stride: int, w_dtype: int,
                    T: int, H: int, F: int, E: int, k: int, y_perm, err_word, workspace, stream=None):
     num_slots = pool.numel() // slot_stride
+    if (x.numel() < T * H or perm.numel() < T * k or offsets.numel() < E + 1 or lut_row.numel() < E
+            or y_perm.numel() < T * k * H or (group_mask is not None and group_mask.numel() < E)):
+        raise ValueError("moe_expert_ffn: an argument is smaller than its shape needs")
     _call("moe_expert_ffn", _dev(x), dtype_code(x), _dev(perm), _dev(offsets), _dev(lut_row),
           _dev(group_mask), _dev(pool), slot_stride, num_slots, w_dtype, T, H, F, E, k, _dev(y_perm),
           _dev(err_word), _dev(workspace), workspace.numel() * workspace.element_size(),
@@ -194,6 +205,9 @@ def moe_combine(y_perm, inv, topk_w, T: int, k: int, H: int, shared_y=None, out=
     if out is None:
         out = torch.empty(T, H, device=topk_w.device, dtype=out_dtype)
     n_sh = 0 if shared_y is None else shared_y.shape[0]
+    if (inv.numel() < T * k or topk_w.numel() < T * k or out.numel() < T * H
+            or (shared_y is not None and shared_y.numel() < n_sh * T * H)):
+        raise ValueError("moe_combine: an argument is smaller than its shape needs")
     _call("moe_combine", _dev(y_perm), _dev(inv), _dev(topk_w), T, k, H, _dev(shared_y), n_sh,
           _dev(out), dtype_code(out), _stream(stream))
     return out

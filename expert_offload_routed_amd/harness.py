@@ -91,6 +91,9 @@ class SlotCacheLayer:
         self.masks_h = torch.zeros(64, self.E, dtype=torch.int32, pin_memory=True)
         self.dist_h = torch.zeros(self.E + 1, dtype=torch.int32, pin_memory=True)
         self.dist_d = torch.zeros(self.E + 1, dtype=torch.int32, device=dev)
+        self.perm = {n: torch.zeros(c, dtype=torch.int32, device=dev) for n, c in (
+            ("counts", self.E), ("offsets", self.E + 1), ("perm", max(tk, 1)), ("inv", max(tk, 1)),
+            ("distinct", self.E), ("n_distinct", 1))}
         # shared experts: resident pool of their own, identity table
         self.n_sh = sh.n_shared
         if self.n_sh:
@@ -147,7 +150,7 @@ class SlotCacheLayer:
         cs = torch.cuda.current_stream()
         wr, bias = self.routers[layer]
         B.moe_route(x, wr, bias, k, True, self.logits[:T], self.ids[:T], self.topw[:T])
-        self.perm = B.moe_permute(self.ids[:T], E, out=getattr(self, "perm", None))
+        B.moe_permute(self.ids[:T], E, out=self.perm)
         # the distinct routed set goes to the host for the residency plan
         self.dist_d[:E].copy_(self.perm["distinct"])
         self.dist_d[E:].copy_(self.perm["n_distinct"])
