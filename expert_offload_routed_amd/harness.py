@@ -143,7 +143,10 @@ class SlotCacheLayer:
 
     # ----------------------------------------------------------------- step
     def forward(self, x: torch.Tensor, layer: int = 0, out: torch.Tensor | None = None,
-                stats: StepStats | None = None) -> torch.Tensor:
+                stats: StepStats | None = None, ffn_events: list | None = None) -> torch.Tensor:
+        """One layer step. ``ffn_events`` (optional list) receives a (start, end)
+        pair of events recorded on the compute stream around every routed
+        moe_expert_ffn call, with the number of expert groups it ran."""
         T = x.shape[0]
         assert T <= self.t_max
         E, k, H, F = self.E, self.k, self.H, self.F
@@ -175,19 +178,27 @@ class SlotCacheLayer:
         ev = torch.cuda.Event()
         ev.record(cs)
         self.fill_stream.wait_event(ev)
-        ffn = lambda mask: B.moe_expert_ffn(x, self.perm["perm"], self.perm["offsets"], lut_row, mask,
-                                            self.pool, self.stride, self.wcode, T, H, F, E, k,
-                                            self.y_perm, self.err, self.ws)
-        ffn(self.masks[0])
+        def ffn(mask, groups):
+            if ffn_events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(cs)
+            B.moe_expert_ffn(x, self.perm["perm"], self.perm["offsets"], lut_row, mask, self.pool,
+                             self.stride, self.wcode, T, H, F, E, k, self.y_perm, self.err, self.ws)
+            if ffn_events is not None:
+                e1.record(cs)
+                ffn_events.append((e0, e1, groups))
+
+        ffn(self.masks[0], int(is_hit.sum()))
         fe, fs, fw = plan["fill_expert"], plan["fill_slot"], plan["fill_wave"]
         for w in range(nw):
             if w > 0:  # the next wave overwrites slots the previous waves read
                 ev = torch.cuda.Event()
                 ev.record(cs)
                 self.fill_stream.wait_event(ev)
-            for i in np.flatnonzero(fw == w):
+            sel = np.flatnonzero(fw == w)
+            for i in sel:
                 self._fill(int(fs[i]), layer, int(fe[i]), self.fill_stream, cs)
-            ffn(self.masks[1 + w])
+            ffn(self.masks[1 + w], len(sel))
         shared_y = None
         if self.n_sh:
             sp, so = self.shared_perm(T)
