@@ -46,31 +46,30 @@ def expert_bytes(shape) -> int:
     return 3 * shape.H * shape.F * es
 
 
-def run_steps(layer, xs, ffn_events=None, stats=None):
-    for x in xs:
-        layer.forward(x, ffn_events=ffn_events, stats=stats)
-
-
 def timed(layer, shape, T, steps, warmup, label, ffn_timing=False):
+    """Warm up, then time exactly ``steps`` layer steps between two device synchronisations."""
     xs = [W.tokens(shape, T, step=i, device="cuda") for i in range(steps + warmup)]
-    run_steps(layer, xs[:warmup])
+    out = torch.empty(T, shape.H, dtype=layer.out_dtype, device="cuda")
+    for x in xs[:warmup]:
+        layer.forward(x, out=out)
     torch.cuda.synchronize()
-    ev = [] if ffn_timing else None
+    layer.ctx.set_timing(ffn_timing)
     st = Hn.StepStats()
     t0 = time.perf_counter()
-    run_steps(layer, xs[warmup:], ffn_events=ev, stats=st)
+    for x in xs[warmup:]:
+        layer.forward(x, out=out, stats=st)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     res = {"tokens_per_step": T, "tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3,
            "distinct_per_step": st.distinct / steps, "fills_per_step": st.fills / steps}
-    if ev is not None:
-        ms = [a.elapsed_time(b) for a, b, g in ev if g > 0]
-        groups = [g for a, b, g in ev if g > 0]
-        eb = expert_bytes(shape)
-        byts = [g * eb + T * shape.H * 2 + T * shape.k * shape.H * 4 for g in groups]
-        gbs = sum(byts) / (sum(ms) * 1e-3) / 1e9
-        res["ffn"] = {"calls": len(ms), "avg_us": 1e3 * sum(ms) / len(ms),
-                      "avg_bytes": sum(byts) / len(byts), "gbs": gbs}
+    if ffn_timing:
+        ms, n = layer.ctx.ffn_time()
+        layer.ctx.set_timing(False)
+        # algorithmic bytes of the expert FFN per step: the routed experts' weights
+        # (every distinct expert is read once), tokens in, one fp32 row out per assignment
+        byts = (st.distinct / steps) * expert_bytes(shape) + T * shape.H * 2 + T * shape.k * shape.H * 4
+        res["ffn"] = {"calls": n, "avg_us": 1e3 * ms / n, "avg_bytes": byts,
+                      "gbs": byts / (ms / n * 1e-3) / 1e9}
     print(f"# {label}: {res}", file=sys.stderr, flush=True)
     return res
 
@@ -153,7 +152,7 @@ def main():
         "config": {"workload": "Mixtral-8x7B-shaped MoE layer, bf16, E=8 top-2, H=4096, F=14336, "
                                "decode 1 token/step, all experts resident (hit path)",
                    "tokens_per_step": 1, "slots": shape.E, "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "moe_expert_ffn (plan + W13 GEMV + W2 GEMV launches)", "bound": "hbm",
+        "roofline": {"kernel": "moe_expert_ffn (plan + W13 GEMV + W2 GEMV launches, one call per step)", "bound": "hbm",
                      "achieved": round(ffn["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ffn["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_us": round(ffn["avg_us"], 2), "bytes_per_call": int(ffn["avg_bytes"])},

@@ -37,6 +37,16 @@ _SIGNATURES = {
     "moe_plan_fills": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp]),
     "moe_version": (ctypes.c_char_p, []),
+    "moe_ctx_workspace_bytes": (_sz, [_i32] * 7),
+    "moe_ctx_create": (_i32, [ctypes.POINTER(_vp)] + [_i32] * 10 + [_vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                                   _vp, _vp, _sz, _vp, _vp]),
+    "moe_ctx_destroy": (_i32, [_vp]),
+    "moe_ctx_place": (_i32, [_vp, _i32, _i32, _i32]),
+    "moe_layer_forward": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp]),
+    "moe_ctx_read_tables": (_i32, [_vp, _vp, _vp, _vp, _vp]),
+    "moe_ctx_outputs": (_i32, [_vp] + [ctypes.POINTER(_vp)] * 6),
+    "moe_ctx_set_timing": (_i32, [_vp, _i32]),
+    "moe_ctx_ffn_time": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_long)]),
 }
 
 
@@ -248,3 +258,91 @@ def moe_plan_fills(lut: np.ndarray, owner: np.ndarray, last_use: np.ndarray, clo
 
 def moe_version() -> str:
     return lib().moe_version().decode()
+
+
+# ------------------------------------------------------------ layer runtime --
+def moe_ctx_workspace_bytes(t_max, H, F, E, k, w_dtype, n_shared) -> int:
+    return int(lib().moe_ctx_workspace_bytes(t_max, H, F, E, k, w_dtype, n_shared))
+
+
+class LayerContext:
+    """Handle of a moe_layer_ctx (include/moe_runtime.h); keeps its buffers alive."""
+
+    def __init__(self, *, t_max, H, F, E, k, L, S, x_dtype, w_dtype, n_shared, pool, slot_stride, lut,
+                 owner, tags, host_store, blob_of: np.ndarray, shared_pool, err, compute_stream=None,
+                 fill_stream=None):
+        dev = pool.device
+        self.t_max, self.H, self.E, self.k, self.L, self.S = t_max, H, E, k, L, S
+        self.compute_stream = compute_stream or torch.cuda.current_stream(dev)
+        self.fill_stream = fill_stream or torch.cuda.Stream(device=dev)
+        nbytes = moe_ctx_workspace_bytes(t_max, H, F, E, k, w_dtype, n_shared)
+        if nbytes == 0:
+            raise ValueError("moe_ctx_workspace_bytes: bad sizes")
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.blob_of = np.ascontiguousarray(blob_of, dtype=np.int32)
+        if self.blob_of.size != L * E:
+            raise ValueError("blob_of must hold L*E entries")
+        if tags.dtype != torch.int64 or tags.numel() < S or owner.numel() < S or lut.numel() < L * E:
+            raise ValueError("tables too small")
+        self._keep = (pool, lut, owner, tags, host_store, shared_pool, err)
+        self.handle = _vp()
+        _call("moe_ctx_create", ctypes.byref(self.handle), t_max, H, F, E, k, L, S, x_dtype, w_dtype,
+              n_shared, _dev(pool), slot_stride, _dev(lut), _dev(owner), _dev(tags), _host(host_store),
+              _host(self.blob_of), _dev(shared_pool), _dev(err), _dev(self.ws), nbytes,
+              _stream(self.compute_stream), _stream(self.fill_stream))
+
+    def place(self, slot: int, layer: int, expert: int) -> None:
+        _call("moe_ctx_place", self.handle, slot, layer, expert)
+
+    def forward(self, layer: int, x, w_router, bias, out, stats: np.ndarray | None = None) -> None:
+        T = x.shape[0]
+        if T > self.t_max or x.shape[1] != self.H or tuple(w_router.shape) != (self.E, self.H):
+            raise ValueError("moe_layer_forward: shape mismatch")
+        if out.numel() < T * self.H or (bias is not None and bias.numel() != self.E):
+            raise ValueError("moe_layer_forward: output or bias size")
+        _call("moe_layer_forward", self.handle, layer, _dev(x), T, _dev(w_router), _dev(bias), _dev(out),
+              dtype_code(out), _host(stats))
+
+    def tables(self):
+        lut = np.empty(self.L * self.E, np.int32)
+        owner = np.empty(self.S, np.int32)
+        last = np.empty(self.S, np.int64)
+        clock = np.zeros(1, np.int64)
+        _call("moe_ctx_read_tables", self.handle, _host(lut), _host(owner), _host(last), _host(clock))
+        return lut, owner, last, int(clock[0])
+
+    def outputs(self, T: int) -> dict:
+        """Views into the workspace of the last step's routing and permutation."""
+        ptrs = [_vp() for _ in range(6)]
+        _call("moe_ctx_outputs", self.handle, *[ctypes.byref(p) for p in ptrs])
+        base = self.ws.data_ptr()
+        E, k = self.E, self.k
+
+        def view(p, n, dtype, shape):
+            off = p.value - base
+            return self.ws[off:off + n * 4].view(dtype).view(*shape)
+        return dict(logits=view(ptrs[0], T * E, torch.float32, (T, E)),
+                    ids=view(ptrs[1], T * k, torch.int32, (T, k)),
+                    topk_w=view(ptrs[2], T * k, torch.float32, (T, k)),
+                    perm=view(ptrs[3], T * k, torch.int32, (T * k,)),
+                    offsets=view(ptrs[4], E + 1, torch.int32, (E + 1,)),
+                    inv=view(ptrs[5], T * k, torch.int32, (T * k,)))
+
+    def set_timing(self, on: bool) -> None:
+        _call("moe_ctx_set_timing", self.handle, int(on))
+
+    def ffn_time(self) -> tuple[float, int]:
+        ms, n = ctypes.c_double(), ctypes.c_long()
+        _call("moe_ctx_ffn_time", self.handle, ctypes.byref(ms), ctypes.byref(n))
+        return ms.value, n.value
+
+    def close(self) -> None:
+        if getattr(self, "handle", None) and self.handle.value:
+            lib().moe_ctx_destroy(self.handle)
+            self.handle = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

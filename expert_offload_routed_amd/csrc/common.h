@@ -73,13 +73,48 @@ struct __attribute__((aligned(16))) u32x4 {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+
 // Non-temporal 16-byte load for weights that are streamed once.
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p));
   u32x4 r;
-  r.x = __builtin_nontemporal_load(&q->x);
-  r.y = __builtin_nontemporal_load(&q->y);
-  r.z = __builtin_nontemporal_load(&q->z);
-  r.w = __builtin_nontemporal_load(&q->w);
+  r.x = v.x;
+  r.y = v.y;
+  r.z = v.z;
+  r.w = v.w;
+  return r;
+}
+
+// ------------------------------------------------------------------- scans
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan over a workgroup of up to 1024 threads (s_wave: >= 33 ints of
+// LDS); returns this thread's exclusive prefix and the total in *total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nwaves = (blockDim.x + 63) >> 6;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = (lane < nwaves) ? s_wave[lane] : 0;
+    const int winc = wave_inclusive_scan(w);
+    if (lane < 16) s_wave[16 + lane] = winc - w;
+    if (lane == 15) s_wave[32] = winc;
+  }
+  __syncthreads();
+  const int r = s_wave[16 + wave] + inc - v;
+  *total = s_wave[32];
+  __syncthreads();
   return r;
 }

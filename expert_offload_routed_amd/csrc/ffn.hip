@@ -8,54 +8,33 @@
 // Adaptive Residual Offloading for Large-Scale MoE Inference", Eq. (7):
 // y = down(SiLU(gate x) * up x).
 //
-// Kernels (all enqueued on the caller's stream):
-//   ffn_plan_kernel      one workgroup: compacts the selected, non-empty,
-//                        resident groups into a work list in the workspace
-//                        (ascending expert id) and flags absent experts.
-//   ffn_w13_gemv_kernel  decode form of the first projection: each wave owns
-//                        two neurons (their gate and up rows, interleaved in
-//                        the slot) for one group and streams those rows once
-//                        per tile of <= 8 tokens with 16-byte coalesced loads;
-//                        fp32 FMA, wave reduction, SiLU(g) * u fused in the
-//                        epilogue -> h [T*k, F] fp32 in the workspace.
-//   ffn_w2_gemv_kernel   decode form of the down projection: each wave owns
-//                        four output rows and streams them against h.
-// The weights are read exactly once per token tile, so for decode groups
-// (<= 8 rows) the passes are bound by HBM bandwidth on the weight bytes.
+// Kernels (all on the caller's stream):
+//   ffn_plan_kernel  one workgroup: selected, non-empty, resident groups go to
+//                    the GEMV list (<= kGemvMaxRows rows) or are cut into
+//                    kGemmBM-row MFMA tiles; absent experts set MOE_ERR_ABSENT.
+//   GEMV passes      (ffn_gemv.h) decode groups: weight rows streamed once per
+//                    token tile with non-temporal 16-byte loads, split-K over
+//                    the waves of a workgroup; HBM-bound.
+//   GEMM passes      (gemm.hip) groups with more rows: bf16 MFMA tiles.
+// The SwiGLU intermediate h lives in the workspace: bf16 with bf16 weights
+// (the A operand of the second MFMA pass), fp32 with fp32 weights.
+#include <limits.h>
+
 #include "common.h"
+#include "ffn_gemv.h"
 #include "ffn_internal.h"
 
 namespace {
 
-template <int FMT>
-__device__ __forceinline__ void load8(const void* base, size_t elem, float out[8]) {
-  if constexpr (FMT == MOE_BF16) {
-    u32x4 v = ld16(static_cast<const uint16_t*>(base) + elem);
-    out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
-    out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
-    out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
-    out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
-  } else {
-    const float* p = static_cast<const float*>(base) + elem;
-    u32x4 a = ld16(p), b = ld16(p + 4);
-    out[0] = __uint_as_float(a.x); out[1] = __uint_as_float(a.y);
-    out[2] = __uint_as_float(a.z); out[3] = __uint_as_float(a.w);
-    out[4] = __uint_as_float(b.x); out[5] = __uint_as_float(b.y);
-    out[6] = __uint_as_float(b.z); out[7] = __uint_as_float(b.w);
-  }
-}
+constexpr int kGemvGridCap = 8192;  // workgroups of a GEMV pass (they loop over work units)
 
-__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
-
-__global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ lut,
-                                                        const int32_t* __restrict__ mask, int E,
-                                                        int num_slots,
-                                                        FfnItem* __restrict__ items,
-                                                        int32_t* __restrict__ n_items,
-                                                        int32_t* __restrict__ err_word) {
-  __shared__ int s_wave[16];
-  const int e = threadIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(1024) void ffn_plan_kernel(
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ lut,
+    const int32_t* __restrict__ mask, int E, int num_slots, int small_max,
+    FfnItem* __restrict__ items, int32_t* __restrict__ n_items, GemmTile* __restrict__ tiles,
+    int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_word) {
+  __shared__ int s_wave[40];
+  const int e = threadIdx.x;
   int rows = 0, slot = -1, begin = 0;
   bool take = false;
   if (e < E) {
@@ -70,172 +49,62 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
       }
     }
   }
-  const uint64_t m = __ballot(take);
-  if (lane == 0) s_wave[wave] = __popcll(m);
-  __syncthreads();
-  int base = 0, total = 0;
-  for (int w = 0; w < 16; ++w) {
-    if (w < wave) base += s_wave[w];
-    total += s_wave[w];
+  const bool small = take && rows <= small_max;
+  const int ntile = (take && !small) ? (rows + kGemmBM - 1) / kGemmBM : 0;
+  int total_items = 0, total_tiles = 0;
+  const int ipos = block_exclusive_scan(small ? 1 : 0, s_wave, &total_items);
+  const int tpos = block_exclusive_scan(ntile, s_wave, &total_tiles);
+  if (small) items[ipos] = FfnItem{e, slot, begin, rows};
+  for (int i = 0; i < ntile; ++i) {
+    const int r0 = i * kGemmBM;
+    tiles[tpos + i] = GemmTile{e, slot, begin + r0, min(kGemmBM, rows - r0)};
   }
-  if (take) {
-    FfnItem it;
-    it.expert = e;
-    it.slot = slot;
-    it.row_begin = begin;
-    it.rows = rows;
-    items[base + popc_below(m)] = it;
-  }
-  if (e == 0) n_items[0] = total;
-}
-
-// ------------------------------------------------------------ W13 (gate/up)
-template <int WF, int XF, int NT>
-__device__ __forceinline__ void w13_tile(const char* __restrict__ w13, const void* __restrict__ x,
-                                         const int32_t* __restrict__ perm, int prow, int k, int H,
-                                         int F, int n0, float* __restrict__ hbuf) {
-  constexpr size_t esz = (WF == MOE_BF16) ? 2 : 4;
-  const int lane = threadIdx.x & 63;
-  int tok[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) tok[t] = perm[prow + t] / k;
-  float acc[4][NT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[i][t] = 0.f;
-  const size_t rowb = (size_t)H * esz;
-  const char* r0 = w13 + (size_t)(2 * n0) * rowb;
-  for (int c = lane * 8; c < H; c += 64 * 8) {
-    float wv[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) load8<WF>(r0 + i * rowb, c, wv[i]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float xv[8];
-      load8<XF>(x, (size_t)tok[t] * H + c, xv);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[i][t] = fmaf(wv[i][q], xv[q], acc[i][t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const float g0 = wave_sum(acc[0][t]), u0 = wave_sum(acc[1][t]);
-    const float g1 = wave_sum(acc[2][t]), u1 = wave_sum(acc[3][t]);
-    if (lane == t) {
-      float* hrow = hbuf + (size_t)(prow + t) * F;
-      hrow[n0] = silu(g0) * u0;
-      hrow[n0 + 1] = silu(g1) * u1;
-    }
+  if (e == 0) {
+    n_items[0] = total_items;
+    n_tiles[0] = total_tiles;
   }
 }
 
-template <int WF, int XF>
-__global__ __launch_bounds__(256) void ffn_w13_gemv_kernel(const void* __restrict__ x,
-                                                           const int32_t* __restrict__ perm, int k,
-                                                           const FfnItem* __restrict__ items,
-                                                           const int32_t* __restrict__ n_items,
-                                                           const char* __restrict__ pool,
-                                                           size_t stride, size_t off_w13, int H,
-                                                           int F, float* __restrict__ hbuf) {
-  if ((int)blockIdx.y >= n_items[0]) return;
-  const FfnItem it = items[blockIdx.y];
-  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 2;
-  if (n0 >= F) return;
-  const char* w13 = pool + (size_t)it.slot * stride + off_w13;
-  int done = 0;
-  for (; it.rows - done >= 8; done += 8)
-    w13_tile<WF, XF, 8>(w13, x, perm, it.row_begin + done, k, H, F, n0, hbuf);
-  const int p = it.row_begin + done;
-  switch (it.rows - done) {
-    case 1: w13_tile<WF, XF, 1>(w13, x, perm, p, k, H, F, n0, hbuf); break;
-    case 2: w13_tile<WF, XF, 2>(w13, x, perm, p, k, H, F, n0, hbuf); break;
-    case 3: w13_tile<WF, XF, 3>(w13, x, perm, p, k, H, F, n0, hbuf); break;
-    case 4: w13_tile<WF, XF, 4>(w13, x, perm, p, k, H, F, n0, hbuf); break;
-    case 5: w13_tile<WF, XF, 5>(w13, x, perm, p, k, H, F, n0, hbuf); break;
-    case 6: w13_tile<WF, XF, 6>(w13, x, perm, p, k, H, F, n0, hbuf); break;
-    case 7: w13_tile<WF, XF, 7>(w13, x, perm, p, k, H, F, n0, hbuf); break;
-    default: break;
-  }
+template <int WF, int AF, int OF, int RPW, int KS, int U, int MAXNT, bool SWIGLU>
+void launch_pass(const void* act, const int32_t* perm, int k, const FfnItem* items,
+                 const int32_t* n_items, int max_items, const char* pool, size_t stride,
+                 size_t off, int rows, int K, int out_ld, void* out, hipStream_t s) {
+  const unsigned rb = gemv::row_blocks<RPW, KS>(rows);
+  const long long units = (long long)rb * max_items;
+  const unsigned grid = (unsigned)(units < kGemvGridCap ? units : kGemvGridCap);
+  if (grid == 0) return;
+  hipLaunchKernelGGL((gemv::pass_kernel<WF, AF, OF, RPW, KS, U, MAXNT, SWIGLU, true>), dim3(grid),
+                     dim3(256), 0, s, act, perm, k, items, n_items, pool, stride, off, rows, K,
+                     out_ld, (int)rb, out);
 }
 
-// ---------------------------------------------------------------- W2 (down)
-template <int WF, int NT>
-__device__ __forceinline__ void w2_tile(const char* __restrict__ w2, const float* __restrict__ hbuf,
-                                        int prow, int H, int F, int r0, float* __restrict__ y) {
-  constexpr size_t esz = (WF == MOE_BF16) ? 2 : 4;
-  const int lane = threadIdx.x & 63;
-  float acc[4][NT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[i][t] = 0.f;
-  const size_t rowb = (size_t)F * esz;
-  const char* rr = w2 + (size_t)r0 * rowb;
-  for (int c = lane * 8; c < F; c += 64 * 8) {
-    float wv[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) load8<WF>(rr + i * rowb, c, wv[i]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float hv[8];
-      load8<MOE_F32>(hbuf, (size_t)(prow + t) * F + c, hv);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[i][t] = fmaf(wv[i][q], hv[q], acc[i][t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = wave_sum(acc[i][t]);
-    if (lane == t) {
-      float* yrow = y + (size_t)(prow + t) * H + r0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) yrow[i] = s[i];
-    }
-  }
+// bf16 tokens and weights: GEMV for small groups, MFMA tiles for the rest.
+template <int MAXNT>
+void launch_bf16(const void* x, const int32_t* perm, int k, const FfnItem* items,
+                 const int32_t* n_items, int max_items, const GemmTile* tiles,
+                 const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
+                 const SlotLayout& lay, int H, int F, void* hbuf, float* y, hipStream_t s) {
+  launch_pass<MOE_BF16, MOE_BF16, MOE_BF16, 4, 2, 2, MAXNT, true>(
+      x, perm, k, items, n_items, max_items, pool, stride, lay.off_w13, 2 * F, H, F, hbuf, s);
+  if (max_tiles > 0)
+    launch_gemm_bf16(1, x, perm, k, tiles, n_tiles, max_tiles, pool, stride, lay.off_w13, 2 * F, H,
+                     F, hbuf, s);
+  launch_pass<MOE_BF16, MOE_BF16, MOE_F32, 4, 4, 1, MAXNT, false>(
+      hbuf, perm, k, items, n_items, max_items, pool, stride, lay.off_w2, H, F, H, y, s);
+  if (max_tiles > 0)
+    launch_gemm_bf16(2, hbuf, perm, k, tiles, n_tiles, max_tiles, pool, stride, lay.off_w2, H, F, H,
+                     y, s);
 }
 
-template <int WF>
-__global__ __launch_bounds__(256) void ffn_w2_gemv_kernel(const float* __restrict__ hbuf,
-                                                          const FfnItem* __restrict__ items,
-                                                          const int32_t* __restrict__ n_items,
-                                                          const char* __restrict__ pool,
-                                                          size_t stride, size_t off_w2, int H, int F,
-                                                          float* __restrict__ y) {
-  if ((int)blockIdx.y >= n_items[0]) return;
-  const FfnItem it = items[blockIdx.y];
-  const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
-  if (r0 >= H) return;
-  const char* w2 = pool + (size_t)it.slot * stride + off_w2;
-  int done = 0;
-  for (; it.rows - done >= 8; done += 8) w2_tile<WF, 8>(w2, hbuf, it.row_begin + done, H, F, r0, y);
-  const int p = it.row_begin + done;
-  switch (it.rows - done) {
-    case 1: w2_tile<WF, 1>(w2, hbuf, p, H, F, r0, y); break;
-    case 2: w2_tile<WF, 2>(w2, hbuf, p, H, F, r0, y); break;
-    case 3: w2_tile<WF, 3>(w2, hbuf, p, H, F, r0, y); break;
-    case 4: w2_tile<WF, 4>(w2, hbuf, p, H, F, r0, y); break;
-    case 5: w2_tile<WF, 5>(w2, hbuf, p, H, F, r0, y); break;
-    case 6: w2_tile<WF, 6>(w2, hbuf, p, H, F, r0, y); break;
-    case 7: w2_tile<WF, 7>(w2, hbuf, p, H, F, r0, y); break;
-    default: break;
-  }
-}
-
-template <int WF, int XF>
-void launch_dense(const void* x, const int32_t* perm, int k, const FfnItem* items,
-                  const int32_t* n_items, const char* pool, size_t stride, const SlotLayout& lay,
-                  int H, int F, int max_items, float* hbuf, float* y, hipStream_t s) {
-  hipLaunchKernelGGL((ffn_w13_gemv_kernel<WF, XF>), dim3((F / 2 + 3) / 4, max_items), dim3(256), 0,
-                     s, x, perm, k, items, n_items, pool, stride, lay.off_w13, H, F, hbuf);
-  hipLaunchKernelGGL((ffn_w2_gemv_kernel<WF>), dim3((H / 4 + 3) / 4, max_items), dim3(256), 0, s,
-                     hbuf, items, n_items, pool, stride, lay.off_w2, H, F, y);
+// fp32 tokens and weights: GEMV for every group (token tiles of up to 8 rows).
+template <int MAXNT>
+void launch_f32(const void* x, const int32_t* perm, int k, const FfnItem* items,
+                const int32_t* n_items, int max_items, const char* pool, size_t stride,
+                const SlotLayout& lay, int H, int F, void* hbuf, float* y, hipStream_t s) {
+  launch_pass<MOE_F32, MOE_F32, MOE_F32, 4, 2, 1, MAXNT, true>(
+      x, perm, k, items, n_items, max_items, pool, stride, lay.off_w13, 2 * F, H, F, hbuf, s);
+  launch_pass<MOE_F32, MOE_F32, MOE_F32, 4, 4, 1, MAXNT, false>(
+      hbuf, perm, k, items, n_items, max_items, pool, stride, lay.off_w2, H, F, H, y, s);
 }
 
 }  // namespace
@@ -243,9 +112,14 @@ void launch_dense(const void* x, const int32_t* perm, int k, const FfnItem* item
 FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype) {
   FfnWorkspace w{};
   const size_t rows = (size_t)T * k;
-  size_t off = 256;  // n_items at offset 0
+  // upper bound on MFMA tiles: sum over large groups of ceil(rows / BM)
+  const long long large = (long long)(rows / (kGemvMaxRows + 1));
+  w.max_tiles = (int)(rows / kGemmBM + (large < E ? large : E) + 1);
+  size_t off = 256;  // n_items at offset 0, n_tiles at offset 4
   w.items = off;
   off = align_up(off + (size_t)E * sizeof(FfnItem), 256);
+  w.tiles = off;
+  off = align_up(off + (size_t)w.max_tiles * sizeof(GemmTile), 256);
   w.h = off;
   off = align_up(off + rows * F * sizeof(float), 256);
   if (w_dtype == MOE_INT4G128) {
@@ -267,11 +141,16 @@ extern "C" size_t moe_ffn_workspace_bytes(int T, int H, int F, int E, int k, int
   return ffn_workspace_layout(T, H, F, E, k, w_dtype).total;
 }
 
+int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* lut,
+             const int32_t* group_mask, const char* pool, size_t stride, int num_slots,
+             const SlotLayout& lay, int T, int H, int F, int E, int k, float* y, int32_t* err,
+             char* ws, const FfnWorkspace& wl, hipStream_t s);
+
 extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
                               const int32_t* offsets, const int32_t* lut,
                               const int32_t* group_mask, const void* pool_base, size_t slot_stride,
-                              int num_slots, int w_dtype, int T, int H, int F, int E, int k, float* y_perm,
-                              int32_t* err_word, void* workspace, size_t ws_bytes,
+                              int num_slots, int w_dtype, int T, int H, int F, int E, int k,
+                              float* y_perm, int32_t* err_word, void* workspace, size_t ws_bytes,
                               hipStream_t stream) {
   MOE_CHECK_ARG(T >= 0 && k >= 1 && k <= E && E <= 1024);
   MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
@@ -281,32 +160,59 @@ extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
   if (T == 0) return MOE_OK;
   MOE_CHECK_ARG(x && perm && offsets && lut && pool_base && y_perm && err_word && workspace);
   MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)pool_base % 256) == 0);
+  MOE_CHECK_ARG(((uintptr_t)y_perm % 16) == 0);
   const FfnWorkspace ws = ffn_workspace_layout(T, H, F, E, k, w_dtype);
   MOE_CHECK_ARG(ws_bytes >= ws.total && ((uintptr_t)workspace % 256) == 0);
-  if (w_dtype == MOE_INT4G128) return MOE_EUNSUPPORTED;
+  // supported pairs: fp32 tokens with fp32 weights; bf16 tokens with bf16 or int4 weights
+  if (w_dtype == MOE_F32 && x_dtype != MOE_F32) return MOE_EUNSUPPORTED;
+  if (w_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (w_dtype == MOE_BF16 && (H % 64 != 0 || F % 64 != 0)) return MOE_EUNSUPPORTED;
 
   char* wsb = static_cast<char*>(workspace);
+  if (w_dtype == MOE_INT4G128)
+    return ffn_int4(x, perm, offsets, lut, group_mask, static_cast<const char*>(pool_base),
+                    slot_stride, num_slots, lay, T, H, F, E, k, y_perm, err_word, wsb, ws, stream);
+
   int32_t* n_items = reinterpret_cast<int32_t*>(wsb);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(wsb + 4);
   FfnItem* items = reinterpret_cast<FfnItem*>(wsb + ws.items);
-  float* hbuf = reinterpret_cast<float*>(wsb + ws.h);
+  GemmTile* tiles = reinterpret_cast<GemmTile*>(wsb + ws.tiles);
+  void* hbuf = wsb + ws.h;
   const long long tk = (long long)T * k;
   const int max_items = (int)(tk < E ? tk : E);
-  MOE_CHECK_ARG(max_items <= 65535);
+  const bool bf16 = (w_dtype == MOE_BF16);
+  // a group holds at most T rows (a token picks an expert once)
+  const int small_max = bf16 ? kGemvMaxRows : INT_MAX;
+  const int max_tiles = (bf16 && T > kGemvMaxRows) ? ws.max_tiles : 0;
+  MOE_CHECK_ARG(max_tiles <= 65535);
 
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), 0, stream, offsets, lut, group_mask, E,
-                     num_slots, items, n_items, err_word);
+                     num_slots, small_max, items, n_items, tiles, n_tiles, err_word);
   const char* pool = static_cast<const char*>(pool_base);
-  if (w_dtype == MOE_BF16 && x_dtype == MOE_BF16)
-    launch_dense<MOE_BF16, MOE_BF16>(x, perm, k, items, n_items, pool, slot_stride, lay, H, F,
-                                     max_items, hbuf, y_perm, stream);
-  else if (w_dtype == MOE_BF16 && x_dtype == MOE_F32)
-    launch_dense<MOE_BF16, MOE_F32>(x, perm, k, items, n_items, pool, slot_stride, lay, H, F,
-                                    max_items, hbuf, y_perm, stream);
-  else if (w_dtype == MOE_F32 && x_dtype == MOE_F32)
-    launch_dense<MOE_F32, MOE_F32>(x, perm, k, items, n_items, pool, slot_stride, lay, H, F,
-                                   max_items, hbuf, y_perm, stream);
-  else
-    launch_dense<MOE_F32, MOE_BF16>(x, perm, k, items, n_items, pool, slot_stride, lay, H, F,
-                                    max_items, hbuf, y_perm, stream);
+  const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;  // rows of the largest GEMV group
+  if (bf16) {
+    if (nt <= 1)
+      launch_bf16<1>(x, perm, k, items, n_items, max_items, tiles, n_tiles, max_tiles, pool,
+                     slot_stride, lay, H, F, hbuf, y_perm, stream);
+    else if (nt <= 2)
+      launch_bf16<2>(x, perm, k, items, n_items, max_items, tiles, n_tiles, max_tiles, pool,
+                     slot_stride, lay, H, F, hbuf, y_perm, stream);
+    else
+      launch_bf16<4>(x, perm, k, items, n_items, max_items, tiles, n_tiles, max_tiles, pool,
+                     slot_stride, lay, H, F, hbuf, y_perm, stream);
+  } else {
+    if (T <= 1)
+      launch_f32<1>(x, perm, k, items, n_items, max_items, pool, slot_stride, lay, H, F, hbuf,
+                    y_perm, stream);
+    else if (T <= 2)
+      launch_f32<2>(x, perm, k, items, n_items, max_items, pool, slot_stride, lay, H, F, hbuf,
+                    y_perm, stream);
+    else if (T <= 4)
+      launch_f32<4>(x, perm, k, items, n_items, max_items, pool, slot_stride, lay, H, F, hbuf,
+                    y_perm, stream);
+    else
+      launch_f32<8>(x, perm, k, items, n_items, max_items, pool, slot_stride, lay, H, F, hbuf,
+                    y_perm, stream);
+  }
   return moe_launch_status();
 }

@@ -12,6 +12,17 @@ struct FfnItem {
   int32_t rows;       // assignments in the group
 };
 
+// One M-tile of a large group for the MFMA GEMM path.
+struct GemmTile {
+  int32_t expert;
+  int32_t slot;
+  int32_t row_begin;  // first sorted position of the tile
+  int32_t rows;       // rows in the tile (<= kGemmBM)
+};
+
+constexpr int kGemmBM = 64;      // rows of an MFMA M-tile
+constexpr int kGemvMaxRows = 4;  // groups up to this many rows take the GEMV path
+
 // Byte layout of one expert inside a slot (see moe_slot_layout).
 struct SlotLayout {
   size_t slot_bytes, off_w13, off_w2, off_s13, off_s2;
@@ -19,10 +30,16 @@ struct SlotLayout {
 
 // Sections of the moe_expert_ffn workspace (byte offsets).
 struct FfnWorkspace {
-  size_t items, h, xq, xs, hq, hs, total;
+  size_t items, tiles, h, xq, xs, hq, hs, total;
+  int max_tiles;
 };
 
 static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int slot_layout(int H, int F, int w_dtype, SlotLayout* out);
+
+#include <hip/hip_runtime.h>
+void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, const GemmTile* tiles,
+                      const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
+                      size_t off, int N, int K, int out_ld, void* out, hipStream_t s);
 FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype);

@@ -16,36 +16,6 @@
 
 namespace {
 
-// Inclusive scan over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
-
-// Exclusive scan over a 1024-thread block; returns the block total in *total.
-__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int inc = wave_inclusive_scan(v);
-  if (lane == 63) s_wave[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    const int w = (lane < 16) ? s_wave[lane] : 0;
-    const int winc = wave_inclusive_scan(w);
-    if (lane < 16) s_wave[16 + lane] = winc - w;
-    if (lane == 15) s_wave[32] = winc;
-  }
-  __syncthreads();
-  const int r = s_wave[16 + wave] + inc - v;
-  *total = s_wave[32];
-  __syncthreads();
-  return r;
-}
-
 __global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __restrict__ ids, int n,
                                                              int E, int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets,

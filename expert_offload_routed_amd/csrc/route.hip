@@ -8,11 +8,10 @@
 // Sec. II-A, Eq. (1)).
 //
 // Two kernels:
-//   route_logits_kernel: each wave computes EW experts x TT tokens of dot
-//     products over H; lanes stride H with 8-element vectors (16-byte bf16 /
-//     2x16-byte fp32 loads), fp32 FMA, then a wave reduction. Spread over
-//     ceil(E/EW) x ceil(T/TT) waves so a decode step pulls w_router from HBM
-//     with many CUs at once.
+//   route_logits_kernel: one workgroup per (expert, tile of 8 tokens); its
+//     256 threads split H into 8-element vectors (16-byte bf16 / 2x16-byte
+//     fp32 loads), fp32 FMA, then a wave and a cross-wave reduction. A decode
+//     step pulls w_router from HBM with E workgroups at once.
 //   topk_softmax_kernel: one wave per token; lane l holds logits l, l+64, ...
 //     Each of the k rounds takes the wave-wide (value desc, id asc) maximum
 //     through xor shuffles; then softmax over the selected values.
@@ -23,8 +22,7 @@
 
 namespace {
 
-constexpr int kRouteEW = 4;   // experts per wave
-constexpr int kRouteTT = 4;   // tokens per wave
+constexpr int kRouteTT = 8;   // tokens per workgroup
 constexpr int kTopkMaxV = 16; // logits per lane (E <= 1024)
 
 template <int FMT>
@@ -50,52 +48,41 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
                                                            const void* __restrict__ w,
                                                            const float* __restrict__ bias, int T,
                                                            int H, int E, float* __restrict__ logits) {
+  __shared__ float red[4][kRouteTT];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int e0 = (blockIdx.x * 4 + wave) * kRouteEW;
+  const int e = blockIdx.x;
   const int t0 = blockIdx.y * kRouteTT;
-  if (e0 >= E) return;
-  const int ne = min(kRouteEW, E - e0);
   const int nt = min(kRouteTT, T - t0);
 
-  float acc[kRouteEW][kRouteTT];
+  float acc[kRouteTT];
 #pragma unroll
-  for (int e = 0; e < kRouteEW; ++e)
-#pragma unroll
-    for (int t = 0; t < kRouteTT; ++t) acc[e][t] = 0.f;
+  for (int t = 0; t < kRouteTT; ++t) acc[t] = 0.f;
 
-  for (int c = lane * 8; c < H; c += 64 * 8) {
-    float wv[kRouteEW][8];
-#pragma unroll
-    for (int e = 0; e < kRouteEW; ++e) {
-      if (e < ne) {
-        load8<FMT>(w, (size_t)(e0 + e) * H + c, wv[e]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) wv[e][q] = 0.f;
-      }
-    }
+#pragma unroll 2
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    float wv[8];
+    load8<FMT>(w, (size_t)e * H + c, wv);
 #pragma unroll
     for (int t = 0; t < kRouteTT; ++t) {
       if (t < nt) {
         float xv[8];
         load8<FMT>(x, (size_t)(t0 + t) * H + c, xv);
 #pragma unroll
-        for (int e = 0; e < kRouteEW; ++e)
-#pragma unroll
-          for (int q = 0; q < 8; ++q) acc[e][t] = fmaf(wv[e][q], xv[q], acc[e][t]);
+        for (int q = 0; q < 8; ++q) acc[t] = fmaf(wv[q], xv[q], acc[t]);
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < kRouteEW; ++e) {
-#pragma unroll
-    for (int t = 0; t < kRouteTT; ++t) {
-      if (e < ne && t < nt) {
-        float s = wave_sum(acc[e][t]);
-        if (lane == 0) logits[(size_t)(t0 + t) * E + e0 + e] = s + (bias ? bias[e0 + e] : 0.f);
-      }
-    }
+  for (int t = 0; t < kRouteTT; ++t) {
+    const float v = wave_sum(acc[t]);
+    if (lane == 0) red[wave][t] = v;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nt) {
+    const int t = threadIdx.x;
+    const float s = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+    logits[(size_t)(t0 + t) * E + e] = s + (bias ? bias[e] : 0.f);
   }
 }
 
@@ -188,8 +175,7 @@ extern "C" int moe_route(const void* x, int x_dtype, const void* w_router, const
   MOE_CHECK_ARG(x && w_router && logits && topk_ids && topk_w);
   MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)w_router % 16) == 0);
 
-  const int eblocks = (E + kRouteEW - 1) / kRouteEW;
-  dim3 g1((eblocks + 3) / 4, (T + kRouteTT - 1) / kRouteTT);
+  dim3 g1(E, (T + kRouteTT - 1) / kRouteTT);
   if (g1.y > 65535u) return MOE_EUNSUPPORTED;
   if (x_dtype == MOE_BF16)
     hipLaunchKernelGGL(route_logits_kernel<MOE_BF16>, g1, dim3(256), 0, stream, x, w_router, bias,

@@ -1,0 +1,443 @@
+// Layer runtime: one routed-expert MoE layer step over the slot cache, in C++.
+//
+// Order of a step (all on the caller's compute stream unless noted):
+//   moe_route -> moe_permute -> copy the distinct routed set to pinned host
+//   memory and wait for it (the one host synchronisation of a step: the
+//   routed set is known only after the router ran, as the SeqMoE and HybriMoE
+//   summary pages state) -> moe_plan_fills on the host tables -> one copy of
+//   the wave masks -> moe_expert_ffn over the groups that are already
+//   resident, while the misses are copied from the pinned host store on the
+//   fill stream and committed with their tags -> moe_expert_ffn over each
+//   wave of filled groups -> moe_expert_ffn of the shared experts (own
+//   resident pool) -> moe_combine.
+// The context allocates its buffers once, at creation; a step allocates
+// nothing.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "common.h"
+#include "ffn_internal.h"
+#include "moe_runtime.h"
+
+struct moe_layer_ctx {
+  // configuration
+  int t_max, H, F, E, k, L, S, x_dtype, w_dtype, n_shared;
+  char* pool;
+  size_t stride;
+  int32_t* lut;
+  int32_t* owner;
+  uint64_t* tags;
+  const char* host_store;
+  std::vector<int32_t> blob_of;
+  const char* shared_pool;
+  int32_t* err;
+  hipStream_t cs, fs;
+  // device buffers
+  float* logits;
+  int32_t* ids;
+  float* topw;
+  int32_t *counts, *offsets, *perm, *inv, *dist;  // dist: distinct[E] then n_distinct
+  float* y_perm;
+  char* ws;
+  size_t ws_bytes;
+  int32_t* masks;
+  int32_t *sh_perm, *sh_offsets, *sh_lut;
+  float* sh_y;
+  char* sh_ws;
+  size_t sh_ws_bytes;
+  int sh_T;  // T the shared permutation was built for
+  // host state
+  int32_t* dist_h;   // pinned [E+1]
+  int32_t* masks_h;  // pinned [(E+2)*E]
+  int32_t* sh_rows_h;  // pinned [t_max*n_shared + n_shared + 1]
+  std::vector<int32_t> lut_h, owner_h;
+  std::vector<int64_t> last_use;
+  int64_t clock;
+  uint64_t next_tag;
+  std::vector<int32_t> wave_of, is_hit, fill_e, fill_s, fill_w;
+  hipEvent_t ev_fill, ev_compute, ev_t0, ev_t1;
+  int timing, timed_pending;
+  double ffn_ms;
+  long ffn_calls;
+};
+
+namespace {
+
+// Device work buffers of a context, carved from the caller's workspace.
+struct CtxLayout {
+  size_t logits, ids, topw, counts, offsets, perm, inv, dist, y_perm, ws, masks;
+  size_t sh_perm, sh_offsets, sh_lut, sh_y, sh_ws, total;
+  size_t ws_bytes, sh_ws_bytes;
+};
+
+CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int w_dtype, int n_shared) {
+  CtxLayout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + (bytes ? bytes : 1), 256);
+    return at;
+  };
+  const size_t tk = (size_t)t_max * k;
+  l.logits = take((size_t)t_max * E * 4);
+  l.ids = take(tk * 4);
+  l.topw = take(tk * 4);
+  l.counts = take((size_t)E * 4);
+  l.offsets = take((size_t)(E + 1) * 4);
+  l.perm = take(tk * 4);
+  l.inv = take(tk * 4);
+  l.dist = take((size_t)(E + 1) * 4);
+  l.y_perm = take(tk * H * 4);
+  l.ws_bytes = moe_ffn_workspace_bytes(t_max, H, F, E, k, w_dtype);
+  l.ws = take(l.ws_bytes);
+  l.masks = take((size_t)(E + 2) * E * 4);
+  if (n_shared) {
+    l.sh_perm = take((size_t)t_max * n_shared * 4);
+    l.sh_offsets = take((size_t)(n_shared + 1) * 4);
+    l.sh_lut = take((size_t)n_shared * 4);
+    l.sh_y = take((size_t)n_shared * t_max * H * 4);
+    l.sh_ws_bytes = moe_ffn_workspace_bytes(t_max, H, F, n_shared, n_shared, w_dtype);
+    l.sh_ws = take(l.sh_ws_bytes);
+  }
+  l.total = off;
+  return l;
+}
+
+__global__ void commit_after_fill_kernel(int32_t* lut, int32_t idx, int32_t* owner, int32_t slot,
+                                         const uint64_t* tags, uint64_t tag, int32_t* err_word) {
+  if (threadIdx.x != 0) return;
+  if (tags[slot] != tag) {
+    atomicOr(err_word, MOE_ERR_STALE_TAG);
+    return;
+  }
+  const int32_t old = owner[slot];
+  if (old >= 0 && lut[old] == slot) lut[old] = -1;
+  lut[idx] = slot;
+  owner[slot] = idx;
+}
+
+__global__ void write_tag_kernel(uint64_t* tags, int slot, uint64_t tag) {
+  if (threadIdx.x == 0) tags[slot] = tag;
+}
+
+void destroy(moe_layer_ctx* c) {
+  if (!c) return;
+  void* host[] = {c->dist_h, c->masks_h, c->sh_rows_h};
+  for (void* p : host)
+    if (p) (void)hipHostFree(p);
+  hipEvent_t evs[] = {c->ev_fill, c->ev_compute, c->ev_t0, c->ev_t1};
+  for (hipEvent_t e : evs)
+    if (e) (void)hipEventDestroy(e);
+  delete c;
+}
+
+// Copy one expert into a slot on the fill stream, write its tag back, and
+// commit it on the compute stream once the copy is done. update_mirror: also
+// apply the move to the host tables (the step's plan has already done so).
+int fill_slot(moe_layer_ctx* c, int slot, int layer, int expert, bool update_mirror) {
+  const int idx = layer * c->E + expert;
+  const uint64_t tag = c->next_tag++;
+  const char* src = c->host_store + (size_t)c->blob_of[idx] * c->stride;
+  hipError_t e = hipMemcpyAsync(c->pool + (size_t)slot * c->stride, src, c->stride,
+                                hipMemcpyHostToDevice, c->fs);
+  if (e != hipSuccess) return moe_hip_status(e);
+  hipLaunchKernelGGL(write_tag_kernel, dim3(1), dim3(64), 0, c->fs, c->tags, slot, tag);
+  if (c->fs != c->cs) {
+    if ((e = hipEventRecord(c->ev_fill, c->fs)) != hipSuccess) return moe_hip_status(e);
+    if ((e = hipStreamWaitEvent(c->cs, c->ev_fill, 0)) != hipSuccess) return moe_hip_status(e);
+  }
+  hipLaunchKernelGGL(commit_after_fill_kernel, dim3(1), dim3(64), 0, c->cs, c->lut, idx, c->owner,
+                     slot, c->tags, tag, c->err);
+  if (update_mirror) {
+    const int32_t old = c->owner_h[slot];
+    if (old >= 0 && c->lut_h[old] == slot) c->lut_h[old] = -1;
+    c->lut_h[idx] = slot;
+    c->owner_h[slot] = idx;
+  }
+  return moe_launch_status();
+}
+
+// Make the fill stream wait for everything enqueued so far on the compute stream.
+int fills_after_compute(moe_layer_ctx* c) {
+  if (c->fs == c->cs) return MOE_OK;
+  hipError_t e = hipEventRecord(c->ev_compute, c->cs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(c->fs, c->ev_compute, 0);
+  return moe_hip_status(e);
+}
+
+}  // namespace
+
+extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int E, int k, int L,
+                              int S, int x_dtype, int w_dtype, int n_shared, void* pool_base,
+                              size_t slot_stride, int32_t* lut, int32_t* owner,
+                              uint64_t* slot_tags, const void* host_store,
+                              const int32_t* blob_of, const void* shared_pool, int32_t* err_word,
+                              void* workspace, size_t ws_bytes, hipStream_t compute_stream,
+                              hipStream_t fill_stream) {
+  MOE_CHECK_ARG(out && t_max >= 1 && k >= 1 && k <= E && E <= 1024 && L >= 1 && S >= 1);
+  MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
+  MOE_CHECK_ARG(n_shared >= 0 && (n_shared == 0 || shared_pool));
+  MOE_CHECK_ARG(pool_base && lut && owner && slot_tags && host_store && blob_of && err_word);
+  SlotLayout lay;
+  if (slot_layout(H, F, w_dtype, &lay) != MOE_OK) return MOE_EINVAL;
+  MOE_CHECK_ARG(slot_stride >= lay.slot_bytes && slot_stride % 256 == 0);
+  const CtxLayout cl = ctx_layout(t_max, H, F, E, k, w_dtype, n_shared);
+  MOE_CHECK_ARG(workspace && ws_bytes >= cl.total && ((uintptr_t)workspace % 256) == 0);
+  *out = nullptr;
+  moe_layer_ctx* c = new (std::nothrow) moe_layer_ctx();
+  if (!c) return MOE_EHIP;
+  c->t_max = t_max; c->H = H; c->F = F; c->E = E; c->k = k; c->L = L; c->S = S;
+  c->x_dtype = x_dtype; c->w_dtype = w_dtype; c->n_shared = n_shared;
+  c->pool = static_cast<char*>(pool_base);
+  c->stride = slot_stride;
+  c->lut = lut; c->owner = owner; c->tags = slot_tags;
+  c->host_store = static_cast<const char*>(host_store);
+  c->blob_of.assign(blob_of, blob_of + (size_t)L * E);
+  c->shared_pool = static_cast<const char*>(shared_pool);
+  c->err = err_word;
+  c->cs = compute_stream;
+  c->fs = fill_stream;
+  c->lut_h.assign((size_t)L * E, -1);
+  c->owner_h.assign(S, -1);
+  c->last_use.assign(S, 0);
+  c->clock = 0;
+  c->next_tag = 1;
+  c->wave_of.resize(E); c->is_hit.resize(E);
+  c->fill_e.resize(E); c->fill_s.resize(E); c->fill_w.resize(E);
+  c->sh_T = -1;
+  char* wb = static_cast<char*>(workspace);
+  c->logits = reinterpret_cast<float*>(wb + cl.logits);
+  c->ids = reinterpret_cast<int32_t*>(wb + cl.ids);
+  c->topw = reinterpret_cast<float*>(wb + cl.topw);
+  c->counts = reinterpret_cast<int32_t*>(wb + cl.counts);
+  c->offsets = reinterpret_cast<int32_t*>(wb + cl.offsets);
+  c->perm = reinterpret_cast<int32_t*>(wb + cl.perm);
+  c->inv = reinterpret_cast<int32_t*>(wb + cl.inv);
+  c->dist = reinterpret_cast<int32_t*>(wb + cl.dist);
+  c->y_perm = reinterpret_cast<float*>(wb + cl.y_perm);
+  c->ws = wb + cl.ws;
+  c->ws_bytes = cl.ws_bytes;
+  c->masks = reinterpret_cast<int32_t*>(wb + cl.masks);
+  if (n_shared) {
+    c->sh_perm = reinterpret_cast<int32_t*>(wb + cl.sh_perm);
+    c->sh_offsets = reinterpret_cast<int32_t*>(wb + cl.sh_offsets);
+    c->sh_lut = reinterpret_cast<int32_t*>(wb + cl.sh_lut);
+    c->sh_y = reinterpret_cast<float*>(wb + cl.sh_y);
+    c->sh_ws = wb + cl.sh_ws;
+    c->sh_ws_bytes = cl.sh_ws_bytes;
+  }
+  int bad = 0;
+  bad |= hipHostMalloc(reinterpret_cast<void**>(&c->dist_h), (E + 1) * sizeof(int32_t)) != hipSuccess;
+  bad |= hipHostMalloc(reinterpret_cast<void**>(&c->masks_h), (size_t)(E + 2) * E * sizeof(int32_t)) !=
+         hipSuccess;
+  bad |= hipHostMalloc(reinterpret_cast<void**>(&c->sh_rows_h),
+                       ((size_t)t_max * n_shared + n_shared + 1) * sizeof(int32_t)) != hipSuccess;
+  bad |= hipEventCreateWithFlags(&c->ev_fill, hipEventDisableTiming) != hipSuccess;
+  bad |= hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming) != hipSuccess;
+  bad |= hipEventCreate(&c->ev_t0) != hipSuccess;
+  bad |= hipEventCreate(&c->ev_t1) != hipSuccess;
+  if (bad) {
+    (void)hipGetLastError();
+    destroy(c);
+    return MOE_EHIP;
+  }
+  if (n_shared) {
+    std::vector<int32_t> id(n_shared);
+    for (int s = 0; s < n_shared; ++s) id[s] = s;
+    if (hipMemcpy(c->sh_lut, id.data(), n_shared * sizeof(int32_t), hipMemcpyHostToDevice) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      destroy(c);
+      return MOE_EHIP;
+    }
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+extern "C" size_t moe_ctx_workspace_bytes(int t_max, int H, int F, int E, int k, int w_dtype,
+                                          int n_shared) {
+  if (t_max < 1 || H <= 0 || F <= 0 || E < 1 || k < 1 || n_shared < 0) return 0;
+  return ctx_layout(t_max, H, F, E, k, w_dtype, n_shared).total;
+}
+
+extern "C" int moe_ctx_destroy(moe_layer_ctx* ctx) {
+  if (!ctx) return MOE_EINVAL;
+  (void)hipStreamSynchronize(ctx->cs);
+  if (ctx->fs != ctx->cs) (void)hipStreamSynchronize(ctx->fs);
+  destroy(ctx);
+  return MOE_OK;
+}
+
+extern "C" int moe_ctx_place(moe_layer_ctx* c, int slot, int layer, int expert) {
+  MOE_CHECK_ARG(c && slot >= 0 && slot < c->S && layer >= 0 && layer < c->L && expert >= 0 &&
+                expert < c->E);
+  MOE_CHECK_ARG(c->lut_h[(size_t)layer * c->E + expert] < 0);
+  // the copy must not overtake kernels that may still read the slot
+  int rc = fills_after_compute(c);
+  if (rc != MOE_OK) return rc;
+  return fill_slot(c, slot, layer, expert, true);
+}
+
+extern "C" int moe_ctx_read_tables(const moe_layer_ctx* c, int32_t* lut_out, int32_t* owner_out,
+                                   int64_t* last_use_out, int64_t* clock_out) {
+  MOE_CHECK_ARG(c);
+  if (lut_out) memcpy(lut_out, c->lut_h.data(), c->lut_h.size() * sizeof(int32_t));
+  if (owner_out) memcpy(owner_out, c->owner_h.data(), c->owner_h.size() * sizeof(int32_t));
+  if (last_use_out) memcpy(last_use_out, c->last_use.data(), c->last_use.size() * sizeof(int64_t));
+  if (clock_out) *clock_out = c->clock;
+  return MOE_OK;
+}
+
+extern "C" int moe_ctx_set_timing(moe_layer_ctx* c, int enable) {
+  MOE_CHECK_ARG(c);
+  c->timing = enable;
+  c->timed_pending = 0;
+  c->ffn_ms = 0.0;
+  c->ffn_calls = 0;
+  return MOE_OK;
+}
+
+static void collect_timing(moe_layer_ctx* c) {
+  if (!c->timed_pending) return;
+  float ms = 0.f;
+  if (hipEventSynchronize(c->ev_t1) == hipSuccess &&
+      hipEventElapsedTime(&ms, c->ev_t0, c->ev_t1) == hipSuccess) {
+    c->ffn_ms += ms;
+    c->ffn_calls += 1;
+  } else {
+    (void)hipGetLastError();
+  }
+  c->timed_pending = 0;
+}
+
+extern "C" int moe_ctx_ffn_time(moe_layer_ctx* c, double* total_ms, long* steps) {
+  MOE_CHECK_ARG(c && total_ms && steps);
+  collect_timing(c);
+  *total_ms = c->ffn_ms;
+  *steps = c->ffn_calls;
+  return MOE_OK;
+}
+
+extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int T,
+                                 const void* w_router, const float* bias, void* out, int out_dtype,
+                                 int32_t* stats) {
+  MOE_CHECK_ARG(c && layer >= 0 && layer < c->L && T >= 0 && T <= c->t_max);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(x && w_router && out);
+  const int E = c->E, k = c->k, H = c->H, F = c->F;
+  int rc;
+  if ((rc = moe_route(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids, c->topw,
+                      c->cs)) != MOE_OK)
+    return rc;
+  if ((rc = moe_permute(c->ids, T, k, E, c->counts, c->offsets, c->perm, c->inv, c->dist,
+                        c->dist + E, c->cs)) != MOE_OK)
+    return rc;
+  hipError_t e = hipMemcpyAsync(c->dist_h, c->dist, (E + 1) * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, c->cs);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->cs);
+  if (e != hipSuccess) return moe_hip_status(e);
+  collect_timing(c);  // the previous step's events have completed
+
+  const int nd = c->dist_h[E];
+  int32_t n_fills = 0, n_waves = 0;
+  if ((rc = moe_plan_fills(c->lut_h.data(), c->owner_h.data(), c->last_use.data(), &c->clock,
+                           c->S, c->L, E, layer, c->dist_h, nd, c->wave_of.data(),
+                           c->is_hit.data(), c->fill_e.data(), c->fill_s.data(), c->fill_w.data(),
+                           &n_fills, &n_waves)) != MOE_OK)
+    return rc;
+  // The plan moved the host tables to their final state; the device tables
+  // follow as each fill commits, in plan order.
+  // Masks: row 0 = resident groups, row 1 + w = groups filled in wave w.
+  const int rows = n_waves + 1;
+  memset(c->masks_h, 0, (size_t)rows * E * sizeof(int32_t));
+  int hits = 0;
+  for (int i = 0; i < nd; ++i) {
+    const int ex = c->dist_h[i];
+    if (c->is_hit[ex]) {
+      c->masks_h[ex] = 1;
+      ++hits;
+    } else {
+      c->masks_h[(size_t)(1 + c->wave_of[ex]) * E + ex] = 1;
+    }
+  }
+  if ((e = hipMemcpyAsync(c->masks, c->masks_h, (size_t)rows * E * sizeof(int32_t),
+                          hipMemcpyHostToDevice, c->cs)) != hipSuccess)
+    return moe_hip_status(e);
+  // wave 0 fills may start now: only slots not read by this step's resident groups
+  if (n_fills && (rc = fills_after_compute(c)) != MOE_OK) return rc;
+  const int32_t* lut_row = c->lut + (size_t)layer * E;
+  const int num_slots = c->S;
+  const bool timing = c->timing != 0;
+  if (timing && (e = hipEventRecord(c->ev_t0, c->cs)) != hipSuccess) return moe_hip_status(e);
+  if (hits) {
+    if ((rc = moe_expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, c->masks, c->pool,
+                             c->stride, num_slots, c->w_dtype, T, H, F, E, k, c->y_perm, c->err,
+                             c->ws, c->ws_bytes, c->cs)) != MOE_OK)
+      return rc;
+  }
+  int fi = 0;
+  for (int w = 0; w < n_waves; ++w) {
+    if (w > 0 && (rc = fills_after_compute(c)) != MOE_OK) return rc;
+    int nw = 0;
+    for (; fi < n_fills && c->fill_w[fi] == w; ++fi, ++nw)
+      if ((rc = fill_slot(c, c->fill_s[fi], layer, c->fill_e[fi], false)) != MOE_OK) return rc;
+    if (nw && (rc = moe_expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row,
+                                   c->masks + (size_t)(1 + w) * E, c->pool, c->stride, num_slots,
+                                   c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws,
+                                   c->ws_bytes, c->cs)) != MOE_OK)
+      return rc;
+  }
+  if (timing) {
+    if ((e = hipEventRecord(c->ev_t1, c->cs)) != hipSuccess) return moe_hip_status(e);
+    c->timed_pending = 1;
+  }
+  const float* shared_y = nullptr;
+  if (c->n_shared) {
+    const int n = c->n_shared;
+    if (c->sh_T != T) {
+      // rows of shared expert s: flat assignments t*n + s, t ascending
+      int32_t* h = c->sh_rows_h;
+      for (int s = 0; s < n; ++s)
+        for (int t = 0; t < T; ++t) h[(size_t)s * T + t] = t * n + s;
+      for (int s = 0; s <= n; ++s) h[(size_t)T * n + s] = s * T;
+      if ((e = hipMemcpyAsync(c->sh_perm, h, (size_t)T * n * sizeof(int32_t),
+                              hipMemcpyHostToDevice, c->cs)) != hipSuccess ||
+          (e = hipMemcpyAsync(c->sh_offsets, h + (size_t)T * n, (n + 1) * sizeof(int32_t),
+                              hipMemcpyHostToDevice, c->cs)) != hipSuccess)
+        return moe_hip_status(e);
+      c->sh_T = T;
+    }
+    if ((rc = moe_expert_ffn(x, c->x_dtype, c->sh_perm, c->sh_offsets, c->sh_lut, nullptr,
+                             c->shared_pool, c->stride, n, c->w_dtype, T, H, F, n, n, c->sh_y,
+                             c->err, c->sh_ws, c->sh_ws_bytes, c->cs)) != MOE_OK)
+      return rc;
+    shared_y = c->sh_y;
+  }
+  if ((rc = moe_combine(c->y_perm, c->inv, c->topw, T, k, H, shared_y, c->n_shared, out, out_dtype,
+                        c->cs)) != MOE_OK)
+    return rc;
+  if (stats) {
+    stats[0] = nd;
+    stats[1] = hits;
+    stats[2] = n_fills;
+    stats[3] = n_waves;
+  }
+  return MOE_OK;
+}
+
+extern "C" int moe_ctx_outputs(const moe_layer_ctx* c, float** logits, int32_t** ids,
+                               float** topk_w, int32_t** perm, int32_t** offsets,
+                               int32_t** inv) {
+  MOE_CHECK_ARG(c);
+  if (logits) *logits = c->logits;
+  if (ids) *ids = c->ids;
+  if (topk_w) *topk_w = c->topw;
+  if (perm) *perm = c->perm;
+  if (offsets) *offsets = c->offsets;
+  if (inv) *inv = c->inv;
+  return MOE_OK;
+}

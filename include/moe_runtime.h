@@ -1,0 +1,96 @@
+/*
+ * moe_runtime.h - one routed-expert MoE layer step over the slot cache, run
+ * by the library (host orchestration in C++ over the entry points of
+ * moe_offload.h).
+ *
+ * A step follows the pages' problem statement: the routed experts are known
+ * only after the router runs, the expert kernel must see one fixed slot
+ * layout, and misses are copied from a pinned host pool on a separate stream
+ * while resident experts compute (SeqMoE summary page, Mechanism; HybriMoE
+ * summary page, Mechanism: misses = routed set minus cached set). The step
+ * synchronises with the host once, to read the distinct routed set for the
+ * residency plan (moe_plan_fills).
+ *
+ * Ownership: the caller owns the slot pool, the device tables, the pinned
+ * host store, the shared-expert pool, the error word, the device workspace
+ * (moe_ctx_workspace_bytes) and both streams; the context allocates only a
+ * few KB of pinned host staging and its events, once, in moe_ctx_create, and
+ * frees them in moe_ctx_destroy. A context is used by one host thread at a
+ * time. Status codes as in moe_offload.h.
+ */
+#ifndef MOE_RUNTIME_H
+#define MOE_RUNTIME_H
+
+#include "moe_offload.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_layer_ctx moe_layer_ctx;
+
+/* moe_ctx_workspace_bytes: device workspace a context needs (0 on bad sizes). */
+size_t moe_ctx_workspace_bytes(int t_max, int H, int F, int E, int k, int w_dtype, int n_shared);
+
+/* moe_ctx_create: context for a stack of L layers sharing one slot pool.
+ *   t_max       largest token count of a step
+ *   H, F, E, k  hidden size, expert FFN size, routed experts per layer, top-k
+ *   S           slots in the pool (pool_base + s * slot_stride, s < S)
+ *   x_dtype     MOE_F32 or MOE_BF16 (tokens and router weights)
+ *   w_dtype     expert weight format (MOE_F32, MOE_BF16, MOE_INT4G128)
+ *   n_shared    always-on shared experts (0 = none); their packed weights sit
+ *               in shared_pool (n_shared slots of slot_stride bytes, resident)
+ *   lut         [L*E] int32 device table (expert -> slot, -1 = absent)
+ *   owner       [S] int32 device: lut index held by each slot, -1 = empty
+ *   slot_tags   [S] uint64 device
+ *   host_store  pinned host memory: weight set b at host_store + b*slot_stride
+ *   blob_of     host [L*E]: weight set of (layer, expert) (copied at creation)
+ *   err_word    [1] int32 device (MOE_ERR_* bits)
+ *   workspace   device, 256-byte aligned, ws_bytes >= moe_ctx_workspace_bytes()
+ * The device tables must start empty (-1); moe_ctx_place fills the initial
+ * residents. */
+int moe_ctx_create(moe_layer_ctx** ctx, int t_max, int H, int F, int E, int k, int L, int S,
+                   int x_dtype, int w_dtype, int n_shared, void* pool_base, size_t slot_stride,
+                   int32_t* lut, int32_t* owner, uint64_t* slot_tags, const void* host_store,
+                   const int32_t* blob_of, const void* shared_pool, int32_t* err_word,
+                   void* workspace, size_t ws_bytes, hipStream_t compute_stream,
+                   hipStream_t fill_stream);
+
+/* moe_ctx_destroy: wait for both streams, free the context's buffers. */
+int moe_ctx_destroy(moe_layer_ctx* ctx);
+
+/* moe_ctx_place: copy (layer, expert) into an empty or reusable slot before
+ * the first step (initial residency); the expert must not be resident. */
+int moe_ctx_place(moe_layer_ctx* ctx, int slot, int layer, int expert);
+
+/* moe_layer_forward: one step of layer `layer` on T tokens (T <= t_max).
+ *   x         [T,H] device, x_dtype
+ *   w_router  [E,H] device, x_dtype; bias [E] fp32 device or NULL
+ *   out       [T,H] device in out_dtype (MOE_F32 or MOE_BF16)
+ *   stats     host int32[4] or NULL: distinct routed experts, hits, fills, waves
+ * Returns after enqueuing the step (the host waited only for the routed set). */
+int moe_layer_forward(moe_layer_ctx* ctx, int layer, const void* x, int T, const void* w_router,
+                      const float* bias, void* out, int out_dtype, int32_t* stats);
+
+/* moe_ctx_read_tables: host copies of the tables as the plan left them
+ * (lut [L*E], owner [S], last_use [S], clock [1]); any pointer may be NULL. */
+int moe_ctx_read_tables(const moe_layer_ctx* ctx, int32_t* lut, int32_t* owner, int64_t* last_use,
+                        int64_t* clock);
+
+/* moe_ctx_outputs: device buffers of the last step, inside the workspace
+ * (logits [T,E], topk ids and weights [T,k], perm, offsets [E+1], inv); any
+ * pointer may be NULL. */
+int moe_ctx_outputs(const moe_layer_ctx* ctx, float** logits, int32_t** ids, float** topk_w,
+                    int32_t** perm, int32_t** offsets, int32_t** inv);
+
+/* moe_ctx_set_timing: when enabled, each step records HIP events on the
+ * compute stream around its routed moe_expert_ffn calls; moe_ctx_ffn_time
+ * returns the summed milliseconds and the number of timed steps (resetting
+ * happens on moe_ctx_set_timing). */
+int moe_ctx_set_timing(moe_layer_ctx* ctx, int enable);
+int moe_ctx_ffn_time(moe_layer_ctx* ctx, double* total_ms, long* steps);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_RUNTIME_H */

@@ -121,7 +121,10 @@ def _pool_with(shape, lut_perm, layer=0):
 FFN_CASES = [
     (TINY, 16),
     (W.reduced(MIX, E=16, k=4, H=512, F=384), 1),
-    (W.reduced(MIX, E=16, k=4, H=512, F=384), 40),
+    (W.reduced(MIX, E=16, k=4, H=512, F=384), 3),
+    (W.reduced(MIX, E=16, k=4, H=512, F=384), 40),    # GEMV groups and MFMA tiles
+    (W.reduced(MIX, E=16, k=4, H=512, F=384), 300),   # several 64-row tiles, ragged tails
+    (W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), E=16, k=6, H=2048, F=1408), 100),
     (W.reduced(MIX, E=8, k=2, H=256, F=512, wfmt="f32", xfmt="f32"), 29),
 ]
 
@@ -269,12 +272,17 @@ def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1):
             torch.cuda.synchronize()
             assert layer_obj.err.item() == 0
             wr, b = layer_obj.routers[layer]
-            check_routing(x, wr, b, shape.k, layer_obj.logits[:T], layer_obj.ids[:T], layer_obj.topw[:T])
-            ids = layer_obj.ids[:T].cpu().numpy()
+            o = layer_obj.outputs(T)
+            check_routing(x, wr, b, shape.k, o["logits"], o["ids"], o["topk_w"])
+            ids = o["ids"].cpu().numpy()
             pr = O.permute(ids, shape.E)
+            assert o["perm"].cpu().numpy().tolist() == pr["perm"].tolist()
+            assert o["inv"].cpu().numpy().tolist() == pr["inv"].tolist()
             planner.plan(layer, pr["distinct"])
+            lut_h, owner_h, last_use_h, clock_h = layer_obj.tables()
             assert layer_obj.lut.cpu().numpy().reshape(shape.layers, shape.E).tolist() == planner.lut.tolist()
-            assert layer_obj.lut_h.reshape(shape.layers, shape.E).tolist() == planner.lut.tolist()
+            assert lut_h.reshape(shape.layers, shape.E).tolist() == planner.lut.tolist()
+            assert last_use_h.tolist() == planner.last_use and clock_h == planner.clock
             # oracle output on the kernel's selection, oracle weights from its own logits
             ref_logits = O.router_logits(x, wr, b)
             wts = O.gate_weights(ref_logits, ids)
@@ -311,3 +319,36 @@ def test_layer_shared_experts():
 def test_layer_mixtral_full_size_decode():
     """Full Mixtral-shaped layer (H=4096, F=14336), 4 of 8 experts resident, decode T=1 and T=8."""
     _run_layer_case(MIX, 4, "random", [1, 8])
+
+
+def test_layer_mixtral_full_size_prefill_sampled():
+    """Full Mixtral-shaped layer, prefill of 512 tokens (MFMA tiles), all experts resident;
+    the oracle checks a sample of tokens spread over every expert group."""
+    shape = MIX
+    T = 512
+    residency = W.initial_residency(shape, 8, "random")
+    layer = Hn.SlotCacheLayer(shape, 8, residency, T)
+    x = W.tokens(shape, T, device=_dev())
+    out = layer.forward(x)
+    torch.cuda.synchronize()
+    assert layer.err.item() == 0
+    o = layer.outputs(T)
+    wr, b = layer.routers[0]
+    under, _ = check_routing(x, wr, b, shape.k, o["logits"], o["ids"], o["topk_w"])
+    ids = o["ids"].cpu().numpy()
+    ref_logits = O.router_logits(x, wr, b)
+    wts = O.gate_weights(ref_logits, ids)
+    sample = sorted({0, 1, 2, 63, 64, 65, 127, 128, 200, 255, 256, 300, 383, 384, 450, 510, 511})
+    experts = {}
+    x32 = O.as_f32(x)
+    ref = np.zeros((len(sample), shape.H))
+    for i, t in enumerate(sample):
+        for j in range(shape.k):
+            e = int(ids[t, j])
+            if e not in experts:
+                experts[e] = host_weights(shape, e)
+            ref[i] += wts[t, j] * O.expert_forward(x32[t:t + 1], experts[e])[0]
+    got = out.float().cpu().numpy()[sample]
+    r = rel_l2(got, ref)
+    say(f"  prefill sampled rel L2 {r:.3e}, tokens under margin {under}")
+    assert r <= TOL[shape.wfmt]
