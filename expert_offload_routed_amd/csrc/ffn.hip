@@ -109,6 +109,13 @@ void launch_f32(const void* x, const int32_t* perm, int k, const FfnItem* items,
 
 }  // namespace
 
+void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
+                     int num_slots, int small_max, FfnItem* items, int32_t* n_items,
+                     GemmTile* tiles, int32_t* n_tiles, int32_t* err_word, hipStream_t s) {
+  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, lut, mask, E, num_slots,
+                     small_max, items, n_items, tiles, n_tiles, err_word);
+}
+
 FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype) {
   FfnWorkspace w{};
   const size_t rows = (size_t)T * k;
@@ -123,14 +130,19 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype
   w.h = off;
   off = align_up(off + rows * F * sizeof(float), 256);
   if (w_dtype == MOE_INT4G128) {
+    // int8 rows, their fp32 scales and int32 sums per 128-value group
     w.xq = off;
     off = align_up(off + (size_t)T * H, 256);
     w.xs = off;
     off = align_up(off + (size_t)T * sizeof(float), 256);
+    w.xg = off;
+    off = align_up(off + (size_t)T * (H / 128) * sizeof(int32_t), 256);
     w.hq = off;
     off = align_up(off + rows * F, 256);
     w.hs = off;
     off = align_up(off + rows * sizeof(float), 256);
+    w.hg = off;
+    off = align_up(off + rows * (F / 128) * sizeof(int32_t), 256);
   }
   w.total = off;
   return w;
@@ -186,8 +198,8 @@ extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
   const int max_tiles = (bf16 && T > kGemvMaxRows) ? ws.max_tiles : 0;
   MOE_CHECK_ARG(max_tiles <= 65535);
 
-  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), 0, stream, offsets, lut, group_mask, E,
-                     num_slots, small_max, items, n_items, tiles, n_tiles, err_word);
+  launch_ffn_plan(offsets, lut, group_mask, E, num_slots, small_max, items, n_items, tiles, n_tiles,
+                  err_word, stream);
   const char* pool = static_cast<const char*>(pool_base);
   const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;  // rows of the largest GEMV group
   if (bf16) {

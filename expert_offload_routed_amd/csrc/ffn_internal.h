@@ -30,7 +30,7 @@ struct SlotLayout {
 
 // Sections of the moe_expert_ffn workspace (byte offsets).
 struct FfnWorkspace {
-  size_t items, tiles, h, xq, xs, hq, hs, total;
+  size_t items, tiles, h, xq, xs, xg, hq, hs, hg, total;
   int max_tiles;
 };
 
@@ -39,6 +39,11 @@ static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; 
 int slot_layout(int H, int F, int w_dtype, SlotLayout* out);
 
 #include <hip/hip_runtime.h>
+// The FFN work list: groups of <= small_max rows as FfnItem, the others cut
+// into kGemmBM-row GemmTile (see ffn_plan_kernel in ffn.hip).
+void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
+                     int num_slots, int small_max, FfnItem* items, int32_t* n_items,
+                     GemmTile* tiles, int32_t* n_tiles, int32_t* err_word, hipStream_t s);
 void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, const GemmTile* tiles,
                       const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
                       size_t off, int N, int K, int out_ld, void* out, hipStream_t s);

@@ -80,11 +80,32 @@ extern "C" int moe_pack_expert_host(const void* gate, const void* up, const void
   }
   const char* g = static_cast<const char*>(gate);
   const char* u = static_cast<const char*>(up);
+  // int4 rows are stored per 8 consecutive codes c0..c7 as one little-endian
+  // word whose byte i holds c_i in its low nibble and c_{i+4} in its high
+  // nibble, so the low (high) nibbles of a word are 4 consecutive values
+  auto put = [&](char* dst, const char* src, size_t bytes) {
+    if (w_dtype != MOE_INT4G128) {
+      memcpy(dst, src, bytes);
+      return;
+    }
+    const uint8_t* in = reinterpret_cast<const uint8_t*>(src);  // even code in the low nibble
+    for (size_t w = 0; w < bytes / 4; ++w) {
+      uint8_t c[8];
+      for (int i = 0; i < 4; ++i) {
+        c[2 * i] = in[4 * w + i] & 0xF;
+        c[2 * i + 1] = in[4 * w + i] >> 4;
+      }
+      uint32_t word = 0;
+      for (int i = 0; i < 4; ++i) word |= (uint32_t)(c[i] | (c[i + 4] << 4)) << (8 * i);
+      memcpy(dst + 4 * w, &word, 4);
+    }
+  };
   for (int n = 0; n < F; ++n) {
-    memcpy(d + l.off_w13 + (size_t)(2 * n) * rb13, g + (size_t)n * rb13, rb13);
-    memcpy(d + l.off_w13 + (size_t)(2 * n + 1) * rb13, u + (size_t)n * rb13, rb13);
+    put(d + l.off_w13 + (size_t)(2 * n) * rb13, g + (size_t)n * rb13, rb13);
+    put(d + l.off_w13 + (size_t)(2 * n + 1) * rb13, u + (size_t)n * rb13, rb13);
   }
-  memcpy(d + l.off_w2, down, (size_t)H * rb2);
+  for (int r = 0; r < H; ++r)
+    put(d + l.off_w2 + (size_t)r * rb2, static_cast<const char*>(down) + (size_t)r * rb2, rb2);
   if (w_dtype == MOE_INT4G128) {
     const size_t sb13 = (size_t)(H / 128) * 2, sb2 = (size_t)(F / 128) * 2;
     const char* gs = static_cast<const char*>(gate_s);

@@ -108,8 +108,9 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E,
  * slot pool is one allocation: slot s starts at pool_base + s * slot_stride
  * (the fixed-base [num_slots, dim0, dim1] pool of the SeqMoE page).
  *   w13 at off_w13: 2F rows of H values, row 2n = gate row n, row 2n+1 = up
- *                   row n (fp32/bf16 values, or int4 codes packed two per
- *                   byte along H, even index in the low nibble)
+ *                   row n (fp32/bf16 values, or int4 codes: each 32-bit
+ *                   little-endian word holds 8 consecutive codes c0..c7,
+ *                   byte i = c_i in the low nibble, c_{i+4} in the high one)
  *   w2  at off_w2:  H rows of F values (down projection, same packing)
  *   int4 only: s13 at off_s13: [2F, H/128] bf16 scales (rows as w13);
  *              s2 at off_s2: [H, F/128] bf16 scales.

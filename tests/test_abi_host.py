@@ -74,8 +74,16 @@ def test_pack_int4_keeps_codes_and_scales(lib):
     lay = B.moe_slot_layout(256, 128, B.MOE_INT4G128)
     dst = torch.zeros(lay["slot_bytes"], dtype=torch.uint8)
     B.moe_pack_expert_host(dict(w), 256, 128, B.MOE_INT4G128, dst)
-    w13 = dst[lay["off_w13"]:lay["off_w13"] + 256 * 128].view(256, 128)
-    assert torch.equal(w13[0::2], w["gate_q"]) and torch.equal(w13[1::2], w["up_q"])
+    w13 = dst[lay["off_w13"]:lay["off_w13"] + 256 * 128].view(256, 128).numpy()
+    # slot word order: word w of a row holds codes 8w..8w+7; byte i = code 8w+i (low) | 8w+4+i (high)
+    lo, hi = (w13 & 0xF).astype(np.int64), (w13 >> 4).astype(np.int64)
+    codes = np.empty((256, 256), np.int64)
+    for i in range(4):
+        codes[:, i::8] = lo[:, i::4]
+        codes[:, 4 + i::8] = hi[:, i::4]
+    codes = np.where(codes >= 8, codes - 16, codes)
+    assert np.array_equal(codes[0::2], O.decode_int4(w["gate_q"]))
+    assert np.array_equal(codes[1::2], O.decode_int4(w["up_q"]))
     s13 = dst[lay["off_s13"]:lay["off_s13"] + 256 * 2 * 2].view(torch.bfloat16).view(256, 2)
     assert torch.equal(s13[0::2], w["gate_s"]) and torch.equal(s13[1::2], w["up_s"])
     s2 = dst[lay["off_s2"]:lay["off_s2"] + 256 * 1 * 2].view(torch.bfloat16).view(256, 1)

@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 
 TINY = W.shape_of("tiny_e8k2_h256_f512_fp32")
 MIX = W.shape_of("mixtral_e8k2_h4096_f14336_bf16")
+DSV3 = W.shape_of("dsv3_e256k8s1_h7168_f2048_int4")
 
 
 def _dev():
@@ -126,6 +127,12 @@ FFN_CASES = [
     (W.reduced(MIX, E=16, k=4, H=512, F=384), 300),   # several 64-row tiles, ragged tails
     (W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), E=16, k=6, H=2048, F=1408), 100),
     (W.reduced(MIX, E=8, k=2, H=256, F=512, wfmt="f32", xfmt="f32"), 29),
+    (W.reduced(DSV3, E=16, k=4, H=512, F=256), 1),     # int4 weights, int8 activations
+    (W.reduced(DSV3, E=16, k=4, H=512, F=256), 3),
+    (W.reduced(DSV3, E=16, k=4, H=512, F=256), 40),
+    (W.reduced(DSV3, E=16, k=4, H=512, F=256), 300),
+    (W.reduced(DSV3, E=12, k=8, H=7168, F=2048), 2),  # full hidden/FFN sizes
+    (W.reduced(DSV3, E=12, k=8, H=7168, F=2048), 24),
 ]
 
 
@@ -314,6 +321,11 @@ def test_layer_stack_shared_pool():
 def test_layer_shared_experts():
     shape = W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), E=16, k=6, H=256, F=256)
     _run_layer_case(shape, 8, "zipf_rank", [1, 32, 5])
+
+
+def test_layer_int4_shared_expert_misses():
+    shape = W.reduced(DSV3, E=32, k=8, H=256, F=128)
+    _run_layer_case(shape, 12, "zipf_rank", [1, 6, 40, 2])
 
 
 def test_layer_mixtral_full_size_decode():
