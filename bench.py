@@ -54,20 +54,22 @@ def timed(layer, shape, T, steps, warmup, label, ffn_timing=False):
         layer.forward(x, out=out)
     torch.cuda.synchronize()
     layer.ctx.set_timing(ffn_timing)
-    st = Hn.StepStats()
+    c0 = layer.counters()
     t0 = time.perf_counter()
     for x in xs[warmup:]:
-        layer.forward(x, out=out, stats=st)
+        layer.forward(x, out=out)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    c1 = layer.counters()
+    distinct = (c1["distinct"] - c0["distinct"]) / steps
     res = {"tokens_per_step": T, "tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3,
-           "distinct_per_step": st.distinct / steps, "fills_per_step": st.fills / steps}
+           "distinct_per_step": distinct, "fills_per_step": (c1["fills"] - c0["fills"]) / steps}
     if ffn_timing:
         ms, n = layer.ctx.ffn_time()
         layer.ctx.set_timing(False)
         # algorithmic bytes of the expert FFN per step: the routed experts' weights
         # (every distinct expert is read once), tokens in, one fp32 row out per assignment
-        byts = (st.distinct / steps) * expert_bytes(shape) + T * shape.H * 2 + T * shape.k * shape.H * 4
+        byts = distinct * expert_bytes(shape) + T * shape.H * 2 + T * shape.k * shape.H * 4
         res["ffn"] = {"calls": n, "avg_us": 1e3 * ms / n, "avg_bytes": byts,
                       "gbs": byts / (ms / n * 1e-3) / 1e9}
     print(f"# {label}: {res}", file=sys.stderr, flush=True)

@@ -46,6 +46,7 @@ _SIGNATURES = {
     "moe_ctx_read_tables": (_i32, [_vp, _vp, _vp, _vp, _vp]),
     "moe_ctx_outputs": (_i32, [_vp] + [ctypes.POINTER(_vp)] * 6),
     "moe_ctx_set_timing": (_i32, [_vp, _i32]),
+    "moe_ctx_counters": (_i32, [_vp, _vp]),
     "moe_ctx_ffn_time": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_long)]),
 }
 
@@ -327,6 +328,11 @@ class LayerContext:
                     perm=view(ptrs[3], T * k, torch.int32, (T * k,)),
                     offsets=view(ptrs[4], E + 1, torch.int32, (E + 1,)),
                     inv=view(ptrs[5], T * k, torch.int32, (T * k,)))
+
+    def counters(self) -> dict:
+        c = np.zeros(4, np.int64)
+        _call("moe_ctx_counters", self.handle, _host(c))
+        return dict(distinct=int(c[0]), hits=int(c[1]), fills=int(c[2]), waves=int(c[3]))
 
     def set_timing(self, on: bool) -> None:
         _call("moe_ctx_set_timing", self.handle, int(on))

@@ -2,15 +2,20 @@
 //
 // Order of a step (all on the caller's compute stream unless noted):
 //   moe_route -> moe_permute -> copy the distinct routed set to pinned host
-//   memory and wait for it (the one host synchronisation of a step: the
-//   routed set is known only after the router ran, as the SeqMoE and HybriMoE
-//   summary pages state) -> moe_plan_fills on the host tables -> one copy of
-//   the wave masks -> moe_expert_ffn over the groups that are already
-//   resident, while the misses are copied from the pinned host store on the
-//   fill stream and committed with their tags -> moe_expert_ffn over each
-//   wave of filled groups -> moe_expert_ffn of the shared experts (own
-//   resident pool) -> moe_combine.
-// The context allocates its buffers once, at creation; a step allocates
+//   memory -> moe_plan_fills on the host tables -> one copy of the wave masks
+//   -> moe_expert_ffn over the groups that are already resident, while the
+//   misses are copied from the pinned host store on the fill stream and
+//   committed with their tags -> moe_expert_ffn over each wave of filled
+//   groups -> moe_expert_ffn of the shared experts (own resident pool) ->
+//   moe_combine.
+// The routed set is known only after the router ran (SeqMoE and HybriMoE
+// summary pages, Problem), so a step whose layer may miss waits for that copy:
+// the one host synchronisation of a step. When every expert of the layer is
+// resident no residency decision can change, so the step does not wait: the
+// routed set lands in a ring of pinned buffers and its LRU bookkeeping (clock
+// and last use, with no fills) is replayed in step order before the next plan
+// that needs the tables.
+// The context allocates its staging once, at creation; a step allocates
 // nothing.
 #include <stdlib.h>
 #include <string.h>
@@ -21,6 +26,10 @@
 #include "common.h"
 #include "ffn_internal.h"
 #include "moe_runtime.h"
+
+namespace {
+constexpr int kRing = 64;  // deferred routed sets (and timing event pairs) in flight
+}
 
 struct moe_layer_ctx {
   // configuration
@@ -35,7 +44,7 @@ struct moe_layer_ctx {
   const char* shared_pool;
   int32_t* err;
   hipStream_t cs, fs;
-  // device buffers
+  // device buffers (inside the caller's workspace)
   float* logits;
   int32_t* ids;
   float* topw;
@@ -50,16 +59,24 @@ struct moe_layer_ctx {
   size_t sh_ws_bytes;
   int sh_T;  // T the shared permutation was built for
   // host state
-  int32_t* dist_h;   // pinned [E+1]
-  int32_t* masks_h;  // pinned [(E+2)*E]
+  int32_t* ring_h;  // pinned [kRing][E+1]: routed sets of steps
+  hipEvent_t ring_ev[kRing];
+  int ring_layer[kRing];
+  int ring_head, ring_count;  // deferred entries: ring_head .. ring_head + count - 1
+  int ring_next;              // next ring entry to use
+  int32_t* masks_h;    // pinned [(E+2)*E]
   int32_t* sh_rows_h;  // pinned [t_max*n_shared + n_shared + 1]
-  std::vector<int32_t> lut_h, owner_h;
+  std::vector<int32_t> lut_h, owner_h, resident;  // resident[l]: experts of layer l in the pool
   std::vector<int64_t> last_use;
   int64_t clock;
   uint64_t next_tag;
   std::vector<int32_t> wave_of, is_hit, fill_e, fill_s, fill_w;
-  hipEvent_t ev_fill, ev_compute, ev_t0, ev_t1;
-  int timing, timed_pending;
+  hipEvent_t ev_fill, ev_compute;
+  int64_t totals[4];  // over completed plans: distinct, hits, fills, waves
+  // timing of the routed FFN calls: one event pair per step, collected lazily
+  int timing;
+  hipEvent_t tev0[kRing], tev1[kRing];
+  int t_head, t_count;
   double ffn_ms;
   long ffn_calls;
 };
@@ -125,19 +142,30 @@ __global__ void write_tag_kernel(uint64_t* tags, int slot, uint64_t tag) {
 
 void destroy(moe_layer_ctx* c) {
   if (!c) return;
-  void* host[] = {c->dist_h, c->masks_h, c->sh_rows_h};
+  void* host[] = {c->ring_h, c->masks_h, c->sh_rows_h};
   for (void* p : host)
     if (p) (void)hipHostFree(p);
-  hipEvent_t evs[] = {c->ev_fill, c->ev_compute, c->ev_t0, c->ev_t1};
-  for (hipEvent_t e : evs)
-    if (e) (void)hipEventDestroy(e);
+  for (int i = 0; i < kRing; ++i) {
+    if (c->ring_ev[i]) (void)hipEventDestroy(c->ring_ev[i]);
+    if (c->tev0[i]) (void)hipEventDestroy(c->tev0[i]);
+    if (c->tev1[i]) (void)hipEventDestroy(c->tev1[i]);
+  }
+  if (c->ev_fill) (void)hipEventDestroy(c->ev_fill);
+  if (c->ev_compute) (void)hipEventDestroy(c->ev_compute);
   delete c;
 }
 
+void recount_resident(moe_layer_ctx* c) {
+  for (int l = 0; l < c->L; ++l) {
+    int n = 0;
+    for (int e = 0; e < c->E; ++e) n += c->lut_h[(size_t)l * c->E + e] >= 0;
+    c->resident[l] = n;
+  }
+}
+
 // Copy one expert into a slot on the fill stream, write its tag back, and
-// commit it on the compute stream once the copy is done. update_mirror: also
-// apply the move to the host tables (the step's plan has already done so).
-int fill_slot(moe_layer_ctx* c, int slot, int layer, int expert, bool update_mirror) {
+// commit it on the compute stream once the copy is done.
+int fill_slot(moe_layer_ctx* c, int slot, int layer, int expert) {
   const int idx = layer * c->E + expert;
   const uint64_t tag = c->next_tag++;
   const char* src = c->host_store + (size_t)c->blob_of[idx] * c->stride;
@@ -151,12 +179,6 @@ int fill_slot(moe_layer_ctx* c, int slot, int layer, int expert, bool update_mir
   }
   hipLaunchKernelGGL(commit_after_fill_kernel, dim3(1), dim3(64), 0, c->cs, c->lut, idx, c->owner,
                      slot, c->tags, tag, c->err);
-  if (update_mirror) {
-    const int32_t old = c->owner_h[slot];
-    if (old >= 0 && c->lut_h[old] == slot) c->lut_h[old] = -1;
-    c->lut_h[idx] = slot;
-    c->owner_h[slot] = idx;
-  }
   return moe_launch_status();
 }
 
@@ -168,7 +190,64 @@ int fills_after_compute(moe_layer_ctx* c) {
   return moe_hip_status(e);
 }
 
+// Host LRU plan of one routed set (moves the host tables), with counters.
+int run_plan(moe_layer_ctx* c, int layer, const int32_t* distinct, int nd, int32_t* n_fills,
+             int32_t* n_waves) {
+  const int rc = moe_plan_fills(c->lut_h.data(), c->owner_h.data(), c->last_use.data(), &c->clock,
+                                c->S, c->L, c->E, layer, distinct, nd, c->wave_of.data(),
+                                c->is_hit.data(), c->fill_e.data(), c->fill_s.data(),
+                                c->fill_w.data(), n_fills, n_waves);
+  if (rc != MOE_OK) return rc;
+  int hits = 0;
+  for (int i = 0; i < nd; ++i) hits += c->is_hit[distinct[i]];
+  c->totals[0] += nd;
+  c->totals[1] += hits;
+  c->totals[2] += *n_fills;
+  c->totals[3] += *n_waves;
+  if (*n_fills) recount_resident(c);
+  return MOE_OK;
+}
+
+// Replay the bookkeeping of deferred steps, oldest first.
+int drain(moe_layer_ctx* c) {
+  while (c->ring_count > 0) {
+    const int r = c->ring_head;
+    const hipError_t e = hipEventSynchronize(c->ring_ev[r]);
+    if (e != hipSuccess) return moe_hip_status(e);
+    const int32_t* d = c->ring_h + (size_t)r * (c->E + 1);
+    int32_t nf = 0, nw = 0;
+    const int rc = run_plan(c, c->ring_layer[r], d, d[c->E], &nf, &nw);
+    if (rc != MOE_OK) return rc;
+    c->ring_head = (c->ring_head + 1) % kRing;
+    c->ring_count -= 1;
+  }
+  return MOE_OK;
+}
+
+// Fold finished timing pairs into the total; all = every pending pair.
+void collect_timing(moe_layer_ctx* c, bool all) {
+  while (c->t_count > 0 && (all || c->t_count >= kRing - 1)) {
+    const int r = c->t_head;
+    float ms = 0.f;
+    if (hipEventSynchronize(c->tev1[r]) == hipSuccess &&
+        hipEventElapsedTime(&ms, c->tev0[r], c->tev1[r]) == hipSuccess) {
+      c->ffn_ms += ms;
+      c->ffn_calls += 1;
+    } else {
+      (void)hipGetLastError();
+    }
+    c->t_head = (c->t_head + 1) % kRing;
+    c->t_count -= 1;
+  }
+}
+
 }  // namespace
+
+extern "C" size_t moe_ctx_workspace_bytes(int t_max, int H, int F, int E, int k, int w_dtype,
+                                          int n_shared) {
+  if (t_max < 1 || H <= 0 || F <= 0 || E < 1 || k < 1 || n_shared < 0) return 0;
+  return ctx_layout(t_max, H, F, E, k, w_dtype, n_shared).total;
+}
 
 extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int E, int k, int L,
                               int S, int x_dtype, int w_dtype, int n_shared, void* pool_base,
@@ -202,6 +281,7 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->fs = fill_stream;
   c->lut_h.assign((size_t)L * E, -1);
   c->owner_h.assign(S, -1);
+  c->resident.assign(L, 0);
   c->last_use.assign(S, 0);
   c->clock = 0;
   c->next_tag = 1;
@@ -230,15 +310,19 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
     c->sh_ws_bytes = cl.sh_ws_bytes;
   }
   int bad = 0;
-  bad |= hipHostMalloc(reinterpret_cast<void**>(&c->dist_h), (E + 1) * sizeof(int32_t)) != hipSuccess;
-  bad |= hipHostMalloc(reinterpret_cast<void**>(&c->masks_h), (size_t)(E + 2) * E * sizeof(int32_t)) !=
-         hipSuccess;
+  bad |= hipHostMalloc(reinterpret_cast<void**>(&c->ring_h),
+                       (size_t)kRing * (E + 1) * sizeof(int32_t)) != hipSuccess;
+  bad |= hipHostMalloc(reinterpret_cast<void**>(&c->masks_h),
+                       (size_t)(E + 2) * E * sizeof(int32_t)) != hipSuccess;
   bad |= hipHostMalloc(reinterpret_cast<void**>(&c->sh_rows_h),
                        ((size_t)t_max * n_shared + n_shared + 1) * sizeof(int32_t)) != hipSuccess;
   bad |= hipEventCreateWithFlags(&c->ev_fill, hipEventDisableTiming) != hipSuccess;
   bad |= hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming) != hipSuccess;
-  bad |= hipEventCreate(&c->ev_t0) != hipSuccess;
-  bad |= hipEventCreate(&c->ev_t1) != hipSuccess;
+  for (int i = 0; i < kRing; ++i) {
+    bad |= hipEventCreateWithFlags(&c->ring_ev[i], hipEventDisableTiming) != hipSuccess;
+    bad |= hipEventCreate(&c->tev0[i]) != hipSuccess;
+    bad |= hipEventCreate(&c->tev1[i]) != hipSuccess;
+  }
   if (bad) {
     (void)hipGetLastError();
     destroy(c);
@@ -258,12 +342,6 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   return MOE_OK;
 }
 
-extern "C" size_t moe_ctx_workspace_bytes(int t_max, int H, int F, int E, int k, int w_dtype,
-                                          int n_shared) {
-  if (t_max < 1 || H <= 0 || F <= 0 || E < 1 || k < 1 || n_shared < 0) return 0;
-  return ctx_layout(t_max, H, F, E, k, w_dtype, n_shared).total;
-}
-
 extern "C" int moe_ctx_destroy(moe_layer_ctx* ctx) {
   if (!ctx) return MOE_EINVAL;
   (void)hipStreamSynchronize(ctx->cs);
@@ -276,15 +354,25 @@ extern "C" int moe_ctx_place(moe_layer_ctx* c, int slot, int layer, int expert) 
   MOE_CHECK_ARG(c && slot >= 0 && slot < c->S && layer >= 0 && layer < c->L && expert >= 0 &&
                 expert < c->E);
   MOE_CHECK_ARG(c->lut_h[(size_t)layer * c->E + expert] < 0);
-  // the copy must not overtake kernels that may still read the slot
-  int rc = fills_after_compute(c);
+  int rc = drain(c);
   if (rc != MOE_OK) return rc;
-  return fill_slot(c, slot, layer, expert, true);
+  // the copy must not overtake kernels that may still read the slot
+  if ((rc = fills_after_compute(c)) != MOE_OK) return rc;
+  if ((rc = fill_slot(c, slot, layer, expert)) != MOE_OK) return rc;
+  const int idx = layer * c->E + expert;
+  const int32_t old = c->owner_h[slot];
+  if (old >= 0 && c->lut_h[old] == slot) c->lut_h[old] = -1;
+  c->lut_h[idx] = slot;
+  c->owner_h[slot] = idx;
+  recount_resident(c);
+  return MOE_OK;
 }
 
-extern "C" int moe_ctx_read_tables(const moe_layer_ctx* c, int32_t* lut_out, int32_t* owner_out,
+extern "C" int moe_ctx_read_tables(moe_layer_ctx* c, int32_t* lut_out, int32_t* owner_out,
                                    int64_t* last_use_out, int64_t* clock_out) {
   MOE_CHECK_ARG(c);
+  const int rc = drain(c);
+  if (rc != MOE_OK) return rc;
   if (lut_out) memcpy(lut_out, c->lut_h.data(), c->lut_h.size() * sizeof(int32_t));
   if (owner_out) memcpy(owner_out, c->owner_h.data(), c->owner_h.size() * sizeof(int32_t));
   if (last_use_out) memcpy(last_use_out, c->last_use.data(), c->last_use.size() * sizeof(int64_t));
@@ -292,31 +380,26 @@ extern "C" int moe_ctx_read_tables(const moe_layer_ctx* c, int32_t* lut_out, int
   return MOE_OK;
 }
 
+extern "C" int moe_ctx_counters(moe_layer_ctx* c, int64_t* out4) {
+  MOE_CHECK_ARG(c && out4);
+  const int rc = drain(c);
+  if (rc != MOE_OK) return rc;
+  for (int i = 0; i < 4; ++i) out4[i] = c->totals[i];
+  return MOE_OK;
+}
+
 extern "C" int moe_ctx_set_timing(moe_layer_ctx* c, int enable) {
   MOE_CHECK_ARG(c);
+  collect_timing(c, true);
   c->timing = enable;
-  c->timed_pending = 0;
   c->ffn_ms = 0.0;
   c->ffn_calls = 0;
   return MOE_OK;
 }
 
-static void collect_timing(moe_layer_ctx* c) {
-  if (!c->timed_pending) return;
-  float ms = 0.f;
-  if (hipEventSynchronize(c->ev_t1) == hipSuccess &&
-      hipEventElapsedTime(&ms, c->ev_t0, c->ev_t1) == hipSuccess) {
-    c->ffn_ms += ms;
-    c->ffn_calls += 1;
-  } else {
-    (void)hipGetLastError();
-  }
-  c->timed_pending = 0;
-}
-
 extern "C" int moe_ctx_ffn_time(moe_layer_ctx* c, double* total_ms, long* steps) {
   MOE_CHECK_ARG(c && total_ms && steps);
-  collect_timing(c);
+  collect_timing(c, true);
   *total_ms = c->ffn_ms;
   *steps = c->ffn_calls;
   return MOE_OK;
@@ -330,76 +413,96 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   MOE_CHECK_ARG(x && w_router && out);
   const int E = c->E, k = c->k, H = c->H, F = c->F;
   int rc;
+  hipError_t e;
   if ((rc = moe_route(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids, c->topw,
                       c->cs)) != MOE_OK)
     return rc;
   if ((rc = moe_permute(c->ids, T, k, E, c->counts, c->offsets, c->perm, c->inv, c->dist,
                         c->dist + E, c->cs)) != MOE_OK)
     return rc;
-  hipError_t e = hipMemcpyAsync(c->dist_h, c->dist, (E + 1) * sizeof(int32_t),
-                                hipMemcpyDeviceToHost, c->cs);
-  if (e == hipSuccess) e = hipStreamSynchronize(c->cs);
-  if (e != hipSuccess) return moe_hip_status(e);
-  collect_timing(c);  // the previous step's events have completed
 
-  const int nd = c->dist_h[E];
-  int32_t n_fills = 0, n_waves = 0;
-  if ((rc = moe_plan_fills(c->lut_h.data(), c->owner_h.data(), c->last_use.data(), &c->clock,
-                           c->S, c->L, E, layer, c->dist_h, nd, c->wave_of.data(),
-                           c->is_hit.data(), c->fill_e.data(), c->fill_s.data(), c->fill_w.data(),
-                           &n_fills, &n_waves)) != MOE_OK)
-    return rc;
-  // The plan moved the host tables to their final state; the device tables
-  // follow as each fill commits, in plan order.
-  // Masks: row 0 = resident groups, row 1 + w = groups filled in wave w.
-  const int rows = n_waves + 1;
-  memset(c->masks_h, 0, (size_t)rows * E * sizeof(int32_t));
-  int hits = 0;
-  for (int i = 0; i < nd; ++i) {
-    const int ex = c->dist_h[i];
-    if (c->is_hit[ex]) {
-      c->masks_h[ex] = 1;
-      ++hits;
-    } else {
-      c->masks_h[(size_t)(1 + c->wave_of[ex]) * E + ex] = 1;
+  // the routed set goes to the next ring entry
+  if (c->ring_count == kRing && (rc = drain(c)) != MOE_OK) return rc;
+  const int r = c->ring_next;
+  int32_t* dh = c->ring_h + (size_t)r * (E + 1);
+  if ((e = hipMemcpyAsync(dh, c->dist, (E + 1) * sizeof(int32_t), hipMemcpyDeviceToHost, c->cs)) !=
+          hipSuccess ||
+      (e = hipEventRecord(c->ring_ev[r], c->cs)) != hipSuccess)
+    return moe_hip_status(e);
+  c->ring_next = (r + 1) % kRing;
+  const bool all_resident = c->resident[layer] == E;
+
+  int32_t n_fills = 0, n_waves = 0, nd = -1, hits = -1;
+  const int32_t* lut_row = c->lut + (size_t)layer * E;
+  const bool timing = c->timing != 0;
+  if (timing) {
+    collect_timing(c, false);
+    const int tr = (c->t_head + c->t_count) % kRing;
+    if ((e = hipEventRecord(c->tev0[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
+  }
+  if (all_resident) {
+    // no miss is possible: defer the bookkeeping, run every routed group
+    c->ring_layer[r] = layer;
+    c->ring_count += 1;
+    if ((rc = moe_expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, nullptr, c->pool,
+                             c->stride, c->S, c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws,
+                             c->ws_bytes, c->cs)) != MOE_OK)
+      return rc;
+  } else {
+    if ((rc = drain(c)) != MOE_OK) return rc;  // earlier steps first: their entries precede r
+    c->ring_head = c->ring_next;                 // entry r is consumed here, not deferred
+    if ((e = hipEventSynchronize(c->ring_ev[r])) != hipSuccess) return moe_hip_status(e);
+    nd = dh[E];
+    if ((rc = run_plan(c, layer, dh, nd, &n_fills, &n_waves)) != MOE_OK) return rc;
+    // masks: row 0 = resident groups, row 1 + w = groups filled in wave w
+    const int rows = n_waves + 1;
+    memset(c->masks_h, 0, (size_t)rows * E * sizeof(int32_t));
+    hits = 0;
+    for (int i = 0; i < nd; ++i) {
+      const int ex = dh[i];
+      if (c->is_hit[ex]) {
+        c->masks_h[ex] = 1;
+        ++hits;
+      } else {
+        c->masks_h[(size_t)(1 + c->wave_of[ex]) * E + ex] = 1;
+      }
+    }
+    if ((e = hipMemcpyAsync(c->masks, c->masks_h, (size_t)rows * E * sizeof(int32_t),
+                            hipMemcpyHostToDevice, c->cs)) != hipSuccess)
+      return moe_hip_status(e);
+    // wave 0 fills may start now: they only overwrite slots no resident group of this step reads
+    if (n_fills && (rc = fills_after_compute(c)) != MOE_OK) return rc;
+    if (hits) {
+      if ((rc = moe_expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, c->masks, c->pool,
+                               c->stride, c->S, c->w_dtype, T, H, F, E, k, c->y_perm, c->err,
+                               c->ws, c->ws_bytes, c->cs)) != MOE_OK)
+        return rc;
+    }
+    int fi = 0;
+    for (int w = 0; w < n_waves; ++w) {
+      if (w > 0 && (rc = fills_after_compute(c)) != MOE_OK) return rc;
+      int nw = 0;
+      for (; fi < n_fills && c->fill_w[fi] == w; ++fi, ++nw)
+        if ((rc = fill_slot(c, c->fill_s[fi], layer, c->fill_e[fi])) != MOE_OK) return rc;
+      if (nw && (rc = moe_expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row,
+                                     c->masks + (size_t)(1 + w) * E, c->pool, c->stride, c->S,
+                                     c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws,
+                                     c->ws_bytes, c->cs)) != MOE_OK)
+        return rc;
     }
   }
-  if ((e = hipMemcpyAsync(c->masks, c->masks_h, (size_t)rows * E * sizeof(int32_t),
-                          hipMemcpyHostToDevice, c->cs)) != hipSuccess)
-    return moe_hip_status(e);
-  // wave 0 fills may start now: only slots not read by this step's resident groups
-  if (n_fills && (rc = fills_after_compute(c)) != MOE_OK) return rc;
-  const int32_t* lut_row = c->lut + (size_t)layer * E;
-  const int num_slots = c->S;
-  const bool timing = c->timing != 0;
-  if (timing && (e = hipEventRecord(c->ev_t0, c->cs)) != hipSuccess) return moe_hip_status(e);
-  if (hits) {
-    if ((rc = moe_expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, c->masks, c->pool,
-                             c->stride, num_slots, c->w_dtype, T, H, F, E, k, c->y_perm, c->err,
-                             c->ws, c->ws_bytes, c->cs)) != MOE_OK)
-      return rc;
-  }
-  int fi = 0;
-  for (int w = 0; w < n_waves; ++w) {
-    if (w > 0 && (rc = fills_after_compute(c)) != MOE_OK) return rc;
-    int nw = 0;
-    for (; fi < n_fills && c->fill_w[fi] == w; ++fi, ++nw)
-      if ((rc = fill_slot(c, c->fill_s[fi], layer, c->fill_e[fi], false)) != MOE_OK) return rc;
-    if (nw && (rc = moe_expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row,
-                                   c->masks + (size_t)(1 + w) * E, c->pool, c->stride, num_slots,
-                                   c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws,
-                                   c->ws_bytes, c->cs)) != MOE_OK)
-      return rc;
-  }
   if (timing) {
-    if ((e = hipEventRecord(c->ev_t1, c->cs)) != hipSuccess) return moe_hip_status(e);
-    c->timed_pending = 1;
+    const int tr = (c->t_head + c->t_count) % kRing;
+    if ((e = hipEventRecord(c->tev1[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
+    c->t_count += 1;
   }
   const float* shared_y = nullptr;
   if (c->n_shared) {
     const int n = c->n_shared;
     if (c->sh_T != T) {
-      // rows of shared expert s: flat assignments t*n + s, t ascending
+      // rows of shared expert s: flat assignments t*n + s, t ascending; the
+      // pinned staging is rewritten only once the stream drained its last copy
+      if ((e = hipStreamSynchronize(c->cs)) != hipSuccess) return moe_hip_status(e);
       int32_t* h = c->sh_rows_h;
       for (int s = 0; s < n; ++s)
         for (int t = 0; t < T; ++t) h[(size_t)s * T + t] = t * n + s;

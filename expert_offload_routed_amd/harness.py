@@ -45,11 +45,7 @@ class ExpertStore:
 
 @dataclass
 class StepStats:
-    hits: int = 0
-    misses: int = 0
-    fills: int = 0
-    waves: int = 0
-    distinct: int = 0
+    steps: int = 0
 
 
 class SlotCacheLayer:
@@ -102,13 +98,11 @@ class SlotCacheLayer:
         wr, bias = self.routers[layer]
         self.ctx.forward(layer, x, wr, bias, out, self._st)
         if stats is not None:
-            nd, hits, fills, waves = (int(v) for v in self._st)
-            stats.distinct += nd
-            stats.hits += hits
-            stats.misses += nd - hits
-            stats.fills += fills
-            stats.waves += waves
+            stats.steps += 1
         return out
+
+    def counters(self) -> dict:
+        return self.ctx.counters()
 
     def outputs(self, T: int) -> dict:
         return self.ctx.outputs(T)

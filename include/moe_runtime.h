@@ -68,14 +68,26 @@ int moe_ctx_place(moe_layer_ctx* ctx, int slot, int layer, int expert);
  *   w_router  [E,H] device, x_dtype; bias [E] fp32 device or NULL
  *   out       [T,H] device in out_dtype (MOE_F32 or MOE_BF16)
  *   stats     host int32[4] or NULL: distinct routed experts, hits, fills, waves
- * Returns after enqueuing the step (the host waited only for the routed set). */
+ *             of this step; -1 for the first two when the layer was fully
+ *             resident (the step did not wait for its routed set; the
+ *             counters of moe_ctx_counters include it once it completed)
+ * Returns after enqueuing the step. A layer with a non-resident expert waits
+ * for its routed set (the residency plan needs it); a fully resident layer
+ * does not wait, and its LRU bookkeeping is replayed, in step order, before
+ * the next plan, moe_ctx_read_tables or moe_ctx_counters. */
 int moe_layer_forward(moe_layer_ctx* ctx, int layer, const void* x, int T, const void* w_router,
                       const float* bias, void* out, int out_dtype, int32_t* stats);
 
 /* moe_ctx_read_tables: host copies of the tables as the plan left them
- * (lut [L*E], owner [S], last_use [S], clock [1]); any pointer may be NULL. */
-int moe_ctx_read_tables(const moe_layer_ctx* ctx, int32_t* lut, int32_t* owner, int64_t* last_use,
+ * (lut [L*E], owner [S], last_use [S], clock [1]); any pointer may be NULL.
+ * Waits for the routed sets of earlier steps whose bookkeeping was deferred. */
+int moe_ctx_read_tables(moe_layer_ctx* ctx, int32_t* lut, int32_t* owner, int64_t* last_use,
                         int64_t* clock);
+
+/* moe_ctx_counters: totals over all steps so far (waits like
+ * moe_ctx_read_tables): out[0] distinct routed experts, out[1] hits,
+ * out[2] fills, out[3] fill waves. */
+int moe_ctx_counters(moe_layer_ctx* ctx, int64_t* out);
 
 /* moe_ctx_outputs: device buffers of the last step, inside the workspace
  * (logits [T,E], topk ids and weights [T,k], perm, offsets [E+1], inv); any

@@ -299,7 +299,8 @@ def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1):
             ysh = [O.expert_forward(x32, w) for w in sh_w]
             ref = O.combine(y_assign, wts, ysh)
             r = rel_l2(out.float().cpu().numpy(), ref)
-            say(f"  rel L2 {r:.3e}; hits {stats.hits} fills {stats.fills} waves {stats.waves}")
+            cnt = layer_obj.counters()
+            say(f"  rel L2 {r:.3e}; totals so far {cnt}")
             assert r <= TOL[shape.wfmt]
 
 
