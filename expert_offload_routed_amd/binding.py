@@ -26,6 +26,7 @@ _vp, _i32, _i64, _u64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctyp
 _SIGNATURES = {
     "moe_route": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_permute": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_permute": (_i32, [_vp, _i32, _vp, _vp] + [_i32] * 5 + [_vp] * 11),
     "moe_slot_layout": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_pack_expert_host": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "moe_ffn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -168,6 +169,28 @@ def moe_permute(topk_ids, E: int, out: dict | None = None, stream=None) -> dict:
           _dev(o["perm"]), _dev(o["inv"]), _dev(o["distinct"]), _dev(o["n_distinct"]),
           _stream(stream))
     return o
+
+
+def moe_route_permute(x, w_router, bias, k: int, renorm: bool = True, sync_counter=None, stream=None):
+    """Route and permute in one call; returns (logits, ids, weights, permutation dict)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    logits = torch.empty(T, E, device=dev, dtype=torch.float32)
+    ids = torch.empty(T, k, device=dev, dtype=torch.int32)
+    w = torch.empty(T, k, device=dev, dtype=torch.float32)
+    o = {n: torch.empty(c, device=dev, dtype=torch.int32) for n, c in (
+        ("counts", E), ("offsets", E + 1), ("perm", max(T * k, 1)), ("inv", max(T * k, 1)),
+        ("distinct", E), ("n_distinct", 1))}
+    if sync_counter is None:
+        sync_counter = torch.zeros(1, device=dev, dtype=torch.int32)
+    if w_router.dtype != x.dtype or tuple(w_router.shape) != (E, H):
+        raise ValueError("moe_route_permute: w_router must be [E, H] in the dtype of x")
+    _call("moe_route_permute", _dev(x), dtype_code(x), _dev(w_router), _dev(bias), T, H, E, k,
+          int(renorm), _dev(logits), _dev(ids), _dev(w), _dev(o["counts"]), _dev(o["offsets"]),
+          _dev(o["perm"]), _dev(o["inv"]), _dev(o["distinct"]), _dev(o["n_distinct"]),
+          _dev(sync_counter), _stream(stream))
+    return logits, ids, w, o
 
 
 # ------------------------------------------------------------ slot layout --

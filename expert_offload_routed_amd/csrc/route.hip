@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kRouteTT = 8;   // tokens per workgroup
 constexpr int kTopkMaxV = 16; // logits per lane (E <= 1024)
+constexpr int kFrontMaxT = 16; // tokens of the one-launch decode front end
 
 template <int FMT>
 __device__ __forceinline__ void load8(const void* base, size_t elem, float out[8]) {
@@ -91,15 +92,12 @@ __device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
   return v > bv || (v == bv && id < bid);
 }
 
-__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int T,
-                                                           int E, int k, int renorm,
-                                                           int32_t* __restrict__ ids,
-                                                           float* __restrict__ weights) {
-  const int wave = threadIdx.x >> 6;
+// Top-k and routing weights of token t; executed by one whole wave.
+// When s_ids is given, the selected ids are also written there (LDS, [t*k + r]).
+__device__ void topk_token(const float* __restrict__ logits, int t, int E, int k, int renorm,
+                           int32_t* __restrict__ ids, float* __restrict__ weights,
+                           int* s_ids = nullptr) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-
   float v[kTopkMaxV];
   uint32_t avail = 0;  // bit i: logit of expert lane + 64 i still selectable
 #pragma unroll
@@ -142,7 +140,10 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
     for (int i = 0; i < kTopkMaxV; ++i)
       if (i == (r >> 6) && lane == (r & 63)) sel[i] = bv;
     if (r == 0) vmax = bv;
-    if (lane == 0) ids[(size_t)t * k + r] = (bid == INT_MAX) ? -1 : bid;
+    if (lane == 0) {
+      ids[(size_t)t * k + r] = (bid == INT_MAX) ? -1 : bid;
+      if (s_ids) s_ids[t * k + r] = (bid == INT_MAX) ? -1 : bid;
+    }
   }
 
   float denom = 0.f;
@@ -161,6 +162,128 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
     const int r = lane + 64 * i;
     if (r < k) weights[(size_t)t * k + r] = expf(sel[i] - vmax) / denom;
   }
+}
+
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int T,
+                                                           int E, int k, int renorm,
+                                                           int32_t* __restrict__ ids,
+                                                           float* __restrict__ weights) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_token(logits, t, E, k, renorm, ids, weights);
+}
+
+// Decode front end in one launch (T <= kFrontMaxT, T*k <= 1024): workgroup e
+// computes the logits of expert e for every token; the last workgroup to
+// finish (a device-scope counter, released and acquired with agent-scope
+// fences) selects the top-k of every token and sorts the assignments by
+// expert in LDS. The counter is left at zero for the next launch.
+template <int FMT>
+__global__ __launch_bounds__(256) void route_front_kernel(
+    const void* __restrict__ x, const void* __restrict__ w,
+    const float* __restrict__ bias, int T, int H, int E, int k, int renorm,
+    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ weights,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, int32_t* __restrict__ distinct, int32_t* __restrict__ n_distinct,
+    unsigned* __restrict__ done) {
+  __shared__ float red[4][kFrontMaxT];
+  __shared__ int s_ids[1024];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1024];
+  __shared__ int s_wave[40];
+  __shared__ unsigned s_last;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int e = blockIdx.x;
+  {
+    float acc[kFrontMaxT];
+#pragma unroll
+    for (int t = 0; t < kFrontMaxT; ++t) acc[t] = 0.f;
+    for (int c = tid * 8; c < H; c += 256 * 8) {
+      float wv[8];
+      load8<FMT>(w, (size_t)e * H + c, wv);
+#pragma unroll
+      for (int t = 0; t < kFrontMaxT; ++t) {
+        if (t < T) {
+          float xv[8];
+          load8<FMT>(x, (size_t)t * H + c, xv);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[t] = fmaf(wv[q], xv[q], acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kFrontMaxT; ++t) {
+      if (t < T) {
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) red[wave][t] = v;
+      }
+    }
+    __syncthreads();
+    if (tid < T) {
+      const float sum = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+      logits[(size_t)tid * E + e] = sum + (bias ? bias[e] : 0.f);
+    }
+  }
+  // publish this workgroup's logits, then count it
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(done, 1u) == gridDim.x - 1) ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();  // see every other workgroup's logits
+
+  // top-k of every token: wave w takes tokens w, w + 4, ...
+  for (int t = wave; t < T; t += 4) topk_token(logits, t, E, k, renorm, ids, weights, s_ids);
+  const int n = T * k;
+  for (int i = tid; i < 1024; i += 256) s_cnt[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) {
+    const int ex = s_ids[i];
+    if (ex >= 0 && ex < E) atomicAdd(&s_cnt[ex], 1);
+  }
+  __syncthreads();
+  // exclusive scan of counts (4 experts per thread) and compaction of the routed set
+  int c4[4], f4[4], csum = 0, fsum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ex = tid * 4 + j;
+    c4[j] = (ex < E) ? s_cnt[ex] : 0;
+    f4[j] = c4[j] > 0 ? 1 : 0;
+    csum += c4[j];
+    fsum += f4[j];
+  }
+  int total = 0, nd = 0;
+  int cbase = block_exclusive_scan(csum, s_wave, &total);
+  int fbase = block_exclusive_scan(fsum, s_wave, &nd);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ex = tid * 4 + j;
+    if (ex < E) {
+      s_off[ex] = cbase;
+      counts[ex] = c4[j];
+      offsets[ex] = cbase;
+      if (f4[j]) distinct[fbase] = ex;
+    }
+    cbase += c4[j];
+    fbase += f4[j];
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    n_distinct[0] = nd;
+  }
+  __syncthreads();
+  // rank of assignment (t, j): tokens before t that picked the same expert
+  for (int f = tid; f < n; f += 256) {
+    const int ex = s_ids[f];
+    if (ex < 0 || ex >= E) continue;
+    const int t = f / k;
+    int rank = 0;
+    for (int i = 0; i < t * k; ++i) rank += (s_ids[i] == ex) ? 1 : 0;
+    const int pos = s_off[ex] + rank;
+    perm[pos] = f;
+    inv[f] = pos;
+  }
+  if (tid == 0) *done = 0u;
 }
 
 }  // namespace
@@ -185,5 +308,33 @@ extern "C" int moe_route(const void* x, int x_dtype, const void* w_router, const
                        T, H, E, logits);
   hipLaunchKernelGGL(topk_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E,
                      k, renorm, topk_ids, topk_w);
+  return moe_launch_status();
+}
+
+extern "C" int moe_route_permute(const void* x, int x_dtype, const void* w_router, const float* bias,
+                                 int T, int H, int E, int k, int renorm, float* logits,
+                                 int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                 int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* distinct,
+                                 int32_t* n_distinct, uint32_t* sync_counter, hipStream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && H > 0 && H % 8 == 0);
+  MOE_CHECK_ARG(k >= 1 && k <= E && E <= 64 * kTopkMaxV);
+  MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
+  MOE_CHECK_ARG(counts && offsets && distinct && n_distinct && sync_counter);
+  if (T > kFrontMaxT || T * k > 1024 || T == 0) {
+    int rc = moe_route(x, x_dtype, w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w,
+                       stream);
+    if (rc != MOE_OK) return rc;
+    return moe_permute(topk_ids, T, k, E, counts, offsets, perm, inv, distinct, n_distinct, stream);
+  }
+  MOE_CHECK_ARG(x && w_router && logits && topk_ids && topk_w && perm && inv);
+  MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)w_router % 16) == 0);
+  if (x_dtype == MOE_BF16)
+    hipLaunchKernelGGL(route_front_kernel<MOE_BF16>, dim3(E), dim3(256), 0, stream, x, w_router,
+                       bias, T, H, E, k, renorm, logits, topk_ids, topk_w, counts, offsets, perm,
+                       inv, distinct, n_distinct, sync_counter);
+  else
+    hipLaunchKernelGGL(route_front_kernel<MOE_F32>, dim3(E), dim3(256), 0, stream, x, w_router,
+                       bias, T, H, E, k, renorm, logits, topk_ids, topk_w, counts, offsets, perm,
+                       inv, distinct, n_distinct, sync_counter);
   return moe_launch_status();
 }

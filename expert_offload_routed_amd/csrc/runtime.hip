@@ -1,7 +1,8 @@
 // Layer runtime: one routed-expert MoE layer step over the slot cache, in C++.
 //
 // Order of a step (all on the caller's compute stream unless noted):
-//   moe_route -> moe_permute -> copy the distinct routed set to pinned host
+//   moe_route_permute (route + permute; one launch for decode batches) -> copy
+//   the distinct routed set to pinned host
 //   memory -> moe_plan_fills on the host tables -> one copy of the wave masks
 //   -> moe_expert_ffn over the groups that are already resident, while the
 //   misses are copied from the pinned host store on the fill stream and
@@ -49,6 +50,7 @@ struct moe_layer_ctx {
   int32_t* ids;
   float* topw;
   int32_t *counts, *offsets, *perm, *inv, *dist;  // dist: distinct[E] then n_distinct
+  uint32_t* sync;  // counter of the one-launch decode front end
   float* y_perm;
   char* ws;
   size_t ws_bytes;
@@ -85,7 +87,7 @@ namespace {
 
 // Device work buffers of a context, carved from the caller's workspace.
 struct CtxLayout {
-  size_t logits, ids, topw, counts, offsets, perm, inv, dist, y_perm, ws, masks;
+  size_t sync, logits, ids, topw, counts, offsets, perm, inv, dist, y_perm, ws, masks;
   size_t sh_perm, sh_offsets, sh_lut, sh_y, sh_ws, total;
   size_t ws_bytes, sh_ws_bytes;
 };
@@ -99,6 +101,7 @@ CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int w_dtype, int n_s
     return at;
   };
   const size_t tk = (size_t)t_max * k;
+  l.sync = take(4);
   l.logits = take((size_t)t_max * E * 4);
   l.ids = take(tk * 4);
   l.topw = take(tk * 4);
@@ -289,6 +292,7 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->fill_e.resize(E); c->fill_s.resize(E); c->fill_w.resize(E);
   c->sh_T = -1;
   char* wb = static_cast<char*>(workspace);
+  c->sync = reinterpret_cast<uint32_t*>(wb + cl.sync);
   c->logits = reinterpret_cast<float*>(wb + cl.logits);
   c->ids = reinterpret_cast<int32_t*>(wb + cl.ids);
   c->topw = reinterpret_cast<float*>(wb + cl.topw);
@@ -324,6 +328,11 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
     bad |= hipEventCreate(&c->tev1[i]) != hipSuccess;
   }
   if (bad) {
+    (void)hipGetLastError();
+    destroy(c);
+    return MOE_EHIP;
+  }
+  if (hipMemset(c->sync, 0, sizeof(uint32_t)) != hipSuccess) {
     (void)hipGetLastError();
     destroy(c);
     return MOE_EHIP;
@@ -414,11 +423,9 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   const int E = c->E, k = c->k, H = c->H, F = c->F;
   int rc;
   hipError_t e;
-  if ((rc = moe_route(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids, c->topw,
-                      c->cs)) != MOE_OK)
-    return rc;
-  if ((rc = moe_permute(c->ids, T, k, E, c->counts, c->offsets, c->perm, c->inv, c->dist,
-                        c->dist + E, c->cs)) != MOE_OK)
+  if ((rc = moe_route_permute(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
+                              c->topw, c->counts, c->offsets, c->perm, c->inv, c->dist,
+                              c->dist + E, c->sync, c->cs)) != MOE_OK)
     return rc;
 
   // the routed set goes to the next ring entry

@@ -102,6 +102,21 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E,
                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                 int32_t* distinct, int32_t* n_distinct, hipStream_t stream);
 
+/* moe_route_permute: moe_route followed by moe_permute (same arguments and
+ * outputs). For decode batches (T <= 16 and T*k <= 1024) both run in one
+ * launch: the workgroups that compute the logits count themselves on
+ * sync_counter and the last one selects and sorts; otherwise the two calls
+ * are made in turn.
+ *   sync_counter  [1] uint32 device; zero before the first call, and every
+ *                 call leaves it zero (calls sharing it must not overlap)
+ */
+int moe_route_permute(const void* x, int x_dtype, const void* w_router, const float* bias,
+                      int T, int H, int E, int k, int renorm,
+                      float* logits, int32_t* topk_ids, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                      int32_t* distinct, int32_t* n_distinct, uint32_t* sync_counter,
+                      hipStream_t stream);
+
 /* ------------------------------------------------------------- slot layout -
  * The byte layout of one expert inside a slot (and inside the pinned host
  * store, which holds the same bytes so a fill is one contiguous copy). The

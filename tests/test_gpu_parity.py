@@ -80,6 +80,32 @@ def test_route_rejects_bad_args():
         B.moe_route(x[:, :250].contiguous(), wr[:, :250].contiguous(), b, 2)  # H % 8 != 0
 
 
+@pytest.mark.parametrize("shape,T", [(TINY, 16), (TINY, 1), (W.reduced(MIX, H=4096), 5),
+                                     (W.reduced(DSV3, H=7168), 16), (W.reduced(DSV3, H=512), 40),
+                                     (W.reduced(TINY, E=64, k=64, H=64), 16),
+                                     (W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), E=1000, k=16, H=512), 9)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_route_permute_fused(shape, T):
+    """One-launch front end (T <= 16) and its two-call fallback: same bar as the separate stages."""
+    say(f"route_permute {shape.name} T={T}")
+    counter = torch.zeros(1, dtype=torch.int32, device=_dev())
+    for rep in range(3):  # the counter must come back to zero after every call
+        x = W.tokens(shape, T, step=rep, device=_dev())
+        wr, b = W.router(shape, device=_dev())
+        logits, ids, w, p = B.moe_route_permute(x, wr, b, shape.k, sync_counter=counter)
+        torch.cuda.synchronize()
+        assert counter.item() == 0
+        check_routing(x, wr, b, shape.k, logits, ids, w)
+        ref = O.permute(ids.cpu().numpy(), shape.E)
+        n = T * shape.k
+        assert p["counts"].cpu().numpy().tolist() == ref["counts"].tolist()
+        assert p["offsets"].cpu().numpy().tolist() == ref["offsets"].tolist()
+        assert p["perm"].cpu().numpy()[:n].tolist() == ref["perm"].tolist()
+        assert p["inv"].cpu().numpy()[:n].tolist() == ref["inv"].tolist()
+        nd = int(p["n_distinct"].item())
+        assert p["distinct"].cpu().numpy()[:nd].tolist() == ref["distinct"].tolist()
+
+
 # -------------------------------------------------------------- permutation --
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (16, 8, 2), (513, 64, 6), (4096, 256, 8),
                                    (77, 1024, 16), (3, 1, 1)])
