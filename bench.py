@@ -46,32 +46,43 @@ def expert_bytes(shape) -> int:
     return 3 * shape.H * shape.F * es
 
 
-def timed(layer, shape, T, steps, warmup, label, ffn_timing=False):
-    """Warm up, then time exactly ``steps`` layer steps between two device synchronisations."""
-    xs = [W.tokens(shape, T, step=i, device="cuda") for i in range(steps + warmup)]
-    out = torch.empty(T, shape.H, dtype=layer.out_dtype, device="cuda")
-    for x in xs[:warmup]:
-        layer.forward(x, out=out)
-    torch.cuda.synchronize()
-    layer.ctx.set_timing(ffn_timing)
+def _run(layer, xs, out, timing):
+    layer.ctx.set_timing(timing)
     c0 = layer.counters()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for x in xs[warmup:]:
+    for x in xs:
         layer.forward(x, out=out)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     c1 = layer.counters()
-    distinct = (c1["distinct"] - c0["distinct"]) / steps
+    ms, n = layer.ctx.ffn_time()
+    layer.ctx.set_timing(False)
+    return dt, {k: c1[k] - c0[k] for k in c1}, ms, n
+
+
+def timed(layer, shape, T, steps, warmup, label, ffn_timing=False):
+    """Warm up, then time exactly ``steps`` layer steps between two device synchronisations.
+
+    With ffn_timing, the same steps run a second time with HIP events recorded on
+    the compute stream around each step's routed expert FFN (moe_expert_ffn), the
+    dominant kernel; the headline rate comes from the pass without events.
+    """
+    xs = [W.tokens(shape, T, step=i, device="cuda") for i in range(steps + warmup)]
+    out = torch.empty(T, shape.H, dtype=layer.out_dtype, device="cuda")
+    for x in xs[:warmup]:
+        layer.forward(x, out=out)
+    dt, cnt, _, _ = _run(layer, xs[warmup:], out, False)
+    distinct = cnt["distinct"] / steps
     res = {"tokens_per_step": T, "tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3,
-           "distinct_per_step": distinct, "fills_per_step": (c1["fills"] - c0["fills"]) / steps}
+           "distinct_per_step": distinct, "fills_per_step": cnt["fills"] / steps}
     if ffn_timing:
-        ms, n = layer.ctx.ffn_time()
-        layer.ctx.set_timing(False)
+        dt2, cnt2, ms, n = _run(layer, xs[warmup:], out, True)
         # algorithmic bytes of the expert FFN per step: the routed experts' weights
         # (every distinct expert is read once), tokens in, one fp32 row out per assignment
-        byts = distinct * expert_bytes(shape) + T * shape.H * 2 + T * shape.k * shape.H * 4
+        byts = (cnt2["distinct"] / steps) * expert_bytes(shape) + T * shape.H * 2 + T * shape.k * shape.H * 4
         res["ffn"] = {"calls": n, "avg_us": 1e3 * ms / n, "avg_bytes": byts,
-                      "gbs": byts / (ms / n * 1e-3) / 1e9}
+                      "gbs": byts / (ms / n * 1e-3) / 1e9, "ms_per_step_with_events": dt2 / steps * 1e3}
     print(f"# {label}: {res}", file=sys.stderr, flush=True)
     return res
 

@@ -1,9 +1,9 @@
 // Layer runtime: one routed-expert MoE layer step over the slot cache, in C++.
 //
 // Order of a step (all on the caller's compute stream unless noted):
-//   moe_route_permute (route + permute; one launch for decode batches) -> copy
-//   the distinct routed set to pinned host
-//   memory -> moe_plan_fills on the host tables -> one copy of the wave masks
+//   moe_route_permute (route + permute; one launch for decode batches), which
+//   stores the distinct routed set straight into mapped pinned host memory ->
+//   moe_plan_fills on the host tables -> one copy of the wave masks
 //   -> moe_expert_ffn over the groups that are already resident, while the
 //   misses are copied from the pinned host store on the fill stream and
 //   committed with their tags -> moe_expert_ffn over each wave of filled
@@ -61,7 +61,8 @@ struct moe_layer_ctx {
   size_t sh_ws_bytes;
   int sh_T;  // T the shared permutation was built for
   // host state
-  int32_t* ring_h;  // pinned [kRing][E+1]: routed sets of steps
+  int32_t* ring_h;  // pinned [kRing][E+1]: routed sets of steps (written by the device)
+  int32_t* ring_d;  // device address of ring_h
   hipEvent_t ring_ev[kRing];
   int ring_layer[kRing];
   int ring_head, ring_count;  // deferred entries: ring_head .. ring_head + count - 1
@@ -314,8 +315,12 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
     c->sh_ws_bytes = cl.sh_ws_bytes;
   }
   int bad = 0;
+  // coherent, mapped: the permutation kernel stores the routed set straight into it
   bad |= hipHostMalloc(reinterpret_cast<void**>(&c->ring_h),
-                       (size_t)kRing * (E + 1) * sizeof(int32_t)) != hipSuccess;
+                       (size_t)kRing * (E + 1) * sizeof(int32_t),
+                       hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess;
+  if (!bad) bad |= hipHostGetDevicePointer(reinterpret_cast<void**>(&c->ring_d), c->ring_h, 0) !=
+                   hipSuccess;
   bad |= hipHostMalloc(reinterpret_cast<void**>(&c->masks_h),
                        (size_t)(E + 2) * E * sizeof(int32_t)) != hipSuccess;
   bad |= hipHostMalloc(reinterpret_cast<void**>(&c->sh_rows_h),
@@ -423,19 +428,16 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   const int E = c->E, k = c->k, H = c->H, F = c->F;
   int rc;
   hipError_t e;
-  if ((rc = moe_route_permute(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
-                              c->topw, c->counts, c->offsets, c->perm, c->inv, c->dist,
-                              c->dist + E, c->sync, c->cs)) != MOE_OK)
-    return rc;
-
-  // the routed set goes to the next ring entry
+  // the routed set is written by the device into the next ring entry (pinned host memory)
   if (c->ring_count == kRing && (rc = drain(c)) != MOE_OK) return rc;
   const int r = c->ring_next;
   int32_t* dh = c->ring_h + (size_t)r * (E + 1);
-  if ((e = hipMemcpyAsync(dh, c->dist, (E + 1) * sizeof(int32_t), hipMemcpyDeviceToHost, c->cs)) !=
-          hipSuccess ||
-      (e = hipEventRecord(c->ring_ev[r], c->cs)) != hipSuccess)
-    return moe_hip_status(e);
+  int32_t* dd = c->ring_d + (size_t)r * (E + 1);
+  if ((rc = moe_route_permute(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
+                              c->topw, c->counts, c->offsets, c->perm, c->inv, dd, dd + E, c->sync,
+                              c->cs)) != MOE_OK)
+    return rc;
+  if ((e = hipEventRecord(c->ring_ev[r], c->cs)) != hipSuccess) return moe_hip_status(e);
   c->ring_next = (r + 1) % kRing;
   const bool all_resident = c->resident[layer] == E;
 
