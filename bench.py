@@ -121,6 +121,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--case", default=None, choices=["decode1", "decode8", "prefill512", "fills"],
+                    help="run one case of the workload only (for profiling); prints no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU form of "
@@ -132,6 +134,17 @@ def main():
 
     resident = W.initial_residency(shape, shape.E, "random")  # all 8 experts, relabelled slots
     layer = Hn.SlotCacheLayer(shape, shape.E, resident, t_max=512)
+    if args.case is not None:
+        if args.case == "fills":
+            cfg = W.WORKLOADS[WORKLOAD]
+            small = Hn.SlotCacheLayer(shape, cfg["slots"][0],
+                                      W.initial_residency(shape, cfg["slots"][0], "random"), t_max=8,
+                                      store=layer.store)
+            timed(small, shape, 1, K, Wm, "decode T=1, 4 of 8 resident, fills over PCIe")
+        else:
+            T = {"decode1": 1, "decode8": 8, "prefill512": 512}[args.case]
+            timed(layer, shape, T, K, Wm, args.case, ffn_timing=True)
+        return
     head = timed(layer, shape, 1, K, Wm, "decode T=1 hit path", ffn_timing=True)
     also = {}
     if not args.quick:

@@ -11,9 +11,10 @@
 //   pass 2: A = h rows (bf16), W = W2 of the slot, epilogue y[p][n] fp32.
 // Tiles: BM = 64 rows x BN = 128 weight rows x BK = 64, 4 waves in a 2x2
 // layout, each wave 32 x 64 = two v_mfma_f32_32x32x16_bf16 accumulators.
-// A and W tiles are staged through LDS (rows padded to 72 elements) with a
-// register prefetch of the next K tile, so each weight element is fetched
-// from HBM once per M-tile and reused for the tile's 64 rows from LDS.
+// A and W tiles are staged through LDS (rows padded to 72 elements, 8 lanes
+// per coalesced 128-byte row segment); global loads run kAhead K-tiles ahead
+// through a ring of register stages, so each weight element is fetched from
+// HBM once per M-tile and reused for the tile's 64 rows from LDS.
 // Lane layouts (checked on gfx950): A/B operand lane l holds row l % 32,
 // k = 8 (l / 32) .. +7; accumulator r holds row 8 (r / 4) + 4 (l / 32) + r % 4,
 // column l % 32.
@@ -29,6 +30,7 @@ constexpr int BM = kGemmBM;
 constexpr int BN = 128;
 constexpr int BK = 64;
 constexpr int LDS_LD = BK + 8;  // padded row (elements)
+constexpr int kAhead = 3;       // K-tiles of global loads in flight per thread
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
 
@@ -70,21 +72,27 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     brow[i] = reinterpret_cast<const uint16_t*>(wbase) + (size_t)n * K;
   }
 
-  u32x4 ra[2], rb[4];
-  auto gload = [&](int kt) {
+  // register stages: tile kt + kAhead is loaded while tile kt is computed and
+  // tile kt + 1 is written to LDS, so every global load has kAhead - 1 full
+  // compute iterations to land
+  struct Stage {
+    u32x4 a[2], b[4];
+  };
+  Stage st[kAhead];
+  auto gload = [&](Stage& r, int kt) {
     const int kk = kt * BK + lcol;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ra[i] = avalid[i] ? ld16(arow[i] + kk) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 2; ++i) r.a[i] = avalid[i] ? ld16(arow[i] + kk) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rb[i] = ld16_stream(brow[i] + kk);
+    for (int i = 0; i < 4; ++i) r.b[i] = ld16_stream(brow[i] + kk);
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const Stage& r, int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(&sA[buf][(lrow + 32 * i) * LDS_LD + lcol]) = ra[i];
+      *reinterpret_cast<u32x4*>(&sA[buf][(lrow + 32 * i) * LDS_LD + lcol]) = r.a[i];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&sB[buf][(lrow + 32 * i) * LDS_LD + lcol]) = rb[i];
+      *reinterpret_cast<u32x4*>(&sB[buf][(lrow + 32 * i) * LDS_LD + lcol]) = r.b[i];
   };
 
   floatx16 acc[2];
@@ -94,12 +102,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 
   const int nk = K / BK;
-  gload(0);
-  sstore(0);
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s)
+    if (s < nk) gload(st[s], s);
+  sstore(st[0], 0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
+  // iteration kt: refill stage kt % kAhead with tile kt + kAhead, compute LDS
+  // buffer kt % 2, write tile kt + 1 (stage (kt + 1) % kAhead) to the other buffer
+  auto step = [&](Stage& mine, Stage& next, int kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    if (kt + kAhead < nk) gload(mine, kt + kAhead);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kc = ks * 16 + 8 * (lane >> 5);
@@ -111,8 +123,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
       }
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    if (kt + 1 < nk) sstore(next, buf ^ 1);
     __syncthreads();
+  };
+  for (int kt = 0; kt < nk; kt += kAhead) {
+#pragma unroll
+    for (int s = 0; s < kAhead; ++s)
+      if (kt + s < nk) step(st[s], st[(s + 1) % kAhead], kt + s);
   }
 
   // epilogue
