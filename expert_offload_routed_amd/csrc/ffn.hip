@@ -12,9 +12,11 @@
 //   ffn_plan_kernel  one workgroup: selected, non-empty, resident groups go to
 //                    the GEMV list (<= kGemvMaxRows rows) or are cut into
 //                    kGemmBM-row MFMA tiles; absent experts set MOE_ERR_ABSENT.
-//   GEMV passes      (ffn_gemv.h) decode groups: weight rows streamed once per
-//                    token tile with non-temporal 16-byte loads, split-K over
-//                    the waves of a workgroup; HBM-bound.
+//   GEMV passes      decode groups: tile-major bf16 weights (tile_gemv.h),
+//                    every load a contiguous 1 KB chunk, split-K over the
+//                    waves of a workgroup; row-major fp32 weights
+//                    (ffn_gemv.h). Weights are streamed once per token tile
+//                    with non-temporal 16-byte loads; HBM-bound.
 //   GEMM passes      (gemm.hip) groups with more rows: bf16 MFMA tiles.
 // The SwiGLU intermediate h lives in the workspace: bf16 with bf16 weights
 // (the A operand of the second MFMA pass), fp32 with fp32 weights.
@@ -23,6 +25,7 @@
 #include "common.h"
 #include "ffn_gemv.h"
 #include "ffn_internal.h"
+#include "tile_gemv.h"
 
 namespace {
 
@@ -78,19 +81,69 @@ void launch_pass(const void* act, const int32_t* perm, int k, const FfnItem* ite
                      out_ld, (int)rb, out);
 }
 
-// bf16 tokens and weights: GEMV for small groups, MFMA tiles for the rest.
+// One tile-major bf16 GEMV pass: KS waves per RBW row blocks.
+template <int KS, int RBW, int MAXNT, bool SWIGLU, int AF, int OF>
+void launch_tile_pass(const void* act, const int32_t* perm, int k, const FfnItem* items,
+                      const int32_t* n_items, int max_items, const char* pool, size_t stride,
+                      size_t off, int R, int K, int out_ld, void* out, hipStream_t s) {
+  constexpr int NW = KS < 4 ? 4 : KS;
+  constexpr int rb_per_wg = NW / KS * RBW;
+  const int upi = (R / 32 + rb_per_wg - 1) / rb_per_wg;
+  const long long units = (long long)upi * max_items;
+  const unsigned grid = (unsigned)(units < tgemv::kGridCap ? units : tgemv::kGridCap);
+  if (grid == 0) return;
+  constexpr int U = (KS == 16 && MAXNT >= 4) ? 2 : 4;  // stay within 128 VGPRs at 1024 threads
+  hipLaunchKernelGGL((tgemv::bf16_kernel<AF, OF, KS, RBW, NW, U, MAXNT, SWIGLU>), dim3(grid),
+                     dim3(NW * 64), 0, s, act, perm, k, items, n_items, pool, stride, off, R, K,
+                     out_ld, upi, out);
+}
+
+template <int RBW, int MAXNT, bool SWIGLU, int AF, int OF>
+void launch_tile_ks(int ks, const void* act, const int32_t* perm, int k, const FfnItem* items,
+                    const int32_t* n_items, int max_items, const char* pool, size_t stride,
+                    size_t off, int R, int K, int out_ld, void* out, hipStream_t s) {
+#define MOE_TILE_KS(KS_)                                                                         \
+  launch_tile_pass<KS_, RBW, MAXNT, SWIGLU, AF, OF>(act, perm, k, items, n_items, max_items, pool, \
+                                                    stride, off, R, K, out_ld, out, s)
+  switch (ks) {
+    case 1: MOE_TILE_KS(1); break;
+    case 2: MOE_TILE_KS(2); break;
+    case 4: MOE_TILE_KS(4); break;
+    case 8: MOE_TILE_KS(8); break;
+    default:
+      if constexpr (RBW == 1) MOE_TILE_KS(16);  // 1024-thread groups: 128 VGPRs, RBW = 1 only
+      else MOE_TILE_KS(8);
+      break;
+  }
+#undef MOE_TILE_KS
+}
+
+template <int MAXNT, bool SWIGLU, int AF, int OF>
+void launch_tile_any(const void* act, const int32_t* perm, int k, const FfnItem* items,
+                     const int32_t* n_items, int max_items, const char* pool, size_t stride,
+                     size_t off, int R, int K, int out_ld, void* out, hipStream_t s) {
+  const tgemv::Split sp = tgemv::choose_split_bf16(R / 32 * max_items, K / 16, MAXNT);
+  if (sp.rbw == 1)
+    launch_tile_ks<1, MAXNT, SWIGLU, AF, OF>(sp.ks, act, perm, k, items, n_items, max_items, pool,
+                                             stride, off, R, K, out_ld, out, s);
+  else
+    launch_tile_ks<2, MAXNT, SWIGLU, AF, OF>(sp.ks, act, perm, k, items, n_items, max_items, pool,
+                                             stride, off, R, K, out_ld, out, s);
+}
+
+// bf16 tokens and weights: tile-major GEMV for small groups, MFMA tiles for the rest.
 template <int MAXNT>
 void launch_bf16(const void* x, const int32_t* perm, int k, const FfnItem* items,
                  const int32_t* n_items, int max_items, const GemmTile* tiles,
                  const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
                  const SlotLayout& lay, int H, int F, void* hbuf, float* y, hipStream_t s) {
-  launch_pass<MOE_BF16, MOE_BF16, MOE_BF16, 4, 2, 2, MAXNT, true>(
-      x, perm, k, items, n_items, max_items, pool, stride, lay.off_w13, 2 * F, H, F, hbuf, s);
+  launch_tile_any<MAXNT, true, MOE_BF16, MOE_BF16>(x, perm, k, items, n_items, max_items, pool,
+                                                   stride, lay.off_w13, 2 * F, H, F, hbuf, s);
   if (max_tiles > 0)
     launch_gemm_bf16(1, x, perm, k, tiles, n_tiles, max_tiles, pool, stride, lay.off_w13, 2 * F, H,
                      F, hbuf, s);
-  launch_pass<MOE_BF16, MOE_BF16, MOE_F32, 4, 4, 1, MAXNT, false>(
-      hbuf, perm, k, items, n_items, max_items, pool, stride, lay.off_w2, H, F, H, y, s);
+  launch_tile_any<MAXNT, false, MOE_BF16, MOE_F32>(hbuf, perm, k, items, n_items, max_items,
+                                                   pool, stride, lay.off_w2, H, F, H, y, s);
   if (max_tiles > 0)
     launch_gemm_bf16(2, hbuf, perm, k, tiles, n_tiles, max_tiles, pool, stride, lay.off_w2, H, F, H,
                      y, s);

@@ -14,12 +14,14 @@
 // Codes are used in offset form u = q + 8 (0..15: bytes that are valid
 // non-negative int8 for sdot4 and the int8 MFMA); sum q x = sum u x - 8 sum x,
 // where sum x over a 128-value group is precomputed per activation row.
-// Slot word order (moe_slot_layout): a 32-bit word holds 8 consecutive codes,
-// low nibbles = codes 0..3, high nibbles = codes 4..7, so
+// Slot layout (moe_slot_layout): tile-major 1 KB chunks of 32 rows x 64 codes;
+// a 32-bit word holds 8 consecutive codes, low nibbles = codes 0..3, high
+// nibbles = codes 4..7, so
 //   u_lo = (w ^ 0x88888888) & 0x0F0F0F0F, u_hi = ((w ^ 0x88888888) >> 4) & 0x0F0F0F0F
 // are two words of 4 consecutive int8 values in natural order.
 #include "common.h"
 #include "ffn_internal.h"
+#include "tile_gemv.h"
 
 namespace {
 
@@ -109,150 +111,19 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   }
 }
 
-// ------------------------------------------------------------- int4 GEMV ---
-// Same decomposition as the dense decode GEMV: a workgroup owns RPW * (4/KS)
-// rows; KS waves split K in 2048-value chunks (16 code bytes per lane).
-template <int RPW, int KS, int NT, bool SWIGLU>
-__device__ __forceinline__ void gemv_tile(const char* __restrict__ codes, size_t rowb,
-                                          const uint16_t* __restrict__ scales, int sld, int K,
-                                          const int8_t* __restrict__ aq,
-                                          const float* __restrict__ as,
-                                          const int32_t* __restrict__ ag,
-                                          const int32_t* __restrict__ perm, int k, int prow,
-                                          int r0, bool store, int out_ld, float* __restrict__ out,
-                                          float* __restrict__ red) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int slice = wave % KS;
-  int arow[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) arow[t] = SWIGLU ? perm[prow + t] / k : prow + t;
-  float acc[RPW][NT];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
-  const int gld = K / 128;
-  const int nchunks = (K + 2047) / 2048;
-  for (int c = slice; c < nchunks; c += KS) {
-    const int e = c * 2048 + lane * 32;
-    if (e < K) {
-      const int g = e >> 7;
-      u32x4 cw[RPW];
-      float sw[RPW];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        cw[r] = ld16_stream(codes + r * rowb + (e >> 1));
-        sw[r] = bf16_to_f32(scales[(size_t)r * sld + g]);
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int8_t* ap = aq + (size_t)arow[t] * K + e;
-        const u32x4 xa = ld16(ap), xb = ld16(ap + 16);
-        const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-        const int gs = ((lane & 3) == 0) ? ag[(size_t)arow[t] * gld + g] : 0;
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          const uint32_t w[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
-          int is = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            is = __builtin_amdgcn_sdot4((int)u_lo(w[i]), (int)xw[2 * i], is, false);
-            is = __builtin_amdgcn_sdot4((int)u_hi(w[i]), (int)xw[2 * i + 1], is, false);
-          }
-          acc[r][t] = fmaf((float)(is - 8 * gs), sw[r], acc[r][t]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[r][t] = wave_sum(acc[r][t]);
-  if constexpr (KS > 1) {
-    if (lane == 0) {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) red[(wave * RPW + r) * NT + t] = acc[r][t];
-    }
-    __syncthreads();
-    if (slice == 0) {
-#pragma unroll
-      for (int s2 = 1; s2 < KS; ++s2)
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-          for (int t = 0; t < NT; ++t) acc[r][t] += red[((wave + s2) * RPW + r) * NT + t];
-    }
-    __syncthreads();
-  }
-  if (store && slice == 0 && lane < NT) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (lane == t) {
-        const float sx = as[arow[t]];
-        float* o = out + (size_t)(prow + t) * out_ld;
-        if constexpr (SWIGLU) {
-#pragma unroll
-          for (int r = 0; r < RPW; r += 2) o[(r0 + r) / 2] = silu(acc[r][t] * sx) * (acc[r + 1][t] * sx);
-        } else {
-#pragma unroll
-          for (int r = 0; r < RPW; ++r) o[r0 + r] = acc[r][t] * sx;
-        }
-      }
-    }
-  }
-}
-
-template <int RPW, int KS, int MAXNT, bool SWIGLU>
-__global__ __launch_bounds__(256) void gemv_w4a8_kernel(
-    const int8_t* __restrict__ aq, const float* __restrict__ as, const int32_t* __restrict__ ag,
-    const int32_t* __restrict__ perm, int k, const FfnItem* __restrict__ items,
-    const int32_t* __restrict__ n_items, const char* __restrict__ pool, size_t stride,
-    size_t off_codes, size_t off_scales, int rows, int K, int out_ld, int row_blocks,
-    float* __restrict__ out) {
-  __shared__ float red[4 * RPW * MAXNT];
-  constexpr int kBlocksPerWg = 4 / KS;
-  const size_t rowb = (size_t)K / 2;
-  const int sld = K / 128;
-  const int wave = threadIdx.x >> 6;
-  const int units = n_items[0] * row_blocks;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const int item = u / row_blocks;
-    const int rb = u - item * row_blocks;
-    const FfnItem it = items[item];
-    int r0 = (rb * kBlocksPerWg + wave / KS) * RPW;
-    const bool store = r0 < rows;
-    if (!store) r0 = 0;
-    const char* slot = pool + (size_t)it.slot * stride;
-    const char* codes = slot + off_codes + (size_t)r0 * rowb;
-    const uint16_t* scales = reinterpret_cast<const uint16_t*>(slot + off_scales) + (size_t)r0 * sld;
-    int done = 0;
-    for (; it.rows - done >= MAXNT; done += MAXNT)
-      gemv_tile<RPW, KS, MAXNT, SWIGLU>(codes, rowb, scales, sld, K, aq, as, ag, perm, k,
-                                        it.row_begin + done, r0, store, out_ld, out, red);
-    const int rest = it.rows - done, p = it.row_begin + done;
-#define MOE_W4_TILE(NT_)                                                                       \
-  gemv_tile<RPW, KS, NT_, SWIGLU>(codes, rowb, scales, sld, K, aq, as, ag, perm, k, p, r0, store, \
-                                  out_ld, out, red)
-    if constexpr (MAXNT > 1) {
-      if (rest == 1) MOE_W4_TILE(1);
-    }
-    if constexpr (MAXNT > 2) {
-      if (rest == 2) MOE_W4_TILE(2);
-      if (rest == 3) MOE_W4_TILE(3);
-    }
-#undef MOE_W4_TILE
-  }
-}
-
 // -------------------------------------------------------- int8 MFMA GEMM ---
-constexpr int QBM = kGemmBM;  // 64 activation rows
-constexpr int QBN = 128;      // weight rows
-constexpr int QBK = 128;      // one scale group
-constexpr int A_LD = QBK + 16;      // bytes per staged activation row
-constexpr int B_LD = QBK / 2 + 16;  // bytes per staged code row
+constexpr int QBM = kGemmBM;  // activation rows of a tile
+constexpr int QMF = QBM / 32;
+constexpr int QBK = 128;      // one scale group per K tile
+constexpr int A_LD = QBK + 16;  // bytes per staged activation row
+constexpr int kQAhead = 3;      // K tiles of global loads in flight
 
+// Tiles: 128 activation rows x 128 weight rows (four 32-row blocks of the
+// tile-major codes, one per wave), K tiles of 128 = one scale group. A wave's
+// code fragments for a K tile are two whole 1 KB chunks (one 16-byte load per
+// lane each, cacheable so the M-tiles of a group share them in L2); the int8
+// activation tile and its group sums go through LDS. Each K tile: 4 v_mfma_i32_32x32x32_i8 per 32x32
+// accumulator into int32, then folded into fp32 with the group scale.
 template <int PASS>
 __global__ __launch_bounds__(256) void gemm_w4a8_kernel(
     const int8_t* __restrict__ aq, const float* __restrict__ as, const int32_t* __restrict__ ag,
@@ -260,30 +131,25 @@ __global__ __launch_bounds__(256) void gemm_w4a8_kernel(
     const int32_t* __restrict__ n_tiles, const char* __restrict__ pool, size_t stride,
     size_t off_codes, size_t off_scales, int N, int K, int out_ld, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) int8_t sA[2][QBM * A_LD];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][QBN * B_LD];
-  __shared__ float sS[2][QBN];
   __shared__ int sG[2][QBM];
   if ((int)blockIdx.y >= n_tiles[0]) return;
   const GemmTile tl = tiles[blockIdx.y];
-  const int n0 = blockIdx.x * QBN;
-  if (n0 >= N) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int nrb = N / 32;
+  if ((int)blockIdx.x * 4 >= nrb) return;
   const int gld = K / 128;
 
   // activation rows staged by this thread: (tid >> 3) + 32 i, 16 bytes at (tid & 7) * 16
-  const int8_t* arow[2];
-  bool avalid[2];
-  int arowid[2];
+  const int8_t* arow[QMF];
+  bool avalid[QMF];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < QMF; ++i) {
     const int m = (tid >> 3) + 32 * i;
     avalid[i] = m < tl.rows;
     const int p = tl.row_begin + (avalid[i] ? m : 0);
-    arowid[i] = (PASS == 1) ? perm[p] / k : p;
-    arow[i] = aq + (size_t)arowid[i] * K;
+    arow[i] = aq + (size_t)((PASS == 1) ? perm[p] / k : p) * K;
   }
-  // gsum row for the epilogue of a K tile: threads 0..63 own row tid
+  // group-sum row of threads 0..QBM-1
   int grow = 0;
   bool gvalid = false;
   if (tid < QBM) {
@@ -291,161 +157,168 @@ __global__ __launch_bounds__(256) void gemm_w4a8_kernel(
     const int p = tl.row_begin + (gvalid ? tid : 0);
     grow = (PASS == 1) ? perm[p] / k : p;
   }
-  // code rows: (tid >> 2) + 64 i, 16 bytes at (tid & 3) * 16
+  // this wave's 32-row block
+  int rb = blockIdx.x * 4 + wave;
+  const bool nvalid = rb < nrb;
+  if (!nvalid) rb = nrb - 1;
   const char* slot = pool + (size_t)tl.slot * stride;
-  const char* brow[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int n = n0 + (tid >> 2) + 64 * i;
-    if (n >= N) n = N - 1;
-    brow[i] = slot + off_codes + (size_t)n * (K / 2);
-  }
-  const uint16_t* scl = reinterpret_cast<const uint16_t*>(slot + off_scales);
-  int sn = n0 + (tid & 127);
-  if (sn >= N) sn = N - 1;
+  const char* wchunks = slot + off_codes + (size_t)rb * (K / 64) * 1024 + lane * 16;
+  const int n = rb * 32 + (lane & 31);
+  const uint16_t* srow = reinterpret_cast<const uint16_t*>(slot + off_scales) + (size_t)n * gld;
 
-  u32x4 ra[2], rb[2];
-  float rs = 0.f;
-  int rg = 0;
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      ra[i] = avalid[i] ? ld16(arow[i] + kt * QBK + (tid & 7) * 16) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) rb[i] = ld16_stream(brow[i] + kt * (QBK / 2) + (tid & 3) * 16);
-    if (tid < QBN) rs = bf16_to_f32(scl[(size_t)sn * gld + kt]);
-    if (tid < QBM) rg = gvalid ? ag[(size_t)grow * gld + kt] : 0;
+  struct Stage {
+    u32x4 a[QMF], b[2];
+    float sw;
+    int g;
   };
-  auto sstore = [&](int buf) {
+  Stage st[kQAhead];
+  auto gload = [&](Stage& r, int kt) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(&sA[buf][((tid >> 3) + 32 * i) * A_LD + (tid & 7) * 16]) = ra[i];
+    for (int i = 0; i < QMF; ++i)
+      r.a[i] = avalid[i] ? ld16(arow[i] + kt * QBK + (tid & 7) * 16) : u32x4{0u, 0u, 0u, 0u};
+    // cacheable: the other M-tiles of the group read the same chunks
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(&sB[buf][((tid >> 2) + 64 * i) * B_LD + (tid & 3) * 16]) = rb[i];
-    if (tid < QBN) sS[buf][tid] = rs;
-    if (tid < QBM) sG[buf][tid] = rg;
+    for (int c = 0; c < 2; ++c) r.b[c] = ld16(wchunks + (size_t)(2 * kt + c) * 1024);
+    r.sw = bf16_to_f32(srow[kt]);
+    r.g = (tid < QBM && gvalid) ? ag[(size_t)grow * gld + kt] : 0;
   };
+  auto astore = [&](const Stage& r, int buf) {
+#pragma unroll
+    for (int i = 0; i < QMF; ++i)
+      *reinterpret_cast<u32x4*>(&sA[buf][((tid >> 3) + 32 * i) * A_LD + (tid & 7) * 16]) = r.a[i];
+    if (tid < QBM) sG[buf][tid] = r.g;
+  };
+  const int live = (tl.rows + 31) / 32;
 
-  float accf[2][16];
+  float accf[QMF][16];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < QMF; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) accf[j][r] = 0.f;
 
   const int nk = K / QBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    intx16 acci[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int s2 = 0; s2 < kQAhead; ++s2)
+    if (s2 < nk) gload(st[s2], s2);
+  astore(st[0], 0);
+  __syncthreads();
+  auto step = [&](Stage& mine, Stage& next, int kt) {
+    const int buf = kt & 1;
+    intx16 acci[QMF];
+#pragma unroll
+    for (int j = 0; j < QMF; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acci[j][r] = 0;
 #pragma unroll
     for (int ks = 0; ks < QBK / 32; ++ks) {
-      const intx4 a = *reinterpret_cast<const intx4*>(
-          &sA[buf][(wm * 32 + (lane & 31)) * A_LD + ks * 32 + 16 * (lane >> 5)]);
+      const u32x4& cw = mine.b[ks >> 1];
+      const uint32_t w0 = (ks & 1) ? cw.z : cw.x, w1 = (ks & 1) ? cw.w : cw.y;
+      intx4 b;
+      b[0] = (int)u_lo(w0);
+      b[1] = (int)u_hi(w0);
+      b[2] = (int)u_lo(w1);
+      b[3] = (int)u_hi(w1);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint2 w = *reinterpret_cast<const uint2*>(
-            &sB[buf][(wn * 64 + j * 32 + (lane & 31)) * B_LD + ks * 16 + 8 * (lane >> 5)]);
-        intx4 b;
-        b[0] = (int)u_lo(w.x);
-        b[1] = (int)u_hi(w.x);
-        b[2] = (int)u_lo(w.y);
-        b[3] = (int)u_hi(w.y);
-        acci[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acci[j], 0, 0, 0);
+      for (int j = 0; j < QMF; ++j) {
+        if (j < live) {
+          const intx4 a = *reinterpret_cast<const intx4*>(
+              &sA[buf][(j * 32 + (lane & 31)) * A_LD + ks * 32 + 16 * (lane >> 5)]);
+          acci[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acci[j], 0, 0, 0);
+        }
       }
     }
     // fold this scale group into fp32: (sum u x - 8 sum x) * s_w
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float sw = sS[buf][wn * 64 + j * 32 + (lane & 31)];
+    for (int j = 0; j < QMF; ++j)
+      if (j < live)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        accf[j][r] = fmaf((float)(acci[j][r] - 8 * sG[buf][m]), sw, accf[j][r]);
+        const int m = j * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        accf[j][r] = fmaf((float)(acci[j][r] - 8 * sG[buf][m]), mine.sw, accf[j][r]);
       }
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    if (kt + kQAhead < nk) gload(mine, kt + kQAhead);
+    if (kt + 1 < nk) astore(next, buf ^ 1);
     __syncthreads();
+  };
+  for (int kt = 0; kt < nk; kt += kQAhead) {
+#pragma unroll
+    for (int s2 = 0; s2 < kQAhead; ++s2)
+      if (kt + s2 < nk) step(st[s2], st[(s2 + 1) % kQAhead], kt + s2);
   }
 
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < QMF; ++j) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int m = j * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       const bool ok = m < tl.rows;
       const int p = tl.row_begin + (ok ? m : 0);
       const float sx = as[(PASS == 1) ? perm[p] / k : p];
       const float v = accf[j][r] * sx;
       if constexpr (PASS == 1) {
-        const float u = __shfl_xor(v, 1, 64);  // odd column = up of the same neuron
-        if ((n & 1) == 0 && ok && n < N) out[(size_t)p * out_ld + (n >> 1)] = silu(v) * u;
+        const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
+        if ((n & 1) == 0 && ok && nvalid) out[(size_t)p * out_ld + (n >> 1)] = silu(v) * u;
       } else {
-        if (ok && n < N) out[(size_t)p * out_ld + n] = v;
+        if (ok && nvalid) out[(size_t)p * out_ld + n] = v;
       }
     }
   }
 }
 
-template <int RPW, int KS, int MAXNT, bool SWIGLU>
+template <int KS, int RBW, int MAXNT, bool SWIGLU>
 void launch_gemv(const int8_t* aq, const float* as, const int32_t* ag, const int32_t* perm, int k,
                  const FfnItem* items, const int32_t* n_items, int max_items, const char* pool,
-                 size_t stride, size_t off_codes, size_t off_scales, int rows, int K, int out_ld,
+                 size_t stride, size_t off_codes, size_t off_scales, int R, int K, int out_ld,
                  float* out, hipStream_t s) {
-  const int per_wg = RPW * (4 / KS);
-  const long long rb = (rows + per_wg - 1) / per_wg;
-  const long long units = rb * max_items;
-  const unsigned grid = (unsigned)(units < 8192 ? units : 8192);
+  constexpr int NW = KS < 4 ? 4 : KS;
+  constexpr int rb_per_wg = NW / KS * RBW;
+  const int upi = (R / 32 + rb_per_wg - 1) / rb_per_wg;
+  const long long units = (long long)upi * max_items;
+  const unsigned grid = (unsigned)(units < tgemv::kGridCap ? units : tgemv::kGridCap);
   if (grid == 0) return;
-  hipLaunchKernelGGL((gemv_w4a8_kernel<RPW, KS, MAXNT, SWIGLU>), dim3(grid), dim3(256), 0, s, aq,
-                     as, ag, perm, k, items, n_items, pool, stride, off_codes, off_scales, rows, K,
-                     out_ld, (int)rb, out);
+  constexpr int U = RBW >= 4 ? 2 : 4;
+  hipLaunchKernelGGL((tgemv::int4_kernel<KS, RBW, NW, U, MAXNT, SWIGLU>), dim3(grid),
+                     dim3(NW * 64), 0, s, aq, as, ag, perm, k, items, n_items, pool, stride,
+                     off_codes, off_scales, R, K, out_ld, upi, out);
 }
 
-template <int MAXNT>
-void launch_gemv_pair(bool first, const int8_t* aq, const float* as, const int32_t* ag,
-                      const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
-                      int max_items, const char* pool, size_t stride, const SlotLayout& lay, int H,
-                      int F, float* out, hipStream_t s) {
-  if (first) {
-    // K = H: split K over 2 waves when a row spans several 2048-value chunks
-    if (H > 2048)
-      launch_gemv<4, 2, MAXNT, true>(aq, as, ag, perm, k, items, n_items, max_items, pool, stride,
-                                     lay.off_w13, lay.off_s13, 2 * F, H, F, out, s);
-    else
-      launch_gemv<4, 1, MAXNT, true>(aq, as, ag, perm, k, items, n_items, max_items, pool, stride,
-                                     lay.off_w13, lay.off_s13, 2 * F, H, F, out, s);
-  } else {
-    if (F > 2048)
-      launch_gemv<4, 2, MAXNT, false>(aq, as, ag, perm, k, items, n_items, max_items, pool, stride,
-                                      lay.off_w2, lay.off_s2, H, F, H, out, s);
-    else
-      launch_gemv<4, 1, MAXNT, false>(aq, as, ag, perm, k, items, n_items, max_items, pool, stride,
-                                      lay.off_w2, lay.off_s2, H, F, H, out, s);
+template <int RBW, int MAXNT, bool SWIGLU>
+void launch_gemv_ks(int ks, const int8_t* aq, const float* as, const int32_t* ag,
+                    const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
+                    int max_items, const char* pool, size_t stride, size_t off_codes,
+                    size_t off_scales, int R, int K, int out_ld, float* out, hipStream_t s) {
+#define MOE_W4_KS(KS_)                                                                          \
+  launch_gemv<KS_, RBW, MAXNT, SWIGLU>(aq, as, ag, perm, k, items, n_items, max_items, pool,    \
+                                       stride, off_codes, off_scales, R, K, out_ld, out, s)
+  switch (ks) {
+    case 1: MOE_W4_KS(1); break;
+    case 2: MOE_W4_KS(2); break;
+    case 4: MOE_W4_KS(4); break;
+    default: MOE_W4_KS(8); break;
   }
+#undef MOE_W4_KS
 }
 
 void launch_gemv_any(bool first, int nt, const int8_t* aq, const float* as, const int32_t* ag,
                      const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
                      int max_items, const char* pool, size_t stride, const SlotLayout& lay, int H,
                      int F, float* out, hipStream_t s) {
-  if (nt <= 1)
-    launch_gemv_pair<1>(first, aq, as, ag, perm, k, items, n_items, max_items, pool, stride, lay, H,
-                        F, out, s);
-  else if (nt <= 2)
-    launch_gemv_pair<2>(first, aq, as, ag, perm, k, items, n_items, max_items, pool, stride, lay, H,
-                        F, out, s);
-  else
-    launch_gemv_pair<4>(first, aq, as, ag, perm, k, items, n_items, max_items, pool, stride, lay, H,
-                        F, out, s);
+  const int R = first ? 2 * F : H, K = first ? H : F, ld = first ? F : H;
+  const size_t oc = first ? lay.off_w13 : lay.off_w2, os = first ? lay.off_s13 : lay.off_s2;
+  const tgemv::Split sp = tgemv::choose_split_int4(R / 32 * max_items, K / 64);
+#define MOE_W4_NT(NT_)                                                                          \
+  do {                                                                                          \
+    if (first)                                                                                  \
+      launch_gemv_ks<4, NT_, true>(sp.ks, aq, as, ag, perm, k, items, n_items, max_items, pool, stride, \
+                                oc, os, R, K, ld, out, s);                                      \
+    else                                                                                        \
+      launch_gemv_ks<4, NT_, false>(sp.ks, aq, as, ag, perm, k, items, n_items, max_items, pool,       \
+                                 stride, oc, os, R, K, ld, out, s);                             \
+  } while (0)
+  if (nt <= 1) MOE_W4_NT(1);
+  else if (nt <= 2) MOE_W4_NT(2);
+  else MOE_W4_NT(4);
+#undef MOE_W4_NT
 }
 
 }  // namespace
@@ -478,7 +351,7 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   launch_gemv_any(true, nt, xq, xs, xg, perm, k, items, n_items, max_items, pool, stride, lay, H, F,
                   hbuf, s);
   if (max_tiles > 0)
-    hipLaunchKernelGGL(gemm_w4a8_kernel<1>, dim3((2 * F + QBN - 1) / QBN, max_tiles), dim3(256), 0,
+    hipLaunchKernelGGL(gemm_w4a8_kernel<1>, dim3((2 * F / 32 + 3) / 4, max_tiles), dim3(256), 0,
                        s, xq, xs, xg, perm, k, tiles, n_tiles, pool, stride, lay.off_w13,
                        lay.off_s13, 2 * F, H, F, hbuf);
   hipLaunchKernelGGL(quant_rows_kernel<MOE_F32>, dim3((unsigned)tk), dim3(256), 0, s, hbuf, F,
@@ -486,7 +359,7 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   launch_gemv_any(false, nt, hq, hs, hg, perm, k, items, n_items, max_items, pool, stride, lay, H,
                   F, y, s);
   if (max_tiles > 0)
-    hipLaunchKernelGGL(gemm_w4a8_kernel<2>, dim3((H + QBN - 1) / QBN, max_tiles), dim3(256), 0, s,
+    hipLaunchKernelGGL(gemm_w4a8_kernel<2>, dim3((H / 32 + 3) / 4, max_tiles), dim3(256), 0, s,
                        hq, hs, hg, perm, k, tiles, n_tiles, pool, stride, lay.off_w2, lay.off_s2, H,
                        F, H, y);
   return moe_launch_status();

@@ -20,7 +20,7 @@ struct GemmTile {
   int32_t rows;       // rows in the tile (<= kGemmBM)
 };
 
-constexpr int kGemmBM = 64;      // rows of an MFMA M-tile
+constexpr int kGemmBM = 128;     // rows of an MFMA M-tile
 constexpr int kGemvMaxRows = 4;  // groups up to this many rows take the GEMV path
 
 // Byte layout of one expert inside a slot (see moe_slot_layout).

@@ -9,12 +9,16 @@
 //           (rows 2n / 2n+1 = gate / up of neuron n), epilogue
 //           h[p][n] = SiLU(gate) * up, stored bf16;
 //   pass 2: A = h rows (bf16), W = W2 of the slot, epilogue y[p][n] fp32.
-// Tiles: BM = 64 rows x BN = 128 weight rows x BK = 64, 4 waves in a 2x2
-// layout, each wave 32 x 64 = two v_mfma_f32_32x32x16_bf16 accumulators.
-// A and W tiles are staged through LDS (rows padded to 72 elements, 8 lanes
-// per coalesced 128-byte row segment); global loads run kAhead K-tiles ahead
-// through a ring of register stages, so each weight element is fetched from
-// HBM once per M-tile and reused for the tile's 64 rows from LDS.
+// Tiles: BM = 128 activation rows x 128 weight rows, K steps of BK = 64. Each
+// of the 4 waves owns one 32-row block of the tile-major weights (one
+// v_mfma_f32_32x32x16_bf16 accumulator per 32 activation rows; fragments
+// without rows are skipped): its operand fragments are whole 1 KB chunks of
+// the slot, read with one contiguous 16-byte load per lane straight into
+// registers. The loads stay cacheable so that the M-tiles of one group,
+// which run side by side, share the chunks through L2.
+// The activation tile, shared by the 4 waves, is staged through LDS (rows
+// padded to 72 elements, 8 lanes per 128-byte row segment). Global loads run
+// kAhead K-tiles ahead through a ring of register stages.
 // Lane layouts (checked on gfx950): A/B operand lane l holds row l % 32,
 // k = 8 (l / 32) .. +7; accumulator r holds row 8 (r / 4) + 4 (l / 32) + r % 4,
 // column l % 32.
@@ -27,6 +31,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
 
 constexpr int BM = kGemmBM;
+constexpr int MF = BM / 32;  // 32-row activation fragments per tile
 constexpr int BN = 128;
 constexpr int BK = 64;
 constexpr int LDS_LD = BK + 8;  // padded row (elements)
@@ -41,63 +46,53 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     const char* __restrict__ pool, size_t stride, size_t off, int N, int K, int out_ld,
     void* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDS_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDS_LD];
   if ((int)blockIdx.y >= n_tiles[0]) return;
   const GemmTile tl = tiles[blockIdx.y];
-  const int n0 = blockIdx.x * BN;
-  if (n0 >= N) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves
+  const int nrb = N / 32;
+  if ((int)blockIdx.x * 4 >= nrb) return;
 
-  // global -> LDS assignment: 8 threads per 128-byte row chunk of 64 bf16
+  // activation rows this thread stages: (tid >> 3) + 32 i, 16 bytes at (tid & 7) * 8 elements
   const int lrow = tid >> 3, lcol = (tid & 7) * 8;
-  // A rows this thread stages: lrow and lrow + 32 (BM = 64)
-  const uint16_t* arow[2];
-  bool avalid[2];
+  const uint16_t* arow[MF];
+  bool avalid[MF];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < MF; ++i) {
     const int m = lrow + 32 * i;
     avalid[i] = m < tl.rows;
     const int p = tl.row_begin + (avalid[i] ? m : 0);
     const size_t r = (PASS == 1) ? (size_t)(perm[p] / k) : (size_t)p;
     arow[i] = act + r * K;
   }
-  // W rows this thread stages: lrow + 32 i, i < 4
-  const char* wbase = pool + (size_t)tl.slot * stride + off;
-  const uint16_t* brow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int n = n0 + lrow + 32 * i;
-    if (n >= N) n = N - 1;
-    brow[i] = reinterpret_cast<const uint16_t*>(wbase) + (size_t)n * K;
-  }
+  // this wave's 32-row weight block; a block past N re-reads the last one and stores nothing
+  int rb = blockIdx.x * 4 + wave;
+  const bool nvalid = rb < nrb;
+  if (!nvalid) rb = nrb - 1;
+  const char* wchunks = pool + (size_t)tl.slot * stride + off + (size_t)rb * (K / 16) * 1024 + lane * 16;
 
-  // register stages: tile kt + kAhead is loaded while tile kt is computed and
-  // tile kt + 1 is written to LDS, so every global load has kAhead - 1 full
-  // compute iterations to land
+  // register stages: tile kt + kAhead is loaded right after tile kt is used
   struct Stage {
-    u32x4 a[2], b[4];
+    u32x4 a[MF], b[BK / 16];
   };
   Stage st[kAhead];
   auto gload = [&](Stage& r, int kt) {
     const int kk = kt * BK + lcol;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) r.a[i] = avalid[i] ? ld16(arow[i] + kk) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < MF; ++i) r.a[i] = avalid[i] ? ld16(arow[i] + kk) : u32x4{0u, 0u, 0u, 0u};
+    // cacheable: the other M-tiles of the group read the same chunks
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.b[i] = ld16_stream(brow[i] + kk);
+    for (int s = 0; s < BK / 16; ++s) r.b[s] = ld16(wchunks + (size_t)(kt * (BK / 16) + s) * 1024);
   };
-  auto sstore = [&](const Stage& r, int buf) {
+  auto astore = [&](const Stage& r, int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MF; ++i)
       *reinterpret_cast<u32x4*>(&sA[buf][(lrow + 32 * i) * LDS_LD + lcol]) = r.a[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&sB[buf][(lrow + 32 * i) * LDS_LD + lcol]) = r.b[i];
   };
+  const int live = (tl.rows + 31) / 32;  // activation fragments holding rows
 
-  floatx16 acc[2];
+  floatx16 acc[MF];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < MF; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 
@@ -105,25 +100,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 #pragma unroll
   for (int s = 0; s < kAhead; ++s)
     if (s < nk) gload(st[s], s);
-  sstore(st[0], 0);
+  astore(st[0], 0);
   __syncthreads();
-  // iteration kt: refill stage kt % kAhead with tile kt + kAhead, compute LDS
-  // buffer kt % 2, write tile kt + 1 (stage (kt + 1) % kAhead) to the other buffer
   auto step = [&](Stage& mine, Stage& next, int kt) {
     const int buf = kt & 1;
-    if (kt + kAhead < nk) gload(mine, kt + kAhead);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kc = ks * 16 + 8 * (lane >> 5);
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 32 + (lane & 31)) * LDS_LD + kc]);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&mine.b[ks]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 b =
-            *reinterpret_cast<const bf16x8*>(&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * LDS_LD + kc]);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+      for (int j = 0; j < MF; ++j) {
+        if (j < live) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              &sA[buf][(j * 32 + (lane & 31)) * LDS_LD + ks * 16 + 8 * (lane >> 5)]);
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+        }
       }
     }
-    if (kt + 1 < nk) sstore(next, buf ^ 1);
+    if (kt + kAhead < nk) gload(mine, kt + kAhead);
+    if (kt + 1 < nk) astore(next, buf ^ 1);
     __syncthreads();
   };
   for (int kt = 0; kt < nk; kt += kAhead) {
@@ -132,22 +126,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
       if (kt + s < nk) step(st[s], st[(s + 1) % kAhead], kt + s);
   }
 
-  // epilogue
+  // epilogue: accumulator j covers rows 32 j .., weight row n of this lane
+  const int n = rb * 32 + (lane & 31);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < MF; ++j) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int m = j * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       const float v = acc[j][r];
       if constexpr (PASS == 1) {
-        const float u = __shfl_xor(v, 1, 64);  // odd column = up of the same neuron
-        if ((n & 1) == 0 && m < tl.rows && n < N) {
+        const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
+        if ((n & 1) == 0 && m < tl.rows && nvalid) {
           uint16_t* h = static_cast<uint16_t*>(out) + (size_t)(tl.row_begin + m) * out_ld;
           h[n >> 1] = f32_to_bf16_rne(silu(v) * u);
         }
       } else {
-        if (m < tl.rows && n < N)
+        if (m < tl.rows && nvalid)
           static_cast<float*>(out)[(size_t)(tl.row_begin + m) * out_ld + n] = v;
       }
     }
@@ -159,7 +153,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, const GemmTile* tiles,
                       const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
                       size_t off, int N, int K, int out_ld, void* out, hipStream_t s) {
-  const dim3 grid((N + BN - 1) / BN, max_tiles);
+  const dim3 grid((N / 32 + 3) / 4, max_tiles);
   if (pass == 1)
     hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(act), perm, k, tiles, n_tiles, pool, stride, off,

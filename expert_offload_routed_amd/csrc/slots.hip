@@ -26,6 +26,7 @@
 int slot_layout(int H, int F, int w_dtype, SlotLayout* out) {
   if (H <= 0 || F <= 0 || H % 16 != 0 || F % 16 != 0) return MOE_EINVAL;
   SlotLayout l{};
+  if (w_dtype == MOE_BF16 && H % 32 != 0) return MOE_EINVAL;  // 32-row tiles of W2
   if (w_dtype == MOE_F32 || w_dtype == MOE_BF16) {
     const size_t es = (w_dtype == MOE_F32) ? 4 : 2;
     l.off_w13 = 0;
@@ -59,6 +60,46 @@ extern "C" int moe_slot_layout(int H, int F, int w_dtype, size_t* slot_bytes, si
   return MOE_OK;
 }
 
+namespace {
+
+// Tile-major bf16: element (r, c) of W [R, K] in 1 KB chunk (r / 32) * (K / 16) + c / 16,
+// lane (r % 32) + 32 ((c % 16) / 8), element c % 8 of the lane's 16 bytes.
+void pack_tiles_bf16(char* dst, const char* src_rows[], int R, int K) {
+  const int nks = K / 16;
+  for (int rb = 0; rb < R / 32; ++rb)
+    for (int ks = 0; ks < nks; ++ks)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int r = rb * 32 + (lane & 31);
+        const int c = ks * 16 + 8 * (lane >> 5);
+        memcpy(dst + ((size_t)(rb * nks + ks) * 64 + lane) * 16, src_rows[r] + (size_t)c * 2, 16);
+      }
+}
+
+// Signed 4-bit code c of a row in the logical format (even index in the low nibble).
+inline uint8_t code_at(const uint8_t* row, int c) { return (row[c >> 1] >> ((c & 1) * 4)) & 0xF; }
+
+// Tile-major int4: chunk (r / 32) * (K / 64) + c / 64 of 1 KB; lane (r % 32) + 32 ((c % 32) / 16)
+// holds 16 bytes: bytes [8 h, 8 h + 8) for the 16 codes of k-step half h = (c % 64) / 32; in each
+// 4-byte word of 8 consecutive codes, byte i = code i (low nibble) | code i + 4 (high nibble).
+void pack_tiles_int4(char* dst, const uint8_t* src_rows[], int R, int K) {
+  const int nkc = K / 64;
+  for (int rb = 0; rb < R / 32; ++rb)
+    for (int kc = 0; kc < nkc; ++kc)
+      for (int lane = 0; lane < 64; ++lane) {
+        const uint8_t* row = src_rows[rb * 32 + (lane & 31)];
+        uint8_t* out = reinterpret_cast<uint8_t*>(dst) + ((size_t)(rb * nkc + kc) * 64 + lane) * 16;
+        for (int h = 0; h < 2; ++h)
+          for (int w = 0; w < 2; ++w) {
+            const int c0 = kc * 64 + h * 32 + 16 * (lane >> 5) + w * 8;
+            for (int i = 0; i < 4; ++i)
+              out[h * 8 + w * 4 + i] =
+                  (uint8_t)(code_at(row, c0 + i) | (code_at(row, c0 + i + 4) << 4));
+          }
+      }
+}
+
+}  // namespace
+
 extern "C" int moe_pack_expert_host(const void* gate, const void* up, const void* down,
                                     const void* gate_s, const void* up_s, const void* down_s,
                                     int H, int F, int w_dtype, void* dst) {
@@ -67,55 +108,44 @@ extern "C" int moe_pack_expert_host(const void* gate, const void* up, const void
   MOE_CHECK_ARG(gate && up && down && dst);
   char* d = static_cast<char*>(dst);
   memset(d, 0, l.slot_bytes);
-  // bytes of one gate/up row (H inputs) and one down row (F inputs)
-  size_t rb13, rb2;
-  if (w_dtype == MOE_INT4G128) {
-    MOE_CHECK_ARG(gate_s && up_s && down_s);
-    rb13 = H / 2;
-    rb2 = F / 2;
-  } else {
-    const size_t es = (w_dtype == MOE_F32) ? 4 : 2;
-    rb13 = H * es;
-    rb2 = F * es;
-  }
   const char* g = static_cast<const char*>(gate);
   const char* u = static_cast<const char*>(up);
-  // int4 rows are stored per 8 consecutive codes c0..c7 as one little-endian
-  // word whose byte i holds c_i in its low nibble and c_{i+4} in its high
-  // nibble, so the low (high) nibbles of a word are 4 consecutive values
-  auto put = [&](char* dst, const char* src, size_t bytes) {
-    if (w_dtype != MOE_INT4G128) {
-      memcpy(dst, src, bytes);
-      return;
-    }
-    const uint8_t* in = reinterpret_cast<const uint8_t*>(src);  // even code in the low nibble
-    for (size_t w = 0; w < bytes / 4; ++w) {
-      uint8_t c[8];
-      for (int i = 0; i < 4; ++i) {
-        c[2 * i] = in[4 * w + i] & 0xF;
-        c[2 * i + 1] = in[4 * w + i] >> 4;
-      }
-      uint32_t word = 0;
-      for (int i = 0; i < 4; ++i) word |= (uint32_t)(c[i] | (c[i + 4] << 4)) << (8 * i);
-      memcpy(dst + 4 * w, &word, 4);
-    }
-  };
-  for (int n = 0; n < F; ++n) {
-    put(d + l.off_w13 + (size_t)(2 * n) * rb13, g + (size_t)n * rb13, rb13);
-    put(d + l.off_w13 + (size_t)(2 * n + 1) * rb13, u + (size_t)n * rb13, rb13);
-  }
-  for (int r = 0; r < H; ++r)
-    put(d + l.off_w2 + (size_t)r * rb2, static_cast<const char*>(down) + (size_t)r * rb2, rb2);
-  if (w_dtype == MOE_INT4G128) {
-    const size_t sb13 = (size_t)(H / 128) * 2, sb2 = (size_t)(F / 128) * 2;
-    const char* gs = static_cast<const char*>(gate_s);
-    const char* us = static_cast<const char*>(up_s);
+  const char* dn = static_cast<const char*>(down);
+  if (w_dtype == MOE_F32) {  // row-major, gate and up rows interleaved
+    const size_t rb13 = (size_t)H * 4, rb2 = (size_t)F * 4;
     for (int n = 0; n < F; ++n) {
-      memcpy(d + l.off_s13 + (size_t)(2 * n) * sb13, gs + (size_t)n * sb13, sb13);
-      memcpy(d + l.off_s13 + (size_t)(2 * n + 1) * sb13, us + (size_t)n * sb13, sb13);
+      memcpy(d + l.off_w13 + (size_t)(2 * n) * rb13, g + (size_t)n * rb13, rb13);
+      memcpy(d + l.off_w13 + (size_t)(2 * n + 1) * rb13, u + (size_t)n * rb13, rb13);
     }
-    memcpy(d + l.off_s2, down_s, (size_t)H * sb2);
+    memcpy(d + l.off_w2, dn, (size_t)H * rb2);
+    return MOE_OK;
   }
+  // rows of W13 in interleaved order (2n = gate n, 2n + 1 = up n) and of W2
+  const size_t rb13 = (w_dtype == MOE_BF16) ? (size_t)H * 2 : (size_t)H / 2;
+  const size_t rb2 = (w_dtype == MOE_BF16) ? (size_t)F * 2 : (size_t)F / 2;
+  std::vector<const char*> r13(2 * F), r2(H);
+  for (int n = 0; n < F; ++n) {
+    r13[2 * n] = g + (size_t)n * rb13;
+    r13[2 * n + 1] = u + (size_t)n * rb13;
+  }
+  for (int r = 0; r < H; ++r) r2[r] = dn + (size_t)r * rb2;
+  if (w_dtype == MOE_BF16) {
+    pack_tiles_bf16(d + l.off_w13, r13.data(), 2 * F, H);
+    pack_tiles_bf16(d + l.off_w2, r2.data(), H, F);
+    return MOE_OK;
+  }
+  MOE_CHECK_ARG(gate_s && up_s && down_s);
+  pack_tiles_int4(d + l.off_w13, reinterpret_cast<const uint8_t**>(r13.data()), 2 * F, H);
+  pack_tiles_int4(d + l.off_w2, reinterpret_cast<const uint8_t**>(r2.data()), H, F);
+  // scales stay row-major: [2F, H/128] (gate/up interleaved) and [H, F/128]
+  const size_t sb13 = (size_t)(H / 128) * 2, sb2 = (size_t)(F / 128) * 2;
+  const char* gs = static_cast<const char*>(gate_s);
+  const char* us = static_cast<const char*>(up_s);
+  for (int n = 0; n < F; ++n) {
+    memcpy(d + l.off_s13 + (size_t)(2 * n) * sb13, gs + (size_t)n * sb13, sb13);
+    memcpy(d + l.off_s13 + (size_t)(2 * n + 1) * sb13, us + (size_t)n * sb13, sb13);
+  }
+  memcpy(d + l.off_s2, down_s, (size_t)H * sb2);
   return MOE_OK;
 }
 

@@ -1,0 +1,357 @@
+// Decode-form expert GEMV passes over tile-major weights (bf16 and int4),
+// shared by ffn.hip and ffn_int4.hip.
+//
+// Tile-major layout (moe_slot_layout): the weights of a 32-row block are
+// consecutive 1 KB chunks; in chunk ks lane l holds row l % 32 and the K
+// range ks * KC + half (l / 32), so one 16-byte load per lane reads 1 KB of
+// contiguous memory. A pass computes, for every routed group in the work
+// list and every row r of W [R, K], the dot products of r with the group's
+// activation rows:
+//   pass 1 (SWIGLU): W = W13 (row 2n = gate n, row 2n+1 = up n), activations
+//            = tokens x[perm[p] / k]; epilogue h[p][n] = SiLU(g) * u (gate and
+//            up rows sit in neighbouring lanes);
+//   pass 2:  W = W2, activations = h[p]; epilogue y[p][row] = dot.
+// A workgroup has NW waves; KS waves share RBW row blocks and split their
+// chunks (chunk ks goes to wave slice ks % KS), U x RBW chunks in flight per
+// lane; each activation load serves RBW rows. The two K halves of a row
+// (lanes l, l + 32) meet through a shuffle, the KS slices in LDS. Each weight
+// chunk is streamed once per tile of NT <= MAXNT rows.
+#pragma once
+
+#include "common.h"
+#include "ffn_internal.h"
+
+namespace tgemv {
+
+__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
+
+template <int FMT>
+__device__ __forceinline__ void load8(const void* base, size_t elem, float out[8]) {
+  if constexpr (FMT == MOE_BF16) {
+    u32x4 v = ld16(static_cast<const uint16_t*>(base) + elem);
+    out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
+    out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+    out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
+    out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+  } else {
+    const float* p = static_cast<const float*>(base) + elem;
+    u32x4 a = ld16(p), b = ld16(p + 4);
+    out[0] = __uint_as_float(a.x); out[1] = __uint_as_float(a.y);
+    out[2] = __uint_as_float(a.z); out[3] = __uint_as_float(a.w);
+    out[4] = __uint_as_float(b.x); out[5] = __uint_as_float(b.y);
+    out[6] = __uint_as_float(b.z); out[7] = __uint_as_float(b.w);
+  }
+}
+
+__device__ __forceinline__ uint32_t u_lo(uint32_t w) { return (w ^ 0x88888888u) & 0x0F0F0F0Fu; }
+__device__ __forceinline__ uint32_t u_hi(uint32_t w) { return ((w ^ 0x88888888u) >> 4) & 0x0F0F0F0Fu; }
+
+// Final reduction and epilogue, shared by both formats. acc[b][t] holds this
+// lane's partial dot of row (rb0 + b) * 32 + lane % 32 (one K half, one K slice).
+template <int RBW, int NT, int KS, bool SWIGLU, int OF>
+__device__ __forceinline__ void finish(float (&acc)[RBW][NT], const float* scale_t, int prow,
+                                       int rb0, int nrb, int out_ld, void* __restrict__ out,
+                                       float* __restrict__ red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slice = wave % KS;
+#pragma unroll
+  for (int b = 0; b < RBW; ++b)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[b][t] += __shfl_xor(acc[b][t], 32, 64);
+  if constexpr (KS > 1) {
+    if (lane < 32) {
+#pragma unroll
+      for (int b = 0; b < RBW; ++b)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) red[((wave * RBW + b) * 32 + lane) * NT + t] = acc[b][t];
+    }
+    __syncthreads();
+    if (slice == 0) {
+#pragma unroll
+      for (int s = 1; s < KS; ++s)
+#pragma unroll
+        for (int b = 0; b < RBW; ++b)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[b][t] += red[(((wave + s) * RBW + b) * 32 + (lane & 31)) * NT + t];
+    }
+    __syncthreads();
+  }
+  if (slice != 0) return;
+#pragma unroll
+  for (int b = 0; b < RBW; ++b) {
+    const bool store = rb0 + b < nrb;
+    const int row = (rb0 + b) * 32 + (lane & 31);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float v = acc[b][t] * (scale_t ? scale_t[t] : 1.f);
+      if constexpr (SWIGLU) {
+        const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
+        if (store && lane < 32 && (lane & 1) == 0) {
+          const float hv = silu(v) * u;
+          if constexpr (OF == MOE_BF16)
+            static_cast<uint16_t*>(out)[(size_t)(prow + t) * out_ld + (row >> 1)] = f32_to_bf16_rne(hv);
+          else
+            static_cast<float*>(out)[(size_t)(prow + t) * out_ld + (row >> 1)] = hv;
+        }
+      } else {
+        if (store && lane < 32) static_cast<float*>(out)[(size_t)(prow + t) * out_ld + row] = v;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ bf16 ---
+template <int AF, int OF, int KS, int RBW, int U, int NT, bool SWIGLU>
+__device__ __forceinline__ void tile_bf16(const char* __restrict__ wbase, int nks, int K,
+                                          const void* __restrict__ act,
+                                          const int32_t* __restrict__ perm, int k, int prow,
+                                          int rb0, int nrb, int out_ld, void* __restrict__ out,
+                                          float* __restrict__ red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slice = wave % KS;
+  const int kh = 8 * (lane >> 5);
+  size_t arow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) arow[t] = SWIGLU ? (size_t)(perm[prow + t] / k) : (size_t)(prow + t);
+  float acc[RBW][NT];
+#pragma unroll
+  for (int b = 0; b < RBW; ++b)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[b][t] = 0.f;
+  // block b's chunks; blocks past the end re-read the last block (their rows are not stored)
+  const char* wl[RBW];
+#pragma unroll
+  for (int b = 0; b < RBW; ++b) {
+    const int rb = (rb0 + b < nrb) ? rb0 + b : nrb - 1;
+    wl[b] = wbase + (size_t)rb * nks * 1024 + lane * 16;
+  }
+  for (int ks0 = slice; ks0 < nks; ks0 += KS * U) {
+    u32x4 wv[U][RBW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = ks0 + u * KS;
+      if (ks < nks) {
+#pragma unroll
+        for (int b = 0; b < RBW; ++b) wv[u][b] = ld16_stream(wl[b] + (size_t)ks * 1024);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = ks0 + u * KS;
+      if (ks < nks) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float xv[8];
+          load8<AF>(act, arow[t] * K + ks * 16 + kh, xv);
+#pragma unroll
+          for (int b = 0; b < RBW; ++b) {
+            const u32x4& w = wv[u][b];
+            acc[b][t] = fmaf(bf16_lo(w.x), xv[0], acc[b][t]);
+            acc[b][t] = fmaf(bf16_hi(w.x), xv[1], acc[b][t]);
+            acc[b][t] = fmaf(bf16_lo(w.y), xv[2], acc[b][t]);
+            acc[b][t] = fmaf(bf16_hi(w.y), xv[3], acc[b][t]);
+            acc[b][t] = fmaf(bf16_lo(w.z), xv[4], acc[b][t]);
+            acc[b][t] = fmaf(bf16_hi(w.z), xv[5], acc[b][t]);
+            acc[b][t] = fmaf(bf16_lo(w.w), xv[6], acc[b][t]);
+            acc[b][t] = fmaf(bf16_hi(w.w), xv[7], acc[b][t]);
+          }
+        }
+      }
+    }
+  }
+  finish<RBW, NT, KS, SWIGLU, OF>(acc, nullptr, prow, rb0, nrb, out_ld, out, red);
+}
+
+// ------------------------------------------------------------------ int4 ---
+// Codes in offset form u = q + 8; sum q x = sum u x - 8 sum x, the second
+// term added once per (row, 128-value group) from the group sums of x.
+template <int KS, int RBW, int U, int NT, bool SWIGLU>
+__device__ __forceinline__ void tile_int4(const char* __restrict__ wbase, int nkc, int K,
+                                          const uint16_t* __restrict__ scales,
+                                          const int8_t* __restrict__ aq,
+                                          const float* __restrict__ as,
+                                          const int32_t* __restrict__ ag,
+                                          const int32_t* __restrict__ perm, int k, int prow,
+                                          int rb0, int nrb, int out_ld, float* __restrict__ out,
+                                          float* __restrict__ red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slice = wave % KS;
+  const int kh = 16 * (lane >> 5);
+  const int gld = K / 128;
+  int arow[NT];
+  float sx[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    arow[t] = SWIGLU ? perm[prow + t] / k : prow + t;
+    sx[t] = as[arow[t]];
+  }
+  float acc[RBW][NT];
+#pragma unroll
+  for (int b = 0; b < RBW; ++b)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[b][t] = 0.f;
+  const char* wl[RBW];
+  const uint16_t* srow[RBW];
+#pragma unroll
+  for (int b = 0; b < RBW; ++b) {
+    const int rb = (rb0 + b < nrb) ? rb0 + b : nrb - 1;
+    wl[b] = wbase + (size_t)rb * nkc * 1024 + lane * 16;
+    srow[b] = scales + (size_t)(rb * 32 + (lane & 31)) * gld;
+  }
+  for (int kc0 = slice; kc0 < nkc; kc0 += KS * U) {
+    u32x4 cw[U][RBW];
+    float sw[U][RBW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kc = kc0 + u * KS;
+      if (kc < nkc) {
+#pragma unroll
+        for (int b = 0; b < RBW; ++b) {
+          cw[u][b] = ld16_stream(wl[b] + (size_t)kc * 1024);
+          sw[u][b] = bf16_to_f32(srow[b][kc >> 1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kc = kc0 + u * KS;
+      if (kc < nkc) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int8_t* ap = aq + (size_t)arow[t] * K + kc * 64 + kh;
+          const u32x4 a0 = ld16(ap), a1 = ld16(ap + 32);
+          // the group's offset correction, once per row (lane < 32) on its even chunk
+          const int corr = (lane < 32 && (kc & 1) == 0) ? 8 * ag[(size_t)arow[t] * gld + (kc >> 1)] : 0;
+#pragma unroll
+          for (int b = 0; b < RBW; ++b) {
+            const u32x4& w = cw[u][b];
+            int is = -corr;
+            is = __builtin_amdgcn_sdot4((int)u_lo(w.x), (int)a0.x, is, false);
+            is = __builtin_amdgcn_sdot4((int)u_hi(w.x), (int)a0.y, is, false);
+            is = __builtin_amdgcn_sdot4((int)u_lo(w.y), (int)a0.z, is, false);
+            is = __builtin_amdgcn_sdot4((int)u_hi(w.y), (int)a0.w, is, false);
+            is = __builtin_amdgcn_sdot4((int)u_lo(w.z), (int)a1.x, is, false);
+            is = __builtin_amdgcn_sdot4((int)u_hi(w.z), (int)a1.y, is, false);
+            is = __builtin_amdgcn_sdot4((int)u_lo(w.w), (int)a1.z, is, false);
+            is = __builtin_amdgcn_sdot4((int)u_hi(w.w), (int)a1.w, is, false);
+            acc[b][t] = fmaf((float)is, sw[u][b], acc[b][t]);
+          }
+        }
+      }
+    }
+  }
+  finish<RBW, NT, KS, SWIGLU, MOE_F32>(acc, sx, prow, rb0, nrb, out_ld, out, red);
+}
+
+// ---------------------------------------------------------------- kernels --
+// Work unit u = (item u / units_per_item, row-block group u % units_per_item);
+// a group is the NW / KS row blocks of one workgroup.
+#define TGEMV_REST(CALL)                      \
+  if constexpr (MAXNT > 1) {                  \
+    if (rest == 1) CALL(1);                   \
+  }                                           \
+  if constexpr (MAXNT > 2) {                  \
+    if (rest == 2) CALL(2);                   \
+    if (rest == 3) CALL(3);                   \
+  }
+
+template <int AF, int OF, int KS, int RBW, int NW, int U, int MAXNT, bool SWIGLU>
+__global__ __launch_bounds__(NW * 64) void bf16_kernel(
+    const void* __restrict__ act, const int32_t* __restrict__ perm, int k,
+    const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items,
+    const char* __restrict__ pool, size_t stride, size_t off, int R, int K, int out_ld,
+    int units_per_item, void* __restrict__ out) {
+  __shared__ float red[NW * RBW * 32 * MAXNT];
+  const int wave = threadIdx.x >> 6;
+  const int nks = K / 16;
+  const int nrb = R / 32;
+  const int units = n_items[0] * units_per_item;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int item = u / units_per_item;
+    const int rb0 = ((u - item * units_per_item) * (NW / KS) + wave / KS) * RBW;
+    const FfnItem it = items[item];
+    const char* wbase = pool + (size_t)it.slot * stride + off;
+    int done = 0;
+    for (; it.rows - done >= MAXNT; done += MAXNT)
+      tile_bf16<AF, OF, KS, RBW, U, MAXNT, SWIGLU>(wbase, nks, K, act, perm, k, it.row_begin + done,
+                                                   rb0, nrb, out_ld, out, red);
+    const int rest = it.rows - done, p = it.row_begin + done;
+#define TGEMV_BF16(NT_)                                                                        \
+  tile_bf16<AF, OF, KS, RBW, U, NT_, SWIGLU>(wbase, nks, K, act, perm, k, p, rb0, nrb, out_ld, out, \
+                                             red)
+    TGEMV_REST(TGEMV_BF16)
+#undef TGEMV_BF16
+  }
+}
+
+template <int KS, int RBW, int NW, int U, int MAXNT, bool SWIGLU>
+__global__ __launch_bounds__(NW * 64) void int4_kernel(
+    const int8_t* __restrict__ aq, const float* __restrict__ as, const int32_t* __restrict__ ag,
+    const int32_t* __restrict__ perm, int k, const FfnItem* __restrict__ items,
+    const int32_t* __restrict__ n_items, const char* __restrict__ pool, size_t stride,
+    size_t off_codes, size_t off_scales, int R, int K, int out_ld, int units_per_item,
+    float* __restrict__ out) {
+  __shared__ float red[NW * RBW * 32 * MAXNT];
+  const int wave = threadIdx.x >> 6;
+  const int nkc = K / 64;
+  const int nrb = R / 32;
+  const int units = n_items[0] * units_per_item;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int item = u / units_per_item;
+    const int rb0 = ((u - item * units_per_item) * (NW / KS) + wave / KS) * RBW;
+    const FfnItem it = items[item];
+    const char* slot = pool + (size_t)it.slot * stride;
+    const char* wbase = slot + off_codes;
+    const uint16_t* scales = reinterpret_cast<const uint16_t*>(slot + off_scales);
+    int done = 0;
+    for (; it.rows - done >= MAXNT; done += MAXNT)
+      tile_int4<KS, RBW, U, MAXNT, SWIGLU>(wbase, nkc, K, scales, aq, as, ag, perm, k,
+                                           it.row_begin + done, rb0, nrb, out_ld, out, red);
+    const int rest = it.rows - done, p = it.row_begin + done;
+#define TGEMV_INT4(NT_)                                                                           \
+  tile_int4<KS, RBW, U, NT_, SWIGLU>(wbase, nkc, K, scales, aq, as, ag, perm, k, p, rb0, nrb, out_ld, \
+                                     out, red)
+    TGEMV_REST(TGEMV_INT4)
+#undef TGEMV_INT4
+  }
+}
+#undef TGEMV_REST
+
+// Launch split for a pass with row_blocks_total 32-row blocks (over all
+// groups) of nchunks chunks each, measured on gfx950 for decode shapes:
+// - RBW (row blocks per wave) reuses each activation load for RBW rows. For
+//   bf16 it pays once tiles hold >= 2 activation rows; for int4, whose int8
+//   activations take twice the bytes of the codes they meet, RBW = 4 always.
+// - KS (waves splitting one row block's K range) is raised until the pass has
+//   ~8192 waves (bf16) while every wave keeps >= 8 chunks; the int4 split
+//   follows the measured optimum for its two K extents.
+struct Split {
+  int rbw, ks;
+};
+inline Split choose_split_bf16(int row_blocks_total, int nchunks, int maxnt) {
+  Split sp{1, 1};
+  if (maxnt >= 2 && row_blocks_total >= 1024) sp.rbw = 2;
+  const int ks_max = sp.rbw == 1 ? 16 : 8;
+  const long long blocks = row_blocks_total / sp.rbw;
+  while (sp.ks < ks_max && blocks * sp.ks < 8192 && nchunks / (sp.ks * 2) >= 8) sp.ks *= 2;
+  return sp;
+}
+inline Split choose_split_int4(int row_blocks_total, int nchunks) {
+  Split sp{4, 1};
+  const long long blocks = (row_blocks_total + 3) / 4;
+  if (nchunks >= 64)
+    sp.ks = 8;
+  else if (blocks < 1024)
+    while (sp.ks < 4 && nchunks / (sp.ks * 2) >= 8) sp.ks *= 2;
+  return sp;
+}
+
+constexpr int kGridCap = 8192;
+
+template <int KS>
+inline unsigned grid_for(int units) {
+  return (unsigned)(units < kGridCap ? units : kGridCap);
+}
+
+}  // namespace tgemv

@@ -122,16 +122,25 @@ int moe_route_permute(const void* x, int x_dtype, const void* w_router, const fl
  * store, which holds the same bytes so a fill is one contiguous copy). The
  * slot pool is one allocation: slot s starts at pool_base + s * slot_stride
  * (the fixed-base [num_slots, dim0, dim1] pool of the SeqMoE page).
- *   w13 at off_w13: 2F rows of H values, row 2n = gate row n, row 2n+1 = up
- *                   row n (fp32/bf16 values, or int4 codes: each 32-bit
- *                   little-endian word holds 8 consecutive codes c0..c7,
- *                   byte i = c_i in the low nibble, c_{i+4} in the high one)
- *   w2  at off_w2:  H rows of F values (down projection, same packing)
- *   int4 only: s13 at off_s13: [2F, H/128] bf16 scales (rows as w13);
- *              s2 at off_s2: [H, F/128] bf16 scales.
+ * Two matrices: W13 [2F, H] (row 2n = gate row n, row 2n+1 = up row n) at
+ * off_w13 and W2 [H, F] (down projection) at off_w2, each in a layout that
+ * depends on the format:
+ *   MOE_F32:      row-major.
+ *   MOE_BF16:     tile-major: element (r, c) of W [R, K] is bf16 number c % 8
+ *                 of the 16 bytes of lane (r % 32) + 32 ((c % 16) / 8) in the
+ *                 1 KB chunk (r / 32) * (K / 16) + c / 16. A chunk is the
+ *                 operand fragment of one 32x32x16 bf16 MFMA, and the chunks
+ *                 of a 32-row block are consecutive (R % 32 == 0).
+ *   MOE_INT4G128: tile-major: chunk (r / 32) * (K / 64) + c / 64 of 1 KB;
+ *                 lane (r % 32) + 32 ((c % 32) / 16) holds 16 bytes; bytes
+ *                 [8h, 8h + 8) hold the 16 codes of the 32-wide k step
+ *                 h = (c % 64) / 32; each 4-byte word covers 8 consecutive
+ *                 codes c0..c7 with byte i = c_i (low nibble) | c_{i+4} (high
+ *                 nibble). Scales: s13 at off_s13, [2F, H/128] bf16 row-major
+ *                 (rows as W13); s2 at off_s2, [H, F/128].
  * Every section starts on a 256-byte boundary; slot_bytes is a multiple of 4096.
- * Returns MOE_EINVAL for a bad format or sizes (H, F multiples of 16; of 128
- * for int4).
+ * Returns MOE_EINVAL for a bad format or sizes (H, F multiples of 16; H of 32
+ * for bf16; both of 128 for int4).
  */
 int moe_slot_layout(int H, int F, int w_dtype, size_t* slot_bytes,
                     size_t* off_w13, size_t* off_w2, size_t* off_s13, size_t* off_s2);

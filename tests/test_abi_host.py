@@ -56,34 +56,63 @@ def test_slot_layout_rejects_bad_sizes(lib):
         B.moe_slot_layout(256, 256, 7)
 
 
-def test_pack_dense_interleaves_gate_and_up(lib):
-    sh = W.reduced(W.shape_of("mixtral_e8k2_h4096_f14336_bf16"), H=64, F=32)
-    w = W.expert_weights(sh, 3)
-    lay = B.moe_slot_layout(64, 32, B.MOE_BF16)
+def _untile_bf16(buf, R, K):
+    """Inverse of the documented tile-major bf16 layout: [R, K] from slot bytes."""
+    t = buf.view(torch.int16).numpy().reshape(R // 32, K // 16, 2, 32, 8)  # rb, ks, half, row, elem
+    return torch.from_numpy(np.ascontiguousarray(t.transpose(0, 3, 1, 2, 4).reshape(R, K))).view(torch.bfloat16)
+
+
+def test_pack_f32_row_major_interleaved(lib):
+    sh = W.reduced(W.shape_of("tiny_e8k2_h256_f512_fp32"), H=64, F=32)
+    w = W.expert_weights(sh, 2)
+    lay = B.moe_slot_layout(64, 32, B.MOE_F32)
     dst = torch.zeros(lay["slot_bytes"], dtype=torch.uint8)
-    B.moe_pack_expert_host(dict(w), 64, 32, B.MOE_BF16, dst)
-    w13 = dst[lay["off_w13"]:lay["off_w13"] + 2 * 32 * 64 * 2].view(torch.bfloat16).view(64, 64)
+    B.moe_pack_expert_host(dict(w), 64, 32, B.MOE_F32, dst)
+    w13 = dst[:2 * 32 * 64 * 4].view(torch.float32).view(64, 64)
     assert torch.equal(w13[0::2], w["gate"]) and torch.equal(w13[1::2], w["up"])
-    w2 = dst[lay["off_w2"]:lay["off_w2"] + 64 * 32 * 2].view(torch.bfloat16).view(64, 32)
+    assert torch.equal(dst[lay["off_w2"]:lay["off_w2"] + 64 * 32 * 4].view(torch.float32).view(64, 32), w["down"])
+
+
+def test_pack_bf16_tile_major(lib):
+    sh = W.reduced(W.shape_of("mixtral_e8k2_h4096_f14336_bf16"), H=64, F=48)
+    w = W.expert_weights(sh, 3)
+    lay = B.moe_slot_layout(64, 48, B.MOE_BF16)
+    dst = torch.zeros(lay["slot_bytes"], dtype=torch.uint8)
+    B.moe_pack_expert_host(dict(w), 64, 48, B.MOE_BF16, dst)
+    w13 = _untile_bf16(dst[lay["off_w13"]:lay["off_w13"] + 96 * 64 * 2], 96, 64)
+    assert torch.equal(w13[0::2], w["gate"]) and torch.equal(w13[1::2], w["up"])
+    w2 = _untile_bf16(dst[lay["off_w2"]:lay["off_w2"] + 64 * 48 * 2], 64, 48)
     assert torch.equal(w2, w["down"])
+    # one spot check written out by hand: element (r=33, c=21) of W2
+    r, c = 33, 21
+    chunk = (r // 32) * (48 // 16) + c // 16
+    lane = (r % 32) + 32 * ((c % 16) // 8)
+    off = lay["off_w2"] + chunk * 1024 + lane * 16 + (c % 8) * 2
+    assert dst[off:off + 2].view(torch.bfloat16).item() == w["down"][r, c].item()
 
 
-def test_pack_int4_keeps_codes_and_scales(lib):
+def _untile_int4(buf, R, K):
+    """Inverse of the documented tile-major int4 layout: signed codes [R, K]."""
+    b = buf.numpy().reshape(R // 32, K // 64, 2, 32, 2, 2, 4)  # rb, kc, khalf, row, h, word, byte
+    lo, hi = (b & 0xF).astype(np.int64), (b >> 4).astype(np.int64)
+    codes = np.empty((R // 32, K // 64, 2, 32, 2, 2, 8), np.int64)
+    codes[..., :4], codes[..., 4:] = lo, hi
+    # k = kc*64 + h*32 + khalf*16 + word*8 + i
+    codes = codes.transpose(0, 3, 1, 4, 2, 5, 6).reshape(R, K)
+    return np.where(codes >= 8, codes - 16, codes)
+
+
+def test_pack_int4_tile_major_and_scales(lib):
     sh = W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), H=256, F=128)
     w = W.expert_weights(sh, 1)
     lay = B.moe_slot_layout(256, 128, B.MOE_INT4G128)
     dst = torch.zeros(lay["slot_bytes"], dtype=torch.uint8)
     B.moe_pack_expert_host(dict(w), 256, 128, B.MOE_INT4G128, dst)
-    w13 = dst[lay["off_w13"]:lay["off_w13"] + 256 * 128].view(256, 128).numpy()
-    # slot word order: word w of a row holds codes 8w..8w+7; byte i = code 8w+i (low) | 8w+4+i (high)
-    lo, hi = (w13 & 0xF).astype(np.int64), (w13 >> 4).astype(np.int64)
-    codes = np.empty((256, 256), np.int64)
-    for i in range(4):
-        codes[:, i::8] = lo[:, i::4]
-        codes[:, 4 + i::8] = hi[:, i::4]
-    codes = np.where(codes >= 8, codes - 16, codes)
+    codes = _untile_int4(dst[lay["off_w13"]:lay["off_w13"] + 256 * 128], 256, 256)
     assert np.array_equal(codes[0::2], O.decode_int4(w["gate_q"]))
     assert np.array_equal(codes[1::2], O.decode_int4(w["up_q"]))
+    down = _untile_int4(dst[lay["off_w2"]:lay["off_w2"] + 256 * 64], 256, 128)
+    assert np.array_equal(down, O.decode_int4(w["down_q"]))
     s13 = dst[lay["off_s13"]:lay["off_s13"] + 256 * 2 * 2].view(torch.bfloat16).view(256, 2)
     assert torch.equal(s13[0::2], w["gate_s"]) and torch.equal(s13[1::2], w["up_s"])
     s2 = dst[lay["off_s2"]:lay["off_s2"] + 256 * 1 * 2].view(torch.bfloat16).view(256, 1)
