@@ -1,23 +1,32 @@
 """Benchmark of the routed-expert MoE layer over a device-resident slot cache (one MI355X).
 
-Workload: one Mixtral-8x7B-shaped MoE layer in bf16 (8 experts, top-2
-renormalised, hidden 4096, expert FFN 14336 SwiGLU), synthetic seeded tokens
-x ~ N(0, 1) and weights ~ N(0, 0.02). A step is one pass of the whole layer
-(route, permute, slot lookup and residency plan, expert FFN over resident
-slots, combine) over one batch of tokens that are already in HBM.
+A step is one pass of the whole layer (route, permute, slot lookup and
+residency plan, expert FFN over resident slots with fills of the misses,
+shared experts, combine) over one batch of synthetic tokens already in HBM;
+for the 48-layer stack a step runs every layer once.
+
+Default workload: one Mixtral-8x7B-shaped MoE layer in bf16 (8 experts, top-2
+renormalised, hidden 4096, expert FFN 14336 SwiGLU), x ~ N(0, 1), weights ~
+N(0, 0.02).
 
   value     decode, 1 token per step, every routed expert resident (8 slots,
             random expert->slot relabelling): the hit path, tokens/s.
   also      decode 8 tokens and prefill 512 tokens on the same pool; and the
-            config's own cache (4 of 8 experts resident, random table) where
+            workload's own cache (4 of 8 experts resident, random table) where
             misses are copied from pinned host memory (PCIe-inclusive rate,
             reported separately, never the headline value).
-  roofline  the expert FFN (moe_expert_ffn) of the decode step: algorithmic
-            bytes (weights of the routed experts + tokens in + rows out)
-            per call divided by its HIP-event duration on the compute stream.
+  roofline  the expert FFN stage (one moe_expert_ffn call: group plan + W13
+            pass + W2 pass): algorithmic bytes (weights of the distinct routed
+            experts + tokens in + rows out) per call divided by its HIP-event
+            duration on the compute stream.
   cpu_baseline  the oracle (float64 NumPy) on a bounded sample of decode steps.
 
+Other workloads (--workload NAME) print a line of the same form for that
+workload: its hit path at each of its token counts, its own cache with fills,
+and for prefill the MFMA share (flops / time / dense peak) next to the HBM one.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--workload NAME] [--quick] [--case CASE]
 """
 from __future__ import annotations
 
@@ -38,21 +47,31 @@ from expert_offload_routed_amd import harness as Hn  # noqa: E402
 from expert_offload_routed_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-WORKLOAD = "mixtral_e8k2_h4096_f14336_bf16"
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "int4g128": 5000.0, "f32": 157.3}  # dense; int8 ops for int4 weights
+DEFAULT = "mixtral_e8k2_h4096_f14336_bf16"
+METRIC = "MoE-layer tokens/s at 1 GPU + achieved HBM GB/s (decode) / MFMA % (prefill)"
 
 
 def expert_bytes(shape) -> int:
-    es = {"f32": 4, "bf16": 2}[shape.wfmt]
-    return 3 * shape.H * shape.F * es
+    H, F = shape.H, shape.F
+    if shape.is_int4:  # codes, plus one bf16 scale per 128 weights
+        return 3 * H * F // 2 + 3 * (H * F // 128) * 2
+    return 3 * H * F * {"f32": 4, "bf16": 2}[shape.wfmt]
 
 
-def _run(layer, xs, out, timing):
+def _xbytes(shape) -> int:
+    return 4 if shape.xfmt == "f32" else 2
+
+
+def _run(layer, batches, out, timing):
+    """batches: list of steps, each a list of (layer index, x)."""
     layer.ctx.set_timing(timing)
     c0 = layer.counters()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for x in xs:
-        layer.forward(x, out=out)
+    for step in batches:
+        for li, x in step:
+            layer.forward(x, layer=li, out=out)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     c1 = layer.counters()
@@ -61,57 +80,132 @@ def _run(layer, xs, out, timing):
     return dt, {k: c1[k] - c0[k] for k in c1}, ms, n
 
 
-def timed(layer, shape, T, steps, warmup, label, ffn_timing=False):
-    """Warm up, then time exactly ``steps`` layer steps between two device synchronisations.
+def make_batches(shape, T, steps):
+    """steps x layers token batches: independent draws, or AR(1) per layer for a stack."""
+    if shape.layers == 1:
+        return [[(0, W.tokens(shape, T, step=i, device="cuda"))] for i in range(steps)]
+    seqs = [W.token_sequence(shape, T, steps, layer=l, device="cuda") for l in range(shape.layers)]
+    return [[(l, seqs[l][i]) for l in range(shape.layers)] for i in range(steps)]
 
-    With ffn_timing, the same steps run a second time with HIP events recorded on
-    the compute stream around each step's routed expert FFN (moe_expert_ffn), the
-    dominant kernel; the headline rate comes from the pass without events.
+
+def timed(layer, shape, T, steps, warmup, label, ffn_timing=False):
+    """Warm up, then time exactly ``steps`` steps between two device synchronisations.
+
+    With ffn_timing, the same steps run a second time with HIP events on the
+    compute stream around each layer call's expert FFN (routed groups, fill
+    waves, shared experts); the headline rate comes from the pass without events.
     """
-    xs = [W.tokens(shape, T, step=i, device="cuda") for i in range(steps + warmup)]
+    batches = make_batches(shape, T, steps + warmup)
     out = torch.empty(T, shape.H, dtype=layer.out_dtype, device="cuda")
-    for x in xs[:warmup]:
-        layer.forward(x, out=out)
-    dt, cnt, _, _ = _run(layer, xs[warmup:], out, False)
-    distinct = cnt["distinct"] / steps
+    _run(layer, batches[:warmup], out, False)
+    dt, cnt, _, _ = _run(layer, batches[warmup:], out, False)
+    calls = steps * shape.layers
     res = {"tokens_per_step": T, "tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3,
-           "distinct_per_step": distinct, "fills_per_step": cnt["fills"] / steps}
+           "distinct_per_layer_call": cnt["distinct"] / calls,
+           "fills_per_step": cnt["fills"] / steps}
+    if cnt["distinct"] > 0:
+        res["hit_rate"] = cnt["hits"] / cnt["distinct"]
     if ffn_timing:
-        dt2, cnt2, ms, n = _run(layer, xs[warmup:], out, True)
-        # algorithmic bytes of the expert FFN per step: the routed experts' weights
-        # (every distinct expert is read once), tokens in, one fp32 row out per assignment
-        byts = (cnt2["distinct"] / steps) * expert_bytes(shape) + T * shape.H * 2 + T * shape.k * shape.H * 4
-        res["ffn"] = {"calls": n, "avg_us": 1e3 * ms / n, "avg_bytes": byts,
-                      "gbs": byts / (ms / n * 1e-3) / 1e9, "ms_per_step_with_events": dt2 / steps * 1e3}
+        dt2, cnt2, ms, n = _run(layer, batches[warmup:], out, True)
+        eb = expert_bytes(shape)
+        # algorithmic bytes of the expert FFN per layer call: each distinct routed
+        # expert's weights once, the shared experts' weights, tokens in, fp32 rows out
+        per_call = (cnt2["distinct"] / calls) * eb + shape.n_shared * eb + T * shape.H * _xbytes(shape) \
+            + T * (shape.k + shape.n_shared) * shape.H * 4
+        flops = 6.0 * T * (shape.k + shape.n_shared) * shape.H * shape.F
+        us = 1e3 * ms / n
+        res["ffn"] = {"calls": n, "avg_us": us, "bytes_per_call": per_call,
+                      "gbs": per_call / (us * 1e-6) / 1e9,
+                      "mfma_frac": flops / (us * 1e-6) / (MFMA_PEAK_TFLOPS[shape.wfmt] * 1e12),
+                      "ms_per_step_with_events": dt2 / steps * 1e3}
     print(f"# {label}: {res}", file=sys.stderr, flush=True)
     return res
 
 
+def recorded_traffic(key):
+    """HBM bytes per FFN call (FETCH_SIZE + WRITE_SIZE runs, calibrated), as recorded in
+    profiles/ffn_traffic.json; None when absent or when any kernel source changed since."""
+    import glob
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "ffn_traffic.json")))[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha1()
+    for f in sorted(glob.glob(os.path.join(ROOT, "expert_offload_routed_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return rec["read_bytes"] + rec["write_bytes"] if h.hexdigest() == rec["csrc_sha1"] else None
+
+
+def all_resident(shape):
+    """Every layer-expert in its own slot, in a seeded random slot order."""
+    own = [(l, e) for l in range(shape.layers) for e in range(shape.E)]
+    rng = np.random.Generator(np.random.PCG64(W.seed_for(shape, "residency", len(own), 1)))
+    return [own[i] for i in rng.permutation(len(own))]
+
+
 def cpu_baseline(shape, budget_s=15.0):
-    """The oracle as it stands, on a bounded sample of decode steps (T=1)."""
+    """The oracle as it stands, on a bounded sample of decode steps (T=1) of layer 0."""
     import oracle as O
     from threadpoolctl import threadpool_info
 
-    experts = {e: {n: t.cpu() for n, t in W.expert_weights(shape, e, device="cuda").items()}
-               for e in range(shape.E)}
+    E = shape.E
+    cache = {}
+    load_s = [0.0]  # drawing the synthetic weights is setup, not oracle work: not counted
+
+    def weights_of(e):
+        if e not in cache:
+            t = time.perf_counter()
+            cache[e] = {n: v.cpu() for n, v in
+                        W.expert_weights(shape, W.blob_of(shape, 0, e), device="cuda").items()}
+            load_s[0] += time.perf_counter() - t
+        return cache[e]
+
+    shared = [{n: t.cpu() for n, t in W.shared_expert_weights(shape, j, device="cuda").items()}
+              for j in range(shape.n_shared)]
     wr, b = W.router(shape)
-    pool = O.SlotPool(shape.E, 1, shape.E)
-    for e in range(shape.E):
-        pool.fill(e, experts[e])
-        pool.lut[0, e] = e
+    # an oracle pool of E slots, empty at first: each expert is loaded on its first use
+    pool = O.SlotPool(E, 1, E)
+    planner = O.LruSlotPlanner(E, 1, E, [None] * E)
     n, t0 = 0, time.perf_counter()
     while True:
         x = W.tokens(shape, 1, step=n)
-        O.moe_layer(x, wr, b, shape.k, layer=0, pool=pool, planner=None,
-                    weights_of_expert=lambda e: experts[e])
+        O.moe_layer(x, wr, b, shape.k, layer=0, pool=pool, planner=planner,
+                    weights_of_expert=weights_of, shared=shared or None)
         n += 1
-        dt = time.perf_counter() - t0
+        dt = time.perf_counter() - t0 - load_s[0]
         if dt >= budget_s or n >= 64:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} decode steps of 1 token (float64 NumPy oracle, weights upcast per use), "
-                      f"{dt:.1f} s"}
+            "sample": f"{n} decode steps of 1 token, layer 0 (float64 NumPy oracle, weights upcast "
+                      f"per use), {dt:.1f} s"}
+
+
+def calib_copy(steps):
+    """Plain device copy of 1 GiB, for scaling the HBM byte counters (FETCH_SIZE, WRITE_SIZE)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    print(f"# copy 1 GiB x {steps}: {2 * n * steps / dt / 1e9:.1f} GB/s (read + write)", file=sys.stderr)
+
+
+# token counts timed per workload (hit path) and the caches with fills
+PLANS = {
+    "tiny_e8k2_h256_f512_fp32": dict(hit=[16], miss=[]),
+    "mixtral_e8k2_h4096_f14336_bf16": dict(hit=[1, 8, 512], miss=[(4, 1)]),
+    "qwen3moe_l48_e128k8_h2048_f768_bf16": dict(hit=[1, 16], miss=[(2765, 1), (2765, 16)]),
+    "dsv2lite_e64k6s2_h2048_f1408_bf16": dict(hit=[1, 32, 256, 1024], miss=[(16, 1), (32, 1), (48, 1)]),
+    "dsv3_e256k8s1_h7168_f2048_int4": dict(hit=[1, 32, 4096], miss=[(84, 1)]),
+}
+CASES = {"decode1": 1, "decode8": 8, "prefill512": 512}
 
 
 def main():
@@ -119,51 +213,65 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(PLANS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--quick", action="store_true", help="headline workload only")
-    ap.add_argument("--case", default=None, choices=["decode1", "decode8", "prefill512", "fills"],
-                    help="run one case of the workload only (for profiling); prints no JSON line")
+    ap.add_argument("--quick", action="store_true", help="headline case only")
+    ap.add_argument("--case", default=None,
+                    help="one case only, for profiling (prints no JSON line): decode1, decode8, "
+                         "prefill512, fills, T<n> (hit path at n tokens), calib_copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU form of "
               "this layer is a design, not built here.", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
-    shape = W.shape_of(WORKLOAD)
     K, Wm = args.steps, args.warmup
+    if args.case == "calib_copy":
+        calib_copy(K)
+        return
+    shape = W.shape_of(args.workload)
+    plan = PLANS[args.workload]
+    cfg = W.WORKLOADS[args.workload]
+    t_max = max(plan["hit"])
+    store = Hn.ExpertStore(shape)
+    resident = all_resident(shape)
+    S_hit = len(resident)
 
-    resident = W.initial_residency(shape, shape.E, "random")  # all 8 experts, relabelled slots
-    layer = Hn.SlotCacheLayer(shape, shape.E, resident, t_max=512)
     if args.case is not None:
         if args.case == "fills":
-            cfg = W.WORKLOADS[WORKLOAD]
-            small = Hn.SlotCacheLayer(shape, cfg["slots"][0],
-                                      W.initial_residency(shape, cfg["slots"][0], "random"), t_max=8,
-                                      store=layer.store)
-            timed(small, shape, 1, K, Wm, "decode T=1, 4 of 8 resident, fills over PCIe")
+            S, T = plan["miss"][0]
+            small = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]),
+                                      t_max=T, store=store)
+            timed(small, shape, T, K, Wm, f"T={T}, {S} slots, fills over PCIe")
         else:
-            T = {"decode1": 1, "decode8": 8, "prefill512": 512}[args.case]
+            T = CASES[args.case] if args.case in CASES else int(args.case.lstrip("T"))
+            layer = Hn.SlotCacheLayer(shape, S_hit, resident, t_max=T, store=store)
             timed(layer, shape, T, K, Wm, args.case, ffn_timing=True)
         return
-    head = timed(layer, shape, 1, K, Wm, "decode T=1 hit path", ffn_timing=True)
+
+    layer = Hn.SlotCacheLayer(shape, S_hit, resident, t_max=t_max, store=store)
+    head_T = plan["hit"][0]
+    head = timed(layer, shape, head_T, K, Wm, f"T={head_T} hit path", ffn_timing=True)
     also = {}
     if not args.quick:
-        also["decode_T8_hit"] = timed(layer, shape, 8, K, Wm, "decode T=8 hit path", ffn_timing=True)
-        also["prefill_T512_hit"] = timed(layer, shape, 512, max(K // 10, 3), 2, "prefill T=512 hit path",
-                                         ffn_timing=True)
+        for T in plan["hit"][1:]:
+            steps = K if T <= 64 else max(K // 10, 3)
+            also[f"T{T}_hit"] = timed(layer, shape, T, steps, 2, f"T={T} hit path", ffn_timing=True)
         del layer
         torch.cuda.empty_cache()
-        cfg = W.WORKLOADS[WORKLOAD]
-        store = Hn.ExpertStore(shape)
-        small = Hn.SlotCacheLayer(shape, cfg["slots"][0], W.initial_residency(shape, cfg["slots"][0], "random"),
-                                  t_max=8, store=store)
-        r = timed(small, shape, 1, max(K // 5, 5), 2, "decode T=1, 4 of 8 resident, fills over PCIe")
-        r["fill_bytes_per_step"] = r["fills_per_step"] * small.stride
-        also["decode_T1_4of8_with_fills"] = r
+        for S, T in plan["miss"]:
+            small = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]),
+                                      t_max=T, store=store)
+            steps = max(K // 5, 5) if shape.layers == 1 else max(K // 5, 8)
+            r = timed(small, shape, T, steps, 2, f"T={T}, {S} slots ({cfg['residency']}), fills over PCIe")
+            r["fill_bytes_per_step"] = r["fills_per_step"] * store.stride
+            also[f"T{T}_{S}slots_with_fills"] = r
+            del small
+            torch.cuda.empty_cache()
 
     ffn = head["ffn"]
     line = {
-        "metric": "MoE-layer tokens/s at 1 GPU + achieved HBM GB/s (decode) / MFMA % (prefill)",
+        "metric": METRIC,
         "value": round(head["tokens_per_s"], 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -173,18 +281,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": {"bf16": "bf16", "f32": "f32", "int4g128": "int4 weights x int8 activations"}[shape.wfmt],
         "data": "synthetic",
-        "config": {"workload": "Mixtral-8x7B-shaped MoE layer, bf16, E=8 top-2, H=4096, F=14336, "
-                               "decode 1 token/step, all experts resident (hit path)",
-                   "tokens_per_step": 1, "slots": shape.E, "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "moe_expert_ffn (plan + W13 GEMV + W2 GEMV launches, one call per step)", "bound": "hbm",
-                     "achieved": round(ffn["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ffn["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "avg_us": round(ffn["avg_us"], 2), "bytes_per_call": int(ffn["avg_bytes"])},
+        "config": {"workload": f"{args.workload}: E={shape.E} top-{shape.k}, H={shape.H}, F={shape.F}"
+                               + (f", {shape.n_shared} shared" if shape.n_shared else "")
+                               + (f", {shape.layers} layers" if shape.layers > 1 else "")
+                               + f", decode {head_T} token/step, every expert resident (hit path)",
+                   "tokens_per_step": head_T, "slots": S_hit, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "moe_expert_ffn (group plan + W13 GEMV + W2 GEMV launches, one call per "
+                               "layer step)",
+                     "bound": "hbm", "achieved": round(ffn["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ffn["gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(f"{args.workload}/decode{head_T}"),
+                     "avg_us": round(ffn["avg_us"], 2), "bytes_per_call": int(ffn["bytes_per_call"])},
         "also": also,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and shape.layers == 1:
         line["cpu_baseline"] = cpu_baseline(shape)
     print(json.dumps(line), flush=True)
 

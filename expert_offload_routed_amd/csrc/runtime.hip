@@ -76,7 +76,7 @@ struct moe_layer_ctx {
   std::vector<int32_t> wave_of, is_hit, fill_e, fill_s, fill_w;
   hipEvent_t ev_fill, ev_compute;
   int64_t totals[4];  // over completed plans: distinct, hits, fills, waves
-  // timing of the routed FFN calls: one event pair per step, collected lazily
+  // timing of the expert FFN calls (routed, then shared): one event pair per step, collected lazily
   int timing;
   hipEvent_t tev0[kRing], tev1[kRing];
   int t_head, t_count;
@@ -500,11 +500,6 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
         return rc;
     }
   }
-  if (timing) {
-    const int tr = (c->t_head + c->t_count) % kRing;
-    if ((e = hipEventRecord(c->tev1[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
-    c->t_count += 1;
-  }
   const float* shared_y = nullptr;
   if (c->n_shared) {
     const int n = c->n_shared;
@@ -528,6 +523,11 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
                              c->err, c->sh_ws, c->sh_ws_bytes, c->cs)) != MOE_OK)
       return rc;
     shared_y = c->sh_y;
+  }
+  if (timing) {
+    const int tr = (c->t_head + c->t_count) % kRing;
+    if ((e = hipEventRecord(c->tev1[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
+    c->t_count += 1;
   }
   if ((rc = moe_combine(c->y_perm, c->inv, c->topw, T, k, H, shared_y, c->n_shared, out, out_dtype,
                         c->cs)) != MOE_OK)

@@ -96,7 +96,8 @@ int moe_ctx_outputs(const moe_layer_ctx* ctx, float** logits, int32_t** ids, flo
                     int32_t** perm, int32_t** offsets, int32_t** inv);
 
 /* moe_ctx_set_timing: when enabled, each step records HIP events on the
- * compute stream around its routed moe_expert_ffn calls; moe_ctx_ffn_time
+ * compute stream around its expert FFN calls (the routed groups, including
+ * any fill waves, then the shared experts); moe_ctx_ffn_time
  * returns the summed milliseconds and the number of timed steps (resetting
  * happens on moe_ctx_set_timing). */
 int moe_ctx_set_timing(moe_layer_ctx* ctx, int enable);
