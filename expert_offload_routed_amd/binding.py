@@ -308,6 +308,8 @@ class LayerContext:
             raise ValueError("blob_of must hold L*E entries")
         if tags.dtype != torch.int64 or tags.numel() < S or owner.numel() < S or lut.numel() < L * E:
             raise ValueError("tables too small")
+        if pool.numel() < (S + n_shared) * slot_stride:
+            raise ValueError("pool must hold S routed slots followed by n_shared shared slots")
         self._keep = (pool, lut, owner, tags, host_store, shared_pool, err)
         self.handle = _vp()
         _call("moe_ctx_create", ctypes.byref(self.handle), t_max, H, F, E, k, L, S, x_dtype, w_dtype,

@@ -10,8 +10,12 @@
 //
 // Kernels (all on the caller's stream):
 //   ffn_plan_kernel  one workgroup: selected, non-empty, resident groups go to
-//                    the GEMV list (<= kGemvMaxRows rows) or are cut into
+//                    the GEMV list (<= small_max rows) or are cut into
 //                    kGemmBM-row MFMA tiles; absent experts set MOE_ERR_ABSENT.
+//                    Inside the library a call may also carry the shared
+//                    experts as groups E .. E+n_shared-1 (T rows each, slots
+//                    shared_slot0 + s), so one plan and one pair of weight
+//                    passes cover the routed and the shared experts.
 //   GEMV passes      decode groups: tile-major bf16 weights (tile_gemv.h),
 //                    every load a contiguous 1 KB chunk, split-K over the
 //                    waves of a workgroup; row-major fp32 weights
@@ -33,19 +37,20 @@ constexpr int kGemvGridCap = 8192;  // workgroups of a GEMV pass (they loop over
 
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ lut,
-    const int32_t* __restrict__ mask, int E, int num_slots, int small_max,
-    FfnItem* __restrict__ items, int32_t* __restrict__ n_items, GemmTile* __restrict__ tiles,
-    int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_word) {
+    const int32_t* __restrict__ mask, int E, int n_shared, int shared_slot0, int num_slots,
+    int small_max, FfnItem* __restrict__ items, int32_t* __restrict__ n_items,
+    GemmTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_word) {
   __shared__ int s_wave[40];
   const int e = threadIdx.x;
   int rows = 0, slot = -1, begin = 0;
   bool take = false;
-  if (e < E) {
+  if (e < E + n_shared) {
     begin = offsets[e];
     rows = offsets[e + 1] - begin;
-    take = rows > 0 && (mask == nullptr || mask[e] != 0);
+    const bool routed = e < E;
+    take = rows > 0 && (!routed || mask == nullptr || mask[e] != 0);
     if (take) {
-      slot = lut[e];
+      slot = routed ? lut[e] : shared_slot0 + (e - E);
       if (slot < 0 || slot >= num_slots) {
         atomicOr(err_word, MOE_ERR_ABSENT);
         take = false;
@@ -163,39 +168,43 @@ void launch_f32(const void* x, const int32_t* perm, int k, const FfnItem* items,
 }  // namespace
 
 void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
-                     int num_slots, int small_max, FfnItem* items, int32_t* n_items,
-                     GemmTile* tiles, int32_t* n_tiles, int32_t* err_word, hipStream_t s) {
-  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, lut, mask, E, num_slots,
-                     small_max, items, n_items, tiles, n_tiles, err_word);
+                     int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
+                     int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
+                     hipStream_t s) {
+  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, lut, mask, E, n_shared,
+                     shared_slot0, num_slots, small_max, items, n_items, tiles, n_tiles, err_word);
 }
 
-FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype) {
+int ffn_small_max(int T, int k, int E, int n_shared) {
+  // with many rows per group on average, every group takes the MFMA tiles and
+  // the GEMV passes are not launched at all
+  const long long rows = (long long)T * (k + n_shared);
+  return rows > 16LL * (E + n_shared) ? 0 : kGemvMaxRows;
+}
+
+FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype, int n_shared) {
   FfnWorkspace w{};
-  const size_t rows = (size_t)T * k;
-  // upper bound on MFMA tiles: sum over large groups of ceil(rows / BM)
-  const long long large = (long long)(rows / (kGemvMaxRows + 1));
-  w.max_tiles = (int)(rows / kGemmBM + (large < E ? large : E) + 1);
+  const size_t rows = (size_t)T * (k + n_shared);
+  const size_t groups = (size_t)E + n_shared;
+  // upper bound on MFMA tiles: sum over groups of ceil(rows / BM) <= rows / BM + groups
+  w.max_tiles = (int)(rows / kGemmBM + (rows < groups ? rows : groups) + 1);
   size_t off = 256;  // n_items at offset 0, n_tiles at offset 4
   w.items = off;
-  off = align_up(off + (size_t)E * sizeof(FfnItem), 256);
+  off = align_up(off + groups * sizeof(FfnItem), 256);
   w.tiles = off;
   off = align_up(off + (size_t)w.max_tiles * sizeof(GemmTile), 256);
   w.h = off;
   off = align_up(off + rows * F * sizeof(float), 256);
   if (w_dtype == MOE_INT4G128) {
-    // int8 rows, their fp32 scales and int32 sums per 128-value group
+    // int8 rows and their fp32 scales
     w.xq = off;
     off = align_up(off + (size_t)T * H, 256);
     w.xs = off;
     off = align_up(off + (size_t)T * sizeof(float), 256);
-    w.xg = off;
-    off = align_up(off + (size_t)T * (H / 128) * sizeof(int32_t), 256);
     w.hq = off;
     off = align_up(off + rows * F, 256);
     w.hs = off;
     off = align_up(off + rows * sizeof(float), 256);
-    w.hg = off;
-    off = align_up(off + rows * (F / 128) * sizeof(int32_t), 256);
   }
   w.total = off;
   return w;
@@ -203,13 +212,13 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype
 
 extern "C" size_t moe_ffn_workspace_bytes(int T, int H, int F, int E, int k, int w_dtype) {
   if (T < 0 || H <= 0 || F <= 0 || E <= 0 || k <= 0) return 0;
-  return ffn_workspace_layout(T, H, F, E, k, w_dtype).total;
+  return ffn_workspace_layout(T, H, F, E, k, w_dtype, 0).total;
 }
 
 int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* lut,
-             const int32_t* group_mask, const char* pool, size_t stride, int num_slots,
-             const SlotLayout& lay, int T, int H, int F, int E, int k, float* y, int32_t* err,
-             char* ws, const FfnWorkspace& wl, hipStream_t s);
+             const int32_t* group_mask, int n_shared, int shared_slot0, const char* pool,
+             size_t stride, int num_slots, const SlotLayout& lay, int T, int H, int F, int E, int k,
+             float* y, int32_t* err, char* ws, const FfnWorkspace& wl, hipStream_t s);
 
 extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
                               const int32_t* offsets, const int32_t* lut,
@@ -217,7 +226,17 @@ extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
                               int num_slots, int w_dtype, int T, int H, int F, int E, int k,
                               float* y_perm, int32_t* err_word, void* workspace, size_t ws_bytes,
                               hipStream_t stream) {
-  MOE_CHECK_ARG(T >= 0 && k >= 1 && k <= E && E <= 1024);
+  return expert_ffn(x, x_dtype, perm, offsets, lut, group_mask, 0, 0, pool_base, slot_stride,
+                    num_slots, w_dtype, T, H, F, E, k, y_perm, err_word, workspace, ws_bytes,
+                    stream);
+}
+
+int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* offsets,
+               const int32_t* lut, const int32_t* group_mask, int n_shared, int shared_slot0,
+               const void* pool_base, size_t slot_stride, int num_slots, int w_dtype, int T, int H,
+               int F, int E, int k, float* y_perm, int32_t* err_word, void* workspace,
+               size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && k >= 1 && k <= E && n_shared >= 0 && E + n_shared <= 1024);
   MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
   SlotLayout lay;
   if (slot_layout(H, F, w_dtype, &lay) != MOE_OK) return MOE_EINVAL;
@@ -226,7 +245,7 @@ extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
   MOE_CHECK_ARG(x && perm && offsets && lut && pool_base && y_perm && err_word && workspace);
   MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)pool_base % 256) == 0);
   MOE_CHECK_ARG(((uintptr_t)y_perm % 16) == 0);
-  const FfnWorkspace ws = ffn_workspace_layout(T, H, F, E, k, w_dtype);
+  const FfnWorkspace ws = ffn_workspace_layout(T, H, F, E, k, w_dtype, n_shared);
   MOE_CHECK_ARG(ws_bytes >= ws.total && ((uintptr_t)workspace % 256) == 0);
   // supported pairs: fp32 tokens with fp32 weights; bf16 tokens with bf16 or int4 weights
   if (w_dtype == MOE_F32 && x_dtype != MOE_F32) return MOE_EUNSUPPORTED;
@@ -235,8 +254,9 @@ extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
 
   char* wsb = static_cast<char*>(workspace);
   if (w_dtype == MOE_INT4G128)
-    return ffn_int4(x, perm, offsets, lut, group_mask, static_cast<const char*>(pool_base),
-                    slot_stride, num_slots, lay, T, H, F, E, k, y_perm, err_word, wsb, ws, stream);
+    return ffn_int4(x, perm, offsets, lut, group_mask, n_shared, shared_slot0,
+                    static_cast<const char*>(pool_base), slot_stride, num_slots, lay, T, H, F, E, k,
+                    y_perm, err_word, wsb, ws, stream);
 
   int32_t* n_items = reinterpret_cast<int32_t*>(wsb);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(wsb + 4);
@@ -244,15 +264,15 @@ extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
   GemmTile* tiles = reinterpret_cast<GemmTile*>(wsb + ws.tiles);
   void* hbuf = wsb + ws.h;
   const long long tk = (long long)T * k;
-  const int max_items = (int)(tk < E ? tk : E);
   const bool bf16 = (w_dtype == MOE_BF16);
   // a group holds at most T rows (a token picks an expert once)
-  const int small_max = bf16 ? kGemvMaxRows : INT_MAX;
-  const int max_tiles = (bf16 && T > kGemvMaxRows) ? ws.max_tiles : 0;
+  const int small_max = bf16 ? ffn_small_max(T, k, E, n_shared) : INT_MAX;
+  const int max_items = small_max == 0 ? 0 : (int)(tk < E ? tk : E) + n_shared;
+  const int max_tiles = (bf16 && T > small_max) ? ws.max_tiles : 0;
   MOE_CHECK_ARG(max_tiles <= 65535);
 
-  launch_ffn_plan(offsets, lut, group_mask, E, num_slots, small_max, items, n_items, tiles, n_tiles,
-                  err_word, stream);
+  launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max, items,
+                  n_items, tiles, n_tiles, err_word, stream);
   const char* pool = static_cast<const char*>(pool_base);
   const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;  // rows of the largest GEMV group
   if (bf16) {

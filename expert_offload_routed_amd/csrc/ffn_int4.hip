@@ -11,14 +11,15 @@
 // the row scale are applied in fp32. The SwiGLU intermediate is formed in
 // fp32 and quantised per row the same way before the down projection.
 //
-// Codes are used in offset form u = q + 8 (0..15: bytes that are valid
-// non-negative int8 for sdot4 and the int8 MFMA); sum q x = sum u x - 8 sum x,
-// where sum x over a 128-value group is precomputed per activation row.
+// Codes are expanded to int8 bytes holding 16 q: a code moved to the high
+// nibble of its byte keeps its sign, so the expansion is two masks and a shift
+// and no correction term is needed. The integer sums are then 16 sum q x
+// (exact) and the group scale carries the factor 1/16 (exact in fp32).
 // Slot layout (moe_slot_layout): tile-major 1 KB chunks of 32 rows x 64 codes;
 // a 32-bit word holds 8 consecutive codes, low nibbles = codes 0..3, high
 // nibbles = codes 4..7, so
-//   u_lo = (w ^ 0x88888888) & 0x0F0F0F0F, u_hi = ((w ^ 0x88888888) >> 4) & 0x0F0F0F0F
-// are two words of 4 consecutive int8 values in natural order.
+//   (w << 4) & 0xF0F0F0F0  and  w & 0xF0F0F0F0
+// are two words of 4 consecutive int8 values (16 q) in natural order.
 #include "common.h"
 #include "ffn_internal.h"
 #include "tile_gemv.h"
@@ -30,32 +31,34 @@ typedef __attribute__((__vector_size__(16 * sizeof(int)))) int intx16;
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
 
-__device__ __forceinline__ uint32_t u_lo(uint32_t w) { return (w ^ 0x88888888u) & 0x0F0F0F0Fu; }
-__device__ __forceinline__ uint32_t u_hi(uint32_t w) { return ((w ^ 0x88888888u) >> 4) & 0x0F0F0F0Fu; }
 
 // ------------------------------------------------------ row quantisation ---
 // One workgroup per row of K values (K % 128 == 0): s = max|v| / 127,
-// q = clip(rint(v / s), -127, 127), gsum[g] = sum of q over group g.
+// q = clip(rint(v / s), -127, 127).
 // With offsets != NULL, row p is skipped unless it belongs to a selected,
-// resident group (the rows this call computes).
+// resident group (the rows this call computes): groups 0..E-1 are routed
+// (lut, mask), groups E..E+n_shared-1 shared (always computed).
 template <int IN>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const void* __restrict__ in, int K, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ lut, const int32_t* __restrict__ mask, int E, int num_slots,
-    int8_t* __restrict__ q, float* __restrict__ s, int32_t* __restrict__ gsum) {
+    const int32_t* __restrict__ lut, const int32_t* __restrict__ mask, int E, int n_shared,
+    int num_slots, int8_t* __restrict__ q, float* __restrict__ s) {
   __shared__ float s_max[4];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (offsets) {
-    int lo = 0, hi = E;  // largest e with offsets[e] <= row
+    const int G = E + n_shared;
+    int lo = 0, hi = G;  // largest e with offsets[e] <= row
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (offsets[mid] <= row) lo = mid; else hi = mid;
     }
     const int e = lo;
-    if (row >= offsets[E]) return;
-    if (mask && mask[e] == 0) return;
-    const int slot = lut[e];
-    if (slot < 0 || slot >= num_slots) return;
+    if (row >= offsets[G]) return;
+    if (e < E) {
+      if (mask && mask[e] == 0) return;
+      const int slot = lut[e];
+      if (slot < 0 || slot >= num_slots) return;
+    }
   }
   float v[4][8];
   float amax = 0.f;
@@ -90,24 +93,17 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e0 = c * 2048 + tid * 8;
-    int part = 0;
     if (e0 < K) {
       uint32_t w0 = 0, w1 = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float r = rintf(v[c][i] / sc);
         r = fminf(fmaxf(r, -127.f), 127.f);
-        const int qi = (int)r;
-        part += qi;
-        const uint32_t b = (uint32_t)(qi & 0xFF);
+        const uint32_t b = (uint32_t)((int)r & 0xFF);
         if (i < 4) w0 |= b << (8 * i); else w1 |= b << (8 * (i - 4));
       }
       *reinterpret_cast<uint2*>(q + (size_t)row * K + e0) = make_uint2(w0, w1);
     }
-    // 16 consecutive threads hold one 128-value group
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
-    if (e0 < K && (tid & 15) == 0) gsum[(size_t)row * (K / 128) + e0 / 128] = part;
   }
 }
 
@@ -122,16 +118,15 @@ constexpr int kQAhead = 3;      // K tiles of global loads in flight
 // tile-major codes, one per wave), K tiles of 128 = one scale group. A wave's
 // code fragments for a K tile are two whole 1 KB chunks (one 16-byte load per
 // lane each, cacheable so the M-tiles of a group share them in L2); the int8
-// activation tile and its group sums go through LDS. Each K tile: 4 v_mfma_i32_32x32x32_i8 per 32x32
-// accumulator into int32, then folded into fp32 with the group scale.
+// activation tile goes through LDS. Each K tile: 4 v_mfma_i32_32x32x32_i8 per
+// 32x32 accumulator into int32, then folded into fp32 with the group scale.
 template <int PASS>
 __global__ __launch_bounds__(256) void gemm_w4a8_kernel(
-    const int8_t* __restrict__ aq, const float* __restrict__ as, const int32_t* __restrict__ ag,
+    const int8_t* __restrict__ aq, const float* __restrict__ as,
     const int32_t* __restrict__ perm, int k, const GemmTile* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const char* __restrict__ pool, size_t stride,
     size_t off_codes, size_t off_scales, int N, int K, int out_ld, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) int8_t sA[2][QBM * A_LD];
-  __shared__ int sG[2][QBM];
   if ((int)blockIdx.y >= n_tiles[0]) return;
   const GemmTile tl = tiles[blockIdx.y];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -149,14 +144,6 @@ __global__ __launch_bounds__(256) void gemm_w4a8_kernel(
     const int p = tl.row_begin + (avalid[i] ? m : 0);
     arow[i] = aq + (size_t)((PASS == 1) ? perm[p] / k : p) * K;
   }
-  // group-sum row of threads 0..QBM-1
-  int grow = 0;
-  bool gvalid = false;
-  if (tid < QBM) {
-    gvalid = tid < tl.rows;
-    const int p = tl.row_begin + (gvalid ? tid : 0);
-    grow = (PASS == 1) ? perm[p] / k : p;
-  }
   // this wave's 32-row block
   int rb = blockIdx.x * 4 + wave;
   const bool nvalid = rb < nrb;
@@ -169,7 +156,6 @@ __global__ __launch_bounds__(256) void gemm_w4a8_kernel(
   struct Stage {
     u32x4 a[QMF], b[2];
     float sw;
-    int g;
   };
   Stage st[kQAhead];
   auto gload = [&](Stage& r, int kt) {
@@ -179,16 +165,13 @@ __global__ __launch_bounds__(256) void gemm_w4a8_kernel(
     // cacheable: the other M-tiles of the group read the same chunks
 #pragma unroll
     for (int c = 0; c < 2; ++c) r.b[c] = ld16(wchunks + (size_t)(2 * kt + c) * 1024);
-    r.sw = bf16_to_f32(srow[kt]);
-    r.g = (tid < QBM && gvalid) ? ag[(size_t)grow * gld + kt] : 0;
+    r.sw = bf16_to_f32(srow[kt]) * 0.0625f;  // codes enter as 16 q
   };
   auto astore = [&](const Stage& r, int buf) {
 #pragma unroll
     for (int i = 0; i < QMF; ++i)
       *reinterpret_cast<u32x4*>(&sA[buf][((tid >> 3) + 32 * i) * A_LD + (tid & 7) * 16]) = r.a[i];
-    if (tid < QBM) sG[buf][tid] = r.g;
   };
-  const int live = (tl.rows + 31) / 32;
 
   float accf[QMF][16];
 #pragma unroll
@@ -214,28 +197,23 @@ __global__ __launch_bounds__(256) void gemm_w4a8_kernel(
       const u32x4& cw = mine.b[ks >> 1];
       const uint32_t w0 = (ks & 1) ? cw.z : cw.x, w1 = (ks & 1) ? cw.w : cw.y;
       intx4 b;
-      b[0] = (int)u_lo(w0);
-      b[1] = (int)u_hi(w0);
-      b[2] = (int)u_lo(w1);
-      b[3] = (int)u_hi(w1);
+      b[0] = (int)((w0 << 4) & 0xF0F0F0F0u);
+      b[1] = (int)(w0 & 0xF0F0F0F0u);
+      b[2] = (int)((w1 << 4) & 0xF0F0F0F0u);
+      b[3] = (int)(w1 & 0xF0F0F0F0u);
+      // every fragment, rows or not: a uniform MFMA chain schedules better than skipping
 #pragma unroll
       for (int j = 0; j < QMF; ++j) {
-        if (j < live) {
-          const intx4 a = *reinterpret_cast<const intx4*>(
-              &sA[buf][(j * 32 + (lane & 31)) * A_LD + ks * 32 + 16 * (lane >> 5)]);
-          acci[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acci[j], 0, 0, 0);
-        }
+        const intx4 a = *reinterpret_cast<const intx4*>(
+            &sA[buf][(j * 32 + (lane & 31)) * A_LD + ks * 32 + 16 * (lane >> 5)]);
+        acci[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acci[j], 0, 0, 0);
       }
     }
-    // fold this scale group into fp32: (sum u x - 8 sum x) * s_w
+    // fold this scale group into fp32
 #pragma unroll
     for (int j = 0; j < QMF; ++j)
-      if (j < live)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = j * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        accf[j][r] = fmaf((float)(acci[j][r] - 8 * sG[buf][m]), mine.sw, accf[j][r]);
-      }
+      for (int r = 0; r < 16; ++r) accf[j][r] = fmaf((float)acci[j][r], mine.sw, accf[j][r]);
     if (kt + kQAhead < nk) gload(mine, kt + kQAhead);
     if (kt + 1 < nk) astore(next, buf ^ 1);
     __syncthreads();
@@ -266,7 +244,7 @@ __global__ __launch_bounds__(256) void gemm_w4a8_kernel(
 }
 
 template <int KS, int RBW, int MAXNT, bool SWIGLU>
-void launch_gemv(const int8_t* aq, const float* as, const int32_t* ag, const int32_t* perm, int k,
+void launch_gemv(const int8_t* aq, const float* as, const int32_t* perm, int k,
                  const FfnItem* items, const int32_t* n_items, int max_items, const char* pool,
                  size_t stride, size_t off_codes, size_t off_scales, int R, int K, int out_ld,
                  float* out, hipStream_t s) {
@@ -278,17 +256,16 @@ void launch_gemv(const int8_t* aq, const float* as, const int32_t* ag, const int
   if (grid == 0) return;
   constexpr int U = RBW >= 4 ? 2 : 4;
   hipLaunchKernelGGL((tgemv::int4_kernel<KS, RBW, NW, U, MAXNT, SWIGLU>), dim3(grid),
-                     dim3(NW * 64), 0, s, aq, as, ag, perm, k, items, n_items, pool, stride,
+                     dim3(NW * 64), 0, s, aq, as, perm, k, items, n_items, pool, stride,
                      off_codes, off_scales, R, K, out_ld, upi, out);
 }
 
 template <int RBW, int MAXNT, bool SWIGLU>
-void launch_gemv_ks(int ks, const int8_t* aq, const float* as, const int32_t* ag,
-                    const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
+void launch_gemv_ks(int ks, const int8_t* aq, const float* as, const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
                     int max_items, const char* pool, size_t stride, size_t off_codes,
                     size_t off_scales, int R, int K, int out_ld, float* out, hipStream_t s) {
 #define MOE_W4_KS(KS_)                                                                          \
-  launch_gemv<KS_, RBW, MAXNT, SWIGLU>(aq, as, ag, perm, k, items, n_items, max_items, pool,    \
+  launch_gemv<KS_, RBW, MAXNT, SWIGLU>(aq, as, perm, k, items, n_items, max_items, pool,        \
                                        stride, off_codes, off_scales, R, K, out_ld, out, s)
   switch (ks) {
     case 1: MOE_W4_KS(1); break;
@@ -299,8 +276,7 @@ void launch_gemv_ks(int ks, const int8_t* aq, const float* as, const int32_t* ag
 #undef MOE_W4_KS
 }
 
-void launch_gemv_any(bool first, int nt, const int8_t* aq, const float* as, const int32_t* ag,
-                     const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
+void launch_gemv_any(bool first, int nt, const int8_t* aq, const float* as, const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
                      int max_items, const char* pool, size_t stride, const SlotLayout& lay, int H,
                      int F, float* out, hipStream_t s) {
   const int R = first ? 2 * F : H, K = first ? H : F, ld = first ? F : H;
@@ -309,10 +285,10 @@ void launch_gemv_any(bool first, int nt, const int8_t* aq, const float* as, cons
 #define MOE_W4_NT(NT_)                                                                          \
   do {                                                                                          \
     if (first)                                                                                  \
-      launch_gemv_ks<4, NT_, true>(sp.ks, aq, as, ag, perm, k, items, n_items, max_items, pool, stride, \
+      launch_gemv_ks<4, NT_, true>(sp.ks, aq, as, perm, k, items, n_items, max_items, pool, stride, \
                                 oc, os, R, K, ld, out, s);                                      \
     else                                                                                        \
-      launch_gemv_ks<4, NT_, false>(sp.ks, aq, as, ag, perm, k, items, n_items, max_items, pool,       \
+      launch_gemv_ks<4, NT_, false>(sp.ks, aq, as, perm, k, items, n_items, max_items, pool,       \
                                  stride, oc, os, R, K, ld, out, s);                             \
   } while (0)
   if (nt <= 1) MOE_W4_NT(1);
@@ -324,9 +300,9 @@ void launch_gemv_any(bool first, int nt, const int8_t* aq, const float* as, cons
 }  // namespace
 
 int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* lut,
-             const int32_t* group_mask, const char* pool, size_t stride, int num_slots,
-             const SlotLayout& lay, int T, int H, int F, int E, int k, float* y, int32_t* err,
-             char* ws, const FfnWorkspace& wl, hipStream_t s) {
+             const int32_t* group_mask, int n_shared, int shared_slot0, const char* pool,
+             size_t stride, int num_slots, const SlotLayout& lay, int T, int H, int F, int E, int k,
+             float* y, int32_t* err, char* ws, const FfnWorkspace& wl, hipStream_t s) {
   int32_t* n_items = reinterpret_cast<int32_t*>(ws);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + 4);
   FfnItem* items = reinterpret_cast<FfnItem*>(ws + wl.items);
@@ -334,33 +310,35 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   float* hbuf = reinterpret_cast<float*>(ws + wl.h);
   int8_t* xq = reinterpret_cast<int8_t*>(ws + wl.xq);
   float* xs = reinterpret_cast<float*>(ws + wl.xs);
-  int32_t* xg = reinterpret_cast<int32_t*>(ws + wl.xg);
   int8_t* hq = reinterpret_cast<int8_t*>(ws + wl.hq);
   float* hs = reinterpret_cast<float*>(ws + wl.hs);
-  int32_t* hg = reinterpret_cast<int32_t*>(ws + wl.hg);
   if (H > 4 * 2048 || F > 4 * 2048) return MOE_EUNSUPPORTED;  // quant_rows covers 8192 values
   const long long tk = (long long)T * k;
-  const int max_items = (int)(tk < E ? tk : E);
-  const int max_tiles = (T > kGemvMaxRows) ? wl.max_tiles : 0;
+  const long long rows = (long long)T * (k + n_shared);
+  const int small_max = ffn_small_max(T, k, E, n_shared);
+  const int max_items = small_max == 0 ? 0 : (int)(tk < E ? tk : E) + n_shared;
+  const int max_tiles = (T > small_max) ? wl.max_tiles : 0;
   if (max_tiles > 65535) return MOE_EUNSUPPORTED;
-  launch_ffn_plan(offsets, lut, group_mask, E, num_slots, kGemvMaxRows, items, n_items, tiles,
-                  n_tiles, err, s);
+  launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max, items,
+                  n_items, tiles, n_tiles, err, s);
   hipLaunchKernelGGL(quant_rows_kernel<MOE_BF16>, dim3(T), dim3(256), 0, s, x, H, nullptr, nullptr,
-                     nullptr, 0, 0, xq, xs, xg);
+                     nullptr, 0, 0, 0, xq, xs);
   const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;
-  launch_gemv_any(true, nt, xq, xs, xg, perm, k, items, n_items, max_items, pool, stride, lay, H, F,
-                  hbuf, s);
+  if (max_items > 0)
+    launch_gemv_any(true, nt, xq, xs, perm, k, items, n_items, max_items, pool, stride, lay, H, F,
+                    hbuf, s);
   if (max_tiles > 0)
     hipLaunchKernelGGL(gemm_w4a8_kernel<1>, dim3((2 * F / 32 + 3) / 4, max_tiles), dim3(256), 0,
-                       s, xq, xs, xg, perm, k, tiles, n_tiles, pool, stride, lay.off_w13,
+                       s, xq, xs, perm, k, tiles, n_tiles, pool, stride, lay.off_w13,
                        lay.off_s13, 2 * F, H, F, hbuf);
-  hipLaunchKernelGGL(quant_rows_kernel<MOE_F32>, dim3((unsigned)tk), dim3(256), 0, s, hbuf, F,
-                     offsets, lut, group_mask, E, num_slots, hq, hs, hg);
-  launch_gemv_any(false, nt, hq, hs, hg, perm, k, items, n_items, max_items, pool, stride, lay, H,
-                  F, y, s);
+  hipLaunchKernelGGL(quant_rows_kernel<MOE_F32>, dim3((unsigned)rows), dim3(256), 0, s, hbuf, F,
+                     offsets, lut, group_mask, E, n_shared, num_slots, hq, hs);
+  if (max_items > 0)
+    launch_gemv_any(false, nt, hq, hs, perm, k, items, n_items, max_items, pool, stride, lay, H,
+                    F, y, s);
   if (max_tiles > 0)
     hipLaunchKernelGGL(gemm_w4a8_kernel<2>, dim3((H / 32 + 3) / 4, max_tiles), dim3(256), 0, s,
-                       hq, hs, hg, perm, k, tiles, n_tiles, pool, stride, lay.off_w2, lay.off_s2, H,
+                       hq, hs, perm, k, tiles, n_tiles, pool, stride, lay.off_w2, lay.off_s2, H,
                        F, H, y);
   return moe_launch_status();
 }

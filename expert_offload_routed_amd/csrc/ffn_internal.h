@@ -30,7 +30,7 @@ struct SlotLayout {
 
 // Sections of the moe_expert_ffn workspace (byte offsets).
 struct FfnWorkspace {
-  size_t items, tiles, h, xq, xs, xg, hq, hs, hg, total;
+  size_t items, tiles, h, xq, xs, hq, hs, total;
   int max_tiles;
 };
 
@@ -42,9 +42,22 @@ int slot_layout(int H, int F, int w_dtype, SlotLayout* out);
 // The FFN work list: groups of <= small_max rows as FfnItem, the others cut
 // into kGemmBM-row GemmTile (see ffn_plan_kernel in ffn.hip).
 void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
-                     int num_slots, int small_max, FfnItem* items, int32_t* n_items,
-                     GemmTile* tiles, int32_t* n_tiles, int32_t* err_word, hipStream_t s);
+                     int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
+                     int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
+                     hipStream_t s);
+// Largest group that takes the GEMV path (0: every group takes the MFMA tiles).
+int ffn_small_max(int T, int k, int E, int n_shared);
 void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, const GemmTile* tiles,
                       const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
                       size_t off, int N, int K, int out_ld, void* out, hipStream_t s);
-FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype);
+// Workspace of a call over T tokens with E routed experts (k per token) and
+// n_shared shared experts carried as extra groups.
+FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype, int n_shared);
+// moe_expert_ffn with the shared experts as groups E .. E+n_shared-1: offsets
+// has E + n_shared + 1 entries, group E + s holds T rows (perm value t * k for
+// token t) and reads slot shared_slot0 + s; group_mask applies to routed groups.
+int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* offsets,
+               const int32_t* lut, const int32_t* group_mask, int n_shared, int shared_slot0,
+               const void* pool_base, size_t slot_stride, int num_slots, int w_dtype, int T, int H,
+               int F, int E, int k, float* y_perm, int32_t* err_word, void* workspace,
+               size_t ws_bytes, hipStream_t stream);

@@ -92,11 +92,10 @@ __device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
   return v > bv || (v == bv && id < bid);
 }
 
-// Top-k and routing weights of token t; executed by one whole wave.
-// When s_ids is given, the selected ids are also written there (LDS, [t*k + r]).
+// Top-k and routing weights of token t; executed by one whole wave. The
+// outputs ([t*k + r]) may be global memory or LDS.
 __device__ void topk_token(const float* __restrict__ logits, int t, int E, int k, int renorm,
-                           int32_t* __restrict__ ids, float* __restrict__ weights,
-                           int* s_ids = nullptr) {
+                           int32_t* __restrict__ ids, float* __restrict__ weights) {
   const int lane = threadIdx.x & 63;
   float v[kTopkMaxV];
   uint32_t avail = 0;  // bit i: logit of expert lane + 64 i still selectable
@@ -140,10 +139,7 @@ __device__ void topk_token(const float* __restrict__ logits, int t, int E, int k
     for (int i = 0; i < kTopkMaxV; ++i)
       if (i == (r >> 6) && lane == (r & 63)) sel[i] = bv;
     if (r == 0) vmax = bv;
-    if (lane == 0) {
-      ids[(size_t)t * k + r] = (bid == INT_MAX) ? -1 : bid;
-      if (s_ids) s_ids[t * k + r] = (bid == INT_MAX) ? -1 : bid;
-    }
+    if (lane == 0) ids[(size_t)t * k + r] = (bid == INT_MAX) ? -1 : bid;
   }
 
   float denom = 0.f;
@@ -173,11 +169,128 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
   topk_token(logits, t, E, k, renorm, ids, weights);
 }
 
-// Decode front end in one launch (T <= kFrontMaxT, T*k <= 1024): workgroup e
-// computes the logits of expert e for every token; the last workgroup to
-// finish (a device-scope counter, released and acquired with agent-scope
-// fences) selects the top-k of every token and sorts the assignments by
-// expert in LDS. The counter is left at zero for the next launch.
+// Second half of the decode front end, run by one workgroup (any size up to
+// 1024 threads) once the logits of every token are visible at `lg`: top-k of
+// every token (one wave per token), then a stable counting sort of the T*k
+// assignments by expert. Every intermediate stays in LDS and the outputs are
+// written once at the end: a barrier after a global store would wait for the
+// store to complete.
+struct FrontLds {
+  int ids[1024];    // selected expert of assignment t*k + r
+  float w[1024];    // its routing weight
+  int cnt[1024];    // assignments per expert
+  int off[1024];    // first position of each expert
+  int perm[1024];   // assignment at each sorted position
+  int wave[40];     // scan scratch
+};
+
+__device__ void front_select_and_sort(const float* lg, int T, int E, int k, int renorm,
+                                      int32_t* __restrict__ ids, float* __restrict__ weights,
+                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                      int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                      int32_t* __restrict__ distinct,
+                                      int32_t* __restrict__ n_distinct, FrontLds& L, int* s_dist) {
+  const int tid = threadIdx.x, nthr = blockDim.x, wave = tid >> 6, nwaves = nthr >> 6;
+  for (int t = wave; t < T; t += nwaves) topk_token(lg, t, E, k, renorm, L.ids, L.w);
+  const int n = T * k;
+  for (int i = tid; i < 1024; i += nthr) L.cnt[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += nthr) {
+    const int ex = L.ids[i];
+    if (ex >= 0 && ex < E) atomicAdd(&L.cnt[ex], 1);
+  }
+  __syncthreads();
+  // exclusive scan of counts (4 experts per thread) and compaction of the routed set
+  int c4[4], f4[4], csum = 0, fsum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ex = tid * 4 + j;
+    c4[j] = (ex < E) ? L.cnt[ex] : 0;
+    f4[j] = c4[j] > 0 ? 1 : 0;
+    csum += c4[j];
+    fsum += f4[j];
+  }
+  int total = 0, nd = 0;
+  int cbase = block_exclusive_scan(csum, L.wave, &total);
+  int fbase = block_exclusive_scan(fsum, L.wave, &nd);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ex = tid * 4 + j;
+    if (ex < E) {
+      L.off[ex] = cbase;
+      if (f4[j]) s_dist[fbase] = ex;
+    }
+    cbase += c4[j];
+    fbase += f4[j];
+  }
+  __syncthreads();
+  // rank of assignment (t, j): tokens before t that picked the same expert
+  for (int f = tid; f < n; f += nthr) {
+    const int ex = L.ids[f];
+    if (ex < 0 || ex >= E) continue;
+    const int t = f / k;
+    int rank = 0;
+    for (int i = 0; i < t * k; ++i) rank += (L.ids[i] == ex) ? 1 : 0;
+    L.perm[L.off[ex] + rank] = f;
+  }
+  __syncthreads();
+  // outputs, no barrier after this point
+  for (int i = tid; i < n; i += nthr) {
+    ids[i] = L.ids[i];
+    weights[i] = L.w[i];
+    const int f = L.perm[i];
+    perm[i] = f;
+    inv[f] = i;
+  }
+  for (int ex = tid; ex < E; ex += nthr) {
+    counts[ex] = L.cnt[ex];
+    offsets[ex] = L.off[ex];
+  }
+  for (int i = tid; i < nd; i += nthr) distinct[i] = s_dist[i];
+  if (tid == 0) {
+    offsets[E] = total;
+    n_distinct[0] = nd;
+  }
+}
+
+// The decode front end keeps the tokens in LDS (up to kFrontXBytes) so the
+// weight loads of a lane are issued together, one memory round trip per
+// kFrontU chunks, instead of one per loop iteration.
+constexpr int kFrontU = 4;                     // 8-element chunks per lane in flight
+constexpr size_t kFrontXBytes = 128 * 1024;    // tokens staged in LDS (T * H * element size)
+
+// Copy the T token rows (T*H elements) into LDS, 16 bytes per thread per step.
+__device__ __forceinline__ void stage_tokens(const void* __restrict__ x, size_t bytes,
+                                             u32x4* __restrict__ s_x) {
+  const u32x4* src = static_cast<const u32x4*>(x);
+  const int nv = (int)(bytes / 16);
+#pragma unroll 4
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) s_x[i] = src[i];
+}
+
+// acc[t] += w_chunk . x[t][c*8 .. c*8+7] for every token, x read from LDS
+// (staged) or global memory.
+template <int FMT>
+__device__ __forceinline__ void dot_chunk(const float (&wv)[8], const void* __restrict__ x,
+                                          const void* s_x, bool staged, int T, int H, int c,
+                                          float (&acc)[kFrontMaxT]) {
+#pragma unroll
+  for (int t = 0; t < kFrontMaxT; ++t) {
+    if (t < T) {
+      float xv[8];
+      load8<FMT>(staged ? s_x : x, (size_t)t * H + (size_t)c * 8, xv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[t] = fmaf(wv[q], xv[q], acc[t]);
+    }
+  }
+}
+
+// Decode front end in one launch (T <= kFrontMaxT, T*k <= 1024) for routers
+// too large for one workgroup: workgroup e computes the logits of expert e
+// for every token (each lane loads kFrontU weight chunks at once); the last
+// workgroup to finish (a device-scope counter, released and acquired with
+// agent-scope fences) runs the selection and sort. The counter is left at
+// zero for the next launch.
 template <int FMT>
 __global__ __launch_bounds__(256) void route_front_kernel(
     const void* __restrict__ x, const void* __restrict__ w,
@@ -186,29 +299,36 @@ __global__ __launch_bounds__(256) void route_front_kernel(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, int32_t* __restrict__ distinct, int32_t* __restrict__ n_distinct,
     unsigned* __restrict__ done) {
+  __shared__ u32x4 s_x[kFrontXBytes / 16];
   __shared__ float red[4][kFrontMaxT];
-  __shared__ int s_ids[1024];
-  __shared__ int s_cnt[1024];
-  __shared__ int s_off[1024];
-  __shared__ int s_wave[40];
+  __shared__ FrontLds L;
+  __shared__ int s_dist[1024];
   __shared__ unsigned s_last;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int e = blockIdx.x;
+  constexpr int ES = FMT == MOE_BF16 ? 2 : 4;
+  const size_t xbytes = (size_t)T * H * ES;
+  const bool staged = xbytes <= kFrontXBytes;
   {
+    const int nch = H / 8;
     float acc[kFrontMaxT];
 #pragma unroll
     for (int t = 0; t < kFrontMaxT; ++t) acc[t] = 0.f;
-    for (int c = tid * 8; c < H; c += 256 * 8) {
-      float wv[8];
-      load8<FMT>(w, (size_t)e * H + c, wv);
+    for (int cb = 0; cb < nch; cb += 256 * kFrontU) {
+      float wv[kFrontU][8];
 #pragma unroll
-      for (int t = 0; t < kFrontMaxT; ++t) {
-        if (t < T) {
-          float xv[8];
-          load8<FMT>(x, (size_t)t * H + c, xv);
+      for (int u = 0; u < kFrontU; ++u) {
+        const int c = cb + u * 256 + tid;
+        if (c < nch) load8<FMT>(w, (size_t)e * H + (size_t)c * 8, wv[u]);
+      }
+      if (cb == 0 && staged) {
+        stage_tokens(x, xbytes, s_x);
+        __syncthreads();
+      }
 #pragma unroll
-          for (int q = 0; q < 8; ++q) acc[t] = fmaf(wv[q], xv[q], acc[t]);
-        }
+      for (int u = 0; u < kFrontU; ++u) {
+        const int c = cb + u * 256 + tid;
+        if (c < nch) dot_chunk<FMT>(wv[u], x, s_x, staged, T, H, c, acc);
       }
     }
 #pragma unroll
@@ -231,59 +351,87 @@ __global__ __launch_bounds__(256) void route_front_kernel(
   __syncthreads();
   if (!s_last) return;
   __threadfence();  // see every other workgroup's logits
-
-  // top-k of every token: wave w takes tokens w, w + 4, ...
-  for (int t = wave; t < T; t += 4) topk_token(logits, t, E, k, renorm, ids, weights, s_ids);
-  const int n = T * k;
-  for (int i = tid; i < 1024; i += 256) s_cnt[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += 256) {
-    const int ex = s_ids[i];
-    if (ex >= 0 && ex < E) atomicAdd(&s_cnt[ex], 1);
-  }
-  __syncthreads();
-  // exclusive scan of counts (4 experts per thread) and compaction of the routed set
-  int c4[4], f4[4], csum = 0, fsum = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ex = tid * 4 + j;
-    c4[j] = (ex < E) ? s_cnt[ex] : 0;
-    f4[j] = c4[j] > 0 ? 1 : 0;
-    csum += c4[j];
-    fsum += f4[j];
-  }
-  int total = 0, nd = 0;
-  int cbase = block_exclusive_scan(csum, s_wave, &total);
-  int fbase = block_exclusive_scan(fsum, s_wave, &nd);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ex = tid * 4 + j;
-    if (ex < E) {
-      s_off[ex] = cbase;
-      counts[ex] = c4[j];
-      offsets[ex] = cbase;
-      if (f4[j]) distinct[fbase] = ex;
-    }
-    cbase += c4[j];
-    fbase += f4[j];
-  }
-  if (tid == 0) {
-    offsets[E] = total;
-    n_distinct[0] = nd;
-  }
-  __syncthreads();
-  // rank of assignment (t, j): tokens before t that picked the same expert
-  for (int f = tid; f < n; f += 256) {
-    const int ex = s_ids[f];
-    if (ex < 0 || ex >= E) continue;
-    const int t = f / k;
-    int rank = 0;
-    for (int i = 0; i < t * k; ++i) rank += (s_ids[i] == ex) ? 1 : 0;
-    const int pos = s_off[ex] + rank;
-    perm[pos] = f;
-    inv[f] = pos;
-  }
+  front_select_and_sort(logits, T, E, k, renorm, ids, weights, counts, offsets, perm, inv, distinct,
+                        n_distinct, L, s_dist);
   if (tid == 0) *done = 0u;
+}
+
+// Decode front end in one workgroup of 1024 threads, for small routers
+// (E <= kSingleMaxE and E*H weights of at most kSingleMaxBytes): no
+// device-scope hand-off at all. The E*H dot products are split into (expert,
+// H slice) pairs, one wave per pair at a time (16/E slices per expert when
+// E < 16); a pair's partial sums meet in LDS in slice order, then the same
+// workgroup selects and sorts with the logits still in LDS.
+constexpr int kSingleMaxE = 64;
+constexpr size_t kSingleMaxBytes = 64 * 1024;
+
+template <int FMT>
+__global__ __launch_bounds__(1024) void route_front_single_kernel(
+    const void* __restrict__ x, const void* __restrict__ w,
+    const float* __restrict__ bias, int T, int H, int E, int k, int renorm,
+    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ weights,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, int32_t* __restrict__ distinct, int32_t* __restrict__ n_distinct) {
+  __shared__ u32x4 s_x[kFrontXBytes / 16];
+  __shared__ float s_part[16 * kSingleMaxE];  // [pair][t]: pairs * T <= 1024; later the routed set
+  __shared__ float s_lg[kFrontMaxT * kSingleMaxE];
+  __shared__ FrontLds L;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int ES = FMT == MOE_BF16 ? 2 : 4;
+  const size_t xbytes = (size_t)T * H * ES;
+  const bool staged = xbytes <= kFrontXBytes;
+  const int S = E < 16 ? 16 / E : 1;  // H slices per expert
+  const int nch = H / 8;              // 8-element chunks of a row
+  bool first = true;
+  for (int p0 = 0; p0 < E * S; p0 += 16) {
+    const int p = p0 + wave;
+    const bool active = p < E * S;
+    const int e = active ? p / S : 0, sl = active ? p - e * S : 0;
+    const int c0 = sl * nch / S, c1 = active ? (sl + 1) * nch / S : 0;
+    float acc[kFrontMaxT];
+#pragma unroll
+    for (int t = 0; t < kFrontMaxT; ++t) acc[t] = 0.f;
+    for (int cb = c0; cb < c1 || first; cb += 64 * kFrontU) {
+      float wv[kFrontU][8];
+#pragma unroll
+      for (int u = 0; u < kFrontU; ++u) {
+        const int c = cb + u * 64 + lane;
+        if (c < c1) load8<FMT>(w, (size_t)e * H + (size_t)c * 8, wv[u]);
+      }
+      if (first) {  // every wave passes here exactly once, before its first dot product
+        if (staged) stage_tokens(x, xbytes, s_x);
+        __syncthreads();
+        first = false;
+      }
+#pragma unroll
+      for (int u = 0; u < kFrontU; ++u) {
+        const int c = cb + u * 64 + lane;
+        if (c < c1) dot_chunk<FMT>(wv[u], x, s_x, staged, T, H, c, acc);
+      }
+    }
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < kFrontMaxT; ++t) {
+        if (t < T) {
+          const float v = wave_sum(acc[t]);
+          if (lane == 0) s_part[p * T + t] = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < T * E; i += 1024) {
+    const int t = i / E, e = i - t * E;
+    float sum = 0.f;
+    for (int sl = 0; sl < S; ++sl) sum += s_part[(e * S + sl) * T + t];
+    sum += bias ? bias[e] : 0.f;
+    s_lg[i] = sum;
+  }
+  __syncthreads();
+  // s_part is free from here on: it holds the routed set
+  front_select_and_sort(s_lg, T, E, k, renorm, ids, weights, counts, offsets, perm, inv, distinct,
+                        n_distinct, L, reinterpret_cast<int*>(s_part));
+  for (int i = tid; i < T * E; i += 1024) logits[i] = s_lg[i];
 }
 
 }  // namespace
@@ -328,6 +476,18 @@ extern "C" int moe_route_permute(const void* x, int x_dtype, const void* w_route
   }
   MOE_CHECK_ARG(x && w_router && logits && topk_ids && topk_w && perm && inv);
   MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)w_router % 16) == 0);
+  const size_t wbytes = (size_t)E * H * (x_dtype == MOE_BF16 ? 2 : 4);
+  if (E <= kSingleMaxE && wbytes <= kSingleMaxBytes) {
+    if (x_dtype == MOE_BF16)
+      hipLaunchKernelGGL(route_front_single_kernel<MOE_BF16>, dim3(1), dim3(1024), 0, stream, x,
+                         w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w, counts,
+                         offsets, perm, inv, distinct, n_distinct);
+    else
+      hipLaunchKernelGGL(route_front_single_kernel<MOE_F32>, dim3(1), dim3(1024), 0, stream, x,
+                         w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w, counts,
+                         offsets, perm, inv, distinct, n_distinct);
+    return moe_launch_status();
+  }
   if (x_dtype == MOE_BF16)
     hipLaunchKernelGGL(route_front_kernel<MOE_BF16>, dim3(E), dim3(256), 0, stream, x, w_router,
                        bias, T, H, E, k, renorm, logits, topk_ids, topk_w, counts, offsets, perm,

@@ -7,8 +7,10 @@
 //   -> moe_expert_ffn over the groups that are already resident, while the
 //   misses are copied from the pinned host store on the fill stream and
 //   committed with their tags -> moe_expert_ffn over each wave of filled
-//   groups -> moe_expert_ffn of the shared experts (own resident pool) ->
-//   moe_combine.
+//   groups -> moe_combine. The shared experts sit in the n_shared slots after
+//   the S routed ones and ride along as extra groups of the first expert FFN
+//   call of the step (T rows each, placed after the T*k routed rows), so a
+//   step plans and streams its weights once.
 // The routed set is known only after the router ran (SeqMoE and HybriMoE
 // summary pages, Problem), so a step whose layer may miss waits for that copy:
 // the one host synchronisation of a step. When every expert of the layer is
@@ -42,7 +44,6 @@ struct moe_layer_ctx {
   uint64_t* tags;
   const char* host_store;
   std::vector<int32_t> blob_of;
-  const char* shared_pool;
   int32_t* err;
   hipStream_t cs, fs;
   // device buffers (inside the caller's workspace)
@@ -55,11 +56,7 @@ struct moe_layer_ctx {
   char* ws;
   size_t ws_bytes;
   int32_t* masks;
-  int32_t *sh_perm, *sh_offsets, *sh_lut;
-  float* sh_y;
-  char* sh_ws;
-  size_t sh_ws_bytes;
-  int sh_T;  // T the shared permutation was built for
+  int sh_T;  // T the shared groups' rows (perm and offsets tails) were written for
   // host state
   int32_t* ring_h;  // pinned [kRing][E+1]: routed sets of steps (written by the device)
   int32_t* ring_d;  // device address of ring_h
@@ -68,7 +65,7 @@ struct moe_layer_ctx {
   int ring_head, ring_count;  // deferred entries: ring_head .. ring_head + count - 1
   int ring_next;              // next ring entry to use
   int32_t* masks_h;    // pinned [(E+2)*E]
-  int32_t* sh_rows_h;  // pinned [t_max*n_shared + n_shared + 1]
+  int32_t* sh_rows_h;  // pinned [t_max*n_shared + n_shared]: tails of perm and offsets
   std::vector<int32_t> lut_h, owner_h, resident;  // resident[l]: experts of layer l in the pool
   std::vector<int64_t> last_use;
   int64_t clock;
@@ -76,7 +73,7 @@ struct moe_layer_ctx {
   std::vector<int32_t> wave_of, is_hit, fill_e, fill_s, fill_w;
   hipEvent_t ev_fill, ev_compute;
   int64_t totals[4];  // over completed plans: distinct, hits, fills, waves
-  // timing of the expert FFN calls (routed, then shared): one event pair per step, collected lazily
+  // timing of the expert FFN calls of a step: one event pair per step, collected lazily
   int timing;
   hipEvent_t tev0[kRing], tev1[kRing];
   int t_head, t_count;
@@ -88,9 +85,8 @@ namespace {
 
 // Device work buffers of a context, carved from the caller's workspace.
 struct CtxLayout {
-  size_t sync, logits, ids, topw, counts, offsets, perm, inv, dist, y_perm, ws, masks;
-  size_t sh_perm, sh_offsets, sh_lut, sh_y, sh_ws, total;
-  size_t ws_bytes, sh_ws_bytes;
+  size_t sync, logits, ids, topw, counts, offsets, perm, inv, dist, y_perm, ws, masks, total;
+  size_t ws_bytes;
 };
 
 CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int w_dtype, int n_shared) {
@@ -102,27 +98,20 @@ CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int w_dtype, int n_s
     return at;
   };
   const size_t tk = (size_t)t_max * k;
+  const size_t rows = (size_t)t_max * (k + n_shared);  // routed rows, then shared rows
   l.sync = take(4);
   l.logits = take((size_t)t_max * E * 4);
   l.ids = take(tk * 4);
   l.topw = take(tk * 4);
   l.counts = take((size_t)E * 4);
-  l.offsets = take((size_t)(E + 1) * 4);
-  l.perm = take(tk * 4);
+  l.offsets = take((size_t)(E + n_shared + 1) * 4);
+  l.perm = take(rows * 4);
   l.inv = take(tk * 4);
   l.dist = take((size_t)(E + 1) * 4);
-  l.y_perm = take(tk * H * 4);
-  l.ws_bytes = moe_ffn_workspace_bytes(t_max, H, F, E, k, w_dtype);
+  l.y_perm = take(rows * H * 4);
+  l.ws_bytes = ffn_workspace_layout(t_max, H, F, E, k, w_dtype, n_shared).total;
   l.ws = take(l.ws_bytes);
   l.masks = take((size_t)(E + 2) * E * 4);
-  if (n_shared) {
-    l.sh_perm = take((size_t)t_max * n_shared * 4);
-    l.sh_offsets = take((size_t)(n_shared + 1) * 4);
-    l.sh_lut = take((size_t)n_shared * 4);
-    l.sh_y = take((size_t)n_shared * t_max * H * 4);
-    l.sh_ws_bytes = moe_ffn_workspace_bytes(t_max, H, F, n_shared, n_shared, w_dtype);
-    l.sh_ws = take(l.sh_ws_bytes);
-  }
   l.total = off;
   return l;
 }
@@ -262,11 +251,14 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
                               hipStream_t fill_stream) {
   MOE_CHECK_ARG(out && t_max >= 1 && k >= 1 && k <= E && E <= 1024 && L >= 1 && S >= 1);
   MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
-  MOE_CHECK_ARG(n_shared >= 0 && (n_shared == 0 || shared_pool));
+  MOE_CHECK_ARG(n_shared >= 0 && E + n_shared <= 1024);
   MOE_CHECK_ARG(pool_base && lut && owner && slot_tags && host_store && blob_of && err_word);
   SlotLayout lay;
   if (slot_layout(H, F, w_dtype, &lay) != MOE_OK) return MOE_EINVAL;
   MOE_CHECK_ARG(slot_stride >= lay.slot_bytes && slot_stride % 256 == 0);
+  // the shared experts are the n_shared slots right after the S routed slots
+  MOE_CHECK_ARG(n_shared == 0 ||
+                shared_pool == static_cast<const char*>(pool_base) + (size_t)S * slot_stride);
   const CtxLayout cl = ctx_layout(t_max, H, F, E, k, w_dtype, n_shared);
   MOE_CHECK_ARG(workspace && ws_bytes >= cl.total && ((uintptr_t)workspace % 256) == 0);
   *out = nullptr;
@@ -279,7 +271,6 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->lut = lut; c->owner = owner; c->tags = slot_tags;
   c->host_store = static_cast<const char*>(host_store);
   c->blob_of.assign(blob_of, blob_of + (size_t)L * E);
-  c->shared_pool = static_cast<const char*>(shared_pool);
   c->err = err_word;
   c->cs = compute_stream;
   c->fs = fill_stream;
@@ -306,14 +297,6 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->ws = wb + cl.ws;
   c->ws_bytes = cl.ws_bytes;
   c->masks = reinterpret_cast<int32_t*>(wb + cl.masks);
-  if (n_shared) {
-    c->sh_perm = reinterpret_cast<int32_t*>(wb + cl.sh_perm);
-    c->sh_offsets = reinterpret_cast<int32_t*>(wb + cl.sh_offsets);
-    c->sh_lut = reinterpret_cast<int32_t*>(wb + cl.sh_lut);
-    c->sh_y = reinterpret_cast<float*>(wb + cl.sh_y);
-    c->sh_ws = wb + cl.sh_ws;
-    c->sh_ws_bytes = cl.sh_ws_bytes;
-  }
   int bad = 0;
   // coherent, mapped: the permutation kernel stores the routed set straight into it
   bad |= hipHostMalloc(reinterpret_cast<void**>(&c->ring_h),
@@ -341,16 +324,6 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
     (void)hipGetLastError();
     destroy(c);
     return MOE_EHIP;
-  }
-  if (n_shared) {
-    std::vector<int32_t> id(n_shared);
-    for (int s = 0; s < n_shared; ++s) id[s] = s;
-    if (hipMemcpy(c->sh_lut, id.data(), n_shared * sizeof(int32_t), hipMemcpyHostToDevice) !=
-        hipSuccess) {
-      (void)hipGetLastError();
-      destroy(c);
-      return MOE_EHIP;
-    }
   }
   *out = c;
   return MOE_OK;
@@ -425,9 +398,26 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   MOE_CHECK_ARG(c && layer >= 0 && layer < c->L && T >= 0 && T <= c->t_max);
   if (T == 0) return MOE_OK;
   MOE_CHECK_ARG(x && w_router && out);
-  const int E = c->E, k = c->k, H = c->H, F = c->F;
+  const int E = c->E, k = c->k, H = c->H, F = c->F, nsh = c->n_shared;
   int rc;
   hipError_t e;
+  if (nsh && c->sh_T != T) {
+    // rows of the shared groups: group E + s holds rows T*k + s*T + t with
+    // perm value t*k (token t); offsets[E + 1 + s] = T*k + (s + 1)*T. The
+    // pinned staging is rewritten only once the stream drained its last copy.
+    if ((e = hipStreamSynchronize(c->cs)) != hipSuccess) return moe_hip_status(e);
+    int32_t* h = c->sh_rows_h;
+    for (int sh = 0; sh < nsh; ++sh)
+      for (int t = 0; t < T; ++t) h[(size_t)sh * T + t] = t * k;
+    for (int sh = 0; sh < nsh; ++sh) h[(size_t)T * nsh + sh] = T * k + (sh + 1) * T;
+    if ((e = hipMemcpyAsync(c->perm + (size_t)T * k, h, (size_t)T * nsh * sizeof(int32_t),
+                            hipMemcpyHostToDevice, c->cs)) != hipSuccess ||
+        (e = hipMemcpyAsync(c->offsets + E + 1, h + (size_t)T * nsh, nsh * sizeof(int32_t),
+                            hipMemcpyHostToDevice, c->cs)) != hipSuccess)
+      return moe_hip_status(e);
+    c->sh_T = T;
+  }
+  const int nslots = c->S + nsh;
   // the routed set is written by the device into the next ring entry (pinned host memory)
   if (c->ring_count == kRing && (rc = drain(c)) != MOE_OK) return rc;
   const int r = c->ring_next;
@@ -453,9 +443,9 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
     // no miss is possible: defer the bookkeeping, run every routed group
     c->ring_layer[r] = layer;
     c->ring_count += 1;
-    if ((rc = moe_expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, nullptr, c->pool,
-                             c->stride, c->S, c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws,
-                             c->ws_bytes, c->cs)) != MOE_OK)
+    if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, nullptr, nsh, c->S, c->pool,
+                         c->stride, nslots, c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws,
+                         c->ws_bytes, c->cs)) != MOE_OK)
       return rc;
   } else {
     if ((rc = drain(c)) != MOE_OK) return rc;  // earlier steps first: their entries precede r
@@ -481,10 +471,10 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
       return moe_hip_status(e);
     // wave 0 fills may start now: they only overwrite slots no resident group of this step reads
     if (n_fills && (rc = fills_after_compute(c)) != MOE_OK) return rc;
-    if (hits) {
-      if ((rc = moe_expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, c->masks, c->pool,
-                               c->stride, c->S, c->w_dtype, T, H, F, E, k, c->y_perm, c->err,
-                               c->ws, c->ws_bytes, c->cs)) != MOE_OK)
+    if (hits || nsh) {  // resident groups, and the shared experts
+      if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, c->masks, nsh, c->S,
+                           c->pool, c->stride, nslots, c->w_dtype, T, H, F, E, k, c->y_perm,
+                           c->err, c->ws, c->ws_bytes, c->cs)) != MOE_OK)
         return rc;
     }
     int fi = 0;
@@ -493,42 +483,19 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
       int nw = 0;
       for (; fi < n_fills && c->fill_w[fi] == w; ++fi, ++nw)
         if ((rc = fill_slot(c, c->fill_s[fi], layer, c->fill_e[fi])) != MOE_OK) return rc;
-      if (nw && (rc = moe_expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row,
-                                     c->masks + (size_t)(1 + w) * E, c->pool, c->stride, c->S,
-                                     c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws,
-                                     c->ws_bytes, c->cs)) != MOE_OK)
+      if (nw && (rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row,
+                                 c->masks + (size_t)(1 + w) * E, 0, 0, c->pool, c->stride, nslots,
+                                 c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws, c->ws_bytes,
+                                 c->cs)) != MOE_OK)
         return rc;
     }
-  }
-  const float* shared_y = nullptr;
-  if (c->n_shared) {
-    const int n = c->n_shared;
-    if (c->sh_T != T) {
-      // rows of shared expert s: flat assignments t*n + s, t ascending; the
-      // pinned staging is rewritten only once the stream drained its last copy
-      if ((e = hipStreamSynchronize(c->cs)) != hipSuccess) return moe_hip_status(e);
-      int32_t* h = c->sh_rows_h;
-      for (int s = 0; s < n; ++s)
-        for (int t = 0; t < T; ++t) h[(size_t)s * T + t] = t * n + s;
-      for (int s = 0; s <= n; ++s) h[(size_t)T * n + s] = s * T;
-      if ((e = hipMemcpyAsync(c->sh_perm, h, (size_t)T * n * sizeof(int32_t),
-                              hipMemcpyHostToDevice, c->cs)) != hipSuccess ||
-          (e = hipMemcpyAsync(c->sh_offsets, h + (size_t)T * n, (n + 1) * sizeof(int32_t),
-                              hipMemcpyHostToDevice, c->cs)) != hipSuccess)
-        return moe_hip_status(e);
-      c->sh_T = T;
-    }
-    if ((rc = moe_expert_ffn(x, c->x_dtype, c->sh_perm, c->sh_offsets, c->sh_lut, nullptr,
-                             c->shared_pool, c->stride, n, c->w_dtype, T, H, F, n, n, c->sh_y,
-                             c->err, c->sh_ws, c->sh_ws_bytes, c->cs)) != MOE_OK)
-      return rc;
-    shared_y = c->sh_y;
   }
   if (timing) {
     const int tr = (c->t_head + c->t_count) % kRing;
     if ((e = hipEventRecord(c->tev1[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
     c->t_count += 1;
   }
+  const float* shared_y = nsh ? c->y_perm + (size_t)T * k * H : nullptr;
   if ((rc = moe_combine(c->y_perm, c->inv, c->topw, T, k, H, shared_y, c->n_shared, out, out_dtype,
                         c->cs)) != MOE_OK)
     return rc;

@@ -43,8 +43,11 @@ __device__ __forceinline__ void load8(const void* base, size_t elem, float out[8
   }
 }
 
-__device__ __forceinline__ uint32_t u_lo(uint32_t w) { return (w ^ 0x88888888u) & 0x0F0F0F0Fu; }
-__device__ __forceinline__ uint32_t u_hi(uint32_t w) { return ((w ^ 0x88888888u) >> 4) & 0x0F0F0F0Fu; }
+// int4 codes to int8 bytes holding 16 q (exact, in [-128, 112]): a code moved to
+// the high nibble of its byte keeps its sign. A 32-bit word holds codes c..c+3
+// in its low nibbles and c+4..c+7 in its high nibbles.
+__device__ __forceinline__ uint32_t q16_lo(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t q16_hi(uint32_t w) { return w & 0xF0F0F0F0u; }
 
 // Final reduction and epilogue, shared by both formats. acc[b][t] holds this
 // lane's partial dot of row (rb0 + b) * 32 + lane % 32 (one K half, one K slice).
@@ -164,14 +167,13 @@ __device__ __forceinline__ void tile_bf16(const char* __restrict__ wbase, int nk
 }
 
 // ------------------------------------------------------------------ int4 ---
-// Codes in offset form u = q + 8; sum q x = sum u x - 8 sum x, the second
-// term added once per (row, 128-value group) from the group sums of x.
+// Codes expanded to bytes 16 q; the dot products are 16 sum q x (exact int32)
+// and the group scale carries the factor 1/16 (exact in fp32).
 template <int KS, int RBW, int U, int NT, bool SWIGLU>
 __device__ __forceinline__ void tile_int4(const char* __restrict__ wbase, int nkc, int K,
                                           const uint16_t* __restrict__ scales,
                                           const int8_t* __restrict__ aq,
                                           const float* __restrict__ as,
-                                          const int32_t* __restrict__ ag,
                                           const int32_t* __restrict__ perm, int k, int prow,
                                           int rb0, int nrb, int out_ld, float* __restrict__ out,
                                           float* __restrict__ red) {
@@ -209,7 +211,7 @@ __device__ __forceinline__ void tile_int4(const char* __restrict__ wbase, int nk
 #pragma unroll
         for (int b = 0; b < RBW; ++b) {
           cw[u][b] = ld16_stream(wl[b] + (size_t)kc * 1024);
-          sw[u][b] = bf16_to_f32(srow[b][kc >> 1]);
+          sw[u][b] = bf16_to_f32(srow[b][kc >> 1]) * 0.0625f;
         }
       }
     }
@@ -221,20 +223,18 @@ __device__ __forceinline__ void tile_int4(const char* __restrict__ wbase, int nk
         for (int t = 0; t < NT; ++t) {
           const int8_t* ap = aq + (size_t)arow[t] * K + kc * 64 + kh;
           const u32x4 a0 = ld16(ap), a1 = ld16(ap + 32);
-          // the group's offset correction, once per row (lane < 32) on its even chunk
-          const int corr = (lane < 32 && (kc & 1) == 0) ? 8 * ag[(size_t)arow[t] * gld + (kc >> 1)] : 0;
 #pragma unroll
           for (int b = 0; b < RBW; ++b) {
             const u32x4& w = cw[u][b];
-            int is = -corr;
-            is = __builtin_amdgcn_sdot4((int)u_lo(w.x), (int)a0.x, is, false);
-            is = __builtin_amdgcn_sdot4((int)u_hi(w.x), (int)a0.y, is, false);
-            is = __builtin_amdgcn_sdot4((int)u_lo(w.y), (int)a0.z, is, false);
-            is = __builtin_amdgcn_sdot4((int)u_hi(w.y), (int)a0.w, is, false);
-            is = __builtin_amdgcn_sdot4((int)u_lo(w.z), (int)a1.x, is, false);
-            is = __builtin_amdgcn_sdot4((int)u_hi(w.z), (int)a1.y, is, false);
-            is = __builtin_amdgcn_sdot4((int)u_lo(w.w), (int)a1.z, is, false);
-            is = __builtin_amdgcn_sdot4((int)u_hi(w.w), (int)a1.w, is, false);
+            int is = 0;
+            is = __builtin_amdgcn_sdot4((int)q16_lo(w.x), (int)a0.x, is, false);
+            is = __builtin_amdgcn_sdot4((int)q16_hi(w.x), (int)a0.y, is, false);
+            is = __builtin_amdgcn_sdot4((int)q16_lo(w.y), (int)a0.z, is, false);
+            is = __builtin_amdgcn_sdot4((int)q16_hi(w.y), (int)a0.w, is, false);
+            is = __builtin_amdgcn_sdot4((int)q16_lo(w.z), (int)a1.x, is, false);
+            is = __builtin_amdgcn_sdot4((int)q16_hi(w.z), (int)a1.y, is, false);
+            is = __builtin_amdgcn_sdot4((int)q16_lo(w.w), (int)a1.z, is, false);
+            is = __builtin_amdgcn_sdot4((int)q16_hi(w.w), (int)a1.w, is, false);
             acc[b][t] = fmaf((float)is, sw[u][b], acc[b][t]);
           }
         }
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) void bf16_kernel(
 
 template <int KS, int RBW, int NW, int U, int MAXNT, bool SWIGLU>
 __global__ __launch_bounds__(NW * 64) void int4_kernel(
-    const int8_t* __restrict__ aq, const float* __restrict__ as, const int32_t* __restrict__ ag,
+    const int8_t* __restrict__ aq, const float* __restrict__ as,
     const int32_t* __restrict__ perm, int k, const FfnItem* __restrict__ items,
     const int32_t* __restrict__ n_items, const char* __restrict__ pool, size_t stride,
     size_t off_codes, size_t off_scales, int R, int K, int out_ld, int units_per_item,
@@ -306,11 +306,11 @@ __global__ __launch_bounds__(NW * 64) void int4_kernel(
     const uint16_t* scales = reinterpret_cast<const uint16_t*>(slot + off_scales);
     int done = 0;
     for (; it.rows - done >= MAXNT; done += MAXNT)
-      tile_int4<KS, RBW, U, MAXNT, SWIGLU>(wbase, nkc, K, scales, aq, as, ag, perm, k,
+      tile_int4<KS, RBW, U, MAXNT, SWIGLU>(wbase, nkc, K, scales, aq, as, perm, k,
                                            it.row_begin + done, rb0, nrb, out_ld, out, red);
     const int rest = it.rows - done, p = it.row_begin + done;
 #define TGEMV_INT4(NT_)                                                                           \
-  tile_int4<KS, RBW, U, NT_, SWIGLU>(wbase, nkc, K, scales, aq, as, ag, perm, k, p, rb0, nrb, out_ld, \
+  tile_int4<KS, RBW, U, NT_, SWIGLU>(wbase, nkc, K, scales, aq, as, perm, k, p, rb0, nrb, out_ld, \
                                      out, red)
     TGEMV_REST(TGEMV_INT4)
 #undef TGEMV_INT4

@@ -63,17 +63,18 @@ class SlotCacheLayer:
         self.store = store or ExpertStore(sh)
         self.stride, self.wcode = self.store.stride, self.store.wcode
         dev = torch.device(device)
-        self.pool = torch.empty(slots * self.stride, dtype=torch.uint8, device=dev)
+        self.n_sh = sh.n_shared
+        # the S routed slots, then the n_shared slots of the always-resident shared experts
+        self.pool = torch.empty((slots + self.n_sh) * self.stride, dtype=torch.uint8, device=dev)
         self.lut = torch.full((self.L * self.E,), -1, dtype=torch.int32, device=dev)
         self.owner = torch.full((slots,), -1, dtype=torch.int32, device=dev)
         self.tags = torch.zeros(slots, dtype=torch.int64, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         self.routers = [W.router(sh, layer=l, device=dev) for l in range(self.L)]
-        self.n_sh = sh.n_shared
         self.sh_pool = None
         if self.n_sh:
             self.sh_store = ExpertStore(sh, shared=True)
-            self.sh_pool = torch.empty(self.n_sh * self.stride, dtype=torch.uint8, device=dev)
+            self.sh_pool = self.pool[slots * self.stride:]
             for s in range(self.n_sh):
                 self.sh_pool[s * self.stride:(s + 1) * self.stride].copy_(self.sh_store.host[s])
         blob_of = np.array([W.blob_of(sh, l, e) for l in range(self.L) for e in range(self.E)], np.int32)

@@ -35,11 +35,14 @@ size_t moe_ctx_workspace_bytes(int t_max, int H, int F, int E, int k, int w_dtyp
 /* moe_ctx_create: context for a stack of L layers sharing one slot pool.
  *   t_max       largest token count of a step
  *   H, F, E, k  hidden size, expert FFN size, routed experts per layer, top-k
- *   S           slots in the pool (pool_base + s * slot_stride, s < S)
+ *   S           routed slots in the pool (pool_base + s * slot_stride, s < S)
  *   x_dtype     MOE_F32 or MOE_BF16 (tokens and router weights)
  *   w_dtype     expert weight format (MOE_F32, MOE_BF16, MOE_INT4G128)
  *   n_shared    always-on shared experts (0 = none); their packed weights sit
- *               in shared_pool (n_shared slots of slot_stride bytes, resident)
+ *               in the n_shared slots that follow the S routed slots:
+ *               shared_pool must equal pool_base + S * slot_stride (EINVAL
+ *               otherwise). They are computed as extra groups of the step's
+ *               first expert FFN call (one plan, one weight pass for all).
  *   lut         [L*E] int32 device table (expert -> slot, -1 = absent)
  *   owner       [S] int32 device: lut index held by each slot, -1 = empty
  *   slot_tags   [S] uint64 device

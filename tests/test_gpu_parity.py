@@ -83,6 +83,9 @@ def test_route_rejects_bad_args():
 @pytest.mark.parametrize("shape,T", [(TINY, 16), (TINY, 1), (W.reduced(MIX, H=4096), 5),
                                      (W.reduced(DSV3, H=7168), 16), (W.reduced(DSV3, H=512), 40),
                                      (W.reduced(TINY, E=64, k=64, H=64), 16),
+                                     (W.reduced(TINY, E=5, k=3, H=264), 7),     # one workgroup, 3 H slices per expert
+                                     (W.reduced(MIX, E=40, k=4, H=1024), 11),   # one workgroup, 40 (expert, slice) pairs
+                                     (W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), H=2048), 3),
                                      (W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), E=1000, k=16, H=512), 9)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_route_permute_fused(shape, T):
