@@ -108,136 +108,189 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 }
 
 // -------------------------------------------------------- int8 MFMA GEMM ---
-constexpr int QBM = kGemmBM;  // activation rows of a tile
-constexpr int QMF = QBM / 32;
-constexpr int QBK = 128;      // one scale group per K tile
-constexpr int A_LD = QBK + 16;  // bytes per staged activation row
-constexpr int kQAhead = 3;      // K tiles of global loads in flight
+// Tile: 128 activation rows (one GemmTile) x 256 weight rows (eight 32-row
+// blocks of the tile-major codes), K tiles of 128 values = one scale group.
+// 8 waves; wave w computes rows 64 (w & 1) .. +63 against weight blocks
+// 2 (w >> 1), +1: four v_mfma_i32_32x32x32_i8 accumulators.
+//
+// Operands reach LDS through asynchronous global -> LDS copies (16 bytes per
+// lane), in a ring of kQStages stages, so no register holds data in flight:
+//   A: 16 fragments of 1 KB per stage, fragment (mf, ks) holding row
+//      mf*32 + l%32, bytes ks*32 + 16 (l / 32) of the K tile at lane l
+//      (exactly the MFMA operand layout);
+//   B: the 16 code chunks of the tile's 8 weight blocks, as stored;
+//   scales: per wave, the aligned 32-bit word holding each lane's bf16 group
+//      scale (the slot's scale section is 256-byte aligned; the half is picked
+//      by the element index), kept out of registers: a register load would
+//      make the compiler drain every copy in flight before using it.
+// Each wave issues 6 copies per stage; before computing stage kt it waits
+// until only the later stages' copies are outstanding, then one barrier
+// publishes the stage to all waves. The int32 sums of a K tile are folded
+// into fp32 with the group scale / 16; the second fragment's tiles of group
+// kt are folded during group kt+1's first MFMAs.
+constexpr int QBM = kGemmBM;   // activation rows of a tile (128)
+constexpr int QBN = 256;       // weight rows of a tile
+constexpr int QBK = 128;       // one scale group per K tile
+constexpr int kQStages = 4;
+constexpr int kQStageBytes = 16384 + 16384 + 4096;  // A, B, scales
+static_assert(QBM == 128, "the 8-wave int8 tile covers 128 activation rows");
 
-// Tiles: 128 activation rows x 128 weight rows (four 32-row blocks of the
-// tile-major codes, one per wave), K tiles of 128 = one scale group. A wave's
-// code fragments for a K tile are two whole 1 KB chunks (one 16-byte load per
-// lane each, cacheable so the M-tiles of a group share them in L2); the int8
-// activation tile goes through LDS. Each K tile: 4 v_mfma_i32_32x32x32_i8 per
-// 32x32 accumulator into int32, then folded into fp32 with the group scale.
+template <int N_>
+__device__ __forceinline__ void vm_wait() {
+  if constexpr (N_ == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N_ == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+}
+
 template <int PASS>
-__global__ __launch_bounds__(256) void gemm_w4a8_kernel(
+__global__ __launch_bounds__(512) void gemm_w4a8_kernel(
     const int8_t* __restrict__ aq, const float* __restrict__ as,
     const int32_t* __restrict__ perm, int k, const GemmTile* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const char* __restrict__ pool, size_t stride,
     size_t off_codes, size_t off_scales, int N, int K, int out_ld, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) int8_t sA[2][QBM * A_LD];
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kQStages * kQStageBytes];
   if ((int)blockIdx.y >= n_tiles[0]) return;
   const GemmTile tl = tiles[blockIdx.y];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int mh = wave & 1, np = wave >> 1;
   const int nrb = N / 32;
-  if ((int)blockIdx.x * 4 >= nrb) return;
   const int gld = K / 128;
-
-  // activation rows staged by this thread: (tid >> 3) + 32 i, 16 bytes at (tid & 7) * 16
-  const int8_t* arow[QMF];
-  bool avalid[QMF];
-#pragma unroll
-  for (int i = 0; i < QMF; ++i) {
-    const int m = (tid >> 3) + 32 * i;
-    avalid[i] = m < tl.rows;
-    const int p = tl.row_begin + (avalid[i] ? m : 0);
-    arow[i] = aq + (size_t)((PASS == 1) ? perm[p] / k : p) * K;
-  }
-  // this wave's 32-row block
-  int rb = blockIdx.x * 4 + wave;
-  const bool nvalid = rb < nrb;
-  if (!nvalid) rb = nrb - 1;
   const char* slot = pool + (size_t)tl.slot * stride;
-  const char* wchunks = slot + off_codes + (size_t)rb * (K / 64) * 1024 + lane * 16;
-  const int n = rb * 32 + (lane & 31);
-  const uint16_t* srow = reinterpret_cast<const uint16_t*>(slot + off_scales) + (size_t)n * gld;
-
-  struct Stage {
-    u32x4 a[QMF], b[2];
-    float sw;
+  // copies of this wave per stage: A fragments (lmf, lks0), (lmf, lks0 + 1); B chunks of block
+  // `wave` of the tile; the scale words of its own two compute blocks
+  const int lmf = wave >> 1, lks0 = (wave & 1) * 2;
+  const int8_t* a_src;
+  {
+    const int m = lmf * 32 + (lane & 31);
+    const int p = tl.row_begin + (m < tl.rows ? m : 0);  // rows past the tile read row 0
+    a_src = aq + (size_t)((PASS == 1) ? perm[p] / k : p) * K + lks0 * 32 + 16 * (lane >> 5);
+  }
+  int lrb = blockIdx.x * (QBN / 32) + wave;
+  if (lrb >= nrb) lrb = nrb - 1;
+  const char* b_src = slot + off_codes + (size_t)lrb * (K / 64) * 1024 + lane * 16;
+  bool nvalid[2];
+  int rbv[2];
+  size_t se0[2];  // element index of this lane's scale row (row-major [N, K/128] bf16)
+  const uint32_t* scales32 = reinterpret_cast<const uint32_t*>(slot + off_scales);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    int rb = blockIdx.x * (QBN / 32) + np * 2 + nb;
+    nvalid[nb] = rb < nrb;
+    if (!nvalid[nb]) rb = nrb - 1;
+    rbv[nb] = rb;
+    se0[nb] = (size_t)(rb * 32 + (lane & 31)) * gld;
+  }
+  auto stage_a = [&](int buf) { return smem + buf * kQStageBytes; };
+  auto stage_b = [&](int buf) { return smem + buf * kQStageBytes + 16384; };
+  auto stage_s = [&](int buf) { return smem + buf * kQStageBytes + 32768; };
+  auto issue = [&](int kt, int buf) {
+    int8_t* la = stage_a(buf) + (lmf * 4 + lks0) * 1024;
+    __builtin_amdgcn_global_load_lds(a_src + kt * QBK, la, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(a_src + kt * QBK + 32, la + 1024, 16, 0, 0);
+    int8_t* lb = stage_b(buf) + wave * 2048;
+    __builtin_amdgcn_global_load_lds(b_src + (size_t)(2 * kt) * 1024, lb, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b_src + (size_t)(2 * kt + 1) * 1024, lb + 1024, 16, 0, 0);
+    int8_t* ls = stage_s(buf) + wave * 512;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      __builtin_amdgcn_global_load_lds(scales32 + ((se0[nb] + kt) >> 1), ls + nb * 256, 4, 0, 0);
   };
-  Stage st[kQAhead];
-  auto gload = [&](Stage& r, int kt) {
-#pragma unroll
-    for (int i = 0; i < QMF; ++i)
-      r.a[i] = avalid[i] ? ld16(arow[i] + kt * QBK + (tid & 7) * 16) : u32x4{0u, 0u, 0u, 0u};
-    // cacheable: the other M-tiles of the group read the same chunks
-#pragma unroll
-    for (int c = 0; c < 2; ++c) r.b[c] = ld16(wchunks + (size_t)(2 * kt + c) * 1024);
-    r.sw = bf16_to_f32(srow[kt]) * 0.0625f;  // codes enter as 16 q
+  // group kt's scale of compute block nb, as the bits of a float (the bf16 in the high half)
+  auto scale_bits = [&](int buf, int kt, int nb) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(stage_s(buf) + wave * 512 + nb * 256 + lane * 4);
+    return ((se0[nb] + kt) & 1) ? (w & 0xFFFF0000u) : (w << 16);
   };
-  auto astore = [&](const Stage& r, int buf) {
+  float accf[2][2][16];
 #pragma unroll
-    for (int i = 0; i < QMF; ++i)
-      *reinterpret_cast<u32x4*>(&sA[buf][((tid >> 3) + 32 * i) * A_LD + (tid & 7) * 16]) = r.a[i];
+  for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accf[mf][nb][r] = 0.f;
+  intx16 acc[2][2];
+  const intx16 zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  auto fold = [&](int mf, const uint32_t (&sb)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float sw = __uint_as_float(sb[nb]) * 0.0625f;  // codes enter as 16 q
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accf[mf][nb][r] = fmaf((float)acc[mf][nb][r], sw, accf[mf][nb][r]);
+    }
   };
-
-  float accf[QMF][16];
-#pragma unroll
-  for (int j = 0; j < QMF; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) accf[j][r] = 0.f;
-
   const int nk = K / QBK;
 #pragma unroll
-  for (int s2 = 0; s2 < kQAhead; ++s2)
-    if (s2 < nk) gload(st[s2], s2);
-  astore(st[0], 0);
-  __syncthreads();
-  auto step = [&](Stage& mine, Stage& next, int kt) {
-    const int buf = kt & 1;
-    intx16 acci[QMF];
-#pragma unroll
-    for (int j = 0; j < QMF; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acci[j][r] = 0;
-#pragma unroll
-    for (int ks = 0; ks < QBK / 32; ++ks) {
-      const u32x4& cw = mine.b[ks >> 1];
-      const uint32_t w0 = (ks & 1) ? cw.z : cw.x, w1 = (ks & 1) ? cw.w : cw.y;
-      intx4 b;
-      b[0] = (int)((w0 << 4) & 0xF0F0F0F0u);
-      b[1] = (int)(w0 & 0xF0F0F0F0u);
-      b[2] = (int)((w1 << 4) & 0xF0F0F0F0u);
-      b[3] = (int)(w1 & 0xF0F0F0F0u);
-      // every fragment, rows or not: a uniform MFMA chain schedules better than skipping
-#pragma unroll
-      for (int j = 0; j < QMF; ++j) {
-        const intx4 a = *reinterpret_cast<const intx4*>(
-            &sA[buf][(j * 32 + (lane & 31)) * A_LD + ks * 32 + 16 * (lane >> 5)]);
-        acci[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acci[j], 0, 0, 0);
-      }
+  for (int s2 = 0; s2 < kQStages - 1; ++s2)
+    if (s2 < nk) issue(s2, s2);
+  auto step = [&](int kt, int buf) {
+    const int after = nk - 1 - kt;  // stages issued after kt, at most kQStages - 2
+    if (after >= 2) vm_wait<12>(); else if (after == 1) vm_wait<6>(); else vm_wait<0>();
+    asm volatile("s_barrier" ::: "memory");
+    const int pbuf = (buf + kQStages - 1) % kQStages;
+    uint32_t sprev[2] = {0u, 0u};
+    if (kt > 0) {
+      sprev[0] = scale_bits(pbuf, kt - 1, 0);
+      sprev[1] = scale_bits(pbuf, kt - 1, 1);
     }
-    // fold this scale group into fp32
+    const uint32_t scur[2] = {scale_bits(buf, kt, 0), scale_bits(buf, kt, 1)};
+    // every wave has finished group kt - 1, so its stage can be refilled
+    if (kt + kQStages - 1 < nk) issue(kt + kQStages - 1, pbuf);
+    const int8_t* A = stage_a(buf);
+    const int8_t* Bs = stage_b(buf);
+    u32x4 bch[2][2];
 #pragma unroll
-    for (int j = 0; j < QMF; ++j)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) accf[j][r] = fmaf((float)acci[j][r], mine.sw, accf[j][r]);
-    if (kt + kQAhead < nk) gload(mine, kt + kQAhead);
-    if (kt + 1 < nk) astore(next, buf ^ 1);
-    __syncthreads();
+      for (int c = 0; c < 2; ++c)
+        bch[nb][c] = *reinterpret_cast<const u32x4*>(Bs + ((np * 2 + nb) * 2 + c) * 1024 + lane * 16);
+    if (kt > 0) fold(1, sprev);  // before this group overwrites those accumulators
+#pragma unroll
+    for (int mf = 0; mf < 2; ++mf) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const intx4 a = *reinterpret_cast<const intx4*>(A + ((mh * 2 + mf) * 4 + ks) * 1024 + lane * 16);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const u32x4& cw = bch[nb][ks >> 1];
+          const uint32_t w0 = (ks & 1) ? cw.z : cw.x, w1 = (ks & 1) ? cw.w : cw.y;
+          intx4 b;
+          b[0] = (int)((w0 << 4) & 0xF0F0F0F0u);
+          b[1] = (int)(w0 & 0xF0F0F0F0u);
+          b[2] = (int)((w1 << 4) & 0xF0F0F0F0u);
+          b[3] = (int)(w1 & 0xF0F0F0F0u);
+          acc[mf][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, ks == 0 ? zero16 : acc[mf][nb], 0, 0, 0);
+        }
+      }
+      if (mf == 0) fold(0, scur);  // overlaps the second fragment's MFMAs
+    }
   };
-  for (int kt = 0; kt < nk; kt += kQAhead) {
+  for (int kt = 0; kt < nk; kt += kQStages) {
 #pragma unroll
-    for (int s2 = 0; s2 < kQAhead; ++s2)
-      if (kt + s2 < nk) step(st[s2], st[(s2 + 1) % kQAhead], kt + s2);
+    for (int j = 0; j < kQStages; ++j)
+      if (kt + j < nk) step(kt + j, j);
   }
-
+  {
+    const int lb = (nk - 1) % kQStages;
+    const uint32_t sl[2] = {scale_bits(lb, nk - 1, 0), scale_bits(lb, nk - 1, 1)};
+    fold(1, sl);
+  }
 #pragma unroll
-  for (int j = 0; j < QMF; ++j) {
+  for (int mf = 0; mf < 2; ++mf) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = j * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const bool ok = m < tl.rows;
-      const int p = tl.row_begin + (ok ? m : 0);
-      const float sx = as[(PASS == 1) ? perm[p] / k : p];
-      const float v = accf[j][r] * sx;
-      if constexpr (PASS == 1) {
-        const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
-        if ((n & 1) == 0 && ok && nvalid) out[(size_t)p * out_ld + (n >> 1)] = silu(v) * u;
-      } else {
-        if (ok && nvalid) out[(size_t)p * out_ld + n] = v;
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = rbv[nb] * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = (mh * 2 + mf) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const bool ok = m < tl.rows;
+        const int p = tl.row_begin + (ok ? m : 0);
+        const float sx = as[(PASS == 1) ? perm[p] / k : p];
+        const float v = accf[mf][nb][r] * sx;
+        if constexpr (PASS == 1) {
+          const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
+          if ((n & 1) == 0 && ok && nvalid[nb]) out[(size_t)p * out_ld + (n >> 1)] = silu(v) * u;
+        } else {
+          if (ok && nvalid[nb]) out[(size_t)p * out_ld + n] = v;
+        }
       }
     }
   }
@@ -328,7 +381,7 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
     launch_gemv_any(true, nt, xq, xs, perm, k, items, n_items, max_items, pool, stride, lay, H, F,
                     hbuf, s);
   if (max_tiles > 0)
-    hipLaunchKernelGGL(gemm_w4a8_kernel<1>, dim3((2 * F / 32 + 3) / 4, max_tiles), dim3(256), 0,
+    hipLaunchKernelGGL(gemm_w4a8_kernel<1>, dim3((2 * F + QBN - 1) / QBN, max_tiles), dim3(512), 0,
                        s, xq, xs, perm, k, tiles, n_tiles, pool, stride, lay.off_w13,
                        lay.off_s13, 2 * F, H, F, hbuf);
   hipLaunchKernelGGL(quant_rows_kernel<MOE_F32>, dim3((unsigned)rows), dim3(256), 0, s, hbuf, F,
@@ -337,7 +390,7 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
     launch_gemv_any(false, nt, hq, hs, perm, k, items, n_items, max_items, pool, stride, lay, H,
                     F, y, s);
   if (max_tiles > 0)
-    hipLaunchKernelGGL(gemm_w4a8_kernel<2>, dim3((H / 32 + 3) / 4, max_tiles), dim3(256), 0, s,
+    hipLaunchKernelGGL(gemm_w4a8_kernel<2>, dim3((H + QBN - 1) / QBN, max_tiles), dim3(512), 0, s,
                        hq, hs, perm, k, tiles, n_tiles, pool, stride, lay.off_w2, lay.off_s2, H,
                        F, H, y);
   return moe_launch_status();

@@ -162,6 +162,9 @@ FFN_CASES = [
     (W.reduced(DSV3, E=16, k=4, H=512, F=256), 300),
     (W.reduced(DSV3, E=12, k=8, H=7168, F=2048), 2),  # full hidden/FFN sizes
     (W.reduced(DSV3, E=12, k=8, H=7168, F=2048), 24),
+    (W.reduced(DSV3, E=12, k=8, H=7168, F=2048), 200),  # every group on MFMA tiles, some > 128 rows
+    (W.reduced(DSV3, E=8, k=4, H=384, F=384), 40),     # 3 scale groups per row, partial 256-row tiles
+    (W.reduced(DSV3, E=8, k=4, H=384, F=384), 300),
 ]
 
 
