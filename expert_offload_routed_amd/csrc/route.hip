@@ -7,7 +7,11 @@
 // Aware Placement and Pruning for Efficient Mixture-of-Experts Inference",
 // Sec. II-A, Eq. (1)).
 //
-// Two kernels:
+// Kernels:
+//   route_logits_mfma_kernel: bf16 tokens, many tokens and experts: the
+//     logits as a dense contraction on v_mfma_f32_32x32x16_bf16, one
+//     workgroup per 32 tokens x 32 experts, its 8 waves splitting H; the 8
+//     partial tiles meet in LDS, summed in wave order.
 //   route_logits_kernel: one workgroup per (expert, tile of 8 tokens); its
 //     256 threads split H into 8-element vectors (16-byte bf16 / 2x16-byte
 //     fp32 loads), fp32 FMA, then a wave and a cross-wave reduction. A decode
@@ -84,6 +88,56 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
     const int t = threadIdx.x;
     const float s = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
     logits[(size_t)(t0 + t) * E + e] = s + (bias ? bias[e] : 0.f);
+  }
+}
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+
+// MFMA operand lanes (checked on gfx950): lane l holds row l % 32 and the 8
+// K values 8 (l / 32) .. +7 of each 16-wide K step; accumulator r holds row
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+constexpr int kLgSplit = 8;  // waves per workgroup, each a contiguous H slice
+constexpr int kLgU = 8;      // K steps of loads in flight per wave
+__global__ __launch_bounds__(64 * kLgSplit) void route_logits_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const float* __restrict__ bias, int T, int H, int E, float* __restrict__ logits) {
+  __shared__ float red[kLgSplit][32 * 33];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int klen = H / kLgSplit;
+  const int kbeg = wave * klen + 8 * (lane >> 5);
+  const int ta = min(t0 + (lane & 31), T - 1), eb = min(e0 + (lane & 31), E - 1);
+  const uint16_t* pa = x + (size_t)ta * H + kbeg;
+  const uint16_t* pb = w + (size_t)eb * H + kbeg;
+  floatx16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int kk = 0; kk < klen; kk += 16 * kLgU) {
+    u32x4 av[kLgU], bv[kLgU];
+#pragma unroll
+    for (int u = 0; u < kLgU; ++u) {
+      if (kk + u * 16 < klen) {
+        av[u] = ld16(pa + kk + u * 16);
+        bv[u] = ld16(pb + kk + u * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kLgU; ++u) {
+      if (kk + u * 16 < klen)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&av[u]),
+                                                      *reinterpret_cast<const bf16x8*>(&bv[u]), acc, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[wave][(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * 33 + (lane & 31)] = acc[r];
+  __syncthreads();
+  for (int o = tid; o < 1024; o += 64 * kLgSplit) {
+    const int i = o >> 5, j = o & 31;
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kLgSplit; ++v) sum += red[v][i * 33 + j];
+    if (t0 + i < T && e0 + j < E) logits[(size_t)(t0 + i) * E + e0 + j] = sum + (bias ? bias[e0 + j] : 0.f);
   }
 }
 
@@ -448,7 +502,11 @@ extern "C" int moe_route(const void* x, int x_dtype, const void* w_router, const
 
   dim3 g1(E, (T + kRouteTT - 1) / kRouteTT);
   if (g1.y > 65535u) return MOE_EUNSUPPORTED;
-  if (x_dtype == MOE_BF16)
+  if (x_dtype == MOE_BF16 && T >= 64 && E >= 32 && H % (16 * kLgSplit) == 0)
+    hipLaunchKernelGGL(route_logits_mfma_kernel, dim3((T + 31) / 32, (E + 31) / 32),
+                       dim3(64 * kLgSplit), 0, stream, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(w_router), bias, T, H, E, logits);
+  else if (x_dtype == MOE_BF16)
     hipLaunchKernelGGL(route_logits_kernel<MOE_BF16>, g1, dim3(256), 0, stream, x, w_router, bias,
                        T, H, E, logits);
   else
