@@ -13,6 +13,7 @@
 // that baseline made precise (the pages give no hot-path victim rule).
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "common.h"
@@ -243,25 +244,23 @@ extern "C" int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, i
       misses.push_back(e);
     }
   }
-  // Victims: empty slots by id, then the other slots by (last use, id).
+  // Victims (only when something misses): empty slots by id, then the other
+  // slots by (last use, id); only as many as the misses need are ordered.
   std::vector<int> victims, used;
-  for (int s = 0; s < S; ++s)
-    if (owner[s] < 0) victims.push_back(s);
-  std::vector<int> reuse;
-  for (int s = 0; s < S; ++s)
-    if (owner[s] >= 0 && !kept[s]) reuse.push_back(s);
-  // insertion sort by (last_use, slot): small S per call, no allocation churn
-  for (size_t i = 1; i < reuse.size(); ++i) {
-    const int s = reuse[i];
-    size_t j = i;
-    while (j > 0 && (last_use[reuse[j - 1]] > last_use[s] ||
-                     (last_use[reuse[j - 1]] == last_use[s] && reuse[j - 1] > s))) {
-      reuse[j] = reuse[j - 1];
-      --j;
-    }
-    reuse[j] = s;
+  if (!misses.empty()) {
+    for (int s = 0; s < S; ++s)
+      if (owner[s] < 0) victims.push_back(s);
+    std::vector<int> reuse;
+    for (int s = 0; s < S; ++s)
+      if (owner[s] >= 0 && !kept[s]) reuse.push_back(s);
+    const size_t need = misses.size() > victims.size() ? misses.size() - victims.size() : 0;
+    auto older = [&](int a, int b) {
+      return last_use[a] < last_use[b] || (last_use[a] == last_use[b] && a < b);
+    };
+    const size_t take = need < reuse.size() ? need : reuse.size();
+    std::partial_sort(reuse.begin(), reuse.begin() + take, reuse.end(), older);
+    victims.insert(victims.end(), reuse.begin(), reuse.begin() + take);
   }
-  victims.insert(victims.end(), reuse.begin(), reuse.end());
 
   *clock += 1;
   int nf = 0, nw = 1;

@@ -130,7 +130,7 @@ def _lib_state(S, L, E, residency):
 
 
 @pytest.mark.parametrize("S,L,E,kmax,seed", [(4, 1, 8, 2, 0), (3, 2, 6, 4, 1), (16, 1, 64, 6, 2),
-                                             (7, 3, 10, 3, 3), (1, 1, 5, 2, 4)])
+                                             (7, 3, 10, 3, 3), (1, 1, 5, 2, 4), (300, 6, 128, 8, 5)])
 def test_plan_fills_matches_oracle_planner(lib, S, L, E, kmax, seed):
     rng = np.random.default_rng(seed)
     init = [(int(rng.integers(L)), int(e)) for e in rng.choice(E, size=min(S, E) - 1, replace=False)]
