@@ -70,8 +70,10 @@ def _run(layer, batches, out, timing):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for step in batches:
-        for li, x in step:
-            layer.forward(x, layer=li, out=out)
+        if len(step) == 1:
+            layer.forward(step[0][1], layer=step[0][0], out=out)
+        else:  # a stack step: every layer in one native call
+            layer.forward_steps(step, out)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     c1 = layer.counters()

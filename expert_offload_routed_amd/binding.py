@@ -44,6 +44,8 @@ _SIGNATURES = {
     "moe_ctx_destroy": (_i32, [_vp]),
     "moe_ctx_place": (_i32, [_vp, _i32, _i32, _i32]),
     "moe_layer_forward": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp]),
+    "moe_ctx_forward_steps": (_i32, [_vp, _i32, _vp, ctypes.POINTER(_vp), _i32, ctypes.POINTER(_vp),
+                                     ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32]),
     "moe_ctx_read_tables": (_i32, [_vp, _vp, _vp, _vp, _vp]),
     "moe_ctx_outputs": (_i32, [_vp] + [ctypes.POINTER(_vp)] * 6),
     "moe_ctx_set_timing": (_i32, [_vp, _i32]),
@@ -328,6 +330,22 @@ class LayerContext:
             raise ValueError("moe_layer_forward: output or bias size")
         _call("moe_layer_forward", self.handle, layer, _dev(x), T, _dev(w_router), _dev(bias), _dev(out),
               dtype_code(out), _host(stats))
+
+    def forward_steps(self, steps, out_dtype_code: int) -> None:
+        """steps: list of (layer, x, w_router, bias, out), run in order by one moe_ctx_forward_steps call."""
+        n = len(steps)
+        if n == 0:
+            return
+        T = steps[0][1].shape[0]
+        for layer, x, wr, b, out in steps:
+            if (x.shape[0] != T or T > self.t_max or x.shape[1] != self.H or tuple(wr.shape) != (self.E, self.H)
+                    or out.numel() < T * self.H or (b is not None and b.numel() != self.E)
+                    or not 0 <= layer < self.L):
+                raise ValueError("moe_ctx_forward_steps: shape mismatch")
+        layers = np.array([s[0] for s in steps], np.int32)
+        ptrs = lambda i: (ctypes.c_void_p * n)(*[_dev(s[i]) for s in steps])
+        _call("moe_ctx_forward_steps", self.handle, n, _host(layers), ptrs(1), T, ptrs(2), ptrs(3), ptrs(4),
+              out_dtype_code)
 
     def tables(self):
         lut = np.empty(self.L * self.E, np.int32)

@@ -218,7 +218,7 @@ extern "C" size_t moe_ffn_workspace_bytes(int T, int H, int F, int E, int k, int
 int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* lut,
              const int32_t* group_mask, int n_shared, int shared_slot0, const char* pool,
              size_t stride, int num_slots, const SlotLayout& lay, int T, int H, int F, int E, int k,
-             float* y, int32_t* err, char* ws, const FfnWorkspace& wl, hipStream_t s);
+             float* y, int32_t* err, char* ws, const FfnWorkspace& wl, hipStream_t s, bool planned);
 
 extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
                               const int32_t* offsets, const int32_t* lut,
@@ -235,7 +235,7 @@ int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* o
                const int32_t* lut, const int32_t* group_mask, int n_shared, int shared_slot0,
                const void* pool_base, size_t slot_stride, int num_slots, int w_dtype, int T, int H,
                int F, int E, int k, float* y_perm, int32_t* err_word, void* workspace,
-               size_t ws_bytes, hipStream_t stream) {
+               size_t ws_bytes, hipStream_t stream, bool planned) {
   MOE_CHECK_ARG(T >= 0 && k >= 1 && k <= E && n_shared >= 0 && E + n_shared <= 1024);
   MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
   SlotLayout lay;
@@ -256,7 +256,7 @@ int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* o
   if (w_dtype == MOE_INT4G128)
     return ffn_int4(x, perm, offsets, lut, group_mask, n_shared, shared_slot0,
                     static_cast<const char*>(pool_base), slot_stride, num_slots, lay, T, H, F, E, k,
-                    y_perm, err_word, wsb, ws, stream);
+                    y_perm, err_word, wsb, ws, stream, planned);
 
   int32_t* n_items = reinterpret_cast<int32_t*>(wsb);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(wsb + 4);
@@ -271,8 +271,9 @@ int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* o
   const int max_tiles = (bf16 && T > small_max) ? ws.max_tiles : 0;
   MOE_CHECK_ARG(max_tiles <= 65535);
 
-  launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max, items,
-                  n_items, tiles, n_tiles, err_word, stream);
+  if (!planned)
+    launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max,
+                    items, n_items, tiles, n_tiles, err_word, stream);
   const char* pool = static_cast<const char*>(pool_base);
   const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;  // rows of the largest GEMV group
   if (bf16) {

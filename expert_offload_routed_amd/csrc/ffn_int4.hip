@@ -355,7 +355,8 @@ void launch_gemv_any(bool first, int nt, const int8_t* aq, const float* as, cons
 int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* lut,
              const int32_t* group_mask, int n_shared, int shared_slot0, const char* pool,
              size_t stride, int num_slots, const SlotLayout& lay, int T, int H, int F, int E, int k,
-             float* y, int32_t* err, char* ws, const FfnWorkspace& wl, hipStream_t s) {
+             float* y, int32_t* err, char* ws, const FfnWorkspace& wl, hipStream_t s,
+             bool planned) {
   int32_t* n_items = reinterpret_cast<int32_t*>(ws);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + 4);
   FfnItem* items = reinterpret_cast<FfnItem*>(ws + wl.items);
@@ -372,8 +373,9 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   const int max_items = small_max == 0 ? 0 : (int)(tk < E ? tk : E) + n_shared;
   const int max_tiles = (T > small_max) ? wl.max_tiles : 0;
   if (max_tiles > 65535) return MOE_EUNSUPPORTED;
-  launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max, items,
-                  n_items, tiles, n_tiles, err, s);
+  if (!planned)
+    launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max,
+                    items, n_items, tiles, n_tiles, err, s);
   hipLaunchKernelGGL(quant_rows_kernel<MOE_BF16>, dim3(T), dim3(256), 0, s, x, H, nullptr, nullptr,
                      nullptr, 0, 0, 0, xq, xs);
   const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;

@@ -53,6 +53,27 @@ void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, con
 // Workspace of a call over T tokens with E routed experts (k per token) and
 // n_shared shared experts carried as extra groups.
 FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype, int n_shared);
+// Expert FFN work list for the decode front end to write: routed groups
+// through `lut` (E entries) and n_shared shared groups (T rows each after the
+// T*k routed rows, slots shared_slot0 + s), groups of <= small_max rows as
+// items, the others as kGemmBM-row tiles, into the FFN workspace's lists.
+struct FrontPlan {
+  const int32_t* lut;
+  int num_slots, n_shared, shared_slot0, small_max;
+  FfnItem* items;
+  int32_t* n_items;
+  GemmTile* tiles;
+  int32_t* n_tiles;
+  int32_t* err;
+};
+// moe_route_permute that, on its one-launch path, also writes the expert FFN's
+// work list described by *plan (*planned = true); otherwise the FFN plans.
+int route_permute_plan(const void* x, int x_dtype, const void* w_router, const float* bias, int T,
+                       int H, int E, int k, int renorm, float* logits, int32_t* topk_ids,
+                       float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* inv, int32_t* distinct, int32_t* n_distinct,
+                       uint32_t* sync_counter, const FrontPlan* plan, bool* planned,
+                       hipStream_t stream);
 // moe_expert_ffn with the shared experts as groups E .. E+n_shared-1: offsets
 // has E + n_shared + 1 entries, group E + s holds T rows (perm value t * k for
 // token t) and reads slot shared_slot0 + s; group_mask applies to routed groups.
@@ -60,4 +81,4 @@ int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* o
                const int32_t* lut, const int32_t* group_mask, int n_shared, int shared_slot0,
                const void* pool_base, size_t slot_stride, int num_slots, int w_dtype, int T, int H,
                int F, int E, int k, float* y_perm, int32_t* err_word, void* workspace,
-               size_t ws_bytes, hipStream_t stream);
+               size_t ws_bytes, hipStream_t stream, bool planned = false);

@@ -23,6 +23,7 @@
 #include <limits.h>
 
 #include "common.h"
+#include "ffn_internal.h"
 
 namespace {
 
@@ -148,13 +149,14 @@ __device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
 
 // Top-k and routing weights of token t; executed by one whole wave. The
 // outputs ([t*k + r]) may be global memory or LDS.
+template <int NV>
 __device__ void topk_token(const float* __restrict__ logits, int t, int E, int k, int renorm,
                            int32_t* __restrict__ ids, float* __restrict__ weights) {
   const int lane = threadIdx.x & 63;
-  float v[kTopkMaxV];
+  float v[NV];
   uint32_t avail = 0;  // bit i: logit of expert lane + 64 i still selectable
 #pragma unroll
-  for (int i = 0; i < kTopkMaxV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
     v[i] = -INFINITY;
     if (e < E) {
@@ -162,16 +164,16 @@ __device__ void topk_token(const float* __restrict__ logits, int t, int E, int k
       avail |= 1u << i;
     }
   }
-  float sel[kTopkMaxV];  // selected value r is held by lane r % 64 in sel[r / 64]
+  float sel[NV];  // selected value r is held by lane r % 64 in sel[r / 64]
 #pragma unroll
-  for (int i = 0; i < kTopkMaxV; ++i) sel[i] = 0.f;
+  for (int i = 0; i < NV; ++i) sel[i] = 0.f;
   float vmax = 0.f;
 
   for (int r = 0; r < k; ++r) {
     float bv = -INFINITY;
     int bid = INT_MAX;
 #pragma unroll
-    for (int i = 0; i < kTopkMaxV; ++i) {
+    for (int i = 0; i < NV; ++i) {
       if ((avail >> i) & 1u) {
         if (better(v[i], lane + 64 * i, bv, bid)) {
           bv = v[i];
@@ -190,7 +192,7 @@ __device__ void topk_token(const float* __restrict__ logits, int t, int E, int k
     }
     if (bid != INT_MAX && (bid & 63) == lane) avail &= ~(1u << (bid >> 6));
 #pragma unroll
-    for (int i = 0; i < kTopkMaxV; ++i)
+    for (int i = 0; i < NV; ++i)
       if (i == (r >> 6) && lane == (r & 63)) sel[i] = bv;
     if (r == 0) vmax = bv;
     if (lane == 0) ids[(size_t)t * k + r] = (bid == INT_MAX) ? -1 : bid;
@@ -199,16 +201,16 @@ __device__ void topk_token(const float* __restrict__ logits, int t, int E, int k
   float denom = 0.f;
   if (renorm) {
 #pragma unroll
-    for (int i = 0; i < kTopkMaxV; ++i)
+    for (int i = 0; i < NV; ++i)
       if (lane + 64 * i < k) denom += expf(sel[i] - vmax);
   } else {
 #pragma unroll
-    for (int i = 0; i < kTopkMaxV; ++i)
+    for (int i = 0; i < NV; ++i)
       if (lane + 64 * i < E) denom += expf(v[i] - vmax);
   }
   denom = wave_sum(denom);
 #pragma unroll
-  for (int i = 0; i < kTopkMaxV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int r = lane + 64 * i;
     if (r < k) weights[(size_t)t * k + r] = expf(sel[i] - vmax) / denom;
   }
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
                                                            float* __restrict__ weights) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token(logits, t, E, k, renorm, ids, weights);
+  topk_token<kTopkMaxV>(logits, t, E, k, renorm, ids, weights);
 }
 
 // Second half of the decode front end, run by one workgroup (any size up to
@@ -238,14 +240,56 @@ struct FrontLds {
   int wave[40];     // scan scratch
 };
 
+// Work list of the expert FFN written by the front end itself (see FrontPlan):
+// the same items and tiles, in the same order, as the FFN's own plan kernel.
+__device__ void front_plan(const FrontPlan& pl, int T, int E, int k, const FrontLds& L,
+                           int* s_wave) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int G = E + pl.n_shared;
+  const int per = (G + nthr - 1) / nthr;  // groups of this thread: [tid * per, +per)
+  int n_it = 0, n_tl = 0;
+  for (int g = tid * per; g < G && g < (tid + 1) * per; ++g) {
+    const int rows = g < E ? L.cnt[g] : T;
+    if (rows <= 0) continue;
+    const int slot = g < E ? pl.lut[g] : pl.shared_slot0 + (g - E);
+    if (slot < 0 || slot >= pl.num_slots) continue;
+    if (rows <= pl.small_max) ++n_it; else n_tl += (rows + kGemmBM - 1) / kGemmBM;
+  }
+  int tot_it = 0, tot_tl = 0;
+  int ip = block_exclusive_scan(n_it, s_wave, &tot_it);
+  int tp = block_exclusive_scan(n_tl, s_wave, &tot_tl);
+  for (int g = tid * per; g < G && g < (tid + 1) * per; ++g) {
+    const int rows = g < E ? L.cnt[g] : T;
+    if (rows <= 0) continue;
+    const int begin = g < E ? L.off[g] : T * k + (g - E) * T;
+    const int slot = g < E ? pl.lut[g] : pl.shared_slot0 + (g - E);
+    if (slot < 0 || slot >= pl.num_slots) {
+      atomicOr(pl.err, MOE_ERR_ABSENT);
+      continue;
+    }
+    if (rows <= pl.small_max) {
+      pl.items[ip++] = FfnItem{g, slot, begin, rows};
+    } else {
+      for (int r0 = 0; r0 < rows; r0 += kGemmBM)
+        pl.tiles[tp++] = GemmTile{g, slot, begin + r0, min(kGemmBM, rows - r0)};
+    }
+  }
+  if (tid == 0) {
+    pl.n_items[0] = tot_it;
+    pl.n_tiles[0] = tot_tl;
+  }
+}
+
+template <int NV>
 __device__ void front_select_and_sort(const float* lg, int T, int E, int k, int renorm,
                                       int32_t* __restrict__ ids, float* __restrict__ weights,
                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                       int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                                       int32_t* __restrict__ distinct,
-                                      int32_t* __restrict__ n_distinct, FrontLds& L, int* s_dist) {
+                                      int32_t* __restrict__ n_distinct, FrontLds& L, int* s_dist,
+                                      const FrontPlan& pl) {
   const int tid = threadIdx.x, nthr = blockDim.x, wave = tid >> 6, nwaves = nthr >> 6;
-  for (int t = wave; t < T; t += nwaves) topk_token(lg, t, E, k, renorm, L.ids, L.w);
+  for (int t = wave; t < T; t += nwaves) topk_token<NV>(lg, t, E, k, renorm, L.ids, L.w);
   const int n = T * k;
   for (int i = tid; i < 1024; i += nthr) L.cnt[i] = 0;
   __syncthreads();
@@ -288,6 +332,7 @@ __device__ void front_select_and_sort(const float* lg, int T, int E, int k, int 
     L.perm[L.off[ex] + rank] = f;
   }
   __syncthreads();
+  if (pl.lut) front_plan(pl, T, E, k, L, L.wave);  // its scans end with a barrier
   // outputs, no barrier after this point
   for (int i = tid; i < n; i += nthr) {
     ids[i] = L.ids[i];
@@ -324,12 +369,12 @@ __device__ __forceinline__ void stage_tokens(const void* __restrict__ x, size_t 
 
 // acc[t] += w_chunk . x[t][c*8 .. c*8+7] for every token, x read from LDS
 // (staged) or global memory.
-template <int FMT>
+template <int FMT, int MAXT>
 __device__ __forceinline__ void dot_chunk(const float (&wv)[8], const void* __restrict__ x,
                                           const void* s_x, bool staged, int T, int H, int c,
-                                          float (&acc)[kFrontMaxT]) {
+                                          float (&acc)[MAXT]) {
 #pragma unroll
-  for (int t = 0; t < kFrontMaxT; ++t) {
+  for (int t = 0; t < MAXT; ++t) {
     if (t < T) {
       float xv[8];
       load8<FMT>(staged ? s_x : x, (size_t)t * H + (size_t)c * 8, xv);
@@ -345,16 +390,16 @@ __device__ __forceinline__ void dot_chunk(const float (&wv)[8], const void* __re
 // workgroup to finish (a device-scope counter, released and acquired with
 // agent-scope fences) runs the selection and sort. The counter is left at
 // zero for the next launch.
-template <int FMT>
+template <int FMT, int MAXT, int NV>
 __global__ __launch_bounds__(256) void route_front_kernel(
     const void* __restrict__ x, const void* __restrict__ w,
     const float* __restrict__ bias, int T, int H, int E, int k, int renorm,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ weights,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, int32_t* __restrict__ distinct, int32_t* __restrict__ n_distinct,
-    unsigned* __restrict__ done) {
+    unsigned* __restrict__ done, FrontPlan pl) {
   __shared__ u32x4 s_x[kFrontXBytes / 16];
-  __shared__ float red[4][kFrontMaxT];
+  __shared__ float red[4][MAXT];
   __shared__ FrontLds L;
   __shared__ int s_dist[1024];
   __shared__ unsigned s_last;
@@ -365,9 +410,9 @@ __global__ __launch_bounds__(256) void route_front_kernel(
   const bool staged = xbytes <= kFrontXBytes;
   {
     const int nch = H / 8;
-    float acc[kFrontMaxT];
+    float acc[MAXT];
 #pragma unroll
-    for (int t = 0; t < kFrontMaxT; ++t) acc[t] = 0.f;
+    for (int t = 0; t < MAXT; ++t) acc[t] = 0.f;
     for (int cb = 0; cb < nch; cb += 256 * kFrontU) {
       float wv[kFrontU][8];
 #pragma unroll
@@ -382,11 +427,11 @@ __global__ __launch_bounds__(256) void route_front_kernel(
 #pragma unroll
       for (int u = 0; u < kFrontU; ++u) {
         const int c = cb + u * 256 + tid;
-        if (c < nch) dot_chunk<FMT>(wv[u], x, s_x, staged, T, H, c, acc);
+        if (c < nch) dot_chunk<FMT, MAXT>(wv[u], x, s_x, staged, T, H, c, acc);
       }
     }
 #pragma unroll
-    for (int t = 0; t < kFrontMaxT; ++t) {
+    for (int t = 0; t < MAXT; ++t) {
       if (t < T) {
         const float v = wave_sum(acc[t]);
         if (lane == 0) red[wave][t] = v;
@@ -405,8 +450,8 @@ __global__ __launch_bounds__(256) void route_front_kernel(
   __syncthreads();
   if (!s_last) return;
   __threadfence();  // see every other workgroup's logits
-  front_select_and_sort(logits, T, E, k, renorm, ids, weights, counts, offsets, perm, inv, distinct,
-                        n_distinct, L, s_dist);
+  front_select_and_sort<NV>(logits, T, E, k, renorm, ids, weights, counts, offsets, perm, inv, distinct,
+                        n_distinct, L, s_dist, pl);
   if (tid == 0) *done = 0u;
 }
 
@@ -419,13 +464,14 @@ __global__ __launch_bounds__(256) void route_front_kernel(
 constexpr int kSingleMaxE = 64;
 constexpr size_t kSingleMaxBytes = 64 * 1024;
 
-template <int FMT>
+template <int FMT, int MAXT, int NV>
 __global__ __launch_bounds__(1024) void route_front_single_kernel(
     const void* __restrict__ x, const void* __restrict__ w,
     const float* __restrict__ bias, int T, int H, int E, int k, int renorm,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ weights,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, int32_t* __restrict__ distinct, int32_t* __restrict__ n_distinct) {
+    int32_t* __restrict__ inv, int32_t* __restrict__ distinct, int32_t* __restrict__ n_distinct,
+    FrontPlan pl) {
   __shared__ u32x4 s_x[kFrontXBytes / 16];
   __shared__ float s_part[16 * kSingleMaxE];  // [pair][t]: pairs * T <= 1024; later the routed set
   __shared__ float s_lg[kFrontMaxT * kSingleMaxE];
@@ -442,9 +488,9 @@ __global__ __launch_bounds__(1024) void route_front_single_kernel(
     const bool active = p < E * S;
     const int e = active ? p / S : 0, sl = active ? p - e * S : 0;
     const int c0 = sl * nch / S, c1 = active ? (sl + 1) * nch / S : 0;
-    float acc[kFrontMaxT];
+    float acc[MAXT];
 #pragma unroll
-    for (int t = 0; t < kFrontMaxT; ++t) acc[t] = 0.f;
+    for (int t = 0; t < MAXT; ++t) acc[t] = 0.f;
     for (int cb = c0; cb < c1 || first; cb += 64 * kFrontU) {
       float wv[kFrontU][8];
 #pragma unroll
@@ -460,12 +506,12 @@ __global__ __launch_bounds__(1024) void route_front_single_kernel(
 #pragma unroll
       for (int u = 0; u < kFrontU; ++u) {
         const int c = cb + u * 64 + lane;
-        if (c < c1) dot_chunk<FMT>(wv[u], x, s_x, staged, T, H, c, acc);
+        if (c < c1) dot_chunk<FMT, MAXT>(wv[u], x, s_x, staged, T, H, c, acc);
       }
     }
     if (active) {
 #pragma unroll
-      for (int t = 0; t < kFrontMaxT; ++t) {
+      for (int t = 0; t < MAXT; ++t) {
         if (t < T) {
           const float v = wave_sum(acc[t]);
           if (lane == 0) s_part[p * T + t] = v;
@@ -483,8 +529,8 @@ __global__ __launch_bounds__(1024) void route_front_single_kernel(
   }
   __syncthreads();
   // s_part is free from here on: it holds the routed set
-  front_select_and_sort(s_lg, T, E, k, renorm, ids, weights, counts, offsets, perm, inv, distinct,
-                        n_distinct, L, reinterpret_cast<int*>(s_part));
+  front_select_and_sort<NV>(s_lg, T, E, k, renorm, ids, weights, counts, offsets, perm, inv, distinct,
+                        n_distinct, L, reinterpret_cast<int*>(s_part), pl);
   for (int i = tid; i < T * E; i += 1024) logits[i] = s_lg[i];
 }
 
@@ -522,6 +568,18 @@ extern "C" int moe_route_permute(const void* x, int x_dtype, const void* w_route
                                  int32_t* topk_ids, float* topk_w, int32_t* counts,
                                  int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* distinct,
                                  int32_t* n_distinct, uint32_t* sync_counter, hipStream_t stream) {
+  return route_permute_plan(x, x_dtype, w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w,
+                            counts, offsets, perm, inv, distinct, n_distinct, sync_counter, nullptr,
+                            nullptr, stream);
+}
+
+int route_permute_plan(const void* x, int x_dtype, const void* w_router, const float* bias, int T,
+                       int H, int E, int k, int renorm, float* logits, int32_t* topk_ids,
+                       float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* inv, int32_t* distinct, int32_t* n_distinct,
+                       uint32_t* sync_counter, const FrontPlan* plan, bool* planned,
+                       hipStream_t stream) {
+  if (planned) *planned = false;
   MOE_CHECK_ARG(T >= 0 && H > 0 && H % 8 == 0);
   MOE_CHECK_ARG(k >= 1 && k <= E && E <= 64 * kTopkMaxV);
   MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
@@ -535,24 +593,44 @@ extern "C" int moe_route_permute(const void* x, int x_dtype, const void* w_route
   MOE_CHECK_ARG(x && w_router && logits && topk_ids && topk_w && perm && inv);
   MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)w_router % 16) == 0);
   const size_t wbytes = (size_t)E * H * (x_dtype == MOE_BF16 ? 2 : 4);
-  if (E <= kSingleMaxE && wbytes <= kSingleMaxBytes) {
-    if (x_dtype == MOE_BF16)
-      hipLaunchKernelGGL(route_front_single_kernel<MOE_BF16>, dim3(1), dim3(1024), 0, stream, x,
-                         w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w, counts,
-                         offsets, perm, inv, distinct, n_distinct);
-    else
-      hipLaunchKernelGGL(route_front_single_kernel<MOE_F32>, dim3(1), dim3(1024), 0, stream, x,
-                         w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w, counts,
-                         offsets, perm, inv, distinct, n_distinct);
-    return moe_launch_status();
+  const bool single = E <= kSingleMaxE && wbytes <= kSingleMaxBytes;
+  FrontPlan pl{};
+  if (plan && E + plan->n_shared <= 1024) {
+    pl = *plan;
+    if (planned) *planned = true;
   }
-  if (x_dtype == MOE_BF16)
-    hipLaunchKernelGGL(route_front_kernel<MOE_BF16>, dim3(E), dim3(256), 0, stream, x, w_router,
-                       bias, T, H, E, k, renorm, logits, topk_ids, topk_w, counts, offsets, perm,
-                       inv, distinct, n_distinct, sync_counter);
-  else
-    hipLaunchKernelGGL(route_front_kernel<MOE_F32>, dim3(E), dim3(256), 0, stream, x, w_router,
-                       bias, T, H, E, k, renorm, logits, topk_ids, topk_w, counts, offsets, perm,
-                       inv, distinct, n_distinct, sync_counter);
+  // code specialised to the token count and logits per lane: the front end runs once per step,
+  // from a cold instruction cache, so it should hold only the code the step needs
+  const int maxt = T <= 1 ? 1 : (T <= 4 ? 4 : 16);
+  const int nv = E <= 64 ? 1 : (E <= 128 ? 2 : (E <= 256 ? 4 : 16));
+#define MOE_FRONT(FMT_, MAXT_, NV_)                                                               \
+  do {                                                                                           \
+    if (single)                                                                                  \
+      hipLaunchKernelGGL((route_front_single_kernel<FMT_, MAXT_, NV_>), dim3(1), dim3(1024), 0,  \
+                         stream, x, w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w, \
+                         counts, offsets, perm, inv, distinct, n_distinct, pl);                  \
+    else                                                                                         \
+      hipLaunchKernelGGL((route_front_kernel<FMT_, MAXT_, NV_>), dim3(E), dim3(256), 0, stream, x, \
+                         w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w, counts,   \
+                         offsets, perm, inv, distinct, n_distinct, sync_counter, pl);            \
+  } while (0)
+#define MOE_FRONT_NV(FMT_, MAXT_)                   \
+  do {                                              \
+    if (nv == 1) MOE_FRONT(FMT_, MAXT_, 1);         \
+    else if (nv == 2) MOE_FRONT(FMT_, MAXT_, 2);    \
+    else if (nv == 4) MOE_FRONT(FMT_, MAXT_, 4);    \
+    else MOE_FRONT(FMT_, MAXT_, kTopkMaxV);         \
+  } while (0)
+  if (x_dtype == MOE_BF16) {
+    if (maxt == 1) MOE_FRONT_NV(MOE_BF16, 1);
+    else if (maxt == 4) MOE_FRONT_NV(MOE_BF16, 4);
+    else MOE_FRONT_NV(MOE_BF16, kFrontMaxT);
+  } else {
+    if (maxt == 1) MOE_FRONT_NV(MOE_F32, 1);
+    else if (maxt == 4) MOE_FRONT_NV(MOE_F32, 4);
+    else MOE_FRONT_NV(MOE_F32, kFrontMaxT);
+  }
+#undef MOE_FRONT_NV
+#undef MOE_FRONT
   return moe_launch_status();
 }

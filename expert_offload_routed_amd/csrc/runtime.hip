@@ -20,6 +20,7 @@
 // that needs the tables.
 // The context allocates its staging once, at creation; a step allocates
 // nothing.
+#include <limits.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -423,16 +424,32 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   const int r = c->ring_next;
   int32_t* dh = c->ring_h + (size_t)r * (E + 1);
   int32_t* dd = c->ring_d + (size_t)r * (E + 1);
-  if ((rc = moe_route_permute(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
-                              c->topw, c->counts, c->offsets, c->perm, c->inv, dd, dd + E, c->sync,
-                              c->cs)) != MOE_OK)
+  const bool all_resident = c->resident[layer] == E;
+  const int32_t* lut_row = c->lut + (size_t)layer * E;
+  // a fully resident layer's FFN work list comes from the front end itself
+  FrontPlan fp{};
+  bool planned = false;
+  if (all_resident) {
+    const FfnWorkspace wl = ffn_workspace_layout(T, H, F, E, k, c->w_dtype, nsh);
+    fp.lut = lut_row;
+    fp.num_slots = nslots;
+    fp.n_shared = nsh;
+    fp.shared_slot0 = c->S;
+    fp.small_max = c->w_dtype == MOE_F32 ? INT_MAX : ffn_small_max(T, k, E, nsh);
+    fp.items = reinterpret_cast<FfnItem*>(c->ws + wl.items);
+    fp.n_items = reinterpret_cast<int32_t*>(c->ws);
+    fp.tiles = reinterpret_cast<GemmTile*>(c->ws + wl.tiles);
+    fp.n_tiles = reinterpret_cast<int32_t*>(c->ws + 4);
+    fp.err = c->err;
+  }
+  if ((rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
+                               c->topw, c->counts, c->offsets, c->perm, c->inv, dd, dd + E, c->sync,
+                               all_resident ? &fp : nullptr, &planned, c->cs)) != MOE_OK)
     return rc;
   if ((e = hipEventRecord(c->ring_ev[r], c->cs)) != hipSuccess) return moe_hip_status(e);
   c->ring_next = (r + 1) % kRing;
-  const bool all_resident = c->resident[layer] == E;
 
   int32_t n_fills = 0, n_waves = 0, nd = -1, hits = -1;
-  const int32_t* lut_row = c->lut + (size_t)layer * E;
   const bool timing = c->timing != 0;
   if (timing) {
     collect_timing(c, false);
@@ -445,7 +462,7 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
     c->ring_count += 1;
     if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, nullptr, nsh, c->S, c->pool,
                          c->stride, nslots, c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws,
-                         c->ws_bytes, c->cs)) != MOE_OK)
+                         c->ws_bytes, c->cs, planned)) != MOE_OK)
       return rc;
   } else {
     if ((rc = drain(c)) != MOE_OK) return rc;  // earlier steps first: their entries precede r
@@ -504,6 +521,19 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
     stats[1] = hits;
     stats[2] = n_fills;
     stats[3] = n_waves;
+  }
+  return MOE_OK;
+}
+
+extern "C" int moe_ctx_forward_steps(moe_layer_ctx* c, int n, const int32_t* layers,
+                                     const void* const* xs, int T, const void* const* w_routers,
+                                     const float* const* biases, void* const* outs,
+                                     int out_dtype) {
+  MOE_CHECK_ARG(c && n >= 0 && (n == 0 || (layers && xs && w_routers && biases && outs)));
+  for (int i = 0; i < n; ++i) {
+    const int rc = moe_layer_forward(c, layers[i], xs[i], T, w_routers[i], biases[i], outs[i],
+                                     out_dtype, nullptr);
+    if (rc != MOE_OK) return rc;
   }
   return MOE_OK;
 }

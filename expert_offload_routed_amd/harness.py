@@ -102,6 +102,11 @@ class SlotCacheLayer:
             stats.steps += 1
         return out
 
+    def forward_steps(self, steps, out: torch.Tensor) -> None:
+        """Run [(layer, x), ...] in order with one native call; every step writes `out`."""
+        code = B.dtype_code(out)
+        self.ctx.forward_steps([(l, x, self.routers[l][0], self.routers[l][1], out) for l, x in steps], code)
+
     def counters(self) -> dict:
         return self.ctx.counters()
 

@@ -81,6 +81,15 @@ int moe_ctx_place(moe_layer_ctx* ctx, int slot, int layer, int expert);
 int moe_layer_forward(moe_layer_ctx* ctx, int layer, const void* x, int T, const void* w_router,
                       const float* bias, void* out, int out_dtype, int32_t* stats);
 
+/* moe_ctx_forward_steps: n layer steps in order, exactly as n calls of
+ * moe_layer_forward (stats NULL) would run them; host arrays of length n hold
+ * each step's layer and device pointers (bias entries may be NULL). One call
+ * for a whole stack step keeps the host ahead of the GPU. Stops at the first
+ * step that fails and returns its status. */
+int moe_ctx_forward_steps(moe_layer_ctx* ctx, int n, const int32_t* layers, const void* const* xs,
+                          int T, const void* const* w_routers, const float* const* biases,
+                          void* const* outs, int out_dtype);
+
 /* moe_ctx_read_tables: host copies of the tables as the plan left them
  * (lut [L*E], owner [S], last_use [S], clock [1]); any pointer may be NULL.
  * Waits for the routed sets of earlier steps whose bookkeeping was deferred. */

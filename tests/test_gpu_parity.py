@@ -397,3 +397,28 @@ def test_layer_mixtral_full_size_prefill_sampled():
     r = rel_l2(got, ref)
     say(f"  prefill sampled rel L2 {r:.3e}, tokens under margin {under}")
     assert r <= TOL[shape.wfmt]
+
+
+def test_forward_steps_matches_single_calls():
+    """moe_ctx_forward_steps runs the same steps as moe_layer_forward calls: same output, tables, counters."""
+    shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=3, E=16, k=4, H=256,
+                      F=128, blobs=16)
+    say(f"forward_steps {shape.name}")
+    residency = W.initial_residency(shape, 14, "zipf_rank")
+    a = Hn.SlotCacheLayer(shape, 14, residency, 4)
+    b = Hn.SlotCacheLayer(shape, 14, residency, 4, store=a.store)
+    oa = torch.empty(4, shape.H, dtype=torch.bfloat16, device=_dev())
+    ob = torch.empty_like(oa)
+    for step in range(5):
+        T = 1 + step % 4
+        xs = [(l, W.tokens(shape, T, layer=l, step=step, device=_dev())) for l in range(3)]
+        for l, x in xs:
+            a.forward(x, layer=l, out=oa[:T])
+        b.forward_steps(xs, ob[:T])
+        torch.cuda.synchronize()
+        assert torch.equal(oa[:T], ob[:T])
+    assert a.counters() == b.counters()
+    ta, tb = a.tables(), b.tables()
+    for u, v in zip(ta, tb):
+        assert np.array_equal(np.asarray(u), np.asarray(v))
+    assert a.err.item() == 0 and b.err.item() == 0
