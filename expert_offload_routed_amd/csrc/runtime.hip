@@ -397,6 +397,7 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
                                  const void* w_router, const float* bias, void* out, int out_dtype,
                                  int32_t* stats) {
   MOE_CHECK_ARG(c && layer >= 0 && layer < c->L && T >= 0 && T <= c->t_max);
+  MOE_CHECK_ARG(out_dtype == MOE_F32 || out_dtype == MOE_BF16);
   if (T == 0) return MOE_OK;
   MOE_CHECK_ARG(x && w_router && out);
   const int E = c->E, k = c->k, H = c->H, F = c->F, nsh = c->n_shared;

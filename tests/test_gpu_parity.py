@@ -361,6 +361,18 @@ def test_layer_int4_shared_expert_misses():
     _run_layer_case(shape, 12, "zipf_rank", [1, 6, 40, 2])
 
 
+def test_layer_all_resident_decode_bf16_shared():
+    """Every expert resident (the front end plans the FFN; decode steps combine inside the
+    second pass), with shared experts; T > 4 takes the separate combine."""
+    shape = W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), E=16, k=6, H=256, F=256)
+    _run_layer_case(shape, 16, "zipf_rank", [1, 2, 4, 3, 8, 1])
+
+
+def test_layer_all_resident_decode_int4_shared():
+    shape = W.reduced(DSV3, E=16, k=4, H=256, F=128)
+    _run_layer_case(shape, 16, "zipf_rank", [1, 4, 2, 7, 1])
+
+
 def test_layer_mixtral_full_size_decode():
     """Full Mixtral-shaped layer (H=4096, F=14336), 4 of 8 experts resident, decode T=1 and T=8."""
     _run_layer_case(MIX, 4, "random", [1, 8])
