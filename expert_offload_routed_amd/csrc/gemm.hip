@@ -9,16 +9,20 @@
 //           (rows 2n / 2n+1 = gate / up of neuron n), epilogue
 //           h[p][n] = SiLU(gate) * up, stored bf16;
 //   pass 2: A = h rows (bf16), W = W2 of the slot, epilogue y[p][n] fp32.
-// Tiles: BM = 128 activation rows x 128 weight rows, K steps of BK = 64. Each
-// of the 4 waves owns one 32-row block of the tile-major weights (one
-// v_mfma_f32_32x32x16_bf16 accumulator per 32 activation rows; fragments
-// without rows are skipped): its operand fragments are whole 1 KB chunks of
-// the slot, read with one contiguous 16-byte load per lane straight into
-// registers. The loads stay cacheable so that the M-tiles of one group,
-// which run side by side, share the chunks through L2.
-// The activation tile, shared by the 4 waves, is staged through LDS (rows
-// padded to 72 elements, 8 lanes per 128-byte row segment). Global loads run
-// kAhead K-tiles ahead through a ring of register stages.
+// Tile: 128 activation rows (one GemmTile) x 256 weight rows (eight 32-row
+// blocks of the tile-major slot), K steps of 32. 8 waves; wave w computes
+// rows 64 (w & 1) .. +63 against weight blocks 2 (w >> 1), +1: four
+// v_mfma_f32_32x32x16_bf16 accumulators, so each LDS fragment feeds two MFMAs.
+// Operands reach LDS through asynchronous global -> LDS copies (16 bytes per
+// lane) in a ring of kStages stages, no register holding data in flight:
+//   A: 8 fragments of 1 KB per stage, fragment (mf, ks) holding row
+//      mf*32 + l%32, K values ks*16 + 8 (l / 32) .. +7 at lane l (the MFMA
+//      operand layout);
+//   B: the 16 chunks of the tile's 8 weight blocks, as stored.
+// Each wave issues 3 copies per stage; before computing stage kt it waits
+// until only the later stages' copies are outstanding, then one barrier
+// publishes the stage to all waves. A stage is 24 KB, so two workgroups share
+// a CU (4 waves per SIMD).
 // Lane layouts (checked on gfx950): A/B operand lane l holds row l % 32,
 // k = 8 (l / 32) .. +7; accumulator r holds row 8 (r / 4) + 4 (l / 32) + r % 4,
 // column l % 32.
@@ -30,119 +34,122 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
 
-constexpr int BM = kGemmBM;
-constexpr int MF = BM / 32;  // 32-row activation fragments per tile
-constexpr int BN = 128;
-constexpr int BK = 64;
-constexpr int LDS_LD = BK + 8;  // padded row (elements)
-constexpr int kAhead = 3;       // K-tiles of global loads in flight per thread
+constexpr int BM = kGemmBM;  // activation rows of a tile (128)
+constexpr int BN = 256;      // weight rows of a tile
+constexpr int BK = 32;       // K values of a stage
+constexpr int kStages = 3;
+constexpr int kStageBytes = 8192 + 16384;  // A, B
+static_assert(BM == 128, "the 8-wave bf16 tile covers 128 activation rows");
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
 
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (a device-only helper:
+// called straight from the kernel's lambdas the builtin hides the host launch stub)
+__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
 template <int PASS>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ perm, int k,
     const GemmTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
     const char* __restrict__ pool, size_t stride, size_t off, int N, int K, int out_ld,
     void* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDS_LD];
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   if ((int)blockIdx.y >= n_tiles[0]) return;
   const GemmTile tl = tiles[blockIdx.y];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int mh = wave & 1, np = wave >> 1;
   const int nrb = N / 32;
-  if ((int)blockIdx.x * 4 >= nrb) return;
-
-  // activation rows this thread stages: (tid >> 3) + 32 i, 16 bytes at (tid & 7) * 8 elements
-  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
-  const uint16_t* arow[MF];
-  bool avalid[MF];
-#pragma unroll
-  for (int i = 0; i < MF; ++i) {
-    const int m = lrow + 32 * i;
-    avalid[i] = m < tl.rows;
-    const int p = tl.row_begin + (avalid[i] ? m : 0);
+  // copies of this wave per stage: A fragment (lmf, lks); the 2 chunks of weight block `wave`
+  const int lmf = wave >> 1, lks = wave & 1;
+  const uint16_t* a_src;
+  {
+    const int m = lmf * 32 + (lane & 31);
+    const int p = tl.row_begin + (m < tl.rows ? m : 0);  // rows past the tile read row 0
     const size_t r = (PASS == 1) ? (size_t)(perm[p] / k) : (size_t)p;
-    arow[i] = act + r * K;
+    a_src = act + r * K + lks * 16 + 8 * (lane >> 5);
   }
-  // this wave's 32-row weight block; a block past N re-reads the last one and stores nothing
-  int rb = blockIdx.x * 4 + wave;
-  const bool nvalid = rb < nrb;
-  if (!nvalid) rb = nrb - 1;
-  const char* wchunks = pool + (size_t)tl.slot * stride + off + (size_t)rb * (K / 16) * 1024 + lane * 16;
-
-  // register stages: tile kt + kAhead is loaded right after tile kt is used
-  struct Stage {
-    u32x4 a[MF], b[BK / 16];
+  int lrb = blockIdx.x * (BN / 32) + wave;
+  if (lrb >= nrb) lrb = nrb - 1;
+  const char* b_src = pool + (size_t)tl.slot * stride + off + (size_t)lrb * (K / 16) * 1024 + lane * 16;
+  bool nvalid[2];
+  int rbv[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    int rb = blockIdx.x * (BN / 32) + np * 2 + nb;
+    nvalid[nb] = rb < nrb;
+    rbv[nb] = nvalid[nb] ? rb : nrb - 1;
+  }
+  auto stage_a = [&](int buf) { return smem + buf * kStageBytes; };
+  auto stage_b = [&](int buf) { return smem + buf * kStageBytes + 8192; };
+  auto issue = [&](int kt, int buf) {
+    copy16_to_lds(a_src + kt * BK, stage_a(buf) + (lmf * 2 + lks) * 1024);
+    char* lb = stage_b(buf) + wave * 2048;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) copy16_to_lds(b_src + (size_t)(2 * kt + c) * 1024, lb + c * 1024);
   };
-  Stage st[kAhead];
-  auto gload = [&](Stage& r, int kt) {
-    const int kk = kt * BK + lcol;
+  floatx16 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < MF; ++i) r.a[i] = avalid[i] ? ld16(arow[i] + kk) : u32x4{0u, 0u, 0u, 0u};
-    // cacheable: the other M-tiles of the group read the same chunks
+  for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) r.b[s] = ld16(wchunks + (size_t)(kt * (BK / 16) + s) * 1024);
-  };
-  auto astore = [&](const Stage& r, int buf) {
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int i = 0; i < MF; ++i)
-      *reinterpret_cast<u32x4*>(&sA[buf][(lrow + 32 * i) * LDS_LD + lcol]) = r.a[i];
-  };
-  const int live = (tl.rows + 31) / 32;  // activation fragments holding rows
-
-  floatx16 acc[MF];
-#pragma unroll
-  for (int j = 0; j < MF; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-
+      for (int r = 0; r < 16; ++r) acc[mf][nb][r] = 0.f;
   const int nk = K / BK;
 #pragma unroll
-  for (int s = 0; s < kAhead; ++s)
-    if (s < nk) gload(st[s], s);
-  astore(st[0], 0);
-  __syncthreads();
-  auto step = [&](Stage& mine, Stage& next, int kt) {
-    const int buf = kt & 1;
+  for (int s2 = 0; s2 < kStages - 1; ++s2)
+    if (s2 < nk) issue(s2, s2);
+  auto step = [&](int kt, int buf) {
+    // stages issued after kt: at most kStages - 2 = 1, of 3 copies each
+    if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+    // every wave has finished stage kt - 1, whose buffer is refilled now
+    if (kt + kStages - 1 < nk) issue(kt + kStages - 1, (buf + kStages - 1) % kStages);
+    const char* A = stage_a(buf);
+    const char* Bs = stage_b(buf);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&mine.b[ks]);
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 b[2];
 #pragma unroll
-      for (int j = 0; j < MF; ++j) {
-        if (j < live) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &sA[buf][(j * 32 + (lane & 31)) * LDS_LD + ks * 16 + 8 * (lane >> 5)]);
-          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
-        }
+      for (int nb = 0; nb < 2; ++nb)
+        b[nb] = *reinterpret_cast<const bf16x8*>(Bs + ((np * 2 + nb) * 2 + ks) * 1024 + lane * 16);
+#pragma unroll
+      for (int mf = 0; mf < 2; ++mf) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + ((mh * 2 + mf) * 2 + ks) * 1024 + lane * 16);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mf][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[nb], acc[mf][nb], 0, 0, 0);
       }
     }
-    if (kt + kAhead < nk) gload(mine, kt + kAhead);
-    if (kt + 1 < nk) astore(next, buf ^ 1);
-    __syncthreads();
   };
-  for (int kt = 0; kt < nk; kt += kAhead) {
+  for (int kt = 0; kt < nk; kt += kStages) {
 #pragma unroll
-    for (int s = 0; s < kAhead; ++s)
-      if (kt + s < nk) step(st[s], st[(s + 1) % kAhead], kt + s);
+    for (int j = 0; j < kStages; ++j)
+      if (kt + j < nk) step(kt + j, j);
   }
 
-  // epilogue: accumulator j covers rows 32 j .., weight row n of this lane
-  const int n = rb * 32 + (lane & 31);
+  // epilogue: accumulator (mf, nb) covers rows (mh*2 + mf)*32 .., weight row n of this lane
 #pragma unroll
-  for (int j = 0; j < MF; ++j) {
+  for (int mf = 0; mf < 2; ++mf) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = j * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const float v = acc[j][r];
-      if constexpr (PASS == 1) {
-        const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
-        if ((n & 1) == 0 && m < tl.rows && nvalid) {
-          uint16_t* h = static_cast<uint16_t*>(out) + (size_t)(tl.row_begin + m) * out_ld;
-          h[n >> 1] = f32_to_bf16_rne(silu(v) * u);
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = rbv[nb] * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = (mh * 2 + mf) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const float v = acc[mf][nb][r];
+        if constexpr (PASS == 1) {
+          const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
+          if ((n & 1) == 0 && m < tl.rows && nvalid[nb]) {
+            uint16_t* h = static_cast<uint16_t*>(out) + (size_t)(tl.row_begin + m) * out_ld;
+            h[n >> 1] = f32_to_bf16_rne(silu(v) * u);
+          }
+        } else {
+          if (m < tl.rows && nvalid[nb])
+            static_cast<float*>(out)[(size_t)(tl.row_begin + m) * out_ld + n] = v;
         }
-      } else {
-        if (m < tl.rows && nvalid)
-          static_cast<float*>(out)[(size_t)(tl.row_begin + m) * out_ld + n] = v;
       }
     }
   }
@@ -153,13 +160,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, const GemmTile* tiles,
                       const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
                       size_t off, int N, int K, int out_ld, void* out, hipStream_t s) {
-  const dim3 grid((N / 32 + 3) / 4, max_tiles);
+  const dim3 grid((N + BN - 1) / BN, max_tiles);
   if (pass == 1)
-    hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, dim3(256), 0, s,
+    hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, dim3(512), 0, s,
                        static_cast<const uint16_t*>(act), perm, k, tiles, n_tiles, pool, stride, off,
                        N, K, out_ld, out);
   else
-    hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, dim3(256), 0, s,
+    hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, dim3(512), 0, s,
                        static_cast<const uint16_t*>(act), perm, k, tiles, n_tiles, pool, stride, off,
                        N, K, out_ld, out);
 }
