@@ -109,37 +109,146 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 
 // -------------------------------------------------------- int8 MFMA GEMM ---
 // Tile: 128 activation rows (one GemmTile) x 256 weight rows (eight 32-row
-// blocks of the tile-major codes), K tiles of 128 values = one scale group.
-// 8 waves; wave w computes rows 64 (w & 1) .. +63 against weight blocks
-// 2 (w >> 1), +1: four v_mfma_i32_32x32x32_i8 accumulators.
+// blocks of the tile-major codes), K steps of 128 values = one scale group.
+// 8 waves; wave w owns weight block w of the tile and computes all 128 rows
+// against it: four v_mfma_i32_32x32x32_i8 accumulators (32-row blocks mf),
+// only the blocks that hold rows of the tile (a 40-row tile computes two).
 //
-// Operands reach LDS through asynchronous global -> LDS copies (16 bytes per
-// lane), in a ring of kQStages stages, so no register holds data in flight:
-//   A: 16 fragments of 1 KB per stage, fragment (mf, ks) holding row
-//      mf*32 + l%32, bytes ks*32 + 16 (l / 32) of the K tile at lane l
-//      (exactly the MFMA operand layout);
-//   B: the 16 code chunks of the tile's 8 weight blocks, as stored;
-//   scales: per wave, the aligned 32-bit word holding each lane's bf16 group
-//      scale (the slot's scale section is 256-byte aligned; the half is picked
-//      by the element index), kept out of registers: a register load would
-//      make the compiler drain every copy in flight before using it.
-// Each wave issues 6 copies per stage; before computing stage kt it waits
-// until only the later stages' copies are outstanding, then one barrier
-// publishes the stage to all waves. The int32 sums of a K tile are folded
-// into fp32 with the group scale / 16; the second fragment's tiles of group
-// kt are folded during group kt+1's first MFMAs.
-constexpr int QBM = kGemmBM;   // activation rows of a tile (128)
-constexpr int QBN = 256;       // weight rows of a tile
-constexpr int QBK = 128;       // one scale group per K tile
-constexpr int kQStages = 4;
-constexpr int kQStageBytes = 16384 + 16384 + 4096;  // A, B, scales
-static_assert(QBM == 128, "the 8-wave int8 tile covers 128 activation rows");
+// Per K step and wave:
+//   A: two 1 KB fragments of the step's 16 KB activation stage, copied to LDS
+//      asynchronously (16 bytes per lane); fragment (mf, ks) holds row
+//      mf*32 + l%32, bytes ks*32 + 16 (l / 32) at lane l, the MFMA operand
+//      layout; the eight waves' copies fill the stage, one barrier per step
+//      publishes it.
+//   B: the wave's own two 1 KB code chunks, straight into registers (no other
+//      wave reads them), expanded to int8 with two masks and a shift.
+//   scale: the aligned 32-bit word holding the lane's bf16 group scale.
+// Copies run kQAhead steps ahead: A in a ring of kQAhead + 1 LDS stages, B and
+// the scale word in registers. The int32 sums of a group are folded into fp32
+// (group scale / 16) just before the block's accumulator restarts on the next
+// group, so each fold overlaps the other blocks' MFMAs.
+constexpr int QBN = 256;          // weight rows of a tile
+constexpr int QBK = 128;          // one scale group per K step
+constexpr int kQAhead = 3;        // K steps of copies in flight
+constexpr int kQRing = kQAhead + 1;
+constexpr int kQStageBytes = kGemmBM * QBK;  // 16 KB of activations per step
+static_assert(kGemmBM == 128, "the 8-wave int8 tile covers 128 activation rows");
 
 template <int N_>
 __device__ __forceinline__ void vm_wait() {
-  if constexpr (N_ == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N_ == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  // s_waitcnt with only the vector-memory counter limited (N_ < 64)
+  __builtin_amdgcn_s_waitcnt((N_ & 15) | ((N_ >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+template <int PASS, int NMF>
+__device__ __forceinline__ void w4a8_tile(
+    int8_t* smem, const int8_t* __restrict__ aq, const float* __restrict__ as,
+    const int32_t* __restrict__ perm, int k, const GemmTile& tl, const char* __restrict__ slot,
+    size_t off_codes, size_t off_scales, int N, int K, int out_ld, float* __restrict__ out) {
+  constexpr int kOps = 5;  // copies per wave per K step: 2 A, 2 B, 1 scale word
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nrb = N / 32;
+  const int gld = K / 128;  // scale groups per weight row
+  const int nk = K / QBK;
+  const int lmf = wave >> 1, lks0 = (wave & 1) * 2;  // this wave's A fragments
+  const int8_t* a_src;
+  {
+    const int m = lmf * 32 + (lane & 31);
+    const int p = tl.row_begin + (m < tl.rows ? m : 0);  // rows past the tile read row 0
+    a_src = aq + (size_t)((PASS == 1) ? perm[p] / k : p) * K + lks0 * 32 + 16 * (lane >> 5);
+  }
+  int rb = blockIdx.x * (QBN / 32) + wave;
+  const bool nvalid = rb < nrb;
+  if (!nvalid) rb = nrb - 1;
+  const char* b_src = slot + off_codes + (size_t)rb * (K / 64) * 1024 + lane * 16;
+  const size_t se = (size_t)(rb * 32 + (lane & 31)) * gld;  // element index of group 0's scale
+  const uint32_t* s_src = reinterpret_cast<const uint32_t*>(slot + off_scales);
+
+  u32x4 bq[kQRing][2];
+  uint32_t sq[kQRing];
+  auto issue = [&](int kt, int buf) {
+    int8_t* la = smem + buf * kQStageBytes + (lmf * 4 + lks0) * 1024;
+    copy16_to_lds(a_src + kt * QBK, la);
+    copy16_to_lds(a_src + kt * QBK + 32, la + 1024);
+    bq[buf][0] = ld16(b_src + (size_t)(2 * kt) * 1024);
+    bq[buf][1] = ld16(b_src + (size_t)(2 * kt + 1) * 1024);
+    sq[buf] = s_src[(se + kt) >> 1];
+  };
+  const intx16 zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  intx16 acc[4];
+  float accf[4][16];
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf) {
+    acc[mf] = zero16;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accf[mf][r] = 0.f;
+  }
+  auto fold = [&](int mf, float sw) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accf[mf][r] = fmaf((float)acc[mf][r], sw, accf[mf][r]);
+  };
+#pragma unroll
+  for (int s2 = 0; s2 < kQAhead; ++s2)
+    if (s2 < nk) issue(s2, s2);
+  float sprev = 0.f;
+  auto step = [&](int kt, int j) {
+    // this wave's copies of step kt have landed once at most the later steps' are outstanding
+    const int after = nk - 1 - kt;
+    if (after >= 2) vm_wait<2 * kOps>(); else if (after == 1) vm_wait<kOps>(); else vm_wait<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's A copies of step kt; every wave is past step kt - 1
+    if (kt + kQAhead < nk) issue(kt + kQAhead, (j + kQAhead) % kQRing);
+    const int8_t* A = smem + j * kQStageBytes + lane * 16;
+    const uint32_t sb = ((se + kt) & 1) ? (sq[j] & 0xFFFF0000u) : (sq[j] << 16);
+    const float scur = __uint_as_float(sb) * 0.0625f;  // codes enter as 16 q
+    intx4 b[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4& cw = bq[j][ks >> 1];
+      const uint32_t w0 = (ks & 1) ? cw.z : cw.x, w1 = (ks & 1) ? cw.w : cw.y;
+      b[ks][0] = (int)((w0 << 4) & 0xF0F0F0F0u);
+      b[ks][1] = (int)(w0 & 0xF0F0F0F0u);
+      b[ks][2] = (int)((w1 << 4) & 0xF0F0F0F0u);
+      b[ks][3] = (int)(w1 & 0xF0F0F0F0u);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mf = 0; mf < NMF; ++mf) {
+        if (ks == 0 && kt > 0) fold(mf, sprev);  // group kt - 1, before the accumulator restarts
+        const intx4 a = *reinterpret_cast<const intx4*>(A + (mf * 4 + ks) * 1024);
+        acc[mf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[ks], ks == 0 ? zero16 : acc[mf], 0, 0, 0);
+      }
+    sprev = scur;
+  };
+  for (int kt0 = 0; kt0 < nk; kt0 += kQRing) {
+#pragma unroll
+    for (int j = 0; j < kQRing; ++j)
+      if (kt0 + j < nk) step(kt0 + j, j);
+  }
+#pragma unroll
+  for (int mf = 0; mf < NMF; ++mf) fold(mf, sprev);
+  const int n = rb * 32 + (lane & 31);
+#pragma unroll
+  for (int mf = 0; mf < NMF; ++mf) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = mf * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const bool ok = m < tl.rows;
+      const int p = tl.row_begin + (ok ? m : 0);
+      const float sx = as[(PASS == 1) ? perm[p] / k : p];
+      const float v = accf[mf][r] * sx;
+      if constexpr (PASS == 1) {
+        const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
+        if ((n & 1) == 0 && ok && nvalid) out[(size_t)p * out_ld + (n >> 1)] = silu(v) * u;
+      } else {
+        if (ok && nvalid) out[(size_t)p * out_ld + n] = v;
+      }
+    }
+  }
 }
 
 template <int PASS>
@@ -148,152 +257,18 @@ __global__ __launch_bounds__(512) void gemm_w4a8_kernel(
     const int32_t* __restrict__ perm, int k, const GemmTile* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const char* __restrict__ pool, size_t stride,
     size_t off_codes, size_t off_scales, int N, int K, int out_ld, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) int8_t smem[kQStages * kQStageBytes];
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kQRing * kQStageBytes];
   if ((int)blockIdx.y >= n_tiles[0]) return;
   const GemmTile tl = tiles[blockIdx.y];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mh = wave & 1, np = wave >> 1;
-  const int nrb = N / 32;
-  const int gld = K / 128;
   const char* slot = pool + (size_t)tl.slot * stride;
-  // copies of this wave per stage: A fragments (lmf, lks0), (lmf, lks0 + 1); B chunks of block
-  // `wave` of the tile; the scale words of its own two compute blocks
-  const int lmf = wave >> 1, lks0 = (wave & 1) * 2;
-  const int8_t* a_src;
-  {
-    const int m = lmf * 32 + (lane & 31);
-    const int p = tl.row_begin + (m < tl.rows ? m : 0);  // rows past the tile read row 0
-    a_src = aq + (size_t)((PASS == 1) ? perm[p] / k : p) * K + lks0 * 32 + 16 * (lane >> 5);
-  }
-  int lrb = blockIdx.x * (QBN / 32) + wave;
-  if (lrb >= nrb) lrb = nrb - 1;
-  const char* b_src = slot + off_codes + (size_t)lrb * (K / 64) * 1024 + lane * 16;
-  bool nvalid[2];
-  int rbv[2];
-  size_t se0[2];  // element index of this lane's scale row (row-major [N, K/128] bf16)
-  const uint32_t* scales32 = reinterpret_cast<const uint32_t*>(slot + off_scales);
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    int rb = blockIdx.x * (QBN / 32) + np * 2 + nb;
-    nvalid[nb] = rb < nrb;
-    if (!nvalid[nb]) rb = nrb - 1;
-    rbv[nb] = rb;
-    se0[nb] = (size_t)(rb * 32 + (lane & 31)) * gld;
-  }
-  auto stage_a = [&](int buf) { return smem + buf * kQStageBytes; };
-  auto stage_b = [&](int buf) { return smem + buf * kQStageBytes + 16384; };
-  auto stage_s = [&](int buf) { return smem + buf * kQStageBytes + 32768; };
-  auto issue = [&](int kt, int buf) {
-    int8_t* la = stage_a(buf) + (lmf * 4 + lks0) * 1024;
-    __builtin_amdgcn_global_load_lds(a_src + kt * QBK, la, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(a_src + kt * QBK + 32, la + 1024, 16, 0, 0);
-    int8_t* lb = stage_b(buf) + wave * 2048;
-    __builtin_amdgcn_global_load_lds(b_src + (size_t)(2 * kt) * 1024, lb, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(b_src + (size_t)(2 * kt + 1) * 1024, lb + 1024, 16, 0, 0);
-    int8_t* ls = stage_s(buf) + wave * 512;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      __builtin_amdgcn_global_load_lds(scales32 + ((se0[nb] + kt) >> 1), ls + nb * 256, 4, 0, 0);
-  };
-  // group kt's scale of compute block nb, as the bits of a float (the bf16 in the high half)
-  auto scale_bits = [&](int buf, int kt, int nb) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(stage_s(buf) + wave * 512 + nb * 256 + lane * 4);
-    return ((se0[nb] + kt) & 1) ? (w & 0xFFFF0000u) : (w << 16);
-  };
-  float accf[2][2][16];
-#pragma unroll
-  for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) accf[mf][nb][r] = 0.f;
-  intx16 acc[2][2];
-  const intx16 zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-  auto fold = [&](int mf, const uint32_t (&sb)[2]) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float sw = __uint_as_float(sb[nb]) * 0.0625f;  // codes enter as 16 q
-#pragma unroll
-      for (int r = 0; r < 16; ++r) accf[mf][nb][r] = fmaf((float)acc[mf][nb][r], sw, accf[mf][nb][r]);
-    }
-  };
-  const int nk = K / QBK;
-#pragma unroll
-  for (int s2 = 0; s2 < kQStages - 1; ++s2)
-    if (s2 < nk) issue(s2, s2);
-  auto step = [&](int kt, int buf) {
-    const int after = nk - 1 - kt;  // stages issued after kt, at most kQStages - 2
-    if (after >= 2) vm_wait<12>(); else if (after == 1) vm_wait<6>(); else vm_wait<0>();
-    asm volatile("s_barrier" ::: "memory");
-    const int pbuf = (buf + kQStages - 1) % kQStages;
-    uint32_t sprev[2] = {0u, 0u};
-    if (kt > 0) {
-      sprev[0] = scale_bits(pbuf, kt - 1, 0);
-      sprev[1] = scale_bits(pbuf, kt - 1, 1);
-    }
-    const uint32_t scur[2] = {scale_bits(buf, kt, 0), scale_bits(buf, kt, 1)};
-    // every wave has finished group kt - 1, so its stage can be refilled
-    if (kt + kQStages - 1 < nk) issue(kt + kQStages - 1, pbuf);
-    const int8_t* A = stage_a(buf);
-    const int8_t* Bs = stage_b(buf);
-    u32x4 bch[2][2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        bch[nb][c] = *reinterpret_cast<const u32x4*>(Bs + ((np * 2 + nb) * 2 + c) * 1024 + lane * 16);
-    if (kt > 0) fold(1, sprev);  // before this group overwrites those accumulators
-#pragma unroll
-    for (int mf = 0; mf < 2; ++mf) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const intx4 a = *reinterpret_cast<const intx4*>(A + ((mh * 2 + mf) * 4 + ks) * 1024 + lane * 16);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const u32x4& cw = bch[nb][ks >> 1];
-          const uint32_t w0 = (ks & 1) ? cw.z : cw.x, w1 = (ks & 1) ? cw.w : cw.y;
-          intx4 b;
-          b[0] = (int)((w0 << 4) & 0xF0F0F0F0u);
-          b[1] = (int)(w0 & 0xF0F0F0F0u);
-          b[2] = (int)((w1 << 4) & 0xF0F0F0F0u);
-          b[3] = (int)(w1 & 0xF0F0F0F0u);
-          acc[mf][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, ks == 0 ? zero16 : acc[mf][nb], 0, 0, 0);
-        }
-      }
-      if (mf == 0) fold(0, scur);  // overlaps the second fragment's MFMAs
-    }
-  };
-  for (int kt = 0; kt < nk; kt += kQStages) {
-#pragma unroll
-    for (int j = 0; j < kQStages; ++j)
-      if (kt + j < nk) step(kt + j, j);
-  }
-  {
-    const int lb = (nk - 1) % kQStages;
-    const uint32_t sl[2] = {scale_bits(lb, nk - 1, 0), scale_bits(lb, nk - 1, 1)};
-    fold(1, sl);
-  }
-#pragma unroll
-  for (int mf = 0; mf < 2; ++mf) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int n = rbv[nb] * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = (mh * 2 + mf) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const bool ok = m < tl.rows;
-        const int p = tl.row_begin + (ok ? m : 0);
-        const float sx = as[(PASS == 1) ? perm[p] / k : p];
-        const float v = accf[mf][nb][r] * sx;
-        if constexpr (PASS == 1) {
-          const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
-          if ((n & 1) == 0 && ok && nvalid[nb]) out[(size_t)p * out_ld + (n >> 1)] = silu(v) * u;
-        } else {
-          if (ok && nvalid[nb]) out[(size_t)p * out_ld + n] = v;
-        }
-      }
-    }
-  }
+  const int nmf = (tl.rows + 31) >> 5;  // 32-row blocks holding rows of the tile
+#define MOE_W4A8_TILE(M_) \
+  w4a8_tile<PASS, M_>(smem, aq, as, perm, k, tl, slot, off_codes, off_scales, N, K, out_ld, out)
+  if (nmf >= 4) MOE_W4A8_TILE(4);
+  else if (nmf == 3) MOE_W4A8_TILE(3);
+  else if (nmf == 2) MOE_W4A8_TILE(2);
+  else MOE_W4A8_TILE(1);
+#undef MOE_W4A8_TILE
 }
 
 template <int KS, int RBW, int MAXNT, bool SWIGLU>
