@@ -126,18 +126,26 @@ def timed(layer, shape, T, steps, warmup, label, ffn_timing=False):
 
 def recorded_traffic(key):
     """HBM bytes per FFN call (FETCH_SIZE + WRITE_SIZE runs, calibrated), as recorded in
-    profiles/ffn_traffic.json; None when absent or when any kernel source changed since."""
-    import glob
-    import hashlib
+    profiles/ffn_traffic.json; None when absent or when an FFN kernel source changed since."""
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "ffn_traffic.json")))[key]
     except (OSError, KeyError, ValueError):
         return None
+    return rec["read_bytes"] + rec["write_bytes"] if ffn_sources_sha1() == rec["csrc_sha1"] else None
+
+
+# the sources the expert-FFN kernels are compiled from (routing, runtime and combine excluded)
+FFN_SOURCES = ("common.h", "ffn_internal.h", "ffn.hip", "ffn_gemv.h", "tile_gemv.h", "gemm.hip",
+               "ffn_int4.hip")
+
+
+def ffn_sources_sha1() -> str:
+    import hashlib
     h = hashlib.sha1()
-    for f in sorted(glob.glob(os.path.join(ROOT, "expert_offload_routed_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
-    return rec["read_bytes"] + rec["write_bytes"] if h.hexdigest() == rec["csrc_sha1"] else None
+    for name in FFN_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(ROOT, "expert_offload_routed_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
 
 
 def all_resident(shape):
