@@ -18,7 +18,8 @@ Sources, cited by page title and section:
               misses = routed set minus cached set; only routed experts cached;
               LRU as the baseline replacement.
   [MoE-CORE]  MoE-CORE summary page (coordinated expert offload), Mechanism:
-              routed experts in a fixed-budget device cache.
+              routed experts in a fixed-budget device cache; eviction by a
+              routing-history score.
 
 Readings of points the pages leave open (each also listed in the design notes):
   * selection is on the logits (same set as on softmax probabilities), ties go
@@ -31,7 +32,10 @@ Readings of points the pages leave open (each also listed in the design notes):
     (Eq. (7) in [RapidMoE]; its Sec. 4.4 text is garbled on this point);
   * int4 weights are symmetric with one bf16 scale per 128 input values;
     int8 activations use one fp32 scale per row, absmax / 127;
-  * a term whose gate weight is exactly zero is skipped in the weighted sum.
+  * a term whose gate weight is exactly zero is skipped in the weighted sum;
+  * the routing score of an expert at a step is its softmax probability
+    averaged over the step's tokens; eviction scores are kept per layer and
+    compared across layers as they stand.
 """
 from __future__ import annotations
 
@@ -49,6 +53,7 @@ __all__ = [
     "permute", "silu", "swiglu_expert", "decode_int4", "dequant_int4g128",
     "quantize_rows_int8", "swiglu_expert_w4a8", "expert_forward", "combine",
     "SlotPool", "LruSlotPlanner", "Wave", "route", "moe_layer",
+    "step_scores", "MinusRecentScore", "RoutingHistoryScore", "ScoredSlotPlanner",
 ]
 
 
@@ -319,6 +324,8 @@ class LruSlotPlanner:
       its last use. The table keeps the state after the last wave.
     """
 
+    _victim_key = None  # ordering of the reusable slots; None = (last use, slot id)
+
     def __init__(self, num_slots: int, layers: int, E: int,
                  residency: list[tuple[int, int] | None] | None = None):
         if num_slots < 1:
@@ -347,8 +354,9 @@ class LruSlotPlanner:
         misses = [e for e in U if self.lut[layer, e] < 0]
         kept = {int(self.lut[layer, e]) for e in hits}
         empty = [s for s in range(self.S) if self.owner[s] is None]
+        key = self._victim_key or (lambda s: (self.last_use[s], s))
         reusable = sorted((s for s in range(self.S) if self.owner[s] is not None and s not in kept),
-                          key=lambda s: (self.last_use[s], s))
+                          key=key)
         victims = empty + reusable
         used = set(kept)
         waves: list[Wave] = []
@@ -369,6 +377,136 @@ class LruSlotPlanner:
         for s in used:
             self.last_use[s] = self.clock
         return waves
+
+
+# --------------------------------------------------------- eviction scores ---
+def step_scores(logits) -> np.ndarray:
+    """Routing score of every expert at one step: its softmax probability over
+    the step's tokens, averaged over the tokens ([RapidMoE] Sec. 2.1 softmax;
+    the averaging over a batch is the reading for T > 1). fp64."""
+    lg = as_f64(logits).reshape(-1, np.shape(logits)[-1])
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    return p.mean(axis=0)
+
+
+class MinusRecentScore:
+    """[HybriMoE] Mechanism, Minus Recent Score: the routing scores of an
+    expert over the recent steps of its layer are added up and the most recent
+    one is subtracted, so a single high score on the latest step does not
+    protect the expert. The lowest score is evicted first.
+
+    Readings: "recent steps" are the last `window` steps of the layer,
+    including the current one; the sum runs from the oldest to the newest step
+    in float64 and the newest score is then subtracted.
+    """
+
+    def __init__(self, layers: int, E: int, window: int):
+        if window < 1:
+            raise ValueError("window must be at least 1")
+        self.W = window
+        self.hist = [[] for _ in range(layers)]  # per layer: score vectors, oldest first
+
+    def observe(self, layer: int, scores, distinct) -> None:
+        h = self.hist[layer]
+        h.append([float(v) for v in np.asarray(scores, dtype=np.float32)])
+        if len(h) > self.W:
+            h.pop(0)
+
+    def keep(self, layer: int, expert: int) -> float:
+        h = self.hist[layer]
+        if not h:
+            return 0.0
+        total = 0.0
+        for row in h:
+            total += row[expert]
+        return total - h[-1][expert]
+
+
+class RoutingHistoryScore:
+    """[MoE-CORE] Mechanism, routing-history eviction score: four features of
+    an expert -- how often it was selected in a recent window, an exponential
+    moving average of its selections, its current routing score, and its age
+    since it was last selected -- each normalised across the experts of the
+    layer, combined with nonnegative weights. The lowest score is evicted first.
+
+    Readings: the window is the last `window` steps of the layer (the current
+    one included); the moving average is ema <- lam * ema + (1 - lam) * [selected]
+    over every step of the layer, starting at 0; the current score is the
+    routing score of the latest step; a feature is normalised by dividing by its
+    maximum over the layer (0 when that maximum is 0); age enters as freshness
+    1 - age / max_age (age = steps of the layer since the last selection, the
+    step count when never selected; freshness 1 when max_age is 0), so every
+    weight rewards keeping. keep = w_cnt*cnt + w_ema*ema + w_score*score +
+    w_fresh*fresh, summed in that order in float64.
+    """
+
+    def __init__(self, layers: int, E: int, window: int,
+                 weights=(1.0, 1.0, 1.0, 1.0), lam: float = 0.9):
+        if window < 1 or any(w < 0 for w in weights) or not 0.0 <= lam <= 1.0:
+            raise ValueError("bad routing-history parameters")
+        self.W, self.E = window, E
+        self.w = [float(v) for v in weights]
+        self.lam = float(lam)
+        self.steps = [0] * layers
+        self.sel = [[] for _ in range(layers)]        # per layer: selection sets, oldest first
+        self.ema = [[0.0] * E for _ in range(layers)]
+        self.score = [[0.0] * E for _ in range(layers)]
+        self.last = [[0] * E for _ in range(layers)]  # step of the last selection, 0 = never
+
+    def observe(self, layer: int, scores, distinct) -> None:
+        self.steps[layer] += 1
+        n = self.steps[layer]
+        chosen = {int(e) for e in distinct}
+        self.sel[layer].append(chosen)
+        if len(self.sel[layer]) > self.W:
+            self.sel[layer].pop(0)
+        sc = np.asarray(scores, dtype=np.float32)
+        for e in range(self.E):
+            hit = 1.0 if e in chosen else 0.0
+            self.ema[layer][e] = self.lam * self.ema[layer][e] + (1.0 - self.lam) * hit
+            self.score[layer][e] = float(sc[e])
+            if hit:
+                self.last[layer][e] = n
+
+    def _features(self, layer: int):
+        cnt = [float(sum(1 for s in self.sel[layer] if e in s)) for e in range(self.E)]
+        age = [float(self.steps[layer] - self.last[layer][e]) for e in range(self.E)]
+        return cnt, self.ema[layer], self.score[layer], age
+
+    def keep(self, layer: int, expert: int) -> float:
+        cnt, ema, score, age = self._features(layer)
+
+        def norm(f, e):
+            m = max(f)
+            return f[e] / m if m > 0.0 else 0.0
+
+        m_age = max(age)
+        fresh = 1.0 - age[expert] / m_age if m_age > 0.0 else 1.0
+        total = self.w[0] * norm(cnt, expert)
+        total += self.w[1] * norm(ema, expert)
+        total += self.w[2] * norm(score, expert)
+        total += self.w[3] * fresh
+        return total
+
+
+class ScoredSlotPlanner(LruSlotPlanner):
+    """The residency plan of LruSlotPlanner with the victims chosen by an
+    eviction score ([HybriMoE] Minus Recent Score, [MoE-CORE] routing-history
+    score): each call first records the step's routing scores, then the slots
+    not holding a hit are taken by (owner's score, last use, slot id)
+    ascending; empty slots still come first and everything else is unchanged.
+    """
+
+    def __init__(self, num_slots: int, layers: int, E: int, policy,
+                 residency: list[tuple[int, int] | None] | None = None):
+        super().__init__(num_slots, layers, E, residency)
+        self.policy = policy
+        self._victim_key = lambda s: (self.policy.keep(*self.owner[s]), self.last_use[s], s)
+
+    def plan(self, layer: int, distinct, scores=None) -> list[Wave]:
+        self.policy.observe(layer, scores, distinct)
+        return super().plan(layer, distinct)
 
 
 # ------------------------------------------------------------- full layer ---

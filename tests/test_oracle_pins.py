@@ -333,3 +333,117 @@ def test_planner_invariants_random_multilayer():
             assert p.owner[s] == own.get(s)
         if len(U) <= S:
             assert all(p.lut[layer, e] >= 0 for e in U)
+
+
+# ----------------------------------------------------- eviction scores ---
+def _trace(rng, L, E, k, steps):
+    out = []
+    for step in range(steps):
+        layer = step % L
+        T = int(rng.integers(1, 4))
+        logits = rng.normal(size=(T, E))
+        ids = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+        out.append((layer, sorted({int(e) for e in ids.ravel()}), logits))
+    return out
+
+
+def test_step_scores_is_mean_softmax():
+    lg = np.array([[0.0, 1.0, -2.0], [3.0, 3.0, 0.5]])
+    want = scipy.special.softmax(lg, axis=1).mean(axis=0)
+    np.testing.assert_allclose(O.step_scores(lg), want, rtol=1e-15)
+    assert O.step_scores(lg).sum() == pytest.approx(1.0, abs=1e-15)
+
+
+@pytest.mark.parametrize("policy", ["mrs_w1", "fresh_only"])
+def test_scored_planner_reduces_to_lru(policy):
+    # MRS over a window of one step is 0 for every expert, and the routing-history
+    # score with only the freshness weight orders a single layer by last selection:
+    # both leave the (last use, slot id) order of plain LRU.
+    rng = np.random.default_rng(21)
+    L, E, S, k = (3 if policy == "mrs_w1" else 1), 9, 5, 2
+    pol = (O.MinusRecentScore(L, E, 1) if policy == "mrs_w1"
+           else O.RoutingHistoryScore(L, E, 4, weights=(0.0, 0.0, 0.0, 1.0), lam=0.5))
+    a = O.ScoredSlotPlanner(S, L, E, pol)
+    b = O.LruSlotPlanner(S, L, E)
+    for layer, U, logits in _trace(rng, L, E, k, 300):
+        wa = a.plan(layer, U, O.step_scores(logits))
+        wb = b.plan(layer, U)
+        assert [(w.compute, w.fills) for w in wa] == [(w.compute, w.fills) for w in wb]
+        assert np.array_equal(a.lut, b.lut)
+
+
+def test_mrs_hand_trace():
+    # 2 slots holding experts 0 and 1; window of 3 steps.
+    p = O.ScoredSlotPlanner(2, 1, 3, O.MinusRecentScore(1, 3, 3), residency=[(0, 0), (0, 1)])
+    assert p.plan(0, [0], [0.6, 0.1, 0.3])[0].fills == []
+    assert p.plan(0, [1], [0.5, 0.4, 0.1])[0].fills == []
+    # miss 2: MRS(0) = 0.6+0.5+0.2-0.2 = 1.1, MRS(1) = 0.1+0.4+0.1-0.1 = 0.5 -> slot 1 goes
+    # (plain LRU would take slot 0: expert 0 was last used one step earlier than expert 1)
+    assert p.plan(0, [2], [0.2, 0.1, 0.7])[0].fills == [(2, 1)]
+    # miss 1: window is now steps 2..4: MRS(0) = 0.5+0.2+0.1-0.1 = 0.7, MRS(2) = 0.1+0.7+0.1-0.1 = 0.8
+    assert p.plan(0, [1], [0.1, 0.8, 0.1])[0].fills == [(1, 0)]
+    assert p.lut[0].tolist() == [-1, 0, 1]
+
+
+def test_history_count_only_hand_trace():
+    # count over a 4-step window: expert 0 was picked twice, expert 1 once but later
+    def run(planner):
+        fills = []
+        for U in ([0], [0], [1], [2]):
+            fills.append(planner.plan(0, U, [1 / 3] * 3)[0].fills if isinstance(planner, O.ScoredSlotPlanner)
+                         else planner.plan(0, U)[0].fills)
+        return fills
+    scored = O.ScoredSlotPlanner(2, 1, 3, O.RoutingHistoryScore(1, 3, 4, weights=(1.0, 0.0, 0.0, 0.0)),
+                                 residency=[(0, 0), (0, 1)])
+    lru = O.LruSlotPlanner(2, 1, 3, residency=[(0, 0), (0, 1)])
+    assert run(scored)[-1] == [(2, 1)]   # the less often picked expert 1 goes
+    assert run(lru)[-1] == [(2, 0)]      # LRU drops the older expert 0
+
+
+def test_history_ema_closed_form():
+    lam, E = 0.8, 4
+    pol = O.RoutingHistoryScore(1, E, 3, lam=lam)
+    picks = [[0, 2], [1], [0], [], [0, 3], [2]]
+    for U in picks:
+        pol.observe(0, np.full(E, 0.25), U)
+    n = len(picks)
+    for e in range(E):
+        want = sum((1 - lam) * lam ** (n - 1 - i) for i, U in enumerate(picks) if e in U)
+        assert pol.ema[0][e] == pytest.approx(want, rel=1e-14, abs=1e-15)
+    # age since last selection and the window count, by hand
+    assert [n - pol.last[0][e] for e in range(E)] == [1, 4, 0, 1]
+    cnt, _, _, age = pol._features(0)
+    assert cnt == [1.0, 0.0, 1.0, 1.0] and age == [1.0, 4.0, 0.0, 1.0]
+
+
+@pytest.mark.parametrize("policy", ["mrs", "history"])
+def test_scored_plans_invariant_under_power_of_two_score_scale(policy):
+    rng = np.random.default_rng(22)
+    L, E, S, k = 2, 8, 5, 2
+    mk = (lambda: O.MinusRecentScore(L, E, 5)) if policy == "mrs" else \
+        (lambda: O.RoutingHistoryScore(L, E, 5, weights=(0.5, 1.0, 2.0, 0.25), lam=0.75))
+    a, b = O.ScoredSlotPlanner(S, L, E, mk()), O.ScoredSlotPlanner(S, L, E, mk())
+    for layer, U, logits in _trace(rng, L, E, k, 200):
+        sc = O.step_scores(logits).astype(np.float32)
+        wa, wb = a.plan(layer, U, sc), b.plan(layer, U, sc * np.float32(4.0))
+        assert [(w.compute, w.fills) for w in wa] == [(w.compute, w.fills) for w in wb]
+
+
+def test_scored_planner_invariants_random_multilayer():
+    rng = np.random.default_rng(23)
+    L, E, S, k = 3, 10, 7, 3
+    p = O.ScoredSlotPlanner(S, L, E, O.RoutingHistoryScore(L, E, 6))
+    for layer, U, logits in _trace(rng, L, E, k, 300):
+        lut_before = p.lut.copy()
+        hits = [e for e in U if lut_before[layer, e] >= 0]
+        waves = p.plan(layer, U, O.step_scores(logits))
+        assert sorted(e for wv in waves for e in wv.compute) == U
+        fills = [f for wv in waves for f in wv.fills]
+        assert sorted(e for e, _ in fills) == sorted(set(U) - set(hits))
+        kept = {int(lut_before[layer, e]) for e in hits}
+        assert not kept & {s for _, s in waves[0].fills}
+        for s in range(S):
+            o = p.owner[s]
+            assert o is None or p.lut[o] == s
+        if len(U) <= S:
+            assert all(p.lut[layer, e] >= 0 for e in U)
