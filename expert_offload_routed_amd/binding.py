@@ -37,6 +37,10 @@ _SIGNATURES = {
     "slot_commit": (_i32, [_vp, _i32, _vp, _i32, _vp, _u64, _vp, _vp]),
     "moe_plan_fills": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp]),
+    "moe_policy_state_doubles": (_sz, [_i32, _i32, _i32, _i32]),
+    "moe_policy_observe": (_i32, [_i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
+    "moe_plan_fills_policy": (_i32, [_i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                     _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_version": (ctypes.c_char_p, []),
     "moe_ctx_workspace_bytes": (_sz, [_i32] * 7),
     "moe_ctx_create": (_i32, [ctypes.POINTER(_vp)] + [_i32] * 10 + [_vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -266,6 +270,10 @@ def slot_commit(lut, lut_index: int, owner, slot: int, slot_tags, tag: int, err_
 def moe_plan_fills(lut: np.ndarray, owner: np.ndarray, last_use: np.ndarray, clock: np.ndarray,
                    S: int, L: int, E: int, layer: int, distinct: np.ndarray) -> dict:
     """Run the host LRU plan on numpy state arrays (updated in place)."""
+    return _plan(None, lut, owner, last_use, clock, S, L, E, layer, distinct)
+
+
+def _plan(policy, lut, owner, last_use, clock, S, L, E, layer, distinct) -> dict:
     assert lut.dtype == np.int32 and owner.dtype == np.int32
     assert last_use.dtype == np.int64 and clock.dtype == np.int64
     d = np.ascontiguousarray(distinct, dtype=np.int32)
@@ -274,12 +282,42 @@ def moe_plan_fills(lut: np.ndarray, owner: np.ndarray, last_use: np.ndarray, clo
     is_hit = np.empty(E, np.int32)
     fe, fs, fw = (np.empty(max(n, 1), np.int32) for _ in range(3))
     nf, nw = np.zeros(1, np.int32), np.zeros(1, np.int32)
-    _call("moe_plan_fills", _host(lut), _host(owner), _host(last_use), _host(clock), S, L, E, layer,
-          _host(d) if n else None, n, _host(wave_of), _host(is_hit), _host(fe), _host(fs), _host(fw),
-          _host(nf), _host(nw))
+    tail = (_host(lut), _host(owner), _host(last_use), _host(clock), S, L, E, layer,
+            _host(d) if n else None, n, _host(wave_of), _host(is_hit), _host(fe), _host(fs), _host(fw),
+            _host(nf), _host(nw))
+    if policy is None:
+        _call("moe_plan_fills", *tail)
+    else:
+        _call("moe_plan_fills_policy", policy.kind, _host(policy.state), policy.window,
+              _host(policy.params) if policy.params is not None else None, *tail)
     k = int(nf[0])
     return dict(wave_of=wave_of, is_hit=is_hit, fill_expert=fe[:k].copy(), fill_slot=fs[:k].copy(),
                 fill_wave=fw[:k].copy(), n_waves=int(nw[0]))
+
+
+MOE_POLICY_LRU, MOE_POLICY_MRS, MOE_POLICY_HISTORY = 0, 1, 2
+
+
+class EvictionPolicy:
+    """Host state of an eviction policy (moe_policy_* in include/moe_offload.h)."""
+
+    def __init__(self, kind: int, L: int, E: int, window: int = 1, params=None):
+        self.kind, self.L, self.E, self.window = kind, L, E, window
+        self.params = None if params is None else np.ascontiguousarray(params, dtype=np.float64)
+        n = int(lib().moe_policy_state_doubles(kind, L, E, window))
+        if kind != MOE_POLICY_LRU and n == 0:
+            raise MoeError("moe_policy_state_doubles", -1)
+        self.state = np.zeros(max(n, 1), np.float64)
+
+    def observe(self, layer: int, scores: np.ndarray, distinct: np.ndarray) -> None:
+        sc = np.ascontiguousarray(scores, dtype=np.float32)
+        d = np.ascontiguousarray(distinct, dtype=np.int32)
+        _call("moe_policy_observe", self.kind, _host(self.state), self.L, self.E, self.window, layer,
+              _host(sc), _host(d) if d.size else None, d.size,
+              _host(self.params) if self.params is not None else None)
+
+    def plan(self, lut, owner, last_use, clock, S: int, layer: int, distinct) -> dict:
+        return _plan(self, lut, owner, last_use, clock, S, self.L, self.E, layer, distinct)
 
 
 def moe_version() -> str:

@@ -213,15 +213,110 @@ extern "C" int slot_fill(void* pool_base, size_t slot_stride, int32_t slot, cons
 }
 
 // ------------------------------------------------------- host LRU planning --
-extern "C" int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock,
-                              int S, int L, int E, int layer, const int32_t* distinct,
-                              int n_distinct, int32_t* wave_of, int32_t* is_hit,
-                              int32_t* fill_expert, int32_t* fill_slot, int32_t* fill_wave,
-                              int32_t* n_fills, int32_t* n_waves) {
+// ------------------------------------------------------- eviction scores --
+// Host state of an eviction policy, per layer (doubles):
+//   MRS:     [observed steps, ring of the last W score vectors (W x E)]
+//   HISTORY: [observed steps, ring of the last W selection vectors (W x E, 0/1),
+//             ema (E), latest score (E), step of the last selection (E, 0 = never)]
+// All arithmetic is float64 in a fixed order without contraction, so the
+// victim order is reproducible bit for bit.
+namespace {
+
+size_t policy_layer_doubles(int policy, int E, int W) {
+  if (policy == MOE_POLICY_MRS) return 1 + (size_t)W * E;
+  if (policy == MOE_POLICY_HISTORY) return 1 + (size_t)W * E + 3 * (size_t)E;
+  return 0;
+}
+
+#pragma clang fp contract(off)
+
+// Minus Recent Score (HybriMoE summary page, Mechanism): the expert's routing
+// scores over the last W steps of its layer, summed oldest to newest, minus the
+// newest one.
+double mrs_keep(const double* st, int E, int W, int e) {
+  const long n = (long)st[0];
+  if (n == 0) return 0.0;
+  const long m = n < W ? n : W;
+  const double* ring = st + 1;
+  double total = 0.0;
+  for (long i = n - m; i < n; ++i) total += ring[(size_t)(i % W) * E + e];
+  return total - ring[(size_t)((n - 1) % W) * E + e];
+}
+
+// Routing-history score (MoE-CORE summary page, Mechanism): window count, EMA
+// of selections, latest score and freshness (1 - age / max age), each divided
+// by its maximum over the layer, weighted by w[0..3].
+struct HistoryNorm {
+  double m_cnt, m_ema, m_score, m_age;
+};
+
+double history_count(const double* st, int E, int W, int e) {
+  const long n = (long)st[0];
+  const long m = n < W ? n : W;
+  const double* ring = st + 1;
+  double c = 0.0;
+  for (long i = n - m; i < n; ++i) c += ring[(size_t)(i % W) * E + e];
+  return c;
+}
+
+HistoryNorm history_norm(const double* st, int E, int W) {
+  const double* ema = st + 1 + (size_t)W * E;
+  const double* score = ema + E;
+  const double* last = score + E;
+  HistoryNorm h{0.0, 0.0, 0.0, 0.0};
+  for (int e = 0; e < E; ++e) {
+    h.m_cnt = std::max(h.m_cnt, history_count(st, E, W, e));
+    h.m_ema = std::max(h.m_ema, ema[e]);
+    h.m_score = std::max(h.m_score, score[e]);
+    h.m_age = std::max(h.m_age, st[0] - last[e]);
+  }
+  return h;
+}
+
+double history_keep(const double* st, int E, int W, const double* w, const HistoryNorm& h, int e) {
+  const double* ema = st + 1 + (size_t)W * E;
+  const double* score = ema + E;
+  const double* last = score + E;
+  const double cnt = history_count(st, E, W, e);
+  const double age = st[0] - last[e];
+  const double n_cnt = h.m_cnt > 0.0 ? cnt / h.m_cnt : 0.0;
+  const double n_ema = h.m_ema > 0.0 ? ema[e] / h.m_ema : 0.0;
+  const double n_score = h.m_score > 0.0 ? score[e] / h.m_score : 0.0;
+  const double fresh = h.m_age > 0.0 ? 1.0 - age / h.m_age : 1.0;
+  double total = w[0] * n_cnt;
+  total += w[1] * n_ema;
+  total += w[2] * n_score;
+  total += w[3] * fresh;
+  return total;
+}
+
+#pragma clang fp contract(on)
+
+bool policy_args_ok(int policy, const double* state, int W, const double* params) {
+  if (policy == MOE_POLICY_LRU) return true;
+  if (policy != MOE_POLICY_MRS && policy != MOE_POLICY_HISTORY) return false;
+  if (!state || W < 1) return false;
+  if (policy == MOE_POLICY_HISTORY) {
+    if (!params) return false;
+    for (int i = 0; i < 4; ++i)
+      if (!(params[i] >= 0.0)) return false;
+    if (!(params[4] >= 0.0 && params[4] <= 1.0)) return false;
+  }
+  return true;
+}
+
+// The plan of moe_plan_fills with the reusable slots ordered by keep[slot]
+// first when keep is given.
+int plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock, int S, int L,
+               int E, int layer, const int32_t* distinct, int n_distinct, int32_t* wave_of,
+               int32_t* is_hit, int32_t* fill_expert, int32_t* fill_slot, int32_t* fill_wave,
+               int32_t* n_fills, int32_t* n_waves, int policy, const double* state, int W,
+               const double* params) {
   MOE_CHECK_ARG(lut && owner && last_use && clock && wave_of && is_hit && n_fills && n_waves);
   MOE_CHECK_ARG(S >= 1 && L >= 1 && E >= 1 && layer >= 0 && layer < L);
   MOE_CHECK_ARG(n_distinct >= 0 && n_distinct <= E);
   MOE_CHECK_ARG(n_distinct == 0 || (distinct && fill_expert && fill_slot && fill_wave));
+  MOE_CHECK_ARG(policy_args_ok(policy, state, W, params));
   // The routed set must be strictly ascending ids in range.
   for (int i = 0; i < n_distinct; ++i) {
     if (distinct[i] < 0 || distinct[i] >= E) return MOE_EINVAL;
@@ -245,7 +340,8 @@ extern "C" int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, i
     }
   }
   // Victims (only when something misses): empty slots by id, then the other
-  // slots by (last use, id); only as many as the misses need are ordered.
+  // slots by (owner's keep score, last use, id); only as many as the misses
+  // need are ordered.
   std::vector<int> victims, used;
   if (!misses.empty()) {
     for (int s = 0; s < S; ++s)
@@ -254,11 +350,36 @@ extern "C" int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, i
     for (int s = 0; s < S; ++s)
       if (owner[s] >= 0 && !kept[s]) reuse.push_back(s);
     const size_t need = misses.size() > victims.size() ? misses.size() - victims.size() : 0;
-    auto older = [&](int a, int b) {
+    std::vector<double> keep;
+    if (policy != MOE_POLICY_LRU && need > 0) {
+      keep.assign(S, 0.0);
+      const size_t per = policy_layer_doubles(policy, E, W);
+      std::vector<HistoryNorm> norm;
+      std::vector<char> have;
+      if (policy == MOE_POLICY_HISTORY) {
+        norm.resize(L);
+        have.assign(L, 0);
+      }
+      for (int s : reuse) {
+        const int l = owner[s] / E, e = owner[s] % E;
+        const double* st = state + (size_t)l * per;
+        if (policy == MOE_POLICY_MRS) {
+          keep[s] = mrs_keep(st, E, W, e);
+        } else {
+          if (!have[l]) {
+            norm[l] = history_norm(st, E, W);
+            have[l] = 1;
+          }
+          keep[s] = history_keep(st, E, W, params, norm[l], e);
+        }
+      }
+    }
+    auto first = [&](int a, int b) {
+      if (!keep.empty() && keep[a] != keep[b]) return keep[a] < keep[b];
       return last_use[a] < last_use[b] || (last_use[a] == last_use[b] && a < b);
     };
     const size_t take = need < reuse.size() ? need : reuse.size();
-    std::partial_sort(reuse.begin(), reuse.begin() + take, reuse.end(), older);
+    std::partial_sort(reuse.begin(), reuse.begin() + take, reuse.end(), first);
     victims.insert(victims.end(), reuse.begin(), reuse.begin() + take);
   }
 
@@ -283,10 +404,10 @@ extern "C" int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, i
   if (misses.size() <= victims.size()) {
     for (size_t i = 0; i < misses.size(); ++i) assign(misses[i], victims[i], 0);
   } else {
-    const size_t first = victims.size();
-    for (size_t i = 0; i < first; ++i) assign(misses[i], victims[i], 0);
+    const size_t first_n = victims.size();
+    for (size_t i = 0; i < first_n; ++i) assign(misses[i], victims[i], 0);
     int wave = 1;
-    for (size_t i = first; i < misses.size(); i += S, ++wave) {
+    for (size_t i = first_n; i < misses.size(); i += S, ++wave) {
       for (size_t j = i; j < misses.size() && j < i + S; ++j) assign(misses[j], (int)(j - i), wave);
       nw = wave + 1;
     }
@@ -296,5 +417,69 @@ extern "C" int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, i
   *n_waves = (n_distinct == 0) ? 0 : nw;
   return MOE_OK;
 }
+
+}  // namespace
+
+extern "C" int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock,
+                              int S, int L, int E, int layer, const int32_t* distinct,
+                              int n_distinct, int32_t* wave_of, int32_t* is_hit,
+                              int32_t* fill_expert, int32_t* fill_slot, int32_t* fill_wave,
+                              int32_t* n_fills, int32_t* n_waves) {
+  return plan_fills(lut, owner, last_use, clock, S, L, E, layer, distinct, n_distinct, wave_of,
+                    is_hit, fill_expert, fill_slot, fill_wave, n_fills, n_waves, MOE_POLICY_LRU,
+                    nullptr, 0, nullptr);
+}
+
+extern "C" int moe_plan_fills_policy(int policy, const double* state, int window,
+                                     const double* params, int32_t* lut, int32_t* owner,
+                                     int64_t* last_use, int64_t* clock, int S, int L, int E,
+                                     int layer, const int32_t* distinct, int n_distinct,
+                                     int32_t* wave_of, int32_t* is_hit, int32_t* fill_expert,
+                                     int32_t* fill_slot, int32_t* fill_wave, int32_t* n_fills,
+                                     int32_t* n_waves) {
+  return plan_fills(lut, owner, last_use, clock, S, L, E, layer, distinct, n_distinct, wave_of,
+                    is_hit, fill_expert, fill_slot, fill_wave, n_fills, n_waves, policy, state,
+                    window, params);
+}
+
+extern "C" size_t moe_policy_state_doubles(int policy, int L, int E, int window) {
+  if (L < 1 || E < 1 || window < 1) return 0;
+  return (size_t)L * policy_layer_doubles(policy, E, window);
+}
+
+#pragma clang fp contract(off)
+extern "C" int moe_policy_observe(int policy, double* state, int L, int E, int window, int layer,
+                                  const float* scores, const int32_t* distinct, int n_distinct,
+                                  const double* params) {
+  MOE_CHECK_ARG(L >= 1 && E >= 1 && layer >= 0 && layer < L);
+  MOE_CHECK_ARG(policy_args_ok(policy, state, window, params));
+  MOE_CHECK_ARG(n_distinct >= 0 && n_distinct <= E && (n_distinct == 0 || distinct));
+  if (policy == MOE_POLICY_LRU) return MOE_OK;
+  MOE_CHECK_ARG(scores);
+  for (int i = 0; i < n_distinct; ++i)
+    if (distinct[i] < 0 || distinct[i] >= E) return MOE_EINVAL;
+  const int W = window;
+  double* st = state + (size_t)layer * policy_layer_doubles(policy, E, W);
+  const long n = (long)st[0];  // steps observed before this one
+  double* ring = st + 1 + (size_t)(n % W) * E;
+  if (policy == MOE_POLICY_MRS) {
+    for (int e = 0; e < E; ++e) ring[e] = (double)scores[e];
+  } else {
+    double* ema = st + 1 + (size_t)W * E;
+    double* score = ema + E;
+    double* last = score + E;
+    for (int e = 0; e < E; ++e) ring[e] = 0.0;
+    for (int i = 0; i < n_distinct; ++i) ring[distinct[i]] = 1.0;
+    const double lam = params[4];
+    for (int e = 0; e < E; ++e) {
+      ema[e] = lam * ema[e] + (1.0 - lam) * ring[e];
+      score[e] = (double)scores[e];
+      if (ring[e] != 0.0) last[e] = (double)(n + 1);
+    }
+  }
+  st[0] = (double)(n + 1);
+  return MOE_OK;
+}
+#pragma clang fp contract(on)
 
 extern "C" const char* moe_version(void) { return MOE_VERSION_STRING; }

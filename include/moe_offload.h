@@ -263,6 +263,56 @@ int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clo
                    int32_t* fill_expert, int32_t* fill_slot, int32_t* fill_wave,
                    int32_t* n_fills, int32_t* n_waves);
 
+/* ----------------------------------------------- eviction policies (host) -
+ * Which cached expert to evict when a miss needs a slot. LRU is the plan of
+ * moe_plan_fills. Two scores from the pages replace its victim order:
+ *   MOE_POLICY_MRS: Minus Recent Score (HybriMoE summary page, Mechanism): the
+ *     expert's routing scores over the last `window` steps of its layer (the
+ *     current one included), summed oldest to newest, minus the newest one.
+ *   MOE_POLICY_HISTORY: routing-history score (MoE-CORE summary page,
+ *     Mechanism): params = {w_cnt, w_ema, w_score, w_fresh, lambda}, weights
+ *     >= 0, 0 <= lambda <= 1. Features of expert e of a layer: cnt = times
+ *     selected in the last `window` steps; ema <- lambda*ema + (1-lambda)*[selected]
+ *     every step (from 0); score = its latest routing score; age = steps since
+ *     its last selection (the step count if never). Each of cnt, ema, score is
+ *     divided by its maximum over the layer's E experts (0 if that maximum is
+ *     0); fresh = 1 - age / max age (1 if max age is 0). keep = w_cnt*cnt +
+ *     w_ema*ema + w_score*score + w_fresh*fresh, summed in that order.
+ * A routing score is the expert's softmax probability averaged over the
+ * step's tokens (float). All policy arithmetic is float64 in the order given,
+ * without contraction.
+ */
+#define MOE_POLICY_LRU 0
+#define MOE_POLICY_MRS 1
+#define MOE_POLICY_HISTORY 2
+
+/* Doubles of policy state for L layers of E experts (0 for LRU or bad sizes).
+ * The caller zero-fills it once; the layout is internal. */
+size_t moe_policy_state_doubles(int policy, int L, int E, int window);
+
+/* Record one step of `layer` into the policy state: scores [E] (host floats,
+ * the step's routing scores) and the routed set distinct[0..n_distinct). A
+ * no-op for LRU (state, scores may be NULL). Call it once per layer step,
+ * before moe_plan_fills_policy for that step. Returns MOE_EINVAL for bad
+ * sizes, ids or parameters (state untouched). */
+int moe_policy_observe(int policy, double* state, int L, int E, int window, int layer,
+                       const float* scores, const int32_t* distinct, int n_distinct,
+                       const double* params);
+
+/* moe_plan_fills with the slots not holding a hit ordered by (owner's keep
+ * score under `policy`, last use, slot id) ascending: the lowest score is
+ * evicted first; empty slots still come first. Policy LRU gives exactly
+ * moe_plan_fills. state/window/params as for moe_policy_observe (not
+ * modified); the other arguments, state updates and errors as
+ * moe_plan_fills. */
+int moe_plan_fills_policy(int policy, const double* state, int window, const double* params,
+                          int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock,
+                          int S, int L, int E, int layer,
+                          const int32_t* distinct, int n_distinct,
+                          int32_t* wave_of, int32_t* is_hit,
+                          int32_t* fill_expert, int32_t* fill_slot, int32_t* fill_wave,
+                          int32_t* n_fills, int32_t* n_waves);
+
 /* Library version string and the gfx target it was built for (host). */
 const char* moe_version(void);
 

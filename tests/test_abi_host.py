@@ -161,3 +161,72 @@ def test_plan_fills_rejects_unsorted_or_out_of_range(lib):
         with pytest.raises(B.MoeError):
             B.moe_plan_fills(lut, owner, last_use, clock, 2, 1, 4, 0, np.array(bad))
     assert lut.tolist() == [-1] * 4 and int(clock[0]) == 0
+
+
+def _policy_pair(kind, L, E, rng):
+    W = int(rng.integers(1, 6))
+    if kind == "mrs":
+        return O.MinusRecentScore(L, E, W), B.EvictionPolicy(B.MOE_POLICY_MRS, L, E, W)
+    w = [float(v) for v in rng.choice([0.0, 0.25, 0.5, 1.0, 2.0, 3.0], size=4)]
+    lam = float(rng.choice([0.0, 0.5, 0.9, 0.95, 1.0]))
+    return (O.RoutingHistoryScore(L, E, W, weights=w, lam=lam),
+            B.EvictionPolicy(B.MOE_POLICY_HISTORY, L, E, W, params=w + [lam]))
+
+
+@pytest.mark.parametrize("kind", ["mrs", "history"])
+@pytest.mark.parametrize("S,L,E,kmax,seed", [(4, 1, 8, 2, 0), (3, 2, 6, 4, 1), (16, 1, 64, 6, 2),
+                                             (7, 3, 10, 3, 3), (1, 1, 5, 2, 4), (40, 4, 32, 6, 5)])
+def test_policy_plans_match_oracle(lib, kind, S, L, E, kmax, seed):
+    rng = np.random.default_rng(100 + seed)
+    init = [(int(rng.integers(L)), int(e)) for e in rng.choice(E, size=min(S, E) - 1, replace=False)]
+    residency = (list(dict.fromkeys(init)) + [None] * S)[:S]
+    pol_ref, pol = _policy_pair(kind, L, E, rng)
+    ref = O.ScoredSlotPlanner(S, L, E, pol_ref, residency)
+    lut, owner, last_use, clock = _lib_state(S, L, E, residency)
+    for step in range(150):
+        layer = int(rng.integers(L))
+        logits = rng.normal(size=(int(rng.integers(1, 4)), E)) * 2.0
+        if step % 7 == 0:
+            logits[:, :E // 2] = logits[:, :1]  # ties in the scores
+        ids = np.argsort(-logits, axis=1, kind="stable")[:, :int(rng.integers(1, kmax + 1))]
+        U = sorted({int(e) for e in ids.ravel()})
+        scores = O.step_scores(logits).astype(np.float32)
+        waves = ref.plan(layer, U, scores)
+        pol.observe(layer, scores, np.array(U))
+        got = pol.plan(lut, owner, last_use, clock, S, layer, np.array(U))
+        exp_fills = [(e, s, wi) for wi, wv in enumerate(waves) for e, s in wv.fills]
+        assert list(zip(got["fill_expert"], got["fill_slot"], got["fill_wave"])) == exp_fills, step
+        assert got["n_waves"] == len(waves)
+        assert lut.reshape(L, E).tolist() == ref.lut.tolist()
+        assert last_use.tolist() == ref.last_use and int(clock[0]) == ref.clock
+
+
+def test_policy_lru_kind_equals_plain_plan(lib):
+    rng = np.random.default_rng(7)
+    S, L, E = 5, 2, 12
+    a = _lib_state(S, L, E, [None] * S)
+    b = _lib_state(S, L, E, [None] * S)
+    pol = B.EvictionPolicy(B.MOE_POLICY_LRU, L, E)
+    for step in range(100):
+        layer = step % L
+        U = np.array(sorted({int(e) for e in rng.choice(E, size=4)}))
+        ga = B.moe_plan_fills(*a, S, L, E, layer, U)
+        pol.observe(layer, np.zeros(E, np.float32), U)
+        gb = pol.plan(*b, S, layer, U)
+        assert ga["fill_slot"].tolist() == gb["fill_slot"].tolist()
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_policy_rejects_bad_parameters(lib):
+    with pytest.raises(B.MoeError):
+        B.EvictionPolicy(B.MOE_POLICY_MRS, 1, 4, 0)
+    pol = B.EvictionPolicy(B.MOE_POLICY_HISTORY, 1, 4, 2, params=[1.0, -1.0, 0.0, 0.0, 0.5])
+    with pytest.raises(B.MoeError):
+        pol.observe(0, np.zeros(4, np.float32), np.array([1]))
+    pol = B.EvictionPolicy(B.MOE_POLICY_HISTORY, 1, 4, 2, params=[1.0, 1.0, 0.0, 0.0, 1.5])
+    with pytest.raises(B.MoeError):
+        pol.observe(0, np.zeros(4, np.float32), np.array([1]))
+    pol = B.EvictionPolicy(B.MOE_POLICY_MRS, 1, 4, 2)
+    with pytest.raises(B.MoeError):
+        pol.observe(0, np.zeros(4, np.float32), np.array([4]))
+    assert not pol.state.any()
