@@ -43,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+from expert_offload_routed_amd import binding as B  # noqa: E402
 from expert_offload_routed_amd import harness as Hn  # noqa: E402
 from expert_offload_routed_amd import workloads as W  # noqa: E402
 
@@ -216,6 +217,30 @@ PLANS = {
     "dsv3_e256k8s1_h7168_f2048_int4": dict(hit=[1, 32, 4096], miss=[(84, 1)]),
 }
 CASES = {"decode1": 1, "decode8": 8, "prefill512": 512}
+# eviction policies compared on the caches with fills: (kind, window, params). The pages give
+# no window, weights or decay; these are the readings (window of 8 steps, equal weights, 0.9).
+POLICIES = {"lru": (B.MOE_POLICY_LRU, 1, None),
+            "mrs": (B.MOE_POLICY_MRS, 8, None),
+            "history": (B.MOE_POLICY_HISTORY, 8, [1.0, 1.0, 1.0, 1.0, 0.9])}
+
+
+def fill_cases(shape, plan, cfg, store, steps, warmup):
+    """Each cache with fills of the workload under each eviction policy, on the same inputs."""
+    out = {}
+    for S, T in plan["miss"]:
+        res = {}
+        for name, (kind, window, params) in POLICIES.items():
+            small = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]),
+                                      t_max=T, store=store)
+            small.ctx.set_policy(kind, window, params)
+            r = timed(small, shape, T, steps, warmup,
+                      f"T={T}, {S} slots ({cfg['residency']}), {name} eviction, fills over PCIe")
+            r["fill_bytes_per_step"] = r["fills_per_step"] * store.stride
+            res[name] = r
+            del small
+            torch.cuda.empty_cache()
+        out[f"T{T}_{S}slots_with_fills"] = res
+    return out
 
 
 def main():
@@ -228,7 +253,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline case only")
     ap.add_argument("--case", default=None,
                     help="one case only, for profiling (prints no JSON line): decode1, decode8, "
-                         "prefill512, fills, T<n> (hit path at n tokens), calib_copy")
+                         "prefill512, fills, policies (every cache with fills under each eviction "
+                         "policy), T<n> (hit path at n tokens), calib_copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU form of "
@@ -248,7 +274,9 @@ def main():
     S_hit = len(resident)
 
     if args.case is not None:
-        if args.case == "fills":
+        if args.case == "policies":
+            fill_cases(shape, plan, cfg, store, K, Wm)
+        elif args.case == "fills":
             S, T = plan["miss"][0]
             small = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]),
                                       t_max=T, store=store)
@@ -269,15 +297,8 @@ def main():
             also[f"T{T}_hit"] = timed(layer, shape, T, steps, 2, f"T={T} hit path", ffn_timing=True)
         del layer
         torch.cuda.empty_cache()
-        for S, T in plan["miss"]:
-            small = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]),
-                                      t_max=T, store=store)
-            steps = max(K // 5, 5) if shape.layers == 1 else max(K // 5, 8)
-            r = timed(small, shape, T, steps, 2, f"T={T}, {S} slots ({cfg['residency']}), fills over PCIe")
-            r["fill_bytes_per_step"] = r["fills_per_step"] * store.stride
-            also[f"T{T}_{S}slots_with_fills"] = r
-            del small
-            torch.cuda.empty_cache()
+        steps = max(K // 5, 5) if shape.layers == 1 else max(K // 5, 8)
+        also.update(fill_cases(shape, plan, cfg, store, steps, 2))
 
     ffn = head["ffn"]
     line = {

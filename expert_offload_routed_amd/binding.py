@@ -53,6 +53,8 @@ _SIGNATURES = {
     "moe_ctx_read_tables": (_i32, [_vp, _vp, _vp, _vp, _vp]),
     "moe_ctx_outputs": (_i32, [_vp] + [ctypes.POINTER(_vp)] * 6),
     "moe_ctx_set_timing": (_i32, [_vp, _i32]),
+    "moe_ctx_set_policy": (_i32, [_vp, _i32, _i32, _vp]),
+    "moe_ctx_step_scores": (_i32, [_vp, _vp]),
     "moe_ctx_counters": (_i32, [_vp, _vp]),
     "moe_ctx_ffn_time": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_long)]),
 }
@@ -417,6 +419,18 @@ class LayerContext:
 
     def set_timing(self, on: bool) -> None:
         _call("moe_ctx_set_timing", self.handle, int(on))
+
+    def set_policy(self, kind: int, window: int = 1, params=None) -> None:
+        """Eviction policy of the residency plans (MOE_POLICY_LRU / _MRS / _HISTORY)."""
+        p = None if params is None else np.ascontiguousarray(params, dtype=np.float64)
+        self._policy_params = p  # kept alive while the call reads it
+        _call("moe_ctx_set_policy", self.handle, kind, window, _host(p) if p is not None else None)
+
+    def step_scores(self) -> np.ndarray:
+        """Routing scores [E] of the latest step (needs a policy other than LRU)."""
+        out = np.zeros(self.E, np.float32)
+        _call("moe_ctx_step_scores", self.handle, _host(out))
+        return out
 
     def ffn_time(self) -> tuple[float, int]:
         ms, n = ctypes.c_double(), ctypes.c_long()

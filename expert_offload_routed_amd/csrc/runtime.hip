@@ -21,6 +21,7 @@
 // The context allocates its staging once, at creation; a step allocates
 // nothing.
 #include <limits.h>
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -59,7 +60,8 @@ struct moe_layer_ctx {
   int32_t* masks;
   int sh_T;  // T the shared groups' rows (perm and offsets tails) were written for
   // host state
-  int32_t* ring_h;  // pinned [kRing][E+1]: routed sets of steps (written by the device)
+  int32_t* ring_h;  // pinned [kRing][2E+1]: per step the routed set [E], its size, and the
+                    // experts' routing scores [E] (float), written by the device
   int32_t* ring_d;  // device address of ring_h
   hipEvent_t ring_ev[kRing];
   int ring_layer[kRing];
@@ -70,6 +72,11 @@ struct moe_layer_ctx {
   std::vector<int32_t> lut_h, owner_h, resident;  // resident[l]: experts of layer l in the pool
   std::vector<int64_t> last_use;
   int64_t clock;
+  // eviction policy (moe_ctx_set_policy): LRU unless set
+  int policy, window;
+  double params[5];
+  std::vector<double> pol_state;
+  int last_ring;  // ring entry of the latest step
   uint64_t next_tag;
   std::vector<int32_t> wave_of, is_hit, fill_e, fill_s, fill_w;
   hipEvent_t ev_fill, ev_compute;
@@ -130,6 +137,49 @@ __global__ void commit_after_fill_kernel(int32_t* lut, int32_t idx, int32_t* own
   owner[slot] = idx;
 }
 
+// Routing score of every expert at one step: its softmax probability over the
+// step's tokens, averaged over the tokens (the score the eviction policies
+// record). One workgroup of 16 waves; wave w takes tokens w, w + 16, ...;
+// the per-wave partial sums meet in LDS in wave order.
+constexpr int kScoreWaves = 16;
+__global__ __launch_bounds__(kScoreWaves * 64) void step_scores_kernel(const float* __restrict__ logits,
+                                                                      int T, int E, float* out) {
+  __shared__ float part[kScoreWaves][1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kPer = 1024 / 64;  // experts per lane (E <= 1024)
+  float acc[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
+  for (int t = wave; t < T; t += kScoreWaves) {
+    const float* row = logits + (size_t)t * E;
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) m = fmaxf(m, row[e]);
+    }
+    m = wave_max(m);
+    float v[kPer], sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < E ? expf(row[e] - m) : 0.f;
+      sum += v[i];
+    }
+    sum = wave_sum(sum);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) acc[i] += v[i] / sum;
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) part[wave][lane + 64 * i] = acc[i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kScoreWaves * 64) {
+    float s = 0.f;
+    for (int w = 0; w < kScoreWaves; ++w) s += part[w][e];
+    out[e] = s / (float)T;
+  }
+}
+
 __global__ void write_tag_kernel(uint64_t* tags, int slot, uint64_t tag) {
   if (threadIdx.x == 0) tags[slot] = tag;
 }
@@ -184,13 +234,21 @@ int fills_after_compute(moe_layer_ctx* c) {
   return moe_hip_status(e);
 }
 
-// Host LRU plan of one routed set (moves the host tables), with counters.
-int run_plan(moe_layer_ctx* c, int layer, const int32_t* distinct, int nd, int32_t* n_fills,
+// Host plan of one routed set under the context's eviction policy (moves the
+// host tables), with counters; entry = the step's ring entry (routed set, its
+// size, then the routing scores).
+int run_plan(moe_layer_ctx* c, int layer, const int32_t* entry, int32_t* n_fills,
              int32_t* n_waves) {
-  const int rc = moe_plan_fills(c->lut_h.data(), c->owner_h.data(), c->last_use.data(), &c->clock,
-                                c->S, c->L, c->E, layer, distinct, nd, c->wave_of.data(),
-                                c->is_hit.data(), c->fill_e.data(), c->fill_s.data(),
-                                c->fill_w.data(), n_fills, n_waves);
+  const int* distinct = entry;
+  const int nd = entry[c->E];
+  const float* scores = reinterpret_cast<const float*>(entry + c->E + 1);
+  int rc = moe_policy_observe(c->policy, c->pol_state.data(), c->L, c->E, c->window, layer, scores,
+                              distinct, nd, c->params);
+  if (rc != MOE_OK) return rc;
+  rc = moe_plan_fills_policy(c->policy, c->pol_state.data(), c->window, c->params, c->lut_h.data(),
+                             c->owner_h.data(), c->last_use.data(), &c->clock, c->S, c->L, c->E,
+                             layer, distinct, nd, c->wave_of.data(), c->is_hit.data(),
+                             c->fill_e.data(), c->fill_s.data(), c->fill_w.data(), n_fills, n_waves);
   if (rc != MOE_OK) return rc;
   int hits = 0;
   for (int i = 0; i < nd; ++i) hits += c->is_hit[distinct[i]];
@@ -208,9 +266,9 @@ int drain(moe_layer_ctx* c) {
     const int r = c->ring_head;
     const hipError_t e = hipEventSynchronize(c->ring_ev[r]);
     if (e != hipSuccess) return moe_hip_status(e);
-    const int32_t* d = c->ring_h + (size_t)r * (c->E + 1);
+    const int32_t* d = c->ring_h + (size_t)r * (2 * c->E + 1);
     int32_t nf = 0, nw = 0;
-    const int rc = run_plan(c, c->ring_layer[r], d, d[c->E], &nf, &nw);
+    const int rc = run_plan(c, c->ring_layer[r], d, &nf, &nw);
     if (rc != MOE_OK) return rc;
     c->ring_head = (c->ring_head + 1) % kRing;
     c->ring_count -= 1;
@@ -280,6 +338,10 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->resident.assign(L, 0);
   c->last_use.assign(S, 0);
   c->clock = 0;
+  c->policy = MOE_POLICY_LRU;
+  c->window = 1;
+  for (double& v : c->params) v = 0.0;
+  c->last_ring = -1;
   c->next_tag = 1;
   c->wave_of.resize(E); c->is_hit.resize(E);
   c->fill_e.resize(E); c->fill_s.resize(E); c->fill_w.resize(E);
@@ -301,7 +363,7 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   int bad = 0;
   // coherent, mapped: the permutation kernel stores the routed set straight into it
   bad |= hipHostMalloc(reinterpret_cast<void**>(&c->ring_h),
-                       (size_t)kRing * (E + 1) * sizeof(int32_t),
+                       (size_t)kRing * (2 * E + 1) * sizeof(int32_t),
                        hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess;
   if (!bad) bad |= hipHostGetDevicePointer(reinterpret_cast<void**>(&c->ring_d), c->ring_h, 0) !=
                    hipSuccess;
@@ -393,6 +455,36 @@ extern "C" int moe_ctx_ffn_time(moe_layer_ctx* c, double* total_ms, long* steps)
   return MOE_OK;
 }
 
+extern "C" int moe_ctx_set_policy(moe_layer_ctx* c, int policy, int window, const double* params) {
+  MOE_CHECK_ARG(c);
+  size_t n = 0;
+  if (policy != MOE_POLICY_LRU) {
+    n = moe_policy_state_doubles(policy, c->L, c->E, window);
+    MOE_CHECK_ARG(n > 0);
+  }
+  if (policy == MOE_POLICY_HISTORY) {
+    MOE_CHECK_ARG(params);
+    for (int i = 0; i < 4; ++i) MOE_CHECK_ARG(params[i] >= 0.0);
+    MOE_CHECK_ARG(params[4] >= 0.0 && params[4] <= 1.0);
+  }
+  const int rc = drain(c);  // steps so far are booked under the previous policy
+  if (rc != MOE_OK) return rc;
+  c->policy = policy;
+  c->window = policy == MOE_POLICY_LRU ? 1 : window;
+  for (int i = 0; i < 5; ++i) c->params[i] = (policy == MOE_POLICY_HISTORY) ? params[i] : 0.0;
+  c->pol_state.assign(n, 0.0);
+  return MOE_OK;
+}
+
+extern "C" int moe_ctx_step_scores(moe_layer_ctx* c, float* scores) {
+  MOE_CHECK_ARG(c && scores && c->policy != MOE_POLICY_LRU && c->last_ring >= 0);
+  const hipError_t e = hipEventSynchronize(c->ring_ev[c->last_ring]);
+  if (e != hipSuccess) return moe_hip_status(e);
+  memcpy(scores, c->ring_h + (size_t)c->last_ring * (2 * c->E + 1) + c->E + 1,
+         (size_t)c->E * sizeof(float));
+  return MOE_OK;
+}
+
 extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int T,
                                  const void* w_router, const float* bias, void* out, int out_dtype,
                                  int32_t* stats) {
@@ -423,8 +515,8 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   // the routed set is written by the device into the next ring entry (pinned host memory)
   if (c->ring_count == kRing && (rc = drain(c)) != MOE_OK) return rc;
   const int r = c->ring_next;
-  int32_t* dh = c->ring_h + (size_t)r * (E + 1);
-  int32_t* dd = c->ring_d + (size_t)r * (E + 1);
+  int32_t* dh = c->ring_h + (size_t)r * (2 * E + 1);
+  int32_t* dd = c->ring_d + (size_t)r * (2 * E + 1);
   const bool all_resident = c->resident[layer] == E;
   const int32_t* lut_row = c->lut + (size_t)layer * E;
   // a fully resident layer's FFN work list comes from the front end itself
@@ -447,8 +539,14 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
                                c->topw, c->counts, c->offsets, c->perm, c->inv, dd, dd + E, c->sync,
                                all_resident ? &fp : nullptr, &planned, c->cs)) != MOE_OK)
     return rc;
+  if (c->policy != MOE_POLICY_LRU) {  // the scores the policy records, next to the routed set
+    hipLaunchKernelGGL(step_scores_kernel, dim3(1), dim3(kScoreWaves * 64), 0, c->cs, c->logits, T, E,
+                       reinterpret_cast<float*>(dd + E + 1));
+    if ((rc = moe_launch_status()) != MOE_OK) return rc;
+  }
   if ((e = hipEventRecord(c->ring_ev[r], c->cs)) != hipSuccess) return moe_hip_status(e);
   c->ring_next = (r + 1) % kRing;
+  c->last_ring = r;
 
   int32_t n_fills = 0, n_waves = 0, nd = -1, hits = -1;
   const bool timing = c->timing != 0;
@@ -470,7 +568,7 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
     c->ring_head = c->ring_next;                 // entry r is consumed here, not deferred
     if ((e = hipEventSynchronize(c->ring_ev[r])) != hipSuccess) return moe_hip_status(e);
     nd = dh[E];
-    if ((rc = run_plan(c, layer, dh, nd, &n_fills, &n_waves)) != MOE_OK) return rc;
+    if ((rc = run_plan(c, layer, dh, &n_fills, &n_waves)) != MOE_OK) return rc;
     // masks: row 0 = resident groups, row 1 + w = groups filled in wave w
     const int rows = n_waves + 1;
     memset(c->masks_h, 0, (size_t)rows * E * sizeof(int32_t));

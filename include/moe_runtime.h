@@ -107,6 +107,23 @@ int moe_ctx_counters(moe_layer_ctx* ctx, int64_t* out);
 int moe_ctx_outputs(const moe_layer_ctx* ctx, float** logits, int32_t** ids, float** topk_w,
                     int32_t** perm, int32_t** offsets, int32_t** inv);
 
+/* moe_ctx_set_policy: eviction policy of the context's residency plans
+ * (MOE_POLICY_LRU, MOE_POLICY_MRS or MOE_POLICY_HISTORY, include/moe_offload.h;
+ * window and params as for moe_policy_observe, params NULL unless HISTORY).
+ * Steps already enqueued are booked under the previous policy first; the
+ * policy's history starts empty. With a policy other than LRU every step also
+ * computes the experts' routing scores (softmax over each token's logits,
+ * averaged over the step's tokens) into its pinned staging, and each plan
+ * records them (moe_policy_observe) before choosing victims
+ * (moe_plan_fills_policy). Allocates the policy state (host) here, not per
+ * step. MOE_EINVAL on bad arguments. */
+int moe_ctx_set_policy(moe_layer_ctx* ctx, int policy, int window, const double* params);
+
+/* moe_ctx_step_scores: the routing scores [E] (host floats) of the latest
+ * step, waiting for that step's router; MOE_EINVAL under LRU or before any
+ * step. */
+int moe_ctx_step_scores(moe_layer_ctx* ctx, float* scores);
+
 /* moe_ctx_set_timing: when enabled, each step records HIP events on the
  * compute stream around its expert FFN calls (the routed groups, including
  * any fill waves, then the shared experts); moe_ctx_ffn_time

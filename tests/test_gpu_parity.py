@@ -294,12 +294,23 @@ def test_slot_fill_rejects_pageable_host_memory():
 
 
 # --------------------------------------------------------------- whole layer --
-def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1):
-    """Run steps through the harness and compare every step with the oracle."""
+def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, policy=None):
+    """Run steps through the harness and compare every step with the oracle.
+
+    policy = (kind, window, params): the runtime plans under that eviction policy and the
+    oracle's scored planner records the same step scores (the kernel's own, checked against
+    the oracle's softmax of the kernel's logits) before each plan."""
     t_max = max(Ts)
     residency = W.initial_residency(shape, slots, mode)
     layer_obj = Hn.SlotCacheLayer(shape, slots, residency, t_max)
-    planner = O.LruSlotPlanner(slots, shape.layers, shape.E, residency)
+    if policy is None:
+        planner = O.LruSlotPlanner(slots, shape.layers, shape.E, residency)
+    else:
+        kind, window, params = policy
+        layer_obj.ctx.set_policy(kind, window, params)
+        pol = (O.MinusRecentScore(shape.layers, shape.E, window) if kind == B.MOE_POLICY_MRS else
+               O.RoutingHistoryScore(shape.layers, shape.E, window, weights=params[:4], lam=params[4]))
+        planner = O.ScoredSlotPlanner(slots, shape.layers, shape.E, pol, residency)
     sh_w = [host_weights(shape, j, shared=True) for j in range(shape.n_shared)]
     order = layers_order or [0]
     for step, T in enumerate(Ts):
@@ -317,7 +328,12 @@ def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1):
             pr = O.permute(ids, shape.E)
             assert o["perm"].cpu().numpy().tolist() == pr["perm"].tolist()
             assert o["inv"].cpu().numpy().tolist() == pr["inv"].tolist()
-            planner.plan(layer, pr["distinct"])
+            if policy is None:
+                planner.plan(layer, pr["distinct"])
+            else:
+                sc = layer_obj.ctx.step_scores()
+                np.testing.assert_allclose(sc, O.step_scores(o["logits"].cpu().numpy()), rtol=2e-6, atol=1e-7)
+                planner.plan(layer, pr["distinct"], sc)
             lut_h, owner_h, last_use_h, clock_h = layer_obj.tables()
             assert layer_obj.lut.cpu().numpy().reshape(shape.layers, shape.E).tolist() == planner.lut.tolist()
             assert lut_h.reshape(shape.layers, shape.E).tolist() == planner.lut.tolist()
@@ -349,6 +365,19 @@ def test_layer_stack_shared_pool():
     shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=3, E=16, k=4, H=256,
                       F=128, blobs=16)
     _run_layer_case(shape, 14, "zipf_rank", [1, 3, 16], layers_order=[0, 1, 2])
+
+
+def test_layer_stack_policy_mrs():
+    shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=3, E=16, k=4, H=256,
+                      F=128, blobs=16)
+    _run_layer_case(shape, 14, "zipf_rank", [1, 3, 1, 16, 2, 1], layers_order=[0, 1, 2],
+                    policy=(B.MOE_POLICY_MRS, 4, None))
+
+
+def test_layer_policy_history_shared_experts():
+    shape = W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), E=16, k=6, H=256, F=256)
+    _run_layer_case(shape, 8, "zipf_rank", [1, 2, 32, 1, 5, 3],
+                    policy=(B.MOE_POLICY_HISTORY, 6, [1.0, 0.5, 2.0, 0.25, 0.8]))
 
 
 def test_layer_shared_experts():
