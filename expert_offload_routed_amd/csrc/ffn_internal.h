@@ -58,7 +58,8 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype
 // T*k routed rows, slots shared_slot0 + s), groups of <= small_max rows as
 // items, the others as kGemmBM-row tiles, into the FFN workspace's lists.
 struct FrontPlan {
-  const int32_t* lut;
+  float* scores;  // when set: each expert's softmax probability averaged over the tokens [E]
+  const int32_t* lut;  // when set: write the FFN work list below
   int num_slots, n_shared, shared_slot0, small_max;
   FfnItem* items;
   int32_t* n_items;
@@ -67,13 +68,15 @@ struct FrontPlan {
   int32_t* err;
 };
 // moe_route_permute that, on its one-launch path, also writes the expert FFN's
-// work list described by *plan (*planned = true); otherwise the FFN plans.
+// work list described by *plan when plan->lut is set (*planned = true; otherwise
+// the FFN plans) and the routing scores when plan->scores is set (*scored =
+// true; otherwise the caller computes them).
 int route_permute_plan(const void* x, int x_dtype, const void* w_router, const float* bias, int T,
                        int H, int E, int k, int renorm, float* logits, int32_t* topk_ids,
                        float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                        int32_t* inv, int32_t* distinct, int32_t* n_distinct,
                        uint32_t* sync_counter, const FrontPlan* plan, bool* planned,
-                       hipStream_t stream);
+                       bool* scored, hipStream_t stream);
 // moe_expert_ffn with the shared experts as groups E .. E+n_shared-1: offsets
 // has E + n_shared + 1 entries, group E + s holds T rows (perm value t * k for
 // token t) and reads slot shared_slot0 + s; group_mask applies to routed groups.

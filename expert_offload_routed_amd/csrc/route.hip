@@ -238,7 +238,33 @@ struct FrontLds {
   int off[1024];    // first position of each expert
   int perm[1024];   // assignment at each sorted position
   int wave[40];     // scan scratch
+  float tmax[kFrontMaxT], tsum[kFrontMaxT];  // softmax max and sum of each token (scores)
 };
+
+// Softmax normaliser of token t (its max logit and the sum of exp(l - max)) for
+// the routing scores; executed by one whole wave.
+template <int NV>
+__device__ void token_softmax_norm(const float* lg, int t, int E, float* tmax, float* tsum) {
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) m = fmaxf(m, lg[(size_t)t * E + e]);
+  }
+  m = wave_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) s += expf(lg[(size_t)t * E + e] - m);
+  }
+  s = wave_sum(s);
+  if (lane == 0) {
+    tmax[t] = m;
+    tsum[t] = s;
+  }
+}
 
 // Work list of the expert FFN written by the front end itself (see FrontPlan):
 // the same items and tiles, in the same order, as the FFN's own plan kernel.
@@ -289,7 +315,10 @@ __device__ void front_select_and_sort(const float* lg, int T, int E, int k, int 
                                       int32_t* __restrict__ n_distinct, FrontLds& L, int* s_dist,
                                       const FrontPlan& pl) {
   const int tid = threadIdx.x, nthr = blockDim.x, wave = tid >> 6, nwaves = nthr >> 6;
-  for (int t = wave; t < T; t += nwaves) topk_token<NV>(lg, t, E, k, renorm, L.ids, L.w);
+  for (int t = wave; t < T; t += nwaves) {
+    topk_token<NV>(lg, t, E, k, renorm, L.ids, L.w);
+    if (pl.scores) token_softmax_norm<NV>(lg, t, E, L.tmax, L.tsum);
+  }
   const int n = T * k;
   for (int i = tid; i < 1024; i += nthr) L.cnt[i] = 0;
   __syncthreads();
@@ -349,6 +378,13 @@ __device__ void front_select_and_sort(const float* lg, int T, int E, int k, int 
   if (tid == 0) {
     offsets[E] = total;
     n_distinct[0] = nd;
+  }
+  if (pl.scores) {  // routing scores: softmax probability averaged over the tokens
+    for (int ex = tid; ex < E; ex += nthr) {
+      float acc = 0.f;
+      for (int t = 0; t < T; ++t) acc += expf(lg[(size_t)t * E + ex] - L.tmax[t]) / L.tsum[t];
+      pl.scores[ex] = acc / (float)T;
+    }
   }
 }
 
@@ -570,7 +606,7 @@ extern "C" int moe_route_permute(const void* x, int x_dtype, const void* w_route
                                  int32_t* n_distinct, uint32_t* sync_counter, hipStream_t stream) {
   return route_permute_plan(x, x_dtype, w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w,
                             counts, offsets, perm, inv, distinct, n_distinct, sync_counter, nullptr,
-                            nullptr, stream);
+                            nullptr, nullptr, stream);
 }
 
 int route_permute_plan(const void* x, int x_dtype, const void* w_router, const float* bias, int T,
@@ -578,8 +614,9 @@ int route_permute_plan(const void* x, int x_dtype, const void* w_router, const f
                        float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                        int32_t* inv, int32_t* distinct, int32_t* n_distinct,
                        uint32_t* sync_counter, const FrontPlan* plan, bool* planned,
-                       hipStream_t stream) {
+                       bool* scored, hipStream_t stream) {
   if (planned) *planned = false;
+  if (scored) *scored = false;
   MOE_CHECK_ARG(T >= 0 && H > 0 && H % 8 == 0);
   MOE_CHECK_ARG(k >= 1 && k <= E && E <= 64 * kTopkMaxV);
   MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
@@ -595,9 +632,14 @@ int route_permute_plan(const void* x, int x_dtype, const void* w_router, const f
   const size_t wbytes = (size_t)E * H * (x_dtype == MOE_BF16 ? 2 : 4);
   const bool single = E <= kSingleMaxE && wbytes <= kSingleMaxBytes;
   FrontPlan pl{};
-  if (plan && E + plan->n_shared <= 1024) {
+  if (plan) {
     pl = *plan;
-    if (planned) *planned = true;
+    if (pl.lut && E + pl.n_shared <= 1024) {
+      if (planned) *planned = true;
+    } else {
+      pl.lut = nullptr;
+    }
+    if (pl.scores && scored) *scored = true;
   }
   // code specialised to the token count and logits per lane: the front end runs once per step,
   // from a cold instruction cache, so it should hold only the code the step needs

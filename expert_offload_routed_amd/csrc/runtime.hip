@@ -519,9 +519,12 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   int32_t* dd = c->ring_d + (size_t)r * (2 * E + 1);
   const bool all_resident = c->resident[layer] == E;
   const int32_t* lut_row = c->lut + (size_t)layer * E;
-  // a fully resident layer's FFN work list comes from the front end itself
+  // a fully resident layer's FFN work list comes from the front end itself, and so do the
+  // routing scores an eviction policy records (next to the routed set)
   FrontPlan fp{};
-  bool planned = false;
+  bool planned = false, scored = false;
+  const bool want_scores = c->policy != MOE_POLICY_LRU;
+  if (want_scores) fp.scores = reinterpret_cast<float*>(dd + E + 1);
   if (all_resident) {
     const FfnWorkspace wl = ffn_workspace_layout(T, H, F, E, k, c->w_dtype, nsh);
     fp.lut = lut_row;
@@ -537,9 +540,10 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   }
   if ((rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
                                c->topw, c->counts, c->offsets, c->perm, c->inv, dd, dd + E, c->sync,
-                               all_resident ? &fp : nullptr, &planned, c->cs)) != MOE_OK)
+                               (all_resident || want_scores) ? &fp : nullptr, &planned, &scored,
+                               c->cs)) != MOE_OK)
     return rc;
-  if (c->policy != MOE_POLICY_LRU) {  // the scores the policy records, next to the routed set
+  if (want_scores && !scored) {  // the front end did not write them (more tokens)
     hipLaunchKernelGGL(step_scores_kernel, dim3(1), dim3(kScoreWaves * 64), 0, c->cs, c->logits, T, E,
                        reinterpret_cast<float*>(dd + E + 1));
     if ((rc = moe_launch_status()) != MOE_OK) return rc;

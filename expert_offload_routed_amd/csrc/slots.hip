@@ -215,17 +215,28 @@ extern "C" int slot_fill(void* pool_base, size_t slot_stride, int32_t slot, cons
 // ------------------------------------------------------- host LRU planning --
 // ------------------------------------------------------- eviction scores --
 // Host state of an eviction policy, per layer (doubles):
-//   MRS:     [observed steps, ring of the last W score vectors (W x E)]
+//   MRS:     [observed steps, ring of the last W score vectors (W x E), keep (E)]
 //   HISTORY: [observed steps, ring of the last W selection vectors (W x E, 0/1),
-//             ema (E), latest score (E), step of the last selection (E, 0 = never)]
+//             ema (E), latest score (E), step of the last selection (E, 0 = never),
+//             keep (E)]
+// A layer's state changes only when it is observed, so its keep scores are
+// computed then and read by every later plan until its next step.
 // All arithmetic is float64 in a fixed order without contraction, so the
 // victim order is reproducible bit for bit.
 namespace {
 
 size_t policy_layer_doubles(int policy, int E, int W) {
-  if (policy == MOE_POLICY_MRS) return 1 + (size_t)W * E;
-  if (policy == MOE_POLICY_HISTORY) return 1 + (size_t)W * E + 3 * (size_t)E;
+  if (policy == MOE_POLICY_MRS) return 1 + (size_t)W * E + E;
+  if (policy == MOE_POLICY_HISTORY) return 1 + (size_t)W * E + 4 * (size_t)E;
   return 0;
+}
+
+// keep scores of a layer (the last E doubles of its state)
+inline double* keep_of(double* st, int policy, int E, int W) {
+  return st + policy_layer_doubles(policy, E, W) - E;
+}
+inline const double* keep_of(const double* st, int policy, int E, int W) {
+  return st + policy_layer_doubles(policy, E, W) - E;
 }
 
 #pragma clang fp contract(off)
@@ -354,24 +365,13 @@ int plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock, 
     if (policy != MOE_POLICY_LRU && need > 0) {
       keep.assign(S, 0.0);
       const size_t per = policy_layer_doubles(policy, E, W);
-      std::vector<HistoryNorm> norm;
-      std::vector<char> have;
-      if (policy == MOE_POLICY_HISTORY) {
-        norm.resize(L);
-        have.assign(L, 0);
-      }
       for (int s : reuse) {
         const int l = owner[s] / E, e = owner[s] % E;
         const double* st = state + (size_t)l * per;
-        if (policy == MOE_POLICY_MRS) {
-          keep[s] = mrs_keep(st, E, W, e);
-        } else {
-          if (!have[l]) {
-            norm[l] = history_norm(st, E, W);
-            have[l] = 1;
-          }
-          keep[s] = history_keep(st, E, W, params, norm[l], e);
-        }
+        if (st[0] != 0.0)
+          keep[s] = keep_of(st, policy, E, W)[e];
+        else  // a layer never observed has no cached scores yet
+          keep[s] = policy == MOE_POLICY_MRS ? 0.0 : history_keep(st, E, W, params, HistoryNorm{0.0, 0.0, 0.0, 0.0}, e);
       }
     }
     auto first = [&](int a, int b) {
@@ -478,6 +478,13 @@ extern "C" int moe_policy_observe(int policy, double* state, int L, int E, int w
     }
   }
   st[0] = (double)(n + 1);
+  double* keep = keep_of(st, policy, E, W);
+  if (policy == MOE_POLICY_MRS) {
+    for (int e = 0; e < E; ++e) keep[e] = mrs_keep(st, E, W, e);
+  } else {
+    const HistoryNorm h = history_norm(st, E, W);
+    for (int e = 0; e < E; ++e) keep[e] = history_keep(st, E, W, params, h, e);
+  }
   return MOE_OK;
 }
 #pragma clang fp contract(on)
