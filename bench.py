@@ -219,9 +219,11 @@ PLANS = {
 CASES = {"decode1": 1, "decode8": 8, "prefill512": 512}
 # eviction policies compared on the caches with fills: (kind, window, params). The pages give
 # no window, weights or decay; these are the readings (window of 8 steps, equal weights, 0.9).
+# "lru_device": the same LRU plan run by the GPU itself (device orchestration, no host wait).
 POLICIES = {"lru": (B.MOE_POLICY_LRU, 1, None),
             "mrs": (B.MOE_POLICY_MRS, 8, None),
-            "history": (B.MOE_POLICY_HISTORY, 8, [1.0, 1.0, 1.0, 1.0, 0.9])}
+            "history": (B.MOE_POLICY_HISTORY, 8, [1.0, 1.0, 1.0, 1.0, 0.9]),
+            "lru_device": (B.MOE_POLICY_LRU, 1, None)}
 
 
 def fill_cases(shape, plan, cfg, store, steps, warmup):
@@ -233,6 +235,10 @@ def fill_cases(shape, plan, cfg, store, steps, warmup):
             small = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]),
                                       t_max=T, store=store)
             small.ctx.set_policy(kind, window, params)
+            if name.endswith("_device"):
+                if T * shape.k > S:
+                    continue  # more routed experts than slots: only the host plans it
+                small.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
             r = timed(small, shape, T, steps, warmup,
                       f"T={T}, {S} slots ({cfg['residency']}), {name} eviction, fills over PCIe")
             r["fill_bytes_per_step"] = r["fills_per_step"] * store.stride

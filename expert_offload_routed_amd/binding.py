@@ -54,6 +54,7 @@ _SIGNATURES = {
     "moe_ctx_outputs": (_i32, [_vp] + [ctypes.POINTER(_vp)] * 6),
     "moe_ctx_set_timing": (_i32, [_vp, _i32]),
     "moe_ctx_set_policy": (_i32, [_vp, _i32, _i32, _vp]),
+    "moe_ctx_set_orchestration": (_i32, [_vp, _i32]),
     "moe_ctx_step_scores": (_i32, [_vp, _vp]),
     "moe_ctx_counters": (_i32, [_vp, _vp]),
     "moe_ctx_ffn_time": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_long)]),
@@ -298,6 +299,7 @@ def _plan(policy, lut, owner, last_use, clock, S, L, E, layer, distinct) -> dict
 
 
 MOE_POLICY_LRU, MOE_POLICY_MRS, MOE_POLICY_HISTORY = 0, 1, 2
+MOE_ORCH_HOST, MOE_ORCH_DEVICE = 0, 1
 
 
 class EvictionPolicy:
@@ -419,6 +421,10 @@ class LayerContext:
 
     def set_timing(self, on: bool) -> None:
         _call("moe_ctx_set_timing", self.handle, int(on))
+
+    def set_orchestration(self, mode: int) -> None:
+        """MOE_ORCH_HOST or MOE_ORCH_DEVICE (plans and fills on the GPU, no host wait per step)."""
+        _call("moe_ctx_set_orchestration", self.handle, mode)
 
     def set_policy(self, kind: int, window: int = 1, params=None) -> None:
         """Eviction policy of the residency plans (MOE_POLICY_LRU / _MRS / _HISTORY)."""

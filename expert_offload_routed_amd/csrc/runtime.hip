@@ -18,13 +18,22 @@
 // routed set lands in a ring of pinned buffers and its LRU bookkeeping (clock
 // and last use, with no fills) is replayed in step order before the next plan
 // that needs the tables.
-// The context allocates its staging once, at creation; a step allocates
-// nothing.
+// Device orchestration (moe_ctx_set_orchestration): the GPU plans and fills by
+// itself, so a step never waits for the host (SeqMoE summary page, Mechanism:
+// the device owns the cache metadata and starts the miss copy from a kernel,
+// out of the pinned, mapped host pool). One workgroup runs the same LRU plan on
+// the device tables, keeping the slots in (last use, slot id) order; a copy
+// kernel reads the missed experts from the mapped host store into their slots;
+// the expert FFN and the combine follow on the same stream.
+// The context allocates its staging once, at creation, and the device
+// planner's state once, when device orchestration is first switched on; a
+// step allocates nothing.
 #include <limits.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -77,6 +86,16 @@ struct moe_layer_ctx {
   double params[5];
   std::vector<double> pol_state;
   int last_ring;  // ring entry of the latest step
+  // device orchestration (moe_ctx_set_orchestration)
+  int orch;                 // 0: plans on the host; 1: plans and fills on the device
+  const char* store_dev;    // device address of the pinned host store
+  int32_t* d_order;         // [S] slots by (last use, slot id)
+  int64_t* d_last_use;      // [S]
+  int64_t* d_clock;         // [1]
+  int32_t* d_blob;          // [L*E] weight set of each layer-expert
+  int32_t* d_fills;         // [2E] (expert, slot) of the step's fills
+  int32_t* d_nfills;        // [1]
+  int64_t* d_counters;      // [4] as totals, since the last handoff to the host
   uint64_t next_tag;
   std::vector<int32_t> wave_of, is_hit, fill_e, fill_s, fill_w;
   hipEvent_t ev_fill, ev_compute;
@@ -180,6 +199,147 @@ __global__ __launch_bounds__(kScoreWaves * 64) void step_scores_kernel(const flo
   }
 }
 
+// LRU plan of one layer call on the device: the rule of moe_plan_fills for a
+// routed set that fits the pool (n_distinct <= S, one wave). Victims are the
+// empty slots by id, then the slots of `order` (kept sorted by (last use, slot
+// id)) that hold no hit; the slots used by the call move, by id, to the end of
+// the order. Thread t owns slots / order positions 4t .. 4t+3.
+constexpr int kDevPlanMaxS = 4096;
+__global__ __launch_bounds__(1024) void device_plan_kernel(
+    int layer, int E, int S, const int32_t* __restrict__ routed /* [E] then the count */,
+    int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock, int32_t* order,
+    int32_t* fills, int32_t* n_fills, int64_t* counters) {
+  __shared__ uint32_t s_kept[kDevPlanMaxS / 32], s_used[kDevPlanMaxS / 32];
+  __shared__ int s_miss[1024], s_vict[1024], s_wave[40];
+  __shared__ int s_order[kDevPlanMaxS];
+  const int tid = threadIdx.x;
+  const int nd = routed[E];
+  const int64_t now = clock[0] + 1;
+  int32_t* row = lut + (size_t)layer * E;
+  for (int i = tid; i < kDevPlanMaxS / 32; i += blockDim.x) s_kept[i] = s_used[i] = 0u;
+  __syncthreads();
+  int is_hit = 0, is_miss = 0, ex = -1;
+  if (tid < nd) {
+    ex = routed[tid];
+    const int sl = row[ex];
+    if (sl >= 0) {
+      is_hit = 1;
+      atomicOr(&s_kept[sl >> 5], 1u << (sl & 31));
+      atomicOr(&s_used[sl >> 5], 1u << (sl & 31));
+    } else {
+      is_miss = 1;
+    }
+  }
+  int nmiss = 0, nhit = 0;
+  const int mpos = block_exclusive_scan(is_miss, s_wave, &nmiss);  // ends with a barrier
+  (void)block_exclusive_scan(is_hit, s_wave, &nhit);
+  if (is_miss) s_miss[mpos] = ex;
+  // victims: empty slots by id
+  int sl4[4], cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sl = tid * 4 + j;
+    sl4[j] = (sl < S && owner[sl] < 0) ? 1 : 0;
+    cnt += sl4[j];
+  }
+  int nempty = 0;
+  int pos = block_exclusive_scan(cnt, s_wave, &nempty);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (sl4[j]) {
+      if (pos < nmiss) s_vict[pos] = tid * 4 + j;
+      ++pos;
+    }
+  // then the slots holding no hit, in LRU order
+  int o4[4], ok4[4];
+  cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int idx = tid * 4 + j;
+    o4[j] = idx < S ? order[idx] : -1;
+    ok4[j] = (o4[j] >= 0 && owner[o4[j]] >= 0 && !((s_kept[o4[j] >> 5] >> (o4[j] & 31)) & 1u)) ? 1 : 0;
+    cnt += ok4[j];
+  }
+  int nre = 0;
+  pos = nempty + block_exclusive_scan(cnt, s_wave, &nre);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (ok4[j]) {
+      if (pos < nmiss) s_vict[pos] = o4[j];
+      ++pos;
+    }
+  __syncthreads();
+  // fills: miss i -> victim i (n_distinct <= S leaves enough victims)
+  if (tid < nmiss) {
+    const int sl = s_vict[tid], me = s_miss[tid];
+    const int32_t old = owner[sl];
+    if (old >= 0) lut[old] = -1;
+    row[me] = sl;
+    owner[sl] = layer * E + me;
+    fills[2 * tid] = me;
+    fills[2 * tid + 1] = sl;
+    atomicOr(&s_used[sl >> 5], 1u << (sl & 31));
+  }
+  __syncthreads();
+  // new order: the unused slots as they were, then the used slots by id
+  int keep4[4];
+  cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    keep4[j] = (o4[j] >= 0 && !((s_used[o4[j] >> 5] >> (o4[j] & 31)) & 1u)) ? 1 : 0;
+    cnt += keep4[j];
+  }
+  int nkeep = 0;
+  pos = block_exclusive_scan(cnt, s_wave, &nkeep);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (keep4[j]) s_order[pos++] = o4[j];
+  int u4[4];
+  cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sl = tid * 4 + j;
+    u4[j] = (sl < S && ((s_used[sl >> 5] >> (sl & 31)) & 1u)) ? 1 : 0;
+    cnt += u4[j];
+  }
+  int nused = 0;
+  pos = nkeep + block_exclusive_scan(cnt, s_wave, &nused);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (u4[j]) {
+      s_order[pos++] = tid * 4 + j;
+      last_use[tid * 4 + j] = now;
+    }
+  __syncthreads();
+  for (int i = tid; i < S; i += blockDim.x) order[i] = s_order[i];
+  if (tid == 0) {
+    clock[0] = now;
+    n_fills[0] = nmiss;
+    counters[0] += nd;
+    counters[1] += nhit;
+    counters[2] += nmiss;
+    counters[3] += nd > 0 ? 1 : 0;
+  }
+}
+
+// Copy the step's fills from the mapped host store into their slots (16 bytes
+// per lane, every workgroup striding over each expert's bytes in turn).
+__global__ __launch_bounds__(256) void device_fill_kernel(const char* __restrict__ store,
+                                                          const int32_t* __restrict__ blob_of,
+                                                          int layer, int E, char* pool,
+                                                          size_t stride,
+                                                          const int32_t* __restrict__ fills,
+                                                          const int32_t* __restrict__ n_fills) {
+  const int nf = n_fills[0];
+  const size_t per = stride / 16;
+  const size_t g = blockIdx.x * (size_t)blockDim.x + threadIdx.x, gs = (size_t)gridDim.x * blockDim.x;
+  for (int f = 0; f < nf; ++f) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(store + (size_t)blob_of[(size_t)layer * E + fills[2 * f]] * stride);
+    u32x4* dst = reinterpret_cast<u32x4*>(pool + (size_t)fills[2 * f + 1] * stride);
+    for (size_t j = g; j < per; j += gs) dst[j] = src[j];
+  }
+}
+
 __global__ void write_tag_kernel(uint64_t* tags, int slot, uint64_t tag) {
   if (threadIdx.x == 0) tags[slot] = tag;
 }
@@ -194,6 +354,10 @@ void destroy(moe_layer_ctx* c) {
     if (c->tev0[i]) (void)hipEventDestroy(c->tev0[i]);
     if (c->tev1[i]) (void)hipEventDestroy(c->tev1[i]);
   }
+  void* dev[] = {c->d_order, c->d_last_use, c->d_clock, c->d_blob, c->d_fills, c->d_nfills,
+                 c->d_counters};
+  for (void* p : dev)
+    if (p) (void)hipFree(p);
   if (c->ev_fill) (void)hipEventDestroy(c->ev_fill);
   if (c->ev_compute) (void)hipEventDestroy(c->ev_compute);
   delete c;
@@ -293,6 +457,37 @@ void collect_timing(moe_layer_ctx* c, bool all) {
   }
 }
 
+// Hand the residency state from the device planner back to the host tables.
+int sync_from_device(moe_layer_ctx* c) {
+  hipError_t e = hipStreamSynchronize(c->cs);
+  if (e != hipSuccess) return moe_hip_status(e);
+  int64_t cnt[4];
+  if ((e = hipMemcpy(c->lut_h.data(), c->lut, c->lut_h.size() * sizeof(int32_t), hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemcpy(c->owner_h.data(), c->owner, c->owner_h.size() * sizeof(int32_t), hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemcpy(c->last_use.data(), c->d_last_use, c->last_use.size() * sizeof(int64_t), hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemcpy(&c->clock, c->d_clock, sizeof(int64_t), hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemcpy(cnt, c->d_counters, sizeof(cnt), hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemset(c->d_counters, 0, sizeof(cnt))) != hipSuccess)
+    return moe_hip_status(e);
+  for (int i = 0; i < 4; ++i) c->totals[i] += cnt[i];
+  recount_resident(c);
+  return MOE_OK;
+}
+
+// Hand the host tables' LRU state to the device planner (the device tables
+// themselves are already current once the stream runs).
+int push_to_device(moe_layer_ctx* c) {
+  std::vector<int32_t> order(c->S);
+  for (int s = 0; s < c->S; ++s) order[s] = s;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return c->last_use[a] < c->last_use[b]; });
+  hipError_t e = hipStreamSynchronize(c->cs);
+  if (e == hipSuccess) e = hipMemcpy(c->d_order, order.data(), c->S * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(c->d_last_use, c->last_use.data(), c->S * sizeof(int64_t), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(c->d_clock, &c->clock, sizeof(int64_t), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(c->d_counters, 0, 4 * sizeof(int64_t));
+  return moe_hip_status(e);
+}
+
 }  // namespace
 
 extern "C" size_t moe_ctx_workspace_bytes(int t_max, int H, int F, int E, int k, int w_dtype,
@@ -342,6 +537,11 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->window = 1;
   for (double& v : c->params) v = 0.0;
   c->last_ring = -1;
+  c->orch = 0;
+  c->store_dev = nullptr;
+  c->d_order = nullptr;
+  c->d_last_use = c->d_clock = c->d_counters = nullptr;
+  c->d_blob = c->d_fills = c->d_nfills = nullptr;
   c->next_tag = 1;
   c->wave_of.resize(E); c->is_hit.resize(E);
   c->fill_e.resize(E); c->fill_s.resize(E); c->fill_w.resize(E);
@@ -403,9 +603,9 @@ extern "C" int moe_ctx_destroy(moe_layer_ctx* ctx) {
 extern "C" int moe_ctx_place(moe_layer_ctx* c, int slot, int layer, int expert) {
   MOE_CHECK_ARG(c && slot >= 0 && slot < c->S && layer >= 0 && layer < c->L && expert >= 0 &&
                 expert < c->E);
-  MOE_CHECK_ARG(c->lut_h[(size_t)layer * c->E + expert] < 0);
-  int rc = drain(c);
+  int rc = c->orch ? sync_from_device(c) : drain(c);
   if (rc != MOE_OK) return rc;
+  MOE_CHECK_ARG(c->lut_h[(size_t)layer * c->E + expert] < 0);
   // the copy must not overtake kernels that may still read the slot
   if ((rc = fills_after_compute(c)) != MOE_OK) return rc;
   if ((rc = fill_slot(c, slot, layer, expert)) != MOE_OK) return rc;
@@ -415,13 +615,13 @@ extern "C" int moe_ctx_place(moe_layer_ctx* c, int slot, int layer, int expert) 
   c->lut_h[idx] = slot;
   c->owner_h[slot] = idx;
   recount_resident(c);
-  return MOE_OK;
+  return c->orch ? push_to_device(c) : MOE_OK;
 }
 
 extern "C" int moe_ctx_read_tables(moe_layer_ctx* c, int32_t* lut_out, int32_t* owner_out,
                                    int64_t* last_use_out, int64_t* clock_out) {
   MOE_CHECK_ARG(c);
-  const int rc = drain(c);
+  const int rc = c->orch ? sync_from_device(c) : drain(c);
   if (rc != MOE_OK) return rc;
   if (lut_out) memcpy(lut_out, c->lut_h.data(), c->lut_h.size() * sizeof(int32_t));
   if (owner_out) memcpy(owner_out, c->owner_h.data(), c->owner_h.size() * sizeof(int32_t));
@@ -432,7 +632,7 @@ extern "C" int moe_ctx_read_tables(moe_layer_ctx* c, int32_t* lut_out, int32_t* 
 
 extern "C" int moe_ctx_counters(moe_layer_ctx* c, int64_t* out4) {
   MOE_CHECK_ARG(c && out4);
-  const int rc = drain(c);
+  const int rc = c->orch ? sync_from_device(c) : drain(c);
   if (rc != MOE_OK) return rc;
   for (int i = 0; i < 4; ++i) out4[i] = c->totals[i];
   return MOE_OK;
@@ -457,6 +657,7 @@ extern "C" int moe_ctx_ffn_time(moe_layer_ctx* c, double* total_ms, long* steps)
 
 extern "C" int moe_ctx_set_policy(moe_layer_ctx* c, int policy, int window, const double* params) {
   MOE_CHECK_ARG(c);
+  MOE_CHECK_ARG(!c->orch || policy == MOE_POLICY_LRU);  // the device planner runs LRU
   size_t n = 0;
   if (policy != MOE_POLICY_LRU) {
     n = moe_policy_state_doubles(policy, c->L, c->E, window);
@@ -485,6 +686,78 @@ extern "C" int moe_ctx_step_scores(moe_layer_ctx* c, float* scores) {
   return MOE_OK;
 }
 
+extern "C" int moe_ctx_set_orchestration(moe_layer_ctx* c, int mode) {
+  MOE_CHECK_ARG(c && (mode == MOE_ORCH_HOST || mode == MOE_ORCH_DEVICE));
+  if (mode == c->orch) return MOE_OK;
+  if (mode == MOE_ORCH_HOST) {
+    const int rc = sync_from_device(c);
+    if (rc != MOE_OK) return rc;
+    c->orch = 0;
+    return MOE_OK;
+  }
+  MOE_CHECK_ARG(c->S <= kDevPlanMaxS && c->policy == MOE_POLICY_LRU);
+  void* dev = nullptr;
+  if (hipHostGetDevicePointer(&dev, const_cast<void*>(static_cast<const void*>(c->host_store)), 0) !=
+          hipSuccess ||
+      !dev) {
+    (void)hipGetLastError();
+    return MOE_EINVAL;  // the host store must be pinned memory the device can read
+  }
+  c->store_dev = static_cast<const char*>(dev);
+  int rc = drain(c);
+  if (rc != MOE_OK) return rc;
+  if (!c->d_order) {
+    hipError_t e = hipMalloc(&c->d_order, c->S * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc(&c->d_last_use, c->S * sizeof(int64_t));
+    if (e == hipSuccess) e = hipMalloc(&c->d_clock, sizeof(int64_t));
+    if (e == hipSuccess) e = hipMalloc(&c->d_blob, (size_t)c->L * c->E * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc(&c->d_fills, 2 * (size_t)c->E * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc(&c->d_nfills, sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc(&c->d_counters, 4 * sizeof(int64_t));
+    if (e == hipSuccess)
+      e = hipMemcpy(c->d_blob, c->blob_of.data(), c->blob_of.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return moe_hip_status(e);
+  }
+  if ((rc = push_to_device(c)) != MOE_OK) return rc;
+  c->orch = 1;
+  return MOE_OK;
+}
+
+// One layer step planned and filled by the device (T*k <= S): no host wait.
+int forward_device(moe_layer_ctx* c, int layer, const void* x, int T, const void* w_router,
+                   const float* bias, void* out, int out_dtype) {
+  const int E = c->E, k = c->k, H = c->H, F = c->F, nsh = c->n_shared;
+  const int nslots = c->S + nsh;
+  int rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
+                              c->topw, c->counts, c->offsets, c->perm, c->inv, c->dist, c->dist + E,
+                              c->sync, nullptr, nullptr, nullptr, c->cs);
+  if (rc != MOE_OK) return rc;
+  hipLaunchKernelGGL(device_plan_kernel, dim3(1), dim3(1024), 0, c->cs, layer, E, c->S, c->dist,
+                     c->lut, c->owner, c->d_last_use, c->d_clock, c->d_order, c->d_fills,
+                     c->d_nfills, c->d_counters);
+  hipLaunchKernelGGL(device_fill_kernel, dim3(128), dim3(256), 0, c->cs, c->store_dev, c->d_blob,
+                     layer, E, c->pool, c->stride, c->d_fills, c->d_nfills);
+  if ((rc = moe_launch_status()) != MOE_OK) return rc;
+  const bool timing = c->timing != 0;
+  hipError_t e;
+  if (timing) {
+    collect_timing(c, false);
+    const int tr = (c->t_head + c->t_count) % kRing;
+    if ((e = hipEventRecord(c->tev0[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
+  }
+  if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, c->lut + (size_t)layer * E, nullptr, nsh,
+                       c->S, c->pool, c->stride, nslots, c->w_dtype, T, H, F, E, k, c->y_perm,
+                       c->err, c->ws, c->ws_bytes, c->cs)) != MOE_OK)
+    return rc;
+  if (timing) {
+    const int tr = (c->t_head + c->t_count) % kRing;
+    if ((e = hipEventRecord(c->tev1[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
+    c->t_count += 1;
+  }
+  const float* shared_y = nsh ? c->y_perm + (size_t)T * k * H : nullptr;
+  return moe_combine(c->y_perm, c->inv, c->topw, T, k, H, shared_y, c->n_shared, out, out_dtype, c->cs);
+}
+
 extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int T,
                                  const void* w_router, const float* bias, void* out, int out_dtype,
                                  int32_t* stats) {
@@ -510,6 +783,11 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
                             hipMemcpyHostToDevice, c->cs)) != hipSuccess)
       return moe_hip_status(e);
     c->sh_T = T;
+  }
+  if (c->orch) {
+    if (T * k > c->S) return MOE_EUNSUPPORTED;  // more routed experts than slots: plan on the host
+    if (stats) stats[0] = stats[1] = stats[2] = stats[3] = -1;
+    return forward_device(c, layer, x, T, w_router, bias, out, out_dtype);
   }
   const int nslots = c->S + nsh;
   // the routed set is written by the device into the next ring entry (pinned host memory)

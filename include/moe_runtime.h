@@ -124,6 +124,28 @@ int moe_ctx_set_policy(moe_layer_ctx* ctx, int policy, int window, const double*
  * step. */
 int moe_ctx_step_scores(moe_layer_ctx* ctx, float* scores);
 
+/* moe_ctx_set_orchestration: where the residency plan runs.
+ *   MOE_ORCH_HOST (default): the host plans each step that may miss, after
+ *     reading the routed set, and the fills are DMA copies on the fill stream.
+ *   MOE_ORCH_DEVICE: the GPU plans and fills by itself and a step never waits
+ *     for the host (SeqMoE summary page, Mechanism: the device owns the cache
+ *     metadata and starts the miss copy from a kernel out of the pinned,
+ *     mapped host pool). One workgroup runs the LRU plan of moe_plan_fills on
+ *     the device tables (identical tables and fills); a kernel then copies the
+ *     missed experts from the host store (which must be hipHostMalloc memory
+ *     the device can map) into their slots; the expert FFN and the combine
+ *     follow on the compute stream. Needs S <= 4096 and the LRU policy; a step
+ *     with T*k > S returns MOE_EUNSUPPORTED (switch back to the host to run
+ *     it). The per-step stats of moe_layer_forward are -1 in this mode; the
+ *     totals of moe_ctx_counters and the tables of moe_ctx_read_tables are
+ *     read back from the device (a stream synchronisation).
+ * Switching hands the tables over (host -> device: the slots' LRU order and
+ * clock; device -> host: everything). The first switch to the device
+ * allocates the device planner's state (a few KB per slot) once. */
+#define MOE_ORCH_HOST 0
+#define MOE_ORCH_DEVICE 1
+int moe_ctx_set_orchestration(moe_layer_ctx* ctx, int mode);
+
 /* moe_ctx_set_timing: when enabled, each step records HIP events on the
  * compute stream around its expert FFN calls (the routed groups, including
  * any fill waves, then the shared experts); moe_ctx_ffn_time

@@ -294,15 +294,19 @@ def test_slot_fill_rejects_pageable_host_memory():
 
 
 # --------------------------------------------------------------- whole layer --
-def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, policy=None):
+def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, policy=None,
+                    device_plan=False):
     """Run steps through the harness and compare every step with the oracle.
 
     policy = (kind, window, params): the runtime plans under that eviction policy and the
     oracle's scored planner records the same step scores (the kernel's own, checked against
-    the oracle's softmax of the kernel's logits) before each plan."""
+    the oracle's softmax of the kernel's logits) before each plan.
+    device_plan: the runtime plans and fills on the GPU (device orchestration)."""
     t_max = max(Ts)
     residency = W.initial_residency(shape, slots, mode)
     layer_obj = Hn.SlotCacheLayer(shape, slots, residency, t_max)
+    if device_plan:
+        layer_obj.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
     if policy is None:
         planner = O.LruSlotPlanner(slots, shape.layers, shape.E, residency)
     else:
@@ -378,6 +382,52 @@ def test_layer_policy_history_shared_experts():
     shape = W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), E=16, k=6, H=256, F=256)
     _run_layer_case(shape, 8, "zipf_rank", [1, 2, 32, 1, 5, 3],
                     policy=(B.MOE_POLICY_HISTORY, 6, [1.0, 0.5, 2.0, 0.25, 0.8]))
+
+
+def test_layer_stack_device_orchestration():
+    shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=3, E=16, k=4, H=256,
+                      F=128, blobs=16)
+    _run_layer_case(shape, 14, "zipf_rank", [1, 3, 1, 2, 1, 3], layers_order=[0, 1, 2], device_plan=True)
+
+
+def test_layer_device_orchestration_shared_experts_int4():
+    shape = W.reduced(DSV3, E=32, k=8, H=256, F=128)
+    _run_layer_case(shape, 12, "zipf_rank", [1, 1, 1, 1], device_plan=True)
+
+
+def test_device_orchestration_hands_tables_back_and_forth():
+    """Host plans, then device plans, then host again: the tables follow one LRU history."""
+    shape = W.reduced(MIX, E=12, k=3, H=256, F=256)
+    slots = 5
+    residency = W.initial_residency(shape, slots, "random")
+    layer_obj = Hn.SlotCacheLayer(shape, slots, residency, 4)
+    planner = O.LruSlotPlanner(slots, 1, shape.E, residency)
+    n_distinct = n_fills = 0
+    for step, T in enumerate([1, 1, 1, 1, 1, 1]):
+        layer_obj.ctx.set_orchestration(B.MOE_ORCH_DEVICE if step in (2, 3) else B.MOE_ORCH_HOST)
+        say(f"handoff step={step}")
+        x = W.tokens(shape, T, step=step, device=_dev())
+        layer_obj.forward(x)
+        torch.cuda.synchronize()
+        ids = layer_obj.outputs(T)["ids"].cpu().numpy()
+        distinct = O.permute(ids, shape.E)["distinct"]
+        waves = planner.plan(0, distinct)
+        n_distinct += len(distinct)
+        n_fills += sum(len(w.fills) for w in waves)
+        lut_h, _, last_use_h, clock_h = layer_obj.tables()
+        assert lut_h.tolist() == planner.lut[0].tolist()
+        assert last_use_h.tolist() == planner.last_use and clock_h == planner.clock
+    cnt = layer_obj.counters()
+    assert cnt["distinct"] == n_distinct and cnt["fills"] == n_fills
+
+
+def test_device_orchestration_rejects_more_routed_than_slots():
+    shape = W.reduced(MIX, E=12, k=3, H=256, F=256)
+    layer_obj = Hn.SlotCacheLayer(shape, 4, W.initial_residency(shape, 4, "random"), 8)
+    layer_obj.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
+    x = W.tokens(shape, 2, step=0, device=_dev())  # T*k = 6 > 4 slots
+    with pytest.raises(B.MoeError):
+        layer_obj.forward(x)
 
 
 def test_layer_shared_experts():
