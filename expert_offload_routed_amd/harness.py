@@ -56,7 +56,7 @@ class SlotCacheLayer:
     """
 
     def __init__(self, shape: W.MoEShape, slots: int, residency: list, t_max: int,
-                 store: ExpertStore | None = None, device="cuda"):
+                 store: ExpertStore | None = None, device="cuda", compute_stream=None):
         self.shape, self.S, self.t_max, self.device = shape, slots, t_max, device
         sh = shape
         self.E, self.k, self.H, self.F, self.L = sh.E, sh.k, sh.H, sh.F, sh.layers
@@ -83,7 +83,7 @@ class SlotCacheLayer:
             t_max=t_max, H=self.H, F=self.F, E=self.E, k=self.k, L=self.L, S=slots, x_dtype=xcode,
             w_dtype=self.wcode, n_shared=self.n_sh, pool=self.pool, slot_stride=self.stride,
             lut=self.lut, owner=self.owner, tags=self.tags, host_store=self.store.host,
-            blob_of=blob_of, shared_pool=self.sh_pool, err=self.err)
+            blob_of=blob_of, shared_pool=self.sh_pool, err=self.err, compute_stream=compute_stream)
         for s, o in enumerate(residency):
             if o is not None:
                 self.ctx.place(s, o[0], o[1])

@@ -421,6 +421,53 @@ def test_device_orchestration_hands_tables_back_and_forth():
     assert cnt["distinct"] == n_distinct and cnt["fills"] == n_fills
 
 
+def test_device_orchestrated_stack_step_replays_as_a_graph():
+    """A whole stack step (every layer) planned and filled on the device is captured once and
+    replayed; between replays the inputs change in place (so replays miss and fill). Every
+    replay equals an eager device-orchestrated context fed the same inputs."""
+    shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=3, E=16, k=4, H=256,
+                      F=128, blobs=16)
+    slots, T, L = 14, 1, shape.layers
+    residency = W.initial_residency(shape, slots, "zipf_rank")
+    s = torch.cuda.Stream()
+    graphed = Hn.SlotCacheLayer(shape, slots, residency, T, compute_stream=s)
+    eager = Hn.SlotCacheLayer(shape, slots, residency, T, store=graphed.store)
+    for lay in (graphed, eager):
+        lay.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
+    xs = [W.tokens(shape, T, layer=l, step=0, device=_dev()) for l in range(L)]
+    outs_g = [torch.empty(T, shape.H, dtype=graphed.out_dtype, device=_dev()) for _ in range(L)]
+    outs_e = [torch.empty_like(o) for o in outs_g]
+
+    def stack_step(lay, outs):
+        for l in range(L):
+            lay.forward(xs[l], layer=l, out=outs[l])
+
+    with torch.cuda.stream(s):
+        stack_step(graphed, outs_g)  # eager first step (per-T set-up stays out of the graph)
+    stack_step(eager, outs_e)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        stack_step(graphed, outs_g)
+    torch.cuda.synchronize()  # the capture ran nothing: both contexts have done step 0 once
+    for rep in range(5):
+        say(f"graph replay {rep}")
+        for l in range(L):  # eager work between replays: new inputs, in place
+            xs[l].copy_(W.tokens(shape, T, layer=l, step=rep + 1, device=_dev()))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        stack_step(eager, outs_e)
+        torch.cuda.synchronize()
+        assert graphed.err.item() == 0 and eager.err.item() == 0
+        for l in range(L):
+            assert torch.equal(outs_g[l], outs_e[l]), (rep, l)
+        tg, te = graphed.tables(), eager.tables()
+        assert tg[0].tolist() == te[0].tolist() and tg[2].tolist() == te[2].tolist() and tg[3] == te[3]
+    cg, ce = graphed.counters(), eager.counters()
+    assert cg == ce and cg["fills"] > 0
+
+
 def test_device_orchestration_rejects_more_routed_than_slots():
     shape = W.reduced(MIX, E=12, k=3, H=256, F=256)
     layer_obj = Hn.SlotCacheLayer(shape, 4, W.initial_residency(shape, 4, "random"), 8)
