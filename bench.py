@@ -249,6 +249,56 @@ def fill_cases(shape, plan, cfg, store, steps, warmup):
     return out
 
 
+def graph_case(shape, plan, cfg, store, steps, warmup):
+    """Every cache with fills under device orchestration, eager and as one captured HIP graph
+    per stack step (inputs for each step copied into the graph's static input buffer with one
+    copy, inside the timed region)."""
+    for S, T in plan["miss"]:
+        if T * shape.k > S:
+            continue
+        for graphed in (False, True):
+            s = torch.cuda.Stream()
+            lay = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]), t_max=T,
+                                    store=store, compute_stream=s)
+            lay.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
+            batches = make_batches(shape, T, steps + warmup)
+            X = torch.stack([torch.stack([x for _, x in b]) for b in batches])  # [steps, L, T, H]
+            xin = torch.empty_like(X[0])
+            outs = [torch.empty(T, shape.H, dtype=lay.out_dtype, device="cuda") for _ in range(shape.layers)]
+
+            def step():
+                for l in range(shape.layers):
+                    lay.forward(xin[l], layer=l, out=outs[l])
+
+            g = None
+            with torch.cuda.stream(s):
+                for i in range(warmup):
+                    xin.copy_(X[i])
+                    step()
+            torch.cuda.synchronize()
+            if graphed:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    step()
+                torch.cuda.synchronize()
+            c0 = lay.counters()
+            t0 = time.perf_counter()
+            with torch.cuda.stream(s):
+                for i in range(warmup, warmup + steps):
+                    xin.copy_(X[i])
+                    g.replay() if graphed else step()
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            c1 = lay.counters()
+            res = {"tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3,
+                   "fills_per_step": (c1["fills"] - c0["fills"]) / steps,
+                   "hit_rate": (c1["hits"] - c0["hits"]) / max(1, c1["distinct"] - c0["distinct"])}
+            print(f"# T={T}, {S} slots, device orchestration, {'graph' if graphed else 'eager'}: {res}",
+                  file=sys.stderr, flush=True)
+            del lay, g
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,7 +310,8 @@ def main():
     ap.add_argument("--case", default=None,
                     help="one case only, for profiling (prints no JSON line): decode1, decode8, "
                          "prefill512, fills, policies (every cache with fills under each eviction "
-                         "policy), T<n> (hit path at n tokens), calib_copy")
+                         "policy), graph (device orchestration, eager vs one HIP graph per step), "
+                         "T<n> (hit path at n tokens), calib_copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU form of "
@@ -282,6 +333,8 @@ def main():
     if args.case is not None:
         if args.case == "policies":
             fill_cases(shape, plan, cfg, store, K, Wm)
+        elif args.case == "graph":
+            graph_case(shape, plan, cfg, store, K, Wm)
         elif args.case == "fills":
             S, T = plan["miss"][0]
             small = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]),

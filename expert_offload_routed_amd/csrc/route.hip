@@ -29,7 +29,11 @@ namespace {
 
 constexpr int kRouteTT = 8;   // tokens per workgroup
 constexpr int kTopkMaxV = 16; // logits per lane (E <= 1024)
-constexpr int kFrontMaxT = 16; // tokens of the one-launch decode front end
+// The one-launch decode front end is used up to 4 tokens and 128 experts: measured against the
+// separate logits, top-k and permutation kernels it is faster there and slower beyond (at 16
+// tokens and 128 experts 45 us against 22 us; at 256 experts already from one token).
+constexpr int kFrontMaxT = 4;
+constexpr int kFrontMaxE = 128;
 
 template <int FMT>
 __device__ __forceinline__ void load8(const void* base, size_t elem, float out[8]) {
@@ -621,7 +625,7 @@ int route_permute_plan(const void* x, int x_dtype, const void* w_router, const f
   MOE_CHECK_ARG(k >= 1 && k <= E && E <= 64 * kTopkMaxV);
   MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
   MOE_CHECK_ARG(counts && offsets && distinct && n_distinct && sync_counter);
-  if (T > kFrontMaxT || T * k > 1024 || T == 0) {
+  if (T > kFrontMaxT || E > kFrontMaxE || T * k > 1024 || T == 0) {
     int rc = moe_route(x, x_dtype, w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w,
                        stream);
     if (rc != MOE_OK) return rc;
@@ -643,8 +647,8 @@ int route_permute_plan(const void* x, int x_dtype, const void* w_router, const f
   }
   // code specialised to the token count and logits per lane: the front end runs once per step,
   // from a cold instruction cache, so it should hold only the code the step needs
-  const int maxt = T <= 1 ? 1 : (T <= 4 ? 4 : 16);
-  const int nv = E <= 64 ? 1 : (E <= 128 ? 2 : (E <= 256 ? 4 : 16));
+  const int maxt = T <= 1 ? 1 : kFrontMaxT;
+  const int nv = E <= 64 ? 1 : 2;
 #define MOE_FRONT(FMT_, MAXT_, NV_)                                                               \
   do {                                                                                           \
     if (single)                                                                                  \
@@ -659,17 +663,13 @@ int route_permute_plan(const void* x, int x_dtype, const void* w_router, const f
 #define MOE_FRONT_NV(FMT_, MAXT_)                   \
   do {                                              \
     if (nv == 1) MOE_FRONT(FMT_, MAXT_, 1);         \
-    else if (nv == 2) MOE_FRONT(FMT_, MAXT_, 2);    \
-    else if (nv == 4) MOE_FRONT(FMT_, MAXT_, 4);    \
-    else MOE_FRONT(FMT_, MAXT_, kTopkMaxV);         \
+    else MOE_FRONT(FMT_, MAXT_, 2);                 \
   } while (0)
   if (x_dtype == MOE_BF16) {
     if (maxt == 1) MOE_FRONT_NV(MOE_BF16, 1);
-    else if (maxt == 4) MOE_FRONT_NV(MOE_BF16, 4);
     else MOE_FRONT_NV(MOE_BF16, kFrontMaxT);
   } else {
     if (maxt == 1) MOE_FRONT_NV(MOE_F32, 1);
-    else if (maxt == 4) MOE_FRONT_NV(MOE_F32, 4);
     else MOE_FRONT_NV(MOE_F32, kFrontMaxT);
   }
 #undef MOE_FRONT_NV
