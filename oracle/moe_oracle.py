@@ -8,6 +8,11 @@ Sources, cited by page title and section:
               Offloading for Large-Scale MoE Inference", Sec. 2.1 (gating,
               top-k, weighted sum), Algorithm 1 (weighted sum over the routed
               experts), Sec. 4.4-4.5 and Eq. (7) (SwiGLU expert).
+              Sec. 4.2 and Eqs. (3)-(5) (critical set by a multi-modulated
+              threshold on the router scores), Algorithm 1 (critical experts
+              on high-precision weights, the rest on low-precision ones),
+              Sec. 4.4 and Algorithm 3 (residual split of gate/up, two
+              separate quantisations of down).
   [CAP]       "Communication-Aware Placement and Pruning for Efficient
               Mixture-of-Experts Inference", Sec. II-A, Eq. (1) (normalised
               routing weights).
@@ -54,6 +59,8 @@ __all__ = [
     "quantize_rows_int8", "swiglu_expert_w4a8", "expert_forward", "combine",
     "SlotPool", "LruSlotPlanner", "Wave", "route", "moe_layer",
     "step_scores", "MinusRecentScore", "RoutingHistoryScore", "ScoredSlotPlanner",
+    "round_bf16", "quantize_sym_g128", "resplit_expert", "critical_threshold",
+    "critical_experts", "swiglu_expert_split",
 ]
 
 
@@ -507,6 +514,90 @@ class ScoredSlotPlanner(LruSlotPlanner):
     def plan(self, layer: int, distinct, scores=None) -> list[Wave]:
         self.policy.observe(layer, scores, distinct)
         return super().plan(layer, distinct)
+
+
+# ------------------------------------------------- split-precision experts ---
+def round_bf16(a) -> np.ndarray:
+    """float32 -> nearest bfloat16 (ties to even), returned as float32 values."""
+    u = np.ascontiguousarray(as_f32(a)).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def quantize_sym_g128(w, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """Symmetric b-bit quantisation in groups of 128 along K of w [rows, K]:
+    s = bf16(max|w_group| / (2^(b-1) - 1)), q = clip(rint(w / s), -2^(b-1), 2^(b-1) - 1),
+    q = 0 where s = 0. The division and rounding that decide q are float32 (the
+    4-bit rule of the int4 workload, widened to b bits for the residual split).
+    Returns q int8 [rows, K] and s float32 [rows, K/128] (bf16 values)."""
+    w32 = as_f32(w)
+    rows, K = w32.shape
+    g = w32.reshape(rows, K // 128, 128)
+    qmax = np.float32(2 ** (bits - 1) - 1)
+    s = round_bf16(np.max(np.abs(g), axis=2) / qmax)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint(g / s[:, :, None])
+    q = np.where(s[:, :, None] == 0, 0, np.clip(q, -2 ** (bits - 1), 2 ** (bits - 1) - 1))
+    return q.reshape(rows, K).astype(np.int8), s
+
+
+def _deq(q, s) -> np.ndarray:
+    return q.astype(np.float64) * np.repeat(s.astype(np.float64), 128, axis=1)
+
+
+def resplit_expert(gate, up, down, bq: int = 4, br: int = 4) -> dict:
+    """[RapidMoE] Algorithm 3 (RESplit): gate and up are quantised to b_q bits
+    (W^Q) and their residual W - W^Q to b_r bits (W^R), so W^H = W^Q + W^R and
+    W^L = W^Q; down is quantised twice, to b_q bits (W^L) and to b_q + b_r bits
+    (W^H). The residual is formed in float32 from the float32 weights.
+    Returns int8 code arrays and float32 (bf16-valued) scales per part."""
+    out = {}
+    for name, w in (("gate", gate), ("up", up)):
+        q, s = quantize_sym_g128(w, bq)
+        r = as_f32(w) - (q.astype(np.float32) * np.repeat(s, 128, axis=1))
+        rq, rs = quantize_sym_g128(r, br)
+        out[name + "_q"], out[name + "_s"], out[name + "_rq"], out[name + "_rs"] = q, s, rq, rs
+    out["down_lq"], out["down_ls"] = quantize_sym_g128(down, bq)
+    out["down_hq"], out["down_hs"] = quantize_sym_g128(down, bq + br)
+    return out
+
+
+def critical_threshold(theta: float, beta_l: float, phase: str, alpha: float) -> float:
+    """[RapidMoE] Eqs. (3) and (5): Theta(l, t) = Theta * beta(l) * gamma(t), with
+    gamma = 1 for prefill and alpha for decode."""
+    gamma = {"prefill": 1.0, "decode": alpha}[phase]
+    return theta * beta_l * gamma
+
+
+def critical_experts(scores, distinct, threshold) -> list[int]:
+    """[RapidMoE] Eq. (4) with Algorithm 1: the routed experts whose router score
+    (softmax probability, averaged over the step's tokens for several tokens)
+    is at least the threshold. The comparison is float32 (the kernels'), since
+    it decides set membership."""
+    sc = as_f32(scores)
+    th = np.float32(threshold)
+    return [int(e) for e in distinct if sc[int(e)] >= th]
+
+
+def swiglu_expert_split(x_rows, w: dict, critical: bool) -> np.ndarray:
+    """[RapidMoE] Algorithm 1 and Eq. (7): a critical expert runs on
+    W^H (gate, up = W^Q + W^R; down = its b_q + b_r bit quantisation), any other
+    routed expert on W^L (= W^Q; down at b_q bits). Activations are the int8
+    rows of the int4 workload (x and the SwiGLU intermediate quantised per row);
+    products in float64 on exactly dequantised weights."""
+    qx, sx = quantize_rows_int8(x_rows)
+    xh = qx.astype(np.float64) * sx.astype(np.float64)[:, None]
+    def wg(name):
+        W = _deq(w[name + "_q"], w[name + "_s"])
+        return W + _deq(w[name + "_rq"], w[name + "_rs"]) if critical else W
+    g = xh @ wg("gate").T
+    u = xh @ wg("up").T
+    with np.errstate(over="ignore"):
+        h = silu(g) * u
+    qh, sh = quantize_rows_int8(h.astype(np.float32))
+    hh = qh.astype(np.float64) * sh.astype(np.float64)[:, None]
+    down = _deq(w["down_hq"], w["down_hs"]) if critical else _deq(w["down_lq"], w["down_ls"])
+    return hh @ down.T
 
 
 # ------------------------------------------------------------- full layer ---

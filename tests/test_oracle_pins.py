@@ -447,3 +447,93 @@ def test_scored_planner_invariants_random_multilayer():
             assert o is None or p.lut[o] == s
         if len(U) <= S:
             assert all(p.lut[layer, e] >= 0 for e in U)
+
+
+# ------------------------------------------------ split-precision experts ---
+def test_round_bf16_matches_torch_including_ties():
+    rng = np.random.default_rng(31)
+    a = rng.normal(size=4096).astype(np.float32) * np.float32(3.0)
+    hi = rng.integers(0, 1 << 16, size=512, dtype=np.uint32) << 16
+    ties = (hi | np.uint32(0x8000)).view(np.float32)            # exactly halfway
+    ties = ties[np.isfinite(ties)]
+    for v in (a, ties):
+        want = torch.tensor(v).to(torch.bfloat16).to(torch.float32).numpy()
+        np.testing.assert_array_equal(O.round_bf16(v), want)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantize_sym_g128_bounds(bits):
+    rng = np.random.default_rng(32 + bits)
+    w = (rng.normal(size=(6, 512)) * 0.02).astype(np.float32)
+    w[2, 128:256] = 0.0                                     # an all-zero group
+    q, s = O.quantize_sym_g128(w, bits)
+    qmax = 2 ** (bits - 1) - 1
+    g = w.reshape(6, 4, 128)
+    absmax = np.abs(g).max(axis=2)
+    want_s = torch.tensor(absmax / np.float32(qmax)).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(s, want_s)
+    assert q.min() >= -qmax - 1 and q.max() <= qmax
+    assert not q.reshape(6, 4, 128)[2, 1].any() and s[2, 1] == 0
+    recon = q.reshape(6, 4, 128).astype(np.float64) * s[:, :, None]
+    err = np.abs(recon - g)
+    clipped = np.abs(q.reshape(6, 4, 128)) >= qmax
+    assert np.all(err[~clipped] <= s[:, :, None].repeat(128, 2)[~clipped] * 0.5 * (1 + 1e-6))
+    # the largest element of every nonzero group lands on the edge of the code range
+    edge = np.abs(q.reshape(6, 4, 128)).max(axis=2)
+    assert set(np.unique(edge[absmax > 0]).tolist()) <= {qmax, qmax + 1}
+
+
+def test_resplit_residual_and_dual_down():
+    rng = np.random.default_rng(34)
+    H, F = 256, 128
+    gate = (rng.normal(size=(F, H)) * 0.02).astype(np.float32)
+    up = (rng.normal(size=(F, H)) * 0.02).astype(np.float32)
+    down = (rng.normal(size=(H, F)) * 0.02).astype(np.float32)
+    w = O.resplit_expert(gate, up, down)
+    for name, W in (("gate", gate), ("up", up)):
+        wq = w[name + "_q"].astype(np.float64) * np.repeat(w[name + "_s"], 128, 1)
+        wr = w[name + "_rq"].astype(np.float64) * np.repeat(w[name + "_rs"], 128, 1)
+        e_low = np.abs(W - wq).mean()
+        e_high = np.abs(W - (wq + wr)).mean()
+        assert e_high < e_low / 8                         # the residual compensates the error
+        assert np.all(np.abs(W - (wq + wr)) <= np.repeat(w[name + "_rs"], 128, 1) * 0.5 * (1 + 1e-6) + 1e-12)
+    assert np.array_equal(w["down_lq"], O.quantize_sym_g128(down, 4)[0])
+    dh = w["down_hq"].astype(np.float64) * np.repeat(w["down_hs"], 128, 1)
+    dl = w["down_lq"].astype(np.float64) * np.repeat(w["down_ls"], 128, 1)
+    assert np.abs(down - dh).mean() < np.abs(down - dl).mean() / 8
+
+
+def test_critical_threshold_and_set():
+    assert O.critical_threshold(0.1, 2.0, "prefill", 1.5) == pytest.approx(0.2)
+    assert O.critical_threshold(0.1, 2.0, "decode", 1.5) == pytest.approx(0.3)
+    scores = np.array([0.05, 0.30, 0.15, 0.29999], dtype=np.float32)
+    assert O.critical_experts(scores, [0, 1, 2, 3], 0.0) == [0, 1, 2, 3]
+    assert O.critical_experts(scores, [0, 1, 2, 3], 1.01) == []
+    assert O.critical_experts(scores, [1, 2, 3], 0.3) == [1]        # >= includes the boundary
+    assert O.critical_experts(scores, [0, 2], 0.1) == [2]           # only routed experts
+
+
+def _pack_codes(q):
+    """int8 codes [rows, K] -> packed signed nibbles [rows, K/2] (even index low)."""
+    u = (q.astype(np.int16) & 0xF).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_split_low_path_is_the_int4_expert_and_high_path_closer_to_dense():
+    rng = np.random.default_rng(35)
+    H, F, T = 256, 128, 5
+    gate, up, down = ((rng.normal(size=s) * 0.05).astype(np.float32) for s in ((F, H), (F, H), (H, F)))
+    w = O.resplit_expert(gate, up, down)
+    x = rng.normal(size=(T, H)).astype(np.float32)
+    low = O.swiglu_expert_split(x, w, critical=False)
+    w4 = {"gate_q": _pack_codes(w["gate_q"]), "gate_s": w["gate_s"], "up_q": _pack_codes(w["up_q"]),
+          "up_s": w["up_s"], "down_q": _pack_codes(w["down_lq"]), "down_s": w["down_ls"]}
+    np.testing.assert_array_equal(low, O.swiglu_expert_w4a8(x, w4))
+    # a zero residual and an equal down make the two paths identical
+    wz = dict(w, gate_rq=np.zeros_like(w["gate_rq"]), up_rq=np.zeros_like(w["up_rq"]),
+              down_hq=w["down_lq"], down_hs=w["down_ls"])
+    np.testing.assert_array_equal(O.swiglu_expert_split(x, wz, True), low)
+    dense = O.swiglu_expert(x, gate, up, down)
+    high = O.swiglu_expert_split(x, w, critical=True)
+    r = lambda a: np.linalg.norm(a - dense) / np.linalg.norm(dense)
+    assert r(high) < r(low) / 2
