@@ -299,6 +299,65 @@ def graph_case(shape, plan, cfg, store, steps, warmup):
             torch.cuda.empty_cache()
 
 
+def split_bytes(shape) -> tuple[int, int]:
+    """Algorithmic bytes one split-precision expert streams at low (W^L: int4 gate/up/down) and
+    at high precision (W^H: int4 gate/up and their int4 residual, 8-bit down), scales included."""
+    H, F = shape.H, shape.F
+    s13, s2 = 2 * F * (H // 128) * 2, H * (F // 128) * 2
+    low = 2 * F * H // 2 + s13 + H * F // 2 + s2
+    high = 2 * (2 * F * H // 2 + s13) + H * F + s2
+    return low, high
+
+
+def split_case(shape, store, T, steps, warmup, critical_share=0.25):
+    """Split-precision routing on the hit path (every expert resident): every routed expert at
+    low precision, the split (theta set so that about `critical_share` of the routed experts of
+    the calibration steps are critical), and every expert at high precision. For each: tokens/s,
+    the expert FFN's HIP-event time and its algorithmic bytes from the counted critical groups."""
+    layer = Hn.SlotCacheLayer(shape, shape.E, all_resident(shape), t_max=T, store=store)
+    batches = make_batches(shape, T, steps + warmup)
+    out = torch.empty(T, shape.H, dtype=layer.out_dtype, device="cuda")
+    # calibration: the routed experts' scores over the warm-up batches
+    layer.ctx.set_split(True, 0.0)
+    routed_scores = []
+    for b in batches[:warmup]:
+        layer.forward(b[0][1], out=out)
+        sc = layer.ctx.step_scores()
+        ids = np.unique(layer.outputs(T)["ids"].cpu().numpy())
+        routed_scores += sc[ids].tolist()
+    theta = float(np.quantile(routed_scores, 1.0 - critical_share))
+    low_b, high_b = split_bytes(shape)
+    res = {"theta": theta, "expert_bytes_low": low_b, "expert_bytes_high": high_b}
+    for mode, th in (("all_low", float("inf")), ("split", theta), ("all_high", 0.0)):
+        if np.isinf(th):
+            layer.ctx.set_split(True, 3.0e38)
+        else:
+            layer.ctx.set_split(True, th)
+        _run(layer, batches[:warmup], out, False)
+        dt, _, _, _ = _run(layer, batches[warmup:], out, False)
+        _, _, ms, n = _run(layer, batches[warmup:], out, True)
+        # critical groups per step, counted on the same batches (one host read per step)
+        n_hi = n_lo = 0
+        for b in batches[warmup:]:
+            layer.forward(b[0][1], out=out)
+            sc = layer.ctx.step_scores()
+            ids = np.unique(layer.outputs(T)["ids"].cpu().numpy())
+            hi = int(np.sum(sc[ids] >= np.float32(3.0e38 if np.isinf(th) else th)))
+            n_hi += hi
+            n_lo += len(ids) - hi
+        us = 1e3 * ms / n
+        per_call = (n_lo * low_b + n_hi * high_b) / steps + shape.n_shared * high_b \
+            + T * shape.H * _xbytes(shape) + T * (shape.k + shape.n_shared) * shape.H * 4
+        r = {"tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3,
+             "critical_per_step": n_hi / steps, "low_per_step": n_lo / steps,
+             "ffn": {"avg_us": us, "bytes_per_call": per_call, "gbs": per_call / (us * 1e-6) / 1e9}}
+        print(f"# T={T} split precision, {mode}: {r}", file=sys.stderr, flush=True)
+        res[mode] = r
+    del layer
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,7 +370,9 @@ def main():
                     help="one case only, for profiling (prints no JSON line): decode1, decode8, "
                          "prefill512, fills, policies (every cache with fills under each eviction "
                          "policy), graph (device orchestration, eager vs one HIP graph per step), "
-                         "T<n> (hit path at n tokens), calib_copy")
+                         "split (split-precision experts: all low, split, all high; the "
+                         "workload's shape with split-precision slots and 16 distinct weight "
+                         "sets), T<n> (hit path at n tokens), calib_copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU form of "
@@ -325,6 +386,14 @@ def main():
     shape = W.shape_of(args.workload)
     plan = PLANS[args.workload]
     cfg = W.WORKLOADS[args.workload]
+    if args.case == "split":
+        # fp32 masters quantised by the library; 16 weight sets back the E slots (each slot
+        # its own memory, so the HBM traffic is that of E distinct experts)
+        sshape = W.reduced(shape, wfmt="int4g128_resplit", blobs=16, name=shape.name + "_resplit")
+        sstore = Hn.ExpertStore(sshape)
+        for T in (1, 32):
+            split_case(sshape, sstore, T, K, Wm)
+        return
     t_max = max(plan["hit"])
     store = Hn.ExpertStore(shape)
     resident = all_resident(shape)

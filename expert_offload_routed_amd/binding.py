@@ -17,7 +17,7 @@ import torch
 
 from .build import LIB_PATH
 
-MOE_F32, MOE_BF16, MOE_INT4G128 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_INT4G128, MOE_INT4G128_RESPLIT = 0, 1, 2, 3
 MOE_ERR_ABSENT, MOE_ERR_STALE_TAG = 1, 2
 _STATUS = {-1: "invalid argument", -2: "unsupported dtype or shape", -3: "HIP runtime error"}
 
@@ -29,6 +29,10 @@ _SIGNATURES = {
     "moe_route_permute": (_i32, [_vp, _i32, _vp, _vp] + [_i32] * 5 + [_vp] * 11),
     "moe_slot_layout": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_pack_expert_host": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
+    "moe_slot_layout_resplit": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp]),
+    "moe_quantize_resplit_host": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp]),
+    "moe_critical_split": (_i32, [_vp, _i32, ctypes.c_float, _vp, _i32, _vp, _vp]),
+    "moe_step_scores": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "moe_ffn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _i32, _i32, _i32, _i32,
                               _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
@@ -56,6 +60,7 @@ _SIGNATURES = {
     "moe_ctx_set_policy": (_i32, [_vp, _i32, _i32, _vp]),
     "moe_ctx_set_orchestration": (_i32, [_vp, _i32]),
     "moe_ctx_step_scores": (_i32, [_vp, _vp]),
+    "moe_ctx_set_split": (_i32, [_vp, _i32, ctypes.c_float, _vp, ctypes.c_float]),
     "moe_ctx_counters": (_i32, [_vp, _vp]),
     "moe_ctx_ffn_time": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_long)]),
 }
@@ -207,6 +212,43 @@ def moe_slot_layout(H: int, F: int, w_dtype: int) -> dict:
     vals = [ctypes.c_size_t() for _ in range(5)]
     _call("moe_slot_layout", H, F, w_dtype, *[ctypes.addressof(v) for v in vals])
     return dict(zip(("slot_bytes", "off_w13", "off_w2", "off_s13", "off_s2"), (v.value for v in vals)))
+
+
+def moe_slot_layout_resplit(H: int, F: int) -> dict:
+    vals = [ctypes.c_size_t() for _ in range(4)]
+    _call("moe_slot_layout_resplit", H, F, *[ctypes.addressof(v) for v in vals])
+    return dict(zip(("off_r13", "off_rs13", "off_h2", "off_hs2"), (v.value for v in vals)))
+
+
+def moe_quantize_resplit_host(gate, up, down, H: int, F: int, dst) -> None:
+    """Quantise one expert from float32 host tensors (nn.Linear orientation) into a
+    MOE_INT4G128_RESPLIT slot image dst (host uint8, slot bytes)."""
+    ts = [t.detach().to("cpu", torch.float32).contiguous() for t in (gate, up, down)]
+    if (tuple(ts[0].shape) != (F, H) or tuple(ts[1].shape) != (F, H)
+            or tuple(ts[2].shape) != (H, F)):
+        raise ValueError("moe_quantize_resplit_host: gate, up must be [F, H] and down [H, F]")
+    _call("moe_quantize_resplit_host", *[_host(t) for t in ts], H, F, _host(dst))
+
+
+def moe_step_scores(logits, T: int, E: int, scores=None, stream=None):
+    if scores is None:
+        scores = torch.empty(E, device=logits.device, dtype=torch.float32)
+    if logits.numel() < T * E or scores.numel() < E:
+        raise ValueError("moe_step_scores: an argument is smaller than its shape needs")
+    _call("moe_step_scores", _dev(logits), T, E, _dev(scores), _stream(stream))
+    return scores
+
+
+def moe_critical_split(scores, E: int, threshold: float, mask_in=None, rows: int = 1,
+                       mask_out=None, stream=None):
+    if mask_out is None:
+        mask_out = torch.empty(rows, E, device=scores.device, dtype=torch.int32)
+    if (scores.numel() < E or mask_out.numel() < rows * E
+            or (mask_in is not None and mask_in.numel() < rows * E)):
+        raise ValueError("moe_critical_split: an argument is smaller than its shape needs")
+    _call("moe_critical_split", _dev(scores), E, ctypes.c_float(threshold), _dev(mask_in), rows,
+          _dev(mask_out), _stream(stream))
+    return mask_out
 
 
 def moe_pack_expert_host(weights: dict, H: int, F: int, w_dtype: int, dst) -> None:
@@ -432,8 +474,17 @@ class LayerContext:
         self._policy_params = p  # kept alive while the call reads it
         _call("moe_ctx_set_policy", self.handle, kind, window, _host(p) if p is not None else None)
 
+    def set_split(self, enable: bool, theta: float = 0.0, beta=None, gamma: float = 1.0) -> None:
+        """Split-precision routing over MOE_INT4G128_RESPLIT experts: routed expert e of
+        layer l on W^H when its step score >= theta * beta[l] * gamma, else on W^L."""
+        b = None if beta is None else np.ascontiguousarray(beta, dtype=np.float32)
+        self._split_beta = b
+        _call("moe_ctx_set_split", self.handle, int(enable), ctypes.c_float(theta),
+              _host(b) if b is not None else None, ctypes.c_float(gamma))
+
     def step_scores(self) -> np.ndarray:
-        """Routing scores [E] of the latest step (needs a policy other than LRU)."""
+        """Routing scores [E] of the latest step (needs split precision or a policy other
+        than LRU)."""
         out = np.zeros(self.E, np.float32)
         _call("moe_ctx_step_scores", self.handle, _host(out))
         return out

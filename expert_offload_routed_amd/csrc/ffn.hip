@@ -39,7 +39,8 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ lut,
     const int32_t* __restrict__ mask, int E, int n_shared, int shared_slot0, int num_slots,
     int small_max, FfnItem* __restrict__ items, int32_t* __restrict__ n_items,
-    GemmTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_word) {
+    GemmTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_word,
+    int hi_items) {
   __shared__ int s_wave[40];
   const int e = threadIdx.x;
   int rows = 0, slot = -1, begin = 0;
@@ -57,7 +58,9 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(
       }
     }
   }
-  const bool small = take && rows <= small_max;
+  // with split-precision weights a high-precision group is an item whatever its size
+  const bool hi = hi_items && (e >= E || mask == nullptr || mask[e] >= 2);
+  const bool small = take && (rows <= small_max || hi);
   const int ntile = (take && !small) ? (rows + kGemmBM - 1) / kGemmBM : 0;
   int total_items = 0, total_tiles = 0;
   const int ipos = block_exclusive_scan(small ? 1 : 0, s_wave, &total_items);
@@ -170,9 +173,10 @@ void launch_f32(const void* x, const int32_t* perm, int k, const FfnItem* items,
 void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
                      int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
                      int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
-                     hipStream_t s) {
+                     hipStream_t s, bool hi_items) {
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, lut, mask, E, n_shared,
-                     shared_slot0, num_slots, small_max, items, n_items, tiles, n_tiles, err_word);
+                     shared_slot0, num_slots, small_max, items, n_items, tiles, n_tiles, err_word,
+                     hi_items ? 1 : 0);
 }
 
 int ffn_small_max(int T, int k, int E, int n_shared) {
@@ -195,7 +199,7 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype
   off = align_up(off + (size_t)w.max_tiles * sizeof(GemmTile), 256);
   w.h = off;
   off = align_up(off + rows * F * sizeof(float), 256);
-  if (w_dtype == MOE_INT4G128) {
+  if (w_dtype == MOE_INT4G128 || w_dtype == MOE_INT4G128_RESPLIT) {
     // int8 rows and their fp32 scales
     w.xq = off;
     off = align_up(off + (size_t)T * H, 256);
@@ -218,7 +222,8 @@ extern "C" size_t moe_ffn_workspace_bytes(int T, int H, int F, int E, int k, int
 int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* lut,
              const int32_t* group_mask, int n_shared, int shared_slot0, const char* pool,
              size_t stride, int num_slots, const SlotLayout& lay, int T, int H, int F, int E, int k,
-             float* y, int32_t* err, char* ws, const FfnWorkspace& wl, hipStream_t s, bool planned);
+             float* y, int32_t* err, char* ws, const FfnWorkspace& wl, hipStream_t s, bool planned,
+             bool split);
 
 extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
                               const int32_t* offsets, const int32_t* lut,
@@ -253,10 +258,10 @@ int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* o
   if (w_dtype == MOE_BF16 && (H % 64 != 0 || F % 64 != 0)) return MOE_EUNSUPPORTED;
 
   char* wsb = static_cast<char*>(workspace);
-  if (w_dtype == MOE_INT4G128)
+  if (w_dtype == MOE_INT4G128 || w_dtype == MOE_INT4G128_RESPLIT)
     return ffn_int4(x, perm, offsets, lut, group_mask, n_shared, shared_slot0,
                     static_cast<const char*>(pool_base), slot_stride, num_slots, lay, T, H, F, E, k,
-                    y_perm, err_word, wsb, ws, stream, planned);
+                    y_perm, err_word, wsb, ws, stream, planned, w_dtype == MOE_INT4G128_RESPLIT);
 
   int32_t* n_items = reinterpret_cast<int32_t*>(wsb);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(wsb + 4);

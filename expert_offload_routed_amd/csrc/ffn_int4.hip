@@ -271,11 +271,11 @@ __global__ __launch_bounds__(512) void gemm_w4a8_kernel(
 #undef MOE_W4A8_TILE
 }
 
-template <int KS, int RBW, int MAXNT, bool SWIGLU>
+template <int KS, int RBW, int MAXNT, bool SWIGLU, bool SPLIT>
 void launch_gemv(const int8_t* aq, const float* as, const int32_t* perm, int k,
                  const FfnItem* items, const int32_t* n_items, int max_items, const char* pool,
-                 size_t stride, size_t off_codes, size_t off_scales, int R, int K, int out_ld,
-                 float* out, hipStream_t s) {
+                 size_t stride, const tgemv::QuantOffsets& offs, const int32_t* mask, int E, int R,
+                 int K, int out_ld, float* out, hipStream_t s) {
   constexpr int NW = KS < 4 ? 4 : KS;
   constexpr int rb_per_wg = NW / KS * RBW;
   const int upi = (R / 32 + rb_per_wg - 1) / rb_per_wg;
@@ -283,18 +283,19 @@ void launch_gemv(const int8_t* aq, const float* as, const int32_t* perm, int k,
   const unsigned grid = (unsigned)(units < tgemv::kGridCap ? units : tgemv::kGridCap);
   if (grid == 0) return;
   constexpr int U = RBW >= 4 ? 2 : 4;
-  hipLaunchKernelGGL((tgemv::int4_kernel<KS, RBW, NW, U, MAXNT, SWIGLU>), dim3(grid),
-                     dim3(NW * 64), 0, s, aq, as, perm, k, items, n_items, pool, stride,
-                     off_codes, off_scales, R, K, out_ld, upi, out);
+  hipLaunchKernelGGL((tgemv::int4_kernel<KS, RBW, NW, U, MAXNT, SWIGLU, SPLIT>), dim3(grid),
+                     dim3(NW * 64), 0, s, aq, as, perm, k, items, n_items, pool, stride, offs, mask,
+                     E, R, K, out_ld, upi, out);
 }
 
-template <int RBW, int MAXNT, bool SWIGLU>
-void launch_gemv_ks(int ks, const int8_t* aq, const float* as, const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
-                    int max_items, const char* pool, size_t stride, size_t off_codes,
-                    size_t off_scales, int R, int K, int out_ld, float* out, hipStream_t s) {
-#define MOE_W4_KS(KS_)                                                                          \
-  launch_gemv<KS_, RBW, MAXNT, SWIGLU>(aq, as, perm, k, items, n_items, max_items, pool,        \
-                                       stride, off_codes, off_scales, R, K, out_ld, out, s)
+template <int RBW, int MAXNT, bool SWIGLU, bool SPLIT>
+void launch_gemv_ks(int ks, const int8_t* aq, const float* as, const int32_t* perm, int k,
+                    const FfnItem* items, const int32_t* n_items, int max_items, const char* pool,
+                    size_t stride, const tgemv::QuantOffsets& offs, const int32_t* mask, int E,
+                    int R, int K, int out_ld, float* out, hipStream_t s) {
+#define MOE_W4_KS(KS_)                                                                            \
+  launch_gemv<KS_, RBW, MAXNT, SWIGLU, SPLIT>(aq, as, perm, k, items, n_items, max_items, pool,   \
+                                              stride, offs, mask, E, R, K, out_ld, out, s)
   switch (ks) {
     case 1: MOE_W4_KS(1); break;
     case 2: MOE_W4_KS(2); break;
@@ -304,25 +305,36 @@ void launch_gemv_ks(int ks, const int8_t* aq, const float* as, const int32_t* pe
 #undef MOE_W4_KS
 }
 
-void launch_gemv_any(bool first, int nt, const int8_t* aq, const float* as, const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
-                     int max_items, const char* pool, size_t stride, const SlotLayout& lay, int H,
-                     int F, float* out, hipStream_t s) {
+// One GEMV pass (first: gate/up with the SwiGLU epilogue; else: down). With
+// split = true the items of split-precision experts pick their precision from
+// mask (tgemv::int4_kernel).
+void launch_gemv_any(bool first, bool split, int nt, const int8_t* aq, const float* as,
+                     const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
+                     int max_items, const char* pool, size_t stride, const SlotLayout& lay,
+                     const int32_t* mask, int E, int H, int F, float* out, hipStream_t s) {
   const int R = first ? 2 * F : H, K = first ? H : F, ld = first ? F : H;
-  const size_t oc = first ? lay.off_w13 : lay.off_w2, os = first ? lay.off_s13 : lay.off_s2;
+  const tgemv::QuantOffsets offs =
+      first ? tgemv::QuantOffsets{lay.off_w13, lay.off_s13, lay.off_r13, lay.off_rs13}
+            : tgemv::QuantOffsets{lay.off_w2, lay.off_s2, lay.off_h2, lay.off_hs2};
   const tgemv::Split sp = tgemv::choose_split_int4(R / 32 * max_items, K / 64);
-#define MOE_W4_NT(NT_)                                                                          \
-  do {                                                                                          \
-    if (first)                                                                                  \
-      launch_gemv_ks<4, NT_, true>(sp.ks, aq, as, perm, k, items, n_items, max_items, pool, stride, \
-                                oc, os, R, K, ld, out, s);                                      \
-    else                                                                                        \
-      launch_gemv_ks<4, NT_, false>(sp.ks, aq, as, perm, k, items, n_items, max_items, pool,       \
-                                 stride, oc, os, R, K, ld, out, s);                             \
+#define MOE_W4_SPLIT(NT_, FIRST_, SPLIT_)                                                        \
+  launch_gemv_ks<4, NT_, FIRST_, SPLIT_>(sp.ks, aq, as, perm, k, items, n_items, max_items, pool, \
+                                         stride, offs, mask, E, R, K, ld, out, s)
+#define MOE_W4_NT(NT_)                                     \
+  do {                                                     \
+    if (first) {                                           \
+      if (split) MOE_W4_SPLIT(NT_, true, true);            \
+      else MOE_W4_SPLIT(NT_, true, false);                 \
+    } else {                                               \
+      if (split) MOE_W4_SPLIT(NT_, false, true);           \
+      else MOE_W4_SPLIT(NT_, false, false);                \
+    }                                                      \
   } while (0)
   if (nt <= 1) MOE_W4_NT(1);
   else if (nt <= 2) MOE_W4_NT(2);
   else MOE_W4_NT(4);
 #undef MOE_W4_NT
+#undef MOE_W4_SPLIT
 }
 
 }  // namespace
@@ -331,7 +343,7 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
              const int32_t* group_mask, int n_shared, int shared_slot0, const char* pool,
              size_t stride, int num_slots, const SlotLayout& lay, int T, int H, int F, int E, int k,
              float* y, int32_t* err, char* ws, const FfnWorkspace& wl, hipStream_t s,
-             bool planned) {
+             bool planned, bool split) {
   int32_t* n_items = reinterpret_cast<int32_t*>(ws);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + 4);
   FfnItem* items = reinterpret_cast<FfnItem*>(ws + wl.items);
@@ -345,18 +357,19 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   const long long tk = (long long)T * k;
   const long long rows = (long long)T * (k + n_shared);
   const int small_max = ffn_small_max(T, k, E, n_shared);
-  const int max_items = small_max == 0 ? 0 : (int)(tk < E ? tk : E) + n_shared;
+  // split-precision experts: high-precision groups are items whatever their size
+  const int max_items = (small_max == 0 && !split) ? 0 : (int)(tk < E ? tk : E) + n_shared;
   const int max_tiles = (T > small_max) ? wl.max_tiles : 0;
   if (max_tiles > 65535) return MOE_EUNSUPPORTED;
   if (!planned)
     launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max,
-                    items, n_items, tiles, n_tiles, err, s);
+                    items, n_items, tiles, n_tiles, err, s, split);
   hipLaunchKernelGGL(quant_rows_kernel<MOE_BF16>, dim3(T), dim3(256), 0, s, x, H, nullptr, nullptr,
                      nullptr, 0, 0, 0, xq, xs);
   const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;
   if (max_items > 0)
-    launch_gemv_any(true, nt, xq, xs, perm, k, items, n_items, max_items, pool, stride, lay, H, F,
-                    hbuf, s);
+    launch_gemv_any(true, split, nt, xq, xs, perm, k, items, n_items, max_items, pool, stride, lay,
+                    group_mask, E, H, F, hbuf, s);
   if (max_tiles > 0)
     hipLaunchKernelGGL(gemm_w4a8_kernel<1>, dim3((2 * F + QBN - 1) / QBN, max_tiles), dim3(512), 0,
                        s, xq, xs, perm, k, tiles, n_tiles, pool, stride, lay.off_w13,
@@ -364,8 +377,8 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   hipLaunchKernelGGL(quant_rows_kernel<MOE_F32>, dim3((unsigned)rows), dim3(256), 0, s, hbuf, F,
                      offsets, lut, group_mask, E, n_shared, num_slots, hq, hs);
   if (max_items > 0)
-    launch_gemv_any(false, nt, hq, hs, perm, k, items, n_items, max_items, pool, stride, lay, H,
-                    F, y, s);
+    launch_gemv_any(false, split, nt, hq, hs, perm, k, items, n_items, max_items, pool, stride, lay,
+                    group_mask, E, H, F, y, s);
   if (max_tiles > 0)
     hipLaunchKernelGGL(gemm_w4a8_kernel<2>, dim3((H + QBN - 1) / QBN, max_tiles), dim3(512), 0, s,
                        hq, hs, perm, k, tiles, n_tiles, pool, stride, lay.off_w2, lay.off_s2, H,

@@ -26,6 +26,7 @@ constexpr int kGemvMaxRows = 4;  // groups up to this many rows take the GEMV pa
 // Byte layout of one expert inside a slot (see moe_slot_layout).
 struct SlotLayout {
   size_t slot_bytes, off_w13, off_w2, off_s13, off_s2;
+  size_t off_r13, off_rs13, off_h2, off_hs2;  // MOE_INT4G128_RESPLIT only (else 0)
 };
 
 // Sections of the moe_expert_ffn workspace (byte offsets).
@@ -40,11 +41,13 @@ int slot_layout(int H, int F, int w_dtype, SlotLayout* out);
 
 #include <hip/hip_runtime.h>
 // The FFN work list: groups of <= small_max rows as FfnItem, the others cut
-// into kGemmBM-row GemmTile (see ffn_plan_kernel in ffn.hip).
+// into kGemmBM-row GemmTile (see ffn_plan_kernel in ffn.hip). hi_items:
+// split-precision weights, whose high-precision groups (mask NULL or >= 2,
+// shared groups) are items whatever their size.
 void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
                      int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
                      int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
-                     hipStream_t s);
+                     hipStream_t s, bool hi_items = false);
 // Largest group that takes the GEMV path (0: every group takes the MFMA tiles).
 int ffn_small_max(int T, int k, int E, int n_shared);
 void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, const GemmTile* tiles,
@@ -85,3 +88,8 @@ int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* o
                const void* pool_base, size_t slot_stride, int num_slots, int w_dtype, int T, int H,
                int F, int E, int k, float* y_perm, int32_t* err_word, void* workspace,
                size_t ws_bytes, hipStream_t stream, bool planned = false);
+// The routing score of every expert at one step (moe_step_scores) on stream s.
+void launch_step_scores(const float* logits, int T, int E, float* scores, hipStream_t s);
+// moe_critical_split on stream s (arguments checked by the caller).
+void launch_critical_split(const float* scores, int E, float threshold, const int32_t* mask_in,
+                           int rows, int32_t* mask_out, hipStream_t s);

@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <new>
+#include <cmath>
 #include <vector>
 
 #include "common.h"
@@ -67,6 +68,8 @@ struct moe_layer_ctx {
   char* ws;
   size_t ws_bytes;
   int32_t* masks;
+  float* scores;  // [E] routing scores of the latest step (split precision)
+  int32_t* crit;  // [E] group precision of a fully resident step (split precision)
   int sh_T;  // T the shared groups' rows (perm and offsets tails) were written for
   // host state
   int32_t* ring_h;  // pinned [kRing][2E+1]: per step the routed set [E], its size, and the
@@ -86,6 +89,9 @@ struct moe_layer_ctx {
   double params[5];
   std::vector<double> pol_state;
   int last_ring;  // ring entry of the latest step
+  // split-precision experts (moe_ctx_set_split): thresholds per layer
+  int split;
+  std::vector<float> split_th;
   // device orchestration (moe_ctx_set_orchestration)
   int orch;                 // 0: plans on the host; 1: plans and fills on the device
   const char* store_dev;    // device address of the pinned host store
@@ -112,7 +118,8 @@ namespace {
 
 // Device work buffers of a context, carved from the caller's workspace.
 struct CtxLayout {
-  size_t sync, logits, ids, topw, counts, offsets, perm, inv, dist, y_perm, ws, masks, total;
+  size_t sync, logits, ids, topw, counts, offsets, perm, inv, dist, y_perm, ws, masks, scores, crit,
+      total;
   size_t ws_bytes;
 };
 
@@ -139,6 +146,8 @@ CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int w_dtype, int n_s
   l.ws_bytes = ffn_workspace_layout(t_max, H, F, E, k, w_dtype, n_shared).total;
   l.ws = take(l.ws_bytes);
   l.masks = take((size_t)(E + 2) * E * 4);
+  l.scores = take((size_t)E * 4);
+  l.crit = take((size_t)E * 4);
   l.total = off;
   return l;
 }
@@ -156,48 +165,6 @@ __global__ void commit_after_fill_kernel(int32_t* lut, int32_t idx, int32_t* own
   owner[slot] = idx;
 }
 
-// Routing score of every expert at one step: its softmax probability over the
-// step's tokens, averaged over the tokens (the score the eviction policies
-// record). One workgroup of 16 waves; wave w takes tokens w, w + 16, ...;
-// the per-wave partial sums meet in LDS in wave order.
-constexpr int kScoreWaves = 16;
-__global__ __launch_bounds__(kScoreWaves * 64) void step_scores_kernel(const float* __restrict__ logits,
-                                                                      int T, int E, float* out) {
-  __shared__ float part[kScoreWaves][1024];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kPer = 1024 / 64;  // experts per lane (E <= 1024)
-  float acc[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
-  for (int t = wave; t < T; t += kScoreWaves) {
-    const float* row = logits + (size_t)t * E;
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E) m = fmaxf(m, row[e]);
-    }
-    m = wave_max(m);
-    float v[kPer], sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = e < E ? expf(row[e] - m) : 0.f;
-      sum += v[i];
-    }
-    sum = wave_sum(sum);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) acc[i] += v[i] / sum;
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) part[wave][lane + 64 * i] = acc[i];
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kScoreWaves * 64) {
-    float s = 0.f;
-    for (int w = 0; w < kScoreWaves; ++w) s += part[w][e];
-    out[e] = s / (float)T;
-  }
-}
 
 // LRU plan of one layer call on the device: the rule of moe_plan_fills for a
 // routed set that fits the pool (n_distinct <= S, one wave). Victims are the
@@ -537,6 +504,7 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->window = 1;
   for (double& v : c->params) v = 0.0;
   c->last_ring = -1;
+  c->split = 0;
   c->orch = 0;
   c->store_dev = nullptr;
   c->d_order = nullptr;
@@ -560,6 +528,8 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->ws = wb + cl.ws;
   c->ws_bytes = cl.ws_bytes;
   c->masks = reinterpret_cast<int32_t*>(wb + cl.masks);
+  c->scores = reinterpret_cast<float*>(wb + cl.scores);
+  c->crit = reinterpret_cast<int32_t*>(wb + cl.crit);
   int bad = 0;
   // coherent, mapped: the permutation kernel stores the routed set straight into it
   bad |= hipHostMalloc(reinterpret_cast<void**>(&c->ring_h),
@@ -677,8 +647,33 @@ extern "C" int moe_ctx_set_policy(moe_layer_ctx* c, int policy, int window, cons
   return MOE_OK;
 }
 
+extern "C" int moe_ctx_set_split(moe_layer_ctx* c, int enable, float theta, const float* beta,
+                                 float gamma) {
+  MOE_CHECK_ARG(c && (enable == 0 || enable == 1));
+  MOE_CHECK_ARG(!enable || c->w_dtype == MOE_INT4G128_RESPLIT);
+  if (enable) {
+    MOE_CHECK_ARG(std::isfinite(theta) && std::isfinite(gamma));
+    c->split_th.assign(c->L, 0.f);
+    for (int l = 0; l < c->L; ++l) {
+      const double b = beta ? (double)beta[l] : 1.0;
+      MOE_CHECK_ARG(std::isfinite(b));
+      c->split_th[l] = (float)((double)theta * b * (double)gamma);
+    }
+  }
+  // steps already enqueued keep the setting they were enqueued with
+  c->split = enable;
+  return MOE_OK;
+}
+
 extern "C" int moe_ctx_step_scores(moe_layer_ctx* c, float* scores) {
-  MOE_CHECK_ARG(c && scores && c->policy != MOE_POLICY_LRU && c->last_ring >= 0);
+  MOE_CHECK_ARG(c && scores);
+  if (c->split) {  // the scores of the latest step stay on the device
+    hipError_t e = hipStreamSynchronize(c->cs);
+    if (e == hipSuccess) e = hipMemcpy(scores, c->scores, (size_t)c->E * sizeof(float),
+                                       hipMemcpyDeviceToHost);
+    return e == hipSuccess ? MOE_OK : moe_hip_status(e);
+  }
+  MOE_CHECK_ARG(c->policy != MOE_POLICY_LRU && c->last_ring >= 0);
   const hipError_t e = hipEventSynchronize(c->ring_ev[c->last_ring]);
   if (e != hipSuccess) return moe_hip_status(e);
   memcpy(scores, c->ring_h + (size_t)c->last_ring * (2 * c->E + 1) + c->E + 1,
@@ -728,10 +723,17 @@ int forward_device(moe_layer_ctx* c, int layer, const void* x, int T, const void
                    const float* bias, void* out, int out_dtype) {
   const int E = c->E, k = c->k, H = c->H, F = c->F, nsh = c->n_shared;
   const int nslots = c->S + nsh;
+  FrontPlan fp{};
+  fp.scores = c->scores;  // written only for split precision
+  bool scored = false;
   int rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
                               c->topw, c->counts, c->offsets, c->perm, c->inv, c->dist, c->dist + E,
-                              c->sync, nullptr, nullptr, nullptr, c->cs);
+                              c->sync, c->split ? &fp : nullptr, nullptr, &scored, c->cs);
   if (rc != MOE_OK) return rc;
+  if (c->split) {
+    if (!scored) launch_step_scores(c->logits, T, E, c->scores, c->cs);
+    launch_critical_split(c->scores, E, c->split_th[layer], nullptr, 1, c->crit, c->cs);
+  }
   hipLaunchKernelGGL(device_plan_kernel, dim3(1), dim3(1024), 0, c->cs, layer, E, c->S, c->dist,
                      c->lut, c->owner, c->d_last_use, c->d_clock, c->d_order, c->d_fills,
                      c->d_nfills, c->d_counters);
@@ -745,9 +747,10 @@ int forward_device(moe_layer_ctx* c, int layer, const void* x, int T, const void
     const int tr = (c->t_head + c->t_count) % kRing;
     if ((e = hipEventRecord(c->tev0[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
   }
-  if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, c->lut + (size_t)layer * E, nullptr, nsh,
-                       c->S, c->pool, c->stride, nslots, c->w_dtype, T, H, F, E, k, c->y_perm,
-                       c->err, c->ws, c->ws_bytes, c->cs)) != MOE_OK)
+  if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, c->lut + (size_t)layer * E,
+                       c->split ? c->crit : nullptr, nsh, c->S, c->pool, c->stride, nslots,
+                       c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws, c->ws_bytes,
+                       c->cs)) != MOE_OK)
     return rc;
   if (timing) {
     const int tr = (c->t_head + c->t_count) % kRing;
@@ -801,9 +804,14 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   // routing scores an eviction policy records (next to the routed set)
   FrontPlan fp{};
   bool planned = false, scored = false;
-  const bool want_scores = c->policy != MOE_POLICY_LRU;
-  if (want_scores) fp.scores = reinterpret_cast<float*>(dd + E + 1);
-  if (all_resident) {
+  const bool want_scores = c->policy != MOE_POLICY_LRU;  // recorded next to the routed set
+  float* ring_scores = reinterpret_cast<float*>(dd + E + 1);
+  // split precision: the scores stay on the device and decide each group's precision; the
+  // front end's FFN work list is not used (high-precision groups are items at any size)
+  if (c->split) fp.scores = c->scores;
+  else if (want_scores) fp.scores = ring_scores;
+  const bool front_plan = all_resident && c->w_dtype != MOE_INT4G128_RESPLIT;
+  if (front_plan) {
     const FfnWorkspace wl = ffn_workspace_layout(T, H, F, E, k, c->w_dtype, nsh);
     fp.lut = lut_row;
     fp.num_slots = nslots;
@@ -818,14 +826,17 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   }
   if ((rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
                                c->topw, c->counts, c->offsets, c->perm, c->inv, dd, dd + E, c->sync,
-                               (all_resident || want_scores) ? &fp : nullptr, &planned, &scored,
+                               (front_plan || fp.scores) ? &fp : nullptr, &planned, &scored,
                                c->cs)) != MOE_OK)
     return rc;
-  if (want_scores && !scored) {  // the front end did not write them (more tokens)
-    hipLaunchKernelGGL(step_scores_kernel, dim3(1), dim3(kScoreWaves * 64), 0, c->cs, c->logits, T, E,
-                       reinterpret_cast<float*>(dd + E + 1));
+  if (fp.scores && !scored) {  // the front end did not write them (more tokens)
+    launch_step_scores(c->logits, T, E, fp.scores, c->cs);
     if ((rc = moe_launch_status()) != MOE_OK) return rc;
   }
+  if (c->split && want_scores &&
+      (e = hipMemcpyAsync(dh + E + 1, c->scores, (size_t)E * sizeof(float),
+                          hipMemcpyDeviceToHost, c->cs)) != hipSuccess)
+    return moe_hip_status(e);
   if ((e = hipEventRecord(c->ring_ev[r], c->cs)) != hipSuccess) return moe_hip_status(e);
   c->ring_next = (r + 1) % kRing;
   c->last_ring = r;
@@ -841,9 +852,11 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
     // no miss is possible: defer the bookkeeping, run every routed group
     c->ring_layer[r] = layer;
     c->ring_count += 1;
-    if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, nullptr, nsh, c->S, c->pool,
-                         c->stride, nslots, c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws,
-                         c->ws_bytes, c->cs, planned)) != MOE_OK)
+    if (c->split)
+      launch_critical_split(c->scores, E, c->split_th[layer], nullptr, 1, c->crit, c->cs);
+    if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, c->split ? c->crit : nullptr,
+                         nsh, c->S, c->pool, c->stride, nslots, c->w_dtype, T, H, F, E, k,
+                         c->y_perm, c->err, c->ws, c->ws_bytes, c->cs, planned)) != MOE_OK)
       return rc;
   } else {
     if ((rc = drain(c)) != MOE_OK) return rc;  // earlier steps first: their entries precede r
@@ -867,6 +880,9 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
     if ((e = hipMemcpyAsync(c->masks, c->masks_h, (size_t)rows * E * sizeof(int32_t),
                             hipMemcpyHostToDevice, c->cs)) != hipSuccess)
       return moe_hip_status(e);
+    // split precision: each selected group takes its precision from the step's scores
+    if (c->split)
+      launch_critical_split(c->scores, E, c->split_th[layer], c->masks, rows, c->masks, c->cs);
     // wave 0 fills may start now: they only overwrite slots no resident group of this step reads
     if (n_fills && (rc = fills_after_compute(c)) != MOE_OK) return rc;
     if (hits || nsh) {  // resident groups, and the shared experts

@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "common.h"
@@ -34,13 +35,21 @@ int slot_layout(int H, int F, int w_dtype, SlotLayout* out) {
     l.off_w2 = align_up((size_t)2 * F * H * es, 256);
     l.off_s13 = l.off_s2 = 0;
     l.slot_bytes = align_up(l.off_w2 + (size_t)H * F * es, 4096);
-  } else if (w_dtype == MOE_INT4G128) {
+  } else if (w_dtype == MOE_INT4G128 || w_dtype == MOE_INT4G128_RESPLIT) {
     if (H % 128 != 0 || F % 128 != 0) return MOE_EINVAL;
     l.off_w13 = 0;
     l.off_w2 = align_up((size_t)2 * F * (H / 2), 256);
     l.off_s13 = align_up(l.off_w2 + (size_t)H * (F / 2), 256);
     l.off_s2 = align_up(l.off_s13 + (size_t)2 * F * (H / 128) * 2, 256);
-    l.slot_bytes = align_up(l.off_s2 + (size_t)H * (F / 128) * 2, 4096);
+    size_t end = l.off_s2 + (size_t)H * (F / 128) * 2;
+    if (w_dtype == MOE_INT4G128_RESPLIT) {
+      l.off_r13 = align_up(end, 256);                                 // int4 residual of W13
+      l.off_rs13 = align_up(l.off_r13 + (size_t)2 * F * (H / 2), 256);  // its scales
+      l.off_h2 = align_up(l.off_rs13 + (size_t)2 * F * (H / 128) * 2, 256);  // W2 at 8 bits
+      l.off_hs2 = align_up(l.off_h2 + (size_t)H * F, 256);                // its scales
+      end = l.off_hs2 + (size_t)H * (F / 128) * 2;
+    }
+    l.slot_bytes = align_up(end, 4096);
   } else {
     return MOE_EINVAL;
   }
@@ -58,6 +67,18 @@ extern "C" int moe_slot_layout(int H, int F, int w_dtype, size_t* slot_bytes, si
   if (off_w2) *off_w2 = l.off_w2;
   if (off_s13) *off_s13 = l.off_s13;
   if (off_s2) *off_s2 = l.off_s2;
+  return MOE_OK;
+}
+
+extern "C" int moe_slot_layout_resplit(int H, int F, size_t* off_r13, size_t* off_rs13,
+                                       size_t* off_h2, size_t* off_hs2) {
+  SlotLayout l;
+  const int rc = slot_layout(H, F, MOE_INT4G128_RESPLIT, &l);
+  if (rc != MOE_OK) return rc;
+  if (off_r13) *off_r13 = l.off_r13;
+  if (off_rs13) *off_rs13 = l.off_rs13;
+  if (off_h2) *off_h2 = l.off_h2;
+  if (off_hs2) *off_hs2 = l.off_hs2;
   return MOE_OK;
 }
 
@@ -96,6 +117,19 @@ void pack_tiles_int4(char* dst, const uint8_t* src_rows[], int R, int K) {
               out[h * 8 + w * 4 + i] =
                   (uint8_t)(code_at(row, c0 + i) | (code_at(row, c0 + i + 4) << 4));
           }
+      }
+}
+
+// Tile-major int8: chunk (r / 32) * (K / 32) + c / 32 of 1 KB; lane (r % 32) + 32 ((c % 32) / 16)
+// holds the 16 consecutive codes c..c+15 of its row, one byte each.
+void pack_tiles_int8(char* dst, const int8_t* const src_rows[], int R, int K) {
+  const int nkc = K / 32;
+  for (int rb = 0; rb < R / 32; ++rb)
+    for (int kc = 0; kc < nkc; ++kc)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int8_t* row = src_rows[rb * 32 + (lane & 31)];
+        memcpy(dst + ((size_t)(rb * nkc + kc) * 64 + lane) * 16, row + kc * 32 + 16 * (lane >> 5),
+               16);
       }
 }
 
@@ -149,6 +183,108 @@ extern "C" int moe_pack_expert_host(const void* gate, const void* up, const void
   memcpy(d + l.off_s2, down_s, (size_t)H * sb2);
   return MOE_OK;
 }
+
+// ------------------------------------------------- split-precision experts --
+// RapidMoE Algorithm 3 (RESplit) with b_q = b_r = 4: the float32 decisions
+// (the group maximum over 2^(b-1)-1, the code rint(w / s)) are taken exactly
+// as IEEE float32 operations, so contraction into fused multiply-adds is off.
+#pragma clang fp contract(off)
+namespace {
+
+uint16_t bf16_bits_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+float bf16_value(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+// Symmetric b-bit quantisation of one row of K values in groups of 128: codes
+// q[K] (int8) and the bf16 scale of each group s[K / 128].
+void quantize_row_g128(const float* w, int K, int bits, int8_t* q, uint16_t* s) {
+  const float qmax = (float)((1 << (bits - 1)) - 1);
+  const float qlo = -(float)(1 << (bits - 1));
+  for (int g = 0; g < K / 128; ++g) {
+    float m = 0.f;
+    for (int c = 0; c < 128; ++c) m = std::max(m, std::fabs(w[g * 128 + c]));
+    const uint16_t sb = bf16_bits_rne(m / qmax);
+    const float sv = bf16_value(sb);
+    s[g] = sb;
+    for (int c = 0; c < 128; ++c) {
+      float v = 0.f;
+      if (sv != 0.f) v = std::min(std::max(std::rint(w[g * 128 + c] / sv), qlo), qmax);
+      q[g * 128 + c] = (int8_t)v;
+    }
+  }
+}
+
+// int4 codes of a row (int8 values in [-8, 7]) as nibbles, even index in the low nibble.
+void nibbles_of(const int8_t* q, int K, uint8_t* out) {
+  for (int c = 0; c < K; c += 2)
+    out[c / 2] = (uint8_t)((q[c] & 0xF) | ((q[c + 1] & 0xF) << 4));
+}
+
+}  // namespace
+
+extern "C" int moe_quantize_resplit_host(const float* gate, const float* up, const float* down,
+                                         int H, int F, void* dst) {
+  SlotLayout l;
+  if (slot_layout(H, F, MOE_INT4G128_RESPLIT, &l) != MOE_OK) return MOE_EINVAL;
+  MOE_CHECK_ARG(gate && up && down && dst);
+  char* d = static_cast<char*>(dst);
+  memset(d, 0, l.slot_bytes);
+  // W13 rows interleaved (2n = gate n, 2n + 1 = up n): W^Q codes and the residual's codes
+  std::vector<uint8_t> nq((size_t)2 * F * (H / 2)), nr((size_t)2 * F * (H / 2));
+  std::vector<uint16_t> sq((size_t)2 * F * (H / 128)), sr((size_t)2 * F * (H / 128));
+  std::vector<int8_t> q(H), rq(H);
+  std::vector<float> res(H);
+  for (int n = 0; n < F; ++n)
+    for (int j = 0; j < 2; ++j) {
+      const float* w = (j == 0 ? gate : up) + (size_t)n * H;
+      const size_t row = (size_t)2 * n + j;
+      uint16_t* s_row = sq.data() + row * (H / 128);
+      quantize_row_g128(w, H, 4, q.data(), s_row);
+      for (int c = 0; c < H; ++c) res[c] = w[c] - (float)q[c] * bf16_value(s_row[c / 128]);
+      quantize_row_g128(res.data(), H, 4, rq.data(), sr.data() + row * (H / 128));
+      nibbles_of(q.data(), H, nq.data() + row * (H / 2));
+      nibbles_of(rq.data(), H, nr.data() + row * (H / 2));
+    }
+  // W2 [H, F]: W^L at 4 bits, W^H at 8 bits
+  std::vector<uint8_t> nl((size_t)H * (F / 2));
+  std::vector<int8_t> qh((size_t)H * F), ql(F);
+  std::vector<uint16_t> sl((size_t)H * (F / 128)), sh((size_t)H * (F / 128));
+  for (int r = 0; r < H; ++r) {
+    const float* w = down + (size_t)r * F;
+    quantize_row_g128(w, F, 4, ql.data(), sl.data() + (size_t)r * (F / 128));
+    nibbles_of(ql.data(), F, nl.data() + (size_t)r * (F / 2));
+    quantize_row_g128(w, F, 8, qh.data() + (size_t)r * F, sh.data() + (size_t)r * (F / 128));
+  }
+  std::vector<const uint8_t*> r13(2 * F), rr13(2 * F), r2(H);
+  std::vector<const int8_t*> h2(H);
+  for (int i = 0; i < 2 * F; ++i) {
+    r13[i] = nq.data() + (size_t)i * (H / 2);
+    rr13[i] = nr.data() + (size_t)i * (H / 2);
+  }
+  for (int r = 0; r < H; ++r) {
+    r2[r] = nl.data() + (size_t)r * (F / 2);
+    h2[r] = qh.data() + (size_t)r * F;
+  }
+  pack_tiles_int4(d + l.off_w13, r13.data(), 2 * F, H);
+  pack_tiles_int4(d + l.off_w2, r2.data(), H, F);
+  pack_tiles_int4(d + l.off_r13, rr13.data(), 2 * F, H);
+  pack_tiles_int8(d + l.off_h2, h2.data(), H, F);
+  memcpy(d + l.off_s13, sq.data(), sq.size() * 2);
+  memcpy(d + l.off_s2, sl.data(), sl.size() * 2);
+  memcpy(d + l.off_rs13, sr.data(), sr.size() * 2);
+  memcpy(d + l.off_hs2, sh.data(), sh.size() * 2);
+  return MOE_OK;
+}
+#pragma clang fp contract(on)
 
 // -------------------------------------------------------- tags and commits --
 namespace {

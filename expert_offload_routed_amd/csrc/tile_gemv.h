@@ -1,5 +1,6 @@
-// Decode-form expert GEMV passes over tile-major weights (bf16 and int4),
-// shared by ffn.hip and ffn_int4.hip.
+// Decode-form expert GEMV passes over tile-major weights (bf16; int4; and the
+// int4 + int4-residual and int8 forms of split-precision experts), shared by
+// ffn.hip and ffn_int4.hip.
 //
 // Tile-major layout (moe_slot_layout): the weights of a 32-row block are
 // consecutive 1 KB chunks; in chunk ks lane l holds row l % 32 and the K
@@ -169,14 +170,33 @@ __device__ __forceinline__ void tile_bf16(const char* __restrict__ wbase, int nk
 // ------------------------------------------------------------------ int4 ---
 // Codes expanded to bytes 16 q; the dot products are 16 sum q x (exact int32)
 // and the group scale carries the factor 1/16 (exact in fp32).
-template <int KS, int RBW, int U, int NT, bool SWIGLU>
-__device__ __forceinline__ void tile_int4(const char* __restrict__ wbase, int nkc, int K,
+__device__ __forceinline__ int dot64_int4(const u32x4& w, const u32x4& a0, const u32x4& a1) {
+  int is = 0;
+  is = __builtin_amdgcn_sdot4((int)q16_lo(w.x), (int)a0.x, is, false);
+  is = __builtin_amdgcn_sdot4((int)q16_hi(w.x), (int)a0.y, is, false);
+  is = __builtin_amdgcn_sdot4((int)q16_lo(w.y), (int)a0.z, is, false);
+  is = __builtin_amdgcn_sdot4((int)q16_hi(w.y), (int)a0.w, is, false);
+  is = __builtin_amdgcn_sdot4((int)q16_lo(w.z), (int)a1.x, is, false);
+  is = __builtin_amdgcn_sdot4((int)q16_hi(w.z), (int)a1.y, is, false);
+  is = __builtin_amdgcn_sdot4((int)q16_lo(w.w), (int)a1.z, is, false);
+  is = __builtin_amdgcn_sdot4((int)q16_hi(w.w), (int)a1.w, is, false);
+  return is;
+}
+
+// RES adds a second int4 matrix of the same layout (the residual W^R of a
+// split-precision expert, codes at rbase, scales rscales) to the first: both
+// group products are scaled and accumulated into the same fp32 sums.
+template <int KS, int RBW, int U, int NT, bool SWIGLU, bool RES>
+__device__ __forceinline__ void tile_int4(const char* __restrict__ wbase,
                                           const uint16_t* __restrict__ scales,
+                                          const char* __restrict__ rbase,
+                                          const uint16_t* __restrict__ rscales, int nkc, int K,
                                           const int8_t* __restrict__ aq,
                                           const float* __restrict__ as,
                                           const int32_t* __restrict__ perm, int k, int prow,
                                           int rb0, int nrb, int out_ld, float* __restrict__ out,
                                           float* __restrict__ red) {
+  constexpr int UR = RES ? U : 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slice = wave % KS;
   const int kh = 16 * (lane >> 5);
@@ -188,6 +208,88 @@ __device__ __forceinline__ void tile_int4(const char* __restrict__ wbase, int nk
     arow[t] = SWIGLU ? perm[prow + t] / k : prow + t;
     sx[t] = as[arow[t]];
   }
+  float acc[RBW][NT];
+#pragma unroll
+  for (int b = 0; b < RBW; ++b)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[b][t] = 0.f;
+  const char* wl[RBW];
+  const uint16_t* srow[RBW];
+  const char* rl[RBW];
+  const uint16_t* rrow[RBW];
+#pragma unroll
+  for (int b = 0; b < RBW; ++b) {
+    const int rb = (rb0 + b < nrb) ? rb0 + b : nrb - 1;
+    const size_t wo = (size_t)rb * nkc * 1024 + lane * 16;
+    const size_t so = (size_t)(rb * 32 + (lane & 31)) * gld;
+    wl[b] = wbase + wo;
+    srow[b] = scales + so;
+    if constexpr (RES) {
+      rl[b] = rbase + wo;
+      rrow[b] = rscales + so;
+    }
+  }
+  for (int kc0 = slice; kc0 < nkc; kc0 += KS * U) {
+    u32x4 cw[U][RBW];
+    float sw[U][RBW];
+    u32x4 cr[UR][RBW];
+    float sr[UR][RBW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kc = kc0 + u * KS;
+      if (kc < nkc) {
+#pragma unroll
+        for (int b = 0; b < RBW; ++b) {
+          cw[u][b] = ld16_stream(wl[b] + (size_t)kc * 1024);
+          sw[u][b] = bf16_to_f32(srow[b][kc >> 1]) * 0.0625f;
+          if constexpr (RES) {
+            cr[u][b] = ld16_stream(rl[b] + (size_t)kc * 1024);
+            sr[u][b] = bf16_to_f32(rrow[b][kc >> 1]) * 0.0625f;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kc = kc0 + u * KS;
+      if (kc < nkc) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int8_t* ap = aq + (size_t)arow[t] * K + kc * 64 + kh;
+          const u32x4 a0 = ld16(ap), a1 = ld16(ap + 32);
+#pragma unroll
+          for (int b = 0; b < RBW; ++b) {
+            acc[b][t] = fmaf((float)dot64_int4(cw[u][b], a0, a1), sw[u][b], acc[b][t]);
+            if constexpr (RES)
+              acc[b][t] = fmaf((float)dot64_int4(cr[u][b], a0, a1), sr[u][b], acc[b][t]);
+          }
+        }
+      }
+    }
+  }
+  finish<RBW, NT, KS, SWIGLU, MOE_F32>(acc, sx, prow, rb0, nrb, out_ld, out, red);
+}
+
+// ------------------------------------------------------------------ int8 ---
+// 8-bit codes (the high-precision down projection W^H of a split-precision
+// expert): tile-major 1 KB chunks of 32 rows x 32 codes, lane l holding the 16
+// codes of row l % 32 at k offset 16 (l / 32); the integer sums are exact and
+// the group (4 chunks) scale applies in fp32. Second pass only: the
+// activation rows are the permuted rows of h.
+template <int KS, int RBW, int U, int NT>
+__device__ __forceinline__ void tile_int8(const char* __restrict__ wbase,
+                                          const uint16_t* __restrict__ scales, int nkc, int K,
+                                          const int8_t* __restrict__ aq,
+                                          const float* __restrict__ as, int prow, int rb0,
+                                          int nrb, int out_ld, float* __restrict__ out,
+                                          float* __restrict__ red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slice = wave % KS;
+  const int kh = 16 * (lane >> 5);
+  const int gld = K / 128;
+  float sx[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) sx[t] = as[prow + t];
   float acc[RBW][NT];
 #pragma unroll
   for (int b = 0; b < RBW; ++b)
@@ -211,7 +313,7 @@ __device__ __forceinline__ void tile_int4(const char* __restrict__ wbase, int nk
 #pragma unroll
         for (int b = 0; b < RBW; ++b) {
           cw[u][b] = ld16_stream(wl[b] + (size_t)kc * 1024);
-          sw[u][b] = bf16_to_f32(srow[b][kc >> 1]) * 0.0625f;
+          sw[u][b] = bf16_to_f32(srow[b][kc >> 2]);
         }
       }
     }
@@ -221,27 +323,22 @@ __device__ __forceinline__ void tile_int4(const char* __restrict__ wbase, int nk
       if (kc < nkc) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const int8_t* ap = aq + (size_t)arow[t] * K + kc * 64 + kh;
-          const u32x4 a0 = ld16(ap), a1 = ld16(ap + 32);
+          const u32x4 a = ld16(aq + (size_t)(prow + t) * K + kc * 32 + kh);
 #pragma unroll
           for (int b = 0; b < RBW; ++b) {
             const u32x4& w = cw[u][b];
             int is = 0;
-            is = __builtin_amdgcn_sdot4((int)q16_lo(w.x), (int)a0.x, is, false);
-            is = __builtin_amdgcn_sdot4((int)q16_hi(w.x), (int)a0.y, is, false);
-            is = __builtin_amdgcn_sdot4((int)q16_lo(w.y), (int)a0.z, is, false);
-            is = __builtin_amdgcn_sdot4((int)q16_hi(w.y), (int)a0.w, is, false);
-            is = __builtin_amdgcn_sdot4((int)q16_lo(w.z), (int)a1.x, is, false);
-            is = __builtin_amdgcn_sdot4((int)q16_hi(w.z), (int)a1.y, is, false);
-            is = __builtin_amdgcn_sdot4((int)q16_lo(w.w), (int)a1.z, is, false);
-            is = __builtin_amdgcn_sdot4((int)q16_hi(w.w), (int)a1.w, is, false);
+            is = __builtin_amdgcn_sdot4((int)w.x, (int)a.x, is, false);
+            is = __builtin_amdgcn_sdot4((int)w.y, (int)a.y, is, false);
+            is = __builtin_amdgcn_sdot4((int)w.z, (int)a.z, is, false);
+            is = __builtin_amdgcn_sdot4((int)w.w, (int)a.w, is, false);
             acc[b][t] = fmaf((float)is, sw[u][b], acc[b][t]);
           }
         }
       }
     }
   }
-  finish<RBW, NT, KS, SWIGLU, MOE_F32>(acc, sx, prow, rb0, nrb, out_ld, out, red);
+  finish<RBW, NT, KS, false, MOE_F32>(acc, sx, prow, rb0, nrb, out_ld, out, red);
 }
 
 // ---------------------------------------------------------------- kernels --
@@ -285,16 +382,57 @@ __global__ __launch_bounds__(NW * 64) void bf16_kernel(
   }
 }
 
-template <int KS, int RBW, int NW, int U, int MAXNT, bool SWIGLU>
+// Byte offsets inside a slot of the two weight forms a quantised pass reads:
+// lo = the int4 codes and scales every group uses at low precision; hi = the
+// second section of a high-precision group (pass 1: the int4 residual added to
+// lo; pass 2: the 8-bit codes used instead of lo).
+struct QuantOffsets {
+  size_t lo, lo_s, hi, hi_s;
+};
+
+// Item modes of the quantised passes: 0 = int4, 1 = int4 + int4 residual, 2 = int8.
+template <int MODE, int KS, int RBW, int U, int MAXNT, bool SWIGLU>
+__device__ __forceinline__ void quant_item(const char* slot, const QuantOffsets& o, int K,
+                                           const int8_t* aq, const float* as,
+                                           const int32_t* perm, int k, const FfnItem& it, int rb0,
+                                           int nrb, int out_ld, float* out, float* red) {
+  const char* wb = slot + (MODE == 2 ? o.hi : o.lo);
+  const uint16_t* ws = reinterpret_cast<const uint16_t*>(slot + (MODE == 2 ? o.hi_s : o.lo_s));
+  const char* rb = slot + o.hi;
+  const uint16_t* rs = reinterpret_cast<const uint16_t*>(slot + o.hi_s);
+  const int nkc = MODE == 2 ? K / 32 : K / 64;
+  // with the residual, two chunks per step: half the steps in flight keeps the bytes in flight
+  constexpr int UQ = (MODE == 1 && U > 1) ? U / 2 : U;
+#define TGEMV_Q(NT_, P_)                                                                       \
+  do {                                                                                         \
+    if constexpr (MODE == 2)                                                                   \
+      tile_int8<KS, RBW, U, NT_>(wb, ws, nkc, K, aq, as, P_, rb0, nrb, out_ld, out, red);      \
+    else                                                                                       \
+      tile_int4<KS, RBW, UQ, NT_, SWIGLU, MODE == 1>(wb, ws, rb, rs, nkc, K, aq, as, perm, k,   \
+                                                     P_, rb0, nrb, out_ld, out, red);          \
+  } while (0)
+  int done = 0;
+  for (; it.rows - done >= MAXNT; done += MAXNT) TGEMV_Q(MAXNT, it.row_begin + done);
+  const int rest = it.rows - done, p = it.row_begin + done;
+#define TGEMV_QR(NT_) TGEMV_Q(NT_, p)
+  TGEMV_REST(TGEMV_QR)
+#undef TGEMV_QR
+#undef TGEMV_Q
+}
+
+// The quantised GEMV pass. SPLIT = false: every item on the int4 weights.
+// SPLIT = true (split-precision experts): an item runs at high precision when
+// it is a shared group (expert >= E), when mask is NULL, or when mask[expert]
+// >= 2, else on the int4 weights; the choice is uniform over a workgroup.
+template <int KS, int RBW, int NW, int U, int MAXNT, bool SWIGLU, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void int4_kernel(
     const int8_t* __restrict__ aq, const float* __restrict__ as,
     const int32_t* __restrict__ perm, int k, const FfnItem* __restrict__ items,
     const int32_t* __restrict__ n_items, const char* __restrict__ pool, size_t stride,
-    size_t off_codes, size_t off_scales, int R, int K, int out_ld, int units_per_item,
-    float* __restrict__ out) {
+    QuantOffsets offs, const int32_t* __restrict__ mask, int E, int R, int K, int out_ld,
+    int units_per_item, float* __restrict__ out) {
   __shared__ float red[NW * RBW * 32 * MAXNT];
   const int wave = threadIdx.x >> 6;
-  const int nkc = K / 64;
   const int nrb = R / 32;
   const int units = n_items[0] * units_per_item;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
@@ -302,18 +440,14 @@ __global__ __launch_bounds__(NW * 64) void int4_kernel(
     const int rb0 = ((u - item * units_per_item) * (NW / KS) + wave / KS) * RBW;
     const FfnItem it = items[item];
     const char* slot = pool + (size_t)it.slot * stride;
-    const char* wbase = slot + off_codes;
-    const uint16_t* scales = reinterpret_cast<const uint16_t*>(slot + off_scales);
-    int done = 0;
-    for (; it.rows - done >= MAXNT; done += MAXNT)
-      tile_int4<KS, RBW, U, MAXNT, SWIGLU>(wbase, nkc, K, scales, aq, as, perm, k,
-                                           it.row_begin + done, rb0, nrb, out_ld, out, red);
-    const int rest = it.rows - done, p = it.row_begin + done;
-#define TGEMV_INT4(NT_)                                                                           \
-  tile_int4<KS, RBW, U, NT_, SWIGLU>(wbase, nkc, K, scales, aq, as, perm, k, p, rb0, nrb, out_ld, \
-                                     out, red)
-    TGEMV_REST(TGEMV_INT4)
-#undef TGEMV_INT4
+    bool hi = false;
+    if constexpr (SPLIT) hi = it.expert >= E || mask == nullptr || mask[it.expert] >= 2;
+    if (hi)
+      quant_item<SWIGLU ? 1 : 2, KS, RBW, U, MAXNT, SWIGLU>(slot, offs, K, aq, as, perm, k, it,
+                                                            rb0, nrb, out_ld, out, red);
+    else
+      quant_item<0, KS, RBW, U, MAXNT, SWIGLU>(slot, offs, K, aq, as, perm, k, it, rb0, nrb,
+                                               out_ld, out, red);
   }
 }
 #undef TGEMV_REST

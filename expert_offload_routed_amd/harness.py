@@ -16,7 +16,8 @@ import torch
 from . import binding as B
 from . import workloads as W
 
-WFMT_CODE = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "int4g128": B.MOE_INT4G128}
+WFMT_CODE = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "int4g128": B.MOE_INT4G128,
+             "int4g128_resplit": B.MOE_INT4G128_RESPLIT}
 
 
 def weights_to_host(w: dict) -> dict:
@@ -35,7 +36,12 @@ class ExpertStore:
         self.host = torch.empty(max(n, 1), self.stride, dtype=torch.uint8, pin_memory=True)
         for b in range(n):
             w = (W.shared_expert_weights if shared else W.expert_weights)(shape, b, device=gen_device)
-            B.moe_pack_expert_host(weights_to_host(w), shape.H, shape.F, self.wcode, self.host[b])
+            if self.wcode == B.MOE_INT4G128_RESPLIT:  # quantised from the fp32 masters
+                B.moe_quantize_resplit_host(w["gate"], w["up"], w["down"], shape.H, shape.F,
+                                            self.host[b])
+            else:
+                B.moe_pack_expert_host(weights_to_host(w), shape.H, shape.F, self.wcode,
+                                       self.host[b])
             del w
         self.n = n
 

@@ -14,6 +14,8 @@ Conventions of every tensor produced here (nn.Linear orientation, row-major):
   int4 experts      *_q     uint8 [rows, K/2]: two signed 4-bit codes per byte
                             along K, even K index in the low nibble
                     *_s     bf16 [rows, K/128]: one scale per 128 K values
+  split-precision   gate, up, down in fp32 (the masters the split-precision
+  experts           quantiser reads; see the library's moe_quantize_resplit_host)
 
 Large tensors are drawn with torch's seeded generator on the device given, so
 the full-size workloads can be produced on the GPU in seconds; the values then
@@ -39,7 +41,8 @@ class MoEShape:
     H: int                      # hidden size
     F: int                      # expert FFN (intermediate) size
     n_shared: int = 0           # always-on shared experts (weight 1, resident)
-    wfmt: str = "bf16"          # expert weight storage: "f32" | "bf16" | "int4g128"
+    wfmt: str = "bf16"          # expert weight storage: "f32" | "bf16" | "int4g128" |
+                                # "int4g128_resplit" (fp32 masters, split-precision slots)
     xfmt: str = "bf16"          # tokens and router weight: "f32" | "bf16"
     zipf_s: float | None = None  # Zipf exponent of the per-expert logit bias
     layers: int = 1
@@ -99,7 +102,7 @@ def _gen(shape: MoEShape, kind: str, *idx: int, device="cpu") -> torch.Generator
 
 
 def _tdtype(fmt: str) -> torch.dtype:
-    return {"f32": torch.float32, "bf16": torch.bfloat16}[fmt]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "int4g128_resplit": torch.float32}[fmt]
 
 
 # ---------------------------------------------------------------- tensors ---

@@ -50,9 +50,13 @@ extern "C" {
 enum {
   MOE_F32 = 0,      /* IEEE binary32 */
   MOE_BF16 = 1,     /* bfloat16 (upper half of binary32, round-to-nearest-even) */
-  MOE_INT4G128 = 2  /* expert weights only: signed 4-bit codes, one bf16 scale per
-                       128 consecutive input values of an output row; with these
-                       weights the activations are quantised per row to int8 */
+  MOE_INT4G128 = 2,  /* expert weights only: signed 4-bit codes, one bf16 scale per
+                        128 consecutive input values of an output row; with these
+                        weights the activations are quantised per row to int8 */
+  MOE_INT4G128_RESPLIT = 3  /* expert weights only: split precision (RapidMoE Sec. 4.4,
+                        Algorithm 3): the MOE_INT4G128 weights W^Q of gate/up and
+                        W^L of down, then the residual W^R = int4(W - W^Q) of gate/up
+                        and down at 8 bits (W^H); see moe_slot_layout */
 };
 
 /* status codes */
@@ -138,12 +142,24 @@ int moe_route_permute(const void* x, int x_dtype, const void* w_router, const fl
  *                 codes c0..c7 with byte i = c_i (low nibble) | c_{i+4} (high
  *                 nibble). Scales: s13 at off_s13, [2F, H/128] bf16 row-major
  *                 (rows as W13); s2 at off_s2, [H, F/128].
+ *   MOE_INT4G128_RESPLIT: the four MOE_INT4G128 sections at the same offsets
+ *                 (so a slot of this format is also a MOE_INT4G128 slot, read
+ *                 at the low precision), then the residual of W13 as int4 in
+ *                 the same layout at off_r13 with scales [2F, H/128] at
+ *                 off_rs13, and W2 at 8 bits at off_h2: signed bytes,
+ *                 tile-major, chunk (r / 32) * (K / 32) + c / 32 of 1 KB, lane
+ *                 (r % 32) + 32 ((c % 32) / 16), byte c % 16 of its 16; scales
+ *                 [H, F/128] bf16 at off_hs2 (moe_slot_layout_resplit).
  * Every section starts on a 256-byte boundary; slot_bytes is a multiple of 4096.
  * Returns MOE_EINVAL for a bad format or sizes (H, F multiples of 16; H of 32
  * for bf16; both of 128 for int4).
  */
 int moe_slot_layout(int H, int F, int w_dtype, size_t* slot_bytes,
                     size_t* off_w13, size_t* off_w2, size_t* off_s13, size_t* off_s2);
+
+/* The four extra sections of a MOE_INT4G128_RESPLIT slot (see above). */
+int moe_slot_layout_resplit(int H, int F, size_t* off_r13, size_t* off_rs13, size_t* off_h2,
+                            size_t* off_hs2);
 
 /* moe_pack_expert_host (host only, not on the hot path): write one expert in
  * the slot layout into dst (host, slot_bytes). Inputs are host arrays in
@@ -153,6 +169,40 @@ int moe_slot_layout(int H, int F, int w_dtype, size_t* slot_bytes,
 int moe_pack_expert_host(const void* gate, const void* up, const void* down,
                          const void* gate_s, const void* up_s, const void* down_s,
                          int H, int F, int w_dtype, void* dst);
+
+/* moe_quantize_resplit_host (host only, not on the hot path): quantise one
+ * expert from float32 weights gate, up [F,H] and down [H,F] (nn.Linear
+ * orientation) into a MOE_INT4G128_RESPLIT slot at dst (slot_bytes), following
+ * RapidMoE Algorithm 3 with b_q = b_r = 4:
+ *   quant_b(w), per row and group of 128 inputs: s = bf16(max|w| / (2^(b-1)-1))
+ *     (float32 division, round to nearest even), q = clip(rint(w / s),
+ *     -2^(b-1), 2^(b-1)-1) with the division in float32, q = 0 where s = 0;
+ *   gate, up:  W^Q = quant_4(W),  W^R = quant_4(W - q s)  (float32 residual);
+ *   down:      W^L = quant_4(W),  W^H = quant_8(W).
+ * Returns MOE_EINVAL for bad sizes (H, F multiples of 128). */
+int moe_quantize_resplit_host(const float* gate, const float* up, const float* down, int H, int F,
+                              void* dst);
+
+/* moe_critical_split: the precision of every expert group at one step
+ * (RapidMoE Eq. (4) with Algorithm 1): an expert is critical when its routing
+ * score is at least threshold, the score being its router probability
+ * averaged over the step's tokens (the mean of the softmax of each token's
+ * logits, moe_step_scores) and threshold = Theta * beta(l) * gamma(t) (Eqs.
+ * (3), (5)), computed by the caller. For r in [0, rows), e in [0, E):
+ *   mask_out[r*E + e] = 0                            if mask_in && mask_in[r*E + e] == 0
+ *                       2 if scores[e] >= threshold  (critical: W^H)
+ *                       1 otherwise                  (W^L)
+ * i.e. a moe_expert_ffn group mask for MOE_INT4G128_RESPLIT weights. scores
+ * [E] float32, mask_in (NULL: every group) and mask_out [rows, E] int32, all
+ * device; mask_out may equal mask_in. The comparison is float32. Enqueued on
+ * stream. */
+int moe_critical_split(const float* scores, int E, float threshold, const int32_t* mask_in,
+                       int rows, int32_t* mask_out, hipStream_t stream);
+
+/* moe_step_scores: the router probabilities of every expert averaged over the
+ * step's T tokens, from the logits [T,E] (float32) of moe_route; scores [E]
+ * float32 out (device). Enqueued on stream. */
+int moe_step_scores(const float* logits, int T, int E, float* scores, hipStream_t stream);
 
 /* --------------------------------------------------------------- expert FFN -
  * moe_ffn_workspace_bytes: device workspace moe_expert_ffn needs for these
@@ -177,6 +227,13 @@ size_t moe_ffn_workspace_bytes(int T, int H, int F, int E, int k, int w_dtype);
  *   err_word  [1] int32: MOE_ERR_ABSENT is OR-ed in when a selected group's
  *             lut entry is -1 or not below num_slots (that group is skipped)
  *   workspace device buffer of ws_bytes >= moe_ffn_workspace_bytes(...)
+ * With MOE_INT4G128_RESPLIT, group_mask[e] picks the precision of routed
+ * group e (RapidMoE Algorithm 1): 0 skips it, 1 runs it on W^L (the
+ * MOE_INT4G128 sections), 2 on W^H (gate, up = W^Q + W^R, each int4 x int8
+ * group product scaled and summed in fp32; down on its 8-bit codes); a NULL
+ * mask runs every group on W^H. W^H groups always take the GEMV path (token
+ * tiles of up to 4 rows; decode batch sizes), W^L groups the MOE_INT4G128
+ * paths.
  * With MOE_INT4G128 the tokens and the SwiGLU intermediate are quantised per
  * row to int8 (scale = max|row| / 127, IEEE fp32 division, round to nearest
  * even) before the int4 x int8 products (int32 accumulation per 128 values,

@@ -120,9 +120,23 @@ int moe_ctx_outputs(const moe_layer_ctx* ctx, float** logits, int32_t** ids, flo
 int moe_ctx_set_policy(moe_layer_ctx* ctx, int policy, int window, const double* params);
 
 /* moe_ctx_step_scores: the routing scores [E] (host floats) of the latest
- * step, waiting for that step's router; MOE_EINVAL under LRU or before any
- * step. */
+ * step, waiting for that step's router; MOE_EINVAL under LRU without split
+ * precision, or before any step. */
 int moe_ctx_step_scores(moe_layer_ctx* ctx, float* scores);
+
+/* moe_ctx_set_split: split-precision routing for a context over
+ * MOE_INT4G128_RESPLIT experts (RapidMoE Algorithm 1 with the threshold of
+ * Eqs. (3)-(5)). With enable = 1 every step computes the experts' routing
+ * scores (moe_step_scores) and runs routed expert e of layer l on its
+ * high-precision weights W^H when score[e] >= theta * beta[l] * gamma (the
+ * product in double, rounded to float; beta NULL = 1 for every layer), else on
+ * W^L (moe_critical_split); shared experts always run on W^H. gamma is the
+ * phase factor, 1 for prefill and alpha for decode: call again to switch
+ * phase. With enable = 0 (the default) every group runs on W^H. Applies to
+ * steps enqueued from now on. MOE_EINVAL unless the context's weights are
+ * MOE_INT4G128_RESPLIT (enable = 1) or the constants are finite. */
+int moe_ctx_set_split(moe_layer_ctx* ctx, int enable, float theta, const float* beta,
+                      float gamma);
 
 /* moe_ctx_set_orchestration: where the residency plan runs.
  *   MOE_ORCH_HOST (default): the host plans each step that may miss, after

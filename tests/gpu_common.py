@@ -10,7 +10,7 @@ from expert_offload_routed_amd import workloads as W
 
 # Tolerances of the layer's float outputs (relative L2 over a whole output):
 # fp32 weights and tokens 1e-5; bf16 or int4 weights 2e-2.
-TOL = {"f32": 1e-5, "bf16": 2e-2, "int4g128": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "int4g128": 2e-2, "int4g128_resplit": 2e-2}
 
 
 def say(*a):
@@ -30,16 +30,39 @@ def host_weights(shape, blob, shared=False):
     return {k: v.cpu() for k, v in fn(shape, blob, device="cuda").items()}
 
 
-def oracle_y_rows(shape, x, ids, perm_np, offsets_np, layer, distinct, shared_w=None):
-    """Oracle expert output per sorted position, [T*k, H] float64."""
+_SPLIT_CACHE: dict = {}
+
+
+def split_weights(shape, blob, shared=False):
+    """The oracle's split-precision parts (O.resplit_expert) of a weight set's fp32 masters."""
+    key = (shape.name, blob, shared)
+    if key not in _SPLIT_CACHE:
+        w = host_weights(shape, blob, shared)
+        _SPLIT_CACHE.clear()  # one set at a time: full-size parts are large
+        _SPLIT_CACHE[key] = O.resplit_expert(w["gate"].numpy(), w["up"].numpy(), w["down"].numpy())
+    return _SPLIT_CACHE[key]
+
+
+def oracle_expert(shape, x_rows, blob, critical=True, shared=False):
+    """Oracle output of weight set `blob` on x_rows; split-precision experts at W^H
+    when critical, else at W^L."""
+    if shape.wfmt == "int4g128_resplit":
+        return O.swiglu_expert_split(x_rows, split_weights(shape, blob, shared), critical)
+    return O.expert_forward(x_rows, host_weights(shape, blob, shared))
+
+
+def oracle_y_rows(shape, x, ids, perm_np, offsets_np, layer, distinct, critical=None):
+    """Oracle expert output per sorted position, [T*k, H] float64. critical: the
+    experts run at high precision (split-precision experts; None = all)."""
     k = ids.shape[1]
     x32 = O.as_f32(x)
     y = np.zeros((ids.size, shape.H))
     for e in distinct:
         e = int(e)
         rows = perm_np[offsets_np[e]:offsets_np[e + 1]]
-        w = host_weights(shape, W.blob_of(shape, layer, e))
-        y[offsets_np[e]:offsets_np[e + 1]] = O.expert_forward(x32[rows // k], w)
+        hi = critical is None or e in critical
+        y[offsets_np[e]:offsets_np[e + 1]] = oracle_expert(shape, x32[rows // k],
+                                                           W.blob_of(shape, layer, e), hi)
     return y
 
 

@@ -230,3 +230,76 @@ def test_policy_rejects_bad_parameters(lib):
     with pytest.raises(B.MoeError):
         pol.observe(0, np.zeros(4, np.float32), np.array([4]))
     assert not pol.state.any()
+
+
+def test_slot_layout_resplit_extends_int4(lib):
+    H, F = 7168, 2048
+    base = B.moe_slot_layout(H, F, B.MOE_INT4G128)
+    lay = B.moe_slot_layout(H, F, B.MOE_INT4G128_RESPLIT)
+    ext = B.moe_slot_layout_resplit(H, F)
+    for key in ("off_w13", "off_w2", "off_s13", "off_s2"):
+        assert lay[key] == base[key]
+    # sections in order, aligned, each large enough for what it holds
+    sizes = [("off_s2", H * (F // 128) * 2), ("off_r13", 2 * F * H // 2),
+             ("off_rs13", 2 * F * (H // 128) * 2), ("off_h2", H * F), ("off_hs2", H * (F // 128) * 2)]
+    offs = {**lay, **ext}
+    for (a, size), (b, _) in zip(sizes, sizes[1:]):
+        assert offs[b] % 256 == 0 and offs[b] >= offs[a] + size
+    assert lay["slot_bytes"] % 4096 == 0 and lay["slot_bytes"] >= offs["off_hs2"] + H * (F // 128) * 2
+    with pytest.raises(B.MoeError):
+        B.moe_slot_layout_resplit(256 + 64, 256)
+
+
+def _untile_int8(buf, R, K):
+    """Inverse of the documented tile-major 8-bit layout: signed codes [R, K]."""
+    b = buf.view(torch.int8).numpy().reshape(R // 32, K // 32, 2, 32, 16)  # rb, kc, khalf, row, byte
+    return b.transpose(0, 3, 1, 2, 4).reshape(R, K).astype(np.int64)
+
+
+def _resplit_inputs(H, F, seed):
+    """float32 expert weights with the cases the quantiser must decide alike: an
+    all-zero group (scale 0), a lone outlier, and values at exact half steps."""
+    g = torch.Generator().manual_seed(seed)
+    gate = torch.randn(F, H, generator=g) * 0.02
+    up = torch.randn(F, H, generator=g) * 0.02
+    down = torch.randn(H, F, generator=g) * 0.02
+    gate[0, :128] = 0.0
+    up[1, 128:256] = 0.0
+    gate[2, 5] = 1.5
+    down[3, 7] = -0.75
+    # a group whose scale is 2^-6 exactly (max 7 * 2^-6) holding 2.5 and -3.5 steps
+    gate[4, :128] = 0.0
+    gate[4, 0], gate[4, 1], gate[4, 2] = 7 * 2.0 ** -6, 2.5 * 2.0 ** -6, -3.5 * 2.0 ** -6
+    return gate, up, down
+
+
+@pytest.mark.parametrize("H,F,seed", [(256, 256, 0), (384, 128, 1)])
+def test_quantize_resplit_matches_oracle(lib, H, F, seed):
+    gate, up, down = _resplit_inputs(H, F, seed)
+    ref = O.resplit_expert(gate.numpy(), up.numpy(), down.numpy())
+    lay = {**B.moe_slot_layout(H, F, B.MOE_INT4G128_RESPLIT), **B.moe_slot_layout_resplit(H, F)}
+    dst = torch.zeros(lay["slot_bytes"], dtype=torch.uint8)
+    B.moe_quantize_resplit_host(gate, up, down, H, F, dst)
+
+    def sec(key, nbytes):
+        return dst[lay[key]:lay[key] + nbytes]
+
+    def scales(key, R, G):
+        return sec(key, R * G * 2).view(torch.bfloat16).float().view(R, G).numpy()
+
+    q13 = _untile_int4(sec("off_w13", 2 * F * H // 2), 2 * F, H)
+    r13 = _untile_int4(sec("off_r13", 2 * F * H // 2), 2 * F, H)
+    s13, rs13 = scales("off_s13", 2 * F, H // 128), scales("off_rs13", 2 * F, H // 128)
+    for j, name in enumerate(("gate", "up")):
+        assert np.array_equal(q13[j::2], ref[name + "_q"])
+        assert np.array_equal(r13[j::2], ref[name + "_rq"])
+        assert np.array_equal(s13[j::2], ref[name + "_s"])
+        assert np.array_equal(rs13[j::2], ref[name + "_rs"])
+    assert np.array_equal(_untile_int4(sec("off_w2", H * F // 2), H, F), ref["down_lq"])
+    assert np.array_equal(scales("off_s2", H, F // 128), ref["down_ls"])
+    assert np.array_equal(_untile_int8(sec("off_h2", H * F), H, F), ref["down_hq"])
+    assert np.array_equal(scales("off_hs2", H, F // 128), ref["down_hs"])
+    # the planted cases: zero groups code to 0 with scale 0; half steps round to even
+    assert ref["gate_s"][0, 0] == 0 and not ref["gate_q"][0, :128].any()
+    assert ref["gate_s"][4, 0] == 2.0 ** -6
+    assert list(ref["gate_q"][4, :3]) == [7, 2, -4]

@@ -12,7 +12,7 @@ import oracle as O
 from expert_offload_routed_amd import binding as B
 from expert_offload_routed_amd import harness as Hn
 from expert_offload_routed_amd import workloads as W
-from gpu_common import TOL, check_routing, host_weights, oracle_y_rows, rel_l2, say
+from gpu_common import TOL, check_routing, host_weights, oracle_expert, oracle_y_rows, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -295,18 +295,24 @@ def test_slot_fill_rejects_pageable_host_memory():
 
 # --------------------------------------------------------------- whole layer --
 def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, policy=None,
-                    device_plan=False):
+                    device_plan=False, split=None):
     """Run steps through the harness and compare every step with the oracle.
 
     policy = (kind, window, params): the runtime plans under that eviction policy and the
     oracle's scored planner records the same step scores (the kernel's own, checked against
     the oracle's softmax of the kernel's logits) before each plan.
-    device_plan: the runtime plans and fills on the GPU (device orchestration)."""
+    device_plan: the runtime plans and fills on the GPU (device orchestration).
+    split = (theta, beta, gamma): split-precision routing; the oracle takes the critical set
+    from the kernel's own step scores (checked against its softmax) in float32."""
     t_max = max(Ts)
     residency = W.initial_residency(shape, slots, mode)
     layer_obj = Hn.SlotCacheLayer(shape, slots, residency, t_max)
     if device_plan:
         layer_obj.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
+    if split is not None:
+        theta, beta, gamma = split
+        layer_obj.ctx.set_split(True, theta, beta, gamma)
+    n_hi = n_lo = 0
     if policy is None:
         planner = O.LruSlotPlanner(slots, shape.layers, shape.E, residency)
     else:
@@ -315,7 +321,6 @@ def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, pol
         pol = (O.MinusRecentScore(shape.layers, shape.E, window) if kind == B.MOE_POLICY_MRS else
                O.RoutingHistoryScore(shape.layers, shape.E, window, weights=params[:4], lam=params[4]))
         planner = O.ScoredSlotPlanner(slots, shape.layers, shape.E, pol, residency)
-    sh_w = [host_weights(shape, j, shared=True) for j in range(shape.n_shared)]
     order = layers_order or [0]
     for step, T in enumerate(Ts):
         for layer in order:
@@ -332,12 +337,19 @@ def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, pol
             pr = O.permute(ids, shape.E)
             assert o["perm"].cpu().numpy().tolist() == pr["perm"].tolist()
             assert o["inv"].cpu().numpy().tolist() == pr["inv"].tolist()
+            if policy is not None or split is not None:
+                sc = layer_obj.ctx.step_scores()
+                np.testing.assert_allclose(sc, O.step_scores(o["logits"].cpu().numpy()), rtol=2e-6, atol=1e-7)
             if policy is None:
                 planner.plan(layer, pr["distinct"])
             else:
-                sc = layer_obj.ctx.step_scores()
-                np.testing.assert_allclose(sc, O.step_scores(o["logits"].cpu().numpy()), rtol=2e-6, atol=1e-7)
                 planner.plan(layer, pr["distinct"], sc)
+            crit = None
+            if split is not None:
+                th = O.critical_threshold(theta, 1.0 if beta is None else beta[layer], "decode", gamma)
+                crit = set(O.critical_experts(sc, pr["distinct"], th))
+                n_hi += len(crit)
+                n_lo += len(pr["distinct"]) - len(crit)
             lut_h, owner_h, last_use_h, clock_h = layer_obj.tables()
             assert layer_obj.lut.cpu().numpy().reshape(shape.layers, shape.E).tolist() == planner.lut.tolist()
             assert lut_h.reshape(shape.layers, shape.E).tolist() == planner.lut.tolist()
@@ -345,15 +357,19 @@ def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, pol
             # oracle output on the kernel's selection, oracle weights from its own logits
             ref_logits = O.router_logits(x, wr, b)
             wts = O.gate_weights(ref_logits, ids)
-            yr = oracle_y_rows(shape, x, ids, pr["perm"], pr["offsets"], layer, pr["distinct"])
+            yr = oracle_y_rows(shape, x, ids, pr["perm"], pr["offsets"], layer, pr["distinct"],
+                               critical=crit)
             y_assign = yr[pr["inv"]].reshape(T, shape.k, shape.H)
             x32 = O.as_f32(x)
-            ysh = [O.expert_forward(x32, w) for w in sh_w]
+            ysh = [oracle_expert(shape, x32, j, True, shared=True) for j in range(shape.n_shared)]
             ref = O.combine(y_assign, wts, ysh)
             r = rel_l2(out.float().cpu().numpy(), ref)
             cnt = layer_obj.counters()
-            say(f"  rel L2 {r:.3e}; totals so far {cnt}")
+            say(f"  rel L2 {r:.3e}; totals so far {cnt}" +
+                (f"; critical {sorted(crit)}" if crit is not None else ""))
             assert r <= TOL[shape.wfmt]
+    if split is not None:
+        assert n_hi > 0 and n_lo > 0, (n_hi, n_lo)  # both precisions were exercised
 
 
 def test_layer_tiny_fp32_identity():
@@ -475,6 +491,33 @@ def test_device_orchestration_rejects_more_routed_than_slots():
     x = W.tokens(shape, 2, step=0, device=_dev())  # T*k = 6 > 4 slots
     with pytest.raises(B.MoeError):
         layer_obj.forward(x)
+
+
+SPLIT = W.reduced(DSV3, wfmt="int4g128_resplit")
+
+
+def test_layer_split_precision_misses_shared():
+    """Split-precision experts with misses (fills in waves) and a shared expert (always W^H)."""
+    shape = W.reduced(SPLIT, E=16, k=4, H=256, F=128, layers=2)
+    _run_layer_case(shape, 12, "zipf_rank", [1, 4, 2, 24, 1], layers_order=[0, 1],
+                    split=(0.125, [1.0, 0.5], 0.75))
+
+
+def test_layer_split_precision_all_resident():
+    shape = W.reduced(SPLIT, E=16, k=4, H=256, F=128)
+    _run_layer_case(shape, 16, "zipf_rank", [1, 2, 4, 40], split=(0.0625, None, 1.0))
+
+
+def test_layer_split_precision_device_orchestration():
+    shape = W.reduced(SPLIT, E=32, k=8, H=256, F=128, layers=2)
+    _run_layer_case(shape, 24, "zipf_rank", [1, 2, 1, 3], layers_order=[0, 1], device_plan=True,
+                    split=(0.03125, [1.0, 2.0], 1.0))
+
+
+def test_layer_split_precision_with_policy():
+    shape = W.reduced(SPLIT, E=16, k=4, H=256, F=128, layers=2)
+    _run_layer_case(shape, 12, "zipf_rank", [1, 3, 1, 2], layers_order=[0, 1],
+                    policy=(B.MOE_POLICY_MRS, 4, None), split=(0.125, None, 0.5))
 
 
 def test_layer_shared_experts():
