@@ -358,6 +358,33 @@ def split_case(shape, store, T, steps, warmup, critical_share=0.25):
     return res
 
 
+def staging_case(shape, cfg, store, S, T, steps, warmup):
+    """Prefill of T tokens per layer through the workload's own cache (S slots): the decode
+    cache alone (misses filled in waves), then with full-layer staging at the pages' switch
+    floor(resident slots of the layer / k), the next layer loading while one computes."""
+    res = {}
+    for staged in (False, True):
+        lay = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]), t_max=T,
+                                store=store, staging=staged)
+        if staged:
+            lay.ctx.set_staging(True, -1)
+        s0 = lay.ctx.stage_counters()
+        label = f"T={T} prefill, {S} slots, " + ("full-layer staging" if staged else "decode cache only")
+        r = timed(lay, shape, T, steps, warmup, label)
+        s1 = lay.ctx.stage_counters()
+        # staged steps of the timed region only: warm-up steps are counted before it
+        r["stage"] = {k: s1[k] - s0[k] for k in s1}
+        r["copy_bytes_per_step"] = (r["fills_per_step"] * store.stride
+                                    + (s1["stage_copies"] - s0["stage_copies"]) / (steps + warmup)
+                                    * store.stride)
+        print(f"# {label}: copies {r['copy_bytes_per_step'] / 1e9:.2f} GB/step, {r['stage']}",
+              file=sys.stderr, flush=True)
+        res["staging" if staged else "decode_cache"] = r
+        del lay
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,7 +399,8 @@ def main():
                          "policy), graph (device orchestration, eager vs one HIP graph per step), "
                          "split (split-precision experts: all low, split, all high; the "
                          "workload's shape with split-precision slots and 16 distinct weight "
-                         "sets), T<n> (hit path at n tokens), calib_copy")
+                         "sets), staging (prefill through the workload's cache with and without "
+                         "full-layer staging), T<n> (hit path at n tokens), calib_copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU form of "
@@ -386,6 +414,12 @@ def main():
     shape = W.shape_of(args.workload)
     plan = PLANS[args.workload]
     cfg = W.WORKLOADS[args.workload]
+    if args.case == "staging":
+        S = plan["miss"][0][0]
+        store = Hn.ExpertStore(shape)
+        for T in ([256] if shape.layers > 1 else [max(plan["hit"])]):
+            staging_case(shape, cfg, store, S, T, K, Wm)
+        return
     if args.case == "split":
         # fp32 masters quantised by the library; 16 weight sets back the E slots (each slot
         # its own memory, so the HBM traffic is that of E distinct experts)

@@ -61,6 +61,8 @@ _SIGNATURES = {
     "moe_ctx_set_orchestration": (_i32, [_vp, _i32]),
     "moe_ctx_step_scores": (_i32, [_vp, _vp]),
     "moe_ctx_set_split": (_i32, [_vp, _i32, ctypes.c_float, _vp, ctypes.c_float]),
+    "moe_ctx_set_staging": (_i32, [_vp, _i32, _i32, _i32]),
+    "moe_ctx_stage_counters": (_i32, [_vp, _vp]),
     "moe_ctx_counters": (_i32, [_vp, _vp]),
     "moe_ctx_ffn_time": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_long)]),
 }
@@ -383,6 +385,7 @@ class LayerContext:
                  fill_stream=None):
         dev = pool.device
         self.t_max, self.H, self.E, self.k, self.L, self.S = t_max, H, E, k, L, S
+        self.pool_slots = pool.numel() // slot_stride
         self.compute_stream = compute_stream or torch.cuda.current_stream(dev)
         self.fill_stream = fill_stream or torch.cuda.Stream(device=dev)
         nbytes = moe_ctx_workspace_bytes(t_max, H, F, E, k, w_dtype, n_shared)
@@ -481,6 +484,16 @@ class LayerContext:
         self._split_beta = b
         _call("moe_ctx_set_split", self.handle, int(enable), ctypes.c_float(theta),
               _host(b) if b is not None else None, ctypes.c_float(gamma))
+
+    def set_staging(self, enable: bool, threshold: int = -1) -> None:
+        """Prefill full-layer staging in two buffers of E slots after the routed and shared
+        slots of the pool (threshold -1: floor(resident slots of the layer / k))."""
+        _call("moe_ctx_set_staging", self.handle, int(enable), threshold, self.pool_slots)
+
+    def stage_counters(self) -> dict:
+        out = np.zeros(2, np.int64)
+        _call("moe_ctx_stage_counters", self.handle, _host(out))
+        return {"staged_steps": int(out[0]), "stage_copies": int(out[1])}
 
     def step_scores(self) -> np.ndarray:
         """Routing scores [E] of the latest step (needs split precision or a policy other

@@ -282,32 +282,44 @@ void launch_gemv(const int8_t* aq, const float* as, const int32_t* perm, int k,
   const long long units = (long long)upi * max_items;
   const unsigned grid = (unsigned)(units < tgemv::kGridCap ? units : tgemv::kGridCap);
   if (grid == 0) return;
-  constexpr int U = RBW >= 4 ? 2 : 4;
+  constexpr int U = 2;
   hipLaunchKernelGGL((tgemv::int4_kernel<KS, RBW, NW, U, MAXNT, SWIGLU, SPLIT>), dim3(grid),
                      dim3(NW * 64), 0, s, aq, as, perm, k, items, n_items, pool, stride, offs, mask,
                      E, R, K, out_ld, upi, out);
 }
 
-template <int RBW, int MAXNT, bool SWIGLU, bool SPLIT>
-void launch_gemv_ks(int ks, const int8_t* aq, const float* as, const int32_t* perm, int k,
-                    const FfnItem* items, const int32_t* n_items, int max_items, const char* pool,
-                    size_t stride, const tgemv::QuantOffsets& offs, const int32_t* mask, int E,
-                    int R, int K, int out_ld, float* out, hipStream_t s) {
-#define MOE_W4_KS(KS_)                                                                            \
-  launch_gemv<KS_, RBW, MAXNT, SWIGLU, SPLIT>(aq, as, perm, k, items, n_items, max_items, pool,   \
-                                              stride, offs, mask, E, R, K, out_ld, out, s)
-  switch (ks) {
-    case 1: MOE_W4_KS(1); break;
-    case 2: MOE_W4_KS(2); break;
-    case 4: MOE_W4_KS(4); break;
-    default: MOE_W4_KS(8); break;
-  }
-#undef MOE_W4_KS
-}
-
 // One GEMV pass (first: gate/up with the SwiGLU epilogue; else: down). With
 // split = true the items of split-precision experts pick their precision from
 // mask (tgemv::int4_kernel).
+template <int MAXNT, bool FIRST, bool SPLIT>
+void launch_gemv_split(const tgemv::Split& sp, const int8_t* aq, const float* as,
+                       const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
+                       int max_items, const char* pool, size_t stride,
+                       const tgemv::QuantOffsets& offs, const int32_t* mask, int E, int R, int K,
+                       int ld, float* out, hipStream_t s) {
+#define MOE_W4_L(KS_, RBW_)                                                                       \
+  launch_gemv<KS_, RBW_, MAXNT, FIRST, SPLIT>(aq, as, perm, k, items, n_items, max_items, pool,   \
+                                              stride, offs, mask, E, R, K, ld, out, s)
+  if (sp.rbw == 2) {
+    // 1024-thread groups hold 128 VGPRs: one-row tiles only
+    if constexpr (MAXNT == 1) {
+      if (sp.ks >= 16) {
+        MOE_W4_L(16, 2);
+        return;
+      }
+    }
+    MOE_W4_L(8, 2);
+    return;
+  }
+  switch (sp.ks) {
+    case 1: MOE_W4_L(1, 4); break;
+    case 2: MOE_W4_L(2, 4); break;
+    case 4: MOE_W4_L(4, 4); break;
+    default: MOE_W4_L(8, 4); break;
+  }
+#undef MOE_W4_L
+}
+
 void launch_gemv_any(bool first, bool split, int nt, const int8_t* aq, const float* as,
                      const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
                      int max_items, const char* pool, size_t stride, const SlotLayout& lay,
@@ -317,8 +329,8 @@ void launch_gemv_any(bool first, bool split, int nt, const int8_t* aq, const flo
       first ? tgemv::QuantOffsets{lay.off_w13, lay.off_s13, lay.off_r13, lay.off_rs13}
             : tgemv::QuantOffsets{lay.off_w2, lay.off_s2, lay.off_h2, lay.off_hs2};
   const tgemv::Split sp = tgemv::choose_split_int4(R / 32 * max_items, K / 64);
-#define MOE_W4_SPLIT(NT_, FIRST_, SPLIT_)                                                        \
-  launch_gemv_ks<4, NT_, FIRST_, SPLIT_>(sp.ks, aq, as, perm, k, items, n_items, max_items, pool, \
+#define MOE_W4_SPLIT(NT_, FIRST_, SPLIT_)                                                       \
+  launch_gemv_split<NT_, FIRST_, SPLIT_>(sp, aq, as, perm, k, items, n_items, max_items, pool,  \
                                          stride, offs, mask, E, R, K, ld, out, s)
 #define MOE_W4_NT(NT_)                                     \
   do {                                                     \

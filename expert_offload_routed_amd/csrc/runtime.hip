@@ -92,6 +92,17 @@ struct moe_layer_ctx {
   // split-precision experts (moe_ctx_set_split): thresholds per layer
   int split;
   std::vector<float> split_th;
+  // prefill full-layer staging (moe_ctx_set_staging): two buffers of E slots each
+  int stage;               // 0: off; 1: steps with T >= the layer's threshold are staged
+  int stage_thr;           // token threshold; -1: floor(resident slots of the layer / k)
+  int stage_slot0;         // first staging slot: buffer b holds expert e in slot0 + b*E + e
+  int32_t* d_stage_lut;    // [2E] device: those slots, one expert->slot row per buffer
+  int buf_layer[2];        // layer each buffer holds (or is loading); -1: none
+  int buf_last;            // buffer of the latest staged step
+  hipEvent_t ev_ready[2];  // the buffer's load finished (fill stream)
+  hipEvent_t ev_free[2];   // the last compute that read the buffer finished (compute stream)
+  int64_t stage_steps, stage_copies;
+  int next_hint;           // layer of the next step (moe_ctx_forward_steps); -1: layer + 1
   // device orchestration (moe_ctx_set_orchestration)
   int orch;                 // 0: plans on the host; 1: plans and fills on the device
   const char* store_dev;    // device address of the pinned host store
@@ -322,9 +333,13 @@ void destroy(moe_layer_ctx* c) {
     if (c->tev1[i]) (void)hipEventDestroy(c->tev1[i]);
   }
   void* dev[] = {c->d_order, c->d_last_use, c->d_clock, c->d_blob, c->d_fills, c->d_nfills,
-                 c->d_counters};
+                 c->d_counters, c->d_stage_lut};
   for (void* p : dev)
     if (p) (void)hipFree(p);
+  for (int b = 0; b < 2; ++b) {
+    if (c->ev_ready[b]) (void)hipEventDestroy(c->ev_ready[b]);
+    if (c->ev_free[b]) (void)hipEventDestroy(c->ev_free[b]);
+  }
   if (c->ev_fill) (void)hipEventDestroy(c->ev_fill);
   if (c->ev_compute) (void)hipEventDestroy(c->ev_compute);
   delete c;
@@ -505,6 +520,15 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   for (double& v : c->params) v = 0.0;
   c->last_ring = -1;
   c->split = 0;
+  c->stage = 0;
+  c->stage_thr = -1;
+  c->stage_slot0 = S + n_shared;
+  c->d_stage_lut = nullptr;
+  c->buf_layer[0] = c->buf_layer[1] = -1;
+  c->buf_last = -1;
+  c->ev_ready[0] = c->ev_ready[1] = c->ev_free[0] = c->ev_free[1] = nullptr;
+  c->stage_steps = c->stage_copies = 0;
+  c->next_hint = -1;
   c->orch = 0;
   c->store_dev = nullptr;
   c->d_order = nullptr;
@@ -690,7 +714,7 @@ extern "C" int moe_ctx_set_orchestration(moe_layer_ctx* c, int mode) {
     c->orch = 0;
     return MOE_OK;
   }
-  MOE_CHECK_ARG(c->S <= kDevPlanMaxS && c->policy == MOE_POLICY_LRU);
+  MOE_CHECK_ARG(c->S <= kDevPlanMaxS && c->policy == MOE_POLICY_LRU && !c->stage);
   void* dev = nullptr;
   if (hipHostGetDevicePointer(&dev, const_cast<void*>(static_cast<const void*>(c->host_store)), 0) !=
           hipSuccess ||
@@ -761,6 +785,119 @@ int forward_device(moe_layer_ctx* c, int layer, const void* x, int T, const void
   return moe_combine(c->y_perm, c->inv, c->topw, T, k, H, shared_y, c->n_shared, out, out_dtype, c->cs);
 }
 
+// ------------------------------------------------------ full-layer staging --
+extern "C" int moe_ctx_set_staging(moe_layer_ctx* c, int enable, int threshold, int pool_slots) {
+  MOE_CHECK_ARG(c && (enable == 0 || enable == 1) && threshold >= -1);
+  if (!enable) {
+    c->stage = 0;
+    return MOE_OK;
+  }
+  MOE_CHECK_ARG(!c->orch);  // staged steps are planned on the host
+  MOE_CHECK_ARG((long long)pool_slots >= (long long)c->stage_slot0 + 2LL * c->E);
+  hipError_t e = hipSuccess;
+  if (!c->d_stage_lut) {
+    std::vector<int32_t> h(2 * (size_t)c->E);
+    for (int i = 0; i < 2 * c->E; ++i) h[i] = c->stage_slot0 + i;
+    e = hipMalloc(&c->d_stage_lut, h.size() * sizeof(int32_t));
+    if (e == hipSuccess)
+      e = hipMemcpy(c->d_stage_lut, h.data(), h.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+      e = hipEventCreateWithFlags(&c->ev_ready[b], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_free[b], hipEventDisableTiming);
+      // nothing has read or is loading either buffer yet
+      if (e == hipSuccess) e = hipEventRecord(c->ev_free[b], c->cs);
+      if (e == hipSuccess) e = hipEventRecord(c->ev_ready[b], c->cs);
+    }
+    if (e != hipSuccess) return moe_hip_status(e);
+  }
+  c->stage = 1;
+  c->stage_thr = threshold;
+  return MOE_OK;
+}
+
+extern "C" int moe_ctx_stage_counters(moe_layer_ctx* c, int64_t* out) {
+  MOE_CHECK_ARG(c && out);
+  out[0] = c->stage_steps;
+  out[1] = c->stage_copies;
+  return MOE_OK;
+}
+
+namespace {
+
+// Load every routed expert of `layer` into staging buffer b on the fill stream, once the
+// compute that last read the buffer has finished; consecutive weight sets go in one copy.
+int stage_load(moe_layer_ctx* c, int b, int layer) {
+  hipError_t e = hipStreamWaitEvent(c->fs, c->ev_free[b], 0);
+  const int E = c->E;
+  for (int e0 = 0; e0 < E && e == hipSuccess;) {
+    const int32_t blob0 = c->blob_of[(size_t)layer * E + e0];
+    int n = 1;
+    while (e0 + n < E && c->blob_of[(size_t)layer * E + e0 + n] == blob0 + n) ++n;
+    e = hipMemcpyAsync(c->pool + (size_t)(c->stage_slot0 + b * E + e0) * c->stride,
+                       c->host_store + (size_t)blob0 * c->stride, (size_t)n * c->stride,
+                       hipMemcpyHostToDevice, c->fs);
+    e0 += n;
+  }
+  if (e == hipSuccess) e = hipEventRecord(c->ev_ready[b], c->fs);
+  if (e != hipSuccess) return moe_hip_status(e);
+  c->buf_layer[b] = layer;
+  c->stage_copies += E;
+  return MOE_OK;
+}
+
+// One staged step (MoE-CORE summary page, Mechanism): every routed expert of the layer
+// runs from a staging buffer holding the whole layer; the other buffer then starts
+// loading the next layer. The decode cache and its tables are not touched.
+int forward_staged(moe_layer_ctx* c, int layer, const void* x, int T, const void* w_router,
+                   const float* bias, void* out, int out_dtype) {
+  const int E = c->E, k = c->k, H = c->H, F = c->F, nsh = c->n_shared;
+  FrontPlan fp{};
+  fp.scores = c->split ? c->scores : nullptr;
+  bool scored = false;
+  int rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
+                              c->topw, c->counts, c->offsets, c->perm, c->inv, c->dist, c->dist + E,
+                              c->sync, fp.scores ? &fp : nullptr, nullptr, &scored, c->cs);
+  if (rc != MOE_OK) return rc;
+  if (c->split) {
+    if (!scored) launch_step_scores(c->logits, T, E, c->scores, c->cs);
+    launch_critical_split(c->scores, E, c->split_th[layer], nullptr, 1, c->crit, c->cs);
+  }
+  // the buffer holding the layer, else the one the latest staged step did not read
+  int b = c->buf_layer[0] == layer ? 0 : c->buf_layer[1] == layer ? 1 : (c->buf_last == 0 ? 1 : 0);
+  if (c->buf_layer[b] != layer && (rc = stage_load(c, b, layer)) != MOE_OK) return rc;
+  hipError_t e = hipStreamWaitEvent(c->cs, c->ev_ready[b], 0);
+  if (e != hipSuccess) return moe_hip_status(e);
+  const bool timing = c->timing != 0;
+  if (timing) {
+    collect_timing(c, false);
+    const int tr = (c->t_head + c->t_count) % kRing;
+    if ((e = hipEventRecord(c->tev0[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
+  }
+  if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, c->d_stage_lut + (size_t)b * E,
+                       c->split ? c->crit : nullptr, nsh, c->S, c->pool, c->stride,
+                       c->stage_slot0 + 2 * E, c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws,
+                       c->ws_bytes, c->cs)) != MOE_OK)
+    return rc;
+  if (timing) {
+    const int tr = (c->t_head + c->t_count) % kRing;
+    if ((e = hipEventRecord(c->tev1[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
+    c->t_count += 1;
+  }
+  if ((e = hipEventRecord(c->ev_free[b], c->cs)) != hipSuccess) return moe_hip_status(e);
+  c->buf_last = b;
+  c->stage_steps += 1;
+  // prefetch: the other buffer loads the next layer while this one computes
+  const int nl = c->next_hint >= 0 ? c->next_hint : (layer + 1) % c->L;
+  if (nl < c->L && nl != layer && c->buf_layer[1 - b] != nl &&
+      (rc = stage_load(c, 1 - b, nl)) != MOE_OK)
+    return rc;
+  const float* shared_y = nsh ? c->y_perm + (size_t)T * k * H : nullptr;
+  return moe_combine(c->y_perm, c->inv, c->topw, T, k, H, shared_y, c->n_shared, out, out_dtype,
+                     c->cs);
+}
+
+}  // namespace
+
 extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int T,
                                  const void* w_router, const float* bias, void* out, int out_dtype,
                                  int32_t* stats) {
@@ -786,6 +923,12 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
                             hipMemcpyHostToDevice, c->cs)) != hipSuccess)
       return moe_hip_status(e);
     c->sh_T = T;
+  }
+  // staged: a layer not wholly resident, at or above the token threshold
+  if (c->stage && c->resident[layer] < E &&
+      T >= (c->stage_thr >= 0 ? c->stage_thr : c->resident[layer] / k)) {
+    if (stats) stats[0] = stats[1] = stats[2] = stats[3] = -1;
+    return forward_staged(c, layer, x, T, w_router, bias, out, out_dtype);
   }
   if (c->orch) {
     if (T * k > c->S) return MOE_EUNSUPPORTED;  // more routed experts than slots: plan on the host
@@ -928,8 +1071,10 @@ extern "C" int moe_ctx_forward_steps(moe_layer_ctx* c, int n, const int32_t* lay
                                      int out_dtype) {
   MOE_CHECK_ARG(c && n >= 0 && (n == 0 || (layers && xs && w_routers && biases && outs)));
   for (int i = 0; i < n; ++i) {
+    c->next_hint = i + 1 < n ? layers[i + 1] : -1;  // the staging prefetch follows the given order
     const int rc = moe_layer_forward(c, layers[i], xs[i], T, w_routers[i], biases[i], outs[i],
                                      out_dtype, nullptr);
+    c->next_hint = -1;
     if (rc != MOE_OK) return rc;
   }
   return MOE_OK;

@@ -472,11 +472,14 @@ inline Split choose_split_bf16(int row_blocks_total, int nchunks, int maxnt) {
   return sp;
 }
 inline Split choose_split_int4(int row_blocks_total, int nchunks) {
+  // long rows (the gate/up pass of wide experts): two row blocks per wave, 8 or 16 waves
+  // per row block; a few hundred workgroups of 8 waves leave a second, mostly idle round
+  // on part of the 256 CUs, so small passes take 16 waves (measured at 9 and 33 groups of
+  // 4096 x 7168)
+  if (nchunks >= 64) return Split{2, (row_blocks_total + 1) / 2 < 1024 ? 16 : 8};
   Split sp{4, 1};
   const long long blocks = (row_blocks_total + 3) / 4;
-  if (nchunks >= 64)
-    sp.ks = 8;
-  else if (blocks < 1024)
+  if (blocks < 1024)
     while (sp.ks < 4 && nchunks / (sp.ks * 2) >= 8) sp.ks *= 2;
   return sp;
 }

@@ -62,7 +62,8 @@ class SlotCacheLayer:
     """
 
     def __init__(self, shape: W.MoEShape, slots: int, residency: list, t_max: int,
-                 store: ExpertStore | None = None, device="cuda", compute_stream=None):
+                 store: ExpertStore | None = None, device="cuda", compute_stream=None,
+                 staging: bool = False):
         self.shape, self.S, self.t_max, self.device = shape, slots, t_max, device
         sh = shape
         self.E, self.k, self.H, self.F, self.L = sh.E, sh.k, sh.H, sh.F, sh.layers
@@ -70,8 +71,10 @@ class SlotCacheLayer:
         self.stride, self.wcode = self.store.stride, self.store.wcode
         dev = torch.device(device)
         self.n_sh = sh.n_shared
-        # the S routed slots, then the n_shared slots of the always-resident shared experts
-        self.pool = torch.empty((slots + self.n_sh) * self.stride, dtype=torch.uint8, device=dev)
+        # the S routed slots, then the n_shared slots of the always-resident shared experts,
+        # then (staging) two buffers of E slots for prefill full-layer staging
+        self.pool_slots = slots + self.n_sh + (2 * self.E if staging else 0)
+        self.pool = torch.empty(self.pool_slots * self.stride, dtype=torch.uint8, device=dev)
         self.lut = torch.full((self.L * self.E,), -1, dtype=torch.int32, device=dev)
         self.owner = torch.full((slots,), -1, dtype=torch.int32, device=dev)
         self.tags = torch.zeros(slots, dtype=torch.int64, device=dev)
@@ -80,7 +83,7 @@ class SlotCacheLayer:
         self.sh_pool = None
         if self.n_sh:
             self.sh_store = ExpertStore(sh, shared=True)
-            self.sh_pool = self.pool[slots * self.stride:]
+            self.sh_pool = self.pool[slots * self.stride:(slots + self.n_sh) * self.stride]
             for s in range(self.n_sh):
                 self.sh_pool[s * self.stride:(s + 1) * self.stride].copy_(self.sh_store.host[s])
         blob_of = np.array([W.blob_of(sh, l, e) for l in range(self.L) for e in range(self.E)], np.int32)

@@ -138,6 +138,28 @@ int moe_ctx_step_scores(moe_layer_ctx* ctx, float* scores);
 int moe_ctx_set_split(moe_layer_ctx* ctx, int enable, float theta, const float* beta,
                       float gamma);
 
+/* moe_ctx_set_staging: prefill full-layer staging (MoE-CORE summary page,
+ * Mechanism). Two staging buffers, each holding every routed expert of one
+ * layer, live in the pool after the routed and shared slots: buffer b holds
+ * expert e in slot S + n_shared + b*E + e (the pool allocation must hold
+ * pool_slots >= S + n_shared + 2E slots; the caller owns it). With enable = 1
+ * a step of layer l whose layer is not wholly resident and whose token count
+ * T >= threshold (threshold = -1: floor(K_l / k), K_l = the decode cache's
+ * slots holding layer l's experts) runs every routed expert from the buffer
+ * holding layer l, loading it first (one copy per run of consecutive weight
+ * sets, on the fill stream, after the compute that last read the buffer);
+ * once the step's compute is enqueued the other buffer starts loading the
+ * next layer (l + 1 mod L, or the next layer given to moe_ctx_forward_steps).
+ * A buffer that already holds the layer is not reloaded. Staged steps leave
+ * the decode cache (tables, recency, policy history, counters) untouched;
+ * their stats are -1. Not with device orchestration (MOE_EINVAL). The context
+ * allocates a [2E] device table and four events on the first enable. */
+int moe_ctx_set_staging(moe_layer_ctx* ctx, int enable, int threshold, int pool_slots);
+
+/* moe_ctx_stage_counters: out[0] staged steps, out[1] experts copied into the
+ * staging buffers, since creation. */
+int moe_ctx_stage_counters(moe_layer_ctx* ctx, int64_t* out);
+
 /* moe_ctx_set_orchestration: where the residency plan runs.
  *   MOE_ORCH_HOST (default): the host plans each step that may miss, after
  *     reading the routed set, and the fills are DMA copies on the fill stream.

@@ -295,7 +295,7 @@ def test_slot_fill_rejects_pageable_host_memory():
 
 # --------------------------------------------------------------- whole layer --
 def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, policy=None,
-                    device_plan=False, split=None):
+                    device_plan=False, split=None, staging=None):
     """Run steps through the harness and compare every step with the oracle.
 
     policy = (kind, window, params): the runtime plans under that eviction policy and the
@@ -303,10 +303,15 @@ def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, pol
     the oracle's softmax of the kernel's logits) before each plan.
     device_plan: the runtime plans and fills on the GPU (device orchestration).
     split = (theta, beta, gamma): split-precision routing; the oracle takes the critical set
-    from the kernel's own step scores (checked against its softmax) in float32."""
+    from the kernel's own step scores (checked against its softmax) in float32.
+    staging = token threshold: steps of layers not wholly resident with T >= threshold run
+    from the full-layer staging buffers; the oracle's planner (the decode cache) skips them.
+    Returns the layer object."""
     t_max = max(Ts)
     residency = W.initial_residency(shape, slots, mode)
-    layer_obj = Hn.SlotCacheLayer(shape, slots, residency, t_max)
+    layer_obj = Hn.SlotCacheLayer(shape, slots, residency, t_max, staging=staging is not None)
+    if staging is not None:
+        layer_obj.ctx.set_staging(True, staging)
     if device_plan:
         layer_obj.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
     if split is not None:
@@ -340,7 +345,12 @@ def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, pol
             if policy is not None or split is not None:
                 sc = layer_obj.ctx.step_scores()
                 np.testing.assert_allclose(sc, O.step_scores(o["logits"].cpu().numpy()), rtol=2e-6, atol=1e-7)
-            if policy is None:
+            n_res = int(np.sum(planner.lut[layer] >= 0))
+            staged = (staging is not None and n_res < shape.E
+                      and T >= (staging if staging >= 0 else n_res // shape.k))
+            if staged:
+                pass  # the decode cache is not touched
+            elif policy is None:
                 planner.plan(layer, pr["distinct"])
             else:
                 planner.plan(layer, pr["distinct"], sc)
@@ -370,6 +380,7 @@ def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, pol
             assert r <= TOL[shape.wfmt]
     if split is not None:
         assert n_hi > 0 and n_lo > 0, (n_hi, n_lo)  # both precisions were exercised
+    return layer_obj
 
 
 def test_layer_tiny_fp32_identity():
@@ -518,6 +529,29 @@ def test_layer_split_precision_with_policy():
     shape = W.reduced(SPLIT, E=16, k=4, H=256, F=128, layers=2)
     _run_layer_case(shape, 12, "zipf_rank", [1, 3, 1, 2], layers_order=[0, 1],
                     policy=(B.MOE_POLICY_MRS, 4, None), split=(0.125, None, 0.5))
+
+
+def test_layer_staging_prefill_stack():
+    """Prefill steps at or above the threshold run from the two full-layer buffers (the next
+    layer loads while the current one computes); decode steps in between use the decode cache,
+    whose tables the staged steps leave alone."""
+    shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=3, E=16, k=4, H=256,
+                      F=128, blobs=16)
+    lay = _run_layer_case(shape, 14, "zipf_rank", [1, 24, 3, 40, 1], layers_order=[0, 1, 2],
+                          staging=8)
+    # first staged round: buffer 0 loads layer 0, then layers 1, 2, 0 are each prefetched
+    # while the previous one computes; second round: 3 prefetches, every step a buffer hit
+    assert lay.ctx.stage_counters() == {"staged_steps": 6, "stage_copies": 16 * 7}
+
+
+def test_layer_staging_split_shared_rule_threshold():
+    """The pages' switch, floor(resident slots / k), with split-precision experts and a
+    shared expert: a single layer is loaded once and stays staged."""
+    shape = W.reduced(SPLIT, E=16, k=4, H=256, F=128)
+    lay = _run_layer_case(shape, 8, "zipf_rank", [1, 2, 4, 24, 1], staging=-1,
+                          split=(0.125, None, 1.0))
+    # 8 resident slots, k = 4: steps of T >= 2 are staged
+    assert lay.ctx.stage_counters() == {"staged_steps": 3, "stage_copies": 16}
 
 
 def test_layer_shared_experts():
