@@ -271,8 +271,8 @@ __global__ __launch_bounds__(512) void gemm_w4a8_kernel(
 #undef MOE_W4A8_TILE
 }
 
-template <int KS, int RBW, int MAXNT, bool SWIGLU, bool SPLIT>
-void launch_gemv(const int8_t* aq, const float* as, const int32_t* perm, int k,
+template <int KS, int RBW, int MAXNT, bool SWIGLU, bool SPLIT, bool QIN>
+void launch_gemv(const int8_t* aq, const float* as, const void* raw, const int32_t* perm, int k,
                  const FfnItem* items, const int32_t* n_items, int max_items, const char* pool,
                  size_t stride, const tgemv::QuantOffsets& offs, const int32_t* mask, int E, int R,
                  int K, int out_ld, float* out, hipStream_t s) {
@@ -283,23 +283,26 @@ void launch_gemv(const int8_t* aq, const float* as, const int32_t* perm, int k,
   const unsigned grid = (unsigned)(units < tgemv::kGridCap ? units : tgemv::kGridCap);
   if (grid == 0) return;
   constexpr int U = 2;
-  hipLaunchKernelGGL((tgemv::int4_kernel<KS, RBW, NW, U, MAXNT, SWIGLU, SPLIT>), dim3(grid),
-                     dim3(NW * 64), 0, s, aq, as, perm, k, items, n_items, pool, stride, offs, mask,
-                     E, R, K, out_ld, upi, out);
+  const size_t lds = QIN ? (size_t)MAXNT * K : 0;  // the tile's int8 rows (K <= 8192)
+  hipLaunchKernelGGL((tgemv::int4_kernel<KS, RBW, NW, U, MAXNT, SWIGLU, SPLIT, QIN>), dim3(grid),
+                     dim3(NW * 64), lds, s, aq, as, raw, perm, k, items, n_items, pool, stride,
+                     offs, mask, E, R, K, out_ld, upi, out);
 }
 
 // One GEMV pass (first: gate/up with the SwiGLU epilogue; else: down). With
 // split = true the items of split-precision experts pick their precision from
-// mask (tgemv::int4_kernel).
-template <int MAXNT, bool FIRST, bool SPLIT>
-void launch_gemv_split(const tgemv::Split& sp, const int8_t* aq, const float* as,
+// mask; with QIN the workgroups quantise their activation rows from raw
+// themselves, else they read aq / as (tgemv::int4_kernel).
+template <int MAXNT, bool FIRST, bool SPLIT, bool QIN>
+void launch_gemv_split(const tgemv::Split& sp, const int8_t* aq, const float* as, const void* raw,
                        const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
                        int max_items, const char* pool, size_t stride,
                        const tgemv::QuantOffsets& offs, const int32_t* mask, int E, int R, int K,
                        int ld, float* out, hipStream_t s) {
 #define MOE_W4_L(KS_, RBW_)                                                                       \
-  launch_gemv<KS_, RBW_, MAXNT, FIRST, SPLIT>(aq, as, perm, k, items, n_items, max_items, pool,   \
-                                              stride, offs, mask, E, R, K, ld, out, s)
+  launch_gemv<KS_, RBW_, MAXNT, FIRST, SPLIT, QIN>(aq, as, raw, perm, k, items, n_items,         \
+                                                   max_items, pool, stride, offs, mask, E, R, K,  \
+                                                   ld, out, s)
   if (sp.rbw == 2) {
     // 1024-thread groups hold 128 VGPRs: one-row tiles only
     if constexpr (MAXNT == 1) {
@@ -321,7 +324,8 @@ void launch_gemv_split(const tgemv::Split& sp, const int8_t* aq, const float* as
 }
 
 void launch_gemv_any(bool first, bool split, int nt, const int8_t* aq, const float* as,
-                     const int32_t* perm, int k, const FfnItem* items, const int32_t* n_items,
+                     const void* raw, const int32_t* perm, int k, const FfnItem* items,
+                     const int32_t* n_items,
                      int max_items, const char* pool, size_t stride, const SlotLayout& lay,
                      const int32_t* mask, int E, int H, int F, float* out, hipStream_t s) {
   const int R = first ? 2 * F : H, K = first ? H : F, ld = first ? F : H;
@@ -329,9 +333,17 @@ void launch_gemv_any(bool first, bool split, int nt, const int8_t* aq, const flo
       first ? tgemv::QuantOffsets{lay.off_w13, lay.off_s13, lay.off_r13, lay.off_rs13}
             : tgemv::QuantOffsets{lay.off_w2, lay.off_s2, lay.off_h2, lay.off_hs2};
   const tgemv::Split sp = tgemv::choose_split_int4(R / 32 * max_items, K / 64);
-#define MOE_W4_SPLIT(NT_, FIRST_, SPLIT_)                                                       \
-  launch_gemv_split<NT_, FIRST_, SPLIT_>(sp, aq, as, perm, k, items, n_items, max_items, pool,  \
-                                         stride, offs, mask, E, R, K, ld, out, s)
+#define MOE_W4_SPLIT(NT_, FIRST_, SPLIT_)                                                        \
+  do {                                                                                           \
+    if (raw)                                                                                     \
+      launch_gemv_split<NT_, FIRST_, SPLIT_, true>(sp, aq, as, raw, perm, k, items, n_items,     \
+                                                   max_items, pool, stride, offs, mask, E, R, K, \
+                                                   ld, out, s);                                  \
+    else                                                                                         \
+      launch_gemv_split<NT_, FIRST_, SPLIT_, false>(sp, aq, as, raw, perm, k, items, n_items,    \
+                                                    max_items, pool, stride, offs, mask, E, R,   \
+                                                    K, ld, out, s);                              \
+  } while (0)
 #define MOE_W4_NT(NT_)                                     \
   do {                                                     \
     if (first) {                                           \
@@ -376,21 +388,26 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   if (!planned)
     launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max,
                     items, n_items, tiles, n_tiles, err, s, split);
-  hipLaunchKernelGGL(quant_rows_kernel<MOE_BF16>, dim3(T), dim3(256), 0, s, x, H, nullptr, nullptr,
-                     nullptr, 0, 0, 0, xq, xs);
+  // with no MFMA tile every row is quantised by the GEMV workgroups that read it (a
+  // decode step then runs two weight passes and no separate quantisation launch)
+  const bool fused = max_tiles == 0;
+  if (!fused)
+    hipLaunchKernelGGL(quant_rows_kernel<MOE_BF16>, dim3(T), dim3(256), 0, s, x, H, nullptr,
+                       nullptr, nullptr, 0, 0, 0, xq, xs);
   const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;
   if (max_items > 0)
-    launch_gemv_any(true, split, nt, xq, xs, perm, k, items, n_items, max_items, pool, stride, lay,
-                    group_mask, E, H, F, hbuf, s);
+    launch_gemv_any(true, split, nt, xq, xs, fused ? x : nullptr, perm, k, items, n_items,
+                    max_items, pool, stride, lay, group_mask, E, H, F, hbuf, s);
   if (max_tiles > 0)
     hipLaunchKernelGGL(gemm_w4a8_kernel<1>, dim3((2 * F + QBN - 1) / QBN, max_tiles), dim3(512), 0,
                        s, xq, xs, perm, k, tiles, n_tiles, pool, stride, lay.off_w13,
                        lay.off_s13, 2 * F, H, F, hbuf);
-  hipLaunchKernelGGL(quant_rows_kernel<MOE_F32>, dim3((unsigned)rows), dim3(256), 0, s, hbuf, F,
-                     offsets, lut, group_mask, E, n_shared, num_slots, hq, hs);
+  if (!fused)
+    hipLaunchKernelGGL(quant_rows_kernel<MOE_F32>, dim3((unsigned)rows), dim3(256), 0, s, hbuf, F,
+                       offsets, lut, group_mask, E, n_shared, num_slots, hq, hs);
   if (max_items > 0)
-    launch_gemv_any(false, split, nt, hq, hs, perm, k, items, n_items, max_items, pool, stride, lay,
-                    group_mask, E, H, F, y, s);
+    launch_gemv_any(false, split, nt, hq, hs, fused ? hbuf : nullptr, perm, k, items, n_items,
+                    max_items, pool, stride, lay, group_mask, E, H, F, y, s);
   if (max_tiles > 0)
     hipLaunchKernelGGL(gemm_w4a8_kernel<2>, dim3((H + QBN - 1) / QBN, max_tiles), dim3(512), 0, s,
                        hq, hs, perm, k, tiles, n_tiles, pool, stride, lay.off_w2, lay.off_s2, H,

@@ -186,7 +186,9 @@ __device__ __forceinline__ int dot64_int4(const u32x4& w, const u32x4& a0, const
 // RES adds a second int4 matrix of the same layout (the residual W^R of a
 // split-precision expert, codes at rbase, scales rscales) to the first: both
 // group products are scaled and accumulated into the same fp32 sums.
-template <int KS, int RBW, int U, int NT, bool SWIGLU, bool RES>
+// LDSA: the tile's NT activation rows are rows 0..NT-1 of aq / as (staged in
+// LDS by stage_rows) instead of rows of the global int8 buffers.
+template <int KS, int RBW, int U, int NT, bool SWIGLU, bool RES, bool LDSA = false>
 __device__ __forceinline__ void tile_int4(const char* __restrict__ wbase,
                                           const uint16_t* __restrict__ scales,
                                           const char* __restrict__ rbase,
@@ -205,7 +207,7 @@ __device__ __forceinline__ void tile_int4(const char* __restrict__ wbase,
   float sx[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    arow[t] = SWIGLU ? perm[prow + t] / k : prow + t;
+    arow[t] = LDSA ? t : SWIGLU ? perm[prow + t] / k : prow + t;
     sx[t] = as[arow[t]];
   }
   float acc[RBW][NT];
@@ -276,7 +278,7 @@ __device__ __forceinline__ void tile_int4(const char* __restrict__ wbase,
 // codes of row l % 32 at k offset 16 (l / 32); the integer sums are exact and
 // the group (4 chunks) scale applies in fp32. Second pass only: the
 // activation rows are the permuted rows of h.
-template <int KS, int RBW, int U, int NT>
+template <int KS, int RBW, int U, int NT, bool LDSA = false>
 __device__ __forceinline__ void tile_int8(const char* __restrict__ wbase,
                                           const uint16_t* __restrict__ scales, int nkc, int K,
                                           const int8_t* __restrict__ aq,
@@ -287,9 +289,13 @@ __device__ __forceinline__ void tile_int8(const char* __restrict__ wbase,
   const int slice = wave % KS;
   const int kh = 16 * (lane >> 5);
   const int gld = K / 128;
+  int arow[NT];
   float sx[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) sx[t] = as[prow + t];
+  for (int t = 0; t < NT; ++t) {
+    arow[t] = LDSA ? t : prow + t;
+    sx[t] = as[arow[t]];
+  }
   float acc[RBW][NT];
 #pragma unroll
   for (int b = 0; b < RBW; ++b)
@@ -323,7 +329,7 @@ __device__ __forceinline__ void tile_int8(const char* __restrict__ wbase,
       if (kc < nkc) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const u32x4 a = ld16(aq + (size_t)(prow + t) * K + kc * 32 + kh);
+          const u32x4 a = ld16(aq + (size_t)arow[t] * K + kc * 32 + kh);
 #pragma unroll
           for (int b = 0; b < RBW; ++b) {
             const u32x4& w = cw[u][b];
@@ -390,12 +396,73 @@ struct QuantOffsets {
   size_t lo, lo_s, hi, hi_s;
 };
 
+// The int8 rows of a tile, quantised by the workgroup into LDS: NT rows of K
+// values (bf16 tokens x[perm[p] / k] when GATHER, else fp32 rows p of h),
+// each with s = max|v| / 127 (1 for a zero row) and q = clip(rint(v / s),
+// -127, 127), the rule of quant_rows_kernel, so the codes are the same.
+template <bool GATHER, int NT>
+__device__ __forceinline__ void stage_rows(const void* __restrict__ raw,
+                                           const int32_t* __restrict__ perm, int k, int prow,
+                                           int K, int8_t* q, float* s, float* wmax) {
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  __syncthreads();  // the previous tile's readers are done with q and s
+#pragma unroll 1
+  for (int t = 0; t < NT; ++t) {
+    const size_t row = GATHER ? (size_t)(perm[prow + t] / k) : (size_t)(prow + t);
+    auto load8v = [&](int e0, float v[8]) {
+      if constexpr (GATHER) {
+        load8<MOE_BF16>(raw, row * K + e0, v);
+      } else {
+        load8<MOE_F32>(raw, row * K + e0, v);
+      }
+    };
+    float amax = 0.f;
+    for (int e0 = tid * 8; e0 < K; e0 += nthr * 8) {
+      float v[8];
+      load8v(e0, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+    float m = 0.f;
+    for (int w = 0; w < (nthr >> 6); ++w) m = fmaxf(m, wmax[w]);
+    const float sc = (m == 0.f) ? 1.f : m / 127.f;
+    for (int e0 = tid * 8; e0 < K; e0 += nthr * 8) {
+      float v[8];
+      load8v(e0, v);
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float r = rintf(v[i] / sc);
+        r = fminf(fmaxf(r, -127.f), 127.f);
+        const uint32_t b = (uint32_t)((int)r & 0xFF);
+        if (i < 4) w0 |= b << (8 * i); else w1 |= b << (8 * (i - 4));
+      }
+      *reinterpret_cast<uint2*>(q + (size_t)t * K + e0) = make_uint2(w0, w1);
+    }
+    if (tid == 0) s[t] = sc;
+    __syncthreads();  // wmax is reused by the next row; q and s are complete
+  }
+}
+
+// LDS of a workgroup that quantises its own activation rows (QIN).
+struct StageLds {
+  int8_t* q;    // [MAXNT][K]
+  float* s;     // [MAXNT]
+  float* wmax;  // [16]
+};
+
 // Item modes of the quantised passes: 0 = int4, 1 = int4 + int4 residual, 2 = int8.
-template <int MODE, int KS, int RBW, int U, int MAXNT, bool SWIGLU>
+// QIN: the activation rows are quantised per tile by the workgroup (stage_rows,
+// from raw) instead of read from the int8 buffers aq / as.
+template <int MODE, int KS, int RBW, int U, int MAXNT, bool SWIGLU, bool QIN>
 __device__ __forceinline__ void quant_item(const char* slot, const QuantOffsets& o, int K,
-                                           const int8_t* aq, const float* as,
-                                           const int32_t* perm, int k, const FfnItem& it, int rb0,
-                                           int nrb, int out_ld, float* out, float* red) {
+                                           const int8_t* aq, const float* as, const void* raw,
+                                           const StageLds& st, const int32_t* perm, int k,
+                                           const FfnItem& it, int rb0, int nrb, int out_ld,
+                                           float* out, float* red) {
   const char* wb = slot + (MODE == 2 ? o.hi : o.lo);
   const uint16_t* ws = reinterpret_cast<const uint16_t*>(slot + (MODE == 2 ? o.hi_s : o.lo_s));
   const char* rb = slot + o.hi;
@@ -405,11 +472,16 @@ __device__ __forceinline__ void quant_item(const char* slot, const QuantOffsets&
   constexpr int UQ = (MODE == 1 && U > 1) ? U / 2 : U;
 #define TGEMV_Q(NT_, P_)                                                                       \
   do {                                                                                         \
+    if constexpr (QIN) stage_rows<SWIGLU, NT_>(raw, perm, k, P_, K, st.q, st.s, st.wmax);      \
+    const int8_t* aq_ = QIN ? st.q : aq;                                                       \
+    const float* as_ = QIN ? st.s : as;                                                        \
     if constexpr (MODE == 2)                                                                   \
-      tile_int8<KS, RBW, U, NT_>(wb, ws, nkc, K, aq, as, P_, rb0, nrb, out_ld, out, red);      \
+      tile_int8<KS, RBW, U, NT_, QIN>(wb, ws, nkc, K, aq_, as_, P_, rb0, nrb, out_ld, out,     \
+                                      red);                                                    \
     else                                                                                       \
-      tile_int4<KS, RBW, UQ, NT_, SWIGLU, MODE == 1>(wb, ws, rb, rs, nkc, K, aq, as, perm, k,   \
-                                                     P_, rb0, nrb, out_ld, out, red);          \
+      tile_int4<KS, RBW, UQ, NT_, SWIGLU, MODE == 1, QIN>(wb, ws, rb, rs, nkc, K, aq_, as_,    \
+                                                          perm, k, P_, rb0, nrb, out_ld, out,  \
+                                                          red);                                \
   } while (0)
   int done = 0;
   for (; it.rows - done >= MAXNT; done += MAXNT) TGEMV_Q(MAXNT, it.row_begin + done);
@@ -424,14 +496,21 @@ __device__ __forceinline__ void quant_item(const char* slot, const QuantOffsets&
 // SPLIT = true (split-precision experts): an item runs at high precision when
 // it is a shared group (expert >= E), when mask is NULL, or when mask[expert]
 // >= 2, else on the int4 weights; the choice is uniform over a workgroup.
-template <int KS, int RBW, int NW, int U, int MAXNT, bool SWIGLU, bool SPLIT>
+// QIN: the workgroup quantises each tile's activation rows itself, from raw
+// (bf16 tokens in the gate/up pass, fp32 h in the down pass), into
+// MAXNT * K bytes of dynamic LDS; aq and as are then unused.
+template <int KS, int RBW, int NW, int U, int MAXNT, bool SWIGLU, bool SPLIT, bool QIN>
 __global__ __launch_bounds__(NW * 64) void int4_kernel(
-    const int8_t* __restrict__ aq, const float* __restrict__ as,
+    const int8_t* __restrict__ aq, const float* __restrict__ as, const void* __restrict__ raw,
     const int32_t* __restrict__ perm, int k, const FfnItem* __restrict__ items,
     const int32_t* __restrict__ n_items, const char* __restrict__ pool, size_t stride,
     QuantOffsets offs, const int32_t* __restrict__ mask, int E, int R, int K, int out_ld,
     int units_per_item, float* __restrict__ out) {
   __shared__ float red[NW * RBW * 32 * MAXNT];
+  __shared__ float st_s[MAXNT];
+  __shared__ float st_wmax[16];
+  extern __shared__ __attribute__((aligned(16))) int8_t st_q[];
+  const StageLds st{st_q, st_s, st_wmax};
   const int wave = threadIdx.x >> 6;
   const int nrb = R / 32;
   const int units = n_items[0] * units_per_item;
@@ -443,11 +522,11 @@ __global__ __launch_bounds__(NW * 64) void int4_kernel(
     bool hi = false;
     if constexpr (SPLIT) hi = it.expert >= E || mask == nullptr || mask[it.expert] >= 2;
     if (hi)
-      quant_item<SWIGLU ? 1 : 2, KS, RBW, U, MAXNT, SWIGLU>(slot, offs, K, aq, as, perm, k, it,
-                                                            rb0, nrb, out_ld, out, red);
+      quant_item<SWIGLU ? 1 : 2, KS, RBW, U, MAXNT, SWIGLU, QIN>(
+          slot, offs, K, aq, as, raw, st, perm, k, it, rb0, nrb, out_ld, out, red);
     else
-      quant_item<0, KS, RBW, U, MAXNT, SWIGLU>(slot, offs, K, aq, as, perm, k, it, rb0, nrb,
-                                               out_ld, out, red);
+      quant_item<0, KS, RBW, U, MAXNT, SWIGLU, QIN>(slot, offs, K, aq, as, raw, st, perm, k, it,
+                                                    rb0, nrb, out_ld, out, red);
   }
 }
 #undef TGEMV_REST
@@ -455,8 +534,8 @@ __global__ __launch_bounds__(NW * 64) void int4_kernel(
 // Launch split for a pass with row_blocks_total 32-row blocks (over all
 // groups) of nchunks chunks each, measured on gfx950 for decode shapes:
 // - RBW (row blocks per wave) reuses each activation load for RBW rows. For
-//   bf16 it pays once tiles hold >= 2 activation rows; for int4, whose int8
-//   activations take twice the bytes of the codes they meet, RBW = 4 always.
+//   bf16 it pays once tiles hold >= 2 activation rows; int4, whose int8
+//   activations take twice the bytes of the codes they meet, uses 2 or 4.
 // - KS (waves splitting one row block's K range) is raised until the pass has
 //   ~8192 waves (bf16) while every wave keeps >= 8 chunks; the int4 split
 //   follows the measured optimum for its two K extents.
