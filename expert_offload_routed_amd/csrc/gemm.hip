@@ -54,18 +54,10 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ perm, int k,
     const GemmTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
     const char* __restrict__ pool, size_t stride, size_t off, int N, int K, int out_ld,
-    void* __restrict__ out, int n_slabs, int max_tiles) {
+    void* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
-  // workgroup g runs on XCD g % 8: each XCD takes a contiguous range of (weight slab,
-  // tile) in slab-major, tile-minor order, so the M-tiles of one group and slab run side
-  // by side on one XCD and all but the first read the slab from that XCD's L2
-  const int g = blockIdx.x, total = n_slabs * max_tiles;
-  const int per = (total + 7) / 8;
-  const int lin = (g % 8) * per + g / 8;
-  if (lin >= total) return;
-  const int slab = lin / max_tiles, ty = lin - slab * max_tiles;
-  if (ty >= n_tiles[0]) return;
-  const GemmTile tl = tiles[ty];
+  if ((int)blockIdx.y >= n_tiles[0]) return;
+  const GemmTile tl = tiles[blockIdx.y];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int mh = wave & 1, np = wave >> 1;
   const int nrb = N / 32;
@@ -78,14 +70,14 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(
     const size_t r = (PASS == 1) ? (size_t)(perm[p] / k) : (size_t)p;
     a_src = act + r * K + lks * 16 + 8 * (lane >> 5);
   }
-  int lrb = slab * (BN / 32) + wave;
+  int lrb = blockIdx.x * (BN / 32) + wave;
   if (lrb >= nrb) lrb = nrb - 1;
   const char* b_src = pool + (size_t)tl.slot * stride + off + (size_t)lrb * (K / 16) * 1024 + lane * 16;
   bool nvalid[2];
   int rbv[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    int rb = slab * (BN / 32) + np * 2 + nb;
+    int rb = blockIdx.x * (BN / 32) + np * 2 + nb;
     nvalid[nb] = rb < nrb;
     rbv[nb] = nvalid[nb] ? rb : nrb - 1;
   }
@@ -168,14 +160,13 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(
 void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, const GemmTile* tiles,
                       const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
                       size_t off, int N, int K, int out_ld, void* out, hipStream_t s) {
-  const int n_slabs = (N + BN - 1) / BN;
-  const int total = n_slabs * max_tiles;
-  const dim3 grid((total + 7) / 8 * 8);
-  const uint16_t* a = static_cast<const uint16_t*>(act);
+  const dim3 grid((N + BN - 1) / BN, max_tiles);
   if (pass == 1)
-    hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, dim3(512), 0, s, a, perm, k, tiles,
-                       n_tiles, pool, stride, off, N, K, out_ld, out, n_slabs, max_tiles);
+    hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, dim3(512), 0, s,
+                       static_cast<const uint16_t*>(act), perm, k, tiles, n_tiles, pool, stride, off,
+                       N, K, out_ld, out);
   else
-    hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, dim3(512), 0, s, a, perm, k, tiles,
-                       n_tiles, pool, stride, off, N, K, out_ld, out, n_slabs, max_tiles);
+    hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, dim3(512), 0, s,
+                       static_cast<const uint16_t*>(act), perm, k, tiles, n_tiles, pool, stride, off,
+                       N, K, out_ld, out);
 }
