@@ -425,8 +425,8 @@ def main():
         # its own memory, so the HBM traffic is that of E distinct experts)
         sshape = W.reduced(shape, wfmt="int4g128_resplit", blobs=16, name=shape.name + "_resplit")
         sstore = Hn.ExpertStore(sshape)
-        for T in (1, 32):
-            split_case(sshape, sstore, T, K, Wm)
+        for T in (1, 32, 512):
+            split_case(sshape, sstore, T, K if T <= 32 else max(K // 4, 3), Wm)
         return
     t_max = max(plan["hit"])
     store = Hn.ExpertStore(shape)

@@ -39,8 +39,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ lut,
     const int32_t* __restrict__ mask, int E, int n_shared, int shared_slot0, int num_slots,
     int small_max, FfnItem* __restrict__ items, int32_t* __restrict__ n_items,
-    GemmTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_word,
-    int hi_items) {
+    GemmTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_word) {
   __shared__ int s_wave[40];
   const int e = threadIdx.x;
   int rows = 0, slot = -1, begin = 0;
@@ -58,9 +57,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(
       }
     }
   }
-  // with split-precision weights a high-precision group is an item whatever its size
-  const bool hi = hi_items && (e >= E || mask == nullptr || mask[e] >= 2);
-  const bool small = take && (rows <= small_max || hi);
+  const bool small = take && rows <= small_max;
   const int ntile = (take && !small) ? (rows + kGemmBM - 1) / kGemmBM : 0;
   int total_items = 0, total_tiles = 0;
   const int ipos = block_exclusive_scan(small ? 1 : 0, s_wave, &total_items);
@@ -173,10 +170,9 @@ void launch_f32(const void* x, const int32_t* perm, int k, const FfnItem* items,
 void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
                      int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
                      int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
-                     hipStream_t s, bool hi_items) {
+                     hipStream_t s) {
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, lut, mask, E, n_shared,
-                     shared_slot0, num_slots, small_max, items, n_items, tiles, n_tiles, err_word,
-                     hi_items ? 1 : 0);
+                     shared_slot0, num_slots, small_max, items, n_items, tiles, n_tiles, err_word);
 }
 
 int ffn_small_max(int T, int k, int E, int n_shared) {

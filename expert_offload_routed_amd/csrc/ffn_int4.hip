@@ -144,12 +144,24 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
-template <int PASS, int NMF>
+// Weight forms of an MFMA tile: WM 0 = int4 codes (W^L, the int4 format);
+// WM 1 = int4 codes plus the int4 residual W^R of a split-precision expert
+// (gate/up at W^H: each K step runs the group's MFMAs twice, once per code
+// set, each folded with its own scale); WM 2 = 8-bit codes (down at W^H:
+// 1 KB chunks of 32 rows x 32 codes, already the MFMA operand, group scale
+// without the factor 1/16). The forms with more code bytes per step keep one
+// step of copies in flight instead of three, to stay within the registers.
+template <int PASS, int NMF, int WM>
 __device__ __forceinline__ void w4a8_tile(
     int8_t* smem, const int8_t* __restrict__ aq, const float* __restrict__ as,
     const int32_t* __restrict__ perm, int k, const GemmTile& tl, const char* __restrict__ slot,
-    size_t off_codes, size_t off_scales, int N, int K, int out_ld, float* __restrict__ out) {
-  constexpr int kOps = 5;  // copies per wave per K step: 2 A, 2 B, 1 scale word
+    size_t off_codes, size_t off_scales, size_t off_rcodes, size_t off_rscales, int N, int K,
+    int out_ld, float* __restrict__ out) {
+  constexpr int AH = WM == 0 ? kQAhead : 1;  // K steps of copies in flight
+  constexpr int RING = AH + 1;
+  constexpr int NB = WM == 0 ? 2 : 4;        // 1 KB code chunks per wave per K step
+  constexpr int NS = WM == 1 ? 2 : 1;        // scale words per wave per K step
+  constexpr int kOps = 2 + NB + NS;          // copies per wave per K step (2 for A)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nrb = N / 32;
   const int gld = K / 128;  // scale groups per weight row
@@ -164,19 +176,33 @@ __device__ __forceinline__ void w4a8_tile(
   int rb = blockIdx.x * (QBN / 32) + wave;
   const bool nvalid = rb < nrb;
   if (!nvalid) rb = nrb - 1;
-  const char* b_src = slot + off_codes + (size_t)rb * (K / 64) * 1024 + lane * 16;
+  // chunk c of K step kt: int4 (K / 64 chunks per block, 2 per step), int8 (K / 32, 4 per step)
+  const size_t blk = (size_t)rb * (K / (WM == 2 ? 32 : 64)) * 1024 + lane * 16;
+  const char* b_src = slot + off_codes + blk;
+  const char* r_src = slot + off_rcodes + blk;
   const size_t se = (size_t)(rb * 32 + (lane & 31)) * gld;  // element index of group 0's scale
   const uint32_t* s_src = reinterpret_cast<const uint32_t*>(slot + off_scales);
+  const uint32_t* rs_src = reinterpret_cast<const uint32_t*>(slot + off_rscales);
 
-  u32x4 bq[kQRing][2];
-  uint32_t sq[kQRing];
+  u32x4 bq[RING][NB];
+  uint32_t sq[RING][NS];
   auto issue = [&](int kt, int buf) {
     int8_t* la = smem + buf * kQStageBytes + (lmf * 4 + lks0) * 1024;
     copy16_to_lds(a_src + kt * QBK, la);
     copy16_to_lds(a_src + kt * QBK + 32, la + 1024);
-    bq[buf][0] = ld16(b_src + (size_t)(2 * kt) * 1024);
-    bq[buf][1] = ld16(b_src + (size_t)(2 * kt + 1) * 1024);
-    sq[buf] = s_src[(se + kt) >> 1];
+    if constexpr (WM == 2) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bq[buf][c] = ld16(b_src + (size_t)(4 * kt + c) * 1024);
+    } else {
+      bq[buf][0] = ld16(b_src + (size_t)(2 * kt) * 1024);
+      bq[buf][1] = ld16(b_src + (size_t)(2 * kt + 1) * 1024);
+      if constexpr (WM == 1) {
+        bq[buf][2] = ld16(r_src + (size_t)(2 * kt) * 1024);
+        bq[buf][3] = ld16(r_src + (size_t)(2 * kt + 1) * 1024);
+      }
+    }
+    sq[buf][0] = s_src[(se + kt) >> 1];
+    if constexpr (WM == 1) sq[buf][1] = rs_src[(se + kt) >> 1];
   };
   const intx16 zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   intx16 acc[4];
@@ -192,41 +218,71 @@ __device__ __forceinline__ void w4a8_tile(
     for (int r = 0; r < 16; ++r) accf[mf][r] = fmaf((float)acc[mf][r], sw, accf[mf][r]);
   };
 #pragma unroll
-  for (int s2 = 0; s2 < kQAhead; ++s2)
+  for (int s2 = 0; s2 < AH; ++s2)
     if (s2 < nk) issue(s2, s2);
   float sprev = 0.f;
+  bool started = false;  // an accumulator holds a group not yet folded
   auto step = [&](int kt, int j) {
     // this wave's copies of step kt have landed once at most the later steps' are outstanding
     const int after = nk - 1 - kt;
-    if (after >= 2) vm_wait<2 * kOps>(); else if (after == 1) vm_wait<kOps>(); else vm_wait<0>();
-    __builtin_amdgcn_s_barrier();  // every wave's A copies of step kt; every wave is past step kt - 1
-    if (kt + kQAhead < nk) issue(kt + kQAhead, (j + kQAhead) % kQRing);
-    const int8_t* A = smem + j * kQStageBytes + lane * 16;
-    const uint32_t sb = ((se + kt) & 1) ? (sq[j] & 0xFFFF0000u) : (sq[j] << 16);
-    const float scur = __uint_as_float(sb) * 0.0625f;  // codes enter as 16 q
-    intx4 b[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x4& cw = bq[j][ks >> 1];
-      const uint32_t w0 = (ks & 1) ? cw.z : cw.x, w1 = (ks & 1) ? cw.w : cw.y;
-      b[ks][0] = (int)((w0 << 4) & 0xF0F0F0F0u);
-      b[ks][1] = (int)(w0 & 0xF0F0F0F0u);
-      b[ks][2] = (int)((w1 << 4) & 0xF0F0F0F0u);
-      b[ks][3] = (int)(w1 & 0xF0F0F0F0u);
+    if constexpr (AH >= 3) {
+      if (after >= 2) vm_wait<2 * kOps>(); else if (after == 1) vm_wait<kOps>(); else vm_wait<0>();
+    } else {
+      vm_wait<0>();
     }
+    __builtin_amdgcn_s_barrier();  // every wave's A copies of step kt; every wave is past step kt - 1
+    if (kt + AH < nk) issue(kt + AH, (j + AH) % RING);
+    const int8_t* A0 = smem + j * kQStageBytes + lane * 16;
+    const int hi16 = (int)((se + kt) & 1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int sub = 0; sub < (WM == 1 ? 2 : 1); ++sub) {
+      // the residual pass reads its A fragments from LDS again rather than holding the
+      // first pass's in registers (an offset of zero the compiler cannot see through)
+      int zero = 0;
+      if (sub > 0) asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+      const int8_t* A = A0 + zero;
+      const uint32_t word = sq[j][sub];
+      const uint32_t sb = hi16 ? (word & 0xFFFF0000u) : (word << 16);
+      const float scur = __uint_as_float(sb) * (WM == 2 ? 1.f : 0.0625f);  // int4 enters as 16 q
+      // the B operand of k step ks: int8 chunks as they are; int4 words expanded to 16 q
+      auto operand = [&](int ks) {
+        intx4 b;
+        if constexpr (WM == 2) {
+          const u32x4& cw = bq[j][ks];
+          b[0] = (int)cw.x; b[1] = (int)cw.y; b[2] = (int)cw.z; b[3] = (int)cw.w;
+        } else {
+          const u32x4& cw = bq[j][2 * sub + (ks >> 1)];
+          const uint32_t w0 = (ks & 1) ? cw.z : cw.x, w1 = (ks & 1) ? cw.w : cw.y;
+          b[0] = (int)((w0 << 4) & 0xF0F0F0F0u);
+          b[1] = (int)(w0 & 0xF0F0F0F0u);
+          b[2] = (int)((w1 << 4) & 0xF0F0F0F0u);
+          b[3] = (int)(w1 & 0xF0F0F0F0u);
+        }
+        return b;
+      };
+      intx4 b[WM == 0 ? 4 : 1];  // the int4 form expands its four operands up front
+      if constexpr (WM == 0) {
 #pragma unroll
-      for (int mf = 0; mf < NMF; ++mf) {
-        if (ks == 0 && kt > 0) fold(mf, sprev);  // group kt - 1, before the accumulator restarts
-        const intx4 a = *reinterpret_cast<const intx4*>(A + (mf * 4 + ks) * 1024);
-        acc[mf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[ks], ks == 0 ? zero16 : acc[mf], 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks) b[ks] = operand(ks);
       }
-    sprev = scur;
-  };
-  for (int kt0 = 0; kt0 < nk; kt0 += kQRing) {
 #pragma unroll
-    for (int j = 0; j < kQRing; ++j)
+      for (int ks = 0; ks < 4; ++ks) {
+        const intx4 bk = WM == 0 ? b[WM == 0 ? ks : 0] : operand(ks);
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf) {
+          // the previous group (or code set), before the accumulator restarts
+          if (ks == 0 && started) fold(mf, sprev);
+          const intx4 a = *reinterpret_cast<const intx4*>(A + (mf * 4 + ks) * 1024);
+          acc[mf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bk, ks == 0 ? zero16 : acc[mf], 0, 0, 0);
+        }
+      }
+      sprev = scur;
+      started = true;
+    }
+  };
+  for (int kt0 = 0; kt0 < nk; kt0 += RING) {
+#pragma unroll
+    for (int j = 0; j < RING; ++j)
       if (kt0 + j < nk) step(kt0 + j, j);
   }
 #pragma unroll
@@ -251,19 +307,30 @@ __device__ __forceinline__ void w4a8_tile(
   }
 }
 
-template <int PASS>
+// One MFMA pass over the tile list. HI = false: the tiles on W^L (every tile
+// without split precision); HI = true: the tiles on W^H (WM 1 in the gate/up
+// pass, WM 2 in the down pass). With split = 1 (split-precision experts) a
+// tile is W^H when its group is shared (expert >= E), when mask is NULL or
+// when mask[expert] >= 2; each kernel skips the other kind. o holds the W^L
+// section (lo) and the W^H one (hi) of the pass.
+template <int PASS, bool HI>
 __global__ __launch_bounds__(512) void gemm_w4a8_kernel(
     const int8_t* __restrict__ aq, const float* __restrict__ as,
     const int32_t* __restrict__ perm, int k, const GemmTile* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const char* __restrict__ pool, size_t stride,
-    size_t off_codes, size_t off_scales, int N, int K, int out_ld, float* __restrict__ out) {
+    tgemv::QuantOffsets o, const int32_t* __restrict__ mask, int E, int split, int N, int K,
+    int out_ld, float* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) int8_t smem[kQRing * kQStageBytes];
   if ((int)blockIdx.y >= n_tiles[0]) return;
   const GemmTile tl = tiles[blockIdx.y];
   const char* slot = pool + (size_t)tl.slot * stride;
   const int nmf = (tl.rows + 31) >> 5;  // 32-row blocks holding rows of the tile
-#define MOE_W4A8_TILE(M_) \
-  w4a8_tile<PASS, M_>(smem, aq, as, perm, k, tl, slot, off_codes, off_scales, N, K, out_ld, out)
+  const bool hi = split && (tl.expert >= E || mask == nullptr || mask[tl.expert] >= 2);
+  if (hi != HI) return;
+  constexpr int WM = HI ? (PASS == 1 ? 1 : 2) : 0;
+#define MOE_W4A8_TILE(M_)                                                                         \
+  w4a8_tile<PASS, M_, WM>(smem, aq, as, perm, k, tl, slot, WM == 2 ? o.hi : o.lo,                 \
+                          WM == 2 ? o.hi_s : o.lo_s, o.hi, o.hi_s, N, K, out_ld, out)
   if (nmf >= 4) MOE_W4A8_TILE(4);
   else if (nmf == 3) MOE_W4A8_TILE(3);
   else if (nmf == 2) MOE_W4A8_TILE(2);
@@ -381,13 +448,12 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   const long long tk = (long long)T * k;
   const long long rows = (long long)T * (k + n_shared);
   const int small_max = ffn_small_max(T, k, E, n_shared);
-  // split-precision experts: high-precision groups are items whatever their size
-  const int max_items = (small_max == 0 && !split) ? 0 : (int)(tk < E ? tk : E) + n_shared;
+  const int max_items = small_max == 0 ? 0 : (int)(tk < E ? tk : E) + n_shared;
   const int max_tiles = (T > small_max) ? wl.max_tiles : 0;
   if (max_tiles > 65535) return MOE_EUNSUPPORTED;
   if (!planned)
     launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max,
-                    items, n_items, tiles, n_tiles, err, s, split);
+                    items, n_items, tiles, n_tiles, err, s);
   // with no MFMA tile every row is quantised by the GEMV workgroups that read it (a
   // decode step then runs two weight passes and no separate quantisation launch)
   const bool fused = max_tiles == 0;
@@ -398,19 +464,28 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   if (max_items > 0)
     launch_gemv_any(true, split, nt, xq, xs, fused ? x : nullptr, perm, k, items, n_items,
                     max_items, pool, stride, lay, group_mask, E, H, F, hbuf, s);
-  if (max_tiles > 0)
-    hipLaunchKernelGGL(gemm_w4a8_kernel<1>, dim3((2 * F + QBN - 1) / QBN, max_tiles), dim3(512), 0,
-                       s, xq, xs, perm, k, tiles, n_tiles, pool, stride, lay.off_w13,
-                       lay.off_s13, 2 * F, H, F, hbuf);
+  const tgemv::QuantOffsets o13{lay.off_w13, lay.off_s13, lay.off_r13, lay.off_rs13};
+  const tgemv::QuantOffsets o2{lay.off_w2, lay.off_s2, lay.off_h2, lay.off_hs2};
+  const dim3 g13((2 * F + QBN - 1) / QBN, max_tiles), g2((H + QBN - 1) / QBN, max_tiles);
+  if (max_tiles > 0) {
+    hipLaunchKernelGGL((gemm_w4a8_kernel<1, false>), g13, dim3(512), 0, s, xq, xs, perm, k, tiles,
+                       n_tiles, pool, stride, o13, group_mask, E, split ? 1 : 0, 2 * F, H, F, hbuf);
+    if (split)
+      hipLaunchKernelGGL((gemm_w4a8_kernel<1, true>), g13, dim3(512), 0, s, xq, xs, perm, k,
+                         tiles, n_tiles, pool, stride, o13, group_mask, E, 1, 2 * F, H, F, hbuf);
+  }
   if (!fused)
     hipLaunchKernelGGL(quant_rows_kernel<MOE_F32>, dim3((unsigned)rows), dim3(256), 0, s, hbuf, F,
                        offsets, lut, group_mask, E, n_shared, num_slots, hq, hs);
   if (max_items > 0)
     launch_gemv_any(false, split, nt, hq, hs, fused ? hbuf : nullptr, perm, k, items, n_items,
                     max_items, pool, stride, lay, group_mask, E, H, F, y, s);
-  if (max_tiles > 0)
-    hipLaunchKernelGGL(gemm_w4a8_kernel<2>, dim3((H + QBN - 1) / QBN, max_tiles), dim3(512), 0, s,
-                       hq, hs, perm, k, tiles, n_tiles, pool, stride, lay.off_w2, lay.off_s2, H,
-                       F, H, y);
+  if (max_tiles > 0) {
+    hipLaunchKernelGGL((gemm_w4a8_kernel<2, false>), g2, dim3(512), 0, s, hq, hs, perm, k, tiles,
+                       n_tiles, pool, stride, o2, group_mask, E, split ? 1 : 0, H, F, H, y);
+    if (split)
+      hipLaunchKernelGGL((gemm_w4a8_kernel<2, true>), g2, dim3(512), 0, s, hq, hs, perm, k,
+                         tiles, n_tiles, pool, stride, o2, group_mask, E, 1, H, F, H, y);
+  }
   return moe_launch_status();
 }

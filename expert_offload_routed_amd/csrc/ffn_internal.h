@@ -41,13 +41,11 @@ int slot_layout(int H, int F, int w_dtype, SlotLayout* out);
 
 #include <hip/hip_runtime.h>
 // The FFN work list: groups of <= small_max rows as FfnItem, the others cut
-// into kGemmBM-row GemmTile (see ffn_plan_kernel in ffn.hip). hi_items:
-// split-precision weights, whose high-precision groups (mask NULL or >= 2,
-// shared groups) are items whatever their size.
+// into kGemmBM-row GemmTile (see ffn_plan_kernel in ffn.hip).
 void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
                      int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
                      int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
-                     hipStream_t s, bool hi_items = false);
+                     hipStream_t s);
 // Largest group that takes the GEMV path (0: every group takes the MFMA tiles).
 int ffn_small_max(int T, int k, int E, int n_shared);
 void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, const GemmTile* tiles,

@@ -91,6 +91,7 @@ SPLIT_FFN_CASES = [
     (_split_shape(E=8, k=4, H=384, F=384), 40),     # 3 scale groups per row, partial tiles
     (_split_shape(E=12, k=8, H=7168, F=2048), 2),   # full hidden/FFN sizes
     (_split_shape(E=12, k=8, H=7168, F=2048), 24),
+    (_split_shape(E=12, k=8, H=7168, F=2048), 200),  # both precisions on MFMA tiles, 2 per group
 ]
 
 
