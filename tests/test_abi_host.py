@@ -250,6 +250,15 @@ def test_slot_layout_resplit_extends_int4(lib):
         B.moe_slot_layout_resplit(256 + 64, 256)
 
 
+def test_quantize_resplit_rejects_bad_sizes(lib):
+    w = torch.zeros(64, 192)
+    dst = torch.zeros(1 << 20, dtype=torch.uint8)
+    with pytest.raises(B.MoeError):  # H = 192 is not a multiple of 128
+        B.moe_quantize_resplit_host(w, w, w.t().contiguous(), 192, 64, dst)
+    with pytest.raises(ValueError):  # shapes that do not match H, F
+        B.moe_quantize_resplit_host(w, w, w, 192, 64, dst)
+
+
 def _untile_int8(buf, R, K):
     """Inverse of the documented tile-major 8-bit layout: signed codes [R, K]."""
     b = buf.view(torch.int8).numpy().reshape(R // 32, K // 32, 2, 32, 16)  # rb, kc, khalf, row, byte

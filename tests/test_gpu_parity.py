@@ -554,6 +554,35 @@ def test_layer_staging_split_shared_rule_threshold():
     assert lay.ctx.stage_counters() == {"staged_steps": 3, "stage_copies": 16}
 
 
+def test_split_and_staging_reject_bad_settings():
+    """Split routing needs split-precision weights and finite constants; staging needs room
+    for its buffers in the pool and excludes device orchestration."""
+    shape = W.reduced(MIX, E=8, k=2, H=256, F=256)
+    plain = Hn.SlotCacheLayer(shape, 4, W.initial_residency(shape, 4, "random"), 8)
+    with pytest.raises(B.MoeError):
+        plain.ctx.set_split(True, 0.1)  # bf16 weights
+    plain.ctx.set_split(False)  # switching off is always allowed
+    with pytest.raises(B.MoeError):
+        plain.ctx.set_staging(True)  # the pool has no room for the staging buffers
+    staged = Hn.SlotCacheLayer(shape, 4, W.initial_residency(shape, 4, "random"), 8, staging=True)
+    staged.ctx.set_staging(True)
+    with pytest.raises(B.MoeError):
+        staged.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
+    staged.ctx.set_staging(False)
+    staged.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
+    with pytest.raises(B.MoeError):
+        staged.ctx.set_staging(True)
+    with pytest.raises(B.MoeError):
+        staged.ctx.set_staging(True, threshold=-2)
+    sp = W.reduced(SPLIT, E=8, k=2, H=256, F=128)
+    split = Hn.SlotCacheLayer(sp, 8, W.initial_residency(sp, 8, "identity"), 4)
+    with pytest.raises(B.MoeError):
+        split.ctx.set_split(True, float("nan"))
+    with pytest.raises(B.MoeError):
+        split.ctx.set_split(True, 0.1, beta=[float("inf")])
+    split.ctx.set_split(True, 0.1, beta=[0.5], gamma=0.75)
+
+
 def test_layer_shared_experts():
     shape = W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), E=16, k=6, H=256, F=256)
     _run_layer_case(shape, 8, "zipf_rank", [1, 32, 5])
