@@ -30,6 +30,11 @@ typedef __attribute__((__vector_size__(4 * sizeof(int)))) int intx4;
 typedef __attribute__((__vector_size__(16 * sizeof(int)))) int intx16;
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
+// SiLU of the MFMA tile epilogue: g / (1 + e^-g) from the hardware exp2 and
+// reciprocal (about 1 ulp each; the result is quantised to int8 next)
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
 
 
 // ------------------------------------------------------ row quantisation ---
@@ -114,25 +119,46 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 // against it: four v_mfma_i32_32x32x32_i8 accumulators (32-row blocks mf),
 // only the blocks that hold rows of the tile (a 40-row tile computes two).
 //
-// Per K step and wave:
-//   A: two 1 KB fragments of the step's 16 KB activation stage, copied to LDS
-//      asynchronously (16 bytes per lane); fragment (mf, ks) holds row
-//      mf*32 + l%32, bytes ks*32 + 16 (l / 32) at lane l, the MFMA operand
-//      layout; the eight waves' copies fill the stage, one barrier per step
-//      publishes it.
-//   B: the wave's own two 1 KB code chunks, straight into registers (no other
-//      wave reads them), expanded to int8 with two masks and a shift.
-//   scale: the aligned 32-bit word holding the lane's bf16 group scale.
-// Copies run kQAhead steps ahead: A in a ring of kQAhead + 1 LDS stages, B and
-// the scale word in registers. The int32 sums of a group are folded into fp32
-// (group scale / 16) just before the block's accumulator restarts on the next
-// group, so each fold overlaps the other blocks' MFMAs.
+// Every operand reaches LDS by asynchronous global -> LDS copies (each lane
+// copies 16 bytes to the instruction's LDS base + 16 lane):
+//   A: the step's 128 rows x 128 int8 values (16 KB). One copy instruction
+//      takes 8 whole rows (8 lanes per 128-byte row), and the eight waves
+//      copy two each. Row r's 16-byte chunk c lands in slot
+//      8 (r % 8) + (c ^ (r % 8)) of its 8-row KB, so the MFMA operand reads
+//      (lane l: row mf*32 + l%32, chunk 2 ks + l/32) hit eight different
+//      16-byte bank groups in each set of 8 lanes.
+//   B: the wave's own two 1 KB code chunks per step (no other wave reads
+//      them), read back 16 bytes per lane and expanded to int8 with two masks
+//      and a shift.
+//   scales: the wave's 32 rows x K/128 bf16 group scales, copied once per
+//      tile (contiguous in the slot) into a table read 2 bytes per lane and
+//      step.
+// Copies run three steps ahead into a ring of four 32 KB stages; one barrier
+// per step publishes a stage and frees the oldest. Issuing 16-byte copies of
+// 32 different rows, or one scale word per lane and step, cost four and eight
+// times the cache lines per byte and left the loop bound by those requests.
+// The int32 sums of a group are folded into fp32 (group scale / 16) just
+// before the block's accumulator restarts on the next group, so each fold
+// overlaps the other blocks' MFMAs.
 constexpr int QBN = 256;          // weight rows of a tile
 constexpr int QBK = 128;          // one scale group per K step
-constexpr int kQAhead = 3;        // K steps of copies in flight
-constexpr int kQRing = kQAhead + 1;
-constexpr int kQStageBytes = kGemmBM * QBK;  // 16 KB of activations per step
+constexpr int kQABytes = kGemmBM * QBK;  // 16 KB of activations per step
+constexpr int kQMaxGroups = 64;   // K <= 8192
 static_assert(kGemmBM == 128, "the 8-wave int8 tile covers 128 activation rows");
+// Per weight form WM (below): K steps of copies in flight, 1 KB code chunks per
+// wave and step, scale tables, and the LDS of a workgroup: the ring of stages
+// (activations, then each wave's code chunks), then the scale tables of the eight
+// waves (32 rows x kQMaxGroups bf16 each).
+__host__ __device__ constexpr int q_ahead(int wm) { return wm == 0 ? 3 : 1; }
+__host__ __device__ constexpr int q_chunks(int wm) { return wm == 0 ? 2 : 4; }
+__host__ __device__ constexpr int q_tables(int wm) { return wm == 1 ? 2 : 1; }
+__host__ __device__ constexpr int q_stage_bytes(int wm) { return kQABytes + 8 * q_chunks(wm) * 1024; }
+__host__ __device__ constexpr int q_table_bytes() { return 8 * 32 * kQMaxGroups * 2; }
+__host__ __device__ constexpr int q_lds_bytes(int wm) {
+  return (q_ahead(wm) + 1) * q_stage_bytes(wm) + q_tables(wm) * q_table_bytes();
+}
+static_assert(q_lds_bytes(0) <= 160 * 1024 && q_lds_bytes(1) <= 160 * 1024 &&
+              q_lds_bytes(2) <= 160 * 1024, "a workgroup's LDS is at most 160 KB");
 
 template <int N_>
 __device__ __forceinline__ void vm_wait() {
@@ -140,8 +166,19 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N_ & 15) | ((N_ >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+// Asynchronous global -> LDS copy of the MFMA tile: 16 bytes per lane to
+// lds + 16 lane (lds is the same for every lane of the wave), issued from
+// inline assembly so that the compiler does not track it: it would otherwise
+// wait for every copy in flight before each LDS read it cannot prove disjoint
+// from them, which drains the copy ring every step. The caller orders the
+// copies with explicit waits on the vector-memory counter (in-order
+// completion) and barriers, and waits for all of them before the workgroup
+// ends. The compiler's own waits stay correct: a copy it does not know about
+// only makes them more conservative.
+__device__ __forceinline__ void dma16_to_lds(const void* g, void* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(l), "v"(g) : "memory", "m0");
 }
 
 // Weight forms of an MFMA tile: WM 0 = int4 codes (W^L, the int4 format);
@@ -150,60 +187,87 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, void* lds) {
 // set, each folded with its own scale); WM 2 = 8-bit codes (down at W^H:
 // 1 KB chunks of 32 rows x 32 codes, already the MFMA operand, group scale
 // without the factor 1/16). The forms with more code bytes per step keep one
-// step of copies in flight instead of three, to stay within the registers.
+// step of copies in flight instead of three, to stay within the LDS.
 template <int PASS, int NMF, int WM>
 __device__ __forceinline__ void w4a8_tile(
     int8_t* smem, const int8_t* __restrict__ aq, const float* __restrict__ as,
     const int32_t* __restrict__ perm, int k, const GemmTile& tl, const char* __restrict__ slot,
     size_t off_codes, size_t off_scales, size_t off_rcodes, size_t off_rscales, int N, int K,
     int out_ld, float* __restrict__ out) {
-  constexpr int AH = WM == 0 ? kQAhead : 1;  // K steps of copies in flight
+  constexpr int AH = q_ahead(WM);            // K steps of copies in flight
   constexpr int RING = AH + 1;
-  constexpr int NB = WM == 0 ? 2 : 4;        // 1 KB code chunks per wave per K step
-  constexpr int NS = WM == 1 ? 2 : 1;        // scale words per wave per K step
-  constexpr int kOps = 2 + NB + NS;          // copies per wave per K step (2 for A)
+  constexpr int NB = q_chunks(WM);           // 1 KB code chunks per wave per K step
+  constexpr int NT = q_tables(WM);           // scale tables (W^Q and W^R for WM 1)
+  constexpr int kOps = 2 + NB;               // copies per wave per K step (2 for A)
+  constexpr int kStage = q_stage_bytes(WM);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nrb = N / 32;
   const int gld = K / 128;  // scale groups per weight row
   const int nk = K / QBK;
-  const int lmf = wave >> 1, lks0 = (wave & 1) * 2;  // this wave's A fragments
-  const int8_t* a_src;
-  {
-    const int m = lmf * 32 + (lane & 31);
-    const int p = tl.row_begin + (m < tl.rows ? m : 0);  // rows past the tile read row 0
-    a_src = aq + (size_t)((PASS == 1) ? perm[p] / k : p) * K + lks0 * 32 + 16 * (lane >> 5);
-  }
   int rb = blockIdx.x * (QBN / 32) + wave;
   const bool nvalid = rb < nrb;
   if (!nvalid) rb = nrb - 1;
+
+  // the row scale of each tile row, held by thread m until the loop is over
+  float my_rs = 0.f;
+  if (tid < kGemmBM) {
+    const int p = tl.row_begin + (tid < tl.rows ? tid : 0);
+    my_rs = as[(PASS == 1) ? perm[p] / k : p];
+  }
+  // this lane's two A copies: rows 16 wave + 8 q + lane/8, chunk (lane%8) ^ (lane/8)
+  const int8_t* a_src[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int m = 16 * wave + 8 * q + (lane >> 3);
+    const int p = tl.row_begin + (m < tl.rows ? m : 0);  // rows past the tile read row 0
+    a_src[q] = aq + (size_t)((PASS == 1) ? perm[p] / k : p) * K + 16 * ((lane & 7) ^ (lane >> 3));
+  }
   // chunk c of K step kt: int4 (K / 64 chunks per block, 2 per step), int8 (K / 32, 4 per step)
   const size_t blk = (size_t)rb * (K / (WM == 2 ? 32 : 64)) * 1024 + lane * 16;
   const char* b_src = slot + off_codes + blk;
   const char* r_src = slot + off_rcodes + blk;
-  const size_t se = (size_t)(rb * 32 + (lane & 31)) * gld;  // element index of group 0's scale
-  const uint32_t* s_src = reinterpret_cast<const uint32_t*>(slot + off_scales);
-  const uint32_t* rs_src = reinterpret_cast<const uint32_t*>(slot + off_rscales);
-
-  u32x4 bq[RING][NB];
-  uint32_t sq[RING][NS];
-  auto issue = [&](int kt, int buf) {
-    int8_t* la = smem + buf * kQStageBytes + (lmf * 4 + lks0) * 1024;
-    copy16_to_lds(a_src + kt * QBK, la);
-    copy16_to_lds(a_src + kt * QBK + 32, la + 1024);
-    if constexpr (WM == 2) {
+  int8_t* tables = smem + RING * kStage;
+  // the scale tables: rows 32 rb .. 32 rb + 31 of [N, K/128] bf16, 64 gld contiguous bytes
+  {
+    const int tbytes = 64 * gld;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bq[buf][c] = ld16(b_src + (size_t)(4 * kt + c) * 1024);
-    } else {
-      bq[buf][0] = ld16(b_src + (size_t)(2 * kt) * 1024);
-      bq[buf][1] = ld16(b_src + (size_t)(2 * kt + 1) * 1024);
-      if constexpr (WM == 1) {
-        bq[buf][2] = ld16(r_src + (size_t)(2 * kt) * 1024);
-        bq[buf][3] = ld16(r_src + (size_t)(2 * kt + 1) * 1024);
+    for (int t = 0; t < NT; ++t) {
+      const char* src = slot + (t == 0 ? off_scales : off_rscales) + (size_t)rb * tbytes;
+      int8_t* dst = tables + (t * 8 + wave) * (32 * kQMaxGroups * 2);
+      for (int q = 0; q * 1024 < tbytes; ++q) {
+        const int b = q * 1024 + lane * 16;
+        dma16_to_lds(src + (b < tbytes ? b : tbytes - 16), dst + q * 1024);
       }
     }
-    sq[buf][0] = s_src[(se + kt) >> 1];
-    if constexpr (WM == 1) sq[buf][1] = rs_src[(se + kt) >> 1];
+  }
+  const uint16_t* stab = reinterpret_cast<const uint16_t*>(tables + wave * (32 * kQMaxGroups * 2))
+                         + (lane & 31) * gld;
+
+  auto issue = [&](int kt, int buf) {
+    int8_t* st = smem + buf * kStage;
+    dma16_to_lds(a_src[0] + kt * QBK, st + (2 * wave) * 1024);
+    dma16_to_lds(a_src[1] + kt * QBK, st + (2 * wave + 1) * 1024);
+    int8_t* lb = st + kQABytes + wave * NB * 1024;
+    if constexpr (WM == 2) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dma16_to_lds(b_src + (size_t)(4 * kt + c) * 1024, lb + c * 1024);
+    } else {
+      dma16_to_lds(b_src + (size_t)(2 * kt) * 1024, lb);
+      dma16_to_lds(b_src + (size_t)(2 * kt + 1) * 1024, lb + 1024);
+      if constexpr (WM == 1) {
+        dma16_to_lds(r_src + (size_t)(2 * kt) * 1024, lb + 2048);
+        dma16_to_lds(r_src + (size_t)(2 * kt + 1) * 1024, lb + 3072);
+      }
+    }
   };
+  // the lane's A operand of k step ks inside a 32-row block: row l%32 of the block,
+  // chunk 2 ks + l/32, at the swizzled slot of its 8-row KB
+  int aoff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int x = lane & 7, c = 2 * ks + (lane >> 5);
+    aoff[ks] = ((lane & 31) >> 3) * 1024 + (8 * x + (c ^ x)) * 16;
+  }
   const intx16 zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   intx16 acc[4];
   float accf[4][16];
@@ -223,7 +287,8 @@ __device__ __forceinline__ void w4a8_tile(
   float sprev = 0.f;
   bool started = false;  // an accumulator holds a group not yet folded
   auto step = [&](int kt, int j) {
-    // this wave's copies of step kt have landed once at most the later steps' are outstanding
+    // this wave's copies of step kt (and the scale tables) have landed once at most the
+    // later steps' are outstanding
     const int after = nk - 1 - kt;
     if constexpr (AH >= 3) {
       if (after >= 2) vm_wait<2 * kOps>(); else if (after == 1) vm_wait<kOps>(); else vm_wait<0>();
@@ -232,8 +297,8 @@ __device__ __forceinline__ void w4a8_tile(
     }
     __builtin_amdgcn_s_barrier();  // every wave's A copies of step kt; every wave is past step kt - 1
     if (kt + AH < nk) issue(kt + AH, (j + AH) % RING);
-    const int8_t* A0 = smem + j * kQStageBytes + lane * 16;
-    const int hi16 = (int)((se + kt) & 1);
+    const int8_t* A0 = smem + j * kStage;
+    const u32x4* bq = reinterpret_cast<const u32x4*>(smem + j * kStage + kQABytes + wave * NB * 1024) + lane;
 #pragma unroll
     for (int sub = 0; sub < (WM == 1 ? 2 : 1); ++sub) {
       // the residual pass reads its A fragments from LDS again rather than holding the
@@ -241,17 +306,16 @@ __device__ __forceinline__ void w4a8_tile(
       int zero = 0;
       if (sub > 0) asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
       const int8_t* A = A0 + zero;
-      const uint32_t word = sq[j][sub];
-      const uint32_t sb = hi16 ? (word & 0xFFFF0000u) : (word << 16);
+      const uint32_t sb = (uint32_t)stab[sub * (8 * 32 * kQMaxGroups) + kt] << 16;
       const float scur = __uint_as_float(sb) * (WM == 2 ? 1.f : 0.0625f);  // int4 enters as 16 q
       // the B operand of k step ks: int8 chunks as they are; int4 words expanded to 16 q
       auto operand = [&](int ks) {
         intx4 b;
         if constexpr (WM == 2) {
-          const u32x4& cw = bq[j][ks];
+          const u32x4 cw = bq[ks * 64];
           b[0] = (int)cw.x; b[1] = (int)cw.y; b[2] = (int)cw.z; b[3] = (int)cw.w;
         } else {
-          const u32x4& cw = bq[j][2 * sub + (ks >> 1)];
+          const u32x4 cw = bq[(2 * sub + (ks >> 1)) * 64];
           const uint32_t w0 = (ks & 1) ? cw.z : cw.x, w1 = (ks & 1) ? cw.w : cw.y;
           b[0] = (int)((w0 << 4) & 0xF0F0F0F0u);
           b[1] = (int)(w0 & 0xF0F0F0F0u);
@@ -272,7 +336,7 @@ __device__ __forceinline__ void w4a8_tile(
         for (int mf = 0; mf < NMF; ++mf) {
           // the previous group (or code set), before the accumulator restarts
           if (ks == 0 && started) fold(mf, sprev);
-          const intx4 a = *reinterpret_cast<const intx4*>(A + (mf * 4 + ks) * 1024);
+          const intx4 a = *reinterpret_cast<const intx4*>(A + aoff[ks] + mf * 4096);
           acc[mf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bk, ks == 0 ? zero16 : acc[mf], 0, 0, 0);
         }
       }
@@ -287,21 +351,37 @@ __device__ __forceinline__ void w4a8_tile(
   }
 #pragma unroll
   for (int mf = 0; mf < NMF; ++mf) fold(mf, sprev);
+  // the row scales go to the first ring stage once every wave is done with it (the
+  // last step's wait left no copy in flight)
+  float* srow = reinterpret_cast<float*>(smem);
+  __syncthreads();
+  if (tid < kGemmBM) srow[tid] = my_rs;
+  __syncthreads();
+
   const int n = rb * 32 + (lane & 31);
+  // accumulator element r of block mf holds tile row mf*32 + 8(r/4) + 4(lane/32) + r%4
+  auto row_of = [&](int mf, int r) { return mf * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
 #pragma unroll
   for (int mf = 0; mf < NMF; ++mf) {
+    if constexpr (PASS == 1) {
+      // lanes 2i and 2i+1 hold the gate and up rows of neuron n/2; after one exchange per
+      // pair of elements the even lane forms elements r < 8, the odd lane elements r + 8
+      const bool odd = lane & 1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = mf * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const bool ok = m < tl.rows;
-      const int p = tl.row_begin + (ok ? m : 0);
-      const float sx = as[(PASS == 1) ? perm[p] / k : p];
-      const float v = accf[mf][r] * sx;
-      if constexpr (PASS == 1) {
-        const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
-        if ((n & 1) == 0 && ok && nvalid) out[(size_t)p * out_ld + (n >> 1)] = silu(v) * u;
-      } else {
-        if (ok && nvalid) out[(size_t)p * out_ld + n] = v;
+      for (int r = 0; r < 8; ++r) {
+        const float lo = accf[mf][r] * srow[row_of(mf, r)];
+        const float hi = accf[mf][r + 8] * srow[row_of(mf, r + 8)];
+        const float got = __shfl_xor(odd ? lo : hi, 1, 64);
+        const float g = odd ? got : lo, u = odd ? hi : got;
+        const int m = row_of(mf, odd ? r + 8 : r);
+        if (m < tl.rows && nvalid)
+          out[(size_t)(tl.row_begin + m) * out_ld + (n >> 1)] = silu_fast(g) * u;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = row_of(mf, r);
+        if (m < tl.rows && nvalid) out[(size_t)(tl.row_begin + m) * out_ld + n] = accf[mf][r] * srow[m];
       }
     }
   }
@@ -320,14 +400,14 @@ __global__ __launch_bounds__(512) void gemm_w4a8_kernel(
     const int32_t* __restrict__ n_tiles, const char* __restrict__ pool, size_t stride,
     tgemv::QuantOffsets o, const int32_t* __restrict__ mask, int E, int split, int N, int K,
     int out_ld, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) int8_t smem[kQRing * kQStageBytes];
+  constexpr int WM = HI ? (PASS == 1 ? 1 : 2) : 0;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[q_lds_bytes(WM)];
   if ((int)blockIdx.y >= n_tiles[0]) return;
   const GemmTile tl = tiles[blockIdx.y];
   const char* slot = pool + (size_t)tl.slot * stride;
   const int nmf = (tl.rows + 31) >> 5;  // 32-row blocks holding rows of the tile
   const bool hi = split && (tl.expert >= E || mask == nullptr || mask[tl.expert] >= 2);
   if (hi != HI) return;
-  constexpr int WM = HI ? (PASS == 1 ? 1 : 2) : 0;
 #define MOE_W4A8_TILE(M_)                                                                         \
   w4a8_tile<PASS, M_, WM>(smem, aq, as, perm, k, tl, slot, WM == 2 ? o.hi : o.lo,                 \
                           WM == 2 ? o.hi_s : o.lo_s, o.hi, o.hi_s, N, K, out_ld, out)
