@@ -144,6 +144,7 @@ constexpr int QBN = 256;          // weight rows of a tile
 constexpr int QBK = 128;          // one scale group per K step
 constexpr int kQABytes = kGemmBM * QBK;  // 16 KB of activations per step
 constexpr int kQMaxGroups = 64;   // K <= 8192
+constexpr int kQCorr = 4;         // K steps between offset corrections of the fold
 static_assert(kGemmBM == 128, "the 8-wave int8 tile covers 128 activation rows");
 // Per weight form WM (below): K steps of copies in flight, 1 KB code chunks per
 // wave and step, scale tables, and the LDS of a workgroup: the ring of stages
@@ -268,24 +269,57 @@ __device__ __forceinline__ void w4a8_tile(
     const int x = lane & 7, c = 2 * ks + (lane >> 5);
     aoff[ks] = ((lane & 31) >> 3) * 1024 + (8 * x + (c ^ x)) * 16;
   }
-  const intx16 zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  // Each group's integer sum P starts from the bit pattern of kMagic = 1.5 * 2^23, so the
+  // int32 sum kMagic_bits + P (|P| <= 128 * 128 * 127 < 2^22) is the float kMagic + P
+  // exactly and a fold is one fma on the accumulator's bits. Each fold adds the offset
+  // kMagic * s, the same for every element of the lane (one weight row); the folded
+  // scales are summed in pend and the offsets removed every kQCorr steps and at the
+  // end, so |accf| stays near kQCorr * kMagic * s (fp32 rounding about 1e-6 of it).
+  // The form with two code sets per step (WM 1) keeps the plain fold (convert, then
+  // fma): it has no registers left for the constant.
+  constexpr bool MAGIC = WM != 1;
+  constexpr int kMagicBits = MAGIC ? 0x4B400000 : 0;
+  constexpr float kMagic = MAGIC ? 12582912.f : 0.f;
+  // the MFMAs' C operand of a group's first k step, held in registers (a value the
+  // compiler cannot see as a constant, so it is not rebuilt before every group)
+  intx16 magic16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  if constexpr (MAGIC) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int v;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(kMagicBits));
+      magic16[r] = v;
+    }
+  }
   intx16 acc[4];
   float accf[4][16];
 #pragma unroll
   for (int mf = 0; mf < 4; ++mf) {
-    acc[mf] = zero16;
+    acc[mf] = magic16;
 #pragma unroll
     for (int r = 0; r < 16; ++r) accf[mf][r] = 0.f;
   }
+  float pend = 0.f;  // scales folded since the last offset correction
   auto fold = [&](int mf, float sw) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) accf[mf][r] = fmaf((float)acc[mf][r], sw, accf[mf][r]);
+    for (int r = 0; r < 16; ++r)
+      accf[mf][r] = fmaf(MAGIC ? __int_as_float(acc[mf][r]) : (float)acc[mf][r], sw, accf[mf][r]);
+  };
+  auto fold_corr = [&](int mf, float sw, float corr) {
+    if constexpr (MAGIC) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accf[mf][r] = fmaf(__int_as_float(acc[mf][r]), sw, accf[mf][r] - corr);
+    } else {
+      fold(mf, sw);
+    }
   };
 #pragma unroll
   for (int s2 = 0; s2 < AH; ++s2)
     if (s2 < nk) issue(s2, s2);
-  float sprev = 0.f;
-  bool started = false;  // an accumulator holds a group not yet folded
+  float sprev = 0.f;  // the scale of the group in the accumulators (0 before the first)
+  // the plain fold skips the first step's (empty) fold; the magic one must fold it to
+  // count its kMagic out evenly, and it adds 0 there
+  bool started = MAGIC;
   auto step = [&](int kt, int j) {
     // this wave's copies of step kt (and the scale tables) have landed once at most the
     // later steps' are outstanding
@@ -329,17 +363,24 @@ __device__ __forceinline__ void w4a8_tile(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) b[ks] = operand(ks);
       }
+      // every kQCorr steps the fold of the previous group also removes the pending offsets
+      const bool correct = MAGIC && (j % kQCorr) == 0 && sub == 0;
+      const float corr = MAGIC ? kMagic * pend : 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const intx4 bk = WM == 0 ? b[WM == 0 ? ks : 0] : operand(ks);
 #pragma unroll
         for (int mf = 0; mf < NMF; ++mf) {
-          // the previous group (or code set), before the accumulator restarts
-          if (ks == 0 && started) fold(mf, sprev);
+          // the previous group (or code set), before the accumulator restarts; before the
+          // first group the accumulator holds kMagic and sprev is 0, so the fold adds 0
+          if (ks == 0 && started) {
+            if (correct) fold_corr(mf, sprev, corr); else fold(mf, sprev);
+          }
           const intx4 a = *reinterpret_cast<const intx4*>(A + aoff[ks] + mf * 4096);
-          acc[mf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bk, ks == 0 ? zero16 : acc[mf], 0, 0, 0);
+          acc[mf] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bk, ks == 0 ? magic16 : acc[mf], 0, 0, 0);
         }
       }
+      if constexpr (MAGIC) pend = correct ? sprev : pend + sprev;
       sprev = scur;
       started = true;
     }
@@ -349,8 +390,12 @@ __device__ __forceinline__ void w4a8_tile(
     for (int j = 0; j < RING; ++j)
       if (kt0 + j < nk) step(kt0 + j, j);
   }
+  {
+    const float corr = MAGIC ? kMagic * pend : 0.f;
 #pragma unroll
-  for (int mf = 0; mf < NMF; ++mf) fold(mf, sprev);
+    for (int mf = 0; mf < NMF; ++mf) fold_corr(mf, sprev, corr);
+  }
+  const float off = MAGIC ? kMagic * sprev : 0.f;  // the last group's offset
   // the row scales go to the first ring stage once every wave is done with it (the
   // last step's wait left no copy in flight)
   float* srow = reinterpret_cast<float*>(smem);
@@ -369,8 +414,8 @@ __device__ __forceinline__ void w4a8_tile(
       const bool odd = lane & 1;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const float lo = accf[mf][r] * srow[row_of(mf, r)];
-        const float hi = accf[mf][r + 8] * srow[row_of(mf, r + 8)];
+        const float lo = (accf[mf][r] - off) * srow[row_of(mf, r)];
+        const float hi = (accf[mf][r + 8] - off) * srow[row_of(mf, r + 8)];
         const float got = __shfl_xor(odd ? lo : hi, 1, 64);
         const float g = odd ? got : lo, u = odd ? hi : got;
         const int m = row_of(mf, odd ? r + 8 : r);
@@ -381,7 +426,8 @@ __device__ __forceinline__ void w4a8_tile(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = row_of(mf, r);
-        if (m < tl.rows && nvalid) out[(size_t)(tl.row_begin + m) * out_ld + n] = accf[mf][r] * srow[m];
+        if (m < tl.rows && nvalid)
+          out[(size_t)(tl.row_begin + m) * out_ld + n] = (accf[mf][r] - off) * srow[m];
       }
     }
   }
