@@ -15,9 +15,14 @@
 // v_mfma_f32_32x32x16_bf16 accumulators, so each LDS fragment feeds two MFMAs.
 // Operands reach LDS through asynchronous global -> LDS copies (16 bytes per
 // lane) in a ring of kStages stages, no register holding data in flight:
-//   A: 8 fragments of 1 KB per stage, fragment (mf, ks) holding row
-//      mf*32 + l%32, K values ks*16 + 8 (l / 32) .. +7 at lane l (the MFMA
-//      operand layout);
+//   A: the stage's 128 rows x 32 K values (64 bytes a row), one copy
+//      instruction per wave covering 16 whole rows (4 lanes a row). Row r's
+//      16-byte chunk c lands in slot 4 (r % 16) + (c ^ ((r / 4) % 4)) of its
+//      16-row KB, so the MFMA operand reads (lane l: row mf*32 + l%32, chunk
+//      2 ks + l/32) of any 16 consecutive lanes hit 16 different 16-byte
+//      groups of the 256 bytes the 64 LDS banks serve at once. (Copies of 32
+//      rows x 32 bytes cost twice the cache-line requests and left the loop
+//      bound by them.)
 //   B: the 16 chunks of the tile's 8 weight blocks, as stored.
 // Each wave issues 3 copies per stage; before computing stage kt it waits
 // until only the later stages' copies are outstanding, then one barrier
@@ -61,14 +66,21 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int mh = wave & 1, np = wave >> 1;
   const int nrb = N / 32;
-  // copies of this wave per stage: A fragment (lmf, lks); the 2 chunks of weight block `wave`
-  const int lmf = wave >> 1, lks = wave & 1;
+  // copies of this wave per stage: rows 16 wave .. +15 of A (row m into slot `lane` of KB
+  // `wave`, so chunk (lane % 4) ^ ((m / 4) % 4)); the 2 chunks of weight block `wave`
   const uint16_t* a_src;
   {
-    const int m = lmf * 32 + (lane & 31);
+    const int m = 16 * wave + (lane >> 2);
     const int p = tl.row_begin + (m < tl.rows ? m : 0);  // rows past the tile read row 0
     const size_t r = (PASS == 1) ? (size_t)(perm[p] / k) : (size_t)p;
-    a_src = act + r * K + lks * 16 + 8 * (lane >> 5);
+    a_src = act + r * K + 8 * ((lane & 3) ^ ((m >> 2) & 3));
+  }
+  // the lane's A operand of k step ks inside a 32-row block (row l%32, chunk 2 ks + l/32)
+  int aoff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int r = lane & 31, c = 2 * ks + (lane >> 5);
+    aoff[ks] = (r >> 4) * 1024 + (4 * (r & 15) + (c ^ ((r >> 2) & 3))) * 16;
   }
   int lrb = blockIdx.x * (BN / 32) + wave;
   if (lrb >= nrb) lrb = nrb - 1;
@@ -84,7 +96,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(
   auto stage_a = [&](int buf) { return smem + buf * kStageBytes; };
   auto stage_b = [&](int buf) { return smem + buf * kStageBytes + 8192; };
   auto issue = [&](int kt, int buf) {
-    copy16_to_lds(a_src + kt * BK, stage_a(buf) + (lmf * 2 + lks) * 1024);
+    copy16_to_lds(a_src + kt * BK, stage_a(buf) + wave * 1024);
     char* lb = stage_b(buf) + wave * 2048;
 #pragma unroll
     for (int c = 0; c < 2; ++c) copy16_to_lds(b_src + (size_t)(2 * kt + c) * 1024, lb + c * 1024);
@@ -117,7 +129,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(
         b[nb] = *reinterpret_cast<const bf16x8*>(Bs + ((np * 2 + nb) * 2 + ks) * 1024 + lane * 16);
 #pragma unroll
       for (int mf = 0; mf < 2; ++mf) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + ((mh * 2 + mf) * 2 + ks) * 1024 + lane * 16);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + (mh * 2 + mf) * 2048 + aoff[ks]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           acc[mf][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[nb], acc[mf][nb], 0, 0, 0);
