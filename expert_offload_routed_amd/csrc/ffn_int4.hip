@@ -124,9 +124,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 //   A: the step's 128 rows x 128 int8 values (16 KB). One copy instruction
 //      takes 8 whole rows (8 lanes per 128-byte row), and the eight waves
 //      copy two each. Row r's 16-byte chunk c lands in slot
-//      8 (r % 8) + (c ^ (r % 8)) of its 8-row KB, so the MFMA operand reads
-//      (lane l: row mf*32 + l%32, chunk 2 ks + l/32) hit eight different
-//      16-byte bank groups in each set of 8 lanes.
+//      8 (r % 8) + (c ^ ((r / 2) % 8)) of its 8-row KB, so the MFMA operand
+//      reads (lane l: row mf*32 + l%32, chunk 2 ks + l/32) of any 16
+//      consecutive lanes hit 16 different 16-byte groups of the 256 bytes the
+//      64 LDS banks serve at once.
 //   B: the wave's own two 1 KB code chunks per step (no other wave reads
 //      them), read back 16 bytes per lane and expanded to int8 with two masks
 //      and a shift.
@@ -215,13 +216,14 @@ __device__ __forceinline__ void w4a8_tile(
     const int p = tl.row_begin + (tid < tl.rows ? tid : 0);
     my_rs = as[(PASS == 1) ? perm[p] / k : p];
   }
-  // this lane's two A copies: rows 16 wave + 8 q + lane/8, chunk (lane%8) ^ (lane/8)
+  // this lane's two A copies: row m = 16 wave + 8 q + lane/8 into slot lane of its KB,
+  // so chunk (lane%8) ^ ((m / 2) % 8)
   const int8_t* a_src[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int m = 16 * wave + 8 * q + (lane >> 3);
     const int p = tl.row_begin + (m < tl.rows ? m : 0);  // rows past the tile read row 0
-    a_src[q] = aq + (size_t)((PASS == 1) ? perm[p] / k : p) * K + 16 * ((lane & 7) ^ (lane >> 3));
+    a_src[q] = aq + (size_t)((PASS == 1) ? perm[p] / k : p) * K + 16 * ((lane & 7) ^ ((m >> 1) & 7));
   }
   // chunk c of K step kt: int4 (K / 64 chunks per block, 2 per step), int8 (K / 32, 4 per step)
   const size_t blk = (size_t)rb * (K / (WM == 2 ? 32 : 64)) * 1024 + lane * 16;
@@ -266,8 +268,8 @@ __device__ __forceinline__ void w4a8_tile(
   int aoff[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int x = lane & 7, c = 2 * ks + (lane >> 5);
-    aoff[ks] = ((lane & 31) >> 3) * 1024 + (8 * x + (c ^ x)) * 16;
+    const int r = lane & 31, c = 2 * ks + (lane >> 5);  // row within the 32-row block
+    aoff[ks] = (r >> 3) * 1024 + (8 * (r & 7) + (c ^ ((r >> 1) & 7))) * 16;
   }
   // Each group's integer sum P starts from the bit pattern of kMagic = 1.5 * 2^23, so the
   // int32 sum kMagic_bits + P (|P| <= 128 * 128 * 127 < 2^22) is the float kMagic + P
