@@ -457,12 +457,14 @@ struct StageLds {
 // Item modes of the quantised passes: 0 = int4, 1 = int4 + int4 residual, 2 = int8.
 // QIN: the activation rows are quantised per tile by the workgroup (stage_rows,
 // from raw) instead of read from the int8 buffers aq / as.
+// staged: the activation row held in the LDS stage when it holds one row (its row
+// index in raw), else -1; a one-row tile of the same row is not quantised again.
 template <int MODE, int KS, int RBW, int U, int MAXNT, bool SWIGLU, bool QIN>
 __device__ __forceinline__ void quant_item(const char* slot, const QuantOffsets& o, int K,
                                            const int8_t* aq, const float* as, const void* raw,
                                            const StageLds& st, const int32_t* perm, int k,
                                            const FfnItem& it, int rb0, int nrb, int out_ld,
-                                           float* out, float* red) {
+                                           float* out, float* red, int& staged) {
   const char* wb = slot + (MODE == 2 ? o.hi : o.lo);
   const uint16_t* ws = reinterpret_cast<const uint16_t*>(slot + (MODE == 2 ? o.hi_s : o.lo_s));
   const char* rb = slot + o.hi;
@@ -472,7 +474,12 @@ __device__ __forceinline__ void quant_item(const char* slot, const QuantOffsets&
   constexpr int UQ = (MODE == 1 && U > 1) ? U / 2 : U;
 #define TGEMV_Q(NT_, P_)                                                                       \
   do {                                                                                         \
-    if constexpr (QIN) stage_rows<SWIGLU, NT_>(raw, perm, k, P_, K, st.q, st.s, st.wmax);      \
+    if constexpr (QIN) {                                                                       \
+      const int key_ = NT_ == 1 ? (SWIGLU ? perm[P_] / k : (P_)) : -1;                         \
+      if (key_ < 0 || key_ != staged)                                                          \
+        stage_rows<SWIGLU, NT_>(raw, perm, k, P_, K, st.q, st.s, st.wmax);                     \
+      staged = key_;                                                                           \
+    }                                                                                          \
     const int8_t* aq_ = QIN ? st.q : aq;                                                       \
     const float* as_ = QIN ? st.s : as;                                                        \
     if constexpr (MODE == 2)                                                                   \
@@ -513,8 +520,16 @@ __global__ __launch_bounds__(NW * 64) void int4_kernel(
   const StageLds st{st_q, st_s, st_wmax};
   const int wave = threadIdx.x >> 6;
   const int nrb = R / 32;
+  // One-row tiles (the launch holds only the resident workgroups): a contiguous range of
+  // units per workgroup, so consecutive units mostly share an item and its staged row.
+  // Otherwise one unit per workgroup in turn (grid-stride), the workgroups with work
+  // first when fewer items are present than the grid was sized for.
   const int units = n_items[0] * units_per_item;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+  const int ub = MAXNT == 1 ? (int)((long long)units * blockIdx.x / gridDim.x) : (int)blockIdx.x;
+  const int ue = MAXNT == 1 ? (int)((long long)units * (blockIdx.x + 1) / gridDim.x) : units;
+  const int us = MAXNT == 1 ? 1 : (int)gridDim.x;
+  int staged = -1;
+  for (int u = ub; u < ue; u += us) {
     const int item = u / units_per_item;
     const int rb0 = ((u - item * units_per_item) * (NW / KS) + wave / KS) * RBW;
     const FfnItem it = items[item];
@@ -523,10 +538,10 @@ __global__ __launch_bounds__(NW * 64) void int4_kernel(
     if constexpr (SPLIT) hi = it.expert >= E || mask == nullptr || mask[it.expert] >= 2;
     if (hi)
       quant_item<SWIGLU ? 1 : 2, KS, RBW, U, MAXNT, SWIGLU, QIN>(
-          slot, offs, K, aq, as, raw, st, perm, k, it, rb0, nrb, out_ld, out, red);
+          slot, offs, K, aq, as, raw, st, perm, k, it, rb0, nrb, out_ld, out, red, staged);
     else
       quant_item<0, KS, RBW, U, MAXNT, SWIGLU, QIN>(slot, offs, K, aq, as, raw, st, perm, k, it,
-                                                    rb0, nrb, out_ld, out, red);
+                                                    rb0, nrb, out_ld, out, red, staged);
   }
 }
 #undef TGEMV_REST
