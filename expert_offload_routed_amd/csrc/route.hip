@@ -220,13 +220,16 @@ __device__ void topk_token(const float* __restrict__ logits, int t, int E, int k
   }
 }
 
+// NV logits per lane (E <= 64 NV): a launch at decode sizes runs from a cold
+// instruction cache, so it holds only the code its E needs.
+template <int NV>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int T,
                                                            int E, int k, int renorm,
                                                            int32_t* __restrict__ ids,
                                                            float* __restrict__ weights) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token<kTopkMaxV>(logits, t, E, k, renorm, ids, weights);
+  topk_token<NV>(logits, t, E, k, renorm, ids, weights);
 }
 
 // Second half of the decode front end, run by one workgroup (any size up to
@@ -598,8 +601,14 @@ extern "C" int moe_route(const void* x, int x_dtype, const void* w_router, const
   else
     hipLaunchKernelGGL(route_logits_kernel<MOE_F32>, g1, dim3(256), 0, stream, x, w_router, bias,
                        T, H, E, logits);
-  hipLaunchKernelGGL(topk_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E,
-                     k, renorm, topk_ids, topk_w);
+#define MOE_TOPK(NV_)                                                                      \
+  hipLaunchKernelGGL(topk_softmax_kernel<NV_>, dim3((T + 3) / 4), dim3(256), 0, stream, logits, \
+                     T, E, k, renorm, topk_ids, topk_w)
+  if (E <= 64) MOE_TOPK(1);
+  else if (E <= 128) MOE_TOPK(2);
+  else if (E <= 256) MOE_TOPK(4);
+  else MOE_TOPK(kTopkMaxV);
+#undef MOE_TOPK
   return moe_launch_status();
 }
 
