@@ -160,6 +160,8 @@ FFN_CASES = [
     (W.reduced(DSV3, E=16, k=4, H=512, F=256), 3),
     (W.reduced(DSV3, E=16, k=4, H=512, F=256), 40),
     (W.reduced(DSV3, E=16, k=4, H=512, F=256), 300),
+    (W.reduced(DSV3, E=12, k=8, H=7168, F=2048), 1),  # full sizes, one token: workgroups take
+                                                       # several units of the gate/up pass
     (W.reduced(DSV3, E=12, k=8, H=7168, F=2048), 2),  # full hidden/FFN sizes
     (W.reduced(DSV3, E=12, k=8, H=7168, F=2048), 24),
     (W.reduced(DSV3, E=12, k=8, H=7168, F=2048), 200),  # every group on MFMA tiles, some > 128 rows
