@@ -137,7 +137,7 @@ def recorded_traffic(key):
 
 # the sources the expert-FFN kernels are compiled from (routing, runtime and combine excluded)
 FFN_SOURCES = ("common.h", "ffn_internal.h", "ffn.hip", "ffn_gemv.h", "tile_gemv.h", "gemm.hip",
-               "ffn_int4.hip")
+               "skinny.hip", "ffn_int4.hip")
 
 
 def ffn_sources_sha1() -> str:

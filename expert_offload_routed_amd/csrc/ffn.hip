@@ -136,19 +136,28 @@ void launch_tile_any(const void* act, const int32_t* perm, int k, const FfnItem*
                                              stride, off, R, K, out_ld, out, s);
 }
 
-// bf16 tokens and weights: tile-major GEMV for small groups, MFMA tiles for the rest.
+// bf16 tokens and weights: small groups on the tile-major GEMV (one token) or the MFMA
+// GEMV (decode batches, skinny.hip), MFMA tiles for the rest.
 template <int MAXNT>
 void launch_bf16(const void* x, const int32_t* perm, int k, const FfnItem* items,
                  const int32_t* n_items, int max_items, const GemmTile* tiles,
                  const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
                  const SlotLayout& lay, int H, int F, void* hbuf, float* y, hipStream_t s) {
-  launch_tile_any<MAXNT, true, MOE_BF16, MOE_BF16>(x, perm, k, items, n_items, max_items, pool,
-                                                   stride, lay.off_w13, 2 * F, H, F, hbuf, s);
+  if constexpr (MAXNT == 1)
+    launch_tile_any<MAXNT, true, MOE_BF16, MOE_BF16>(x, perm, k, items, n_items, max_items, pool,
+                                                     stride, lay.off_w13, 2 * F, H, F, hbuf, s);
+  else
+    launch_skinny_bf16(1, x, perm, k, items, n_items, max_items, pool, stride, lay.off_w13, 2 * F,
+                       H, F, hbuf, s);
   if (max_tiles > 0)
     launch_gemm_bf16(1, x, perm, k, tiles, n_tiles, max_tiles, pool, stride, lay.off_w13, 2 * F, H,
                      F, hbuf, s);
-  launch_tile_any<MAXNT, false, MOE_BF16, MOE_F32>(hbuf, perm, k, items, n_items, max_items,
-                                                   pool, stride, lay.off_w2, H, F, H, y, s);
+  if constexpr (MAXNT == 1)
+    launch_tile_any<MAXNT, false, MOE_BF16, MOE_F32>(hbuf, perm, k, items, n_items, max_items,
+                                                     pool, stride, lay.off_w2, H, F, H, y, s);
+  else
+    launch_skinny_bf16(2, hbuf, perm, k, items, n_items, max_items, pool, stride, lay.off_w2, H, F,
+                       H, y, s);
   if (max_tiles > 0)
     launch_gemm_bf16(2, hbuf, perm, k, tiles, n_tiles, max_tiles, pool, stride, lay.off_w2, H, F, H,
                      y, s);
@@ -175,11 +184,13 @@ void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* 
                      shared_slot0, num_slots, small_max, items, n_items, tiles, n_tiles, err_word);
 }
 
-int ffn_small_max(int T, int k, int E, int n_shared) {
+int ffn_small_max(int T, int k, int E, int n_shared, int w_dtype) {
   // with many rows per group on average, every group takes the MFMA tiles and
   // the GEMV passes are not launched at all
   const long long rows = (long long)T * (k + n_shared);
-  return rows > 16LL * (E + n_shared) ? 0 : kGemvMaxRows;
+  if (rows > 16LL * (E + n_shared)) return 0;
+  // bf16 decode batches: groups of up to 32 rows on the MFMA GEMV; one token: the GEMV
+  return (w_dtype == MOE_BF16 && T >= 2) ? kSkinnyMaxRows : kGemvMaxRows;
 }
 
 FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype, int n_shared) {
@@ -267,7 +278,7 @@ int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* o
   const long long tk = (long long)T * k;
   const bool bf16 = (w_dtype == MOE_BF16);
   // a group holds at most T rows (a token picks an expert once)
-  const int small_max = bf16 ? ffn_small_max(T, k, E, n_shared) : INT_MAX;
+  const int small_max = bf16 ? ffn_small_max(T, k, E, n_shared, w_dtype) : INT_MAX;
   const int max_items = small_max == 0 ? 0 : (int)(tk < E ? tk : E) + n_shared;
   const int max_tiles = (bf16 && T > small_max) ? ws.max_tiles : 0;
   MOE_CHECK_ARG(max_tiles <= 65535);
@@ -276,17 +287,13 @@ int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* o
     launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max,
                     items, n_items, tiles, n_tiles, err_word, stream);
   const char* pool = static_cast<const char*>(pool_base);
-  const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;  // rows of the largest GEMV group
   if (bf16) {
-    if (nt <= 1)
+    if (T <= 1)
       launch_bf16<1>(x, perm, k, items, n_items, max_items, tiles, n_tiles, max_tiles, pool,
                      slot_stride, lay, H, F, hbuf, y_perm, stream);
-    else if (nt <= 2)
-      launch_bf16<2>(x, perm, k, items, n_items, max_items, tiles, n_tiles, max_tiles, pool,
-                     slot_stride, lay, H, F, hbuf, y_perm, stream);
     else
-      launch_bf16<4>(x, perm, k, items, n_items, max_items, tiles, n_tiles, max_tiles, pool,
-                     slot_stride, lay, H, F, hbuf, y_perm, stream);
+      launch_bf16<kSkinnyMaxRows>(x, perm, k, items, n_items, max_items, tiles, n_tiles,
+                                  max_tiles, pool, slot_stride, lay, H, F, hbuf, y_perm, stream);
   } else {
     if (T <= 1)
       launch_f32<1>(x, perm, k, items, n_items, max_items, pool, slot_stride, lay, H, F, hbuf,

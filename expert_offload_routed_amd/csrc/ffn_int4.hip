@@ -177,7 +177,9 @@ __device__ __forceinline__ void vm_wait() {
 // copies with explicit waits on the vector-memory counter (in-order
 // completion) and barriers, and waits for all of them before the workgroup
 // ends. The compiler's own waits stay correct: a copy it does not know about
-// only makes them more conservative.
+// only makes them more conservative. m0 is listed as clobbered; the kernels
+// that use these copies hold no other m0 value (their code writes m0 only right
+// before each copy).
 __device__ __forceinline__ void dma16_to_lds(const void* g, void* lds) {
   const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -614,7 +616,7 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   if (H > 4 * 2048 || F > 4 * 2048) return MOE_EUNSUPPORTED;  // quant_rows covers 8192 values
   const long long tk = (long long)T * k;
   const long long rows = (long long)T * (k + n_shared);
-  const int small_max = ffn_small_max(T, k, E, n_shared);
+  const int small_max = ffn_small_max(T, k, E, n_shared, MOE_INT4G128);
   const int max_items = small_max == 0 ? 0 : (int)(tk < E ? tk : E) + n_shared;
   const int max_tiles = (T > small_max) ? wl.max_tiles : 0;
   if (max_tiles > 65535) return MOE_EUNSUPPORTED;

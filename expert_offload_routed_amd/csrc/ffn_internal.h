@@ -22,6 +22,9 @@ struct GemmTile {
 
 constexpr int kGemmBM = 128;     // rows of an MFMA M-tile
 constexpr int kGemvMaxRows = 4;  // groups up to this many rows take the GEMV path
+// bf16 with two or more tokens: groups up to this many rows take the MFMA GEMV (skinny.hip)
+constexpr int kSkinnyMaxRows = 32;
+constexpr int kSkinnyGridCap = 16384;  // workgroups of a skinny pass (they loop over units)
 
 // Byte layout of one expert inside a slot (see moe_slot_layout).
 struct SlotLayout {
@@ -47,7 +50,14 @@ void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* 
                      int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
                      hipStream_t s);
 // Largest group that takes the GEMV path (0: every group takes the MFMA tiles).
-int ffn_small_max(int T, int k, int E, int n_shared);
+int ffn_small_max(int T, int k, int E, int n_shared, int w_dtype);
+// One bf16 pass over the work list's items on MFMA (groups of up to kSkinnyMaxRows rows):
+// pass 1 reads tokens act[perm[p] / k] and writes h = SiLU(gate) * up (bf16), pass 2
+// reads h rows p and writes y (fp32); weights at slot + off, [R, K] tile-major.
+void launch_skinny_bf16(int pass, const void* act, const int32_t* perm, int k,
+                        const FfnItem* items, const int32_t* n_items, int max_items,
+                        const char* pool, size_t stride, size_t off, int R, int K, int out_ld,
+                        void* out, hipStream_t s);
 void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, const GemmTile* tiles,
                       const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
                       size_t off, int N, int K, int out_ld, void* out, hipStream_t s);

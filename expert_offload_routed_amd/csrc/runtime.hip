@@ -960,7 +960,7 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
     fp.num_slots = nslots;
     fp.n_shared = nsh;
     fp.shared_slot0 = c->S;
-    fp.small_max = c->w_dtype == MOE_F32 ? INT_MAX : ffn_small_max(T, k, E, nsh);
+    fp.small_max = c->w_dtype == MOE_F32 ? INT_MAX : ffn_small_max(T, k, E, nsh, c->w_dtype);
     fp.items = reinterpret_cast<FfnItem*>(c->ws + wl.items);
     fp.n_items = reinterpret_cast<int32_t*>(c->ws);
     fp.tiles = reinterpret_cast<GemmTile*>(c->ws + wl.tiles);
