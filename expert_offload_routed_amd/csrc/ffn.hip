@@ -176,6 +176,31 @@ void launch_f32(const void* x, const int32_t* perm, int k, const FfnItem* items,
 
 }  // namespace
 
+long long resident_workgroups(const void* kern, int threads, size_t lds,
+                              std::atomic<long long>& cache) {
+  static std::atomic<int> cus[64];  // compute units per device
+  int dev = 0, n = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          n <= 0)
+        n = 256;
+      cus[dev].store(n, std::memory_order_relaxed);
+    }
+  }
+  long long o = cache.load(std::memory_order_relaxed);  // (lds << 8) | workgroups per CU
+  if (o < 0 || (size_t)(o >> 8) != lds) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, lds) != hipSuccess ||
+        nb < 1)
+      nb = 1;
+    o = ((long long)lds << 8) | (nb > 255 ? 255 : nb);
+    cache.store(o, std::memory_order_relaxed);
+  }
+  return (o & 0xFF) * (long long)n;
+}
+
 void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
                      int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
                      int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,

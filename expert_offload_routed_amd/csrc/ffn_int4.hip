@@ -20,8 +20,6 @@
 // nibbles = codes 4..7, so
 //   (w << 4) & 0xF0F0F0F0  and  w & 0xF0F0F0F0
 // are two words of 4 consecutive int8 values (16 q) in natural order.
-#include <atomic>
-
 #include "common.h"
 #include "ffn_internal.h"
 #include "tile_gemv.h"
@@ -469,20 +467,6 @@ __global__ __launch_bounds__(512) void gemm_w4a8_kernel(
 #undef MOE_W4A8_TILE
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 // The quantised GEMV pass. With one-row tiles (decode of one token) every unit costs the
 // same and, in the gate/up pass, reads the same staged token row: the grid then holds only
 // as many workgroups as are resident at once (occupancy x compute units), each taking a
@@ -506,18 +490,9 @@ void launch_gemv(const int8_t* aq, const float* as, const void* raw, const int32
   const auto kern = tgemv::int4_kernel<KS, RBW, NW, U, MAXNT, SWIGLU, SPLIT, QIN>;
   long long g = units;
   if constexpr (MAXNT == 1) {
-    // workgroups per compute unit for this instantiation and LDS size: (lds << 8) | blocks
-    static std::atomic<long long> occ{-1};
-    long long o = occ.load(std::memory_order_relaxed);
-    if (o < 0 || (size_t)(o >> 8) != lds) {
-      int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kern),
-                                                       NW * 64, lds) != hipSuccess || nb < 1)
-        nb = 1;
-      o = ((long long)lds << 8) | (nb > 255 ? 255 : nb);
-      occ.store(o, std::memory_order_relaxed);
-    }
-    const long long resident = (o & 0xFF) * (long long)device_cus();
+    static std::atomic<long long> occ{-1};  // per instantiation
+    const long long resident =
+        resident_workgroups(reinterpret_cast<const void*>(kern), NW * 64, lds, occ);
     if (g > resident) g = resident;
   }
   if (g > tgemv::kGridCap) g = tgemv::kGridCap;

@@ -1,6 +1,8 @@
 // Internal layouts shared by the host code of the FFN and slot sources.
 #pragma once
 
+#include <atomic>
+
 #include <stddef.h>
 #include <stdint.h>
 
@@ -49,6 +51,11 @@ void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* 
                      int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
                      int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
                      hipStream_t s);
+// Workgroups of kernel `kern` resident at once on the current device (occupancy with
+// `threads` threads and `lds` bytes of dynamic LDS, times the compute units). `cache`,
+// one per kernel instantiation, keeps the occupancy for the last LDS size.
+long long resident_workgroups(const void* kern, int threads, size_t lds,
+                              std::atomic<long long>& cache);
 // Largest group that takes the GEMV path (0: every group takes the MFMA tiles).
 int ffn_small_max(int T, int k, int E, int n_shared, int w_dtype);
 // One bf16 pass over the work list's items on MFMA (groups of up to kSkinnyMaxRows rows):
