@@ -214,8 +214,10 @@ int ffn_small_max(int T, int k, int E, int n_shared, int w_dtype) {
   // the GEMV passes are not launched at all
   const long long rows = (long long)T * (k + n_shared);
   if (rows > 16LL * (E + n_shared)) return 0;
-  // bf16 decode batches: groups of up to 32 rows on the MFMA GEMV; one token: the GEMV
-  return (w_dtype == MOE_BF16 && T >= 2) ? kSkinnyMaxRows : kGemvMaxRows;
+  // decode batches of bf16 or int4 (not split-precision) experts: groups of up to 32 rows
+  // on the MFMA GEMV; one token: the GEMV
+  return ((w_dtype == MOE_BF16 || w_dtype == MOE_INT4G128) && T >= 2) ? kSkinnyMaxRows
+                                                                       : kGemvMaxRows;
 }
 
 FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype, int n_shared) {

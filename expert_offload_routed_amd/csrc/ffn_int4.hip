@@ -591,23 +591,32 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   if (H > 4 * 2048 || F > 4 * 2048) return MOE_EUNSUPPORTED;  // quant_rows covers 8192 values
   const long long tk = (long long)T * k;
   const long long rows = (long long)T * (k + n_shared);
-  const int small_max = ffn_small_max(T, k, E, n_shared, MOE_INT4G128);
+  const int small_max =
+      ffn_small_max(T, k, E, n_shared, split ? MOE_INT4G128_RESPLIT : MOE_INT4G128);
+  // decode batches (not split-precision): groups of up to 32 rows on the MFMA GEMV, which
+  // reads the rows quantised by quant_rows_kernel
   const int max_items = small_max == 0 ? 0 : (int)(tk < E ? tk : E) + n_shared;
   const int max_tiles = (T > small_max) ? wl.max_tiles : 0;
   if (max_tiles > 65535) return MOE_EUNSUPPORTED;
   if (!planned)
     launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max,
                     items, n_items, tiles, n_tiles, err, s);
-  // with no MFMA tile every row is quantised by the GEMV workgroups that read it (a
-  // decode step then runs two weight passes and no separate quantisation launch)
-  const bool fused = max_tiles == 0;
+  const bool skinny = !split && T >= 2 && small_max > kGemvMaxRows;
+  // with no MFMA tile (and no MFMA GEMV) every row is quantised by the GEMV workgroups
+  // that read it (a decode step then runs two weight passes and no separate quantisation)
+  const bool fused = max_tiles == 0 && !skinny;
   if (!fused)
     hipLaunchKernelGGL(quant_rows_kernel<MOE_BF16>, dim3(T), dim3(256), 0, s, x, H, nullptr,
                        nullptr, nullptr, 0, 0, 0, xq, xs);
   const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;
-  if (max_items > 0)
-    launch_gemv_any(true, split, nt, xq, xs, fused ? x : nullptr, perm, k, items, n_items,
-                    max_items, pool, stride, lay, group_mask, E, H, F, hbuf, s);
+  if (max_items > 0) {
+    if (skinny)
+      launch_skinny_w4a8(1, xq, xs, perm, k, items, n_items, max_items, pool, stride, lay.off_w13,
+                         lay.off_s13, 2 * F, H, F, hbuf, s);
+    else
+      launch_gemv_any(true, split, nt, xq, xs, fused ? x : nullptr, perm, k, items, n_items,
+                      max_items, pool, stride, lay, group_mask, E, H, F, hbuf, s);
+  }
   const tgemv::QuantOffsets o13{lay.off_w13, lay.off_s13, lay.off_r13, lay.off_rs13};
   const tgemv::QuantOffsets o2{lay.off_w2, lay.off_s2, lay.off_h2, lay.off_hs2};
   const dim3 g13((2 * F + QBN - 1) / QBN, max_tiles), g2((H + QBN - 1) / QBN, max_tiles);
@@ -621,9 +630,14 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   if (!fused)
     hipLaunchKernelGGL(quant_rows_kernel<MOE_F32>, dim3((unsigned)rows), dim3(256), 0, s, hbuf, F,
                        offsets, lut, group_mask, E, n_shared, num_slots, hq, hs);
-  if (max_items > 0)
-    launch_gemv_any(false, split, nt, hq, hs, fused ? hbuf : nullptr, perm, k, items, n_items,
-                    max_items, pool, stride, lay, group_mask, E, H, F, y, s);
+  if (max_items > 0) {
+    if (skinny)
+      launch_skinny_w4a8(2, hq, hs, perm, k, items, n_items, max_items, pool, stride, lay.off_w2,
+                         lay.off_s2, H, F, H, y, s);
+    else
+      launch_gemv_any(false, split, nt, hq, hs, fused ? hbuf : nullptr, perm, k, items, n_items,
+                      max_items, pool, stride, lay, group_mask, E, H, F, y, s);
+  }
   if (max_tiles > 0) {
     hipLaunchKernelGGL((gemm_w4a8_kernel<2, false>), g2, dim3(512), 0, s, hq, hs, perm, k, tiles,
                        n_tiles, pool, stride, o2, group_mask, E, split ? 1 : 0, H, F, H, y);

@@ -24,7 +24,8 @@ struct GemmTile {
 
 constexpr int kGemmBM = 128;     // rows of an MFMA M-tile
 constexpr int kGemvMaxRows = 4;  // groups up to this many rows take the GEMV path
-// bf16 with two or more tokens: groups up to this many rows take the MFMA GEMV (skinny.hip)
+// bf16 or int4 with two or more tokens: groups up to this many rows take the MFMA GEMV
+// (skinny.hip)
 constexpr int kSkinnyMaxRows = 32;
 constexpr int kSkinnyGridCap = 16384;  // workgroups of a skinny pass (they loop over units)
 
@@ -65,6 +66,13 @@ void launch_skinny_bf16(int pass, const void* act, const int32_t* perm, int k,
                         const FfnItem* items, const int32_t* n_items, int max_items,
                         const char* pool, size_t stride, size_t off, int R, int K, int out_ld,
                         void* out, hipStream_t s);
+// The same over int4 weights (codes at off_codes, group scales at off_scales) with int8 rows
+// aq and their scales as (pass 1: tokens perm[p] / k, pass 2: h rows p); out is fp32 (pass 1:
+// h = SiLU(gate) * up, pass 2: y).
+void launch_skinny_w4a8(int pass, const int8_t* aq, const float* as, const int32_t* perm, int k,
+                        const FfnItem* items, const int32_t* n_items, int max_items,
+                        const char* pool, size_t stride, size_t off_codes, size_t off_scales,
+                        int R, int K, int out_ld, float* out, hipStream_t s);
 void launch_gemm_bf16(int pass, const void* act, const int32_t* perm, int k, const GemmTile* tiles,
                       const int32_t* n_tiles, int max_tiles, const char* pool, size_t stride,
                       size_t off, int N, int K, int out_ld, void* out, hipStream_t s);

@@ -139,7 +139,10 @@ def test_expert_ffn_split_precision(shape, T):
         hr = np.concatenate(hi_rows)
         say(f"  high rows rel L2 {rel_l2(y_h[hr], yr[hr]):.3e}")
         assert rel_l2(y_h[hr], yr[hr]) <= TOL[shape.wfmt]
-    # low rows: bitwise what the int4 path computes on the same slots
+    # low rows: what the int4 path computes on the same slots. With one token both take
+    # the same GEMV, so bit for bit; with more, the int4 path runs groups of up to 32 rows
+    # on the MFMA GEMV while split-precision steps keep the GEMV and the MFMA tiles, which
+    # fold the same exact group sums in another fp32 order (a few int8 codes of h flip)
     if lo_rows:
         lr = np.concatenate(lo_rows)
         lo_mask = torch.from_numpy(np.where(mask_np == 1, 1, 0).astype(np.int32)).to(_dev())
@@ -149,7 +152,12 @@ def test_expert_ffn_split_precision(shape, T):
         B.moe_expert_ffn(x, p["perm"], p["offsets"], lut, lo_mask, pool, stride, B.MOE_INT4G128, T, H, F,
                          E, k, y4, err, ws4)
         torch.cuda.synchronize()
-        assert torch.equal(y[lr], y4[lr])
+        if T == 1:
+            assert torch.equal(y[lr], y4[lr])
+        else:
+            d = rel_l2(y_h[lr], y4.cpu().numpy()[lr])
+            say(f"  low rows vs the int4 path: rel L2 {d:.3e}")
+            assert d <= 5e-3
     # no mask: every group at high precision; determinism of the high rows
     y2 = torch.full_like(y, 7.0)
     B.moe_expert_ffn(x, p["perm"], p["offsets"], lut, None, pool, stride, code, T, H, F, E, k, y2, err, ws)
