@@ -8,10 +8,15 @@
 //     ids (integer atomics: the counts do not depend on their order), then a
 //     block-wide exclusive scan for the offsets and a second scan that
 //     compacts the experts with a non-zero count.
-//   permute_rank_kernel (one wave per expert): a token picks an expert at most
-//     once, so an expert's rows are the tokens that picked it in ascending
-//     order. The wave walks the tokens 64 at a time; a ballot of "picked this
-//     expert" and the popcount of the lanes below give each row its rank.
+//   permute_rank_kernel (one workgroup of 8 waves per expert): a token picks
+//     an expert at most once, so an expert's rows are the tokens that picked
+//     it in ascending order, which is the order of the flat index t * k + j of
+//     the picks. The workgroup walks the flat ids in rounds of 8 x 64 x 64
+//     entries, each wave a contiguous 4096 of them, 64 a load: first every
+//     lane keeps one bit per load ("this entry is the expert") and the wave
+//     counts them; after a barrier each wave starts at the expert's offset
+//     plus the counts of the waves before it, and a ballot of the kept bits
+//     and the popcount of the lanes below give each row its rank.
 #include "common.h"
 
 namespace {
@@ -26,9 +31,16 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __re
   const int tid = threadIdx.x;
   s_cnt[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += 1024) {
-    const int e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+  for (int i0 = 0; i0 < n; i0 += 8 * 1024) {  // 8 loads in flight per thread
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 1024 + tid;
+      ev[u] = i < n ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (ev[u] >= 0 && ev[u] < E) atomicAdd(&s_cnt[ev[u]], 1);
   }
   __syncthreads();
   const int c = (tid < E) ? s_cnt[tid] : 0;
@@ -46,35 +58,60 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __re
   }
 }
 
-__global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __restrict__ ids, int T,
-                                                           int k, int E,
-                                                           const int32_t* __restrict__ counts,
-                                                           const int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ perm,
-                                                           int32_t* __restrict__ inv) {
+constexpr int kRankWaves = 8;
+constexpr int kRankLoads = 64;  // loads of 64 entries per wave and round (one bit each per lane)
+
+__global__ __launch_bounds__(64 * kRankWaves) void permute_rank_kernel(
+    const int32_t* __restrict__ ids, long long n, int E, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ int s_n[kRankWaves];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + wave;
-  if (e >= E) return;
+  const int e = blockIdx.x;
   const int cnt = counts[e];
-  if (cnt == 0) return;
-  int pos = offsets[e];
-  const int end = pos + cnt;
-  for (int t0 = 0; t0 < T && pos < end; t0 += 64) {
-    const int t = t0 + lane;
-    int jf = -1;
-    if (t < T) {
-      const int32_t* row = ids + (size_t)t * k;
-      for (int j = 0; j < k; ++j)
-        if (row[j] == e) jf = j;
+  if (cnt == 0) return;  // the same for the whole workgroup
+  int base = offsets[e];
+  const int end = base + cnt;
+  constexpr long long kRound = (long long)kRankWaves * kRankLoads * 64;
+  for (long long r0 = 0; r0 < n; r0 += kRound) {
+    const int32_t* blk = ids + r0;
+    const int rem = (int)(n - r0 < kRound ? n - r0 : kRound);  // entries of this round
+    const int l0 = wave * kRankLoads * 64 + lane;
+    uint64_t mine = 0;  // bit i: entry r0 + l0 + 64 i is this expert
+    for (int i0 = 0; i0 < kRankLoads; i0 += 16) {
+      int v[16];  // 16 loads in flight (entries past the round's end read its last entry)
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int l = l0 + 64 * (i0 + u);
+        v[u] = blk[l < rem ? l : rem - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        mine |= (uint64_t)(l0 + 64 * (i0 + u) < rem && v[u] == e) << (i0 + u);
     }
-    const uint64_t m = __ballot(jf >= 0);
-    if (jf >= 0) {
-      const int p = pos + popc_below(m);
-      const int f = t * k + jf;
-      perm[p] = f;
-      inv[f] = p;
+    const int cw = wave_sum_int(__popcll(mine));
+    if (lane == 0) s_n[wave] = cw;
+    __syncthreads();
+    int pos = base, total = 0;
+#pragma unroll
+    for (int v = 0; v < kRankWaves; ++v) {
+      const int c = s_n[v];
+      pos += v < wave ? c : 0;
+      total += c;
     }
-    pos += __popcll(m);
+    for (int i = 0; i < kRankLoads; ++i) {
+      const bool hit = (mine >> i) & 1;
+      const uint64_t m = __ballot(hit);
+      if (hit) {
+        const int p = pos + popc_below(m);
+        const long long f = r0 + l0 + 64 * i;
+        perm[p] = (int32_t)f;
+        inv[f] = p;
+      }
+      pos += __popcll(m);
+    }
+    base += total;
+    if (base >= end) break;  // every row of the expert is placed (the same for all waves)
+    __syncthreads();         // s_n is rewritten by the next round
   }
 }
 
@@ -90,7 +127,7 @@ extern "C" int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t
   hipLaunchKernelGGL(permute_count_kernel, dim3(1), dim3(1024), 0, stream, topk_ids, T * k, E,
                      counts, offsets, distinct, n_distinct);
   if (T > 0)
-    hipLaunchKernelGGL(permute_rank_kernel, dim3((E + 3) / 4), dim3(256), 0, stream, topk_ids, T,
-                       k, E, counts, offsets, perm, inv);
+    hipLaunchKernelGGL(permute_rank_kernel, dim3(E), dim3(64 * kRankWaves), 0, stream, topk_ids,
+                       (long long)T * k, E, counts, offsets, perm, inv);
   return moe_launch_status();
 }

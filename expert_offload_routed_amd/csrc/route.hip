@@ -10,8 +10,11 @@
 // Kernels:
 //   route_logits_mfma_kernel: bf16 tokens, many tokens and experts: the
 //     logits as a dense contraction on v_mfma_f32_32x32x16_bf16, one
-//     workgroup per 32 tokens x 32 experts, its 8 waves splitting H; the 8
-//     partial tiles meet in LDS, summed in wave order.
+//     workgroup per 64 tokens x 64 experts. Each K step of 64 values copies
+//     the tile's 64 token rows and 64 router rows (128 bytes each) into LDS
+//     with asynchronous global -> LDS copies, 8 whole rows per instruction, in
+//     a ring of 8 stages; wave w computes the 32 x 32 block w % 4 over half of
+//     every step's K, and the two halves meet in LDS in a fixed order.
 //   route_logits_kernel: one workgroup per (expert, tile of 8 tokens); its
 //     256 threads split H into 8-element vectors (16-byte bf16 / 2x16-byte
 //     fp32 loads), fp32 FMA, then a wave and a cross-wave reduction. A decode
@@ -102,47 +105,97 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
 // MFMA operand lanes (checked on gfx950): lane l holds row l % 32 and the 8
 // K values 8 (l / 32) .. +7 of each 16-wide K step; accumulator r holds row
 // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
-constexpr int kLgSplit = 8;  // waves per workgroup, each a contiguous H slice
-constexpr int kLgU = 8;      // K steps of loads in flight per wave
-__global__ __launch_bounds__(64 * kLgSplit) void route_logits_mfma_kernel(
+constexpr int kLgRows = 64;    // tokens and experts of a tile
+constexpr int kLgK = 64;       // K values of a stage (128 bytes a row)
+constexpr int kLgStages = 8;  // 7 stages of copies in flight: the loop is bound by their latency
+constexpr int kLgStageBytes = 2 * kLgRows * kLgK * 2;  // token rows, then router rows
+
+// Asynchronous global -> LDS copy, 16 bytes per lane to lds + 16 lane (lds is
+// the same for every lane of the wave), issued from inline assembly so that
+// the compiler does not wait for every copy in flight before each LDS read it
+// cannot prove disjoint from them. The kernel orders the copies with explicit
+// waits on the vector-memory counter and barriers, and waits for all of them
+// before it ends. m0 is listed as clobbered; the kernel holds no other m0 value.
+__device__ __forceinline__ void lg_copy16(const void* g, void* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(l), "v"(g) : "memory", "m0");
+}
+
+template <int N_>
+__device__ __forceinline__ void lg_vm_wait() {
+  // s_waitcnt with only the vector-memory counter limited (N_ < 64)
+  __builtin_amdgcn_s_waitcnt((N_ & 15) | ((N_ >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__global__ __launch_bounds__(512) void route_logits_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const float* __restrict__ bias, int T, int H, int E, float* __restrict__ logits) {
-  __shared__ float red[kLgSplit][32 * 33];
+  __shared__ __attribute__((aligned(1024))) char smem[kLgStages * kLgStageBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
-  const int klen = H / kLgSplit;
-  const int kbeg = wave * klen + 8 * (lane >> 5);
-  const int ta = min(t0 + (lane & 31), T - 1), eb = min(e0 + (lane & 31), E - 1);
-  const uint16_t* pa = x + (size_t)ta * H + kbeg;
-  const uint16_t* pb = w + (size_t)eb * H + kbeg;
+  const int t0 = blockIdx.x * kLgRows, e0 = blockIdx.y * kLgRows;
+  // copies: wave w takes rows 8 w .. 8 w + 7 of both operands, 8 lanes a row; row r's
+  // 16-byte chunk c sits at position c ^ ((r / 2) % 8) of the row's 128 bytes, so the
+  // operand reads of 16 consecutive lanes (16 consecutive rows, one chunk) cover all 16
+  // groups of 16 bytes that the 64 LDS banks serve at once. Rows past the end read the
+  // last row; their results are not stored.
+  const int cr = 8 * wave + (lane >> 3);
+  const int cc = (lane & 7) ^ ((cr >> 1) & 7);
+  const uint16_t* a_src = x + (size_t)min(t0 + cr, T - 1) * H + 8 * cc;
+  const uint16_t* b_src = w + (size_t)min(e0 + cr, E - 1) * H + 8 * cc;
+  // compute: block (tm, te) of 32 tokens x 32 experts, K steps 2 kh and 2 kh + 1 of the 4
+  const int tm = wave & 1, te = (wave >> 1) & 1, kh = wave >> 2;
+  int roff[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int r = lane & 31, c = 2 * (2 * kh + s) + (lane >> 5);
+    roff[s] = r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+  }
+  auto issue = [&](int kt, int buf) {
+    char* st = smem + buf * kLgStageBytes;
+    lg_copy16(a_src + kt * kLgK, st + wave * 1024);
+    lg_copy16(b_src + kt * kLgK, st + kLgRows * 128 + wave * 1024);
+  };
   floatx16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  for (int kk = 0; kk < klen; kk += 16 * kLgU) {
-    u32x4 av[kLgU], bv[kLgU];
+  const int nk = H / kLgK;
 #pragma unroll
-    for (int u = 0; u < kLgU; ++u) {
-      if (kk + u * 16 < klen) {
-        av[u] = ld16(pa + kk + u * 16);
-        bv[u] = ld16(pb + kk + u * 16);
-      }
-    }
+  for (int s = 0; s < kLgStages - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt % kLgStages;
+    // copies issued after step kt: kLgStages - 2 stages of 2 until the last stages, then
+    // wait for all
+    if (kt + kLgStages - 2 < nk) lg_vm_wait<2 * (kLgStages - 2)>(); else lg_vm_wait<0>();
+    __builtin_amdgcn_s_barrier();  // stage kt is in LDS; every wave is past step kt - 1
+    if (kt + kLgStages - 1 < nk) issue(kt + kLgStages - 1, (kt + kLgStages - 1) % kLgStages);
+    const char* A = smem + buf * kLgStageBytes + tm * 32 * 128;
+    const char* Bm = smem + buf * kLgStageBytes + kLgRows * 128 + te * 32 * 128;
 #pragma unroll
-    for (int u = 0; u < kLgU; ++u) {
-      if (kk + u * 16 < klen)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&av[u]),
-                                                      *reinterpret_cast<const bf16x8*>(&bv[u]), acc, 0, 0, 0);
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + roff[s]);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bm + roff[s]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
     }
   }
+  __syncthreads();  // every wave is done with the ring: its memory holds the upper K halves
+  float* red = reinterpret_cast<float*>(smem) + (wave & 3) * (32 * 33);
+  if (kh == 1) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[wave][(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * 33 + (lane & 31)] = acc[r];
+    for (int r = 0; r < 16; ++r) red[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * 33 + (lane & 31)] = acc[r];
+  }
   __syncthreads();
-  for (int o = tid; o < 1024; o += 64 * kLgSplit) {
-    const int i = o >> 5, j = o & 31;
-    float sum = 0.f;
+  if (kh == 0) {
+    const int e = e0 + te * 32 + (lane & 31);
+    const float be = (bias && e < E) ? bias[e] : 0.f;
 #pragma unroll
-    for (int v = 0; v < kLgSplit; ++v) sum += red[v][i * 33 + j];
-    if (t0 + i < T && e0 + j < E) logits[(size_t)(t0 + i) * E + e0 + j] = sum + (bias ? bias[e0 + j] : 0.f);
+    for (int r = 0; r < 16; ++r) {
+      const int i = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int t = t0 + tm * 32 + i;
+      const float v = acc[r] + red[i * 33 + (lane & 31)];
+      if (t < T && e < E) logits[(size_t)t * E + e] = v + be;
+    }
   }
 }
 
@@ -591,9 +644,9 @@ extern "C" int moe_route(const void* x, int x_dtype, const void* w_router, const
 
   dim3 g1(E, (T + kRouteTT - 1) / kRouteTT);
   if (g1.y > 65535u) return MOE_EUNSUPPORTED;
-  if (x_dtype == MOE_BF16 && T >= 64 && E >= 32 && H % (16 * kLgSplit) == 0)
-    hipLaunchKernelGGL(route_logits_mfma_kernel, dim3((T + 31) / 32, (E + 31) / 32),
-                       dim3(64 * kLgSplit), 0, stream, static_cast<const uint16_t*>(x),
+  if (x_dtype == MOE_BF16 && T >= 64 && E >= 32 && H % kLgK == 0)
+    hipLaunchKernelGGL(route_logits_mfma_kernel, dim3((T + kLgRows - 1) / kLgRows, (E + kLgRows - 1) / kLgRows),
+                       dim3(512), 0, stream, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(w_router), bias, T, H, E, logits);
   else if (x_dtype == MOE_BF16)
     hipLaunchKernelGGL(route_logits_kernel<MOE_BF16>, g1, dim3(256), 0, stream, x, w_router, bias,

@@ -31,6 +31,8 @@ ROUTE_CASES = [
     (W.reduced(MIX, E=8, k=2, H=4096), 37),
     (W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), H=2048), 300),
     (W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), H=7168), 64),
+    (W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), H=7168), 4096),  # prefill size
+    (W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), E=96, k=6, H=1024), 1000),  # ragged tiles
     (W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), E=1000, k=16, H=512), 9),
     (W.reduced(TINY, E=5, k=5, H=24), 3),
 ]
@@ -111,7 +113,9 @@ def test_route_permute_fused(shape, T):
 
 # -------------------------------------------------------------- permutation --
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (16, 8, 2), (513, 64, 6), (4096, 256, 8),
-                                   (77, 1024, 16), (3, 1, 1)])
+                                   (77, 1024, 16), (3, 1, 1),
+                                   (9001, 64, 6),    # 54006 picks: two rounds of the rank kernel
+                                   (20000, 8, 2)])   # 40000 picks, one expert in almost every row
 def test_permute_stage(T, E, k):
     say(f"permute T={T} E={E} k={k}")
     g = torch.Generator().manual_seed(T * 7 + E)
