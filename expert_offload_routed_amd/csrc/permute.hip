@@ -76,8 +76,11 @@ __global__ __launch_bounds__(64 * kRankWaves) void permute_rank_kernel(
     const int32_t* blk = ids + r0;
     const int rem = (int)(n - r0 < kRound ? n - r0 : kRound);  // entries of this round
     const int l0 = wave * kRankLoads * 64 + lane;
+    // loads of this wave that reach entries of the round (the same for all its lanes)
+    const int first = wave * kRankLoads * 64;
+    const int nl = rem <= first ? 0 : min(kRankLoads, (rem - first + 63) / 64);
     uint64_t mine = 0;  // bit i: entry r0 + l0 + 64 i is this expert
-    for (int i0 = 0; i0 < kRankLoads; i0 += 16) {
+    for (int i0 = 0; i0 < nl; i0 += 16) {
       int v[16];  // 16 loads in flight (entries past the round's end read its last entry)
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(64 * kRankWaves) void permute_rank_kernel(
       pos += v < wave ? c : 0;
       total += c;
     }
-    for (int i = 0; i < kRankLoads; ++i) {
+    for (int i = 0; i < nl; ++i) {
       const bool hit = (mine >> i) & 1;
       const uint64_t m = __ballot(hit);
       if (hit) {

@@ -33,6 +33,8 @@ ROUTE_CASES = [
     (W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), H=7168), 64),
     (W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), H=7168), 4096),  # prefill size
     (W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), E=96, k=6, H=1024), 1000),  # ragged tiles
+    (W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), E=40, k=4, H=520), 100),  # H not a multiple
+                                                                                      # of 64: FMA logits
     (W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), E=1000, k=16, H=512), 9),
     (W.reduced(TINY, E=5, k=5, H=24), 3),
 ]
