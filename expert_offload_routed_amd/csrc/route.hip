@@ -630,18 +630,32 @@ __global__ __launch_bounds__(1024) void route_front_single_kernel(
   for (int i = tid; i < T * E; i += 1024) logits[i] = s_lg[i];
 }
 
-}  // namespace
+// Second half of the front end after a separate logits launch, for the token and
+// expert counts the one-launch front end does not take (more than kFrontMaxT
+// tokens or more than kFrontMaxE experts) while T <= kSelectMaxT and T*k <=
+// kSelectMaxN: one workgroup of 1024 threads selects (one wave per token, all
+// tokens at once), sorts and plans,
+// replacing the top-k, count, rank and plan launches (each a few microseconds
+// from a cold instruction cache at decode sizes). Its rank step compares each
+// assignment with every earlier one, so the bound stays small.
+constexpr int kSelectMaxT = 16;  // the workgroup's waves
+constexpr int kSelectMaxN = 256;
 
-extern "C" int moe_route(const void* x, int x_dtype, const void* w_router, const float* bias,
-                         int T, int H, int E, int k, int renorm, float* logits,
-                         int32_t* topk_ids, float* topk_w, hipStream_t stream) {
-  MOE_CHECK_ARG(T >= 0 && H > 0 && H % 8 == 0);
-  MOE_CHECK_ARG(k >= 1 && k <= E && E <= 64 * kTopkMaxV);
-  MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
-  if (T == 0) return MOE_OK;
-  MOE_CHECK_ARG(x && w_router && logits && topk_ids && topk_w);
-  MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)w_router % 16) == 0);
+template <int NV>
+__global__ __launch_bounds__(1024) void select_sort_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ distinct,
+    int32_t* __restrict__ n_distinct, FrontPlan pl) {
+  __shared__ FrontLds L;
+  __shared__ int s_dist[1024];
+  front_select_and_sort<NV>(logits, T, E, k, renorm, ids, weights, counts, offsets, perm, inv,
+                            distinct, n_distinct, L, s_dist, pl);
+}
 
+// Router logits of T > 0 tokens (arguments checked by the caller).
+int launch_logits(const void* x, int x_dtype, const void* w_router, const float* bias, int T,
+                  int H, int E, float* logits, hipStream_t stream) {
   dim3 g1(E, (T + kRouteTT - 1) / kRouteTT);
   if (g1.y > 65535u) return MOE_EUNSUPPORTED;
   if (x_dtype == MOE_BF16 && T >= 64 && E >= 32 && H % kLgK == 0)
@@ -654,6 +668,23 @@ extern "C" int moe_route(const void* x, int x_dtype, const void* w_router, const
   else
     hipLaunchKernelGGL(route_logits_kernel<MOE_F32>, g1, dim3(256), 0, stream, x, w_router, bias,
                        T, H, E, logits);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_route(const void* x, int x_dtype, const void* w_router, const float* bias,
+                         int T, int H, int E, int k, int renorm, float* logits,
+                         int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && H > 0 && H % 8 == 0);
+  MOE_CHECK_ARG(k >= 1 && k <= E && E <= 64 * kTopkMaxV);
+  MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(x && w_router && logits && topk_ids && topk_w);
+  MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)w_router % 16) == 0);
+
+  int rc = launch_logits(x, x_dtype, w_router, bias, T, H, E, logits, stream);
+  if (rc != MOE_OK) return rc;
 #define MOE_TOPK(NV_)                                                                      \
   hipLaunchKernelGGL(topk_softmax_kernel<NV_>, dim3((T + 3) / 4), dim3(256), 0, stream, logits, \
                      T, E, k, renorm, topk_ids, topk_w)
@@ -687,7 +718,8 @@ int route_permute_plan(const void* x, int x_dtype, const void* w_router, const f
   MOE_CHECK_ARG(k >= 1 && k <= E && E <= 64 * kTopkMaxV);
   MOE_CHECK_ARG(x_dtype == MOE_F32 || x_dtype == MOE_BF16);
   MOE_CHECK_ARG(counts && offsets && distinct && n_distinct && sync_counter);
-  if (T > kFrontMaxT || E > kFrontMaxE || T * k > 1024 || T == 0) {
+  const bool front = T <= kFrontMaxT && E <= kFrontMaxE && T * k <= 1024;
+  if (T == 0 || (!front && (T > kSelectMaxT || T * k > kSelectMaxN || E > 64 * kTopkMaxV))) {
     int rc = moe_route(x, x_dtype, w_router, bias, T, H, E, k, renorm, logits, topk_ids, topk_w,
                        stream);
     if (rc != MOE_OK) return rc;
@@ -706,6 +738,23 @@ int route_permute_plan(const void* x, int x_dtype, const void* w_router, const f
       pl.lut = nullptr;
     }
     if (pl.scores && scored) *scored = true;
+  }
+  if (!front) {  // logits, then one workgroup selects, sorts and plans
+    if (T > kFrontMaxT) {  // its LDS holds the softmax normalisers of kFrontMaxT tokens
+      pl.scores = nullptr;
+      if (scored) *scored = false;
+    }
+    int rc = launch_logits(x, x_dtype, w_router, bias, T, H, E, logits, stream);
+    if (rc != MOE_OK) return rc;
+#define MOE_SELECT(NV_)                                                                          \
+  hipLaunchKernelGGL(select_sort_kernel<NV_>, dim3(1), dim3(1024), 0, stream, logits, T, E, k, renorm, \
+                     topk_ids, topk_w, counts, offsets, perm, inv, distinct, n_distinct, pl)
+    if (E <= 64) MOE_SELECT(1);
+    else if (E <= 128) MOE_SELECT(2);
+    else if (E <= 256) MOE_SELECT(4);
+    else MOE_SELECT(kTopkMaxV);
+#undef MOE_SELECT
+    return moe_launch_status();
   }
   // code specialised to the token count and logits per lane: the front end runs once per step,
   // from a cold instruction cache, so it should hold only the code the step needs
