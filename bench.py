@@ -125,12 +125,16 @@ def timed(layer, shape, T, steps, warmup, label, ffn_timing=False):
     return res
 
 
-def recorded_traffic(key):
+def recorded_traffic(*keys):
     """HBM bytes per FFN call (FETCH_SIZE + WRITE_SIZE runs, calibrated), as recorded in
-    profiles/ffn_traffic.json; None when absent or when an FFN kernel source changed since."""
+    profiles/ffn_traffic.json under the first of keys present; None when absent or when an
+    FFN kernel source changed since."""
     try:
-        rec = json.load(open(os.path.join(ROOT, "profiles", "ffn_traffic.json")))[key]
-    except (OSError, KeyError, ValueError):
+        recs = json.load(open(os.path.join(ROOT, "profiles", "ffn_traffic.json")))
+    except (OSError, ValueError):
+        return None
+    rec = next((recs[k] for k in keys if k in recs), None)
+    if rec is None:
         return None
     return rec["read_bytes"] + rec["write_bytes"] if ffn_sources_sha1() == rec["csrc_sha1"] else None
 
@@ -485,7 +489,8 @@ def main():
                                "layer step)",
                      "bound": "hbm", "achieved": round(ffn["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ffn["gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(f"{args.workload}/decode{head_T}"),
+                     "traffic": recorded_traffic(f"{args.workload}/decode{head_T}",
+                                                 f"{args.workload}/T{head_T}"),
                      "avg_us": round(ffn["avg_us"], 2), "bytes_per_call": int(ffn["bytes_per_call"])},
         "also": also,
     }
