@@ -289,15 +289,24 @@ class SlotPool:
     [SeqMoE] Mechanism: one pool of slots shared by every MoE layer; a lookup
     table rewrites expert ids to slot ids, so the expert computation reads an
     expert's weights through its slot. Here a slot holds a reference to the
-    weights last copied into it.
+    weights last copied into it, and ``owner`` the (layer, expert) whose table
+    entry points at it.
     """
 
     def __init__(self, num_slots: int, layers: int, E: int):
         self.content: list[dict | None] = [None] * num_slots
+        self.owner: list[tuple[int, int] | None] = [None] * num_slots
         self.lut = np.full((layers, E), -1, dtype=np.int32)
 
-    def fill(self, slot: int, weights: dict) -> None:
+    def commit(self, slot: int, layer: int, expert: int, weights: dict) -> None:
+        """Copy an expert into a slot and point its table entry there; the
+        slot's previous owner loses its entry (it is no longer resident)."""
+        old = self.owner[slot]
+        if old is not None:
+            self.lut[old] = -1
         self.content[slot] = weights
+        self.owner[slot] = (layer, expert)
+        self.lut[layer, expert] = slot
 
     def weights_of(self, layer: int, expert: int) -> dict:
         slot = int(self.lut[layer, expert])
@@ -606,31 +615,40 @@ def moe_layer(x, w_router, bias, k: int, *, layer: int, pool: SlotPool,
               shared: list[dict] | None = None, renorm: bool = True) -> dict:
     """One routed-expert layer over the slot pool.
 
-    route -> permute -> residency plan (fills copy the expert's weights into
-    its slot) -> each routed (t, j) runs expert ids[t, j] with the weights
-    read through pool.lut -> weighted combine (+ shared experts, weight 1).
+    route -> permute -> residency plan -> for each wave of the plan: the
+    wave's fills copy the expert's weights into their slots (the slot's
+    previous expert leaves the table), then each (t, j) routed to an expert
+    the wave computes runs with the weights read through pool.lut as it stands
+    after those fills -> weighted combine (+ shared experts, weight 1).
+    A later wave may overwrite a slot an earlier wave read; the earlier
+    experts are already computed ([SeqMoE] Mechanism: the expert kernel reads
+    experts through the slot table; misses are copied in before use).
+    Without a planner every routed expert must already be resident.
     ``weights_of_expert(e)`` returns the host-store weights of expert e of
     this layer (what a fill copies).
     """
     r = route(x, w_router, bias, k, renorm)
     ids = r["ids"]
     p = permute(ids, w_router.shape[0])
-    waves = []
     if planner is not None:
         waves = planner.plan(layer, p["distinct"])
-        for wave in waves:
-            for e, s in wave.fills:
-                pool.fill(s, weights_of_expert(e))
-        pool.lut[layer] = planner.lut[layer]
+    else:
+        waves = [Wave(compute=[int(e) for e in p["distinct"]])]
     x_rows = as_f32(x)  # exact for fp32 and bf16 tokens; each expert form converts further
     T = ids.shape[0]
     H = as_f64(w_router).shape[1]
     y = np.zeros((T, k, H), dtype=np.float64)
-    for e in p["distinct"]:
-        e = int(e)
-        f = p["perm"][p["offsets"][e]:p["offsets"][e + 1]]
-        t_rows, j_rows = f // k, f % k
-        y[t_rows, j_rows] = expert_forward(x_rows[t_rows], pool.weights_of(layer, e))
+    for wave in waves:
+        for e, s in wave.fills:
+            pool.commit(s, layer, e, weights_of_expert(e))
+        for e in wave.compute:
+            e = int(e)
+            f = p["perm"][p["offsets"][e]:p["offsets"][e + 1]]
+            t_rows, j_rows = f // k, f % k
+            y[t_rows, j_rows] = expert_forward(x_rows[t_rows], pool.weights_of(layer, e))
+    if planner is not None and not np.array_equal(pool.lut, planner.lut):
+        raise AssertionError("pool table differs from the planner's after the last wave")
     y_sh = [expert_forward(x_rows, w) for w in (shared or [])]
     out = combine(y, r["weights"], y_sh)
-    return dict(route=r, perm=p, waves=waves, y=y, y_shared=y_sh, out=out)
+    return dict(route=r, perm=p, waves=waves if planner is not None else [], y=y,
+                y_shared=y_sh, out=out)

@@ -209,6 +209,55 @@ def test_w4a8_expert_close_to_dense_on_dequantised_weights():
     assert 0 < rel < 0.03  # only the two int8 activation roundings differ
 
 
+def test_int8_rows_half_steps_round_to_even():
+    # absmax 254 gives s = 2 exactly; 5/2, 3/2, -5/2, 1/2, -3/2 sit on half steps
+    a = np.array([[254.0, 5.0, 3.0, -5.0, 1.0, -3.0, 7.0, 0.0]], np.float32)
+    q, s = O.quantize_rows_int8(a)
+    assert s.tolist() == [2.0]
+    assert q.tolist() == [[127, 2, 2, -2, 0, -2, 4, 0]]
+
+
+def _nibbles(codes) -> np.ndarray:
+    """Signed codes [rows, K] -> packed bytes [rows, K/2], even K in the low nibble."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_w4a8_expert_exposes_requantised_h_by_hand():
+    # One group (H = F = 128). Gate and up read only input 1; down is the identity,
+    # so y = h_hat, the int8 requantisation of h = SiLU(g) * u, can be read off.
+    # Token row 0: x = [127, 64, 0...] -> s_x = 1, x_hat[1] = 64, g = 64 (SiLU(64) = 64
+    # exactly in float64), u[n] = 64 * d_n * s_n, so h[n] = 4096 * d_n * s_n.
+    # Row 1 is row 0 doubled: s_x = 2, g = 128, h = 4 * h_row0, s_h = 4.
+    H = F = 128
+    d = np.zeros(F, np.int64)
+    su = np.full(F, 2.0 ** -13)
+    for n, (dn, sn) in enumerate([(1, 127 * 2.0 ** -12), (5, 2.0 ** -13), (7, 2.0 ** -13),
+                                  (-5, 2.0 ** -13), (1, 253 * 2.0 ** -13), (1, 2.0 ** -13),
+                                  (3, 2.0 ** -13), (-3, 2.0 ** -13), (-8, 2.0 ** -12),
+                                  (7, 2.0 ** -14)]):
+        d[n], su[n] = dn, sn
+    # h row 0:  127, 2.5, 3.5, -2.5, 126.5, 0.5, 1.5, -1.5, -8, 1.75, 0, ...
+    # absmax 127 -> s_h = 1; rint to even: 127, 2, 4, -2, 126, 0, 2, -2, -8, 2, 0, ...
+    gate_codes = np.zeros((F, H), np.int64)
+    gate_codes[:, 1] = 1
+    up_codes = np.zeros((F, H), np.int64)
+    up_codes[:, 1] = d
+    down_codes = np.eye(H, F, dtype=np.int64)
+    w = {"gate_q": _nibbles(gate_codes), "gate_s": torch.ones(F, 1, dtype=torch.bfloat16),
+         "up_q": _nibbles(up_codes), "up_s": torch.tensor(su[:, None], dtype=torch.bfloat16),
+         "down_q": _nibbles(down_codes), "down_s": torch.ones(H, 1, dtype=torch.bfloat16)}
+    assert torch.tensor(su, dtype=torch.bfloat16).double().numpy().tolist() == su.tolist()
+    x = np.zeros((2, H), np.float32)
+    x[0, :2] = [127.0, 64.0]
+    x[1, :2] = [254.0, 128.0]
+    y = O.swiglu_expert_w4a8(x, w)
+    want = np.zeros(H)
+    want[:10] = [127, 2, 4, -2, 126, 0, 2, -2, -8, 2]
+    assert y[0].tolist() == want.tolist()
+    assert y[1].tolist() == (4 * want).tolist()
+
+
 # ---------------------------------------------------------------- combine ---
 def test_combine_linearity_and_zero_weight_poison():
     rng = np.random.default_rng(10)
@@ -233,8 +282,7 @@ def _tiny_layer(lut_perm, E=8, k=2, H=64, F=96, T=12):
     experts = [W.expert_weights(sh, e) for e in range(E)]
     pool = O.SlotPool(E, 1, E)
     for e in range(E):
-        pool.fill(lut_perm[e], experts[e])
-        pool.lut[0, e] = lut_perm[e]
+        pool.commit(lut_perm[e], 0, e, experts[e])
     return O.moe_layer(x, wr, b, k, layer=0, pool=pool, planner=None,
                        weights_of_expert=lambda e: experts[e]), experts, x, wr, b
 
@@ -262,6 +310,74 @@ def test_layer_weighted_sum_by_hand():
             e = experts[ids[t, j]]
             acc = acc + w[t, j] * O.swiglu_expert(x[t:t + 1].numpy(), e["gate"], e["up"], e["down"])[0]
         np.testing.assert_allclose(res["out"][t], acc, rtol=1e-13, atol=1e-15)
+
+
+def _hand_expert(seed, H, F):
+    g = np.random.default_rng(seed)
+    return {"gate": g.normal(size=(F, H)) * 0.3, "up": g.normal(size=(F, H)) * 0.3,
+            "down": g.normal(size=(H, F)) * 0.3}
+
+
+def _dense_token(x_t, w):
+    xt = torch.tensor(np.asarray(x_t, np.float64))
+    t = {n: torch.tensor(v) for n, v in w.items()}
+    return Fnn.linear(Fnn.silu(Fnn.linear(xt, t["gate"])) * Fnn.linear(xt, t["up"]), t["down"]).numpy()
+
+
+def test_layer_two_waves_by_hand():
+    # 2 slots, 4 experts. Slot 0 holds expert 0, slot 1 expert 3. Router = identity, so
+    # token 0 = [3, 2, 0, 0] routes to (0, 1) and token 1 = [1, 0, 4, 0] to (2, 0).
+    # U = {0, 1, 2}: hit 0 (slot 0), misses 1, 2; one victim (slot 1) -> wave 1 computes
+    # 0 and 1 (1 filled into slot 1), wave 2 computes 2, filled into slot 0, which held
+    # expert 0 in wave 1.
+    H, F, E, k = 4, 3, 4, 2
+    experts = [_hand_expert(40 + e, H, F) for e in range(E)]
+    x = np.array([[3.0, 2.0, 0.0, 0.0], [1.0, 0.0, 4.0, 0.0]], np.float32)
+    wr = np.eye(E, H, dtype=np.float32)
+    pool = O.SlotPool(2, 1, E)
+    pool.commit(0, 0, 0, experts[0])
+    pool.commit(1, 0, 3, experts[3])
+    planner = O.LruSlotPlanner(2, 1, E, residency=[(0, 0), (0, 3)])
+    res = O.moe_layer(x, wr, None, k, layer=0, pool=pool, planner=planner,
+                      weights_of_expert=lambda e: experts[e])
+    assert res["route"]["ids"].tolist() == [[0, 1], [2, 0]]
+    assert [(wv.compute, wv.fills) for wv in res["waves"]] == [([0, 1], [(1, 1)]), ([2], [(2, 0)])]
+    assert pool.lut[0].tolist() == [-1, 1, 0, -1]
+    assert pool.owner == [(0, 2), (0, 1)]
+    wts = res["route"]["weights"]
+    for t in range(2):
+        want = sum(wts[t, j] * _dense_token(x[t], experts[res["route"]["ids"][t, j]]) for j in range(k))
+        np.testing.assert_allclose(res["out"][t], want, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("S,T,resident", [(3, 40, 2), (1, 9, 0), (4, 25, 4)])
+def test_layer_more_routed_than_slots_equals_direct_indexing(S, T, resident):
+    sh = W.reduced(W.shape_of("tiny_e8k2_h256_f512_fp32"), H=64, F=96, zipf_s=None)
+    x = W.tokens(sh, T)
+    wr, b = W.router(sh)
+    experts = [W.expert_weights(sh, e) for e in range(sh.E)]
+    pool = O.SlotPool(S, 1, sh.E)
+    own = [(0, e) for e in (5, 1, 6, 2)[:resident]] + [None] * (S - resident)
+    for s, o in enumerate(own):
+        if o is not None:
+            pool.commit(s, 0, o[1], experts[o[1]])
+    planner = O.LruSlotPlanner(S, 1, sh.E, residency=own)
+    res = O.moe_layer(x, wr, b, sh.k, layer=0, pool=pool, planner=planner,
+                      weights_of_expert=lambda e: experts[e])
+    U = res["perm"]["distinct"]
+    assert len(U) > S and len(res["waves"]) >= 2
+    ids, wts = res["route"]["ids"], res["route"]["weights"]
+    xs = O.as_f64(x)
+    for t in range(T):
+        want = sum(wts[t, j] * _dense_token(xs[t], {n: O.as_f64(v) for n, v in experts[ids[t, j]].items()})
+                   for j in range(sh.k))
+        np.testing.assert_allclose(res["out"][t], want, rtol=1e-11, atol=1e-13)
+    # the table after the last wave is what the pool holds: every resident entry points
+    # at a slot whose contents are that expert
+    for e in range(sh.E):
+        s = pool.lut[0, e]
+        if s >= 0:
+            assert pool.content[s] is experts[e]
 
 
 # ------------------------------------------------------- LRU slot planner ---
