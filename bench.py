@@ -5,25 +5,29 @@ residency plan, expert FFN over resident slots with fills of the misses,
 shared experts, combine) over one batch of synthetic tokens already in HBM;
 for the 48-layer stack a step runs every layer once.
 
-Default workload: one Mixtral-8x7B-shaped MoE layer in bf16 (8 experts, top-2
-renormalised, hidden 4096, expert FFN 14336 SwiGLU), x ~ N(0, 1), weights ~
-N(0, 0.02).
+Default workload: the largest layer that fits one GPU, DeepSeek-V3-shaped with
+int4 weights (256 routed experts, top-8, one shared expert, hidden 7168, expert
+FFN 2048 SwiGLU, symmetric int4 codes with one bf16 scale per 128 inputs) and
+int8 per-token activations.
 
-  value     decode, 1 token per step, every routed expert resident (8 slots,
-            random expert->slot relabelling): the hit path, tokens/s.
-  also      decode 8 tokens and prefill 512 tokens on the same pool; and the
-            workload's own cache (4 of 8 experts resident, random table) where
-            misses are copied from pinned host memory (PCIe-inclusive rate,
-            reported separately, never the headline value).
-  roofline  the expert FFN stage (one moe_expert_ffn call: group plan + W13
-            pass + W2 pass): algorithmic bytes (weights of the distinct routed
-            experts + tokens in + rows out) per call divided by its HIP-event
-            duration on the compute stream.
-  cpu_baseline  the oracle (float64 NumPy) on a bounded sample of decode steps.
+  value     decode, 1 token per step, every routed expert of the step resident
+            (the hit path), tokens/s. The step's weights (about 205 MB) fit the
+            256 MB MALL, so the timed steps rotate over replicas of the slot pool
+            and no step finds its weights left in the MALL by the previous one.
+  also      the same workload at 32 and 4096 tokens (prefill: MFMA share of the
+            int8 peak next to the HBM one), its own cache of 84 slots with misses
+            copied from pinned host memory (PCIe-inclusive rate, reported apart,
+            never the headline value), and the other four workloads' hit paths
+            and caches.
+  roofline  the expert FFN stage (one moe_expert_ffn call: group plan + gate/up
+            pass + down pass): algorithmic bytes (weights of the distinct routed
+            experts and the shared one + tokens in + rows out) per call divided
+            by its HIP-event duration on the compute stream.
+  cpu_baseline  the oracle (float64 NumPy) on a bounded sample of the headline's
+            decode steps, on every core the process may use.
 
 Other workloads (--workload NAME) print a line of the same form for that
-workload: its hit path at each of its token counts, its own cache with fills,
-and for prefill the MFMA share (flops / time / dense peak) next to the HBM one.
+workload. --case runs one case without a JSON line (profiling).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workload NAME] [--quick] [--case CASE]
@@ -49,7 +53,7 @@ from expert_offload_routed_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "int4g128": 5000.0, "f32": 157.3}  # dense; int8 ops for int4 weights
-DEFAULT = "mixtral_e8k2_h4096_f14336_bf16"
+DEFAULT = "dsv3_e256k8s1_h7168_f2048_int4"
 METRIC = "MoE-layer tokens/s at 1 GPU + achieved HBM GB/s (decode) / MFMA % (prefill)"
 
 
@@ -64,23 +68,32 @@ def _xbytes(shape) -> int:
     return 4 if shape.xfmt == "f32" else 2
 
 
-def _run(layer, batches, out, timing):
-    """batches: list of steps, each a list of (layer index, x)."""
-    layer.ctx.set_timing(timing)
-    c0 = layer.counters()
+def _run(layers, batches, out, timing):
+    """batches: list of steps, each a list of (layer index, x); step i runs on
+    layers[i % len(layers)] (replicas of one slot pool, see timed)."""
+    for lay in layers:
+        lay.ctx.set_timing(timing)
+    c0 = [lay.counters() for lay in layers]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for step in batches:
+    for i, step in enumerate(batches):
+        lay = layers[i % len(layers)]
         if len(step) == 1:
-            layer.forward(step[0][1], layer=step[0][0], out=out)
+            lay.forward(step[0][1], layer=step[0][0], out=out)
         else:  # a stack step: every layer in one native call
-            layer.forward_steps(step, out)
+            lay.forward_steps(step, out)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    c1 = layer.counters()
-    ms, n = layer.ctx.ffn_time()
-    layer.ctx.set_timing(False)
-    return dt, {k: c1[k] - c0[k] for k in c1}, ms, n
+    cnt = {}
+    ms = n = 0
+    for lay, a in zip(layers, c0):
+        b = lay.counters()
+        for k in b:
+            cnt[k] = cnt.get(k, 0) + b[k] - a[k]
+        m, c = lay.ctx.ffn_time()
+        ms, n = ms + m, n + c
+        lay.ctx.set_timing(False)
+    return dt, cnt, ms, n
 
 
 def make_batches(shape, T, steps):
@@ -91,25 +104,28 @@ def make_batches(shape, T, steps):
     return [[(l, seqs[l][i]) for l in range(shape.layers)] for i in range(steps)]
 
 
-def timed(layer, shape, T, steps, warmup, label, ffn_timing=False):
+def timed(layers, shape, T, steps, warmup, label, ffn_timing=False):
     """Warm up, then time exactly ``steps`` steps between two device synchronisations.
 
-    With ffn_timing, the same steps run a second time with HIP events on the
-    compute stream around each layer call's expert FFN (routed groups, fill
-    waves, shared experts); the headline rate comes from the pass without events.
+    layers: one layer object, or replicas of it (each its own slot pool holding the
+    same experts) that the steps use in turn, so that a step's weights were last read
+    several steps earlier. With ffn_timing, the same steps run a second time with HIP
+    events on the compute stream around each layer call's expert FFN (routed groups,
+    fill waves, shared experts); the headline rate comes from the pass without events.
     """
+    layers = layers if isinstance(layers, (list, tuple)) else [layers]
     batches = make_batches(shape, T, steps + warmup)
-    out = torch.empty(T, shape.H, dtype=layer.out_dtype, device="cuda")
-    _run(layer, batches[:warmup], out, False)
-    dt, cnt, _, _ = _run(layer, batches[warmup:], out, False)
+    out = torch.empty(T, shape.H, dtype=layers[0].out_dtype, device="cuda")
+    _run(layers, batches[:warmup], out, False)
+    dt, cnt, _, _ = _run(layers, batches[warmup:], out, False)
     calls = steps * shape.layers
     res = {"tokens_per_step": T, "tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3,
            "distinct_per_layer_call": cnt["distinct"] / calls,
-           "fills_per_step": cnt["fills"] / steps}
+           "fills_per_step": cnt["fills"] / steps, "pool_replicas": len(layers)}
     if cnt["distinct"] > 0:
         res["hit_rate"] = cnt["hits"] / cnt["distinct"]
     if ffn_timing:
-        dt2, cnt2, ms, n = _run(layer, batches[warmup:], out, True)
+        dt2, cnt2, ms, n = _run(layers, batches[warmup:], out, True)
         eb = expert_bytes(shape)
         # algorithmic bytes of the expert FFN per layer call: each distinct routed
         # expert's weights once, the shared experts' weights, tokens in, fp32 rows out
@@ -121,8 +137,21 @@ def timed(layer, shape, T, steps, warmup, label, ffn_timing=False):
                       "gbs": per_call / (us * 1e-6) / 1e9,
                       "mfma_frac": flops / (us * 1e-6) / (MFMA_PEAK_TFLOPS[shape.wfmt] * 1e12),
                       "ms_per_step_with_events": dt2 / steps * 1e3}
-    print(f"# {label}: {res}", file=sys.stderr, flush=True)
+    print(f"# {shape.name} {label}: {res}", file=sys.stderr, flush=True)
     return res
+
+
+def replicas_for(shape, T, max_bytes=24e9):
+    """Pool replicas a hit-path timing rotates over: enough that the weights of the
+    steps in between exceed 1 GB (four times the 256 MB MALL), at most 8 and at most
+    max_bytes of pools. The 48-layer stack reads GBs per step: one pool."""
+    if shape.layers > 1:
+        return 1
+    p = 1.0 - (1.0 - 1.0 / shape.E) ** (T * shape.k)  # chance that an expert is routed
+    per_step = (shape.E * p + shape.n_shared) * expert_bytes(shape)
+    pool = (shape.E + shape.n_shared) * expert_bytes(shape)
+    r = int(np.ceil(1e9 / per_step)) + 1 if per_step < 1e9 else 1
+    return max(1, min(8, r, int(max_bytes // pool)))
 
 
 def recorded_traffic(*keys):
@@ -160,11 +189,25 @@ def all_resident(shape):
     return [own[i] for i in rng.permutation(len(own))]
 
 
-def cpu_baseline(shape, budget_s=15.0):
-    """The oracle as it stands, on a bounded sample of decode steps (T=1) of layer 0."""
+def cpu_baseline(shape, budget_s=20.0):
+    """The oracle as it stands (float64 NumPy), on a bounded sample of the headline's decode
+    steps (1 token per step, layer 0, every routed expert resident in the oracle's pool), on
+    every core the process may use (BLAS threads set to that count, capped by the thread
+    budget the environment sets)."""
     import oracle as O
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
+    affinity = len(os.sched_getaffinity(0))
+    env_cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(affinity, env_cap) if env_cap > 0 else affinity
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     E = shape.E
     cache = {}
     load_s = [0.0]  # drawing the synthetic weights is setup, not oracle work: not counted
@@ -180,22 +223,25 @@ def cpu_baseline(shape, budget_s=15.0):
     shared = [{n: t.cpu() for n, t in W.shared_expert_weights(shape, j, device="cuda").items()}
               for j in range(shape.n_shared)]
     wr, b = W.router(shape)
-    # an oracle pool of E slots, empty at first: each expert is loaded on its first use
+    # the oracle's pool of E slots starts empty: an expert is copied in on its first use
     pool = O.SlotPool(E, 1, E)
     planner = O.LruSlotPlanner(E, 1, E, [None] * E)
-    n, t0 = 0, time.perf_counter()
-    while True:
-        x = W.tokens(shape, 1, step=n)
-        O.moe_layer(x, wr, b, shape.k, layer=0, pool=pool, planner=planner,
-                    weights_of_expert=weights_of, shared=shared or None)
-        n += 1
-        dt = time.perf_counter() - t0 - load_s[0]
-        if dt >= budget_s or n >= 64:
-            break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} decode steps of 1 token, layer 0 (float64 NumPy oracle, weights upcast "
-                      f"per use), {dt:.1f} s"}
+    n, work = 0, 0.0
+    with threadpool_limits(limits=threads):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        while True:
+            x = W.tokens(shape, 1, step=n)
+            t0, l0 = time.perf_counter(), load_s[0]
+            O.moe_layer(x, wr, b, shape.k, layer=0, pool=pool, planner=planner,
+                        weights_of_expert=weights_of, shared=shared or None)
+            work += time.perf_counter() - t0 - (load_s[0] - l0)
+            n += 1
+            if work >= budget_s or n >= 64:
+                break
+    return {"value": n / work, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{n} decode steps of 1 token of {shape.name}, layer 0 (float64 NumPy oracle, "
+                      f"int4 weights dequantised per use), {work:.1f} s of oracle time",
+            "affinity_cores": affinity, "cpu_model": model}
 
 
 def calib_copy(steps):
@@ -230,12 +276,14 @@ POLICIES = {"lru": (B.MOE_POLICY_LRU, 1, None),
             "lru_device": (B.MOE_POLICY_LRU, 1, None)}
 
 
-def fill_cases(shape, plan, cfg, store, steps, warmup):
-    """Each cache with fills of the workload under each eviction policy, on the same inputs."""
+def fill_cases(shape, plan, cfg, store, steps, warmup, policies=tuple(POLICIES)):
+    """Each cache with fills of the workload under each of the eviction policies named, on
+    the same inputs (rates include the PCIe copies of the misses)."""
     out = {}
     for S, T in plan["miss"]:
         res = {}
-        for name, (kind, window, params) in POLICIES.items():
+        for name in policies:
+            kind, window, params = POLICIES[name]
             small = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]),
                                       t_max=T, store=store)
             small.ctx.set_policy(kind, window, params)
@@ -389,10 +437,45 @@ def staging_case(shape, cfg, store, S, T, steps, warmup):
     return res
 
 
+def hit_layers(shape, T, store, t_max=None):
+    """Hit-path layer objects (every layer-expert resident), replicated per replicas_for."""
+    resident = all_resident(shape)
+    n = replicas_for(shape, T)
+    return [Hn.SlotCacheLayer(shape, len(resident), resident, t_max=t_max or T, store=store)
+            for _ in range(n)]
+
+
+def workload_report(name, K, Wm, quick=False, policies=("lru", "lru_device")):
+    """Hit path at each token count of the workload (expert FFN timed with events) and its
+    caches with fills. Returns (first hit-path result, dict of the others)."""
+    shape, plan, cfg = W.shape_of(name), PLANS[name], W.WORKLOADS[name]
+    store = Hn.ExpertStore(shape)
+    res = {}
+    head = None
+    for i, T in enumerate(plan["hit"]):
+        if quick and i > 0:
+            break
+        steps = K if T <= 64 else max(K // 10, 3)
+        layers = hit_layers(shape, T, store)
+        r = timed(layers, shape, T, steps, Wm if i == 0 else 2, f"T={T} hit path", ffn_timing=True)
+        del layers
+        torch.cuda.empty_cache()
+        if head is None:
+            head = r
+        else:
+            res[f"T{T}_hit"] = r
+    if not quick:
+        steps = max(K // 5, 5) if shape.layers == 1 else max(K // 5, 8)
+        res.update(fill_cases(shape, plan, cfg, store, steps, 2, policies))
+    del store
+    torch.cuda.empty_cache()
+    return head, res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(PLANS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -432,14 +515,10 @@ def main():
         for T in (1, 32, 512):
             split_case(sshape, sstore, T, K if T <= 32 else max(K // 4, 3), Wm)
         return
-    t_max = max(plan["hit"])
-    store = Hn.ExpertStore(shape)
-    resident = all_resident(shape)
-    S_hit = len(resident)
-
     if args.case is not None:
+        store = Hn.ExpertStore(shape)
         if args.case == "policies":
-            fill_cases(shape, plan, cfg, store, K, Wm)
+            fill_cases(shape, plan, cfg, store, K, Wm, tuple(POLICIES))
         elif args.case == "graph":
             graph_case(shape, plan, cfg, store, K, Wm)
         elif args.case == "fills":
@@ -449,22 +528,18 @@ def main():
             timed(small, shape, T, K, Wm, f"T={T}, {S} slots, fills over PCIe")
         else:
             T = CASES[args.case] if args.case in CASES else int(args.case.lstrip("T"))
-            layer = Hn.SlotCacheLayer(shape, S_hit, resident, t_max=T, store=store)
-            timed(layer, shape, T, K, Wm, args.case, ffn_timing=True)
+            timed(hit_layers(shape, T, store), shape, T, K, Wm, args.case, ffn_timing=True)
         return
 
-    layer = Hn.SlotCacheLayer(shape, S_hit, resident, t_max=t_max, store=store)
+    head, also = workload_report(args.workload, K, Wm, args.quick)
     head_T = plan["hit"][0]
-    head = timed(layer, shape, head_T, K, Wm, f"T={head_T} hit path", ffn_timing=True)
-    also = {}
-    if not args.quick:
-        for T in plan["hit"][1:]:
-            steps = K if T <= 64 else max(K // 10, 3)
-            also[f"T{T}_hit"] = timed(layer, shape, T, steps, 2, f"T={T} hit path", ffn_timing=True)
-        del layer
-        torch.cuda.empty_cache()
-        steps = max(K // 5, 5) if shape.layers == 1 else max(K // 5, 8)
-        also.update(fill_cases(shape, plan, cfg, store, steps, 2))
+    if not args.quick and args.workload == DEFAULT:
+        others = {}
+        for name in PLANS:
+            if name != DEFAULT:
+                h, rest = workload_report(name, max(K // 2, 5), 2)
+                others[name] = {f"T{h['tokens_per_step']}_hit": h, **rest}
+        also["other_workloads"] = others
 
     ffn = head["ffn"]
     line = {
@@ -483,10 +558,13 @@ def main():
         "config": {"workload": f"{args.workload}: E={shape.E} top-{shape.k}, H={shape.H}, F={shape.F}"
                                + (f", {shape.n_shared} shared" if shape.n_shared else "")
                                + (f", {shape.layers} layers" if shape.layers > 1 else "")
-                               + f", decode {head_T} token/step, every expert resident (hit path)",
-                   "tokens_per_step": head_T, "slots": S_hit, "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "moe_expert_ffn (group plan + W13 GEMV + W2 GEMV launches, one call per "
-                               "layer step)",
+                               + f", decode {head_T} token/step, every routed expert of the step "
+                                 "resident (hit path); the workload's own cache with fills over "
+                                 "PCIe is under also",
+                   "tokens_per_step": head_T, "slots": shape.layers * shape.E,
+                   "pool_replicas": head["pool_replicas"], "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "moe_expert_ffn (group plan + gate/up pass + down pass launches, one "
+                               "call per layer step)",
                      "bound": "hbm", "achieved": round(ffn["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ffn["gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(f"{args.workload}/decode{head_T}",

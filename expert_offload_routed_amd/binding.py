@@ -34,11 +34,14 @@ _SIGNATURES = {
     "moe_critical_split": (_i32, [_vp, _i32, ctypes.c_float, _vp, _i32, _vp, _vp]),
     "moe_step_scores": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "moe_ffn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "moe_ffn_workspace_offsets": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "moe_quantize_rows_int8": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "moe_expert_ffn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _i32, _i32, _i32, _i32,
                               _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _vp]),
     "slot_fill": (_i32, [_vp, _sz, _i32, _vp, _sz, _vp, _i32, _vp, _vp, _u64, _vp, _vp, _vp]),
     "slot_commit": (_i32, [_vp, _i32, _vp, _i32, _vp, _u64, _vp, _vp]),
+    "slot_prefetch": (_i32, [_vp, _sz, _i32, _vp, _sz, _vp, _u64, _vp]),
     "moe_plan_fills": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp]),
     "moe_policy_state_doubles": (_sz, [_i32, _i32, _i32, _i32]),
@@ -46,7 +49,11 @@ _SIGNATURES = {
     "moe_plan_fills_policy": (_i32, [_i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                      _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_version": (ctypes.c_char_p, []),
-    "moe_ctx_workspace_bytes": (_sz, [_i32] * 7),
+    "moe_prefetch_count": (_i32, [ctypes.c_double, ctypes.c_double, _sz, _i32]),
+    "moe_plan_prefetch": (_i32, [_i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                 _vp, _i32, _vp, ctypes.c_double, ctypes.c_double, _sz, _vp, _vp,
+                                 _vp]),
+    "moe_ctx_workspace_bytes": (_sz, [_i32] * 9),
     "moe_ctx_create": (_i32, [ctypes.POINTER(_vp)] + [_i32] * 10 + [_vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp,
                                                                    _vp, _vp, _sz, _vp, _vp]),
     "moe_ctx_destroy": (_i32, [_vp]),
@@ -274,6 +281,23 @@ def moe_ffn_workspace_bytes(T, H, F, E, k, w_dtype) -> int:
     return int(lib().moe_ffn_workspace_bytes(T, H, F, E, k, w_dtype))
 
 
+def moe_ffn_workspace_offsets(T, H, F, E, k, w_dtype) -> dict:
+    offs = (ctypes.c_size_t * 5)()
+    _call("moe_ffn_workspace_offsets", T, H, F, E, k, w_dtype, ctypes.cast(offs, _vp))
+    return dict(zip(("h", "xq", "xs", "hq", "hs"), (int(v) for v in offs)))
+
+
+def moe_quantize_rows_int8(a, stream=None):
+    """Per-row int8 codes and scales of a [rows, K] fp32 or bf16 device tensor."""
+    a = a.contiguous()
+    rows, K = a.shape
+    q = torch.empty(rows, K, dtype=torch.int8, device=a.device)
+    s = torch.empty(rows, dtype=torch.float32, device=a.device)
+    _call("moe_quantize_rows_int8", _dev(a), dtype_code(a), rows, K, _dev(q), _dev(s),
+          _stream(stream))
+    return q, s
+
+
 def moe_expert_ffn(x, perm, offsets, lut_row, group_mask, pool, slot_stride: int, w_dtype: int,
                    T: int, H: int, F: int, E: int, k: int, y_perm, err_word, workspace, stream=None):
     num_slots = pool.numel() // slot_stride
@@ -306,6 +330,13 @@ def slot_fill(pool, slot_stride: int, slot: int, host_src, nbytes: int, lut, lut
     src = host_src if isinstance(host_src, int) else host_src.data_ptr()
     _call("slot_fill", _dev(pool), slot_stride, slot, src, nbytes, _dev(lut), lut_index, _dev(owner),
           _dev(slot_tags), tag, _dev(err_word), _stream(fill_stream), _stream(compute_stream))
+
+
+def slot_prefetch(pool, slot_stride: int, slot: int, host_src, nbytes: int, slot_tags, tag: int,
+                  fill_stream=None):
+    src = host_src if isinstance(host_src, int) else host_src.data_ptr()
+    _call("slot_prefetch", _dev(pool), slot_stride, slot, src, nbytes, _dev(slot_tags), tag,
+          _stream(fill_stream))
 
 
 def slot_commit(lut, lut_index: int, owner, slot: int, slot_tags, tag: int, err_word, stream=None):
@@ -346,6 +377,29 @@ MOE_POLICY_LRU, MOE_POLICY_MRS, MOE_POLICY_HISTORY = 0, 1, 2
 MOE_ORCH_HOST, MOE_ORCH_DEVICE = 0, 1
 
 
+def moe_prefetch_count(window_us: float, bw_gbs: float, expert_bytes: int, free_slots: int) -> int:
+    return int(lib().moe_prefetch_count(window_us, bw_gbs, expert_bytes, free_slots))
+
+
+def moe_plan_prefetch(policy, lut, owner, last_use, clock, S: int, L: int, E: int, layer: int,
+                      pred_ids, pred_scores, window_us: float, bw_gbs: float,
+                      expert_bytes: int) -> list:
+    """Host prefetch plan on numpy state arrays (updated in place); policy None = LRU.
+    Returns [(expert, slot)]."""
+    p = np.ascontiguousarray(np.asarray(pred_ids).ravel(), dtype=np.int32)
+    sc = np.ascontiguousarray(pred_scores, dtype=np.float32)
+    fe, fs = np.empty(E, np.int32), np.empty(E, np.int32)
+    nf = np.zeros(1, np.int32)
+    kind = MOE_POLICY_LRU if policy is None else policy.kind
+    state = None if policy is None else _host(policy.state)
+    window = 1 if policy is None else policy.window
+    params = None if policy is None or policy.params is None else _host(policy.params)
+    _call("moe_plan_prefetch", kind, state, window, params, _host(lut), _host(owner),
+          _host(last_use), _host(clock), S, L, E, layer, _host(p) if p.size else None, p.size,
+          _host(sc), window_us, bw_gbs, expert_bytes, _host(fe), _host(fs), _host(nf))
+    return [(int(fe[i]), int(fs[i])) for i in range(int(nf[0]))]
+
+
 class EvictionPolicy:
     """Host state of an eviction policy (moe_policy_* in include/moe_offload.h)."""
 
@@ -373,8 +427,8 @@ def moe_version() -> str:
 
 
 # ------------------------------------------------------------ layer runtime --
-def moe_ctx_workspace_bytes(t_max, H, F, E, k, w_dtype, n_shared) -> int:
-    return int(lib().moe_ctx_workspace_bytes(t_max, H, F, E, k, w_dtype, n_shared))
+def moe_ctx_workspace_bytes(t_max, H, F, E, k, L, S, w_dtype, n_shared) -> int:
+    return int(lib().moe_ctx_workspace_bytes(t_max, H, F, E, k, L, S, w_dtype, n_shared))
 
 
 class LayerContext:
@@ -388,7 +442,7 @@ class LayerContext:
         self.pool_slots = pool.numel() // slot_stride
         self.compute_stream = compute_stream or torch.cuda.current_stream(dev)
         self.fill_stream = fill_stream or torch.cuda.Stream(device=dev)
-        nbytes = moe_ctx_workspace_bytes(t_max, H, F, E, k, w_dtype, n_shared)
+        nbytes = moe_ctx_workspace_bytes(t_max, H, F, E, k, L, S, w_dtype, n_shared)
         if nbytes == 0:
             raise ValueError("moe_ctx_workspace_bytes: bad sizes")
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)

@@ -253,6 +253,19 @@ extern "C" size_t moe_ffn_workspace_bytes(int T, int H, int F, int E, int k, int
   return ffn_workspace_layout(T, H, F, E, k, w_dtype, 0).total;
 }
 
+extern "C" int moe_ffn_workspace_offsets(int T, int H, int F, int E, int k, int w_dtype,
+                                         size_t* offs) {
+  MOE_CHECK_ARG(T >= 0 && H > 0 && F > 0 && E > 0 && k > 0 && offs);
+  MOE_CHECK_ARG(w_dtype >= MOE_F32 && w_dtype <= MOE_INT4G128_RESPLIT);
+  const FfnWorkspace w = ffn_workspace_layout(T, H, F, E, k, w_dtype, 0);
+  offs[0] = w.h;
+  offs[1] = w.xq;
+  offs[2] = w.xs;
+  offs[3] = w.hq;
+  offs[4] = w.hs;
+  return MOE_OK;
+}
+
 int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* lut,
              const int32_t* group_mask, int n_shared, int shared_slot0, const char* pool,
              size_t stride, int num_slots, const SlotLayout& lay, int T, int H, int F, int E, int k,

@@ -272,15 +272,12 @@ __device__ __forceinline__ void w4a8_tile(
     const int r = lane & 31, c = 2 * ks + (lane >> 5);  // row within the 32-row block
     aoff[ks] = (r >> 3) * 1024 + (8 * (r & 7) + (c ^ ((r >> 1) & 7))) * 16;
   }
-  // Each group's integer sum P starts from the bit pattern of kMagic = 1.5 * 2^23, so the
-  // int32 sum kMagic_bits + P (|P| <= 128 * 128 * 127 < 2^22) is the float kMagic + P
-  // exactly and a fold is one fma on the accumulator's bits. Each fold adds the offset
-  // kMagic * s, the same for every element of the lane (one weight row); the folded
-  // scales are summed in pend and the offsets removed every kQCorr steps and at the
-  // end, so |accf| stays near kQCorr * kMagic * s (fp32 rounding about 1e-6 of it).
-  // The form with two code sets per step (WM 1) keeps the plain fold (convert, then
-  // fma): it has no registers left for the constant.
-  constexpr bool MAGIC = WM != 1;
+  // Each group's int32 sum P is folded into the fp32 sums as fma(float(P), s, acc):
+  // float(P) is exact (|P| <= 128 * 128 * 127 < 2^24) and so is P * s for the small
+  // integer codes of a group, so a fold rounds once. (Starting P from the bit pattern of
+  // 1.5 * 2^23 saves the conversion, but leaves an offset of 1.5 * 2^23 * s per group
+  // in the sums, whose rounding then swamps the groups of a row with small scales.)
+  constexpr bool MAGIC = false;
   constexpr int kMagicBits = MAGIC ? 0x4B400000 : 0;
   constexpr float kMagic = MAGIC ? 12582912.f : 0.f;
   // the MFMAs' C operand of a group's first k step, held in registers (a value the
@@ -573,6 +570,23 @@ void launch_gemv_any(bool first, bool split, int nt, const int8_t* aq, const flo
 }
 
 }  // namespace
+
+// a6q as a stage of its own: per-row int8 codes of rows [rows, K] (the rule every
+// int4 pass uses for the tokens and the SwiGLU intermediate).
+extern "C" int moe_quantize_rows_int8(const void* in, int in_dtype, int rows, int K, int8_t* q,
+                                      float* s, hipStream_t stream) {
+  MOE_CHECK_ARG(rows >= 0 && K >= 8 && K % 8 == 0 && K <= 4 * 2048);
+  MOE_CHECK_ARG(in_dtype == MOE_F32 || in_dtype == MOE_BF16);
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK_ARG(in && q && s && ((uintptr_t)in % 16) == 0 && ((uintptr_t)q % 8) == 0);
+  if (in_dtype == MOE_BF16)
+    hipLaunchKernelGGL(quant_rows_kernel<MOE_BF16>, dim3((unsigned)rows), dim3(256), 0, stream, in,
+                       K, nullptr, nullptr, nullptr, 0, 0, 0, q, s);
+  else
+    hipLaunchKernelGGL(quant_rows_kernel<MOE_F32>, dim3((unsigned)rows), dim3(256), 0, stream, in,
+                       K, nullptr, nullptr, nullptr, 0, 0, 0, q, s);
+  return moe_launch_status();
+}
 
 int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* lut,
              const int32_t* group_mask, int n_shared, int shared_slot0, const char* pool,

@@ -25,8 +25,9 @@
 // the device tables, keeping the slots in (last use, slot id) order; a copy
 // kernel reads the missed experts from the mapped host store into their slots;
 // the expert FFN and the combine follow on the same stream.
-// The context allocates its staging once, at creation, and the device
-// planner's state once, when device orchestration is first switched on; a
+// The context allocates its pinned host staging and events once, at creation
+// (the staging buffers' events on the first staging enable); every device buffer,
+// the device planner's tables included, lives in the caller's workspace, and a
 // step allocates nothing.
 #include <limits.h>
 #include <math.h>
@@ -97,6 +98,7 @@ struct moe_layer_ctx {
   int stage_thr;           // token threshold; -1: floor(resident slots of the layer / k)
   int stage_slot0;         // first staging slot: buffer b holds expert e in slot0 + b*E + e
   int32_t* d_stage_lut;    // [2E] device: those slots, one expert->slot row per buffer
+  bool stage_ready;        // the table is written and the events exist
   int buf_layer[2];        // layer each buffer holds (or is loading); -1: none
   int buf_last;            // buffer of the latest staged step
   hipEvent_t ev_ready[2];  // the buffer's load finished (fill stream)
@@ -105,6 +107,7 @@ struct moe_layer_ctx {
   int next_hint;           // layer of the next step (moe_ctx_forward_steps); -1: layer + 1
   // device orchestration (moe_ctx_set_orchestration)
   int orch;                 // 0: plans on the host; 1: plans and fills on the device
+  bool orch_ready;          // d_blob is written (the tables below live in the workspace)
   const char* store_dev;    // device address of the pinned host store
   int32_t* d_order;         // [S] slots by (last use, slot id)
   int64_t* d_last_use;      // [S]
@@ -132,9 +135,12 @@ struct CtxLayout {
   size_t sync, logits, ids, topw, counts, offsets, perm, inv, dist, y_perm, ws, masks, scores, crit,
       total;
   size_t ws_bytes;
+  // device orchestration's tables and staging's slot table (used only once switched on)
+  size_t order, last_use, clock, blob, fills, nfills, counters, stage_lut;
 };
 
-CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int w_dtype, int n_shared) {
+CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int L, int S, int w_dtype,
+                     int n_shared) {
   CtxLayout l{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -159,6 +165,14 @@ CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int w_dtype, int n_s
   l.masks = take((size_t)(E + 2) * E * 4);
   l.scores = take((size_t)E * 4);
   l.crit = take((size_t)E * 4);
+  l.order = take((size_t)S * 4);
+  l.last_use = take((size_t)S * 8);
+  l.clock = take(8);
+  l.blob = take((size_t)L * E * 4);
+  l.fills = take(2 * (size_t)E * 4);
+  l.nfills = take(4);
+  l.counters = take(4 * 8);
+  l.stage_lut = take(2 * (size_t)E * 4);
   l.total = off;
   return l;
 }
@@ -332,10 +346,6 @@ void destroy(moe_layer_ctx* c) {
     if (c->tev0[i]) (void)hipEventDestroy(c->tev0[i]);
     if (c->tev1[i]) (void)hipEventDestroy(c->tev1[i]);
   }
-  void* dev[] = {c->d_order, c->d_last_use, c->d_clock, c->d_blob, c->d_fills, c->d_nfills,
-                 c->d_counters, c->d_stage_lut};
-  for (void* p : dev)
-    if (p) (void)hipFree(p);
   for (int b = 0; b < 2; ++b) {
     if (c->ev_ready[b]) (void)hipEventDestroy(c->ev_ready[b]);
     if (c->ev_free[b]) (void)hipEventDestroy(c->ev_free[b]);
@@ -472,10 +482,10 @@ int push_to_device(moe_layer_ctx* c) {
 
 }  // namespace
 
-extern "C" size_t moe_ctx_workspace_bytes(int t_max, int H, int F, int E, int k, int w_dtype,
-                                          int n_shared) {
-  if (t_max < 1 || H <= 0 || F <= 0 || E < 1 || k < 1 || n_shared < 0) return 0;
-  return ctx_layout(t_max, H, F, E, k, w_dtype, n_shared).total;
+extern "C" size_t moe_ctx_workspace_bytes(int t_max, int H, int F, int E, int k, int L, int S,
+                                          int w_dtype, int n_shared) {
+  if (t_max < 1 || H <= 0 || F <= 0 || E < 1 || k < 1 || L < 1 || S < 1 || n_shared < 0) return 0;
+  return ctx_layout(t_max, H, F, E, k, L, S, w_dtype, n_shared).total;
 }
 
 extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int E, int k, int L,
@@ -495,7 +505,7 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   // the shared experts are the n_shared slots right after the S routed slots
   MOE_CHECK_ARG(n_shared == 0 ||
                 shared_pool == static_cast<const char*>(pool_base) + (size_t)S * slot_stride);
-  const CtxLayout cl = ctx_layout(t_max, H, F, E, k, w_dtype, n_shared);
+  const CtxLayout cl = ctx_layout(t_max, H, F, E, k, L, S, w_dtype, n_shared);
   MOE_CHECK_ARG(workspace && ws_bytes >= cl.total && ((uintptr_t)workspace % 256) == 0);
   *out = nullptr;
   moe_layer_ctx* c = new (std::nothrow) moe_layer_ctx();
@@ -523,7 +533,6 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->stage = 0;
   c->stage_thr = -1;
   c->stage_slot0 = S + n_shared;
-  c->d_stage_lut = nullptr;
   c->buf_layer[0] = c->buf_layer[1] = -1;
   c->buf_last = -1;
   c->ev_ready[0] = c->ev_ready[1] = c->ev_free[0] = c->ev_free[1] = nullptr;
@@ -531,9 +540,7 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->next_hint = -1;
   c->orch = 0;
   c->store_dev = nullptr;
-  c->d_order = nullptr;
-  c->d_last_use = c->d_clock = c->d_counters = nullptr;
-  c->d_blob = c->d_fills = c->d_nfills = nullptr;
+  c->orch_ready = false;
   c->next_tag = 1;
   c->wave_of.resize(E); c->is_hit.resize(E);
   c->fill_e.resize(E); c->fill_s.resize(E); c->fill_w.resize(E);
@@ -554,6 +561,15 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->masks = reinterpret_cast<int32_t*>(wb + cl.masks);
   c->scores = reinterpret_cast<float*>(wb + cl.scores);
   c->crit = reinterpret_cast<int32_t*>(wb + cl.crit);
+  c->d_order = reinterpret_cast<int32_t*>(wb + cl.order);
+  c->d_last_use = reinterpret_cast<int64_t*>(wb + cl.last_use);
+  c->d_clock = reinterpret_cast<int64_t*>(wb + cl.clock);
+  c->d_blob = reinterpret_cast<int32_t*>(wb + cl.blob);
+  c->d_fills = reinterpret_cast<int32_t*>(wb + cl.fills);
+  c->d_nfills = reinterpret_cast<int32_t*>(wb + cl.nfills);
+  c->d_counters = reinterpret_cast<int64_t*>(wb + cl.counters);
+  c->d_stage_lut = reinterpret_cast<int32_t*>(wb + cl.stage_lut);
+  c->stage_ready = false;
   int bad = 0;
   // coherent, mapped: the permutation kernel stores the routed set straight into it
   bad |= hipHostMalloc(reinterpret_cast<void**>(&c->ring_h),
@@ -725,17 +741,11 @@ extern "C" int moe_ctx_set_orchestration(moe_layer_ctx* c, int mode) {
   c->store_dev = static_cast<const char*>(dev);
   int rc = drain(c);
   if (rc != MOE_OK) return rc;
-  if (!c->d_order) {
-    hipError_t e = hipMalloc(&c->d_order, c->S * sizeof(int32_t));
-    if (e == hipSuccess) e = hipMalloc(&c->d_last_use, c->S * sizeof(int64_t));
-    if (e == hipSuccess) e = hipMalloc(&c->d_clock, sizeof(int64_t));
-    if (e == hipSuccess) e = hipMalloc(&c->d_blob, (size_t)c->L * c->E * sizeof(int32_t));
-    if (e == hipSuccess) e = hipMalloc(&c->d_fills, 2 * (size_t)c->E * sizeof(int32_t));
-    if (e == hipSuccess) e = hipMalloc(&c->d_nfills, sizeof(int32_t));
-    if (e == hipSuccess) e = hipMalloc(&c->d_counters, 4 * sizeof(int64_t));
-    if (e == hipSuccess)
-      e = hipMemcpy(c->d_blob, c->blob_of.data(), c->blob_of.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (!c->orch_ready) {  // the weight set table, in the caller's workspace
+    const hipError_t e = hipMemcpy(c->d_blob, c->blob_of.data(),
+                                   c->blob_of.size() * sizeof(int32_t), hipMemcpyHostToDevice);
     if (e != hipSuccess) return moe_hip_status(e);
+    c->orch_ready = true;
   }
   if ((rc = push_to_device(c)) != MOE_OK) return rc;
   c->orch = 1;
@@ -795,12 +805,10 @@ extern "C" int moe_ctx_set_staging(moe_layer_ctx* c, int enable, int threshold, 
   MOE_CHECK_ARG(!c->orch);  // staged steps are planned on the host
   MOE_CHECK_ARG((long long)pool_slots >= (long long)c->stage_slot0 + 2LL * c->E);
   hipError_t e = hipSuccess;
-  if (!c->d_stage_lut) {
+  if (!c->stage_ready) {  // the buffers' slot table, in the caller's workspace
     std::vector<int32_t> h(2 * (size_t)c->E);
     for (int i = 0; i < 2 * c->E; ++i) h[i] = c->stage_slot0 + i;
-    e = hipMalloc(&c->d_stage_lut, h.size() * sizeof(int32_t));
-    if (e == hipSuccess)
-      e = hipMemcpy(c->d_stage_lut, h.data(), h.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    e = hipMemcpy(c->d_stage_lut, h.data(), h.size() * sizeof(int32_t), hipMemcpyHostToDevice);
     for (int b = 0; b < 2 && e == hipSuccess; ++b) {
       e = hipEventCreateWithFlags(&c->ev_ready[b], hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_free[b], hipEventDisableTiming);
@@ -809,6 +817,7 @@ extern "C" int moe_ctx_set_staging(moe_layer_ctx* c, int enable, int threshold, 
       if (e == hipSuccess) e = hipEventRecord(c->ev_ready[b], c->cs);
     }
     if (e != hipSuccess) return moe_hip_status(e);
+    c->stage_ready = true;
   }
   c->stage = 1;
   c->stage_thr = threshold;

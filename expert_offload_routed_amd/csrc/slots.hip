@@ -348,6 +348,23 @@ extern "C" int slot_fill(void* pool_base, size_t slot_stride, int32_t slot, cons
   return moe_launch_status();
 }
 
+extern "C" int slot_prefetch(void* pool_base, size_t slot_stride, int32_t slot,
+                             const void* host_src, size_t bytes, uint64_t* slot_tags,
+                             uint64_t tag, hipStream_t fill_stream) {
+  MOE_CHECK_ARG(pool_base && host_src && slot_tags && slot >= 0 && bytes <= slot_stride);
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host_src) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_EINVAL;  // not memory the runtime knows: pageable host memory
+  }
+  if (attr.type != hipMemoryTypeHost) return MOE_EINVAL;
+  char* dst = static_cast<char*>(pool_base) + (size_t)slot * slot_stride;
+  const hipError_t e = hipMemcpyAsync(dst, host_src, bytes, hipMemcpyHostToDevice, fill_stream);
+  if (e != hipSuccess) return moe_hip_status(e);
+  hipLaunchKernelGGL(tag_writeback_kernel, dim3(1), dim3(64), 0, fill_stream, slot_tags, slot, tag);
+  return moe_launch_status();
+}
+
 // ------------------------------------------------------- host LRU planning --
 // ------------------------------------------------------- eviction scores --
 // Host state of an eviction policy, per layer (doubles):
@@ -576,6 +593,84 @@ extern "C" int moe_plan_fills_policy(int policy, const double* state, int window
   return plan_fills(lut, owner, last_use, clock, S, L, E, layer, distinct, n_distinct, wave_of,
                     is_hit, fill_expert, fill_slot, fill_wave, n_fills, n_waves, policy, state,
                     window, params);
+}
+
+extern "C" int moe_prefetch_count(double window_us, double bw_gbs, size_t expert_bytes,
+                                  int free_slots) {
+  if (!(window_us > 0.0) || expert_bytes == 0 || free_slots <= 0 || !(bw_gbs > 0.0)) return 0;
+  const double n = std::floor(window_us * bw_gbs * 1000.0 / (double)expert_bytes);
+  return n < (double)free_slots ? (int)n : free_slots;
+}
+
+extern "C" int moe_plan_prefetch(int policy, const double* state, int window,
+                                 const double* params, int32_t* lut, int32_t* owner,
+                                 int64_t* last_use, const int64_t* clock, int S, int L, int E,
+                                 int layer, const int32_t* pred_ids, int n_pred,
+                                 const float* pred_scores, double window_us, double bw_gbs,
+                                 size_t expert_bytes, int32_t* fill_expert, int32_t* fill_slot,
+                                 int32_t* n_fills) {
+  MOE_CHECK_ARG(lut && owner && last_use && clock && n_fills && pred_scores);
+  MOE_CHECK_ARG(S >= 1 && L >= 1 && E >= 1 && layer >= 0 && layer < L && n_pred >= 0);
+  MOE_CHECK_ARG(n_pred == 0 || (pred_ids && fill_expert && fill_slot));
+  MOE_CHECK_ARG(policy_args_ok(policy, state, window, params));
+  *n_fills = 0;
+  std::vector<char> pred(E, 0);
+  for (int i = 0; i < n_pred; ++i) {
+    if (pred_ids[i] < 0 || pred_ids[i] >= E) return MOE_EINVAL;
+    pred[pred_ids[i]] = 1;
+  }
+  int32_t* row = lut + (size_t)layer * E;
+  std::vector<int> cand;
+  for (int e = 0; e < E; ++e)
+    if (pred[e] && row[e] < 0) cand.push_back(e);
+  std::stable_sort(cand.begin(), cand.end(),
+                   [&](int a, int b) { return pred_scores[a] > pred_scores[b]; });
+  if (cand.empty()) return MOE_OK;
+  // free slots: empty ones by id, then those the current step did not use and that hold no
+  // predicted expert of this layer, in the victim order of the policy
+  std::vector<int> freeslots, reuse;
+  for (int s = 0; s < S; ++s) {
+    if (owner[s] < 0) {
+      freeslots.push_back(s);
+    } else if (last_use[s] < *clock) {
+      const int l = owner[s] / E, e = owner[s] % E;
+      if (!(l == layer && pred[e])) reuse.push_back(s);
+    }
+  }
+  std::vector<double> keep;
+  if (policy != MOE_POLICY_LRU && !reuse.empty()) {
+    keep.assign(S, 0.0);
+    const size_t per = policy_layer_doubles(policy, E, window);
+    for (int s : reuse) {
+      const int l = owner[s] / E, e = owner[s] % E;
+      const double* st = state + (size_t)l * per;
+      if (st[0] != 0.0)
+        keep[s] = keep_of(st, policy, E, window)[e];
+      else
+        keep[s] = policy == MOE_POLICY_MRS
+                      ? 0.0
+                      : history_keep(st, E, window, params, HistoryNorm{0.0, 0.0, 0.0, 0.0}, e);
+    }
+  }
+  std::sort(reuse.begin(), reuse.end(), [&](int a, int b) {
+    if (!keep.empty() && keep[a] != keep[b]) return keep[a] < keep[b];
+    return last_use[a] < last_use[b] || (last_use[a] == last_use[b] && a < b);
+  });
+  freeslots.insert(freeslots.end(), reuse.begin(), reuse.end());
+  int n = moe_prefetch_count(window_us, bw_gbs, expert_bytes, (int)freeslots.size());
+  if (n > (int)cand.size()) n = (int)cand.size();
+  for (int i = 0; i < n; ++i) {
+    const int e = cand[i], s = freeslots[i];
+    const int32_t old = owner[s];
+    if (old >= 0) lut[old] = -1;
+    row[e] = s;
+    owner[s] = layer * E + e;
+    last_use[s] = *clock;
+    fill_expert[i] = e;
+    fill_slot[i] = s;
+  }
+  *n_fills = n;
+  return MOE_OK;
 }
 
 extern "C" size_t moe_policy_state_doubles(int policy, int L, int E, int window) {

@@ -210,6 +210,33 @@ int moe_step_scores(const float* logits, int T, int E, float* scores, hipStream_
  */
 size_t moe_ffn_workspace_bytes(int T, int H, int F, int E, int k, int w_dtype);
 
+/* moe_ffn_workspace_offsets: where moe_expert_ffn keeps its intermediates
+ * inside the workspace, as byte offsets (0 where the weight format has none):
+ *   offs[0] h  [T*k, F] fp32: SwiGLU intermediate of sorted position p (row p)
+ *   offs[1] xq [T, H] int8 and offs[2] xs [T] fp32: int8 codes and row scales
+ *           of the tokens (MOE_INT4G128 weights)
+ *   offs[3] hq [T*k, F] int8 and offs[4] hs [T*k] fp32: the same for h
+ * With MOE_INT4G128 weights xq/xs/hq/hs are written by calls that run MFMA
+ * tiles or the MFMA GEMV (T >= 2); a one-token call quantises inside the GEMV
+ * workgroups' LDS and leaves them unwritten, and h holds fp32 values only for
+ * rows of computed groups. Host-only; offs is a host array of 5 entries.
+ * Returns MOE_EINVAL for bad sizes or formats. */
+int moe_ffn_workspace_offsets(int T, int H, int F, int E, int k, int w_dtype, size_t* offs);
+
+/* moe_quantize_rows_int8: the int8 activation rows that int4 weights meet
+ * (the int4 workload's W4A8 definition: per-row symmetric int8), as a stage
+ * of its own. For each row r of in [rows, K]:
+ *   s[r] = max_c |in[r,c]| / 127 (IEEE fp32 division), or 1 for a zero row
+ *   q[r,c] = clip(rint(in[r,c] / s[r]), -127, 127)   (round to nearest even)
+ * the rule moe_expert_ffn applies to the tokens and to the SwiGLU
+ * intermediate before each int4 projection.
+ *   in   [rows, K] in in_dtype (MOE_F32 or MOE_BF16), 16-byte aligned
+ *   q    [rows, K] int8 out; s [rows] fp32 out
+ * Requires K % 8 == 0, 8 <= K <= 8192; rows == 0 is a no-op. Enqueued on
+ * stream. */
+int moe_quantize_rows_int8(const void* in, int in_dtype, int rows, int K, int8_t* q, float* s,
+                           hipStream_t stream);
+
 /* moe_expert_ffn: grouped SwiGLU FFN of every routed expert group, reading the
  * expert's weights through the slot table (SeqMoE Mechanism; RapidMoE Eq. (7)):
  *   for each expert e with offsets[e] < offsets[e+1] and group_mask[e] != 0:
@@ -286,6 +313,22 @@ int slot_fill(void* pool_base, size_t slot_stride, int32_t slot,
               uint64_t* slot_tags, uint64_t tag, int32_t* err_word,
               hipStream_t fill_stream, hipStream_t compute_stream);
 
+/* slot_prefetch: the copy half of slot_fill, for a copy started before the
+ * expert is known to be needed (MoE-CORE summary page, Mechanism: the next
+ * layer's experts are predicted and copied ahead; SeqMoE summary page,
+ * Mechanism: a per-slot tag is the only synchronisation between a copy and
+ * its use):
+ *   fill_stream: copy bytes host_src -> pool_base + slot*slot_stride;
+ *                then slot_tags[slot] = tag
+ * The table is not touched: the caller commits later with slot_commit(tag),
+ * on the stream that will read the slot, after waiting for fill_stream. A
+ * later fill of the same slot with a newer tag makes that commit a refused,
+ * stale one (MOE_ERR_STALE_TAG), so a prefetch that lost its slot can never
+ * point the table at another expert's bytes. host_src must be page-locked
+ * (MOE_EINVAL otherwise). Arguments as in slot_fill. */
+int slot_prefetch(void* pool_base, size_t slot_stride, int32_t slot, const void* host_src,
+                  size_t bytes, uint64_t* slot_tags, uint64_t tag, hipStream_t fill_stream);
+
 /* slot_commit: the commit step of slot_fill alone, on one stream, for a copy
  * whose tag was written back by other means (e.g. a prefetcher). Same rule
  * and same error bit as above. */
@@ -319,6 +362,37 @@ int moe_plan_fills(int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clo
                    int32_t* wave_of, int32_t* is_hit,
                    int32_t* fill_expert, int32_t* fill_slot, int32_t* fill_wave,
                    int32_t* n_fills, int32_t* n_waves);
+
+/* ------------------------------------------------- miss prefetch (host) -
+ * moe_prefetch_count: how many experts a prefetch copy can hide (MoE-CORE
+ * summary page, Mechanism): floor(window_us * bw_gbs * 1000 / expert_bytes)
+ * in float64, where window_us = remaining compute of the current layer plus
+ * the attention of the next, minus the launch overhead (microseconds) and
+ * bw_gbs the host-to-device bandwidth (GB/s); capped by free_slots; 0 when
+ * the window or the bandwidth is not positive. */
+int moe_prefetch_count(double window_us, double bw_gbs, size_t expert_bytes, int free_slots);
+
+/* moe_plan_prefetch (host only): after the current step's plan, choose the
+ * experts of the next step's layer `layer` to copy ahead. The next layer's
+ * router evaluated on the current hidden state predicted the routed ids
+ * pred_ids [n_pred] and the routing scores pred_scores [E] (softmax
+ * probability averaged over the tokens). Candidates: the predicted experts not
+ * resident in `layer`, by score descending, ties to the lower id. Free slots:
+ * empty slots by id, then slots whose last use is before *clock (the current
+ * step did not use them) and that hold no predicted expert of `layer`, in the
+ * victim order of moe_plan_fills_policy. The first moe_prefetch_count(window,
+ * bw, expert_bytes, free) candidates (at most all) take the free slots in
+ * order: the tables move as for a fill, and the slot's last use becomes
+ * *clock. Outputs fill_expert/fill_slot [n_fills] (E entries suffice). The
+ * caller copies them (slot_prefetch) and commits each with slot_commit.
+ * Arguments otherwise as moe_plan_fills_policy; MOE_EINVAL for bad sizes, ids
+ * or parameters. */
+int moe_plan_prefetch(int policy, const double* state, int window, const double* params,
+                      int32_t* lut, int32_t* owner, int64_t* last_use, const int64_t* clock,
+                      int S, int L, int E, int layer, const int32_t* pred_ids, int n_pred,
+                      const float* pred_scores, double window_us, double bw_gbs,
+                      size_t expert_bytes, int32_t* fill_expert, int32_t* fill_slot,
+                      int32_t* n_fills);
 
 /* ----------------------------------------------- eviction policies (host) -
  * Which cached expert to evict when a miss needs a slot. LRU is the plan of

@@ -13,9 +13,10 @@
  *
  * Ownership: the caller owns the slot pool, the device tables, the pinned
  * host store, the shared-expert pool, the error word, the device workspace
- * (moe_ctx_workspace_bytes) and both streams; the context allocates only a
- * few KB of pinned host staging and its events, once, in moe_ctx_create, and
- * frees them in moe_ctx_destroy. A context is used by one host thread at a
+ * (moe_ctx_workspace_bytes) and both streams; the context allocates no device
+ * memory, only a few KB of pinned host staging and its events, once, in
+ * moe_ctx_create (and four events on the first staging enable), and frees them in
+ * moe_ctx_destroy. A context is used by one host thread at a
  * time. Status codes as in moe_offload.h.
  */
 #ifndef MOE_RUNTIME_H
@@ -29,8 +30,12 @@ extern "C" {
 
 typedef struct moe_layer_ctx moe_layer_ctx;
 
-/* moe_ctx_workspace_bytes: device workspace a context needs (0 on bad sizes). */
-size_t moe_ctx_workspace_bytes(int t_max, int H, int F, int E, int k, int w_dtype, int n_shared);
+/* moe_ctx_workspace_bytes: device workspace a context of these sizes needs (0 on
+ * bad sizes): the step's buffers, the expert FFN's workspace, and the tables of
+ * device orchestration (O(S + L*E)) and of full-layer staging (O(E)), so that the
+ * context allocates no device memory. L layers, S routed slots. */
+size_t moe_ctx_workspace_bytes(int t_max, int H, int F, int E, int k, int L, int S, int w_dtype,
+                               int n_shared);
 
 /* moe_ctx_create: context for a stack of L layers sharing one slot pool.
  *   t_max       largest token count of a step
@@ -152,8 +157,9 @@ int moe_ctx_set_split(moe_layer_ctx* ctx, int enable, float theta, const float* 
  * next layer (l + 1 mod L, or the next layer given to moe_ctx_forward_steps).
  * A buffer that already holds the layer is not reloaded. Staged steps leave
  * the decode cache (tables, recency, policy history, counters) untouched;
- * their stats are -1. Not with device orchestration (MOE_EINVAL). The context
- * allocates a [2E] device table and four events on the first enable. */
+ * their stats are -1. Not with device orchestration (MOE_EINVAL). The first
+ * enable writes the buffers' [2E] slot table into the workspace and creates four
+ * events. */
 int moe_ctx_set_staging(moe_layer_ctx* ctx, int enable, int threshold, int pool_slots);
 
 /* moe_ctx_stage_counters: out[0] staged steps, out[1] experts copied into the
@@ -176,8 +182,9 @@ int moe_ctx_stage_counters(moe_layer_ctx* ctx, int64_t* out);
  *     totals of moe_ctx_counters and the tables of moe_ctx_read_tables are
  *     read back from the device (a stream synchronisation).
  * Switching hands the tables over (host -> device: the slots' LRU order and
- * clock; device -> host: everything). The first switch to the device
- * allocates the device planner's state (a few KB per slot) once. */
+ * clock; device -> host: everything). The device planner's state sits in
+ * the workspace; the first switch to the device writes its weight set table
+ * there. */
 #define MOE_ORCH_HOST 0
 #define MOE_ORCH_DEVICE 1
 int moe_ctx_set_orchestration(moe_layer_ctx* ctx, int mode);

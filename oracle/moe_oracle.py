@@ -60,7 +60,8 @@ __all__ = [
     "SlotPool", "LruSlotPlanner", "Wave", "route", "moe_layer",
     "step_scores", "MinusRecentScore", "RoutingHistoryScore", "ScoredSlotPlanner",
     "round_bf16", "quantize_sym_g128", "resplit_expert", "critical_threshold",
-    "critical_experts", "swiglu_expert_split",
+    "critical_experts", "swiglu_expert_split", "prefetch_window", "prefetch_count",
+    "prefetch_candidates",
 ]
 
 
@@ -203,24 +204,24 @@ def swiglu_expert(x_rows, gate, up, down) -> np.ndarray:
     return h @ as_f64(down).T
 
 
+# the two signed 4-bit codes of each byte value: low nibble first; a nibble v
+# in [0, 16) stands for the two's-complement value (v ^ 8) - 8
+_NIBBLE_PAIRS = np.array([[((b & 15) ^ 8) - 8, ((b >> 4) ^ 8) - 8] for b in range(256)],
+                         dtype=np.int8)
+
+
 def decode_int4(codes) -> np.ndarray:
     """Packed signed 4-bit codes [rows, K/2] (even K in the low nibble) -> int8 [rows, K]."""
     b = _np(codes).astype(np.uint8)
-    lo = (b & 0x0F).astype(np.int16)
-    hi = (b >> 4).astype(np.int16)
-    lo = np.where(lo >= 8, lo - 16, lo)
-    hi = np.where(hi >= 8, hi - 16, hi)
-    out = np.empty((b.shape[0], b.shape[1] * 2), dtype=np.int8)
-    out[:, 0::2] = lo
-    out[:, 1::2] = hi
-    return out
+    return _NIBBLE_PAIRS[b].reshape(b.shape[0], b.shape[1] * 2)
 
 
 def dequant_int4g128(codes, scales) -> np.ndarray:
     """W_hat[n, c] = q[n, c] * s[n, c // 128] (exact in float64)."""
-    q = decode_int4(codes).astype(np.float64)
+    q = decode_int4(codes)
     s = as_f64(scales)
-    return q * np.repeat(s, 128, axis=1)
+    rows, K = q.shape
+    return (q.reshape(rows, K // 128, 128).astype(np.float64) * s[:, :, None]).reshape(rows, K)
 
 
 def quantize_rows_int8(a) -> tuple[np.ndarray, np.ndarray]:
@@ -255,7 +256,12 @@ def swiglu_expert_w4a8(x_rows, w: dict) -> np.ndarray:
     return hh @ dequant_int4g128(w["down_q"], w["down_s"]).T
 
 
-def expert_forward(x_rows, w: dict) -> np.ndarray:
+def expert_forward(x_rows, w: dict, critical: bool = True) -> np.ndarray:
+    """One expert on a block of rows, in the form its weights are stored: split
+    precision (at W^H when ``critical``, else W^L), int4 group-128 with int8
+    rows, or dense fp32/bf16 values."""
+    if "down_lq" in w:
+        return swiglu_expert_split(x_rows, w, critical)
     if "gate_q" in w:
         return swiglu_expert_w4a8(x_rows, w)
     return swiglu_expert(x_rows, w["gate"], w["up"], w["down"])
@@ -393,6 +399,60 @@ class LruSlotPlanner:
         for s in used:
             self.last_use[s] = self.clock
         return waves
+
+    def prefetch(self, layer: int, pred_ids, pred_scores, window_us: float, bw_gbs: float,
+                 expert_bytes: int) -> list[tuple[int, int]]:
+        """Prefetch for the next layer's step, after the current step's plan ([MoE-CORE]
+        Mechanism): the prefetch_candidates of `layer`, as many as prefetch_count allows,
+        go to free slots in the victim order: empty slots first, then slots the current
+        step did not use (last use before the clock) and that hold no predicted expert of
+        `layer`. A prefetched slot gets the current clock as its last use (it waits for
+        its step). Returns [(expert, slot)] in order."""
+        cand = prefetch_candidates(pred_ids, pred_scores, self.lut[layer])
+        pred = {int(e) for e in np.asarray(pred_ids).ravel()}
+        empty = [s for s in range(self.S) if self.owner[s] is None]
+        key = self._victim_key or (lambda s: (self.last_use[s], s))
+        reusable = sorted((s for s in range(self.S)
+                           if self.owner[s] is not None and self.last_use[s] < self.clock
+                           and not (self.owner[s][0] == layer and self.owner[s][1] in pred)),
+                          key=key)
+        free = empty + reusable
+        n = min(prefetch_count(window_us, bw_gbs, expert_bytes, len(free)), len(cand))
+        out = []
+        for e, s in zip(cand[:n], free[:n]):
+            self._assign(layer, e, s)
+            self.last_use[s] = self.clock
+            out.append((e, s))
+        return out
+
+
+# ------------------------------------------------------- miss prefetch ---
+def prefetch_window(t_remain_us: float, t_attn_us: float, t_launch_us: float) -> float:
+    """[MoE-CORE] Mechanism: the time a prefetch copy can hide, the remaining compute of
+    layer l plus the attention of layer l+1, minus the launch overhead (microseconds)."""
+    return t_remain_us + t_attn_us - t_launch_us
+
+
+def prefetch_count(window_us: float, bw_gbs: float, expert_bytes: int, free_slots: int) -> int:
+    """[MoE-CORE] Mechanism: as many experts as the window can hide at the host-to-device
+    bandwidth, floor(window * BW / expert bytes), further capped by the free slots; none
+    when the window is not positive. float64 in this order (microseconds, GB/s, bytes)."""
+    if not window_us > 0.0:
+        return 0
+    n = int(np.floor(window_us * bw_gbs * 1000.0 / float(expert_bytes)))
+    return max(0, min(n, free_slots))
+
+
+def prefetch_candidates(pred_ids, pred_scores, lut_row) -> list[int]:
+    """[MoE-CORE] Mechanism: the next layer's router evaluated on the current hidden state
+    predicts its routed set; the candidates are the predicted experts not resident, the
+    top predicted first. Readings: the predicted set is the union of the tokens' top-k;
+    "top" orders by the predicted routing score (the softmax probability averaged over the
+    step's tokens, float32 as given), ties to the lower id."""
+    sc = as_f32(pred_scores)
+    pred = sorted({int(e) for e in np.asarray(pred_ids).ravel()})
+    cand = [e for e in pred if lut_row[e] < 0]
+    return sorted(cand, key=lambda e: (-float(sc[e]), e))
 
 
 # --------------------------------------------------------- eviction scores ---
@@ -612,7 +672,8 @@ def swiglu_expert_split(x_rows, w: dict, critical: bool) -> np.ndarray:
 # ------------------------------------------------------------- full layer ---
 def moe_layer(x, w_router, bias, k: int, *, layer: int, pool: SlotPool,
               planner: LruSlotPlanner | None, weights_of_expert,
-              shared: list[dict] | None = None, renorm: bool = True) -> dict:
+              shared: list[dict] | None = None, renorm: bool = True,
+              scores=None, critical=None, rows=None) -> dict:
     """One routed-expert layer over the slot pool.
 
     route -> permute -> residency plan -> for each wave of the plan: the
@@ -626,17 +687,26 @@ def moe_layer(x, w_router, bias, k: int, *, layer: int, pool: SlotPool,
     Without a planner every routed expert must already be resident.
     ``weights_of_expert(e)`` returns the host-store weights of expert e of
     this layer (what a fill copies).
+
+    scores: the step's routing scores, handed to a scored planner's plan.
+    critical: for split-precision weights, the routed experts that run at high
+    precision ([RapidMoE] Algorithm 1; None = all); shared experts always do.
+    rows: token indices whose outputs are computed (None = all); the routing,
+    the permutation and the plan still cover every token, and the other rows
+    of ``y`` and ``out`` stay zero.
     """
     r = route(x, w_router, bias, k, renorm)
     ids = r["ids"]
     p = permute(ids, w_router.shape[0])
     if planner is not None:
-        waves = planner.plan(layer, p["distinct"])
+        waves = (planner.plan(layer, p["distinct"]) if scores is None
+                 else planner.plan(layer, p["distinct"], scores))
     else:
         waves = [Wave(compute=[int(e) for e in p["distinct"]])]
     x_rows = as_f32(x)  # exact for fp32 and bf16 tokens; each expert form converts further
     T = ids.shape[0]
     H = as_f64(w_router).shape[1]
+    keep = np.ones(T, dtype=bool) if rows is None else np.isin(np.arange(T), rows)
     y = np.zeros((T, k, H), dtype=np.float64)
     for wave in waves:
         for e, s in wave.fills:
@@ -644,11 +714,21 @@ def moe_layer(x, w_router, bias, k: int, *, layer: int, pool: SlotPool,
         for e in wave.compute:
             e = int(e)
             f = p["perm"][p["offsets"][e]:p["offsets"][e + 1]]
+            f = f[keep[f // k]]
+            if f.size == 0:
+                continue
             t_rows, j_rows = f // k, f % k
-            y[t_rows, j_rows] = expert_forward(x_rows[t_rows], pool.weights_of(layer, e))
+            hi = critical is None or e in critical
+            y[t_rows, j_rows] = expert_forward(x_rows[t_rows], pool.weights_of(layer, e), hi)
     if planner is not None and not np.array_equal(pool.lut, planner.lut):
         raise AssertionError("pool table differs from the planner's after the last wave")
-    y_sh = [expert_forward(x_rows, w) for w in (shared or [])]
+    sel = np.flatnonzero(keep)
+    y_sh = []
+    for w in shared or []:
+        ys = np.zeros((T, H), dtype=np.float64)
+        ys[sel] = expert_forward(x_rows[sel], w, True)
+        y_sh.append(ys)
     out = combine(y, r["weights"], y_sh)
+    out[~keep] = 0.0
     return dict(route=r, perm=p, waves=waves if planner is not None else [], y=y,
                 y_shared=y_sh, out=out)

@@ -312,3 +312,57 @@ def test_quantize_resplit_matches_oracle(lib, H, F, seed):
     assert ref["gate_s"][0, 0] == 0 and not ref["gate_q"][0, :128].any()
     assert ref["gate_s"][4, 0] == 2.0 ** -6
     assert list(ref["gate_q"][4, :3]) == [7, 2, -4]
+
+
+def test_prefetch_count_matches_oracle(lib):
+    rng = np.random.default_rng(31)
+    for _ in range(500):
+        w = float(rng.choice([-10.0, 0.0, rng.uniform(0, 3000)]))
+        bw = float(rng.uniform(1, 100))
+        eb = int(rng.integers(1, 400_000_000))
+        free = int(rng.integers(0, 20))
+        assert B.moe_prefetch_count(w, bw, eb, free) == O.prefetch_count(w, bw, eb, free)
+    assert B.moe_prefetch_count(1000.0, 50.0, 10_000_000, 8) == 5
+
+
+@pytest.mark.parametrize("kind", ["lru", "mrs", "history"])
+@pytest.mark.parametrize("S,L,E,kmax,seed", [(6, 2, 8, 2, 0), (20, 3, 16, 4, 1), (5, 4, 6, 3, 2)])
+def test_plan_prefetch_matches_oracle(lib, kind, S, L, E, kmax, seed):
+    """Steps of a stack: each layer's plan, then a prefetch for the next layer from a
+    predicted routing (random windows, including ones that hide nothing); the library's
+    tables and prefetch choices equal the oracle planner's at every step."""
+    rng = np.random.default_rng(300 + seed)
+    init = [(int(rng.integers(L)), int(e)) for e in rng.choice(E, size=min(S, E) - 1, replace=False)]
+    residency = (list(dict.fromkeys(init)) + [None] * S)[:S]
+    if kind == "lru":
+        ref, pol = O.LruSlotPlanner(S, L, E, residency), None
+    else:
+        pol_ref, pol = _policy_pair(kind, L, E, rng)
+        ref = O.ScoredSlotPlanner(S, L, E, pol_ref, residency)
+    lut, owner, last_use, clock = _lib_state(S, L, E, residency)
+    for step in range(120):
+        layer, nxt = step % L, (step + 1) % L
+        logits = rng.normal(size=(int(rng.integers(1, 4)), E)) * 2.0
+        ids = np.argsort(-logits, axis=1, kind="stable")[:, :int(rng.integers(1, kmax + 1))]
+        U = sorted({int(e) for e in ids.ravel()})
+        scores = O.step_scores(logits).astype(np.float32)
+        if kind == "lru":
+            ref.plan(layer, U)
+            B.moe_plan_fills(lut, owner, last_use, clock, S, L, E, layer, np.array(U))
+        else:
+            ref.plan(layer, U, scores)
+            pol.observe(layer, scores, np.array(U))
+            pol.plan(lut, owner, last_use, clock, S, layer, np.array(U))
+        plog = rng.normal(size=(int(rng.integers(1, 4)), E)) * 2.0
+        if step % 5 == 0:
+            plog[:, :E // 2] = plog[:, :1]  # tied predicted scores
+        pids = np.argsort(-plog, axis=1, kind="stable")[:, :kmax]
+        psc = O.step_scores(plog).astype(np.float32)
+        win = float(rng.choice([0.0, 150.0, 1e6]))
+        exp = ref.prefetch(nxt, pids, psc, win, 50.0, 9_437_184)
+        got = B.moe_plan_prefetch(pol, lut, owner, last_use, clock, S, L, E, nxt, pids, psc, win,
+                                  50.0, 9_437_184)
+        assert got == exp, step
+        assert lut.reshape(L, E).tolist() == ref.lut.tolist()
+        assert last_use.tolist() == ref.last_use and int(clock[0]) == ref.clock
+        assert owner.tolist() == [-1 if o is None else o[0] * E + o[1] for o in ref.owner]

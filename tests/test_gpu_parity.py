@@ -12,7 +12,8 @@ import oracle as O
 from expert_offload_routed_amd import binding as B
 from expert_offload_routed_amd import harness as Hn
 from expert_offload_routed_amd import workloads as W
-from gpu_common import TOL, check_routing, host_weights, oracle_expert, oracle_y_rows, rel_l2, say
+from gpu_common import (TOL, check_routing, host_weights, oracle_expert, oracle_y_rows, rel_l2,
+                        run_layer_case as _run_layer_case, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -302,95 +303,6 @@ def test_slot_fill_rejects_pageable_host_memory():
 
 
 # --------------------------------------------------------------- whole layer --
-def _run_layer_case(shape, slots, mode, Ts, layers_order=None, seed_steps=1, policy=None,
-                    device_plan=False, split=None, staging=None):
-    """Run steps through the harness and compare every step with the oracle.
-
-    policy = (kind, window, params): the runtime plans under that eviction policy and the
-    oracle's scored planner records the same step scores (the kernel's own, checked against
-    the oracle's softmax of the kernel's logits) before each plan.
-    device_plan: the runtime plans and fills on the GPU (device orchestration).
-    split = (theta, beta, gamma): split-precision routing; the oracle takes the critical set
-    from the kernel's own step scores (checked against its softmax) in float32.
-    staging = token threshold: steps of layers not wholly resident with T >= threshold run
-    from the full-layer staging buffers; the oracle's planner (the decode cache) skips them.
-    Returns the layer object."""
-    t_max = max(Ts)
-    residency = W.initial_residency(shape, slots, mode)
-    layer_obj = Hn.SlotCacheLayer(shape, slots, residency, t_max, staging=staging is not None)
-    if staging is not None:
-        layer_obj.ctx.set_staging(True, staging)
-    if device_plan:
-        layer_obj.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
-    if split is not None:
-        theta, beta, gamma = split
-        layer_obj.ctx.set_split(True, theta, beta, gamma)
-    n_hi = n_lo = 0
-    if policy is None:
-        planner = O.LruSlotPlanner(slots, shape.layers, shape.E, residency)
-    else:
-        kind, window, params = policy
-        layer_obj.ctx.set_policy(kind, window, params)
-        pol = (O.MinusRecentScore(shape.layers, shape.E, window) if kind == B.MOE_POLICY_MRS else
-               O.RoutingHistoryScore(shape.layers, shape.E, window, weights=params[:4], lam=params[4]))
-        planner = O.ScoredSlotPlanner(slots, shape.layers, shape.E, pol, residency)
-    order = layers_order or [0]
-    for step, T in enumerate(Ts):
-        for layer in order:
-            say(f"layer {shape.name} step={step} layer={layer} T={T}")
-            x = W.tokens(shape, T, layer=layer, step=step, device=_dev())
-            stats = Hn.StepStats()
-            out = layer_obj.forward(x, layer=layer, stats=stats)
-            torch.cuda.synchronize()
-            assert layer_obj.err.item() == 0
-            wr, b = layer_obj.routers[layer]
-            o = layer_obj.outputs(T)
-            check_routing(x, wr, b, shape.k, o["logits"], o["ids"], o["topk_w"])
-            ids = o["ids"].cpu().numpy()
-            pr = O.permute(ids, shape.E)
-            assert o["perm"].cpu().numpy().tolist() == pr["perm"].tolist()
-            assert o["inv"].cpu().numpy().tolist() == pr["inv"].tolist()
-            if policy is not None or split is not None:
-                sc = layer_obj.ctx.step_scores()
-                np.testing.assert_allclose(sc, O.step_scores(o["logits"].cpu().numpy()), rtol=2e-6, atol=1e-7)
-            n_res = int(np.sum(planner.lut[layer] >= 0))
-            staged = (staging is not None and n_res < shape.E
-                      and T >= (staging if staging >= 0 else n_res // shape.k))
-            if staged:
-                pass  # the decode cache is not touched
-            elif policy is None:
-                planner.plan(layer, pr["distinct"])
-            else:
-                planner.plan(layer, pr["distinct"], sc)
-            crit = None
-            if split is not None:
-                th = O.critical_threshold(theta, 1.0 if beta is None else beta[layer], "decode", gamma)
-                crit = set(O.critical_experts(sc, pr["distinct"], th))
-                n_hi += len(crit)
-                n_lo += len(pr["distinct"]) - len(crit)
-            lut_h, owner_h, last_use_h, clock_h = layer_obj.tables()
-            assert layer_obj.lut.cpu().numpy().reshape(shape.layers, shape.E).tolist() == planner.lut.tolist()
-            assert lut_h.reshape(shape.layers, shape.E).tolist() == planner.lut.tolist()
-            assert last_use_h.tolist() == planner.last_use and clock_h == planner.clock
-            # oracle output on the kernel's selection, oracle weights from its own logits
-            ref_logits = O.router_logits(x, wr, b)
-            wts = O.gate_weights(ref_logits, ids)
-            yr = oracle_y_rows(shape, x, ids, pr["perm"], pr["offsets"], layer, pr["distinct"],
-                               critical=crit)
-            y_assign = yr[pr["inv"]].reshape(T, shape.k, shape.H)
-            x32 = O.as_f32(x)
-            ysh = [oracle_expert(shape, x32, j, True, shared=True) for j in range(shape.n_shared)]
-            ref = O.combine(y_assign, wts, ysh)
-            r = rel_l2(out.float().cpu().numpy(), ref)
-            cnt = layer_obj.counters()
-            say(f"  rel L2 {r:.3e}; totals so far {cnt}" +
-                (f"; critical {sorted(crit)}" if crit is not None else ""))
-            assert r <= TOL[shape.wfmt]
-    if split is not None:
-        assert n_hi > 0 and n_lo > 0, (n_hi, n_lo)  # both precisions were exercised
-    return layer_obj
-
-
 def test_layer_tiny_fp32_identity():
     _run_layer_case(TINY, 8, "identity", [16, 16])
 
@@ -602,8 +514,9 @@ def test_layer_int4_shared_expert_misses():
 
 
 def test_layer_all_resident_decode_bf16_shared():
-    """Every expert resident (the front end plans the FFN; decode steps combine inside the
-    second pass), with shared experts; T > 4 takes the separate combine."""
+    """Every expert resident, with shared experts: decode steps of 1 to 8 tokens, whose
+    routing front end (one launch up to 4 tokens, logits then one selecting workgroup
+    beyond) writes the FFN's work list itself, so the FFN call runs without its plan."""
     shape = W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), E=16, k=6, H=256, F=256)
     _run_layer_case(shape, 16, "zipf_rank", [1, 2, 4, 3, 8, 1])
 
@@ -616,39 +529,6 @@ def test_layer_all_resident_decode_int4_shared():
 def test_layer_mixtral_full_size_decode():
     """Full Mixtral-shaped layer (H=4096, F=14336), 4 of 8 experts resident, decode T=1 and T=8."""
     _run_layer_case(MIX, 4, "random", [1, 8])
-
-
-def test_layer_mixtral_full_size_prefill_sampled():
-    """Full Mixtral-shaped layer, prefill of 512 tokens (MFMA tiles), all experts resident;
-    the oracle checks a sample of tokens spread over every expert group."""
-    shape = MIX
-    T = 512
-    residency = W.initial_residency(shape, 8, "random")
-    layer = Hn.SlotCacheLayer(shape, 8, residency, T)
-    x = W.tokens(shape, T, device=_dev())
-    out = layer.forward(x)
-    torch.cuda.synchronize()
-    assert layer.err.item() == 0
-    o = layer.outputs(T)
-    wr, b = layer.routers[0]
-    under, _ = check_routing(x, wr, b, shape.k, o["logits"], o["ids"], o["topk_w"])
-    ids = o["ids"].cpu().numpy()
-    ref_logits = O.router_logits(x, wr, b)
-    wts = O.gate_weights(ref_logits, ids)
-    sample = sorted({0, 1, 2, 63, 64, 65, 127, 128, 200, 255, 256, 300, 383, 384, 450, 510, 511})
-    experts = {}
-    x32 = O.as_f32(x)
-    ref = np.zeros((len(sample), shape.H))
-    for i, t in enumerate(sample):
-        for j in range(shape.k):
-            e = int(ids[t, j])
-            if e not in experts:
-                experts[e] = host_weights(shape, e)
-            ref[i] += wts[t, j] * O.expert_forward(x32[t:t + 1], experts[e])[0]
-    got = out.float().cpu().numpy()[sample]
-    r = rel_l2(got, ref)
-    say(f"  prefill sampled rel L2 {r:.3e}, tokens under margin {under}")
-    assert r <= TOL[shape.wfmt]
 
 
 def test_forward_steps_matches_single_calls():
@@ -674,3 +554,39 @@ def test_forward_steps_matches_single_calls():
     for u, v in zip(ta, tb):
         assert np.array_equal(np.asarray(u), np.asarray(v))
     assert a.err.item() == 0 and b.err.item() == 0
+
+
+def test_prefetch_commit_overtaken_by_a_demand_fill_is_refused():
+    """A prefetch copies expert A into slot 1 (tag 5) and is committed late; meanwhile a demand
+    fill puts expert B into the same slot (tag 6, committed). The late commit of A finds tag 6
+    and is refused: the table keeps B, A stays absent and the slot holds B's bytes. The order
+    is forced from the host (each call completes before the next is issued)."""
+    shape = W.reduced(MIX, E=6, k=2, H=256, F=128)
+    store = Hn.ExpertStore(shape)
+    S, E = 3, 6
+    pool = torch.zeros(S * store.stride, dtype=torch.uint8, device=_dev())
+    lut = torch.full((E,), -1, dtype=torch.int32, device=_dev())
+    owner = torch.full((S,), -1, dtype=torch.int32, device=_dev())
+    tags = torch.zeros(S, dtype=torch.int64, device=_dev())
+    err = torch.zeros(1, dtype=torch.int32, device=_dev())
+    fs = torch.cuda.Stream()
+    cs = torch.cuda.current_stream()
+    A, B_ = 4, 2
+    B.slot_prefetch(pool, store.stride, 1, store.host[A], store.stride, tags, 5, fs)
+    torch.cuda.synchronize()
+    assert tags.cpu().tolist() == [0, 5, 0] and lut.cpu().tolist() == [-1] * E  # copied, not committed
+    B.slot_fill(pool, store.stride, 1, store.host[B_], store.stride, lut, B_, owner, tags, 6, err, fs, cs)
+    torch.cuda.synchronize()
+    B.slot_commit(lut, A, owner, 1, tags, 5, err)  # the prefetch's commit, now stale
+    torch.cuda.synchronize()
+    assert err.item() == B.MOE_ERR_STALE_TAG
+    assert lut.cpu().tolist() == [-1, -1, 1, -1, -1, -1] and owner.cpu().tolist() == [-1, B_, -1]
+    assert torch.equal(pool[store.stride:2 * store.stride].cpu(), store.host[B_])
+    # an uncontested prefetch commits normally
+    err.zero_()
+    B.slot_prefetch(pool, store.stride, 0, store.host[A], store.stride, tags, 7, fs)
+    fs.synchronize()
+    B.slot_commit(lut, A, owner, 0, tags, 7, err)
+    torch.cuda.synchronize()
+    assert err.item() == 0 and lut.cpu().tolist()[A] == 0
+    assert torch.equal(pool[:store.stride].cpu(), store.host[A])

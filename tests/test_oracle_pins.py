@@ -14,6 +14,7 @@ import scipy.special
 import torch
 import torch.nn.functional as Fnn
 
+import hand_cases as HC
 import oracle as O
 from expert_offload_routed_amd import workloads as W
 
@@ -217,45 +218,16 @@ def test_int8_rows_half_steps_round_to_even():
     assert q.tolist() == [[127, 2, 2, -2, 0, -2, 4, 0]]
 
 
-def _nibbles(codes) -> np.ndarray:
-    """Signed codes [rows, K] -> packed bytes [rows, K/2], even K in the low nibble."""
-    c = np.asarray(codes, dtype=np.int64) & 0xF
-    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
-
-
-def test_w4a8_expert_exposes_requantised_h_by_hand():
-    # One group (H = F = 128). Gate and up read only input 1; down is the identity,
-    # so y = h_hat, the int8 requantisation of h = SiLU(g) * u, can be read off.
-    # Token row 0: x = [127, 64, 0...] -> s_x = 1, x_hat[1] = 64, g = 64 (SiLU(64) = 64
-    # exactly in float64), u[n] = 64 * d_n * s_n, so h[n] = 4096 * d_n * s_n.
-    # Row 1 is row 0 doubled: s_x = 2, g = 128, h = 4 * h_row0, s_h = 4.
-    H = F = 128
-    d = np.zeros(F, np.int64)
-    su = np.full(F, 2.0 ** -13)
-    for n, (dn, sn) in enumerate([(1, 127 * 2.0 ** -12), (5, 2.0 ** -13), (7, 2.0 ** -13),
-                                  (-5, 2.0 ** -13), (1, 253 * 2.0 ** -13), (1, 2.0 ** -13),
-                                  (3, 2.0 ** -13), (-3, 2.0 ** -13), (-8, 2.0 ** -12),
-                                  (7, 2.0 ** -14)]):
-        d[n], su[n] = dn, sn
-    # h row 0:  127, 2.5, 3.5, -2.5, 126.5, 0.5, 1.5, -1.5, -8, 1.75, 0, ...
-    # absmax 127 -> s_h = 1; rint to even: 127, 2, 4, -2, 126, 0, 2, -2, -8, 2, 0, ...
-    gate_codes = np.zeros((F, H), np.int64)
-    gate_codes[:, 1] = 1
-    up_codes = np.zeros((F, H), np.int64)
-    up_codes[:, 1] = d
-    down_codes = np.eye(H, F, dtype=np.int64)
-    w = {"gate_q": _nibbles(gate_codes), "gate_s": torch.ones(F, 1, dtype=torch.bfloat16),
-         "up_q": _nibbles(up_codes), "up_s": torch.tensor(su[:, None], dtype=torch.bfloat16),
-         "down_q": _nibbles(down_codes), "down_s": torch.ones(H, 1, dtype=torch.bfloat16)}
-    assert torch.tensor(su, dtype=torch.bfloat16).double().numpy().tolist() == su.tolist()
-    x = np.zeros((2, H), np.float32)
-    x[0, :2] = [127.0, 64.0]
-    x[1, :2] = [254.0, 128.0]
-    y = O.swiglu_expert_w4a8(x, w)
-    want = np.zeros(H)
-    want[:10] = [127, 2, 4, -2, 126, 0, 2, -2, -8, 2]
-    assert y[0].tolist() == want.tolist()
-    assert y[1].tolist() == (4 * want).tolist()
+@pytest.mark.parametrize("H,F", [(128, 128), (512, 256)])
+def test_w4a8_expert_exposes_requantised_h_by_hand(H, F):
+    # tests/hand_cases.py: gate and up read single inputs, down is the identity, so
+    # y = h_hat, the int8 requantisation of h, and the values are worked out by hand there
+    # (half steps of x and of h round to even; one scale per row).
+    w = HC.w4a8_expert(H, F)
+    y = O.swiglu_expert_w4a8(HC.tokens(4, H), w)
+    assert y[0, :14].tolist() == [127, 2, 4, -2, 126, 0, 2, -2, -8, 2, 2, 4, -2, 2]
+    assert y.tolist() == HC.expected_y(4, H, F).tolist()
+    assert y[1].tolist() == (4 * y[0]).tolist()
 
 
 # ---------------------------------------------------------------- combine ---
@@ -275,7 +247,7 @@ def test_combine_linearity_and_zero_weight_poison():
 
 
 # ---------------------------------------------------------- full layer ------
-def _tiny_layer(lut_perm, E=8, k=2, H=64, F=96, T=12):
+def _tiny_layer(lut_perm, E=8, k=2, H=64, F=96, T=12, **kw):
     sh = W.reduced(W.shape_of("tiny_e8k2_h256_f512_fp32"), E=E, k=k, H=H, F=F)
     x = W.tokens(sh, T)
     wr, b = W.router(sh)
@@ -284,7 +256,7 @@ def _tiny_layer(lut_perm, E=8, k=2, H=64, F=96, T=12):
     for e in range(E):
         pool.commit(lut_perm[e], 0, e, experts[e])
     return O.moe_layer(x, wr, b, k, layer=0, pool=pool, planner=None,
-                       weights_of_expert=lambda e: experts[e]), experts, x, wr, b
+                       weights_of_expert=lambda e: experts[e], **kw), experts, x, wr, b
 
 
 def test_slot_relabel_invariance():
@@ -378,6 +350,36 @@ def test_layer_more_routed_than_slots_equals_direct_indexing(S, T, resident):
         s = pool.lut[0, e]
         if s >= 0:
             assert pool.content[s] is experts[e]
+
+
+def test_layer_sampled_rows_are_the_full_rows():
+    full, *_ = _tiny_layer(list(range(8)), T=12)
+    rows = [0, 5, 11]
+    part, *_ = _tiny_layer(list(range(8)), T=12, rows=rows)
+    assert np.array_equal(part["out"][rows], full["out"][rows])
+    assert not np.any(part["out"][[t for t in range(12) if t not in rows]])
+    assert np.array_equal(part["route"]["ids"], full["route"]["ids"])
+
+
+def test_layer_critical_set_picks_the_precision_per_expert():
+    sh = W.reduced(W.shape_of("dsv3_e256k8s1_h7168_f2048_int4"), E=4, k=2, H=256, F=128,
+                   wfmt="int4g128_resplit", zipf_s=None)
+    g = np.random.default_rng(21)
+    masters = [[g.normal(size=s) * 0.02 for s in ((128, 256), (128, 256), (256, 128))] for _ in range(4)]
+    experts = [O.resplit_expert(*m) for m in masters]
+    x = W.tokens(sh, 6)
+    wr, b = W.router(sh)
+    pool = O.SlotPool(4, 1, 4)
+    for e in range(4):
+        pool.commit(e, 0, e, experts[e])
+    crit = {1, 3}
+    res = O.moe_layer(x, wr, b, 2, layer=0, pool=pool, planner=None,
+                      weights_of_expert=lambda e: experts[e], critical=crit)
+    ids, wts = res["route"]["ids"], res["route"]["weights"]
+    for t in range(6):
+        want = sum(wts[t, j] * O.swiglu_expert_split(O.as_f32(x)[t:t + 1], experts[ids[t, j]],
+                                                     int(ids[t, j]) in crit)[0] for j in range(2))
+        np.testing.assert_allclose(res["out"][t], want, rtol=1e-13, atol=1e-15)
 
 
 # ------------------------------------------------------- LRU slot planner ---
@@ -653,3 +655,43 @@ def test_split_low_path_is_the_int4_expert_and_high_path_closer_to_dense():
     high = O.swiglu_expert_split(x, w, critical=True)
     r = lambda a: np.linalg.norm(a - dense) / np.linalg.norm(dense)
     assert r(high) < r(low) / 2
+
+
+# ----------------------------------------------------------- miss prefetch ---
+def test_prefetch_count_by_hand():
+    # 1000 us at 50 GB/s moves 50 MB: five 9.437184 MB experts, capped by 3 free slots
+    w = O.prefetch_window(t_remain_us=300.0, t_attn_us=750.0, t_launch_us=50.0)
+    assert w == 1000.0
+    assert O.prefetch_count(w, 50.0, 9437184, 8) == 5
+    assert O.prefetch_count(w, 50.0, 9437184, 3) == 3
+    assert O.prefetch_count(w, 50.0, 10_000_000, 8) == 5   # exactly 5.0 experts
+    assert O.prefetch_count(w, 50.0, 10_000_001, 8) == 4
+    assert O.prefetch_count(0.0, 50.0, 1, 8) == 0
+    assert O.prefetch_count(O.prefetch_window(10.0, 0.0, 20.0), 50.0, 1, 8) == 0  # negative window
+
+
+def test_prefetch_candidates_by_hand():
+    lut_row = np.array([0, -1, -1, 3, -1, -1])
+    scores = np.array([0.9, 0.1, 0.3, 0.8, 0.3, 0.05], np.float32)
+    # predicted set {0, 1, 2, 3, 4}; resident 0 and 3; the rest by score, tie 2/4 to the lower id
+    assert O.prefetch_candidates([[0, 2], [4, 1], [3, 2]], scores, lut_row) == [2, 4, 1]
+
+
+def test_planner_prefetch_hand_trace():
+    # 4 slots, 2 layers of 6 experts. Slots 0, 1 hold layer 0's experts 0, 1; slots 2, 3 hold
+    # layer 1's experts 2 and 5.
+    p = O.LruSlotPlanner(4, 2, 6, residency=[(0, 0), (0, 1), (1, 2), (1, 5)])
+    p.plan(0, [0, 1])  # the current step (layer 0) uses slots 0 and 1 at clock 1
+    scores = np.array([0.0, 0.0, 0.3, 0.5, 0.2, 0.0], np.float32)
+    # layer 1 predicted {2, 3, 4}: 2 is resident; candidates 3 (0.5), 4 (0.2). Free slots: not
+    # used at clock 1 and not holding a predicted expert of layer 1: slot 3 only.
+    got = p.prefetch(1, [[2, 3], [3, 4]], scores, window_us=1000.0, bw_gbs=50.0, expert_bytes=1000)
+    assert got == [(3, 3)]
+    assert p.lut[1].tolist() == [-1, -1, 2, 3, -1, -1] and p.owner[3] == (1, 3)
+    assert p.last_use == [1, 1, 0, 1]
+    # a window that hides nothing prefetches nothing
+    q = O.LruSlotPlanner(4, 2, 6, residency=[(0, 0), (0, 1), None, (1, 5)])
+    q.plan(0, [0, 1])
+    assert q.prefetch(1, [[2, 3]], scores, 0.0, 50.0, 1000) == []
+    # an empty slot comes first, then the least recently used free slot
+    assert q.prefetch(1, [[2, 3]], scores, 1000.0, 50.0, 1000) == [(3, 2), (2, 3)]
