@@ -96,15 +96,23 @@ def _run(layers, batches, out, timing):
     return dt, cnt, ms, n
 
 
-def make_batches(shape, T, steps):
-    """steps x layers token batches: independent draws, or AR(1) per layer for a stack."""
+def make_batches(shape, T, steps, layer_rho=None):
+    """steps x layers token batches: independent draws, or AR(1) per layer for a stack.
+
+    layer_rho (stack only): chain the layers' inputs as a stand-in for a residual stream,
+    x[l+1] = rho x[l] + sqrt(1 - rho^2) e[l+1], where e[l] is layer l's own AR(1) input, so
+    that layer l's tokens carry information about layer l+1's routing."""
     if shape.layers == 1:
         return [[(0, W.tokens(shape, T, step=i, device="cuda"))] for i in range(steps)]
     seqs = [W.token_sequence(shape, T, steps, layer=l, device="cuda") for l in range(shape.layers)]
+    if layer_rho is not None:
+        c = float(np.sqrt(1.0 - layer_rho * layer_rho))
+        for l in range(1, shape.layers):
+            seqs[l] = (layer_rho * seqs[l - 1].float() + c * seqs[l].float()).to(seqs[l].dtype)
     return [[(l, seqs[l][i]) for l in range(shape.layers)] for i in range(steps)]
 
 
-def timed(layers, shape, T, steps, warmup, label, ffn_timing=False):
+def timed(layers, shape, T, steps, warmup, label, ffn_timing=False, layer_rho=None):
     """Warm up, then time exactly ``steps`` steps between two device synchronisations.
 
     layers: one layer object, or replicas of it (each its own slot pool holding the
@@ -114,7 +122,7 @@ def timed(layers, shape, T, steps, warmup, label, ffn_timing=False):
     fill waves, shared experts); the headline rate comes from the pass without events.
     """
     layers = layers if isinstance(layers, (list, tuple)) else [layers]
-    batches = make_batches(shape, T, steps + warmup)
+    batches = make_batches(shape, T, steps + warmup, layer_rho)
     out = torch.empty(T, shape.H, dtype=layers[0].out_dtype, device="cuda")
     _run(layers, batches[:warmup], out, False)
     dt, cnt, _, _ = _run(layers, batches[warmup:], out, False)
@@ -170,7 +178,7 @@ def recorded_traffic(*keys):
 
 # the sources the expert-FFN kernels are compiled from (routing, runtime and combine excluded)
 FFN_SOURCES = ("common.h", "ffn_internal.h", "ffn.hip", "ffn_gemv.h", "tile_gemv.h", "gemm.hip",
-               "skinny.hip", "ffn_int4.hip")
+               "skinny.hip", "ffn_int4.hip", "decode_int4.hip")
 
 
 def ffn_sources_sha1() -> str:
@@ -472,6 +480,36 @@ def workload_report(name, K, Wm, quick=False, policies=("lru", "lru_device")):
     return head, res
 
 
+def prefetch_case(shape, cfg, store, S, T, steps, warmup, t_remain_us=20.0, t_launch_us=5.0,
+                  bw_gbs=55.0, t_attn_list=(0.0, 200.0, 1000.0)):
+    """Stack steps through the workload's own cache (S slots), without and with the miss
+    prefetch of the next layer (MoE-CORE summary page, Mechanism), for attention times the
+    layer itself does not have (the window is t_remain + t_attn - t_launch; the step still
+    pays the copies, since no attention runs here to hide them)."""
+    res = {}
+    for rho, t_attn in [(r_, t_) for r_ in (None, 0.9) for t_ in (None,) + tuple(t_attn_list)]:
+        lay = Hn.SlotCacheLayer(shape, S, W.initial_residency(shape, S, cfg["residency"]), t_max=T,
+                                store=store)
+        if t_attn is not None:
+            lay.ctx.set_prefetch(True, t_remain_us, t_attn, t_launch_us, bw_gbs)
+        p0 = lay.ctx.prefetch_counters()
+        label = ("no prefetch" if t_attn is None else f"prefetch, t_attn = {t_attn:g} us") + \
+            ("" if rho is None else f", layer inputs chained (rho {rho:g})")
+        r = timed(lay, shape, T, steps, warmup, f"T={T}, {S} slots, {label}", layer_rho=rho)
+        p1 = lay.ctx.prefetch_counters()
+        r["prefetched_per_step"] = (p1["prefetched"] - p0["prefetched"]) / (steps + warmup)
+        r["prefetch_used_per_step"] = (p1["prefetch_used"] - p0["prefetch_used"]) / (steps + warmup)
+        if t_attn is not None:
+            r["window_us"] = t_remain_us + t_attn - t_launch_us
+        print(f"# {label}: prefetched/step {r['prefetched_per_step']:.2f}, used/step "
+              f"{r['prefetch_used_per_step']:.2f}", file=sys.stderr, flush=True)
+        res[("none" if t_attn is None else f"t_attn_{t_attn:g}us")
+            + ("" if rho is None else f"_chained{rho:g}")] = r
+        del lay
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,7 +525,9 @@ def main():
                          "split (split-precision experts: all low, split, all high; the "
                          "workload's shape with split-precision slots and 16 distinct weight "
                          "sets), staging (prefill through the workload's cache with and without "
-                         "full-layer staging), T<n> (hit path at n tokens), calib_copy")
+                         "full-layer staging), prefetch (stack steps through the workload's cache "
+                         "with and without the next layer's miss prefetch), T<n> (hit path at n "
+                         "tokens), calib_copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU form of "
@@ -506,6 +546,10 @@ def main():
         store = Hn.ExpertStore(shape)
         for T in ([256] if shape.layers > 1 else [max(plan["hit"])]):
             staging_case(shape, cfg, store, S, T, K, Wm)
+        return
+    if args.case == "prefetch":
+        S, T = plan["miss"][0]
+        prefetch_case(shape, cfg, Hn.ExpertStore(shape), S, T, K, Wm)
         return
     if args.case == "split":
         # fp32 masters quantised by the library; 16 weight sets back the E slots (each slot

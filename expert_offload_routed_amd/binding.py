@@ -64,6 +64,9 @@ _SIGNATURES = {
     "moe_ctx_read_tables": (_i32, [_vp, _vp, _vp, _vp, _vp]),
     "moe_ctx_outputs": (_i32, [_vp] + [ctypes.POINTER(_vp)] * 6),
     "moe_ctx_set_timing": (_i32, [_vp, _i32]),
+    "moe_ctx_set_prefetch": (_i32, [_vp, _i32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                    ctypes.c_double]),
+    "moe_ctx_prefetch_counters": (_i32, [_vp, _vp]),
     "moe_ctx_set_policy": (_i32, [_vp, _i32, _i32, _vp]),
     "moe_ctx_set_orchestration": (_i32, [_vp, _i32]),
     "moe_ctx_step_scores": (_i32, [_vp, _vp]),
@@ -517,6 +520,15 @@ class LayerContext:
         c = np.zeros(4, np.int64)
         _call("moe_ctx_counters", self.handle, _host(c))
         return dict(distinct=int(c[0]), hits=int(c[1]), fills=int(c[2]), waves=int(c[3]))
+
+    def set_prefetch(self, on: bool, t_remain_us: float = 0.0, t_attn_us: float = 0.0,
+                     t_launch_us: float = 0.0, bw_gbs: float = 1.0) -> None:
+        _call("moe_ctx_set_prefetch", self.handle, int(on), t_remain_us, t_attn_us, t_launch_us, bw_gbs)
+
+    def prefetch_counters(self) -> dict:
+        out = np.zeros(2, np.int64)
+        _call("moe_ctx_prefetch_counters", self.handle, _host(out))
+        return {"prefetched": int(out[0]), "prefetch_used": int(out[1])}
 
     def set_timing(self, on: bool) -> None:
         _call("moe_ctx_set_timing", self.handle, int(on))

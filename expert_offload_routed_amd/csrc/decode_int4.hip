@@ -1,0 +1,260 @@
+// One-token int4 expert passes: every row block of the call in one even share
+// per workgroup.
+//
+// With one token a pass is a GEMV per routed expert over its tile-major int4
+// weights (1 KB chunks of 32 rows x 64 codes; RapidMoE Eq. (7) through the
+// slot table of the SeqMoE summary page). Work units of whole row-block pairs
+// leave the pass with a ragged last round whenever their count is not a
+// multiple of the resident workgroups (576 units on 256 workgroups: a third
+// round on a quarter of them). Here the flat list of the call's row blocks,
+// in (group, row block) order, is cut into one contiguous share per resident
+// workgroup (equal to within one row block), and:
+//   * wave j of the 16 takes the j-th sixteenth of the K chunks of every row
+//     block of the share and streams them in one loop, kDecP chunks in flight
+//     per lane, with no barrier until the share is done;
+//   * the share's group scales (32 rows x K/128 bf16 per row block, contiguous
+//     in the slot) are copied to LDS first, with the activation rows;
+//   * each wave keeps one partial per (row block, row) in LDS; one barrier,
+//     then each row block is summed over the 16 waves in a fixed order and
+//     finished (activation scale, SwiGLU epilogue), so the result does not
+//     depend on timing.
+// Numerics are those of the int4 GEMV: per chunk the exact int32 dot of 16 q
+// with the int8 row, times the group scale / 16, accumulated in fp32.
+#include "common.h"
+#include "ffn_internal.h"
+#include "tile_gemv.h"
+
+namespace {
+
+constexpr int kDecNW = 16;  // waves per workgroup
+constexpr int kDecP = 8;    // chunks in flight per lane
+
+// SWIGLU (gate/up pass): one token row for every group (row perm[p] / k of the bf16
+// tokens; T = 1), out = h (fp32, row p, column n of rows 2n, 2n+1).
+// Otherwise (down pass): row p of the fp32 h for each group; out = y (fp32).
+template <bool SWIGLU, int MAXRB>
+__global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
+    const void* __restrict__ raw, const int32_t* __restrict__ perm, int k,
+    const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+    const char* __restrict__ pool, size_t stride, size_t off_codes, size_t off_scales, int R,
+    int K, int out_ld, float* __restrict__ out) {
+  // dynamic LDS: activation rows [SWIGLU ? 1 : n_items][K] int8, then the share's scales
+  // [MAXRB][32][K/128] bf16
+  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+  __shared__ float act_s[kStreamMaxItems];
+  __shared__ float wmax[16];
+  __shared__ float red[kDecNW][MAXRB][32];
+  const int n_items = n_items_p[0];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int rbi = R / 32, nkc = K / 64, G = K / 128;
+  const int total_rb = n_items * rbi;
+  const int b0 = (int)((long long)total_rb * blockIdx.x / gridDim.x);
+  const int b1 = (int)((long long)total_rb * (blockIdx.x + 1) / gridDim.x);
+  const int nrb = b1 - b0;  // <= MAXRB (the launch checks)
+  const size_t act_bytes = (size_t)(SWIGLU ? 1 : n_items) * K;
+  int8_t* act_q = lds;
+  uint16_t* sc_lds = reinterpret_cast<uint16_t*>(lds + ((act_bytes + 15) & ~(size_t)15));
+  // this wave's K slice of every row block of the share, as one stream of chunks walked by
+  // two cursors (the loads kDecP chunks ahead of the sums); all cursor state is uniform
+  const int c0 = nkc * wave / kDecNW, c1 = nkc * (wave + 1) / kDecNW;
+  const int nq = nrb * (c1 - c0);
+  const int kh = 16 * (lane >> 5);
+  struct Cursor {
+    int r, c, item;
+    const char* base;  // the row block's first chunk, this lane's 16 bytes
+  };
+  auto at_block = [&](Cursor& u, int r) {
+    const int b = b0 + r, item = b / rbi, rb = b - item * rbi;
+    u.r = r;
+    u.c = c0;
+    u.item = item;
+    u.base = pool + (size_t)items[item].slot * stride + off_codes + (size_t)rb * nkc * 1024 + lane * 16;
+  };
+  // the next chunk; a load cursor past the share stays on its last chunk (loaded again, unused)
+  auto advance = [&](Cursor& u) {
+    if (u.c + 1 < c1) {
+      ++u.c;
+    } else if (u.r + 1 < nrb) {
+      at_block(u, u.r + 1);
+    }
+  };
+  float acc = 0.f;
+  Cursor sum_at{}, load_at{};
+  // the partial of row block r (after the K halves of a row meet) into LDS
+  auto flush = [&](int r) {
+    const float v = acc + __shfl_xor(acc, 32, 64);
+    if (lane < 32) red[wave][r][lane] = v;
+    acc = 0.f;
+  };
+  auto consume = [&](const u32x4& wv) {
+    const int8_t* ap = act_q + (SWIGLU ? 0 : (size_t)sum_at.item * K) + (size_t)sum_at.c * 64 + kh;
+    const u32x4 a0 = ld16(ap), a1 = ld16(ap + 32);
+    const uint16_t sraw = sc_lds[((size_t)sum_at.r * 32 + (lane & 31)) * G + (sum_at.c >> 1)];
+    acc = fmaf((float)tgemv::dot64_int4(wv, a0, a1), bf16_to_f32(sraw) * 0.0625f, acc);
+    if (sum_at.c + 1 == c1) flush(sum_at.r);  // uniform: the row block's slice is done
+    advance(sum_at);
+  };
+  // the first kDecP chunks go out before the staging below, so their latency overlaps it
+  u32x4 buf[kDecP];
+  if (nq > 0) {
+    at_block(sum_at, 0);
+    at_block(load_at, 0);
+#pragma unroll
+    for (int i = 0; i < kDecP; ++i) {
+      buf[i] = ld16_stream(load_at.base + (size_t)load_at.c * 1024);
+      advance(load_at);
+    }
+  }
+  // the share's scales: row block r's 64 G bytes, copied 16 bytes per thread
+  {
+    const int sbytes = 64 * G;
+    const int per = sbytes / 16;
+    for (int i = threadIdx.x; i < nrb * per; i += blockDim.x) {
+      const int r = i / per, o = (i - r * per) * 16;
+      const int b = b0 + r, item = b / rbi, rb = b - item * rbi;
+      const char* src = pool + (size_t)items[item].slot * stride + off_scales + (size_t)rb * sbytes + o;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(sc_lds) + (size_t)r * sbytes + o) = ld16(src);
+    }
+  }
+  // the activation rows, quantised into LDS (same rule and codes as quant_rows_kernel)
+  if constexpr (SWIGLU) {
+    if (n_items > 0) tgemv::stage_rows<true, 1>(raw, perm, k, items[0].row_begin, K, act_q, act_s, wmax);
+  } else {
+    // one wave per h row, all rows at once: s = max|v| / 127 (1 for a zero row),
+    // q = clip(rint(v / s), -127, 127)
+    for (int i = wave; i < n_items; i += kDecNW) {
+      const float* hr = static_cast<const float*>(raw) + (size_t)items[i].row_begin * K;
+      float amax = 0.f;
+      for (int e0 = lane * 4; e0 < K; e0 += 256) {
+        const u32x4 v = ld16(hr + e0);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(__uint_as_float(v.x)), fabsf(__uint_as_float(v.y))),
+                                 fmaxf(fabsf(__uint_as_float(v.z)), fabsf(__uint_as_float(v.w)))));
+      }
+      amax = wave_max(amax);
+      const float sc = (amax == 0.f) ? 1.f : amax / 127.f;
+      if (lane == 0) act_s[i] = sc;
+      for (int e0 = lane * 4; e0 < K; e0 += 256) {
+        const u32x4 v = ld16(hr + e0);
+        const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                            __uint_as_float(v.w)};
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float rr = rintf(f[j] / sc);
+          rr = fminf(fmaxf(rr, -127.f), 127.f);
+          word |= (uint32_t)((int)rr & 0xFF) << (8 * j);
+        }
+        *reinterpret_cast<uint32_t*>(act_q + (size_t)i * K + e0) = word;
+      }
+    }
+  }
+  __syncthreads();
+
+  if (nq > 0) {
+    int q0 = 0;
+    for (; q0 + 2 * kDecP <= nq; q0 += kDecP) {
+#pragma unroll
+      for (int i = 0; i < kDecP; ++i) {
+        consume(buf[i]);
+        // the register's next load goes out after its value is used, so the loads of one
+        // trip stay in flight across the back edge
+        __builtin_amdgcn_sched_barrier(0);
+        buf[i] = ld16_stream(load_at.base + (size_t)load_at.c * 1024);
+        advance(load_at);
+      }
+    }
+    // nq - q0 chunks left (fewer than 2 kDecP); the first min(kDecP, left) are loaded
+#pragma unroll
+    for (int i = 0; i < kDecP; ++i) {
+      if (q0 + i < nq) {
+        consume(buf[i]);
+        if (q0 + kDecP + i < nq) {
+          buf[i] = ld16_stream(load_at.base + (size_t)load_at.c * 1024);
+          advance(load_at);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kDecP; ++i)
+      if (q0 + kDecP + i < nq) consume(buf[i]);
+  }
+  __syncthreads();
+  // each row block of the share: the 16 waves' partials in wave order, then the epilogue
+  for (int r = wave; r < nrb; r += kDecNW) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecNW; ++w) v += red[w][r][lane & 31];
+    const int b = b0 + r, item = b / rbi, rb = b - item * rbi;
+    const FfnItem it = items[item];
+    v *= act_s[SWIGLU ? 0 : item];
+    const int row = rb * 32 + (lane & 31);
+    if constexpr (SWIGLU) {
+      const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
+      if (lane < 32 && (lane & 1) == 0)
+        out[(size_t)it.row_begin * out_ld + (row >> 1)] = tgemv::silu(v) * u;
+    } else {
+      if (lane < 32) out[(size_t)it.row_begin * out_ld + row] = v;
+    }
+  }
+}
+
+template <bool SWIGLU, int MAXRB>
+int launch_rb(const void* raw, const int32_t* perm, int k, const FfnItem* items,
+              const int32_t* n_items, int max_items, const char* pool, size_t stride,
+              size_t off_codes, size_t off_scales, int R, int K, int out_ld, float* out,
+              hipStream_t s, long long grid, size_t lds) {
+  hipLaunchKernelGGL((int4_decode_kernel<SWIGLU, MAXRB>), dim3((unsigned)grid), dim3(kDecNW * 64),
+                     lds, s, raw, perm, k, items, n_items, pool, stride, off_codes, off_scales, R,
+                     K, out_ld, out);
+  return moe_launch_status();
+}
+
+size_t decode_lds(bool swiglu, int max_items, int K, int maxrb) {
+  const size_t act = (size_t)(swiglu ? 1 : max_items) * K;
+  return ((act + 15) & ~(size_t)15) + (size_t)maxrb * 64 * (K / 128);
+}
+
+}  // namespace
+
+bool decode_int4_fits(int max_items, int R, int K, bool swiglu) {
+  if (max_items < 1 || max_items > kStreamMaxItems || R % 32 != 0 || K % 128 != 0 ||
+      K / 64 < kDecNW)
+    return false;
+  return decode_lds(swiglu, max_items, K, 16) <= 96 * 1024;
+}
+
+int launch_decode_int4(bool swiglu, const void* raw, const int32_t* perm, int k,
+                       const FfnItem* items, const int32_t* n_items, int max_items,
+                       const char* pool, size_t stride, size_t off_codes, size_t off_scales, int R,
+                       int K, int out_ld, float* out, hipStream_t s) {
+  // the grid: one workgroup per compute unit (the kernel keeps 16 waves of up to 128
+  // VGPRs and its LDS share resident); every share has at most ceil(blocks / grid) <= MAXRB
+  static std::atomic<int> cus{0};
+  int n = cus.load(std::memory_order_relaxed);
+  if (n <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus.store(n, std::memory_order_relaxed);
+  }
+  const long long blocks = (long long)max_items * (R / 32);
+  long long grid = n;
+  if (grid > blocks) grid = blocks;
+  const long long per = (blocks + grid - 1) / grid;
+  if (per <= 8)
+    return swiglu ? launch_rb<true, 8>(raw, perm, k, items, n_items, max_items, pool, stride,
+                                       off_codes, off_scales, R, K, out_ld, out, s, grid,
+                                       decode_lds(true, max_items, K, 8))
+                  : launch_rb<false, 8>(raw, perm, k, items, n_items, max_items, pool, stride,
+                                        off_codes, off_scales, R, K, out_ld, out, s, grid,
+                                        decode_lds(false, max_items, K, 8));
+  if (per <= 16)
+    return swiglu ? launch_rb<true, 16>(raw, perm, k, items, n_items, max_items, pool, stride,
+                                        off_codes, off_scales, R, K, out_ld, out, s, grid,
+                                        decode_lds(true, max_items, K, 16))
+                  : launch_rb<false, 16>(raw, perm, k, items, n_items, max_items, pool, stride,
+                                         off_codes, off_scales, R, K, out_ld, out, s, grid,
+                                         decode_lds(false, max_items, K, 16));
+  return MOE_EUNSUPPORTED;
+}

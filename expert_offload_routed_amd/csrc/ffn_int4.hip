@@ -623,6 +623,16 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
     hipLaunchKernelGGL(quant_rows_kernel<MOE_BF16>, dim3(T), dim3(256), 0, s, x, H, nullptr,
                        nullptr, nullptr, 0, 0, 0, xq, xs);
   const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;
+  // one token: both passes over even shares of the call's row blocks
+  if (T == 1 && !split && fused && max_items > 0 && decode_int4_fits(max_items, 2 * F, H, true) &&
+      decode_int4_fits(max_items, H, F, false)) {
+    int rc = launch_decode_int4(true, x, perm, k, items, n_items, max_items, pool, stride,
+                                lay.off_w13, lay.off_s13, 2 * F, H, F, hbuf, s);
+    if (rc == MOE_OK)
+      rc = launch_decode_int4(false, hbuf, perm, k, items, n_items, max_items, pool, stride,
+                              lay.off_w2, lay.off_s2, H, F, H, y, s);
+    if (rc != MOE_EUNSUPPORTED) return rc;
+  }
   if (max_items > 0) {
     if (skinny)
       launch_skinny_w4a8(1, xq, xs, perm, k, items, n_items, max_items, pool, stride, lay.off_w13,

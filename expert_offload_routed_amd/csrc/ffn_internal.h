@@ -41,6 +41,10 @@ struct FfnWorkspace {
   int max_tiles;
 };
 
+// One-token int4 passes over even shares of row blocks (decode_int4.hip)
+constexpr int kStreamMaxItems = 64;  // groups of a one-token call they take
+bool decode_int4_fits(int max_items, int R, int K, bool swiglu);
+
 static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int slot_layout(int H, int F, int w_dtype, SlotLayout* out);
@@ -52,6 +56,13 @@ void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* 
                      int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
                      int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
                      hipStream_t s);
+// One one-token int4 pass over the work list's items: the call's row blocks in one even
+// share per workgroup (pass 1 with the SwiGLU epilogue from the bf16 tokens; pass 2 from
+// the fp32 h rows). MOE_EUNSUPPORTED when a share would exceed 16 row blocks.
+int launch_decode_int4(bool swiglu, const void* raw, const int32_t* perm, int k,
+                       const FfnItem* items, const int32_t* n_items, int max_items,
+                       const char* pool, size_t stride, size_t off_codes, size_t off_scales, int R,
+                       int K, int out_ld, float* out, hipStream_t s);
 // Workgroups of kernel `kern` resident at once on the current device (occupancy with
 // `threads` threads and `lds` bytes of dynamic LDS, times the compute units). `cache`,
 // one per kernel instantiation, keeps the occupancy for the last LDS size.
@@ -85,6 +96,9 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype
 // items, the others as kGemmBM-row tiles, into the FFN workspace's lists.
 struct FrontPlan {
   float* scores;  // when set: each expert's softmax probability averaged over the tokens [E]
+  int32_t* crit;  // when set with scores: group precision [E], 2 if scores[e] >= crit_threshold
+                  // (split-precision experts at high precision), else 1
+  float crit_threshold;
   const int32_t* lut;  // when set: write the FFN work list below
   int num_slots, n_shared, shared_slot0, small_max;
   FfnItem* items;

@@ -443,7 +443,11 @@ __device__ void front_select_and_sort(const float* lg, int T, int E, int k, int 
     for (int ex = tid; ex < E; ex += nthr) {
       float acc = 0.f;
       for (int t = 0; t < T; ++t) acc += expf(lg[(size_t)t * E + ex] - L.tmax[t]) / L.tsum[t];
-      pl.scores[ex] = acc / (float)T;
+      const float sc = acc / (float)T;
+      pl.scores[ex] = sc;
+      // split precision: the critical gate on the same float (RapidMoE Eqs. (3)-(4)):
+      // 2 = high precision (score >= threshold), 1 = low precision
+      if (pl.crit) pl.crit[ex] = sc >= pl.crit_threshold ? 2 : 1;
     }
   }
 }

@@ -120,6 +120,22 @@ struct moe_layer_ctx {
   std::vector<int32_t> wave_of, is_hit, fill_e, fill_s, fill_w;
   hipEvent_t ev_fill, ev_compute;
   int64_t totals[4];  // over completed plans: distinct, hits, fills, waves
+  // miss prefetch (moe_ctx_set_prefetch): the next step's layer and router (given by
+  // moe_ctx_forward_steps), the overlap window and bandwidth, the speculative routing
+  int prefetch;
+  double pf_window_us, pf_bw_gbs;
+  const void* next_wr;
+  const float* next_bias;
+  float* spec_logits;  // device [t_max*E]
+  int32_t* spec_ids;   // device [t_max*k]
+  float* spec_w;       // device [t_max*k]
+  float* spec_scores;  // device [E]
+  int32_t* spec_h;     // pinned [t_max*k] predicted ids, then [E] predicted scores (float)
+  hipEvent_t ev_pf_before;             // compute before the current step's expert FFN
+  std::vector<char> pf_pending;        // [L*E] prefetched, not yet planned by its layer
+  std::vector<int32_t> pf_e, pf_s;     // the latest prefetch's experts and slots
+  std::vector<uint64_t> pf_tag;
+  int64_t pf_issued, pf_used;
   // timing of the expert FFN calls of a step: one event pair per step, collected lazily
   int timing;
   hipEvent_t tev0[kRing], tev1[kRing];
@@ -137,6 +153,8 @@ struct CtxLayout {
   size_t ws_bytes;
   // device orchestration's tables and staging's slot table (used only once switched on)
   size_t order, last_use, clock, blob, fills, nfills, counters, stage_lut;
+  // the prefetch's speculative routing of the next layer
+  size_t spec_logits, spec_ids, spec_w, spec_scores;
 };
 
 CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int L, int S, int w_dtype,
@@ -173,6 +191,10 @@ CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int L, int S, int w_
   l.nfills = take(4);
   l.counters = take(4 * 8);
   l.stage_lut = take(2 * (size_t)E * 4);
+  l.spec_logits = take((size_t)t_max * E * 4);
+  l.spec_ids = take(tk * 4);
+  l.spec_w = take(tk * 4);
+  l.spec_scores = take((size_t)E * 4);
   l.total = off;
   return l;
 }
@@ -338,7 +360,7 @@ __global__ void write_tag_kernel(uint64_t* tags, int slot, uint64_t tag) {
 
 void destroy(moe_layer_ctx* c) {
   if (!c) return;
-  void* host[] = {c->ring_h, c->masks_h, c->sh_rows_h};
+  void* host[] = {c->ring_h, c->masks_h, c->sh_rows_h, c->spec_h};
   for (void* p : host)
     if (p) (void)hipHostFree(p);
   for (int i = 0; i < kRing; ++i) {
@@ -352,6 +374,7 @@ void destroy(moe_layer_ctx* c) {
   }
   if (c->ev_fill) (void)hipEventDestroy(c->ev_fill);
   if (c->ev_compute) (void)hipEventDestroy(c->ev_compute);
+  if (c->ev_pf_before) (void)hipEventDestroy(c->ev_pf_before);
   delete c;
 }
 
@@ -408,6 +431,10 @@ int run_plan(moe_layer_ctx* c, int layer, const int32_t* entry, int32_t* n_fills
   if (rc != MOE_OK) return rc;
   int hits = 0;
   for (int i = 0; i < nd; ++i) hits += c->is_hit[distinct[i]];
+  // prefetched experts of this layer: used when routed now; pending no longer either way
+  char* pend = c->pf_pending.data() + (size_t)layer * c->E;
+  for (int i = 0; i < nd; ++i) c->pf_used += pend[distinct[i]];
+  memset(pend, 0, c->E);
   c->totals[0] += nd;
   c->totals[1] += hits;
   c->totals[2] += *n_fills;
@@ -570,6 +597,16 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->d_counters = reinterpret_cast<int64_t*>(wb + cl.counters);
   c->d_stage_lut = reinterpret_cast<int32_t*>(wb + cl.stage_lut);
   c->stage_ready = false;
+  c->spec_logits = reinterpret_cast<float*>(wb + cl.spec_logits);
+  c->spec_ids = reinterpret_cast<int32_t*>(wb + cl.spec_ids);
+  c->spec_w = reinterpret_cast<float*>(wb + cl.spec_w);
+  c->spec_scores = reinterpret_cast<float*>(wb + cl.spec_scores);
+  c->prefetch = 0;
+  c->pf_window_us = c->pf_bw_gbs = 0.0;
+  c->next_wr = nullptr;
+  c->next_bias = nullptr;
+  c->pf_pending.assign((size_t)L * E, 0);
+  c->pf_issued = c->pf_used = 0;
   int bad = 0;
   // coherent, mapped: the permutation kernel stores the routed set straight into it
   bad |= hipHostMalloc(reinterpret_cast<void**>(&c->ring_h),
@@ -581,6 +618,9 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
                        (size_t)(E + 2) * E * sizeof(int32_t)) != hipSuccess;
   bad |= hipHostMalloc(reinterpret_cast<void**>(&c->sh_rows_h),
                        ((size_t)t_max * n_shared + n_shared + 1) * sizeof(int32_t)) != hipSuccess;
+  bad |= hipHostMalloc(reinterpret_cast<void**>(&c->spec_h),
+                       ((size_t)t_max * k + E) * sizeof(int32_t)) != hipSuccess;
+  bad |= hipEventCreateWithFlags(&c->ev_pf_before, hipEventDisableTiming) != hipSuccess;
   bad |= hipEventCreateWithFlags(&c->ev_fill, hipEventDisableTiming) != hipSuccess;
   bad |= hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming) != hipSuccess;
   for (int i = 0; i < kRing; ++i) {
@@ -645,6 +685,30 @@ extern "C" int moe_ctx_counters(moe_layer_ctx* c, int64_t* out4) {
   const int rc = c->orch ? sync_from_device(c) : drain(c);
   if (rc != MOE_OK) return rc;
   for (int i = 0; i < 4; ++i) out4[i] = c->totals[i];
+  return MOE_OK;
+}
+
+extern "C" int moe_ctx_set_prefetch(moe_layer_ctx* c, int enable, double t_remain_us,
+                                    double t_attn_us, double t_launch_us, double bw_gbs) {
+  MOE_CHECK_ARG(c && (enable == 0 || enable == 1));
+  if (!enable) {
+    c->prefetch = 0;
+    return MOE_OK;
+  }
+  MOE_CHECK_ARG(std::isfinite(t_remain_us) && std::isfinite(t_attn_us) &&
+                std::isfinite(t_launch_us) && std::isfinite(bw_gbs) && bw_gbs > 0.0);
+  c->pf_window_us = t_remain_us + t_attn_us - t_launch_us;
+  c->pf_bw_gbs = bw_gbs;
+  c->prefetch = 1;
+  return MOE_OK;
+}
+
+extern "C" int moe_ctx_prefetch_counters(moe_layer_ctx* c, int64_t* out) {
+  MOE_CHECK_ARG(c && out);
+  const int rc = c->orch ? sync_from_device(c) : drain(c);
+  if (rc != MOE_OK) return rc;
+  out[0] = c->pf_issued;
+  out[1] = c->pf_used;
   return MOE_OK;
 }
 
@@ -758,14 +822,18 @@ int forward_device(moe_layer_ctx* c, int layer, const void* x, int T, const void
   const int E = c->E, k = c->k, H = c->H, F = c->F, nsh = c->n_shared;
   const int nslots = c->S + nsh;
   FrontPlan fp{};
-  fp.scores = c->scores;  // written only for split precision
+  fp.scores = c->scores;  // written only for split precision, with the critical gate
+  if (c->split) {
+    fp.crit = c->crit;
+    fp.crit_threshold = c->split_th[layer];
+  }
   bool scored = false;
   int rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
                               c->topw, c->counts, c->offsets, c->perm, c->inv, c->dist, c->dist + E,
                               c->sync, c->split ? &fp : nullptr, nullptr, &scored, c->cs);
   if (rc != MOE_OK) return rc;
-  if (c->split) {
-    if (!scored) launch_step_scores(c->logits, T, E, c->scores, c->cs);
+  if (c->split && !scored) {  // more tokens than the front end scores: separate launches
+    launch_step_scores(c->logits, T, E, c->scores, c->cs);
     launch_critical_split(c->scores, E, c->split_th[layer], nullptr, 1, c->crit, c->cs);
   }
   hipLaunchKernelGGL(device_plan_kernel, dim3(1), dim3(1024), 0, c->cs, layer, E, c->S, c->dist,
@@ -862,13 +930,17 @@ int forward_staged(moe_layer_ctx* c, int layer, const void* x, int T, const void
   const int E = c->E, k = c->k, H = c->H, F = c->F, nsh = c->n_shared;
   FrontPlan fp{};
   fp.scores = c->split ? c->scores : nullptr;
+  if (c->split) {
+    fp.crit = c->crit;
+    fp.crit_threshold = c->split_th[layer];
+  }
   bool scored = false;
   int rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
                               c->topw, c->counts, c->offsets, c->perm, c->inv, c->dist, c->dist + E,
                               c->sync, fp.scores ? &fp : nullptr, nullptr, &scored, c->cs);
   if (rc != MOE_OK) return rc;
-  if (c->split) {
-    if (!scored) launch_step_scores(c->logits, T, E, c->scores, c->cs);
+  if (c->split && !scored) {
+    launch_step_scores(c->logits, T, E, c->scores, c->cs);
     launch_critical_split(c->scores, E, c->split_th[layer], nullptr, 1, c->crit, c->cs);
   }
   // the buffer holding the layer, else the one the latest staged step did not read
@@ -903,6 +975,54 @@ int forward_staged(moe_layer_ctx* c, int layer, const void* x, int T, const void
   const float* shared_y = nsh ? c->y_perm + (size_t)T * k * H : nullptr;
   return moe_combine(c->y_perm, c->inv, c->topw, T, k, H, shared_y, c->n_shared, out, out_dtype,
                      c->cs);
+}
+
+// Plan the prefetch of layer nl from the speculative routing of this step (after its own
+// plan, which the deferred bookkeeping replays first) and start the copies on the fill
+// stream once the compute enqueued before this step's expert FFN has finished.
+int plan_and_copy_prefetch(moe_layer_ctx* c, int nl, int T, int32_t* n_pf) {
+  const int E = c->E, k = c->k;
+  *n_pf = 0;
+  int rc = drain(c);  // replays this step's deferred plan too; waits for the speculative copies
+  if (rc != MOE_OK) return rc;
+  hipError_t e = hipEventSynchronize(c->ev_pf_before);
+  if (e != hipSuccess) return moe_hip_status(e);
+  c->pf_e.resize(E);
+  c->pf_s.resize(E);
+  c->pf_tag.resize(E);
+  const float* pscores = reinterpret_cast<const float*>(c->spec_h + (size_t)T * k);
+  rc = moe_plan_prefetch(c->policy, c->pol_state.data(), c->window, c->params, c->lut_h.data(),
+                         c->owner_h.data(), c->last_use.data(), &c->clock, c->S, c->L, E, nl,
+                         c->spec_h, T * k, pscores, c->pf_window_us, c->pf_bw_gbs, c->stride,
+                         c->pf_e.data(), c->pf_s.data(), n_pf);
+  if (rc != MOE_OK || *n_pf == 0) return rc;
+  recount_resident(c);
+  if (c->fs != c->cs && (e = hipStreamWaitEvent(c->fs, c->ev_pf_before, 0)) != hipSuccess)
+    return moe_hip_status(e);
+  for (int i = 0; i < *n_pf; ++i) {
+    const int idx = nl * E + c->pf_e[i];
+    c->pf_tag[i] = c->next_tag++;
+    rc = slot_prefetch(c->pool, c->stride, c->pf_s[i],
+                       c->host_store + (size_t)c->blob_of[idx] * c->stride, c->stride, c->tags,
+                       c->pf_tag[i], c->fs);
+    if (rc != MOE_OK) return rc;
+    c->pf_pending[idx] = 1;
+  }
+  c->pf_issued += *n_pf;
+  return MOE_OK;
+}
+
+int commit_prefetch(moe_layer_ctx* c, int nl, int n_pf) {
+  hipError_t e;
+  if (c->fs != c->cs) {
+    if ((e = hipEventRecord(c->ev_fill, c->fs)) != hipSuccess) return moe_hip_status(e);
+    if ((e = hipStreamWaitEvent(c->cs, c->ev_fill, 0)) != hipSuccess) return moe_hip_status(e);
+  }
+  for (int i = 0; i < n_pf; ++i)
+    hipLaunchKernelGGL(commit_after_fill_kernel, dim3(1), dim3(64), 0, c->cs, c->lut,
+                       nl * c->E + c->pf_e[i], c->owner, c->pf_s[i], c->tags, c->pf_tag[i],
+                       c->err);
+  return moe_launch_status();
 }
 
 }  // namespace
@@ -962,6 +1082,11 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
   // front end's FFN work list is not used (high-precision groups are items at any size)
   if (c->split) fp.scores = c->scores;
   else if (want_scores) fp.scores = ring_scores;
+  // a wholly resident layer takes each group's precision straight from the front end
+  if (c->split && all_resident) {
+    fp.crit = c->crit;
+    fp.crit_threshold = c->split_th[layer];
+  }
   const bool front_plan = all_resident && c->w_dtype != MOE_INT4G128_RESPLIT;
   if (front_plan) {
     const FfnWorkspace wl = ffn_workspace_layout(T, H, F, E, k, c->w_dtype, nsh);
@@ -990,6 +1115,23 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
                           hipMemcpyDeviceToHost, c->cs)) != hipSuccess)
     return moe_hip_status(e);
   if ((e = hipEventRecord(c->ring_ev[r], c->cs)) != hipSuccess) return moe_hip_status(e);
+  // miss prefetch: the next step's router on this step's tokens predicts its routed set
+  // (MoE-CORE summary page, Mechanism); enqueued after the routed set's event, so the host
+  // plans this step while the prediction runs, and reads it once the FFN is enqueued
+  const int nl = c->next_hint;
+  const bool pf = c->prefetch && nl >= 0 && c->next_wr && c->resident[nl] < E;
+  if (pf) {
+    if ((rc = moe_route(x, c->x_dtype, c->next_wr, c->next_bias, T, H, E, k, 1, c->spec_logits,
+                        c->spec_ids, c->spec_w, c->cs)) != MOE_OK)
+      return rc;
+    launch_step_scores(c->spec_logits, T, E, c->spec_scores, c->cs);
+    if ((e = hipMemcpyAsync(c->spec_h, c->spec_ids, (size_t)T * k * sizeof(int32_t),
+                            hipMemcpyDeviceToHost, c->cs)) != hipSuccess ||
+        (e = hipMemcpyAsync(c->spec_h + (size_t)T * k, c->spec_scores, (size_t)E * sizeof(float),
+                            hipMemcpyDeviceToHost, c->cs)) != hipSuccess ||
+        (e = hipEventRecord(c->ev_pf_before, c->cs)) != hipSuccess)
+      return moe_hip_status(e);
+  }
   c->ring_next = (r + 1) % kRing;
   c->last_ring = r;
 
@@ -1004,7 +1146,7 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
     // no miss is possible: defer the bookkeeping, run every routed group
     c->ring_layer[r] = layer;
     c->ring_count += 1;
-    if (c->split)
+    if (c->split && !scored)  // the front end did not write the scores (and gate)
       launch_critical_split(c->scores, E, c->split_th[layer], nullptr, 1, c->crit, c->cs);
     if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, c->split ? c->crit : nullptr,
                          nsh, c->S, c->pool, c->stride, nslots, c->w_dtype, T, H, F, E, k,
@@ -1061,10 +1203,16 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
     if ((e = hipEventRecord(c->tev1[tr], c->cs)) != hipSuccess) return moe_hip_status(e);
     c->t_count += 1;
   }
+  // the prefetch copies start behind this step's fills and overlap its expert FFN (the slots
+  // they take were not used by this step, only by compute enqueued before it)
+  int32_t n_pf = 0;
+  if (pf && (rc = plan_and_copy_prefetch(c, nl, T, &n_pf)) != MOE_OK) return rc;
   const float* shared_y = nsh ? c->y_perm + (size_t)T * k * H : nullptr;
   if ((rc = moe_combine(c->y_perm, c->inv, c->topw, T, k, H, shared_y, c->n_shared, out, out_dtype,
                         c->cs)) != MOE_OK)
     return rc;
+  // the compute stream commits each prefetched expert once its copy has landed
+  if (n_pf && (rc = commit_prefetch(c, nl, n_pf)) != MOE_OK) return rc;
   if (stats) {
     stats[0] = nd;
     stats[1] = hits;
@@ -1080,10 +1228,15 @@ extern "C" int moe_ctx_forward_steps(moe_layer_ctx* c, int n, const int32_t* lay
                                      int out_dtype) {
   MOE_CHECK_ARG(c && n >= 0 && (n == 0 || (layers && xs && w_routers && biases && outs)));
   for (int i = 0; i < n; ++i) {
-    c->next_hint = i + 1 < n ? layers[i + 1] : -1;  // the staging prefetch follows the given order
+    // the staging prefetch and the miss prefetch follow the given order
+    c->next_hint = i + 1 < n ? layers[i + 1] : -1;
+    c->next_wr = i + 1 < n ? w_routers[i + 1] : nullptr;
+    c->next_bias = i + 1 < n ? biases[i + 1] : nullptr;
     const int rc = moe_layer_forward(c, layers[i], xs[i], T, w_routers[i], biases[i], outs[i],
                                      out_dtype, nullptr);
     c->next_hint = -1;
+    c->next_wr = nullptr;
+    c->next_bias = nullptr;
     if (rc != MOE_OK) return rc;
   }
   return MOE_OK;

@@ -166,6 +166,28 @@ int moe_ctx_set_staging(moe_layer_ctx* ctx, int enable, int threshold, int pool_
  * staging buffers, since creation. */
 int moe_ctx_stage_counters(moe_layer_ctx* ctx, int64_t* out);
 
+/* moe_ctx_set_prefetch: miss prefetch (MoE-CORE summary page, Mechanism).
+ * Within moe_ctx_forward_steps, a step whose next step's layer is not wholly
+ * resident also evaluates the next step's router on its own tokens (before the
+ * next step's real input exists) and prefetches the top predicted experts that
+ * are not resident: moe_plan_prefetch after the step's own plan, with window
+ * t_remain_us + t_attn_us - t_launch_us (the caller's estimates of the
+ * remaining compute of this layer, the attention of the next one, and the
+ * launch overhead, in microseconds) and bw_gbs the host-to-device bandwidth.
+ * Each copy (slot_prefetch) starts on the fill stream behind the step's own
+ * fills, as soon as the compute enqueued before this step's expert FFN has
+ * finished, so it overlaps that FFN; the compute stream commits it by tag at
+ * the end of the step, before the next step. Host orchestration only (steps
+ * under device orchestration or full-layer staging do not prefetch), and a
+ * step waits for the host to read the prediction. enable = 0 switches it off;
+ * MOE_EINVAL for non-finite times or a bandwidth <= 0. */
+int moe_ctx_set_prefetch(moe_layer_ctx* ctx, int enable, double t_remain_us, double t_attn_us,
+                         double t_launch_us, double bw_gbs);
+
+/* moe_ctx_prefetch_counters: out[0] experts prefetched, out[1] prefetched
+ * experts that their layer's next step routed, since creation. */
+int moe_ctx_prefetch_counters(moe_layer_ctx* ctx, int64_t* out);
+
 /* moe_ctx_set_orchestration: where the residency plan runs.
  *   MOE_ORCH_HOST (default): the host plans each step that may miss, after
  *     reading the routed set, and the fills are DMA copies on the fill stream.

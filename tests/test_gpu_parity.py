@@ -12,7 +12,7 @@ import oracle as O
 from expert_offload_routed_amd import binding as B
 from expert_offload_routed_amd import harness as Hn
 from expert_offload_routed_amd import workloads as W
-from gpu_common import (TOL, check_routing, host_weights, oracle_expert, oracle_y_rows, rel_l2,
+from gpu_common import (TOL, OracleWeights, check_routing, oracle_y_rows, rel_l2,
                         run_layer_case as _run_layer_case, say)
 
 pytestmark = pytest.mark.gpu
@@ -590,3 +590,58 @@ def test_prefetch_commit_overtaken_by_a_demand_fill_is_refused():
     torch.cuda.synchronize()
     assert err.item() == 0 and lut.cpu().tolist()[A] == 0
     assert torch.equal(pool[:store.stride].cpu(), store.host[A])
+
+
+@pytest.mark.parametrize("window_us,slots", [(1e6, 10), (5.0, 12), (0.0, 10)])  # all free, 1, none
+def test_forward_steps_prefetch_next_layer(window_us, slots):
+    """Miss prefetch inside a stack step (MoE-CORE summary page, Mechanism): each layer's step
+    also evaluates the next layer's router on its own tokens and copies the top predicted
+    non-resident experts ahead, as many as the window hides at the given bandwidth. The
+    oracle's planner does the same (moe_layer, then prefetch with the oracle's own
+    prediction) and its pool takes the same copies: outputs, tables and the prefetch
+    count must agree after every stack step."""
+    shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=3, E=16, k=4, H=256,
+                      F=128, blobs=16)
+    L, E, k = shape.layers, shape.E, shape.k
+    residency = W.initial_residency(shape, slots, "zipf_rank")
+    lay = Hn.SlotCacheLayer(shape, slots, residency, t_max=3)
+    bw = 50.0
+    lay.ctx.set_prefetch(True, t_remain_us=0.0, t_attn_us=window_us, t_launch_us=0.0, bw_gbs=bw)
+    wts = OracleWeights(shape)
+    pool = O.SlotPool(slots, L, E)
+    for s_, o_ in enumerate(residency):
+        if o_ is not None:
+            pool.commit(s_, o_[0], o_[1], wts.of(*o_))
+    planner = O.LruSlotPlanner(slots, L, E, residency)
+    n_pf = 0
+    for step, T in enumerate([1, 2, 1, 3, 1, 2]):
+        say(f"prefetch window={window_us} step={step} T={T}")
+        xs = [W.tokens(shape, T, layer=l, step=step, device=_dev()) for l in range(L)]
+        outs = [torch.empty(T, shape.H, dtype=torch.bfloat16, device=_dev()) for _ in range(L)]
+        lay.ctx.forward_steps([(l, xs[l], *lay.routers[l], outs[l]) for l in range(L)], B.MOE_BF16)
+        torch.cuda.synchronize()
+        assert lay.err.item() == 0
+        for l in range(L):
+            wr, b = lay.routers[l]
+            ref = O.moe_layer(xs[l], wr, b, k, layer=l, pool=pool, planner=planner,
+                              weights_of_expert=lambda e, l=l: wts.of(l, e))
+            r = rel_l2(outs[l].float().cpu().numpy(), ref["out"])
+            assert r <= TOL[shape.wfmt], (step, l, r)
+            if l + 1 < L:
+                pr = O.route(xs[l], *lay.routers[l + 1], k)
+                sc = O.step_scores(pr["logits"]).astype(np.float32)
+                got = planner.prefetch(l + 1, pr["ids"], sc, window_us, bw, lay.stride)
+                for e, s_ in got:
+                    pool.commit(s_, l + 1, e, wts.of(l + 1, e))
+                n_pf += len(got)
+        lut_h, owner_h, last_use_h, clock_h = lay.tables()
+        assert lay.lut.cpu().numpy().reshape(L, E).tolist() == planner.lut.tolist(), step
+        assert lut_h.reshape(L, E).tolist() == planner.lut.tolist()
+        assert last_use_h.tolist() == planner.last_use and clock_h == planner.clock
+    pc = lay.ctx.prefetch_counters()
+    say(f"  prefetched {pc}, oracle {n_pf}")
+    assert pc["prefetched"] == n_pf
+    if window_us >= 1e6:
+        assert n_pf > 0
+    if window_us == 0.0:
+        assert n_pf == 0
