@@ -35,6 +35,9 @@ _SIGNATURES = {
     "moe_step_scores": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "moe_ffn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_ffn_workspace_offsets": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "moe_expert_ffn_noalloc": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _vp, _vp, _vp]),
+    "moe_noalloc_scratch_bytes": (_sz, []),
     "moe_quantize_rows_int8": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "moe_expert_ffn": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _i32, _i32, _i32, _i32, _i32,
                               _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
@@ -311,6 +314,22 @@ def moe_expert_ffn(x, perm, offsets, lut_row, group_mask, pool, slot_stride: int
           _dev(group_mask), _dev(pool), slot_stride, num_slots, w_dtype, T, H, F, E, k, _dev(y_perm),
           _dev(err_word), _dev(workspace), workspace.numel() * workspace.element_size(),
           _stream(stream))
+
+
+def moe_expert_ffn_noalloc(x, perm, offsets, lut_row, group_mask, pool, slot_stride: int,
+                           w_dtype: int, T: int, H: int, F: int, E: int, k: int, y_perm, err_word,
+                           stream=None):
+    num_slots = pool.numel() // slot_stride
+    if (x.numel() < T * H or perm.numel() < T * k or offsets.numel() < E + 1 or lut_row.numel() < E
+            or y_perm.numel() < T * k * H or (group_mask is not None and group_mask.numel() < E)):
+        raise ValueError("moe_expert_ffn_noalloc: an argument is smaller than its shape needs")
+    _call("moe_expert_ffn_noalloc", _dev(x), dtype_code(x), _dev(perm), _dev(offsets), _dev(lut_row),
+          _dev(group_mask), _dev(pool), slot_stride, num_slots, w_dtype, T, H, F, E, k, _dev(y_perm),
+          _dev(err_word), _stream(stream))
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    return int(lib().moe_noalloc_scratch_bytes())
 
 
 # ---------------------------------------------------------------- combine --

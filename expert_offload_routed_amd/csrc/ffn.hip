@@ -26,6 +26,8 @@
 // (the A operand of the second MFMA pass), fp32 with fp32 weights.
 #include <limits.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "ffn_gemv.h"
 #include "ffn_internal.h"
@@ -281,6 +283,59 @@ extern "C" int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm,
   return expert_ffn(x, x_dtype, perm, offsets, lut, group_mask, 0, 0, pool_base, slot_stride,
                     num_slots, w_dtype, T, H, F, E, k, y_perm, err_word, workspace, ws_bytes,
                     stream);
+}
+
+// ----------------------------------------------- allocation-free variant --
+// moe_expert_ffn_noalloc keeps its workspace in this array. In host code the name
+// is only a stand-in for the device symbol: every host use goes through the address
+// hipGetSymbolAddress returns on the device (one copy per GPU, looked up once per
+// device on its first call there).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return moe_hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MOE_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" size_t moe_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int moe_expert_ffn_noalloc(const void* x, int x_dtype, const int32_t* perm,
+                                      const int32_t* offsets, const int32_t* lut,
+                                      const int32_t* group_mask, const void* pool_base,
+                                      size_t slot_stride, int num_slots, int w_dtype, int T,
+                                      int H, int F, int E, int k, float* y_perm,
+                                      int32_t* err_word, hipStream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && H > 0 && F > 0 && k >= 1 && k <= E && E <= 1024);
+  if (T == 0) return MOE_OK;
+  const FfnWorkspace w = ffn_workspace_layout(T, H, F, E, k, w_dtype, 0);
+  if (w.total > kNoAllocScratchBytes) return MOE_EINVAL;  // beyond the static scratch
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc != MOE_OK) return rc;
+  return expert_ffn(x, x_dtype, perm, offsets, lut, group_mask, 0, 0, pool_base, slot_stride,
+                    num_slots, w_dtype, T, H, F, E, k, y_perm, err_word, ws,
+                    kNoAllocScratchBytes, stream);
 }
 
 int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* offsets,

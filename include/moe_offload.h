@@ -273,6 +273,30 @@ int moe_expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_
                    float* y_perm, int32_t* err_word, void* workspace, size_t ws_bytes,
                    hipStream_t stream);
 
+/* moe_expert_ffn_noalloc: moe_expert_ffn without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * kernels and results as moe_expert_ffn with n_shared = 0; the workspace is a
+ * static device array of moe_noalloc_scratch_bytes() bytes (32 MB) inside the
+ * library, one copy per GPU, held until the process ends. The call allocates
+ * nothing; its first call on a device looks up that device's copy of the array
+ * (a host-side query, no allocation). Sizes whose moe_ffn_workspace_bytes
+ * exceed the array return MOE_EINVAL (decode batches fit: e.g. 32 tokens of
+ * the 7168 x 2048 int4 expert shape need about 6 MB). Every call on a GPU
+ * shares that GPU's array: calls whose execution overlaps on one GPU (other
+ * streams, other threads) race and must not be issued; calls in order on one
+ * stream are safe. The array keeps the last call's contents; each call writes
+ * or clears everything it reads. */
+int moe_expert_ffn_noalloc(const void* x, int x_dtype, const int32_t* perm,
+                           const int32_t* offsets, const int32_t* lut,
+                           const int32_t* group_mask, const void* pool_base, size_t slot_stride,
+                           int num_slots, int w_dtype, int T, int H, int F, int E, int k,
+                           float* y_perm, int32_t* err_word, hipStream_t stream);
+
+/* moe_noalloc_scratch_bytes: size of the static array moe_expert_ffn_noalloc
+ * uses as its workspace (host-only query). */
+size_t moe_noalloc_scratch_bytes(void);
+
 /* ------------------------------------------------------------------ combine -
  * moe_combine: weighted sum of the routed experts' outputs (RapidMoE Sec. 2.1,
  * Algorithm 1; CAP Eq. (1)) plus the always-on shared experts (weight 1):
