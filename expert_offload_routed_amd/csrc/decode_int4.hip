@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
   __shared__ float act_s[kStreamMaxItems];
   __shared__ float wmax[16];
+  __shared__ unsigned row_max[kStreamMaxItems];
   __shared__ float red[kDecNW][MAXRB][32];
   const int n_items = n_items_p[0];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -118,33 +119,122 @@ __global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
   }
   // the activation rows, quantised into LDS (same rule and codes as quant_rows_kernel)
   if constexpr (SWIGLU) {
-    if (n_items > 0) tgemv::stage_rows<true, 1>(raw, perm, k, items[0].row_begin, K, act_q, act_s, wmax);
-  } else {
-    // one wave per h row, all rows at once: s = max|v| / 127 (1 for a zero row),
-    // q = clip(rint(v / s), -127, 127)
-    for (int i = wave; i < n_items; i += kDecNW) {
-      const float* hr = static_cast<const float*>(raw) + (size_t)items[i].row_begin * K;
+    // the token row (bf16; every group reads the same one): eight values per thread, loaded
+    // once and held in registers (K <= 8 * blockDim, which the launch checks), a block-wide
+    // max, then the codes: s = max|v| / 127 (1 for a zero row), q = clip(rint(v / s), -127, 127)
+    if (n_items > 0) {
+      const int e0 = (int)threadIdx.x * 8;
+      float v[8];
       float amax = 0.f;
-      for (int e0 = lane * 4; e0 < K; e0 += 256) {
-        const u32x4 v = ld16(hr + e0);
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(__uint_as_float(v.x)), fabsf(__uint_as_float(v.y))),
-                                 fmaxf(fabsf(__uint_as_float(v.z)), fabsf(__uint_as_float(v.w)))));
+      if (e0 < K) {
+        const u32x4 w = ld16(static_cast<const uint16_t*>(raw) +
+                             (size_t)(perm[items[0].row_begin] / k) * K + e0);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(ww[i] << 16);
+          v[2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
       }
       amax = wave_max(amax);
-      const float sc = (amax == 0.f) ? 1.f : amax / 127.f;
-      if (lane == 0) act_s[i] = sc;
-      for (int e0 = lane * 4; e0 < K; e0 += 256) {
-        const u32x4 v = ld16(hr + e0);
-        const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                            __uint_as_float(v.w)};
+      if (lane == 0) wmax[wave] = amax;
+      __syncthreads();
+      float m = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecNW; ++w) m = fmaxf(m, wmax[w]);
+      const float sc = (m == 0.f) ? 1.f : m / 127.f;
+      if (e0 < K) {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float r = rintf(v[i] / sc);
+          r = fminf(fmaxf(r, -127.f), 127.f);
+          const uint32_t b = (uint32_t)((int)r & 0xFF);
+          if (i < 4) w0 |= b << (8 * i); else w1 |= b << (8 * (i - 4));
+        }
+        *reinterpret_cast<uint2*>(act_q + e0) = make_uint2(w0, w1);
+      }
+      if (threadIdx.x == 0) act_s[0] = sc;
+    }
+  } else if (nrb > 0) {
+    // only the h rows of the share's groups (one or two for a large R): every thread loads
+    // its float4s of those rows at once (a row-wide max through an LDS max over the float
+    // bits, which order like the values for |v|), then quantises them from registers:
+    // s = max|v| / 127 (1 for a zero row), q = clip(rint(v / s), -127, 127)
+    const int i0 = b0 / rbi, nrow = (b1 - 1) / rbi - i0 + 1;
+    const int q4 = K / 4, nv = nrow * q4;
+    for (int r = threadIdx.x; r < nrow; r += blockDim.x) row_max[r] = 0u;
+    __syncthreads();
+    constexpr int NV = 4;  // float4 per thread held in registers
+    const int nthr = blockDim.x;
+    for (int base = 0; base < nv; base += NV * nthr) {
+      u32x4 v[NV];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int idx = base + u * nthr + (int)threadIdx.x;
+        if (idx < nv) {
+          const int r = idx / q4;
+          v[u] = ld16(static_cast<const float*>(raw) + (size_t)items[i0 + r].row_begin * K +
+                      (size_t)(idx - r * q4) * 4);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int idx = base + u * nthr + (int)threadIdx.x;
+        if (idx < nv) {
+          const float m = fmaxf(fmaxf(fabsf(__uint_as_float(v[u].x)), fabsf(__uint_as_float(v[u].y))),
+                                fmaxf(fabsf(__uint_as_float(v[u].z)), fabsf(__uint_as_float(v[u].w))));
+          atomicMax(&row_max[idx / q4], __float_as_uint(m));
+        }
+      }
+      if (base + NV * nthr < nv) continue;  // more than one round: the codes read again below
+      __syncthreads();
+      for (int r = threadIdx.x; r < nrow; r += nthr) {
+        const float amax = __uint_as_float(row_max[r]);
+        act_s[i0 + r] = (amax == 0.f) ? 1.f : amax / 127.f;
+      }
+      if (base == 0) {  // one round: the values are still in registers
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int idx = u * nthr + (int)threadIdx.x;
+          if (idx < nv) {
+            const int r = idx / q4;
+            const float amax = __uint_as_float(row_max[r]);
+            const float sc = (amax == 0.f) ? 1.f : amax / 127.f;
+            const float f[4] = {__uint_as_float(v[u].x), __uint_as_float(v[u].y),
+                                __uint_as_float(v[u].z), __uint_as_float(v[u].w)};
+            uint32_t word = 0;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              float rr = rintf(f[jj] / sc);
+              rr = fminf(fmaxf(rr, -127.f), 127.f);
+              word |= (uint32_t)((int)rr & 0xFF) << (8 * jj);
+            }
+            *reinterpret_cast<uint32_t*>(act_q + (size_t)(i0 + r) * K + (size_t)(idx - r * q4) * 4) = word;
+          }
+        }
+      }
+    }
+    if (nv > NV * nthr) {
+      // several rounds: the maxima are complete (the last round's barrier); quantise again
+      for (int idx = threadIdx.x; idx < nv; idx += nthr) {
+        const int r = idx / q4;
+        const float amax = __uint_as_float(row_max[r]);
+        const float sc = (amax == 0.f) ? 1.f : amax / 127.f;
+        const u32x4 vv = ld16(static_cast<const float*>(raw) + (size_t)items[i0 + r].row_begin * K +
+                              (size_t)(idx - r * q4) * 4);
+        const float f[4] = {__uint_as_float(vv.x), __uint_as_float(vv.y), __uint_as_float(vv.z),
+                            __uint_as_float(vv.w)};
         uint32_t word = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float rr = rintf(f[j] / sc);
+        for (int jj = 0; jj < 4; ++jj) {
+          float rr = rintf(f[jj] / sc);
           rr = fminf(fmaxf(rr, -127.f), 127.f);
-          word |= (uint32_t)((int)rr & 0xFF) << (8 * j);
+          word |= (uint32_t)((int)rr & 0xFF) << (8 * jj);
         }
-        *reinterpret_cast<uint32_t*>(act_q + (size_t)i * K + e0) = word;
+        *reinterpret_cast<uint32_t*>(act_q + (size_t)(i0 + r) * K + (size_t)(idx - r * q4) * 4) = word;
       }
     }
   }
@@ -218,7 +308,7 @@ size_t decode_lds(bool swiglu, int max_items, int K, int maxrb) {
 
 bool decode_int4_fits(int max_items, int R, int K, bool swiglu) {
   if (max_items < 1 || max_items > kStreamMaxItems || R % 32 != 0 || K % 128 != 0 ||
-      K / 64 < kDecNW)
+      K / 64 < kDecNW || (swiglu && K > 8 * kDecNW * 64))
     return false;
   return decode_lds(swiglu, max_items, K, 16) <= 96 * 1024;
 }
