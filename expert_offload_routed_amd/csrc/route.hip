@@ -657,6 +657,199 @@ __global__ __launch_bounds__(1024) void select_sort_kernel(
                             distinct, n_distinct, L, s_dist, pl);
 }
 
+// Second half of the front end for one token, in one wave: top-k (topk_token), the
+// routing scores, then every output written straight from registers. With one token each
+// selected expert holds exactly one assignment, so the counting sort reduces to ranking
+// the k selected ids: assignment r goes to sorted position rank(r) = #{selected ids <
+// id_r}, counts are 0/1 and offsets[e] = #{selected ids < e}. The FFN work list (when
+// pl.lut is set) is the plan kernel's: the routed groups in id order, then the shared
+// groups, each of one row, groups whose slot is out of range skipped and flagged.
+constexpr int kDecodeSelectMaxK = 64;
+// Order-preserving key of a logit (larger value, larger key); NaN and absent logits get 0,
+// below every number (-inf included), as the (value desc, id asc) rule never prefers them.
+__device__ __forceinline__ uint32_t logit_key(float f, bool present) {
+  const uint32_t u = __float_as_uint(f);
+  if (!present || f != f) return 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int NV>
+__global__ __launch_bounds__(64) void decode_select_kernel(
+    const float* __restrict__ logits, int E, int k, int renorm, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ distinct,
+    int32_t* __restrict__ n_distinct, FrontPlan pl) {
+  __shared__ uint32_t s_key[kDecodeSelectMaxK];
+  __shared__ int s_cid[kDecodeSelectMaxK];  // candidate id (for ties), in id order
+  __shared__ float s_cv[kDecodeSelectMaxK];
+  __shared__ int s_ids[kDecodeSelectMaxK];  // selection order r: expert (or -1)
+  __shared__ float s_sel[kDecodeSelectMaxK];
+  const int lane = threadIdx.x;
+  float v[NV];
+  uint32_t key[NV];
+  int lutv[NV];  // slot-table entries, loaded with the logits (the plan looks them up by id)
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? logits[e] : -INFINITY;
+    lutv[i] = (pl.lut && e < E) ? pl.lut[e] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) key[i] = logit_key(v[i], lane + 64 * i < E);
+  // the k-th largest key: the largest tau with #{key >= tau} >= k, bit by bit from the top
+  uint32_t tau = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+    if (cnt >= k) tau = cand;
+  }
+  // selected: every key above tau, then keys equal to tau by ascending id up to k
+  int n_gt = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) n_gt += __popcll(__ballot(key[i] > tau));
+  const int need = k - n_gt;
+  int eq_before = 0, base = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint64_t meq = __ballot(key[i] == tau);
+    const bool sel = key[i] > tau || (key[i] == tau && eq_before + popc_below(meq) < need);
+    eq_before += __popcll(meq);
+    const uint64_t ms = __ballot(sel);
+    if (sel) {
+      const int p = base + popc_below(ms);  // candidates in id order
+      s_key[p] = key[i];
+      s_cid[p] = lane + 64 * i;
+      s_cv[p] = v[i];
+    }
+    base += __popcll(ms);
+  }
+  __syncthreads();
+  // selection order: (value desc, id asc), i.e. key desc, id asc
+  if (lane < k) {
+    const uint32_t mk = s_key[lane];
+    const int mi = s_cid[lane];
+    int r = 0;
+    for (int q = 0; q < k; ++q) {
+      const uint32_t qk = s_key[q];
+      r += (qk > mk || (qk == mk && s_cid[q] < mi)) ? 1 : 0;
+    }
+    s_ids[r] = mk == 0u ? -1 : mi;
+    s_sel[r] = s_cv[lane];
+  }
+  __syncthreads();
+  const float vmax = s_sel[0];
+  const float sel = lane < k ? s_sel[lane] : 0.f;
+  // routing weights: softmax over the selected (renorm) or over all E, as topk_token forms it
+  float denom = 0.f;
+  if (renorm) {
+    if (lane < k) denom += expf(sel - vmax);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (lane + 64 * i < E) denom += expf(v[i] - vmax);
+  }
+  denom = wave_sum(denom);
+  const float w_mine = lane < k ? expf(sel - vmax) / denom : 0.f;
+  const int my = lane < k ? s_ids[lane] : -1;
+  const bool valid = my >= 0 && my < E;
+  // sorted position: valid ids in ascending order, then the invalid assignments in order
+  int below = 0, nvalid = 0, inval_before = 0;
+  for (int j = 0; j < k; ++j) {
+    const int o = s_ids[j];
+    const bool ov = o >= 0 && o < E;
+    nvalid += ov ? 1 : 0;
+    below += (ov && valid && o < my) ? 1 : 0;
+    inval_before += (!ov && j < lane) ? 1 : 0;
+  }
+  if (lane < k) {
+    const int pos = valid ? below : nvalid + inval_before;
+    ids[lane] = my;
+    weights[lane] = w_mine;
+    perm[pos] = lane;
+    inv[lane] = pos;
+    if (valid) distinct[pos] = my;
+  }
+  for (int e = lane; e < E; e += 64) {
+    int c = 0, o = 0;
+    for (int j = 0; j < k; ++j) {
+      const int id = s_ids[j];
+      c += (id == e) ? 1 : 0;
+      o += (id >= 0 && id < e) ? 1 : 0;
+    }
+    counts[e] = c;
+    offsets[e] = o;
+  }
+  if (lane == 0) {
+    offsets[E] = nvalid;
+    n_distinct[0] = nvalid;
+  }
+  if (pl.scores) {  // each expert's softmax probability (one token: the average is the value)
+    // the normaliser as token_softmax_norm forms it (max of every logit = the first selected)
+    const float m = vmax;
+    float sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (lane + 64 * i < E) sm += expf(v[i] - m);
+    sm = wave_sum(sm);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = lane + 64 * i;
+      if (e >= E) continue;
+      float acc = 0.f;
+      acc += expf(v[i] - m) / sm;
+      const float sc = acc / 1.f;
+      pl.scores[e] = sc;
+      if (pl.crit) pl.crit[e] = sc >= pl.crit_threshold ? 2 : 1;
+    }
+  }
+  if (pl.lut) {
+    // group g of this lane: routed lane r < k holds its selected expert (position `below`
+    // among the routed groups), lane k + s the shared group E + s
+    const int ns = pl.n_shared;
+    const bool routed = lane < k && valid;
+    const bool shared = lane >= k && lane < k + ns;
+    int slot = -1, g = -1, begin = 0;
+    // slot of the selected id: entry my % 64 of every lane's register my / 64 (a uniform loop)
+    int lut_my = -1;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int got = __shfl(lutv[i], (my >= 0 ? my : 0) & 63, 64);
+      if (my >= 0 && (my >> 6) == i) lut_my = got;
+    }
+    if (routed) {
+      g = my;
+      slot = lut_my;
+      begin = below;
+    } else if (shared) {
+      g = E + (lane - k);
+      slot = pl.shared_slot0 + (lane - k);
+      begin = k + (lane - k);
+    }
+    const bool take = (routed || shared) && slot >= 0 && slot < pl.num_slots;
+    if ((routed || shared) && !take) atomicOr(pl.err, MOE_ERR_ABSENT);
+    // position among the taken groups in group order: routed ones by id, shared after them
+    const unsigned long long taken = __ballot(take);
+    int pos = 0;
+    for (int j = 0; j < k + ns && j < 64; ++j) {
+      if (!((taken >> j) & 1ull)) continue;
+      const int gj = __shfl(g, j, 64);
+      pos += (gj < g) ? 1 : 0;
+    }
+    const int n_taken = __popcll(taken);
+    const bool as_item = 1 <= pl.small_max;
+    if (take) {
+      if (as_item) pl.items[pos] = FfnItem{g, slot, begin, 1};
+      else pl.tiles[pos] = GemmTile{g, slot, begin, 1};
+    }
+    if (lane == 0) {
+      pl.n_items[0] = as_item ? n_taken : 0;
+      pl.n_tiles[0] = as_item ? 0 : n_taken;
+    }
+  }
+}
+
 // Router logits of T > 0 tokens (arguments checked by the caller).
 int launch_logits(const void* x, int x_dtype, const void* w_router, const float* bias, int T,
                   int H, int E, float* logits, hipStream_t stream) {
@@ -742,6 +935,20 @@ int route_permute_plan(const void* x, int x_dtype, const void* w_router, const f
       pl.lut = nullptr;
     }
     if (pl.scores && scored) *scored = true;
+  }
+  if (T == 1 && k <= kDecodeSelectMaxK && k + (plan ? plan->n_shared : 0) <= 64) {
+    // one token: the logits kernel, then one wave selects, ranks and plans
+    int rc = launch_logits(x, x_dtype, w_router, bias, T, H, E, logits, stream);
+    if (rc != MOE_OK) return rc;
+#define MOE_DSELECT(NV_)                                                                          \
+  hipLaunchKernelGGL(decode_select_kernel<NV_>, dim3(1), dim3(64), 0, stream, logits, E, k, renorm, \
+                     topk_ids, topk_w, counts, offsets, perm, inv, distinct, n_distinct, pl)
+    if (E <= 64) MOE_DSELECT(1);
+    else if (E <= 128) MOE_DSELECT(2);
+    else if (E <= 256) MOE_DSELECT(4);
+    else MOE_DSELECT(kTopkMaxV);
+#undef MOE_DSELECT
+    return moe_launch_status();
   }
   if (!front) {  // logits, then one workgroup selects, sorts and plans
     if (T > kFrontMaxT) {  // its LDS holds the softmax normalisers of kFrontMaxT tokens

@@ -91,10 +91,17 @@ def test_route_rejects_bad_args():
                                      (W.reduced(TINY, E=5, k=3, H=264), 7),     # one workgroup, 3 H slices per expert
                                      (W.reduced(MIX, E=40, k=4, H=1024), 11),   # one workgroup, 40 (expert, slice) pairs
                                      (W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), H=2048), 3),
-                                     (W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), E=1000, k=16, H=512), 9)],
+                                     (W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), E=1000, k=16, H=512), 9),
+                                     # one token: logits, then the one-wave select (k <= 64)
+                                     (W.reduced(DSV3, H=7168), 1),
+                                     (W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), 1),
+                                     (W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), E=1000, k=16, H=512), 1),
+                                     (W.reduced(TINY, E=64, k=64, H=64), 1),
+                                     (W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), H=2048), 1)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_route_permute_fused(shape, T):
-    """One-launch front end (T <= 16) and its two-call fallback: same bar as the separate stages."""
+    """One-launch front end (T <= 16), the one-token select, and the two-call fallback: same bar
+    as the separate stages."""
     say(f"route_permute {shape.name} T={T}")
     counter = torch.zeros(1, dtype=torch.int32, device=_dev())
     for rep in range(3):  # the counter must come back to zero after every call
