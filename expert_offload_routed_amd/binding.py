@@ -18,7 +18,7 @@ import torch
 from .build import LIB_PATH
 
 MOE_F32, MOE_BF16, MOE_INT4G128, MOE_INT4G128_RESPLIT = 0, 1, 2, 3
-MOE_ERR_ABSENT, MOE_ERR_STALE_TAG = 1, 2
+MOE_ERR_ABSENT, MOE_ERR_STALE_TAG, MOE_ERR_SYNC = 1, 2, 4
 _STATUS = {-1: "invalid argument", -2: "unsupported dtype or shape", -3: "HIP runtime error"}
 
 _vp, _i32, _i64, _u64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t

@@ -32,20 +32,59 @@ constexpr int kDecP = 8;    // chunks in flight per lane
 // SWIGLU (gate/up pass): one token row for every group (row perm[p] / k of the bf16
 // tokens; T = 1), out = h (fp32, row p, column n of rows 2n, 2n+1).
 // Otherwise (down pass): row p of the fp32 h for each group; out = y (fp32).
+// The workgroup's LDS of a pass: activation rows [SWIGLU ? 1 : n_items][K] int8, then the
+// share's scales [MAXRB][32][K/128] bf16 (dynamic), and the fixed arrays below.
+template <int MAXRB>
+struct PassLds {
+  int8_t* dyn;
+  float* act_s;      // [kStreamMaxItems]
+  float* wmax;       // [16]
+  unsigned* row_max; // [kStreamMaxItems]
+  float (*red)[MAXRB][32];  // [kDecNW]
+};
+
+// Cross-workgroup hand-off of the one-launch form (both passes in one kernel): the gate/up
+// pass writes h with device-scope stores and, once they have completed, adds per group the
+// row blocks it finished to signal[group]; the down pass waits, before it reads h (with
+// device-scope loads), until wait[group] holds all 2F/32 row blocks of each group its share
+// reads. A wait that passes spin_cap polls (workgroups not all resident) gives up and flags
+// MOE_ERR_SYNC instead of hanging.
+struct PassSync {
+  int32_t* signal;
+  const int32_t* wait;
+  int wait_target;
+  int32_t* err;
+  int spin_cap;
+};
+
+// h handed between the workgroups of one launch goes through device-scope stores and loads
+// (written through to, and read from, the level every XCD shares), so neither side needs an
+// L2 writeback or invalidate; the counter is bumped only after the stores have completed.
+__device__ __forceinline__ void store_h(float* p, float v, bool shared) {
+  if (shared) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+__device__ __forceinline__ u32x4 load_h4(const float* p, bool shared) {
+  if (!shared) return ld16(p);
+  u32x4 r;
+  r.x = __float_as_uint(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  r.y = __float_as_uint(__hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  r.z = __float_as_uint(__hip_atomic_load(p + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  r.w = __float_as_uint(__hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return r;
+}
+
 template <bool SWIGLU, int MAXRB>
-__global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
+__device__ __forceinline__ void decode_pass(
     const void* __restrict__ raw, const int32_t* __restrict__ perm, int k,
-    const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
-    const char* __restrict__ pool, size_t stride, size_t off_codes, size_t off_scales, int R,
-    int K, int out_ld, float* __restrict__ out) {
-  // dynamic LDS: activation rows [SWIGLU ? 1 : n_items][K] int8, then the share's scales
-  // [MAXRB][32][K/128] bf16
-  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
-  __shared__ float act_s[kStreamMaxItems];
-  __shared__ float wmax[16];
-  __shared__ unsigned row_max[kStreamMaxItems];
-  __shared__ float red[kDecNW][MAXRB][32];
-  const int n_items = n_items_p[0];
+    const FfnItem* __restrict__ items, int n_items, const char* __restrict__ pool, size_t stride,
+    size_t off_codes, size_t off_scales, int R, int K, int out_ld, float* __restrict__ out,
+    const PassLds<MAXRB>& L, const PassSync& sy) {
+  int8_t* lds = L.dyn;
+  float* act_s = L.act_s;
+  float* wmax = L.wmax;
+  unsigned* row_max = L.row_max;
+  float (*red)[MAXRB][32] = L.red;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int rbi = R / 32, nkc = K / 64, G = K / 128;
   const int total_rb = n_items * rbi;
@@ -117,6 +156,27 @@ __global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
       *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(sc_lds) + (size_t)r * sbytes + o) = ld16(src);
     }
   }
+  // one launch: the h rows this share reads are complete once every row block of their
+  // groups is counted (weights and scales above do not depend on them)
+  if (sy.wait != nullptr && nrb > 0) {
+    if (threadIdx.x == 0) {
+      const int g0 = b0 / rbi, g1 = (b1 - 1) / rbi;
+      bool late = false;
+      for (int g = g0; g <= g1; ++g) {
+        int spins = 0;
+        while (__hip_atomic_load(sy.wait + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               sy.wait_target) {
+          if (++spins > sy.spin_cap) {
+            late = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      if (late) atomicOr(sy.err, MOE_ERR_SYNC);
+    }
+    __syncthreads();
+  }
   // the activation rows, quantised into LDS (same rule and codes as quant_rows_kernel)
   if constexpr (SWIGLU) {
     // the token row (bf16; every group reads the same one): eight values per thread, loaded
@@ -176,8 +236,8 @@ __global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
         const int idx = base + u * nthr + (int)threadIdx.x;
         if (idx < nv) {
           const int r = idx / q4;
-          v[u] = ld16(static_cast<const float*>(raw) + (size_t)items[i0 + r].row_begin * K +
-                      (size_t)(idx - r * q4) * 4);
+          v[u] = load_h4(static_cast<const float*>(raw) + (size_t)items[i0 + r].row_begin * K +
+                         (size_t)(idx - r * q4) * 4, sy.wait != nullptr);
         }
       }
 #pragma unroll
@@ -223,8 +283,8 @@ __global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
         const int r = idx / q4;
         const float amax = __uint_as_float(row_max[r]);
         const float sc = (amax == 0.f) ? 1.f : amax / 127.f;
-        const u32x4 vv = ld16(static_cast<const float*>(raw) + (size_t)items[i0 + r].row_begin * K +
-                              (size_t)(idx - r * q4) * 4);
+        const u32x4 vv = load_h4(static_cast<const float*>(raw) + (size_t)items[i0 + r].row_begin * K +
+                                 (size_t)(idx - r * q4) * 4, sy.wait != nullptr);
         const float f[4] = {__uint_as_float(vv.x), __uint_as_float(vv.y), __uint_as_float(vv.z),
                             __uint_as_float(vv.w)};
         uint32_t word = 0;
@@ -281,11 +341,64 @@ __global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
     if constexpr (SWIGLU) {
       const float u = __shfl_xor(v, 1, 64);  // odd row = up of the same neuron
       if (lane < 32 && (lane & 1) == 0)
-        out[(size_t)it.row_begin * out_ld + (row >> 1)] = tgemv::silu(v) * u;
+        store_h(out + (size_t)it.row_begin * out_ld + (row >> 1), tgemv::silu(v) * u,
+                sy.signal != nullptr);
     } else {
       if (lane < 32) out[(size_t)it.row_begin * out_ld + row] = v;
     }
   }
+  if (sy.signal != nullptr && nrb > 0) {
+    // every wave's device-scope h stores of the share have completed (vector-memory counter
+    // at zero) before the barrier, and the counts go out after it
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int g = b0 / rbi; g <= (b1 - 1) / rbi; ++g) {
+        const int lo = g * rbi > b0 ? g * rbi : b0, hi = (g + 1) * rbi < b1 ? (g + 1) * rbi : b1;
+        __hip_atomic_fetch_add(sy.signal + g, hi - lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+template <bool SWIGLU, int MAXRB>
+__global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
+    const void* __restrict__ raw, const int32_t* __restrict__ perm, int k,
+    const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+    const char* __restrict__ pool, size_t stride, size_t off_codes, size_t off_scales, int R,
+    int K, int out_ld, float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+  __shared__ float act_s[kStreamMaxItems];
+  __shared__ float wmax[16];
+  __shared__ unsigned row_max[kStreamMaxItems];
+  __shared__ float red[kDecNW][MAXRB][32];
+  const PassLds<MAXRB> L{lds, act_s, wmax, row_max, red};
+  decode_pass<SWIGLU, MAXRB>(raw, perm, k, items, n_items_p[0], pool, stride, off_codes, off_scales,
+                             R, K, out_ld, out, L, PassSync{nullptr, nullptr, 0, nullptr, 0});
+}
+
+// Both passes of a one-token call in one launch (one workgroup per compute unit, all
+// resident): each workgroup runs its gate/up share, counts it per group, then its down
+// share, whose weight loads and scale copies go out before it waits for the h rows.
+template <int MAXRB>
+__global__ __launch_bounds__(kDecNW * 64) void int4_decode_fused_kernel(
+    const void* __restrict__ x, const int32_t* __restrict__ perm, int k,
+    const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+    const char* __restrict__ pool, size_t stride, size_t off_w13, size_t off_s13, size_t off_w2,
+    size_t off_s2, int H, int F, float* __restrict__ hbuf, float* __restrict__ y,
+    int32_t* __restrict__ sync, int32_t* __restrict__ err, int spin_cap) {
+  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+  __shared__ float act_s[kStreamMaxItems];
+  __shared__ float wmax[16];
+  __shared__ unsigned row_max[kStreamMaxItems];
+  __shared__ float red[kDecNW][MAXRB][32];
+  const PassLds<MAXRB> L{lds, act_s, wmax, row_max, red};
+  const int n_items = n_items_p[0];
+  decode_pass<true, MAXRB>(x, perm, k, items, n_items, pool, stride, off_w13, off_s13, 2 * F, H, F,
+                           hbuf, L, PassSync{sync, nullptr, 0, err, spin_cap});
+  __syncthreads();  // the LDS of the first pass is free
+  decode_pass<false, MAXRB>(hbuf, perm, k, items, n_items, pool, stride, off_w2, off_s2, H, F, H, y,
+                            L, PassSync{nullptr, sync, 2 * F / 32, err, spin_cap});
 }
 
 template <bool SWIGLU, int MAXRB>
@@ -304,6 +417,20 @@ size_t decode_lds(bool swiglu, int max_items, int K, int maxrb) {
   return ((act + 15) & ~(size_t)15) + (size_t)maxrb * 64 * (K / 128);
 }
 
+// compute units of the current device (queried once)
+int decode_cus() {
+  static std::atomic<int> cus{0};
+  int n = cus.load(std::memory_order_relaxed);
+  if (n <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 }  // namespace
 
 bool decode_int4_fits(int max_items, int R, int K, bool swiglu) {
@@ -319,15 +446,7 @@ int launch_decode_int4(bool swiglu, const void* raw, const int32_t* perm, int k,
                        int K, int out_ld, float* out, hipStream_t s) {
   // the grid: one workgroup per compute unit (the kernel keeps 16 waves of up to 128
   // VGPRs and its LDS share resident); every share has at most ceil(blocks / grid) <= MAXRB
-  static std::atomic<int> cus{0};
-  int n = cus.load(std::memory_order_relaxed);
-  if (n <= 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus.store(n, std::memory_order_relaxed);
-  }
+  const int n = decode_cus();
   const long long blocks = (long long)max_items * (R / 32);
   long long grid = n;
   if (grid > blocks) grid = blocks;
@@ -346,5 +465,37 @@ int launch_decode_int4(bool swiglu, const void* raw, const int32_t* perm, int k,
                   : launch_rb<false, 16>(raw, perm, k, items, n_items, max_items, pool, stride,
                                          off_codes, off_scales, R, K, out_ld, out, s, grid,
                                          decode_lds(false, max_items, K, 16));
+  return MOE_EUNSUPPORTED;
+}
+
+int launch_decode_int4_fused(const void* x, const int32_t* perm, int k, const FfnItem* items,
+                             const int32_t* n_items, int max_items, const char* pool,
+                             size_t stride, size_t off_w13, size_t off_s13, size_t off_w2,
+                             size_t off_s2, int H, int F, float* hbuf, float* y, int32_t* sync,
+                             int32_t* err, hipStream_t s) {
+  if (!decode_int4_fits(max_items, 2 * F, H, true) || !decode_int4_fits(max_items, H, F, false))
+    return MOE_EUNSUPPORTED;
+  const int n = decode_cus();
+  // one workgroup per compute unit; one fits per unit (1024 threads of at most 128 VGPRs
+  // and over 80 KB of LDS), so the grid is resident at once and every wait ends
+  const long long b1 = (long long)max_items * (2 * F / 32), b2 = (long long)max_items * (H / 32);
+  const long long grid = n;
+  const long long per = ((b1 > b2 ? b1 : b2) + grid - 1) / grid;
+  constexpr int kSpinCap = 1 << 16;  // polls before a wait gives up (about 0.1 s; a normal wait is a few)
+  const size_t l1 = decode_lds(true, max_items, H, 16), l2 = decode_lds(false, max_items, F, 16);
+  size_t lds = l1 > l2 ? l1 : l2;
+  if (lds < 84 * 1024) lds = 84 * 1024;  // keeps a second workgroup off the unit
+  if (per <= 8) {
+    hipLaunchKernelGGL((int4_decode_fused_kernel<8>), dim3((unsigned)grid), dim3(kDecNW * 64), lds,
+                       s, x, perm, k, items, n_items, pool, stride, off_w13, off_s13, off_w2,
+                       off_s2, H, F, hbuf, y, sync, err, kSpinCap);
+    return moe_launch_status();
+  }
+  if (per <= 16) {
+    hipLaunchKernelGGL((int4_decode_fused_kernel<16>), dim3((unsigned)grid), dim3(kDecNW * 64), lds,
+                       s, x, perm, k, items, n_items, pool, stride, off_w13, off_s13, off_w2,
+                       off_s2, H, F, hbuf, y, sync, err, kSpinCap);
+    return moe_launch_status();
+  }
   return MOE_EUNSUPPORTED;
 }

@@ -41,9 +41,11 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ lut,
     const int32_t* __restrict__ mask, int E, int n_shared, int shared_slot0, int num_slots,
     int small_max, FfnItem* __restrict__ items, int32_t* __restrict__ n_items,
-    GemmTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_word) {
+    GemmTile* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ err_word,
+    int32_t* __restrict__ sync) {
   __shared__ int s_wave[40];
   const int e = threadIdx.x;
+  if (e < kStreamMaxItems) sync[e] = 0;  // the one-token FFN launch's hand-off counters
   int rows = 0, slot = -1, begin = 0;
   bool take = false;
   if (e < E + n_shared) {
@@ -206,9 +208,10 @@ long long resident_workgroups(const void* kern, int threads, size_t lds,
 void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
                      int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
                      int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
-                     hipStream_t s) {
+                     int32_t* sync, hipStream_t s) {
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, lut, mask, E, n_shared,
-                     shared_slot0, num_slots, small_max, items, n_items, tiles, n_tiles, err_word);
+                     shared_slot0, num_slots, small_max, items, n_items, tiles, n_tiles, err_word,
+                     sync);
 }
 
 int ffn_small_max(int T, int k, int E, int n_shared, int w_dtype) {
@@ -229,6 +232,8 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int F, int E, int k, int w_dtype
   // upper bound on MFMA tiles: sum over groups of ceil(rows / BM) <= rows / BM + groups
   w.max_tiles = (int)(rows / kGemmBM + (rows < groups ? rows : groups) + 1);
   size_t off = 256;  // n_items at offset 0, n_tiles at offset 4
+  w.sync = off;
+  off = align_up(off + kStreamMaxItems * sizeof(int32_t), 256);
   w.items = off;
   off = align_up(off + groups * sizeof(FfnItem), 256);
   w.tiles = off;
@@ -380,7 +385,8 @@ int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* o
 
   if (!planned)
     launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max,
-                    items, n_items, tiles, n_tiles, err_word, stream);
+                    items, n_items, tiles, n_tiles, err_word,
+                    reinterpret_cast<int32_t*>(wsb + ws.sync), stream);
   const char* pool = static_cast<const char*>(pool_base);
   if (bf16) {
     if (T <= 1)

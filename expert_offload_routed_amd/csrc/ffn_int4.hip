@@ -614,7 +614,7 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   if (max_tiles > 65535) return MOE_EUNSUPPORTED;
   if (!planned)
     launch_ffn_plan(offsets, lut, group_mask, E, n_shared, shared_slot0, num_slots, small_max,
-                    items, n_items, tiles, n_tiles, err, s);
+                    items, n_items, tiles, n_tiles, err, reinterpret_cast<int32_t*>(ws + wl.sync), s);
   const bool skinny = !split && T >= 2 && small_max > kGemvMaxRows;
   // with no MFMA tile (and no MFMA GEMV) every row is quantised by the GEMV workgroups
   // that read it (a decode step then runs two weight passes and no separate quantisation)
@@ -623,10 +623,14 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
     hipLaunchKernelGGL(quant_rows_kernel<MOE_BF16>, dim3(T), dim3(256), 0, s, x, H, nullptr,
                        nullptr, nullptr, 0, 0, 0, xq, xs);
   const int nt = T < kGemvMaxRows ? T : kGemvMaxRows;
-  // one token: both passes over even shares of the call's row blocks
+  // one token: both passes over even shares of the call's row blocks, in one launch when it fits
   if (T == 1 && !split && fused && max_items > 0 && decode_int4_fits(max_items, 2 * F, H, true) &&
       decode_int4_fits(max_items, H, F, false)) {
-    int rc = launch_decode_int4(true, x, perm, k, items, n_items, max_items, pool, stride,
+    int rc = launch_decode_int4_fused(x, perm, k, items, n_items, max_items, pool, stride,
+                                      lay.off_w13, lay.off_s13, lay.off_w2, lay.off_s2, H, F, hbuf,
+                                      y, reinterpret_cast<int32_t*>(ws + wl.sync), err, s);
+    if (rc != MOE_EUNSUPPORTED) return rc;
+    rc = launch_decode_int4(true, x, perm, k, items, n_items, max_items, pool, stride,
                                 lay.off_w13, lay.off_s13, 2 * F, H, F, hbuf, s);
     if (rc == MOE_OK)
       rc = launch_decode_int4(false, hbuf, perm, k, items, n_items, max_items, pool, stride,

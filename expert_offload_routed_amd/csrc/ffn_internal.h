@@ -37,6 +37,7 @@ struct SlotLayout {
 
 // Sections of the moe_expert_ffn workspace (byte offsets).
 struct FfnWorkspace {
+  size_t sync;  // kStreamMaxItems int32 counters, zeroed by whichever kernel writes the work list
   size_t items, tiles, h, xq, xs, hq, hs, total;
   int max_tiles;
 };
@@ -44,6 +45,13 @@ struct FfnWorkspace {
 // One-token int4 passes over even shares of row blocks (decode_int4.hip)
 constexpr int kStreamMaxItems = 64;  // groups of a one-token call they take
 bool decode_int4_fits(int max_items, int R, int K, bool swiglu);
+// Both one-token int4 passes in one launch, handing h over through the sync counters
+// (zero at launch); MOE_EUNSUPPORTED when the call does not fit it.
+int launch_decode_int4_fused(const void* x, const int32_t* perm, int k, const FfnItem* items,
+                             const int32_t* n_items, int max_items, const char* pool,
+                             size_t stride, size_t off_w13, size_t off_s13, size_t off_w2,
+                             size_t off_s2, int H, int F, float* hbuf, float* y, int32_t* sync,
+                             int32_t* err, hipStream_t s);
 
 static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -55,7 +63,7 @@ int slot_layout(int H, int F, int w_dtype, SlotLayout* out);
 void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* mask, int E,
                      int n_shared, int shared_slot0, int num_slots, int small_max, FfnItem* items,
                      int32_t* n_items, GemmTile* tiles, int32_t* n_tiles, int32_t* err_word,
-                     hipStream_t s);
+                     int32_t* sync, hipStream_t s);
 // One one-token int4 pass over the work list's items: the call's row blocks in one even
 // share per workgroup (pass 1 with the SwiGLU epilogue from the bf16 tokens; pass 2 from
 // the fp32 h rows). MOE_EUNSUPPORTED when a share would exceed 16 row blocks.
@@ -106,6 +114,7 @@ struct FrontPlan {
   GemmTile* tiles;
   int32_t* n_tiles;
   int32_t* err;
+  int32_t* sync;  // when set with lut: the FFN's kStreamMaxItems hand-off counters, zeroed
 };
 // moe_route_permute that, on its one-launch path, also writes the expert FFN's
 // work list described by *plan when plan->lut is set (*planned = true; otherwise

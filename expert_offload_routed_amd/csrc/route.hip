@@ -364,6 +364,8 @@ __device__ void front_plan(const FrontPlan& pl, int T, int E, int k, const Front
     pl.n_items[0] = tot_it;
     pl.n_tiles[0] = tot_tl;
   }
+  if (pl.sync)  // the one-token FFN launch's hand-off counters start at zero
+    for (int i = tid; i < kStreamMaxItems; i += nthr) pl.sync[i] = 0;
 }
 
 template <int NV>
@@ -847,6 +849,8 @@ __global__ __launch_bounds__(64) void decode_select_kernel(
       pl.n_items[0] = as_item ? n_taken : 0;
       pl.n_tiles[0] = as_item ? 0 : n_taken;
     }
+    if (pl.sync)  // the one-token FFN launch's hand-off counters start at zero
+      for (int i = lane; i < kStreamMaxItems; i += 64) pl.sync[i] = 0;
   }
 }
 

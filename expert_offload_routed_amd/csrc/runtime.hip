@@ -1100,6 +1100,7 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
     fp.tiles = reinterpret_cast<GemmTile*>(c->ws + wl.tiles);
     fp.n_tiles = reinterpret_cast<int32_t*>(c->ws + 4);
     fp.err = c->err;
+    fp.sync = reinterpret_cast<int32_t*>(c->ws + wl.sync);
   }
   if ((rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
                                c->topw, c->counts, c->offsets, c->perm, c->inv, dd, dd + E, c->sync,

@@ -65,6 +65,8 @@ enum { MOE_OK = 0, MOE_EINVAL = -1, MOE_EUNSUPPORTED = -2, MOE_EHIP = -3 };
 /* device error-word bits */
 #define MOE_ERR_ABSENT 1    /* a routed expert had no slot (table entry -1); its rows were skipped */
 #define MOE_ERR_STALE_TAG 2 /* a commit found another tag in the slot; table left unchanged */
+#define MOE_ERR_SYNC 4      /* a one-token expert FFN launch waited past its limit for h rows of
+                               other workgroups (not all resident at once); its y is invalid */
 
 /* ------------------------------------------------------------------ gating -
  * moe_route: router logits, top-k selection and routing weights.
@@ -252,7 +254,11 @@ int moe_quantize_rows_int8(const void* in, int in_dtype, int rows, int K, int8_t
  *   pool_base, slot_stride, num_slots: the slot pool; w_dtype the weight format
  *   y_perm    [T*k,H] fp32 out: rows of skipped groups are left untouched
  *   err_word  [1] int32: MOE_ERR_ABSENT is OR-ed in when a selected group's
- *             lut entry is -1 or not below num_slots (that group is skipped)
+ *             lut entry is -1 or not below num_slots (that group is skipped);
+ *             MOE_ERR_SYNC when the one-token int4 launch (both passes in one
+ *             launch, one workgroup per compute unit) could not hand h over
+ *             between its workgroups within its wait limit, as when another
+ *             kernel holds compute units meanwhile (y_perm is then invalid)
  *   workspace device buffer of ws_bytes >= moe_ffn_workspace_bytes(...)
  * With MOE_INT4G128_RESPLIT, group_mask[e] picks the precision of routed
  * group e (RapidMoE Algorithm 1): 0 skips it, 1 runs it on W^L (the
