@@ -27,6 +27,8 @@
 namespace {
 
 constexpr int kDecNW = 16;  // waves per workgroup
+constexpr int kDecWgPerCu = 16 / kDecNW;  // workgroups resident per compute unit
+constexpr int kTokRegs = (8192 + 8 * kDecNW * 64 - 1) / (8 * kDecNW * 64);  // token row: K <= 8192
 constexpr int kDecP = 8;    // chunks in flight per lane
 
 // SWIGLU (gate/up pass): one token row for every group (row perm[p] / k of the bf16
@@ -91,6 +93,8 @@ __device__ __forceinline__ void decode_pass(
   const int b0 = (int)((long long)total_rb * blockIdx.x / gridDim.x);
   const int b1 = (int)((long long)total_rb * (blockIdx.x + 1) / gridDim.x);
   const int nrb = b1 - b0;  // <= MAXRB (the launch checks)
+  // an empty share (more workgroups than row blocks) has nothing to load, wait for or count
+  if (nrb == 0) return;
   const size_t act_bytes = (size_t)(SWIGLU ? 1 : n_items) * K;
   int8_t* act_q = lds;
   uint16_t* sc_lds = reinterpret_cast<uint16_t*>(lds + ((act_bytes + 15) & ~(size_t)15));
@@ -134,31 +138,64 @@ __device__ __forceinline__ void decode_pass(
     if (sum_at.c + 1 == c1) flush(sum_at.r);  // uniform: the row block's slice is done
     advance(sum_at);
   };
-  // the first kDecP chunks go out before the staging below, so their latency overlaps it
-  u32x4 buf[kDecP];
-  if (nq > 0) {
-    at_block(sum_at, 0);
-    at_block(load_at, 0);
+  // Vector loads return in issue order, so a wait for a value also waits for every load
+  // issued before it. The loads the staging below needs (the share's scales, and the token
+  // row of the gate/up pass) therefore go out first, then the first kDecP weight chunks,
+  // which stay in flight while the staging waits for the earlier ones.
+  // The share's scales: row block r's 64 G bytes, 16 bytes per thread, the first
+  // kScaleRegs pieces of each thread held in registers until the staging.
+  constexpr int kScaleRegs = 2;
+  const int sbytes = 64 * G, per = sbytes / 16, nsc = nrb * per;
+  auto scale_src = [&](int i, int& dst) {
+    const int r = i / per, o = (i - r * per) * 16;
+    const int b = b0 + r, item = b / rbi, rb = b - item * rbi;
+    dst = r * sbytes + o;
+    return pool + (size_t)items[item].slot * stride + off_scales + (size_t)rb * sbytes + o;
+  };
+  u32x4 sreg[kScaleRegs];
+  int sdst[kScaleRegs];
+  // These loads are issued by every lane (indexes past the end are clamped to valid ones,
+  // whose values are not used), so the waits before their first use count only the loads
+  // issued after them.
 #pragma unroll
-    for (int i = 0; i < kDecP; ++i) {
-      buf[i] = ld16_stream(load_at.base + (size_t)load_at.c * 1024);
-      advance(load_at);
+  for (int u = 0; u < kScaleRegs; ++u) {
+    const int i = (int)threadIdx.x + u * (int)blockDim.x;
+    sreg[u] = ld16(scale_src(i < nsc ? i : nsc - 1, sdst[u]));
+  }
+  // the token row (bf16; every group reads the same one): eight values per thread and register
+  u32x4 tok[kTokRegs];
+  if constexpr (SWIGLU) {
+    const uint16_t* trow = static_cast<const uint16_t*>(raw) + (size_t)(perm[items[0].row_begin] / k) * K;
+#pragma unroll
+    for (int u = 0; u < kTokRegs; ++u) {
+      const int e = ((int)threadIdx.x + u * (int)blockDim.x) * 8;
+      tok[u] = ld16(trow + (e < K ? e : K - 8));
     }
   }
-  // the share's scales: row block r's 64 G bytes, copied 16 bytes per thread
-  {
-    const int sbytes = 64 * G;
-    const int per = sbytes / 16;
-    for (int i = threadIdx.x; i < nrb * per; i += blockDim.x) {
-      const int r = i / per, o = (i - r * per) * 16;
-      const int b = b0 + r, item = b / rbi, rb = b - item * rbi;
-      const char* src = pool + (size_t)items[item].slot * stride + off_scales + (size_t)rb * sbytes + o;
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(sc_lds) + (size_t)r * sbytes + o) = ld16(src);
-    }
+  __builtin_amdgcn_sched_barrier(0);
+  // nq > 0: a share has a row block and every wave a chunk of it (K / 64 >= 16 waves)
+  u32x4 buf[kDecP];
+  at_block(sum_at, 0);
+  at_block(load_at, 0);
+#pragma unroll
+  for (int i = 0; i < kDecP; ++i) {
+    buf[i] = ld16_stream(load_at.base + (size_t)load_at.c * 1024);
+    advance(load_at);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < kScaleRegs; ++u) {
+    const int i = (int)threadIdx.x + u * (int)blockDim.x;
+    if (i < nsc) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(sc_lds) + sdst[u]) = sreg[u];
+  }
+  for (int i = (int)threadIdx.x + kScaleRegs * (int)blockDim.x; i < nsc; i += blockDim.x) {
+    int dst;
+    const char* src = scale_src(i, dst);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(sc_lds) + dst) = ld16(src);
   }
   // one launch: the h rows this share reads are complete once every row block of their
   // groups is counted (weights and scales above do not depend on them)
-  if (sy.wait != nullptr && nrb > 0) {
+  if (sy.wait != nullptr) {
     if (threadIdx.x == 0) {
       const int g0 = b0 / rbi, g1 = (b1 - 1) / rbi;
       bool late = false;
@@ -179,24 +216,25 @@ __device__ __forceinline__ void decode_pass(
   }
   // the activation rows, quantised into LDS (same rule and codes as quant_rows_kernel)
   if constexpr (SWIGLU) {
-    // the token row (bf16; every group reads the same one): eight values per thread, loaded
-    // once and held in registers (K <= 8 * blockDim, which the launch checks), a block-wide
-    // max, then the codes: s = max|v| / 127 (1 for a zero row), q = clip(rint(v / s), -127, 127)
-    if (n_items > 0) {
-      const int e0 = (int)threadIdx.x * 8;
-      float v[8];
+    // the token row, held in registers (K <= 8 * kTokRegs * blockDim, which the launch checks): a
+    // block-wide max, then the codes: s = max|v| / 127 (1 for a zero row),
+    // q = clip(rint(v / s), -127, 127)
+    {
+      float v[kTokRegs][8];
       float amax = 0.f;
-      if (e0 < K) {
-        const u32x4 w = ld16(static_cast<const uint16_t*>(raw) +
-                             (size_t)(perm[items[0].row_begin] / k) * K + e0);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = __uint_as_float(ww[i] << 16);
-          v[2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+      for (int u = 0; u < kTokRegs; ++u) {
+        const int e = ((int)threadIdx.x + u * (int)blockDim.x) * 8;
+        if (e < K) {
+          const uint32_t ww[4] = {tok[u].x, tok[u].y, tok[u].z, tok[u].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[u][2 * i] = __uint_as_float(ww[i] << 16);
+            v[u][2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
       }
       amax = wave_max(amax);
       if (lane == 0) wmax[wave] = amax;
@@ -205,20 +243,24 @@ __device__ __forceinline__ void decode_pass(
 #pragma unroll
       for (int w = 0; w < kDecNW; ++w) m = fmaxf(m, wmax[w]);
       const float sc = (m == 0.f) ? 1.f : m / 127.f;
-      if (e0 < K) {
-        uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float r = rintf(v[i] / sc);
-          r = fminf(fmaxf(r, -127.f), 127.f);
-          const uint32_t b = (uint32_t)((int)r & 0xFF);
-          if (i < 4) w0 |= b << (8 * i); else w1 |= b << (8 * (i - 4));
+      for (int u = 0; u < kTokRegs; ++u) {
+        const int e = ((int)threadIdx.x + u * (int)blockDim.x) * 8;
+        if (e < K) {
+          uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float r = rintf(v[u][i] / sc);
+            r = fminf(fmaxf(r, -127.f), 127.f);
+            const uint32_t b = (uint32_t)((int)r & 0xFF);
+            if (i < 4) w0 |= b << (8 * i); else w1 |= b << (8 * (i - 4));
+          }
+          *reinterpret_cast<uint2*>(act_q + e) = make_uint2(w0, w1);
         }
-        *reinterpret_cast<uint2*>(act_q + e0) = make_uint2(w0, w1);
       }
       if (threadIdx.x == 0) act_s[0] = sc;
     }
-  } else if (nrb > 0) {
+  } else {
     // only the h rows of the share's groups (one or two for a large R): every thread loads
     // its float4s of those rows at once (a row-wide max through an LDS max over the float
     // bits, which order like the values for |v|), then quantises them from registers:
@@ -300,7 +342,7 @@ __device__ __forceinline__ void decode_pass(
   }
   __syncthreads();
 
-  if (nq > 0) {
+  {
     int q0 = 0;
     for (; q0 + 2 * kDecP <= nq; q0 += kDecP) {
 #pragma unroll
@@ -347,7 +389,7 @@ __device__ __forceinline__ void decode_pass(
       if (lane < 32) out[(size_t)it.row_begin * out_ld + row] = v;
     }
   }
-  if (sy.signal != nullptr && nrb > 0) {
+  if (sy.signal != nullptr) {
     // every wave's device-scope h stores of the share have completed (vector-memory counter
     // at zero) before the barrier, and the counts go out after it
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
@@ -362,7 +404,7 @@ __device__ __forceinline__ void decode_pass(
 }
 
 template <bool SWIGLU, int MAXRB>
-__global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
+__global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(4))) void int4_decode_kernel(
     const void* __restrict__ raw, const int32_t* __restrict__ perm, int k,
     const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
     const char* __restrict__ pool, size_t stride, size_t off_codes, size_t off_scales, int R,
@@ -381,7 +423,8 @@ __global__ __launch_bounds__(kDecNW * 64) void int4_decode_kernel(
 // resident): each workgroup runs its gate/up share, counts it per group, then its down
 // share, whose weight loads and scale copies go out before it waits for the h rows.
 template <int MAXRB>
-__global__ __launch_bounds__(kDecNW * 64) void int4_decode_fused_kernel(
+__global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(4))) void
+int4_decode_fused_kernel(
     const void* __restrict__ x, const int32_t* __restrict__ perm, int k,
     const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
     const char* __restrict__ pool, size_t stride, size_t off_w13, size_t off_s13, size_t off_w2,
@@ -435,7 +478,7 @@ int decode_cus() {
 
 bool decode_int4_fits(int max_items, int R, int K, bool swiglu) {
   if (max_items < 1 || max_items > kStreamMaxItems || R % 32 != 0 || K % 128 != 0 ||
-      K / 64 < kDecNW || (swiglu && K > 8 * kDecNW * 64))
+      K / 64 < kDecNW || (swiglu && K > 8 * kTokRegs * kDecNW * 64))
     return false;
   return decode_lds(swiglu, max_items, K, 16) <= 96 * 1024;
 }
@@ -444,11 +487,11 @@ int launch_decode_int4(bool swiglu, const void* raw, const int32_t* perm, int k,
                        const FfnItem* items, const int32_t* n_items, int max_items,
                        const char* pool, size_t stride, size_t off_codes, size_t off_scales, int R,
                        int K, int out_ld, float* out, hipStream_t s) {
-  // the grid: one workgroup per compute unit (the kernel keeps 16 waves of up to 128
-  // VGPRs and its LDS share resident); every share has at most ceil(blocks / grid) <= MAXRB
+  // the grid: the workgroups the compute units keep resident (16 waves of up to 128 VGPRs
+  // per unit); every share has at most ceil(blocks / grid) <= MAXRB
   const int n = decode_cus();
   const long long blocks = (long long)max_items * (R / 32);
-  long long grid = n;
+  long long grid = (long long)n * kDecWgPerCu;
   if (grid > blocks) grid = blocks;
   const long long per = (blocks + grid - 1) / grid;
   if (per <= 8)
@@ -476,15 +519,23 @@ int launch_decode_int4_fused(const void* x, const int32_t* perm, int k, const Ff
   if (!decode_int4_fits(max_items, 2 * F, H, true) || !decode_int4_fits(max_items, H, F, false))
     return MOE_EUNSUPPORTED;
   const int n = decode_cus();
-  // one workgroup per compute unit; one fits per unit (1024 threads of at most 128 VGPRs
-  // and over 80 KB of LDS), so the grid is resident at once and every wait ends
+  // kDecWgPerCu workgroups per compute unit, exactly as many as fit on one (16 waves of at
+  // most 128 VGPRs; the LDS request below admits no more), so the grid is resident at once
+  // and every wait ends
   const long long b1 = (long long)max_items * (2 * F / 32), b2 = (long long)max_items * (H / 32);
-  const long long grid = n;
+  const long long grid = (long long)n * kDecWgPerCu;
   const long long per = ((b1 > b2 ? b1 : b2) + grid - 1) / grid;
   constexpr int kSpinCap = 1 << 16;  // polls before a wait gives up (about 0.1 s; a normal wait is a few)
-  const size_t l1 = decode_lds(true, max_items, H, 16), l2 = decode_lds(false, max_items, F, 16);
+  const int maxrb = per <= 8 ? 8 : 16;
+  const size_t l1 = decode_lds(true, max_items, H, maxrb), l2 = decode_lds(false, max_items, F, maxrb);
   size_t lds = l1 > l2 ? l1 : l2;
-  if (lds < 84 * 1024) lds = 84 * 1024;  // keeps a second workgroup off the unit
+  // 160 KB of LDS per unit: a workgroup's total (this request plus its static arrays) above
+  // 160 / (kDecWgPerCu + 1) KB keeps one more off the unit; at most 160 / kDecWgPerCu KB
+  // lets kDecWgPerCu share it
+  const size_t stat = sizeof(float) * (2 * kStreamMaxItems + 16 + (size_t)kDecNW * maxrb * 32);
+  const size_t lo = 160 * 1024 / (kDecWgPerCu + 1) + 1024, hi = 160 * 1024 / kDecWgPerCu - 512;
+  if (lds + stat < lo) lds = lo - stat;
+  if (lds + stat > hi) return MOE_EUNSUPPORTED;
   if (per <= 8) {
     hipLaunchKernelGGL((int4_decode_fused_kernel<8>), dim3((unsigned)grid), dim3(kDecNW * 64), lds,
                        s, x, perm, k, items, n_items, pool, stride, off_w13, off_s13, off_w2,
