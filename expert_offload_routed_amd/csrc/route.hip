@@ -19,6 +19,8 @@
 //     256 threads split H into 8-element vectors (16-byte bf16 / 2x16-byte
 //     fp32 loads), fp32 FMA, then a wave and a cross-wave reduction. A decode
 //     step pulls w_router from HBM with E workgroups at once.
+//   route_logits1_kernel: one token: one workgroup of 512 threads per expert,
+//     every load of the router row and the token issued before the first FMA.
 //   topk_softmax_kernel: one wave per token; lane l holds logits l, l+64, ...
 //     Each of the k rounds takes the wave-wide (value desc, id asc) maximum
 //     through xor shuffles; then softmax over the selected values.
@@ -96,6 +98,80 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
     const int t = threadIdx.x;
     const float s = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
     logits[(size_t)(t0 + t) * E + e] = s + (bias ? bias[e] : 0.f);
+  }
+}
+
+// One token: one workgroup of 512 threads per expert. Every thread issues all its NCH
+// loads of 8-value chunks of the router row and of the token before its first FMA, so a
+// logit costs one memory round trip rather than one per chunk. Chunks past H load a valid
+// chunk again and leave the sum unchanged (a select, so no branch takes the loads apart
+// from the sums).
+constexpr int kLg1Threads = 512;
+constexpr int kLg1MaxChunks = 4;  // H <= 512 * 8 * 4
+template <int FMT, int NCH>
+__global__ __launch_bounds__(kLg1Threads) void route_logits1_kernel(
+    const void* __restrict__ x, const void* __restrict__ w, const float* __restrict__ bias, int H,
+    int E, float* __restrict__ logits) {
+  __shared__ float red[kLg1Threads / 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x;
+  // raw 16-byte words (bf16: one per chunk, fp32: two), unpacked only after every load is out
+  constexpr int WPC = FMT == MOE_BF16 ? 1 : 2;
+  u32x4 wr[NCH][WPC], xr[NCH][WPC];
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int c = ((int)threadIdx.x + u * kLg1Threads) * 8;
+    const size_t cc = (size_t)(c < H ? c : H - 8);
+    const char* wp = static_cast<const char*>(w) + ((size_t)e * H + cc) * (FMT == MOE_BF16 ? 2 : 4);
+    const char* xp = static_cast<const char*>(x) + cc * (FMT == MOE_BF16 ? 2 : 4);
+#pragma unroll
+    for (int j = 0; j < WPC; ++j) {
+      wr[u][j] = ld16(wp + 16 * j);
+      xr[u][j] = ld16(xp + 16 * j);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load out before the first use
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    float wv[8], xv[8];
+    if constexpr (FMT == MOE_BF16) {
+      const uint32_t a[4] = {wr[u][0].x, wr[u][0].y, wr[u][0].z, wr[u][0].w};
+      const uint32_t b[4] = {xr[u][0].x, xr[u][0].y, xr[u][0].z, xr[u][0].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wv[2 * i] = bf16_lo(a[i]);
+        wv[2 * i + 1] = bf16_hi(a[i]);
+        xv[2 * i] = bf16_lo(b[i]);
+        xv[2 * i + 1] = bf16_hi(b[i]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t a[4] = {wr[u][j].x, wr[u][j].y, wr[u][j].z, wr[u][j].w};
+        const uint32_t b[4] = {xr[u][j].x, xr[u][j].y, xr[u][j].z, xr[u][j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wv[4 * j + i] = __uint_as_float(a[i]);
+          xv[4 * j + i] = __uint_as_float(b[i]);
+        }
+      }
+    }
+    const bool in = ((int)threadIdx.x + u * kLg1Threads) * 8 < H;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float f = fmaf(wv[q], xv[q], acc);
+      acc = in ? f : acc;
+    }
+  }
+  const float v = wave_sum(acc);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kLg1Threads / 64; ++i) s += red[i];
+    logits[e] = s + (bias ? bias[e] : 0.f);
   }
 }
 
@@ -662,8 +738,9 @@ __global__ __launch_bounds__(1024) void select_sort_kernel(
 // Second half of the front end for one token, in one wave: top-k (topk_token), the
 // routing scores, then every output written straight from registers. With one token each
 // selected expert holds exactly one assignment, so the counting sort reduces to ranking
-// the k selected ids: assignment r goes to sorted position rank(r) = #{selected ids <
-// id_r}, counts are 0/1 and offsets[e] = #{selected ids < e}. The FFN work list (when
+// the selected ids: the valid ones (finite logits) take sorted positions in id order, so
+// offsets[e] = #{valid selected ids < e} and counts are 0/1, both read off the selection
+// ballots; invalid assignments follow them in selection order. The FFN work list (when
 // pl.lut is set) is the plan kernel's: the routed groups in id order, then the shared
 // groups, each of one row, groups whose slot is out of range skipped and flagged.
 constexpr int kDecodeSelectMaxK = 64;
@@ -681,15 +758,17 @@ __global__ __launch_bounds__(64) void decode_select_kernel(
     float* __restrict__ weights, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* __restrict__ distinct,
     int32_t* __restrict__ n_distinct, FrontPlan pl) {
-  __shared__ uint32_t s_key[kDecodeSelectMaxK];
-  __shared__ int s_cid[kDecodeSelectMaxK];  // candidate id (for ties), in id order
+  __shared__ uint32_t s_key[kDecodeSelectMaxK];  // candidates in id order: key, id, value,
+  __shared__ int s_cid[kDecodeSelectMaxK];       // sorted position (-1: invalid)
   __shared__ float s_cv[kDecodeSelectMaxK];
-  __shared__ int s_ids[kDecodeSelectMaxK];  // selection order r: expert (or -1)
+  __shared__ int s_cpos[kDecodeSelectMaxK];
+  __shared__ int s_ids[kDecodeSelectMaxK];  // selection order r: expert (or -1), value, position
   __shared__ float s_sel[kDecodeSelectMaxK];
+  __shared__ int s_pos[kDecodeSelectMaxK];
   const int lane = threadIdx.x;
   float v[NV];
   uint32_t key[NV];
-  int lutv[NV];  // slot-table entries, loaded with the logits (the plan looks them up by id)
+  int lutv[NV];  // slot-table entries, loaded with the logits
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
@@ -712,21 +791,45 @@ __global__ __launch_bounds__(64) void decode_select_kernel(
 #pragma unroll
   for (int i = 0; i < NV; ++i) n_gt += __popcll(__ballot(key[i] > tau));
   const int need = k - n_gt;
-  int eq_before = 0, base = 0;
+  const bool as_item = 1 <= pl.small_max;
+  // in id order: candidates, counts and offsets of the valid selected ids, and the work
+  // list's routed groups (valid selected ids whose slot is in range)
+  int eq_before = 0, base = 0, vbase = 0, tbase = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
     const uint64_t meq = __ballot(key[i] == tau);
     const bool sel = key[i] > tau || (key[i] == tau && eq_before + popc_below(meq) < need);
     eq_before += __popcll(meq);
-    const uint64_t ms = __ballot(sel);
+    const bool val = sel && key[i] != 0u;
+    const uint64_t ms = __ballot(sel), mv = __ballot(val);
+    const int vpos = vbase + popc_below(mv);  // #{valid selected ids < e}
+    if (e < E) {
+      counts[e] = val ? 1 : 0;
+      offsets[e] = vpos;
+    }
     if (sel) {
-      const int p = base + popc_below(ms);  // candidates in id order
+      const int p = base + popc_below(ms);
       s_key[p] = key[i];
-      s_cid[p] = lane + 64 * i;
+      s_cid[p] = e;
       s_cv[p] = v[i];
+      s_cpos[p] = val ? vpos : -1;
+    }
+    if (pl.lut) {
+      const bool take = val && lutv[i] >= 0 && lutv[i] < pl.num_slots;
+      if (val && !take) atomicOr(pl.err, MOE_ERR_ABSENT);
+      const uint64_t mt = __ballot(take);
+      if (take) {
+        const int q = tbase + popc_below(mt);
+        if (as_item) pl.items[q] = FfnItem{e, lutv[i], vpos, 1};
+        else pl.tiles[q] = GemmTile{e, lutv[i], vpos, 1};
+      }
+      tbase += __popcll(mt);
     }
     base += __popcll(ms);
+    vbase += __popcll(mv);
   }
+  const int nvalid = vbase;
   __syncthreads();
   // selection order: (value desc, id asc), i.e. key desc, id asc
   if (lane < k) {
@@ -739,10 +842,15 @@ __global__ __launch_bounds__(64) void decode_select_kernel(
     }
     s_ids[r] = mk == 0u ? -1 : mi;
     s_sel[r] = s_cv[lane];
+    s_pos[r] = s_cpos[lane];
   }
   __syncthreads();
   const float vmax = s_sel[0];
   const float sel = lane < k ? s_sel[lane] : 0.f;
+  // exp(v - max) of every logit, for the weights over all E and for the scores
+  float ex[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) ex[i] = lane + 64 * i < E ? expf(v[i] - vmax) : 0.f;
   // routing weights: softmax over the selected (renorm) or over all E, as topk_token forms it
   float denom = 0.f;
   if (renorm) {
@@ -750,38 +858,21 @@ __global__ __launch_bounds__(64) void decode_select_kernel(
   } else {
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      if (lane + 64 * i < E) denom += expf(v[i] - vmax);
+      if (lane + 64 * i < E) denom += ex[i];
   }
   denom = wave_sum(denom);
   const float w_mine = lane < k ? expf(sel - vmax) / denom : 0.f;
   const int my = lane < k ? s_ids[lane] : -1;
-  const bool valid = my >= 0 && my < E;
+  const bool valid = my >= 0;
   // sorted position: valid ids in ascending order, then the invalid assignments in order
-  int below = 0, nvalid = 0, inval_before = 0;
-  for (int j = 0; j < k; ++j) {
-    const int o = s_ids[j];
-    const bool ov = o >= 0 && o < E;
-    nvalid += ov ? 1 : 0;
-    below += (ov && valid && o < my) ? 1 : 0;
-    inval_before += (!ov && j < lane) ? 1 : 0;
-  }
+  const int inval_before = popc_below(__ballot(lane < k && !valid));
   if (lane < k) {
-    const int pos = valid ? below : nvalid + inval_before;
+    const int pos = valid ? s_pos[lane] : nvalid + inval_before;
     ids[lane] = my;
     weights[lane] = w_mine;
     perm[pos] = lane;
     inv[lane] = pos;
     if (valid) distinct[pos] = my;
-  }
-  for (int e = lane; e < E; e += 64) {
-    int c = 0, o = 0;
-    for (int j = 0; j < k; ++j) {
-      const int id = s_ids[j];
-      c += (id == e) ? 1 : 0;
-      o += (id >= 0 && id < e) ? 1 : 0;
-    }
-    counts[e] = c;
-    offsets[e] = o;
   }
   if (lane == 0) {
     offsets[E] = nvalid;
@@ -789,63 +880,37 @@ __global__ __launch_bounds__(64) void decode_select_kernel(
   }
   if (pl.scores) {  // each expert's softmax probability (one token: the average is the value)
     // the normaliser as token_softmax_norm forms it (max of every logit = the first selected)
-    const float m = vmax;
     float sm = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      if (lane + 64 * i < E) sm += expf(v[i] - m);
+      if (lane + 64 * i < E) sm += ex[i];
     sm = wave_sum(sm);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = lane + 64 * i;
       if (e >= E) continue;
       float acc = 0.f;
-      acc += expf(v[i] - m) / sm;
+      acc += ex[i] / sm;
       const float sc = acc / 1.f;
       pl.scores[e] = sc;
       if (pl.crit) pl.crit[e] = sc >= pl.crit_threshold ? 2 : 1;
     }
   }
   if (pl.lut) {
-    // group g of this lane: routed lane r < k holds its selected expert (position `below`
-    // among the routed groups), lane k + s the shared group E + s
+    // the shared groups E + s after the routed ones, lane s holding group E + s (row k + s)
     const int ns = pl.n_shared;
-    const bool routed = lane < k && valid;
-    const bool shared = lane >= k && lane < k + ns;
-    int slot = -1, g = -1, begin = 0;
-    // slot of the selected id: entry my % 64 of every lane's register my / 64 (a uniform loop)
-    int lut_my = -1;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int got = __shfl(lutv[i], (my >= 0 ? my : 0) & 63, 64);
-      if (my >= 0 && (my >> 6) == i) lut_my = got;
-    }
-    if (routed) {
-      g = my;
-      slot = lut_my;
-      begin = below;
-    } else if (shared) {
-      g = E + (lane - k);
-      slot = pl.shared_slot0 + (lane - k);
-      begin = k + (lane - k);
-    }
-    const bool take = (routed || shared) && slot >= 0 && slot < pl.num_slots;
-    if ((routed || shared) && !take) atomicOr(pl.err, MOE_ERR_ABSENT);
-    // position among the taken groups in group order: routed ones by id, shared after them
-    const unsigned long long taken = __ballot(take);
-    int pos = 0;
-    for (int j = 0; j < k + ns && j < 64; ++j) {
-      if (!((taken >> j) & 1ull)) continue;
-      const int gj = __shfl(g, j, 64);
-      pos += (gj < g) ? 1 : 0;
-    }
-    const int n_taken = __popcll(taken);
-    const bool as_item = 1 <= pl.small_max;
+    const bool shared = lane < ns;
+    const int slot = pl.shared_slot0 + lane;
+    const bool take = shared && slot >= 0 && slot < pl.num_slots;
+    if (shared && !take) atomicOr(pl.err, MOE_ERR_ABSENT);
+    const uint64_t mt = __ballot(take);
     if (take) {
-      if (as_item) pl.items[pos] = FfnItem{g, slot, begin, 1};
-      else pl.tiles[pos] = GemmTile{g, slot, begin, 1};
+      const int q = tbase + popc_below(mt);
+      if (as_item) pl.items[q] = FfnItem{E + lane, slot, k + lane, 1};
+      else pl.tiles[q] = GemmTile{E + lane, slot, k + lane, 1};
     }
     if (lane == 0) {
+      const int n_taken = tbase + __popcll(mt);
       pl.n_items[0] = as_item ? n_taken : 0;
       pl.n_tiles[0] = as_item ? 0 : n_taken;
     }
@@ -859,7 +924,22 @@ int launch_logits(const void* x, int x_dtype, const void* w_router, const float*
                   int H, int E, float* logits, hipStream_t stream) {
   dim3 g1(E, (T + kRouteTT - 1) / kRouteTT);
   if (g1.y > 65535u) return MOE_EUNSUPPORTED;
-  if (x_dtype == MOE_BF16 && T >= 64 && E >= 32 && H % kLgK == 0)
+  if (T == 1 && H <= kLg1Threads * 8 * kLg1MaxChunks) {
+    const int nch = (H + kLg1Threads * 8 - 1) / (kLg1Threads * 8);
+#define MOE_LG1(FMT_, NCH_)                                                                    \
+  hipLaunchKernelGGL((route_logits1_kernel<FMT_, NCH_>), dim3(E), dim3(kLg1Threads), 0, stream, x, \
+                     w_router, bias, H, E, logits)
+    if (x_dtype == MOE_BF16) {
+      if (nch == 1) MOE_LG1(MOE_BF16, 1);
+      else if (nch == 2) MOE_LG1(MOE_BF16, 2);
+      else MOE_LG1(MOE_BF16, 4);
+    } else {
+      if (nch == 1) MOE_LG1(MOE_F32, 1);
+      else if (nch == 2) MOE_LG1(MOE_F32, 2);
+      else MOE_LG1(MOE_F32, 4);
+    }
+#undef MOE_LG1
+  } else if (x_dtype == MOE_BF16 && T >= 64 && E >= 32 && H % kLgK == 0)
     hipLaunchKernelGGL(route_logits_mfma_kernel, dim3((T + kLgRows - 1) / kLgRows, (E + kLgRows - 1) / kLgRows),
                        dim3(512), 0, stream, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(w_router), bias, T, H, E, logits);
