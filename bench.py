@@ -181,7 +181,7 @@ def recorded_traffic(*keys):
 
 # the sources the expert-FFN kernels are compiled from (routing, runtime and combine excluded)
 FFN_SOURCES = ("common.h", "ffn_internal.h", "ffn.hip", "ffn_gemv.h", "tile_gemv.h", "gemm.hip",
-               "skinny.hip", "ffn_int4.hip", "decode_int4.hip")
+               "skinny.hip", "ffn_int4.hip", "decode_share.h", "decode_int4.hip", "decode_bf16.hip")
 
 
 def ffn_sources_sha1() -> str:

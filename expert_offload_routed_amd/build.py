@@ -21,7 +21,7 @@ LIB_NAME = "libmoe_offload.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["route.hip", "permute.hip", "ffn.hip", "ffn_int4.hip", "gemm.hip", "skinny.hip",
-           "decode_int4.hip", "combine.hip", "slots.hip", "split.hip", "runtime.hip"]
+           "decode_int4.hip", "decode_bf16.hip", "combine.hip", "slots.hip", "split.hip", "runtime.hip"]
 ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

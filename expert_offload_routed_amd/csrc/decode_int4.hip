@@ -21,15 +21,15 @@
 // Numerics are those of the int4 GEMV: per chunk the exact int32 dot of 16 q
 // with the int8 row, times the group scale / 16, accumulated in fp32.
 #include "common.h"
+#include "decode_share.h"
 #include "ffn_internal.h"
 #include "tile_gemv.h"
 
 namespace {
 
-constexpr int kDecNW = 16;  // waves per workgroup
-constexpr int kDecWgPerCu = 16 / kDecNW;  // workgroups resident per compute unit
+using namespace decode_share;
+
 constexpr int kTokRegs = (8192 + 8 * kDecNW * 64 - 1) / (8 * kDecNW * 64);  // token row: K <= 8192
-constexpr int kDecP = 8;    // chunks in flight per lane
 
 // SWIGLU (gate/up pass): one token row for every group (row perm[p] / k of the bf16
 // tokens; T = 1), out = h (fp32, row p, column n of rows 2n, 2n+1).
@@ -43,20 +43,6 @@ struct PassLds {
   float* wmax;       // [16]
   unsigned* row_max; // [kStreamMaxItems]
   float (*red)[MAXRB][32];  // [kDecNW]
-};
-
-// Cross-workgroup hand-off of the one-launch form (both passes in one kernel): the gate/up
-// pass writes h with device-scope stores and, once they have completed, adds per group the
-// row blocks it finished to signal[group]; the down pass waits, before it reads h (with
-// device-scope loads), until wait[group] holds all 2F/32 row blocks of each group its share
-// reads. A wait that passes spin_cap polls (workgroups not all resident) gives up and flags
-// MOE_ERR_SYNC instead of hanging.
-struct PassSync {
-  int32_t* signal;
-  const int32_t* wait;
-  int wait_target;
-  int32_t* err;
-  int spin_cap;
 };
 
 // h handed between the workgroups of one launch goes through device-scope stores and loads
@@ -90,8 +76,8 @@ __device__ __forceinline__ void decode_pass(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int rbi = R / 32, nkc = K / 64, G = K / 128;
   const int total_rb = n_items * rbi;
-  const int b0 = (int)((long long)total_rb * blockIdx.x / gridDim.x);
-  const int b1 = (int)((long long)total_rb * (blockIdx.x + 1) / gridDim.x);
+  int b0, b1;
+  share_of(total_rb, b0, b1);
   const int nrb = b1 - b0;  // <= MAXRB (the launch checks)
   // an empty share (more workgroups than row blocks) has nothing to load, wait for or count
   if (nrb == 0) return;
@@ -195,25 +181,7 @@ __device__ __forceinline__ void decode_pass(
   }
   // one launch: the h rows this share reads are complete once every row block of their
   // groups is counted (weights and scales above do not depend on them)
-  if (sy.wait != nullptr) {
-    if (threadIdx.x == 0) {
-      const int g0 = b0 / rbi, g1 = (b1 - 1) / rbi;
-      bool late = false;
-      for (int g = g0; g <= g1; ++g) {
-        int spins = 0;
-        while (__hip_atomic_load(sy.wait + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               sy.wait_target) {
-          if (++spins > sy.spin_cap) {
-            late = true;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-      }
-      if (late) atomicOr(sy.err, MOE_ERR_SYNC);
-    }
-    __syncthreads();
-  }
+  if (sy.wait != nullptr) wait_groups(sy, b0 / rbi, (b1 - 1) / rbi);
   // the activation rows, quantised into LDS (same rule and codes as quant_rows_kernel)
   if constexpr (SWIGLU) {
     // the token row, held in registers (K <= 8 * kTokRegs * blockDim, which the launch checks): a
@@ -389,18 +357,7 @@ __device__ __forceinline__ void decode_pass(
       if (lane < 32) out[(size_t)it.row_begin * out_ld + row] = v;
     }
   }
-  if (sy.signal != nullptr) {
-    // every wave's device-scope h stores of the share have completed (vector-memory counter
-    // at zero) before the barrier, and the counts go out after it
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int g = b0 / rbi; g <= (b1 - 1) / rbi; ++g) {
-        const int lo = g * rbi > b0 ? g * rbi : b0, hi = (g + 1) * rbi < b1 ? (g + 1) * rbi : b1;
-        __hip_atomic_fetch_add(sy.signal + g, hi - lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+  if (sy.signal != nullptr) signal_groups(sy, b0, b1, rbi);
 }
 
 template <bool SWIGLU, int MAXRB>
@@ -460,20 +417,6 @@ size_t decode_lds(bool swiglu, int max_items, int K, int maxrb) {
   return ((act + 15) & ~(size_t)15) + (size_t)maxrb * 64 * (K / 128);
 }
 
-// compute units of the current device (queried once)
-int decode_cus() {
-  static std::atomic<int> cus{0};
-  int n = cus.load(std::memory_order_relaxed);
-  if (n <= 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus.store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 }  // namespace
 
 bool decode_int4_fits(int max_items, int R, int K, bool swiglu) {
@@ -525,17 +468,12 @@ int launch_decode_int4_fused(const void* x, const int32_t* perm, int k, const Ff
   const long long b1 = (long long)max_items * (2 * F / 32), b2 = (long long)max_items * (H / 32);
   const long long grid = (long long)n * kDecWgPerCu;
   const long long per = ((b1 > b2 ? b1 : b2) + grid - 1) / grid;
-  constexpr int kSpinCap = 1 << 16;  // polls before a wait gives up (about 0.1 s; a normal wait is a few)
   const int maxrb = per <= 8 ? 8 : 16;
   const size_t l1 = decode_lds(true, max_items, H, maxrb), l2 = decode_lds(false, max_items, F, maxrb);
   size_t lds = l1 > l2 ? l1 : l2;
-  // 160 KB of LDS per unit: a workgroup's total (this request plus its static arrays) above
-  // 160 / (kDecWgPerCu + 1) KB keeps one more off the unit; at most 160 / kDecWgPerCu KB
-  // lets kDecWgPerCu share it
   const size_t stat = sizeof(float) * (2 * kStreamMaxItems + 16 + (size_t)kDecNW * maxrb * 32);
-  const size_t lo = 160 * 1024 / (kDecWgPerCu + 1) + 1024, hi = 160 * 1024 / kDecWgPerCu - 512;
-  if (lds + stat < lo) lds = lo - stat;
-  if (lds + stat > hi) return MOE_EUNSUPPORTED;
+  lds = resident_lds(lds, stat);
+  if (lds == 0) return MOE_EUNSUPPORTED;
   if (per <= 8) {
     hipLaunchKernelGGL((int4_decode_fused_kernel<8>), dim3((unsigned)grid), dim3(kDecNW * 64), lds,
                        s, x, perm, k, items, n_items, pool, stride, off_w13, off_s13, off_w2,

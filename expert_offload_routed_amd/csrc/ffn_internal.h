@@ -53,6 +53,17 @@ int launch_decode_int4_fused(const void* x, const int32_t* perm, int k, const Ff
                              size_t off_s2, int H, int F, float* hbuf, float* y, int32_t* sync,
                              int32_t* err, hipStream_t s);
 
+// The bf16 counterparts (decode_bf16.hip): h is bf16 (rows of F values), y fp32.
+bool decode_bf16_fits(int max_items, int R, int K, bool swiglu);
+int launch_decode_bf16_fused(const void* x, const int32_t* perm, int k, const FfnItem* items,
+                             const int32_t* n_items, int max_items, const char* pool,
+                             size_t stride, size_t off_w13, size_t off_w2, int H, int F,
+                             void* hbuf, float* y, int32_t* sync, int32_t* err, hipStream_t s);
+int launch_decode_bf16(bool swiglu, const void* raw, const int32_t* perm, int k,
+                       const FfnItem* items, const int32_t* n_items, int max_items,
+                       const char* pool, size_t stride, size_t off_w, int R, int K, int out_ld,
+                       void* out, hipStream_t s);
+
 static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int slot_layout(int H, int F, int w_dtype, SlotLayout* out);
