@@ -12,6 +12,8 @@
 
 namespace {
 
+constexpr int kCombineBatch = 8;  // rows of a token whose loads are in flight together
+
 template <int OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
@@ -22,14 +24,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= H) return;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const float wt = w[(size_t)t * k + j];
-    if (wt != 0.f) {
-      const u32x4 v = ld16(y + (size_t)inv[(size_t)t * k + j] * H + c);
-      a0 = fmaf(wt, __uint_as_float(v.x), a0);
-      a1 = fmaf(wt, __uint_as_float(v.y), a1);
-      a2 = fmaf(wt, __uint_as_float(v.z), a2);
-      a3 = fmaf(wt, __uint_as_float(v.w), a3);
+  // kCombineBatch rows at a time: every row of the batch is loaded (an index past k reads row
+  // k - 1 again, unused) before the first is summed, so a token costs one memory round trip
+  // per batch rather than one per row; the sums keep the fixed j order
+  for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+    u32x4 v[kCombineBatch];
+    float wb[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int j = j0 + u < k ? j0 + u : k - 1;
+      wb[u] = w[(size_t)t * k + j];
+      v[u] = ld16(y + (size_t)inv[(size_t)t * k + j] * H + c);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch out before the first sum
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      // a row past k or of zero weight leaves the sums as they are (selects, not branches,
+      // so that no load is moved behind one)
+      const bool use = j0 + u < k && wb[u] != 0.f;
+      const float f0 = fmaf(wb[u], __uint_as_float(v[u].x), a0);
+      const float f1 = fmaf(wb[u], __uint_as_float(v[u].y), a1);
+      const float f2 = fmaf(wb[u], __uint_as_float(v[u].z), a2);
+      const float f3 = fmaf(wb[u], __uint_as_float(v[u].w), a3);
+      a0 = use ? f0 : a0;
+      a1 = use ? f1 : a1;
+      a2 = use ? f2 : a2;
+      a3 = use ? f3 : a3;
     }
   }
   for (int s = 0; s < n_shared; ++s) {
