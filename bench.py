@@ -466,6 +466,27 @@ def hit_layers(shape, T, store, t_max=None):
 HEAD_POLICY = "mrs"
 
 
+def pcie_copy(store, n=10) -> dict:
+    """One expert's bytes copied from the pinned host store into device memory on a side
+    stream, the copy a fill issues (hipMemcpyAsync host to device), alone and timed with
+    events: the PCIe rate the fills are bound by."""
+    dst = torch.empty(store.stride, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nb = store.host.shape[0]
+    with torch.cuda.stream(s):
+        for i in range(2):
+            dst.copy_(store.host[i % nb], non_blocking=True)
+        ev0.record(s)
+        for i in range(n):
+            dst.copy_(store.host[(i + 2) % nb], non_blocking=True)
+        ev1.record(s)
+    ev1.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / n
+    del dst
+    return {"bytes": int(store.stride), "us": round(us, 1), "gbs": round(store.stride / us / 1e3, 2)}
+
+
 def workload_report(name, K, Wm, quick=False, policies=("lru", "lru_device", "mrs"), head_steps=None):
     """Hit path at each token count of the workload (expert FFN timed with events) and its
     caches with fills (quick: the first hit path and the first cache under HEAD_POLICY).
@@ -487,6 +508,8 @@ def workload_report(name, K, Wm, quick=False, policies=("lru", "lru_device", "mr
         else:
             res[f"T{T}_hit"] = r
     steps = max(K // 5, 5) if shape.layers == 1 else max(K // 5, 8)
+    if plan["miss"]:
+        res["pcie_copy"] = pcie_copy(store)
     if not quick:
         res.update(fill_cases(shape, plan, cfg, store, steps, 2, policies, head_steps))
     elif plan["miss"]:
@@ -636,9 +659,14 @@ def main():
                                + f", decode {head['tokens_per_step']} token/step " + head_desc,
                    "tokens_per_step": head["tokens_per_step"], "hit_rate": head.get("hit_rate"),
                    "fills_per_step": head.get("fills_per_step"),
+                   # the fills' bytes over the whole step time, against one copy's rate alone
+                   "fill_gbs_in_step": (round(head["fill_bytes_per_step"] / head["ms_per_step"] / 1e6, 2)
+                                        if head.get("fill_bytes_per_step") else None),
+                   "pcie_copy_gbs": also.get("pcie_copy", {}).get("gbs"),
                    "pool_replicas": head["pool_replicas"], "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "moe_expert_ffn (group plan + gate/up pass + down pass launches, one "
-                               f"call per layer step), {hit_T} token/step, all routed experts resident",
+        "roofline": {"kernel": "moe_expert_ffn, one call per layer step (at one token one launch of "
+                               "both passes, the work list written by the router's select), "
+                               f"{hit_T} token/step, all routed experts resident",
                      "bound": "hbm", "achieved": round(ffn["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ffn["gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(f"{args.workload}/decode{hit_T}",

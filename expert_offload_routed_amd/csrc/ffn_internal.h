@@ -66,6 +66,11 @@ int launch_decode_bf16(bool swiglu, const void* raw, const int32_t* perm, int k,
 
 static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Copy of `bytes` (a multiple of 16, both addresses 16-byte aligned) from pinned host memory,
+// read through its device address src_dev, to device memory dst: a copy kernel on `stream`
+// (slots.hip). MOE_EINVAL when the sizes or alignments do not fit it.
+int launch_host_copy(void* dst, const void* src_dev, size_t bytes, hipStream_t stream);
+
 int slot_layout(int H, int F, int w_dtype, SlotLayout* out);
 
 #include <hip/hip_runtime.h>

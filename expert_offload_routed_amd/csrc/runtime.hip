@@ -391,9 +391,16 @@ void recount_resident(moe_layer_ctx* c) {
 int fill_slot(moe_layer_ctx* c, int slot, int layer, int expert) {
   const int idx = layer * c->E + expert;
   const uint64_t tag = c->next_tag++;
-  const char* src = c->host_store + (size_t)c->blob_of[idx] * c->stride;
-  hipError_t e = hipMemcpyAsync(c->pool + (size_t)slot * c->stride, src, c->stride,
-                                hipMemcpyHostToDevice, c->fs);
+  const size_t off = (size_t)c->blob_of[idx] * c->stride;
+  hipError_t e = hipSuccess;
+  if (c->store_dev) {  // the store is mapped: a copy kernel (the stride is a multiple of 256)
+    const int rc = launch_host_copy(c->pool + (size_t)slot * c->stride, c->store_dev + off,
+                                    c->stride, c->fs);
+    if (rc != MOE_OK) return rc;
+  } else {
+    e = hipMemcpyAsync(c->pool + (size_t)slot * c->stride, c->host_store + off, c->stride,
+                       hipMemcpyHostToDevice, c->fs);
+  }
   if (e != hipSuccess) return moe_hip_status(e);
   hipLaunchKernelGGL(write_tag_kernel, dim3(1), dim3(64), 0, c->fs, c->tags, slot, tag);
   if (c->fs != c->cs) {
@@ -567,6 +574,13 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->next_hint = -1;
   c->orch = 0;
   c->store_dev = nullptr;
+  {  // fills read a store the device can map through a copy kernel
+    void* dev = nullptr;
+    if (hipHostGetDevicePointer(&dev, const_cast<void*>(host_store), 0) == hipSuccess && dev)
+      c->store_dev = static_cast<const char*>(dev);
+    else
+      (void)hipGetLastError();
+  }
   c->orch_ready = false;
   c->next_tag = 1;
   c->wave_of.resize(E); c->is_hit.resize(E);
@@ -910,9 +924,15 @@ int stage_load(moe_layer_ctx* c, int b, int layer) {
     const int32_t blob0 = c->blob_of[(size_t)layer * E + e0];
     int n = 1;
     while (e0 + n < E && c->blob_of[(size_t)layer * E + e0 + n] == blob0 + n) ++n;
-    e = hipMemcpyAsync(c->pool + (size_t)(c->stage_slot0 + b * E + e0) * c->stride,
-                       c->host_store + (size_t)blob0 * c->stride, (size_t)n * c->stride,
-                       hipMemcpyHostToDevice, c->fs);
+    char* dst = c->pool + (size_t)(c->stage_slot0 + b * E + e0) * c->stride;
+    if (c->store_dev) {
+      if (launch_host_copy(dst, c->store_dev + (size_t)blob0 * c->stride, (size_t)n * c->stride,
+                           c->fs) != MOE_OK)
+        e = hipErrorLaunchFailure;
+    } else {
+      e = hipMemcpyAsync(dst, c->host_store + (size_t)blob0 * c->stride, (size_t)n * c->stride,
+                         hipMemcpyHostToDevice, c->fs);
+    }
     e0 += n;
   }
   if (e == hipSuccess) e = hipEventRecord(c->ev_ready[b], c->fs);

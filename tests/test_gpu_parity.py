@@ -169,6 +169,10 @@ FFN_CASES = [
     (W.reduced(MIX, E=16, k=4, H=512, F=384), 40),    # GEMV groups and MFMA tiles
     (W.reduced(MIX, E=16, k=4, H=512, F=384), 300),   # several 64-row tiles, ragged tails
     (W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), E=16, k=6, H=2048, F=1408), 100),
+    # one token, bf16: both passes over even shares of row blocks in one launch
+    (W.reduced(W.shape_of("dsv2lite_e64k6s2_h2048_f1408_bf16"), E=16, k=6, H=2048, F=1408), 1),
+    (W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), E=16, k=8, H=2048, F=768), 1),
+    (W.reduced(MIX, E=4, k=4, H=4096, F=14336), 1),    # shares of 14 row blocks
     (W.reduced(MIX, E=8, k=2, H=256, F=512, wfmt="f32", xfmt="f32"), 29),
     (W.reduced(DSV3, E=16, k=4, H=512, F=256), 1),     # int4 weights, int8 activations
     (W.reduced(DSV3, E=16, k=4, H=512, F=256), 3),
