@@ -118,6 +118,7 @@ struct moe_layer_ctx {
   int64_t* d_counters;      // [4] as totals, since the last handoff to the host
   uint64_t next_tag;
   std::vector<int32_t> wave_of, is_hit, fill_e, fill_s, fill_w;
+  std::vector<uint64_t> fill_tag;  // tag of each fill of the step
   hipEvent_t ev_fill, ev_compute;
   int64_t totals[4];  // over completed plans: distinct, hits, fills, waves
   // miss prefetch (moe_ctx_set_prefetch): the next step's layer and router (given by
@@ -388,9 +389,11 @@ void recount_resident(moe_layer_ctx* c) {
 
 // Copy one expert into a slot on the fill stream, write its tag back, and
 // commit it on the compute stream once the copy is done.
-int fill_slot(moe_layer_ctx* c, int slot, int layer, int expert) {
+// The copy half of a fill, on the fill stream: the expert's bytes into the slot, then its
+// tag (returned in *tag).
+int fill_copy(moe_layer_ctx* c, int slot, int layer, int expert, uint64_t* tag) {
   const int idx = layer * c->E + expert;
-  const uint64_t tag = c->next_tag++;
+  *tag = c->next_tag++;
   const size_t off = (size_t)c->blob_of[idx] * c->stride;
   hipError_t e = hipSuccess;
   if (c->store_dev) {  // the store is mapped: a copy kernel (the stride is a multiple of 256)
@@ -402,13 +405,23 @@ int fill_slot(moe_layer_ctx* c, int slot, int layer, int expert) {
                        hipMemcpyHostToDevice, c->fs);
   }
   if (e != hipSuccess) return moe_hip_status(e);
-  hipLaunchKernelGGL(write_tag_kernel, dim3(1), dim3(64), 0, c->fs, c->tags, slot, tag);
-  if (c->fs != c->cs) {
-    if ((e = hipEventRecord(c->ev_fill, c->fs)) != hipSuccess) return moe_hip_status(e);
-    if ((e = hipStreamWaitEvent(c->cs, c->ev_fill, 0)) != hipSuccess) return moe_hip_status(e);
-  }
-  hipLaunchKernelGGL(commit_after_fill_kernel, dim3(1), dim3(64), 0, c->cs, c->lut, idx, c->owner,
-                     slot, c->tags, tag, c->err);
+  hipLaunchKernelGGL(write_tag_kernel, dim3(1), dim3(64), 0, c->fs, c->tags, slot, *tag);
+  return moe_launch_status();
+}
+
+// The compute stream waits for the fill stream's copies so far.
+int compute_after_fills(moe_layer_ctx* c) {
+  if (c->fs == c->cs) return MOE_OK;
+  hipError_t e = hipEventRecord(c->ev_fill, c->fs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(c->cs, c->ev_fill, 0);
+  return moe_hip_status(e);
+}
+
+// The commit half, on the compute stream after the copy: the table entry and the owner,
+// once the slot's tag is still this fill's.
+int fill_commit(moe_layer_ctx* c, int slot, int layer, int expert, uint64_t tag) {
+  hipLaunchKernelGGL(commit_after_fill_kernel, dim3(1), dim3(64), 0, c->cs, c->lut,
+                     layer * c->E + expert, c->owner, slot, c->tags, tag, c->err);
   return moe_launch_status();
 }
 
@@ -672,7 +685,10 @@ extern "C" int moe_ctx_place(moe_layer_ctx* c, int slot, int layer, int expert) 
   MOE_CHECK_ARG(c->lut_h[(size_t)layer * c->E + expert] < 0);
   // the copy must not overtake kernels that may still read the slot
   if ((rc = fills_after_compute(c)) != MOE_OK) return rc;
-  if ((rc = fill_slot(c, slot, layer, expert)) != MOE_OK) return rc;
+  uint64_t tag = 0;
+  if ((rc = fill_copy(c, slot, layer, expert, &tag)) != MOE_OK ||
+      (rc = compute_after_fills(c)) != MOE_OK || (rc = fill_commit(c, slot, layer, expert, tag)) != MOE_OK)
+    return rc;
   const int idx = layer * c->E + expert;
   const int32_t old = c->owner_h[slot];
   if (old >= 0 && c->lut_h[old] == slot) c->lut_h[old] = -1;
@@ -1192,30 +1208,43 @@ extern "C" int moe_layer_forward(moe_layer_ctx* c, int layer, const void* x, int
         c->masks_h[(size_t)(1 + c->wave_of[ex]) * E + ex] = 1;
       }
     }
+    // wave 0 fills only overwrite slots no resident group of this step reads: their copies
+    // go out first (behind the compute stream's work so far), before the rest is enqueued
+    c->fill_tag.resize((size_t)n_fills);
+    int fi = 0;
+    if (n_fills && (rc = fills_after_compute(c)) != MOE_OK) return rc;
+    for (; fi < n_fills && c->fill_w[fi] == 0; ++fi)
+      if ((rc = fill_copy(c, c->fill_s[fi], layer, c->fill_e[fi], &c->fill_tag[fi])) != MOE_OK)
+        return rc;
     if ((e = hipMemcpyAsync(c->masks, c->masks_h, (size_t)rows * E * sizeof(int32_t),
                             hipMemcpyHostToDevice, c->cs)) != hipSuccess)
       return moe_hip_status(e);
     // split precision: each selected group takes its precision from the step's scores
     if (c->split)
       launch_critical_split(c->scores, E, c->split_th[layer], c->masks, rows, c->masks, c->cs);
-    // wave 0 fills may start now: they only overwrite slots no resident group of this step reads
-    if (n_fills && (rc = fills_after_compute(c)) != MOE_OK) return rc;
     if (hits || nsh) {  // resident groups, and the shared experts
       if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row, c->masks, nsh, c->S,
                            c->pool, c->stride, nslots, c->w_dtype, T, H, F, E, k, c->y_perm,
                            c->err, c->ws, c->ws_bytes, c->cs)) != MOE_OK)
         return rc;
     }
-    int fi = 0;
+    int fc = 0;  // fills committed
     for (int w = 0; w < n_waves; ++w) {
-      if (w > 0 && (rc = fills_after_compute(c)) != MOE_OK) return rc;
-      int nw = 0;
-      for (; fi < n_fills && c->fill_w[fi] == w; ++fi, ++nw)
-        if ((rc = fill_slot(c, c->fill_s[fi], layer, c->fill_e[fi])) != MOE_OK) return rc;
-      if (nw && (rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row,
-                                 c->masks + (size_t)(1 + w) * E, 0, 0, c->pool, c->stride, nslots,
-                                 c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws, c->ws_bytes,
-                                 c->cs)) != MOE_OK)
+      if (w > 0) {  // a later wave's copies wait for the compute that read its slots
+        if ((rc = fills_after_compute(c)) != MOE_OK) return rc;
+        for (; fi < n_fills && c->fill_w[fi] == w; ++fi)
+          if ((rc = fill_copy(c, c->fill_s[fi], layer, c->fill_e[fi], &c->fill_tag[fi])) != MOE_OK)
+            return rc;
+      }
+      if (fc == fi) continue;  // no fill in this wave
+      if ((rc = compute_after_fills(c)) != MOE_OK) return rc;
+      for (; fc < fi; ++fc)
+        if ((rc = fill_commit(c, c->fill_s[fc], layer, c->fill_e[fc], c->fill_tag[fc])) != MOE_OK)
+          return rc;
+      if ((rc = expert_ffn(x, c->x_dtype, c->perm, c->offsets, lut_row,
+                           c->masks + (size_t)(1 + w) * E, 0, 0, c->pool, c->stride, nslots,
+                           c->w_dtype, T, H, F, E, k, c->y_perm, c->err, c->ws, c->ws_bytes,
+                           c->cs)) != MOE_OK)
         return rc;
     }
   }
