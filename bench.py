@@ -468,8 +468,8 @@ HEAD_POLICY = "mrs"
 
 def pcie_copy(store, n=10) -> dict:
     """One expert's bytes copied from the pinned host store into device memory on a side
-    stream, the copy a fill issues (hipMemcpyAsync host to device), alone and timed with
-    events: the PCIe rate the fills are bound by."""
+    stream (a copy-engine transfer; the fills' copy kernel moves the same 56 GB/s), alone and
+    timed with events: the PCIe rate the fills are bound by."""
     dst = torch.empty(store.stride, dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
