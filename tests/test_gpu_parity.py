@@ -303,6 +303,29 @@ def test_slot_fill_and_tag_commit():
     assert lut.cpu().tolist()[3] == -1 and owner.cpu().tolist()[0] == -1
 
 
+def test_slot_fill_copy_kernel_and_transfer_paths():
+    """A fill copies with a kernel when the pinned source and the sizes are 16-byte aligned,
+    else with a copy-engine transfer: both land the same bytes."""
+    shape = W.reduced(MIX, E=6, k=2, H=256, F=128)
+    store = Hn.ExpertStore(shape)
+    S, E = 2, 6
+    pool = torch.zeros(S * store.stride, dtype=torch.uint8, device=_dev())
+    lut = torch.full((E,), -1, dtype=torch.int32, device=_dev())
+    owner = torch.full((S,), -1, dtype=torch.int32, device=_dev())
+    tags = torch.zeros(S, dtype=torch.int64, device=_dev())
+    err = torch.zeros(1, dtype=torch.int32, device=_dev())
+    base = store.host[3].data_ptr()
+    # aligned interior source, 4096 bytes: the copy kernel
+    B.slot_fill(pool, store.stride, 0, base + 256, 4096, lut, 1, owner, tags, 3, err)
+    # source 8 bytes past alignment, 1000 bytes: the transfer
+    B.slot_fill(pool, store.stride, 1, base + 8, 1000, lut, 2, owner, tags, 4, err)
+    torch.cuda.synchronize()
+    flat = store.host[3]
+    assert torch.equal(pool[:4096].cpu(), flat[256:256 + 4096])
+    assert torch.equal(pool[store.stride:store.stride + 1000].cpu(), flat[8:1008])
+    assert err.item() == 0 and owner.cpu().tolist() == [1, 2]
+
+
 def test_slot_fill_rejects_pageable_host_memory():
     pool = torch.zeros(8192, dtype=torch.uint8, device=_dev())
     lut = torch.full((4,), -1, dtype=torch.int32, device=_dev())
