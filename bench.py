@@ -284,7 +284,8 @@ CASES = {"decode1": 1, "decode8": 8, "prefill512": 512}
 POLICIES = {"lru": (B.MOE_POLICY_LRU, 1, None),
             "mrs": (B.MOE_POLICY_MRS, 8, None),
             "history": (B.MOE_POLICY_HISTORY, 8, [1.0, 1.0, 1.0, 1.0, 0.9]),
-            "lru_device": (B.MOE_POLICY_LRU, 1, None)}
+            "lru_device": (B.MOE_POLICY_LRU, 1, None),
+            "mrs_device": (B.MOE_POLICY_MRS, 8, None)}
 
 
 def fill_cases(shape, plan, cfg, store, steps, warmup, policies=tuple(POLICIES), head=None):
@@ -463,7 +464,11 @@ def hit_layers(shape, T, store, t_max=None):
 # one with the fewest fills on the DeepSeek-V3-shaped decode cache (40 steps at T = 1:
 # 1.08 fills per step against 1.48 under LRU; 1,814 against 1,503 tokens/s with LRU planned
 # on the GPU)
-HEAD_POLICY = "mrs"
+HEAD_POLICY = "mrs_device"
+POLICY_DESC = {"lru": "LRU eviction planned on the host", "lru_device": "LRU eviction planned on the GPU",
+               "mrs": "Minus Recent Score eviction (window 8) planned on the host",
+               "mrs_device": "Minus Recent Score eviction (window 8) planned on the GPU",
+               "history": "routing-history eviction planned on the host"}
 
 
 def pcie_copy(store, n=10) -> dict:
@@ -487,7 +492,8 @@ def pcie_copy(store, n=10) -> dict:
     return {"bytes": int(store.stride), "us": round(us, 1), "gbs": round(store.stride / us / 1e3, 2)}
 
 
-def workload_report(name, K, Wm, quick=False, policies=("lru", "lru_device", "mrs"), head_steps=None):
+def workload_report(name, K, Wm, quick=False, policies=("lru", "lru_device", "mrs", "mrs_device"),
+                    head_steps=None):
     """Hit path at each token count of the workload (expert FFN timed with events) and its
     caches with fills (quick: the first hit path and the first cache under HEAD_POLICY).
     Returns (first hit-path result, dict of the others)."""
@@ -638,7 +644,7 @@ def main():
             head = fills[pol]
             head_desc = (f"through the workload's own cache of {S0} slots ({cfg['residency']} "
                          f"initial residency), misses filled from pinned host memory over PCIe "
-                         f"on the side stream, {pol} eviction")
+                         f"on the side stream, {POLICY_DESC.get(pol, pol)}")
     ffn = hit["ffn"]
     line = {
         "metric": METRIC,

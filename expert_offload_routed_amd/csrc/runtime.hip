@@ -45,6 +45,7 @@
 
 namespace {
 constexpr int kRing = 64;  // deferred routed sets (and timing event pairs) in flight
+constexpr int kDevMrsMaxW = 16;  // Minus Recent Score window the device planner keeps state for
 }
 
 struct moe_layer_ctx {
@@ -116,6 +117,7 @@ struct moe_layer_ctx {
   int32_t* d_fills;         // [2E] (expert, slot) of the step's fills
   int32_t* d_nfills;        // [1]
   int64_t* d_counters;      // [4] as totals, since the last handoff to the host
+  double* d_mrs;            // Minus Recent Score state of the device planner (host layout)
   uint64_t next_tag;
   std::vector<int32_t> wave_of, is_hit, fill_e, fill_s, fill_w;
   std::vector<uint64_t> fill_tag;  // tag of each fill of the step
@@ -153,7 +155,7 @@ struct CtxLayout {
       total;
   size_t ws_bytes;
   // device orchestration's tables and staging's slot table (used only once switched on)
-  size_t order, last_use, clock, blob, fills, nfills, counters, stage_lut;
+  size_t order, last_use, clock, blob, fills, nfills, counters, stage_lut, mrs;
   // the prefetch's speculative routing of the next layer
   size_t spec_logits, spec_ids, spec_w, spec_scores;
 };
@@ -192,6 +194,8 @@ CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int L, int S, int w_
   l.nfills = take(4);
   l.counters = take(4 * 8);
   l.stage_lut = take(2 * (size_t)E * 4);
+  // per layer [observed steps, ring of W score vectors, keep scores], W <= kDevMrsMaxW
+  l.mrs = take((size_t)L * (1 + (size_t)kDevMrsMaxW * E + E) * sizeof(double));
   l.spec_logits = take((size_t)t_max * E * 4);
   l.spec_ids = take(tk * 4);
   l.spec_w = take(tk * 4);
@@ -220,18 +224,25 @@ __global__ void commit_after_fill_kernel(int32_t* lut, int32_t idx, int32_t* own
 // id)) that hold no hit; the slots used by the call move, by id, to the end of
 // the order. Thread t owns slots / order positions 4t .. 4t+3.
 constexpr int kDevPlanMaxS = 4096;
+// With mrs (Minus Recent Score state, W its window) the slots holding no hit are taken by
+// (owner's keep score, last use, slot id) instead, the order of moe_plan_fills_policy: a
+// slot's rank among them is counted against every other, so S^2 comparisons when a step
+// misses (none when it does not).
 __global__ __launch_bounds__(1024) void device_plan_kernel(
     int layer, int E, int S, const int32_t* __restrict__ routed /* [E] then the count */,
     int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock, int32_t* order,
-    int32_t* fills, int32_t* n_fills, int64_t* counters) {
+    int32_t* fills, int32_t* n_fills, int64_t* counters, const double* __restrict__ mrs, int W) {
   __shared__ uint32_t s_kept[kDevPlanMaxS / 32], s_used[kDevPlanMaxS / 32];
   __shared__ int s_miss[1024], s_vict[1024], s_wave[40];
   __shared__ int s_order[kDevPlanMaxS];
+  __shared__ double s_keep[kDevPlanMaxS];   // Minus Recent Score: candidates' keep scores,
+  __shared__ int64_t s_lu[kDevPlanMaxS];    // their last uses
+  __shared__ uint32_t s_cand[kDevPlanMaxS / 32];
   const int tid = threadIdx.x;
   const int nd = routed[E];
   const int64_t now = clock[0] + 1;
   int32_t* row = lut + (size_t)layer * E;
-  for (int i = tid; i < kDevPlanMaxS / 32; i += blockDim.x) s_kept[i] = s_used[i] = 0u;
+  for (int i = tid; i < kDevPlanMaxS / 32; i += blockDim.x) s_kept[i] = s_used[i] = s_cand[i] = 0u;
   __syncthreads();
   int is_hit = 0, is_miss = 0, ex = -1;
   if (tid < nd) {
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(1024) void device_plan_kernel(
       if (pos < nmiss) s_vict[pos] = tid * 4 + j;
       ++pos;
     }
-  // then the slots holding no hit, in LRU order
+  // then the slots holding no hit, in LRU order (or the policy's)
   int o4[4], ok4[4];
   cnt = 0;
 #pragma unroll
@@ -277,12 +288,42 @@ __global__ __launch_bounds__(1024) void device_plan_kernel(
   }
   int nre = 0;
   pos = nempty + block_exclusive_scan(cnt, s_wave, &nre);
+  if (mrs == nullptr) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (ok4[j]) {
-      if (pos < nmiss) s_vict[pos] = o4[j];
-      ++pos;
+    for (int j = 0; j < 4; ++j)
+      if (ok4[j]) {
+        if (pos < nmiss) s_vict[pos] = o4[j];
+        ++pos;
+      }
+  } else if (nmiss > nempty) {  // uniform: the candidates' keep scores and last uses into LDS
+    const size_t per = 1 + (size_t)W * E + E;
+    for (int sl = tid; sl < S; sl += blockDim.x) {
+      const int32_t o = owner[sl];
+      const bool cand = o >= 0 && !((s_kept[sl >> 5] >> (sl & 31)) & 1u);
+      double kv = 0.0;
+      if (cand) {
+        const double* st = mrs + (size_t)(o / E) * per;
+        if (st[0] != 0.0) kv = st[per - E + o % E];  // a layer never observed keeps 0
+      }
+      s_keep[sl] = kv;
+      s_lu[sl] = last_use[sl];
+      if (cand) atomicOr(&s_cand[sl >> 5], 1u << (sl & 31));
     }
+    __syncthreads();
+    for (int sl = tid; sl < S; sl += blockDim.x) {
+      if (!((s_cand[sl >> 5] >> (sl & 31)) & 1u)) continue;
+      const double ka = s_keep[sl];
+      const int64_t la = s_lu[sl];
+      int rank = 0;  // candidates before this one
+      for (int b = 0; b < S; ++b) {
+        if (!((s_cand[b >> 5] >> (b & 31)) & 1u)) continue;
+        const double kb = s_keep[b];
+        const int64_t lb = s_lu[b];
+        rank += (kb < ka || (kb == ka && (lb < la || (lb == la && b < sl)))) ? 1 : 0;
+      }
+      if (nempty + rank < nmiss) s_vict[nempty + rank] = sl;
+    }
+  }
   __syncthreads();
   // fills: miss i -> victim i (n_distinct <= S leaves enough victims)
   if (tid < nmiss) {
@@ -336,6 +377,32 @@ __global__ __launch_bounds__(1024) void device_plan_kernel(
     counters[3] += nd > 0 ? 1 : 0;
   }
 }
+
+#pragma clang fp contract(off)
+// Minus Recent Score on the device (HybriMoE summary page, Mechanism), the arithmetic of
+// moe_policy_observe: the layer's routing scores of this step go into its ring of the last
+// W steps; then every expert's keep score is the sum of its ring entries, oldest to
+// newest, minus the newest (fp64, no contraction). state: per layer [observed steps, ring
+// W x E, keep E]. One workgroup, E <= blockDim.
+__global__ __launch_bounds__(1024) void device_mrs_observe_kernel(double* state, int layer, int E,
+                                                                  int W,
+                                                                  const float* __restrict__ scores) {
+  double* st = state + (size_t)layer * (1 + (size_t)W * E + E);
+  const long n = (long)st[0];  // steps observed before this one
+  double* ring = st + 1;
+  double* keep = st + 1 + (size_t)W * E;
+  const int e = threadIdx.x;
+  if (e < E) {
+    ring[(size_t)(n % W) * E + e] = (double)scores[e];
+    const long n1 = n + 1, m = n1 < W ? n1 : W;
+    double total = 0.0;
+    for (long i = n1 - m; i < n1; ++i) total += ring[(size_t)(i % W) * E + e];
+    keep[e] = total - ring[(size_t)((n1 - 1) % W) * E + e];
+  }
+  __syncthreads();  // every thread has read the count
+  if (threadIdx.x == 0) st[0] = (double)(n + 1);
+}
+#pragma clang fp contract(on)
 
 // Copy the step's fills from the mapped host store into their slots (16 bytes
 // per lane, every workgroup striding over each expert's bytes in turn).
@@ -508,13 +575,17 @@ int sync_from_device(moe_layer_ctx* c) {
       (e = hipMemcpy(cnt, c->d_counters, sizeof(cnt), hipMemcpyDeviceToHost)) != hipSuccess ||
       (e = hipMemset(c->d_counters, 0, sizeof(cnt))) != hipSuccess)
     return moe_hip_status(e);
+  if (c->policy == MOE_POLICY_MRS &&
+      (e = hipMemcpy(c->pol_state.data(), c->d_mrs, c->pol_state.size() * sizeof(double),
+                     hipMemcpyDeviceToHost)) != hipSuccess)
+    return moe_hip_status(e);
   for (int i = 0; i < 4; ++i) c->totals[i] += cnt[i];
   recount_resident(c);
   return MOE_OK;
 }
 
-// Hand the host tables' LRU state to the device planner (the device tables
-// themselves are already current once the stream runs).
+// Hand the host tables' LRU state, and under Minus Recent Score the policy state, to the
+// device planner (the device tables themselves are already current once the stream runs).
 int push_to_device(moe_layer_ctx* c) {
   std::vector<int32_t> order(c->S);
   for (int s = 0; s < c->S; ++s) order[s] = s;
@@ -524,6 +595,9 @@ int push_to_device(moe_layer_ctx* c) {
   if (e == hipSuccess) e = hipMemcpy(c->d_last_use, c->last_use.data(), c->S * sizeof(int64_t), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->d_clock, &c->clock, sizeof(int64_t), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemset(c->d_counters, 0, 4 * sizeof(int64_t));
+  if (e == hipSuccess && c->policy == MOE_POLICY_MRS)
+    e = hipMemcpy(c->d_mrs, c->pol_state.data(), c->pol_state.size() * sizeof(double),
+                  hipMemcpyHostToDevice);
   return moe_hip_status(e);
 }
 
@@ -622,6 +696,7 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->d_fills = reinterpret_cast<int32_t*>(wb + cl.fills);
   c->d_nfills = reinterpret_cast<int32_t*>(wb + cl.nfills);
   c->d_counters = reinterpret_cast<int64_t*>(wb + cl.counters);
+  c->d_mrs = reinterpret_cast<double*>(wb + cl.mrs);
   c->d_stage_lut = reinterpret_cast<int32_t*>(wb + cl.stage_lut);
   c->stage_ready = false;
   c->spec_logits = reinterpret_cast<float*>(wb + cl.spec_logits);
@@ -761,7 +836,9 @@ extern "C" int moe_ctx_ffn_time(moe_layer_ctx* c, double* total_ms, long* steps)
 
 extern "C" int moe_ctx_set_policy(moe_layer_ctx* c, int policy, int window, const double* params) {
   MOE_CHECK_ARG(c);
-  MOE_CHECK_ARG(!c->orch || policy == MOE_POLICY_LRU);  // the device planner runs LRU
+  // the device planner runs LRU and Minus Recent Score (window up to kDevMrsMaxW)
+  MOE_CHECK_ARG(!c->orch || policy == MOE_POLICY_LRU ||
+                (policy == MOE_POLICY_MRS && window >= 1 && window <= kDevMrsMaxW));
   size_t n = 0;
   if (policy != MOE_POLICY_LRU) {
     n = moe_policy_state_doubles(policy, c->L, c->E, window);
@@ -778,6 +855,11 @@ extern "C" int moe_ctx_set_policy(moe_layer_ctx* c, int policy, int window, cons
   c->window = policy == MOE_POLICY_LRU ? 1 : window;
   for (int i = 0; i < 5; ++i) c->params[i] = (policy == MOE_POLICY_HISTORY) ? params[i] : 0.0;
   c->pol_state.assign(n, 0.0);
+  if (c->orch && policy == MOE_POLICY_MRS) {  // the device planner's state starts empty too
+    hipError_t e = hipStreamSynchronize(c->cs);
+    if (e == hipSuccess) e = hipMemset(c->d_mrs, 0, n * sizeof(double));
+    return moe_hip_status(e);
+  }
   return MOE_OK;
 }
 
@@ -801,7 +883,7 @@ extern "C" int moe_ctx_set_split(moe_layer_ctx* c, int enable, float theta, cons
 
 extern "C" int moe_ctx_step_scores(moe_layer_ctx* c, float* scores) {
   MOE_CHECK_ARG(c && scores);
-  if (c->split) {  // the scores of the latest step stay on the device
+  if (c->split || c->orch) {  // the scores of the latest step stay on the device
     hipError_t e = hipStreamSynchronize(c->cs);
     if (e == hipSuccess) e = hipMemcpy(scores, c->scores, (size_t)c->E * sizeof(float),
                                        hipMemcpyDeviceToHost);
@@ -824,7 +906,9 @@ extern "C" int moe_ctx_set_orchestration(moe_layer_ctx* c, int mode) {
     c->orch = 0;
     return MOE_OK;
   }
-  MOE_CHECK_ARG(c->S <= kDevPlanMaxS && c->policy == MOE_POLICY_LRU && !c->stage);
+  MOE_CHECK_ARG(c->S <= kDevPlanMaxS && !c->stage);
+  MOE_CHECK_ARG(c->policy == MOE_POLICY_LRU ||
+                (c->policy == MOE_POLICY_MRS && c->window <= kDevMrsMaxW));
   void* dev = nullptr;
   if (hipHostGetDevicePointer(&dev, const_cast<void*>(static_cast<const void*>(c->host_store)), 0) !=
           hipSuccess ||
@@ -851,8 +935,9 @@ int forward_device(moe_layer_ctx* c, int layer, const void* x, int T, const void
                    const float* bias, void* out, int out_dtype) {
   const int E = c->E, k = c->k, H = c->H, F = c->F, nsh = c->n_shared;
   const int nslots = c->S + nsh;
+  const bool mrs = c->policy == MOE_POLICY_MRS;
   FrontPlan fp{};
-  fp.scores = c->scores;  // written only for split precision, with the critical gate
+  fp.scores = c->scores;  // split precision (with the critical gate) and Minus Recent Score
   if (c->split) {
     fp.crit = c->crit;
     fp.crit_threshold = c->split_th[layer];
@@ -860,15 +945,19 @@ int forward_device(moe_layer_ctx* c, int layer, const void* x, int T, const void
   bool scored = false;
   int rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
                               c->topw, c->counts, c->offsets, c->perm, c->inv, c->dist, c->dist + E,
-                              c->sync, c->split ? &fp : nullptr, nullptr, &scored, c->cs);
+                              c->sync, (c->split || mrs) ? &fp : nullptr, nullptr, &scored, c->cs);
   if (rc != MOE_OK) return rc;
-  if (c->split && !scored) {  // more tokens than the front end scores: separate launches
+  if ((c->split || mrs) && !scored) {  // more tokens than the front end scores: separate launches
     launch_step_scores(c->logits, T, E, c->scores, c->cs);
-    launch_critical_split(c->scores, E, c->split_th[layer], nullptr, 1, c->crit, c->cs);
+    if (c->split) launch_critical_split(c->scores, E, c->split_th[layer], nullptr, 1, c->crit, c->cs);
   }
+  // the step's scores join the layer's history before the plan reads it (as on the host)
+  if (mrs)
+    hipLaunchKernelGGL(device_mrs_observe_kernel, dim3(1), dim3(1024), 0, c->cs, c->d_mrs, layer,
+                       E, c->window, c->scores);
   hipLaunchKernelGGL(device_plan_kernel, dim3(1), dim3(1024), 0, c->cs, layer, E, c->S, c->dist,
                      c->lut, c->owner, c->d_last_use, c->d_clock, c->d_order, c->d_fills,
-                     c->d_nfills, c->d_counters);
+                     c->d_nfills, c->d_counters, mrs ? c->d_mrs : nullptr, c->window);
   hipLaunchKernelGGL(device_fill_kernel, dim3(128), dim3(256), 0, c->cs, c->store_dev, c->d_blob,
                      layer, E, c->pool, c->stride, c->d_fills, c->d_nfills);
   if ((rc = moe_launch_status()) != MOE_OK) return rc;

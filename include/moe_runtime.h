@@ -121,7 +121,8 @@ int moe_ctx_outputs(const moe_layer_ctx* ctx, float** logits, int32_t** ids, flo
  * averaged over the step's tokens) into its pinned staging, and each plan
  * records them (moe_policy_observe) before choosing victims
  * (moe_plan_fills_policy). Allocates the policy state (host) here, not per
- * step. MOE_EINVAL on bad arguments. */
+ * step. Under device orchestration only LRU and MRS with window <= 16 (the
+ * device history is cleared). MOE_EINVAL on bad arguments. */
 int moe_ctx_set_policy(moe_layer_ctx* ctx, int policy, int window, const double* params);
 
 /* moe_ctx_step_scores: the routing scores [E] (host floats) of the latest
@@ -190,21 +191,24 @@ int moe_ctx_prefetch_counters(moe_layer_ctx* ctx, int64_t* out);
 
 /* moe_ctx_set_orchestration: where the residency plan runs.
  *   MOE_ORCH_HOST (default): the host plans each step that may miss, after
- *     reading the routed set, and the fills are DMA copies on the fill stream.
+ *     reading the routed set, and the fills are copies on the fill stream (a copy
+ *     kernel reading the mapped pinned store, else a copy-engine transfer).
  *   MOE_ORCH_DEVICE: the GPU plans and fills by itself and a step never waits
  *     for the host (SeqMoE summary page, Mechanism: the device owns the cache
  *     metadata and starts the miss copy from a kernel out of the pinned,
- *     mapped host pool). One workgroup runs the LRU plan of moe_plan_fills on
- *     the device tables (identical tables and fills); a kernel then copies the
- *     missed experts from the host store (which must be hipHostMalloc memory
- *     the device can map) into their slots; the expert FFN and the combine
- *     follow on the compute stream. Needs S <= 4096 and the LRU policy; a step
+ *     mapped host pool). One workgroup runs the plan of moe_plan_fills (LRU)
+ *     or moe_plan_fills_policy (Minus Recent Score, window <= 16, its history
+ *     recorded on the device as moe_policy_observe does) on the device tables
+ *     (identical tables and fills); a kernel then copies the missed experts
+ *     from the host store (which must be hipHostMalloc memory the device can
+ *     map) into their slots; the expert FFN and the combine follow on the
+ *     compute stream. Needs S <= 4096 and LRU or MRS (window <= 16); a step
  *     with T*k > S returns MOE_EUNSUPPORTED (switch back to the host to run
  *     it). The per-step stats of moe_layer_forward are -1 in this mode; the
  *     totals of moe_ctx_counters and the tables of moe_ctx_read_tables are
  *     read back from the device (a stream synchronisation).
  * Switching hands the tables over (host -> device: the slots' LRU order and
- * clock; device -> host: everything). The device planner's state sits in
+ * clock, and the MRS history; device -> host: everything). The device planner's state sits in
  * the workspace; the first switch to the device writes its weight set table
  * there. */
 #define MOE_ORCH_HOST 0
