@@ -442,14 +442,17 @@ def test_device_orchestration_hands_tables_back_and_forth():
     assert cnt["distinct"] == n_distinct and cnt["fills"] == n_fills
 
 
-def test_device_orchestrated_stack_step_replays_as_a_graph():
+@pytest.mark.parametrize("layers", [3, 1])
+def test_device_orchestrated_stack_step_replays_as_a_graph(layers):
     """A whole stack step (every layer) planned and filled on the device is captured once and
     replayed; between replays the inputs change in place (so replays miss and fill). Every
-    replay equals an eager device-orchestrated context fed the same inputs."""
-    shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=3, E=16, k=4, H=256,
-                      F=128, blobs=16)
-    slots, T, L = 14, 1, shape.layers
-    residency = W.initial_residency(shape, slots, "zipf_rank")
+    replay equals an eager device-orchestrated context fed the same inputs (a 3-layer stack,
+    and one layer whose random initial residency makes most steps fill)."""
+    shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=layers, E=16, k=4,
+                      H=256, F=128, blobs=16)
+    L, T = shape.layers, 1
+    slots = 14 if L > 1 else 5
+    residency = W.initial_residency(shape, slots, "zipf_rank" if L > 1 else "random")
     s = torch.cuda.Stream()
     graphed = Hn.SlotCacheLayer(shape, slots, residency, T, compute_stream=s)
     eager = Hn.SlotCacheLayer(shape, slots, residency, T, store=graphed.store)
