@@ -226,8 +226,7 @@ __global__ void commit_after_fill_kernel(int32_t* lut, int32_t idx, int32_t* own
 constexpr int kDevPlanMaxS = 4096;
 // With mrs (Minus Recent Score state, W its window) the slots holding no hit are taken by
 // (owner's keep score, last use, slot id) instead, the order of moe_plan_fills_policy: a
-// slot's rank among them is counted against every other, so S^2 comparisons when a step
-// misses (none when it does not).
+// bitonic sort of the slots in LDS by that order when a step misses (none when it does not).
 __global__ __launch_bounds__(1024) void device_plan_kernel(
     int layer, int E, int S, const int32_t* __restrict__ routed /* [E] then the count */,
     int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock, int32_t* order,
@@ -310,19 +309,35 @@ __global__ __launch_bounds__(1024) void device_plan_kernel(
       if (cand) atomicOr(&s_cand[sl >> 5], 1u << (sl & 31));
     }
     __syncthreads();
-    for (int sl = tid; sl < S; sl += blockDim.x) {
-      if (!((s_cand[sl >> 5] >> (sl & 31)) & 1u)) continue;
-      const double ka = s_keep[sl];
-      const int64_t la = s_lu[sl];
-      int rank = 0;  // candidates before this one
-      for (int b = 0; b < S; ++b) {
-        if (!((s_cand[b >> 5] >> (b & 31)) & 1u)) continue;
-        const double kb = s_keep[b];
-        const int64_t lb = s_lu[b];
-        rank += (kb < ka || (kb == ka && (lb < la || (lb == la && b < sl)))) ? 1 : 0;
+    // a bitonic sort of the slot ids (padded to a power of two) by that order, candidates
+    // first; the first nmiss - nempty of them are the victims, in order
+    int n2 = 1;
+    while (n2 < S) n2 <<= 1;
+    for (int i = tid; i < n2; i += blockDim.x) s_order[i] = i;
+    __syncthreads();
+    auto before = [&](int a, int b) {  // slot a strictly before slot b
+      const bool ca = a < S && ((s_cand[a >> 5] >> (a & 31)) & 1u);
+      const bool cb = b < S && ((s_cand[b >> 5] >> (b & 31)) & 1u);
+      if (ca != cb) return ca;
+      if (!ca) return a < b;
+      if (s_keep[a] != s_keep[b]) return s_keep[a] < s_keep[b];
+      if (s_lu[a] != s_lu[b]) return s_lu[a] < s_lu[b];
+      return a < b;
+    };
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int q = tid; q < n2 / 2; q += blockDim.x) {
+          const int lo = 2 * q - (q & (stride - 1)), hi = lo + stride;
+          const int a = s_order[lo], b = s_order[hi];
+          if ((lo & size) == 0 ? before(b, a) : before(a, b)) {
+            s_order[lo] = b;
+            s_order[hi] = a;
+          }
+        }
+        __syncthreads();
       }
-      if (nempty + rank < nmiss) s_vict[nempty + rank] = sl;
     }
+    for (int i = tid; i < nmiss - nempty; i += blockDim.x) s_vict[nempty + i] = s_order[i];
   }
   __syncthreads();
   // fills: miss i -> victim i (n_distinct <= S leaves enough victims)
