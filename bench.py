@@ -280,12 +280,13 @@ PLANS = {
 CASES = {"decode1": 1, "decode8": 8, "prefill512": 512}
 # eviction policies compared on the caches with fills: (kind, window, params). The pages give
 # no window, weights or decay; these are the readings (window of 8 steps, equal weights, 0.9).
-# "lru_device": the same LRU plan run by the GPU itself (device orchestration, no host wait).
+# "*_device": the same plan run by the GPU itself (device orchestration, no host wait).
 POLICIES = {"lru": (B.MOE_POLICY_LRU, 1, None),
             "mrs": (B.MOE_POLICY_MRS, 8, None),
             "history": (B.MOE_POLICY_HISTORY, 8, [1.0, 1.0, 1.0, 1.0, 0.9]),
             "lru_device": (B.MOE_POLICY_LRU, 1, None),
-            "mrs_device": (B.MOE_POLICY_MRS, 8, None)}
+            "mrs_device": (B.MOE_POLICY_MRS, 8, None),
+            "history_device": (B.MOE_POLICY_HISTORY, 8, [1.0, 1.0, 1.0, 1.0, 0.9])}
 
 
 def fill_cases(shape, plan, cfg, store, steps, warmup, policies=tuple(POLICIES), head=None):
@@ -468,7 +469,8 @@ HEAD_POLICY = "mrs_device"
 POLICY_DESC = {"lru": "LRU eviction planned on the host", "lru_device": "LRU eviction planned on the GPU",
                "mrs": "Minus Recent Score eviction (window 8) planned on the host",
                "mrs_device": "Minus Recent Score eviction (window 8) planned on the GPU",
-               "history": "routing-history eviction planned on the host"}
+               "history": "routing-history eviction planned on the host",
+               "history_device": "routing-history eviction planned on the GPU"}
 
 
 def pcie_copy(store, n=10) -> dict:

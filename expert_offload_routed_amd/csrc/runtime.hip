@@ -45,7 +45,7 @@
 
 namespace {
 constexpr int kRing = 64;  // deferred routed sets (and timing event pairs) in flight
-constexpr int kDevMrsMaxW = 16;  // Minus Recent Score window the device planner keeps state for
+constexpr int kDevMrsMaxW = 16;  // eviction-score window the device planner keeps state for
 }
 
 struct moe_layer_ctx {
@@ -117,7 +117,7 @@ struct moe_layer_ctx {
   int32_t* d_fills;         // [2E] (expert, slot) of the step's fills
   int32_t* d_nfills;        // [1]
   int64_t* d_counters;      // [4] as totals, since the last handoff to the host
-  double* d_mrs;            // Minus Recent Score state of the device planner (host layout)
+  double* d_pol;            // eviction-score state of the device planner (host layout)
   uint64_t next_tag;
   std::vector<int32_t> wave_of, is_hit, fill_e, fill_s, fill_w;
   std::vector<uint64_t> fill_tag;  // tag of each fill of the step
@@ -155,7 +155,7 @@ struct CtxLayout {
       total;
   size_t ws_bytes;
   // device orchestration's tables and staging's slot table (used only once switched on)
-  size_t order, last_use, clock, blob, fills, nfills, counters, stage_lut, mrs;
+  size_t order, last_use, clock, blob, fills, nfills, counters, stage_lut, pol;
   // the prefetch's speculative routing of the next layer
   size_t spec_logits, spec_ids, spec_w, spec_scores;
 };
@@ -194,8 +194,10 @@ CtxLayout ctx_layout(int t_max, int H, int F, int E, int k, int L, int S, int w_
   l.nfills = take(4);
   l.counters = take(4 * 8);
   l.stage_lut = take(2 * (size_t)E * 4);
-  // per layer [observed steps, ring of W score vectors, keep scores], W <= kDevMrsMaxW
-  l.mrs = take((size_t)L * (1 + (size_t)kDevMrsMaxW * E + E) * sizeof(double));
+  // the eviction-score state in the host layout (moe_policy_state_doubles), W <= kDevMrsMaxW:
+  // per layer [observed steps, ring of W vectors, keep scores], and for the routing-history
+  // score three more vectors (ema, latest score, step of the last selection) before keep
+  l.pol = take((size_t)L * (1 + (size_t)kDevMrsMaxW * E + 4 * (size_t)E) * sizeof(double));
   l.spec_logits = take((size_t)t_max * E * 4);
   l.spec_ids = take(tk * 4);
   l.spec_w = take(tk * 4);
@@ -224,13 +226,15 @@ __global__ void commit_after_fill_kernel(int32_t* lut, int32_t idx, int32_t* own
 // id)) that hold no hit; the slots used by the call move, by id, to the end of
 // the order. Thread t owns slots / order positions 4t .. 4t+3.
 constexpr int kDevPlanMaxS = 4096;
-// With mrs (Minus Recent Score state, W its window) the slots holding no hit are taken by
-// (owner's keep score, last use, slot id) instead, the order of moe_plan_fills_policy: a
-// bitonic sort of the slots in LDS by that order when a step misses (none when it does not).
+// With pol (the eviction-score state: Minus Recent Score or routing-history, per doubles per
+// layer, the keep scores its last E) the slots holding no hit are taken by (owner's keep
+// score, last use, slot id) instead, the order of moe_plan_fills_policy: a bitonic sort of the
+// slots in LDS by that order when a step misses (none when it does not).
 __global__ __launch_bounds__(1024) void device_plan_kernel(
     int layer, int E, int S, const int32_t* __restrict__ routed /* [E] then the count */,
     int32_t* lut, int32_t* owner, int64_t* last_use, int64_t* clock, int32_t* order,
-    int32_t* fills, int32_t* n_fills, int64_t* counters, const double* __restrict__ mrs, int W) {
+    int32_t* fills, int32_t* n_fills, int64_t* counters, const double* __restrict__ pol,
+    long per) {
   __shared__ uint32_t s_kept[kDevPlanMaxS / 32], s_used[kDevPlanMaxS / 32];
   __shared__ int s_miss[1024], s_vict[1024], s_wave[40];
   __shared__ int s_order[kDevPlanMaxS];
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(1024) void device_plan_kernel(
   }
   int nre = 0;
   pos = nempty + block_exclusive_scan(cnt, s_wave, &nre);
-  if (mrs == nullptr) {
+  if (pol == nullptr) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (ok4[j]) {
@@ -295,13 +299,12 @@ __global__ __launch_bounds__(1024) void device_plan_kernel(
         ++pos;
       }
   } else if (nmiss > nempty) {  // uniform: the candidates' keep scores and last uses into LDS
-    const size_t per = 1 + (size_t)W * E + E;
     for (int sl = tid; sl < S; sl += blockDim.x) {
       const int32_t o = owner[sl];
       const bool cand = o >= 0 && !((s_kept[sl >> 5] >> (sl & 31)) & 1u);
       double kv = 0.0;
       if (cand) {
-        const double* st = mrs + (size_t)(o / E) * per;
+        const double* st = pol + (size_t)(o / E) * per;
         if (st[0] != 0.0) kv = st[per - E + o % E];  // a layer never observed keeps 0
       }
       s_keep[sl] = kv;
@@ -416,6 +419,74 @@ __global__ __launch_bounds__(1024) void device_mrs_observe_kernel(double* state,
   }
   __syncthreads();  // every thread has read the count
   if (threadIdx.x == 0) st[0] = (double)(n + 1);
+}
+
+// Routing-history score on the device (MoE-CORE summary page, Mechanism), the arithmetic of
+// moe_policy_observe: this step's selections (0/1 per expert, from the routed set) go into
+// the layer's ring of the last W steps; the moving average, latest routing score and step of
+// the last selection are updated; then every expert's keep score is w0 * count / max count +
+// w1 * ema / max ema + w2 * score / max score + w3 * (1 - age / max age), each term 0 (the
+// last 1) when its maximum over the layer is 0, summed in that order (fp64, no
+// contraction). state: per layer [observed steps, ring W x E, ema E, score E, last E, keep E].
+// One workgroup of 1024 threads, E <= 1024.
+__global__ __launch_bounds__(1024) void device_history_observe_kernel(
+    double* state, int layer, int E, int W, const float* __restrict__ scores,
+    const int32_t* __restrict__ routed /* [E] then the count */, double w0, double w1, double w2,
+    double w3, double lam) {
+  __shared__ double s_max[4][16];
+  double* st = state + (size_t)layer * (1 + (size_t)W * E + 4 * (size_t)E);
+  const long n = (long)st[0];  // steps observed before this one
+  double* ring = st + 1;
+  double* row = ring + (size_t)(n % W) * E;
+  double* ema = ring + (size_t)W * E;
+  double* score = ema + E;
+  double* last = score + E;
+  double* keep = last + E;
+  const int e = threadIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (e < E) row[e] = 0.0;
+  __syncthreads();
+  if (e < routed[E]) row[routed[e]] = 1.0;
+  __syncthreads();
+  const long n1 = n + 1, m = n1 < W ? n1 : W;
+  double f[4] = {0.0, 0.0, 0.0, 0.0};  // count, ema, score, age (0 past E)
+  if (e < E) {
+    const double sel = row[e];
+    ema[e] = lam * ema[e] + (1.0 - lam) * sel;
+    score[e] = (double)scores[e];
+    if (sel != 0.0) last[e] = (double)n1;
+    for (long i = n1 - m; i < n1; ++i) f[0] += ring[(size_t)(i % W) * E + e];
+    f[1] = ema[e];
+    f[2] = score[e];
+    f[3] = (double)n1 - last[e];
+  }
+  // each feature's maximum over the layer (from 0, like the host's; exact in any order)
+  double mx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    double v = f[j];
+    for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+    if (lane == 0) s_max[j][wave] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    double v = 0.0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) v = fmax(v, s_max[j][i]);
+    mx[j] = v;
+  }
+  if (e < E) {
+    const double n_cnt = mx[0] > 0.0 ? f[0] / mx[0] : 0.0;
+    const double n_ema = mx[1] > 0.0 ? f[1] / mx[1] : 0.0;
+    const double n_score = mx[2] > 0.0 ? f[2] / mx[2] : 0.0;
+    const double fresh = mx[3] > 0.0 ? 1.0 - f[3] / mx[3] : 1.0;
+    double total = w0 * n_cnt;
+    total += w1 * n_ema;
+    total += w2 * n_score;
+    total += w3 * fresh;
+    keep[e] = total;
+  }
+  __syncthreads();  // every thread has read the count
+  if (threadIdx.x == 0) st[0] = (double)n1;
 }
 #pragma clang fp contract(on)
 
@@ -590,8 +661,8 @@ int sync_from_device(moe_layer_ctx* c) {
       (e = hipMemcpy(cnt, c->d_counters, sizeof(cnt), hipMemcpyDeviceToHost)) != hipSuccess ||
       (e = hipMemset(c->d_counters, 0, sizeof(cnt))) != hipSuccess)
     return moe_hip_status(e);
-  if (c->policy == MOE_POLICY_MRS &&
-      (e = hipMemcpy(c->pol_state.data(), c->d_mrs, c->pol_state.size() * sizeof(double),
+  if (c->policy != MOE_POLICY_LRU &&
+      (e = hipMemcpy(c->pol_state.data(), c->d_pol, c->pol_state.size() * sizeof(double),
                      hipMemcpyDeviceToHost)) != hipSuccess)
     return moe_hip_status(e);
   for (int i = 0; i < 4; ++i) c->totals[i] += cnt[i];
@@ -599,7 +670,7 @@ int sync_from_device(moe_layer_ctx* c) {
   return MOE_OK;
 }
 
-// Hand the host tables' LRU state, and under Minus Recent Score the policy state, to the
+// Hand the host tables' LRU state, and under an eviction score the policy state, to the
 // device planner (the device tables themselves are already current once the stream runs).
 int push_to_device(moe_layer_ctx* c) {
   std::vector<int32_t> order(c->S);
@@ -610,8 +681,8 @@ int push_to_device(moe_layer_ctx* c) {
   if (e == hipSuccess) e = hipMemcpy(c->d_last_use, c->last_use.data(), c->S * sizeof(int64_t), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->d_clock, &c->clock, sizeof(int64_t), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemset(c->d_counters, 0, 4 * sizeof(int64_t));
-  if (e == hipSuccess && c->policy == MOE_POLICY_MRS)
-    e = hipMemcpy(c->d_mrs, c->pol_state.data(), c->pol_state.size() * sizeof(double),
+  if (e == hipSuccess && c->policy != MOE_POLICY_LRU)
+    e = hipMemcpy(c->d_pol, c->pol_state.data(), c->pol_state.size() * sizeof(double),
                   hipMemcpyHostToDevice);
   return moe_hip_status(e);
 }
@@ -711,7 +782,7 @@ extern "C" int moe_ctx_create(moe_layer_ctx** out, int t_max, int H, int F, int 
   c->d_fills = reinterpret_cast<int32_t*>(wb + cl.fills);
   c->d_nfills = reinterpret_cast<int32_t*>(wb + cl.nfills);
   c->d_counters = reinterpret_cast<int64_t*>(wb + cl.counters);
-  c->d_mrs = reinterpret_cast<double*>(wb + cl.mrs);
+  c->d_pol = reinterpret_cast<double*>(wb + cl.pol);
   c->d_stage_lut = reinterpret_cast<int32_t*>(wb + cl.stage_lut);
   c->stage_ready = false;
   c->spec_logits = reinterpret_cast<float*>(wb + cl.spec_logits);
@@ -851,9 +922,8 @@ extern "C" int moe_ctx_ffn_time(moe_layer_ctx* c, double* total_ms, long* steps)
 
 extern "C" int moe_ctx_set_policy(moe_layer_ctx* c, int policy, int window, const double* params) {
   MOE_CHECK_ARG(c);
-  // the device planner runs LRU and Minus Recent Score (window up to kDevMrsMaxW)
-  MOE_CHECK_ARG(!c->orch || policy == MOE_POLICY_LRU ||
-                (policy == MOE_POLICY_MRS && window >= 1 && window <= kDevMrsMaxW));
+  // the device planner runs LRU and both eviction scores (window up to kDevMrsMaxW)
+  MOE_CHECK_ARG(!c->orch || policy == MOE_POLICY_LRU || (window >= 1 && window <= kDevMrsMaxW));
   size_t n = 0;
   if (policy != MOE_POLICY_LRU) {
     n = moe_policy_state_doubles(policy, c->L, c->E, window);
@@ -870,9 +940,9 @@ extern "C" int moe_ctx_set_policy(moe_layer_ctx* c, int policy, int window, cons
   c->window = policy == MOE_POLICY_LRU ? 1 : window;
   for (int i = 0; i < 5; ++i) c->params[i] = (policy == MOE_POLICY_HISTORY) ? params[i] : 0.0;
   c->pol_state.assign(n, 0.0);
-  if (c->orch && policy == MOE_POLICY_MRS) {  // the device planner's state starts empty too
+  if (c->orch && policy != MOE_POLICY_LRU) {  // the device planner's state starts empty too
     hipError_t e = hipStreamSynchronize(c->cs);
-    if (e == hipSuccess) e = hipMemset(c->d_mrs, 0, n * sizeof(double));
+    if (e == hipSuccess) e = hipMemset(c->d_pol, 0, n * sizeof(double));
     return moe_hip_status(e);
   }
   return MOE_OK;
@@ -922,8 +992,7 @@ extern "C" int moe_ctx_set_orchestration(moe_layer_ctx* c, int mode) {
     return MOE_OK;
   }
   MOE_CHECK_ARG(c->S <= kDevPlanMaxS && !c->stage);
-  MOE_CHECK_ARG(c->policy == MOE_POLICY_LRU ||
-                (c->policy == MOE_POLICY_MRS && c->window <= kDevMrsMaxW));
+  MOE_CHECK_ARG(c->policy == MOE_POLICY_LRU || c->window <= kDevMrsMaxW);
   void* dev = nullptr;
   if (hipHostGetDevicePointer(&dev, const_cast<void*>(static_cast<const void*>(c->host_store)), 0) !=
           hipSuccess ||
@@ -950,9 +1019,9 @@ int forward_device(moe_layer_ctx* c, int layer, const void* x, int T, const void
                    const float* bias, void* out, int out_dtype) {
   const int E = c->E, k = c->k, H = c->H, F = c->F, nsh = c->n_shared;
   const int nslots = c->S + nsh;
-  const bool mrs = c->policy == MOE_POLICY_MRS;
+  const bool scored_pol = c->policy != MOE_POLICY_LRU;  // an eviction score
   FrontPlan fp{};
-  fp.scores = c->scores;  // split precision (with the critical gate) and Minus Recent Score
+  fp.scores = c->scores;  // split precision (with the critical gate) and the eviction scores
   if (c->split) {
     fp.crit = c->crit;
     fp.crit_threshold = c->split_th[layer];
@@ -960,19 +1029,25 @@ int forward_device(moe_layer_ctx* c, int layer, const void* x, int T, const void
   bool scored = false;
   int rc = route_permute_plan(x, c->x_dtype, w_router, bias, T, H, E, k, 1, c->logits, c->ids,
                               c->topw, c->counts, c->offsets, c->perm, c->inv, c->dist, c->dist + E,
-                              c->sync, (c->split || mrs) ? &fp : nullptr, nullptr, &scored, c->cs);
+                              c->sync, (c->split || scored_pol) ? &fp : nullptr, nullptr, &scored,
+                              c->cs);
   if (rc != MOE_OK) return rc;
-  if ((c->split || mrs) && !scored) {  // more tokens than the front end scores: separate launches
+  if ((c->split || scored_pol) && !scored) {  // more tokens than the front end scores: separate launches
     launch_step_scores(c->logits, T, E, c->scores, c->cs);
     if (c->split) launch_critical_split(c->scores, E, c->split_th[layer], nullptr, 1, c->crit, c->cs);
   }
   // the step's scores join the layer's history before the plan reads it (as on the host)
-  if (mrs)
-    hipLaunchKernelGGL(device_mrs_observe_kernel, dim3(1), dim3(1024), 0, c->cs, c->d_mrs, layer,
+  if (c->policy == MOE_POLICY_MRS)
+    hipLaunchKernelGGL(device_mrs_observe_kernel, dim3(1), dim3(1024), 0, c->cs, c->d_pol, layer,
                        E, c->window, c->scores);
+  else if (c->policy == MOE_POLICY_HISTORY)
+    hipLaunchKernelGGL(device_history_observe_kernel, dim3(1), dim3(1024), 0, c->cs, c->d_pol,
+                       layer, E, c->window, c->scores, c->dist, c->params[0], c->params[1],
+                       c->params[2], c->params[3], c->params[4]);
+  const long per = scored_pol ? (long)moe_policy_state_doubles(c->policy, 1, E, c->window) : 0;
   hipLaunchKernelGGL(device_plan_kernel, dim3(1), dim3(1024), 0, c->cs, layer, E, c->S, c->dist,
                      c->lut, c->owner, c->d_last_use, c->d_clock, c->d_order, c->d_fills,
-                     c->d_nfills, c->d_counters, mrs ? c->d_mrs : nullptr, c->window);
+                     c->d_nfills, c->d_counters, scored_pol ? c->d_pol : nullptr, per);
   hipLaunchKernelGGL(device_fill_kernel, dim3(128), dim3(256), 0, c->cs, c->store_dev, c->d_blob,
                      layer, E, c->pool, c->stride, c->d_fills, c->d_nfills);
   if ((rc = moe_launch_status()) != MOE_OK) return rc;

@@ -121,7 +121,7 @@ int moe_ctx_outputs(const moe_layer_ctx* ctx, float** logits, int32_t** ids, flo
  * averaged over the step's tokens) into its pinned staging, and each plan
  * records them (moe_policy_observe) before choosing victims
  * (moe_plan_fills_policy). Allocates the policy state (host) here, not per
- * step. Under device orchestration only LRU and MRS with window <= 16 (the
+ * step. Under device orchestration any policy with window <= 16 (the
  * device history is cleared). MOE_EINVAL on bad arguments. */
 int moe_ctx_set_policy(moe_layer_ctx* ctx, int policy, int window, const double* params);
 
@@ -197,18 +197,19 @@ int moe_ctx_prefetch_counters(moe_layer_ctx* ctx, int64_t* out);
  *     for the host (SeqMoE summary page, Mechanism: the device owns the cache
  *     metadata and starts the miss copy from a kernel out of the pinned,
  *     mapped host pool). One workgroup runs the plan of moe_plan_fills (LRU)
- *     or moe_plan_fills_policy (Minus Recent Score, window <= 16, its history
- *     recorded on the device as moe_policy_observe does) on the device tables
+ *     or moe_plan_fills_policy (Minus Recent Score or the routing-history
+ *     score, window <= 16, its history recorded on the device as
+ *     moe_policy_observe does, with the same arithmetic) on the device tables
  *     (identical tables and fills); a kernel then copies the missed experts
  *     from the host store (which must be hipHostMalloc memory the device can
  *     map) into their slots; the expert FFN and the combine follow on the
- *     compute stream. Needs S <= 4096 and LRU or MRS (window <= 16); a step
+ *     compute stream. Needs S <= 4096 and a window <= 16; a step
  *     with T*k > S returns MOE_EUNSUPPORTED (switch back to the host to run
  *     it). The per-step stats of moe_layer_forward are -1 in this mode; the
  *     totals of moe_ctx_counters and the tables of moe_ctx_read_tables are
  *     read back from the device (a stream synchronisation).
  * Switching hands the tables over (host -> device: the slots' LRU order and
- * clock, and the MRS history; device -> host: everything). The device planner's state sits in
+ * clock, and the policy's history; device -> host: everything). The device planner's state sits in
  * the workspace; the first switch to the device writes its weight set table
  * there. */
 #define MOE_ORCH_HOST 0

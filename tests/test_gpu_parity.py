@@ -387,18 +387,42 @@ def test_layer_device_orchestration_mrs_shared_experts_int4():
                     policy=(B.MOE_POLICY_MRS, 8, None))
 
 
-def test_device_orchestration_hands_mrs_history_back_and_forth():
-    """Host plans under MRS, then the device, then the host again: one history and one set of
-    tables, those of the oracle's scored planner."""
+HIST_PARAMS = [1.0, 0.5, 2.0, 0.25, 0.8]
+
+
+def test_layer_stack_device_orchestration_history():
+    """The routing-history score planned on the device: routing, tables and outputs those of
+    the oracle's scored planner at every layer-step of a 3-layer stack."""
+    shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=3, E=16, k=4, H=256,
+                      F=128, blobs=16)
+    _run_layer_case(shape, 14, "zipf_rank", [1, 3, 1, 2, 1, 3, 1, 2], layers_order=[0, 1, 2],
+                    device_plan=True, policy=(B.MOE_POLICY_HISTORY, 4, HIST_PARAMS))
+
+
+def test_layer_device_orchestration_history_shared_experts_int4():
+    shape = W.reduced(DSV3, E=32, k=8, H=256, F=128)
+    _run_layer_case(shape, 12, "zipf_rank", [1, 1, 1, 1, 1, 1, 1, 1], device_plan=True,
+                    policy=(B.MOE_POLICY_HISTORY, 3, [0.0, 1.0, 0.5, 1.0, 0.5]))
+
+
+@pytest.mark.parametrize("kind", ["mrs", "history"])
+def test_device_orchestration_hands_mrs_history_back_and_forth(kind):
+    """Host plans under an eviction score, then the device, then the host again: one history
+    and one set of tables, those of the oracle's scored planner."""
     shape = W.reduced(MIX, E=12, k=3, H=256, F=256)
     slots, window = 5, 3
     residency = W.initial_residency(shape, slots, "random")
     layer_obj = Hn.SlotCacheLayer(shape, slots, residency, 4)
-    layer_obj.ctx.set_policy(B.MOE_POLICY_MRS, window, None)
-    planner = O.ScoredSlotPlanner(slots, 1, shape.E, O.MinusRecentScore(1, shape.E, window), residency)
+    if kind == "mrs":
+        layer_obj.ctx.set_policy(B.MOE_POLICY_MRS, window, None)
+        pol = O.MinusRecentScore(1, shape.E, window)
+    else:
+        layer_obj.ctx.set_policy(B.MOE_POLICY_HISTORY, window, HIST_PARAMS)
+        pol = O.RoutingHistoryScore(1, shape.E, window, weights=HIST_PARAMS[:4], lam=HIST_PARAMS[4])
+    planner = O.ScoredSlotPlanner(slots, 1, shape.E, pol, residency)
     for step in range(8):
         layer_obj.ctx.set_orchestration(B.MOE_ORCH_DEVICE if step in (2, 3, 4) else B.MOE_ORCH_HOST)
-        say(f"mrs handoff step={step}")
+        say(f"{kind} handoff step={step}")
         x = W.tokens(shape, 1, step=step, device=_dev())
         layer_obj.forward(x)
         torch.cuda.synchronize()
