@@ -43,7 +43,8 @@ __device__ __forceinline__ u32x4 load_h16(const uint32_t* p, bool shared) {
   return r;
 }
 
-// SWIGLU (gate/up pass): raw = the bf16 tokens (row perm[p] / k for every group; T = 1),
+// SWIGLU (gate/up pass): raw = the bf16 tokens (T = 1: row perm[p] / k is row 0 for every
+// group, so the token loads wait for neither the work list nor perm),
 // out = h (bf16, row p, column n of rows 2n, 2n+1). Otherwise (down pass): raw = h (bf16
 // rows p), out = y (fp32). act: the workgroup's dynamic LDS, activation rows
 // [SWIGLU ? 1 : n_items][K] bf16; red: [kDecNW][MAXRB][32] partials.
@@ -115,8 +116,7 @@ __device__ __forceinline__ void bf16_pass(const void* __restrict__ raw,
   u32x4 tok{};
   if constexpr (SWIGLU) {
     const int pc = (int)threadIdx.x < npiece ? (int)threadIdx.x : npiece - 1;
-    tok = ld16(static_cast<const uint16_t*>(raw) + (size_t)(perm[items[0].row_begin] / k) * K +
-               (size_t)pc * 8);
+    tok = ld16(static_cast<const uint16_t*>(raw) + (size_t)pc * 8);  // the one token
   }
   __builtin_amdgcn_sched_barrier(0);
   u32x4 buf[kDecP];

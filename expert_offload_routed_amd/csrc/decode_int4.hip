@@ -31,8 +31,9 @@ using namespace decode_share;
 
 constexpr int kTokRegs = (8192 + 8 * kDecNW * 64 - 1) / (8 * kDecNW * 64);  // token row: K <= 8192
 
-// SWIGLU (gate/up pass): one token row for every group (row perm[p] / k of the bf16
-// tokens; T = 1), out = h (fp32, row p, column n of rows 2n, 2n+1).
+// SWIGLU (gate/up pass): one token row for every group (T = 1: row perm[p] / k of the bf16
+// tokens is row 0 for every p, so its loads need neither the work list nor perm), out = h
+// (fp32, row p, column n of rows 2n, 2n+1).
 // Otherwise (down pass): row p of the fp32 h for each group; out = y (fp32).
 // The workgroup's LDS of a pass: activation rows [SWIGLU ? 1 : n_items][K] int8, then the
 // share's scales [MAXRB][32][K/128] bf16 (dynamic), and the fixed arrays below.
@@ -151,7 +152,7 @@ __device__ __forceinline__ void decode_pass(
   // the token row (bf16; every group reads the same one): eight values per thread and register
   u32x4 tok[kTokRegs];
   if constexpr (SWIGLU) {
-    const uint16_t* trow = static_cast<const uint16_t*>(raw) + (size_t)(perm[items[0].row_begin] / k) * K;
+    const uint16_t* trow = static_cast<const uint16_t*>(raw);  // the one token
 #pragma unroll
     for (int u = 0; u < kTokRegs; ++u) {
       const int e = ((int)threadIdx.x + u * (int)blockDim.x) * 8;
