@@ -462,9 +462,9 @@ def hit_layers(shape, T, store, t_max=None):
 
 
 # the eviction policy of the headline's cache with fills: HybriMoE's Minus Recent Score, the
-# one with the fewest fills on the DeepSeek-V3-shaped decode cache (40 steps at T = 1:
-# 1.08 fills per step against 1.48 under LRU; 1,814 against 1,503 tokens/s with LRU planned
-# on the GPU)
+# one with the fewest fills on the DeepSeek-V3-shaped decode cache (40 steps at T = 1: 1.2
+# fills per step against 1.6 under LRU and 1.475 under the routing-history score; 1,743
+# against 1,395 tokens/s with both planned on the GPU)
 HEAD_POLICY = "mrs_device"
 POLICY_DESC = {"lru": "LRU eviction planned on the host", "lru_device": "LRU eviction planned on the GPU",
                "mrs": "Minus Recent Score eviction (window 8) planned on the host",
