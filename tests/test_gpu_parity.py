@@ -466,12 +466,13 @@ def test_device_orchestration_hands_tables_back_and_forth():
     assert cnt["distinct"] == n_distinct and cnt["fills"] == n_fills
 
 
-@pytest.mark.parametrize("layers", [3, 1])
-def test_device_orchestrated_stack_step_replays_as_a_graph(layers):
+@pytest.mark.parametrize("layers,policy", [(3, "lru"), (1, "lru"), (3, "mrs"), (1, "history")])
+def test_device_orchestrated_stack_step_replays_as_a_graph(layers, policy):
     """A whole stack step (every layer) planned and filled on the device is captured once and
     replayed; between replays the inputs change in place (so replays miss and fill). Every
     replay equals an eager device-orchestrated context fed the same inputs (a 3-layer stack,
-    and one layer whose random initial residency makes most steps fill)."""
+    and one layer whose random initial residency makes most steps fill), under LRU and under
+    both eviction scores (their history recorded on the device by the captured kernels)."""
     shape = W.reduced(W.shape_of("qwen3moe_l48_e128k8_h2048_f768_bf16"), layers=layers, E=16, k=4,
                       H=256, F=128, blobs=16)
     L, T = shape.layers, 1
@@ -481,6 +482,10 @@ def test_device_orchestrated_stack_step_replays_as_a_graph(layers):
     graphed = Hn.SlotCacheLayer(shape, slots, residency, T, compute_stream=s)
     eager = Hn.SlotCacheLayer(shape, slots, residency, T, store=graphed.store)
     for lay in (graphed, eager):
+        if policy == "mrs":
+            lay.ctx.set_policy(B.MOE_POLICY_MRS, 3, None)
+        elif policy == "history":
+            lay.ctx.set_policy(B.MOE_POLICY_HISTORY, 3, HIST_PARAMS)
         lay.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
     xs = [W.tokens(shape, T, layer=l, step=0, device=_dev()) for l in range(L)]
     outs_g = [torch.empty(T, shape.H, dtype=graphed.out_dtype, device=_dev()) for _ in range(L)]
