@@ -255,6 +255,32 @@ def cpu_baseline(shape, budget_s=20.0):
             "affinity_cores": affinity, "cpu_model": model}
 
 
+def cpu_baseline_tiny(budget_s=3.0):
+    """The oracle on the tiny fp32 layer (16 tokens per step, every expert resident in its
+    pool) on one thread: the single-core reference the parity configuration is timed at."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    shape = W.shape_of("tiny_e8k2_h256_f512_fp32")
+    E, T = shape.E, 16
+    weights = {e: W.expert_weights(shape, W.blob_of(shape, 0, e)) for e in range(E)}
+    wr, b = W.router(shape)
+    pool = O.SlotPool(E, 1, E)
+    planner = O.LruSlotPlanner(E, 1, E, [None] * E)
+    n, work = 0, 0.0
+    with threadpool_limits(limits=1):
+        while work < budget_s and n < 256:
+            x = W.tokens(shape, T, step=n)
+            t0 = time.perf_counter()
+            O.moe_layer(x, wr, b, shape.k, layer=0, pool=pool, planner=planner,
+                        weights_of_expert=lambda e: weights[e])
+            work += time.perf_counter() - t0
+            n += 1
+    return {"value": n * T / work, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} steps of {T} tokens of {shape.name} (float64 NumPy oracle), "
+                      f"{work:.1f} s on one thread"}
+
+
 def calib_copy(steps):
     """Plain device copy of 1 GiB, for scaling the HBM byte counters (FETCH_SIZE, WRITE_SIZE)."""
     n = 1 << 30
@@ -684,6 +710,7 @@ def main():
     }
     if not args.no_cpu_baseline and shape.layers == 1:
         line["cpu_baseline"] = cpu_baseline(shape)
+        line["cpu_baseline"]["tiny_fp32_one_thread"] = cpu_baseline_tiny()
     print(json.dumps(line), flush=True)
 
 
