@@ -269,7 +269,7 @@ def cpu_baseline_tiny(budget_s=3.0):
     planner = O.LruSlotPlanner(E, 1, E, [None] * E)
     n, work = 0, 0.0
     with threadpool_limits(limits=1):
-        while work < budget_s and n < 256:
+        while work < budget_s and n < 4096:
             x = W.tokens(shape, T, step=n)
             t0 = time.perf_counter()
             O.moe_layer(x, wr, b, shape.k, layer=0, pool=pool, planner=planner,
