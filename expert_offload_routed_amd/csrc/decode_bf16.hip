@@ -50,7 +50,6 @@ __device__ __forceinline__ u32x4 load_h16(const uint32_t* p, bool shared) {
 // [SWIGLU ? 1 : n_items][K] bf16; red: [kDecNW][MAXRB][32] partials.
 template <bool SWIGLU, int MAXRB>
 __device__ __forceinline__ void bf16_pass(const void* __restrict__ raw,
-                                          const int32_t* __restrict__ perm, int k,
                                           const FfnItem* __restrict__ items, int n_items,
                                           const char* __restrict__ pool, size_t stride,
                                           size_t off_w, int R, int K, int out_ld,
@@ -202,13 +201,13 @@ __device__ __forceinline__ void bf16_pass(const void* __restrict__ raw,
 
 template <bool SWIGLU, int MAXRB>
 __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(4))) void
-bf16_decode_kernel(const void* __restrict__ raw, const int32_t* __restrict__ perm, int k,
-                   const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+bf16_decode_kernel(const void* __restrict__ raw, const FfnItem* __restrict__ items,
+                   const int32_t* __restrict__ n_items_p,
                    const char* __restrict__ pool, size_t stride, size_t off_w, int R, int K,
                    int out_ld, void* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) uint16_t act[];
   __shared__ float red[kDecNW][MAXRB][32];
-  bf16_pass<SWIGLU, MAXRB>(raw, perm, k, items, n_items_p[0], pool, stride, off_w, R, K, out_ld,
+  bf16_pass<SWIGLU, MAXRB>(raw, items, n_items_p[0], pool, stride, off_w, R, K, out_ld,
                            out, act, red, PassSync{nullptr, nullptr, 0, nullptr, 0});
 }
 
@@ -217,8 +216,8 @@ bf16_decode_kernel(const void* __restrict__ raw, const int32_t* __restrict__ per
 // go out before it waits for the h rows.
 template <int MAXRB>
 __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(4))) void
-bf16_decode_fused_kernel(const void* __restrict__ x, const int32_t* __restrict__ perm, int k,
-                         const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+bf16_decode_fused_kernel(const void* __restrict__ x, const FfnItem* __restrict__ items,
+                         const int32_t* __restrict__ n_items_p,
                          const char* __restrict__ pool, size_t stride, size_t off_w13,
                          size_t off_w2, int H, int F, uint16_t* __restrict__ hbuf,
                          float* __restrict__ y, int32_t* __restrict__ sync,
@@ -226,10 +225,10 @@ bf16_decode_fused_kernel(const void* __restrict__ x, const int32_t* __restrict__
   extern __shared__ __attribute__((aligned(16))) uint16_t act[];
   __shared__ float red[kDecNW][MAXRB][32];
   const int n_items = n_items_p[0];
-  bf16_pass<true, MAXRB>(x, perm, k, items, n_items, pool, stride, off_w13, 2 * F, H, F, hbuf, act,
+  bf16_pass<true, MAXRB>(x, items, n_items, pool, stride, off_w13, 2 * F, H, F, hbuf, act,
                          red, PassSync{sync, nullptr, 0, err, spin_cap});
   __syncthreads();  // the LDS of the first pass is free
-  bf16_pass<false, MAXRB>(hbuf, perm, k, items, n_items, pool, stride, off_w2, H, F, H, y, act,
+  bf16_pass<false, MAXRB>(hbuf, items, n_items, pool, stride, off_w2, H, F, H, y, act,
                           red, PassSync{nullptr, sync, 2 * F / 32, err, spin_cap});
 }
 
@@ -246,8 +245,8 @@ bool decode_bf16_fits(int max_items, int R, int K, bool swiglu) {
   return bf16_decode_lds(swiglu, max_items, K) <= 96 * 1024;
 }
 
-int launch_decode_bf16(bool swiglu, const void* raw, const int32_t* perm, int k,
-                       const FfnItem* items, const int32_t* n_items, int max_items,
+int launch_decode_bf16(bool swiglu, const void* raw, const FfnItem* items, const int32_t* n_items,
+                       int max_items,
                        const char* pool, size_t stride, size_t off_w, int R, int K, int out_ld,
                        void* out, hipStream_t s) {
   // the grid: the workgroups the compute units keep resident; every share has at most
@@ -259,7 +258,7 @@ int launch_decode_bf16(bool swiglu, const void* raw, const int32_t* perm, int k,
   const size_t lds = bf16_decode_lds(swiglu, max_items, K);
 #define MOE_BF16_DEC(SW_, MAXRB_)                                                              \
   hipLaunchKernelGGL((bf16_decode_kernel<SW_, MAXRB_>), dim3((unsigned)grid), dim3(kDecNW * 64), \
-                     lds, s, raw, perm, k, items, n_items, pool, stride, off_w, R, K, out_ld, out)
+                     lds, s, raw, items, n_items, pool, stride, off_w, R, K, out_ld, out)
   if (per <= 8) {
     if (swiglu) MOE_BF16_DEC(true, 8);
     else MOE_BF16_DEC(false, 8);
@@ -273,7 +272,7 @@ int launch_decode_bf16(bool swiglu, const void* raw, const int32_t* perm, int k,
   return moe_launch_status();
 }
 
-int launch_decode_bf16_fused(const void* x, const int32_t* perm, int k, const FfnItem* items,
+int launch_decode_bf16_fused(const void* x, const FfnItem* items,
                              const int32_t* n_items, int max_items, const char* pool,
                              size_t stride, size_t off_w13, size_t off_w2, int H, int F,
                              void* hbuf, float* y, int32_t* sync, int32_t* err, hipStream_t s) {
@@ -293,11 +292,11 @@ int launch_decode_bf16_fused(const void* x, const int32_t* perm, int k, const Ff
   uint16_t* h = static_cast<uint16_t*>(hbuf);
   if (per <= 8)
     hipLaunchKernelGGL((bf16_decode_fused_kernel<8>), dim3((unsigned)grid), dim3(kDecNW * 64), lds,
-                       s, x, perm, k, items, n_items, pool, stride, off_w13, off_w2, H, F, h, y,
+                       s, x, items, n_items, pool, stride, off_w13, off_w2, H, F, h, y,
                        sync, err, kSpinCap);
   else
     hipLaunchKernelGGL((bf16_decode_fused_kernel<16>), dim3((unsigned)grid), dim3(kDecNW * 64), lds,
-                       s, x, perm, k, items, n_items, pool, stride, off_w13, off_w2, H, F, h, y,
+                       s, x, items, n_items, pool, stride, off_w13, off_w2, H, F, h, y,
                        sync, err, kSpinCap);
   return moe_launch_status();
 }

@@ -65,8 +65,8 @@ __device__ __forceinline__ u32x4 load_h4(const float* p, bool shared) {
 
 template <bool SWIGLU, int MAXRB>
 __device__ __forceinline__ void decode_pass(
-    const void* __restrict__ raw, const int32_t* __restrict__ perm, int k,
-    const FfnItem* __restrict__ items, int n_items, const char* __restrict__ pool, size_t stride,
+    const void* __restrict__ raw, const FfnItem* __restrict__ items, int n_items,
+    const char* __restrict__ pool, size_t stride,
     size_t off_codes, size_t off_scales, int R, int K, int out_ld, float* __restrict__ out,
     const PassLds<MAXRB>& L, const PassSync& sy) {
   int8_t* lds = L.dyn;
@@ -363,8 +363,8 @@ __device__ __forceinline__ void decode_pass(
 
 template <bool SWIGLU, int MAXRB>
 __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(4))) void int4_decode_kernel(
-    const void* __restrict__ raw, const int32_t* __restrict__ perm, int k,
-    const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+    const void* __restrict__ raw, const FfnItem* __restrict__ items,
+    const int32_t* __restrict__ n_items_p,
     const char* __restrict__ pool, size_t stride, size_t off_codes, size_t off_scales, int R,
     int K, int out_ld, float* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(4))
   __shared__ unsigned row_max[kStreamMaxItems];
   __shared__ float red[kDecNW][MAXRB][32];
   const PassLds<MAXRB> L{lds, act_s, wmax, row_max, red};
-  decode_pass<SWIGLU, MAXRB>(raw, perm, k, items, n_items_p[0], pool, stride, off_codes, off_scales,
+  decode_pass<SWIGLU, MAXRB>(raw, items, n_items_p[0], pool, stride, off_codes, off_scales,
                              R, K, out_ld, out, L, PassSync{nullptr, nullptr, 0, nullptr, 0});
 }
 
@@ -383,8 +383,8 @@ __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(4))
 template <int MAXRB>
 __global__ __launch_bounds__(kDecNW * 64) __attribute__((amdgpu_waves_per_eu(4))) void
 int4_decode_fused_kernel(
-    const void* __restrict__ x, const int32_t* __restrict__ perm, int k,
-    const FfnItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+    const void* __restrict__ x, const FfnItem* __restrict__ items,
+    const int32_t* __restrict__ n_items_p,
     const char* __restrict__ pool, size_t stride, size_t off_w13, size_t off_s13, size_t off_w2,
     size_t off_s2, int H, int F, float* __restrict__ hbuf, float* __restrict__ y,
     int32_t* __restrict__ sync, int32_t* __restrict__ err, int spin_cap) {
@@ -395,20 +395,20 @@ int4_decode_fused_kernel(
   __shared__ float red[kDecNW][MAXRB][32];
   const PassLds<MAXRB> L{lds, act_s, wmax, row_max, red};
   const int n_items = n_items_p[0];
-  decode_pass<true, MAXRB>(x, perm, k, items, n_items, pool, stride, off_w13, off_s13, 2 * F, H, F,
+  decode_pass<true, MAXRB>(x, items, n_items, pool, stride, off_w13, off_s13, 2 * F, H, F,
                            hbuf, L, PassSync{sync, nullptr, 0, err, spin_cap});
   __syncthreads();  // the LDS of the first pass is free
-  decode_pass<false, MAXRB>(hbuf, perm, k, items, n_items, pool, stride, off_w2, off_s2, H, F, H, y,
+  decode_pass<false, MAXRB>(hbuf, items, n_items, pool, stride, off_w2, off_s2, H, F, H, y,
                             L, PassSync{nullptr, sync, 2 * F / 32, err, spin_cap});
 }
 
 template <bool SWIGLU, int MAXRB>
-int launch_rb(const void* raw, const int32_t* perm, int k, const FfnItem* items,
+int launch_rb(const void* raw, const FfnItem* items,
               const int32_t* n_items, int max_items, const char* pool, size_t stride,
               size_t off_codes, size_t off_scales, int R, int K, int out_ld, float* out,
               hipStream_t s, long long grid, size_t lds) {
   hipLaunchKernelGGL((int4_decode_kernel<SWIGLU, MAXRB>), dim3((unsigned)grid), dim3(kDecNW * 64),
-                     lds, s, raw, perm, k, items, n_items, pool, stride, off_codes, off_scales, R,
+                     lds, s, raw, items, n_items, pool, stride, off_codes, off_scales, R,
                      K, out_ld, out);
   return moe_launch_status();
 }
@@ -427,8 +427,8 @@ bool decode_int4_fits(int max_items, int R, int K, bool swiglu) {
   return decode_lds(swiglu, max_items, K, 16) <= 96 * 1024;
 }
 
-int launch_decode_int4(bool swiglu, const void* raw, const int32_t* perm, int k,
-                       const FfnItem* items, const int32_t* n_items, int max_items,
+int launch_decode_int4(bool swiglu, const void* raw, const FfnItem* items, const int32_t* n_items,
+                       int max_items,
                        const char* pool, size_t stride, size_t off_codes, size_t off_scales, int R,
                        int K, int out_ld, float* out, hipStream_t s) {
   // the grid: the workgroups the compute units keep resident (16 waves of up to 128 VGPRs
@@ -439,23 +439,23 @@ int launch_decode_int4(bool swiglu, const void* raw, const int32_t* perm, int k,
   if (grid > blocks) grid = blocks;
   const long long per = (blocks + grid - 1) / grid;
   if (per <= 8)
-    return swiglu ? launch_rb<true, 8>(raw, perm, k, items, n_items, max_items, pool, stride,
+    return swiglu ? launch_rb<true, 8>(raw, items, n_items, max_items, pool, stride,
                                        off_codes, off_scales, R, K, out_ld, out, s, grid,
                                        decode_lds(true, max_items, K, 8))
-                  : launch_rb<false, 8>(raw, perm, k, items, n_items, max_items, pool, stride,
+                  : launch_rb<false, 8>(raw, items, n_items, max_items, pool, stride,
                                         off_codes, off_scales, R, K, out_ld, out, s, grid,
                                         decode_lds(false, max_items, K, 8));
   if (per <= 16)
-    return swiglu ? launch_rb<true, 16>(raw, perm, k, items, n_items, max_items, pool, stride,
+    return swiglu ? launch_rb<true, 16>(raw, items, n_items, max_items, pool, stride,
                                         off_codes, off_scales, R, K, out_ld, out, s, grid,
                                         decode_lds(true, max_items, K, 16))
-                  : launch_rb<false, 16>(raw, perm, k, items, n_items, max_items, pool, stride,
+                  : launch_rb<false, 16>(raw, items, n_items, max_items, pool, stride,
                                          off_codes, off_scales, R, K, out_ld, out, s, grid,
                                          decode_lds(false, max_items, K, 16));
   return MOE_EUNSUPPORTED;
 }
 
-int launch_decode_int4_fused(const void* x, const int32_t* perm, int k, const FfnItem* items,
+int launch_decode_int4_fused(const void* x, const FfnItem* items,
                              const int32_t* n_items, int max_items, const char* pool,
                              size_t stride, size_t off_w13, size_t off_s13, size_t off_w2,
                              size_t off_s2, int H, int F, float* hbuf, float* y, int32_t* sync,
@@ -477,13 +477,13 @@ int launch_decode_int4_fused(const void* x, const int32_t* perm, int k, const Ff
   if (lds == 0) return MOE_EUNSUPPORTED;
   if (per <= 8) {
     hipLaunchKernelGGL((int4_decode_fused_kernel<8>), dim3((unsigned)grid), dim3(kDecNW * 64), lds,
-                       s, x, perm, k, items, n_items, pool, stride, off_w13, off_s13, off_w2,
+                       s, x, items, n_items, pool, stride, off_w13, off_s13, off_w2,
                        off_s2, H, F, hbuf, y, sync, err, kSpinCap);
     return moe_launch_status();
   }
   if (per <= 16) {
     hipLaunchKernelGGL((int4_decode_fused_kernel<16>), dim3((unsigned)grid), dim3(kDecNW * 64), lds,
-                       s, x, perm, k, items, n_items, pool, stride, off_w13, off_s13, off_w2,
+                       s, x, items, n_items, pool, stride, off_w13, off_s13, off_w2,
                        off_s2, H, F, hbuf, y, sync, err, kSpinCap);
     return moe_launch_status();
   }

@@ -393,15 +393,15 @@ int expert_ffn(const void* x, int x_dtype, const int32_t* perm, const int32_t* o
     // it fits
     if (T == 1 && max_items > 0 && max_tiles == 0 && decode_bf16_fits(max_items, 2 * F, H, true) &&
         decode_bf16_fits(max_items, H, F, false)) {
-      int rc = launch_decode_bf16_fused(x, perm, k, items, n_items, max_items, pool, slot_stride,
+      int rc = launch_decode_bf16_fused(x, items, n_items, max_items, pool, slot_stride,
                                         lay.off_w13, lay.off_w2, H, F, hbuf, y_perm,
                                         reinterpret_cast<int32_t*>(wsb + ws.sync), err_word,
                                         stream);
       if (rc == MOE_EUNSUPPORTED) {
-        rc = launch_decode_bf16(true, x, perm, k, items, n_items, max_items, pool, slot_stride,
+        rc = launch_decode_bf16(true, x, items, n_items, max_items, pool, slot_stride,
                                 lay.off_w13, 2 * F, H, F, hbuf, stream);
         if (rc == MOE_OK)
-          rc = launch_decode_bf16(false, hbuf, perm, k, items, n_items, max_items, pool,
+          rc = launch_decode_bf16(false, hbuf, items, n_items, max_items, pool,
                                   slot_stride, lay.off_w2, H, F, H, y_perm, stream);
       }
       if (rc != MOE_EUNSUPPORTED) return rc;

@@ -626,14 +626,14 @@ int ffn_int4(const void* x, const int32_t* perm, const int32_t* offsets, const i
   // one token: both passes over even shares of the call's row blocks, in one launch when it fits
   if (T == 1 && !split && fused && max_items > 0 && decode_int4_fits(max_items, 2 * F, H, true) &&
       decode_int4_fits(max_items, H, F, false)) {
-    int rc = launch_decode_int4_fused(x, perm, k, items, n_items, max_items, pool, stride,
+    int rc = launch_decode_int4_fused(x, items, n_items, max_items, pool, stride,
                                       lay.off_w13, lay.off_s13, lay.off_w2, lay.off_s2, H, F, hbuf,
                                       y, reinterpret_cast<int32_t*>(ws + wl.sync), err, s);
     if (rc != MOE_EUNSUPPORTED) return rc;
-    rc = launch_decode_int4(true, x, perm, k, items, n_items, max_items, pool, stride,
+    rc = launch_decode_int4(true, x, items, n_items, max_items, pool, stride,
                                 lay.off_w13, lay.off_s13, 2 * F, H, F, hbuf, s);
     if (rc == MOE_OK)
-      rc = launch_decode_int4(false, hbuf, perm, k, items, n_items, max_items, pool, stride,
+      rc = launch_decode_int4(false, hbuf, items, n_items, max_items, pool, stride,
                               lay.off_w2, lay.off_s2, H, F, H, y, s);
     if (rc != MOE_EUNSUPPORTED) return rc;
   }

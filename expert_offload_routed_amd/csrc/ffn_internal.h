@@ -47,20 +47,20 @@ constexpr int kStreamMaxItems = 64;  // groups of a one-token call they take
 bool decode_int4_fits(int max_items, int R, int K, bool swiglu);
 // Both one-token int4 passes in one launch, handing h over through the sync counters
 // (zero at launch); MOE_EUNSUPPORTED when the call does not fit it.
-int launch_decode_int4_fused(const void* x, const int32_t* perm, int k, const FfnItem* items,
-                             const int32_t* n_items, int max_items, const char* pool,
+int launch_decode_int4_fused(const void* x, const FfnItem* items, const int32_t* n_items,
+                             int max_items, const char* pool,
                              size_t stride, size_t off_w13, size_t off_s13, size_t off_w2,
                              size_t off_s2, int H, int F, float* hbuf, float* y, int32_t* sync,
                              int32_t* err, hipStream_t s);
 
 // The bf16 counterparts (decode_bf16.hip): h is bf16 (rows of F values), y fp32.
 bool decode_bf16_fits(int max_items, int R, int K, bool swiglu);
-int launch_decode_bf16_fused(const void* x, const int32_t* perm, int k, const FfnItem* items,
-                             const int32_t* n_items, int max_items, const char* pool,
+int launch_decode_bf16_fused(const void* x, const FfnItem* items, const int32_t* n_items,
+                             int max_items, const char* pool,
                              size_t stride, size_t off_w13, size_t off_w2, int H, int F,
                              void* hbuf, float* y, int32_t* sync, int32_t* err, hipStream_t s);
-int launch_decode_bf16(bool swiglu, const void* raw, const int32_t* perm, int k,
-                       const FfnItem* items, const int32_t* n_items, int max_items,
+int launch_decode_bf16(bool swiglu, const void* raw, const FfnItem* items,
+                       const int32_t* n_items, int max_items,
                        const char* pool, size_t stride, size_t off_w, int R, int K, int out_ld,
                        void* out, hipStream_t s);
 
@@ -83,8 +83,8 @@ void launch_ffn_plan(const int32_t* offsets, const int32_t* lut, const int32_t* 
 // One one-token int4 pass over the work list's items: the call's row blocks in one even
 // share per workgroup (pass 1 with the SwiGLU epilogue from the bf16 tokens; pass 2 from
 // the fp32 h rows). MOE_EUNSUPPORTED when a share would exceed 16 row blocks.
-int launch_decode_int4(bool swiglu, const void* raw, const int32_t* perm, int k,
-                       const FfnItem* items, const int32_t* n_items, int max_items,
+int launch_decode_int4(bool swiglu, const void* raw, const FfnItem* items,
+                       const int32_t* n_items, int max_items,
                        const char* pool, size_t stride, size_t off_codes, size_t off_scales, int R,
                        int K, int out_ld, float* out, hipStream_t s);
 // Workgroups of kernel `kern` resident at once on the current device (occupancy with
