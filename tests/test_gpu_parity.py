@@ -250,7 +250,8 @@ def test_expert_ffn_absent_expert_sets_error_and_skips():
 
 # ------------------------------------------------------------------ combine --
 @pytest.mark.parametrize("T,k,H,n_sh,out", [(16, 2, 256, 0, torch.float32), (33, 6, 2048, 2, torch.bfloat16),
-                                            (1, 8, 7168, 1, torch.bfloat16),
+                                            (1, 8, 7168, 1, torch.bfloat16), (1, 2, 256, 0, torch.float32),
+                                            (1, 6, 2048, 2, torch.float32),
                                             (5, 12, 512, 1, torch.float32)])  # two row batches
 def test_combine_stage(T, k, H, n_sh, out):
     g = torch.Generator().manual_seed(T + k)
