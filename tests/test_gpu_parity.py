@@ -531,6 +531,33 @@ def test_device_orchestration_rejects_more_routed_than_slots():
         layer_obj.forward(x)
 
 
+@pytest.mark.parametrize("kind", ["mrs", "history"])
+def test_device_orchestration_policy_window_limit(kind):
+    """The device planner keeps an eviction-score history of at most 16 steps: a longer
+    window is refused (invalid argument) whichever of the two settings comes second, and the
+    context keeps planning under its previous setting."""
+    shape = W.reduced(MIX, E=12, k=3, H=256, F=256)
+    pol = B.MOE_POLICY_MRS if kind == "mrs" else B.MOE_POLICY_HISTORY
+    params = None if kind == "mrs" else HIST_PARAMS
+    layer_obj = Hn.SlotCacheLayer(shape, 5, W.initial_residency(shape, 5, "random"), 4)
+    layer_obj.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
+    with pytest.raises(B.MoeError) as e:
+        layer_obj.ctx.set_policy(pol, 17, params)
+    assert e.value.rc == -1
+    layer_obj.ctx.set_policy(pol, 16, params)  # the largest window the device keeps
+    layer_obj.forward(W.tokens(shape, 1, step=0, device=_dev()))
+    torch.cuda.synchronize()
+    assert layer_obj.err.item() == 0
+    layer_obj.ctx.set_orchestration(B.MOE_ORCH_HOST)
+    layer_obj.ctx.set_policy(pol, 17, params)  # the host keeps any window
+    with pytest.raises(B.MoeError) as e:
+        layer_obj.ctx.set_orchestration(B.MOE_ORCH_DEVICE)
+    assert e.value.rc == -1
+    layer_obj.forward(W.tokens(shape, 1, step=1, device=_dev()))  # still planned on the host
+    torch.cuda.synchronize()
+    assert layer_obj.err.item() == 0
+
+
 SPLIT = W.reduced(DSV3, wfmt="int4g128_resplit")
 
 
