@@ -1,10 +1,11 @@
 """Device state of one routed-expert workload on one GPU, driving the native runtime.
 
 PyTorch provides device memory, pinned host memory and streams. A layer step
-is one call of moe_layer_forward (include/moe_runtime.h), which runs route,
-permute, the host LRU plan, the expert FFN over resident slots overlapped
-with tagged fills of the misses, the shared experts and the combine inside
-libmoe_offload.
+is one call of moe_layer_forward (include/moe_runtime.h). Inside libmoe_offload
+it runs the route and permutation, the eviction plan (LRU, Minus Recent Score
+or routing history; on the host, or on the GPU under device orchestration),
+the expert FFN over resident slots overlapped with tagged fills of the misses,
+the shared experts, and the combine as its own launch.
 """
 from __future__ import annotations
 
