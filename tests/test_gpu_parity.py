@@ -248,6 +248,30 @@ def test_expert_ffn_absent_expert_sets_error_and_skips():
     assert torch.all(y[other] != 7.0)
 
 
+def test_expert_ffn_and_combine_empty_calls():
+    """No tokens: the FFN stage (bf16 and int4 slots) and the combine succeed, leave the error
+    word at zero and write nothing; an output that lives inside a sentinel buffer stays intact."""
+    for shape in (W.reduced(MIX, E=8, k=2, H=256, F=256), W.reduced(DSV3, E=16, k=4, H=512, F=256)):
+        say(f"empty calls {shape.name}")
+        E, k, H, F = shape.E, shape.k, shape.H, shape.F
+        pool, stride, lut = _pool_with(shape, list(range(E)))
+        wcode = Hn.WFMT_CODE[shape.wfmt]
+        x = torch.empty(0, H, dtype=torch.bfloat16, device=_dev())
+        perm = torch.empty(0, dtype=torch.int32, device=_dev())
+        offsets = torch.zeros(E + 1, dtype=torch.int32, device=_dev())
+        ws = torch.empty(B.moe_ffn_workspace_bytes(0, H, F, E, k, wcode), dtype=torch.uint8, device=_dev())
+        big = torch.full((4, H), 7.0, dtype=torch.float32, device=_dev())
+        err = torch.zeros(1, dtype=torch.int32, device=_dev())
+        B.moe_expert_ffn(x, perm, offsets, lut, None, pool, stride, wcode, 0, H, F, E, k, big[:0], err, ws)
+        inv = torch.empty(0, dtype=torch.int32, device=_dev())
+        w = torch.empty(0, k, dtype=torch.float32, device=_dev())
+        out = B.moe_combine(big[:0], inv, w, 0, k, H, None, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert err.item() == 0
+        assert out.shape == (0, H)
+        assert torch.all(big == 7.0)
+
+
 # ------------------------------------------------------------------ combine --
 @pytest.mark.parametrize("T,k,H,n_sh,out", [(16, 2, 256, 0, torch.float32), (33, 6, 2048, 2, torch.bfloat16),
                                             (1, 8, 7168, 1, torch.bfloat16), (1, 2, 256, 0, torch.float32),
