@@ -13,6 +13,7 @@
 namespace {
 
 constexpr int kCombineBatch = 8;  // rows of a token whose loads are in flight together
+constexpr int kSharedRegs = 2;    // shared-expert rows loaded ahead of the routed ones
 
 template <int OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
@@ -23,6 +24,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = blockIdx.y;
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= H) return;
+  // the shared experts' rows do not depend on the routing: the first kSharedRegs go out
+  // before the routed rows (they are still added after them, in s order)
+  u32x4 sv[kSharedRegs];
+#pragma unroll
+  for (int s = 0; s < kSharedRegs; ++s)
+    if (s < n_shared) sv[s] = ld16(shared + ((size_t)s * T + t) * H + c);
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   // kCombineBatch rows at a time: every row of the batch is loaded (an index past k reads row
   // k - 1 again, unused) before the first is summed, so a token costs one memory round trip
@@ -52,13 +59,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       a3 = use ? f3 : a3;
     }
   }
-  for (int s = 0; s < n_shared; ++s) {
-    const u32x4 v = ld16(shared + ((size_t)s * T + t) * H + c);
+  auto add_shared = [&](const u32x4& v) {
     a0 += __uint_as_float(v.x);
     a1 += __uint_as_float(v.y);
     a2 += __uint_as_float(v.z);
     a3 += __uint_as_float(v.w);
-  }
+  };
+#pragma unroll
+  for (int s = 0; s < kSharedRegs; ++s)
+    if (s < n_shared) add_shared(sv[s]);
+  for (int s = kSharedRegs; s < n_shared; ++s) add_shared(ld16(shared + ((size_t)s * T + t) * H + c));
   if constexpr (OUT == MOE_BF16) {
     uint16_t* o = static_cast<uint16_t*>(out) + (size_t)t * H + c;
     const uint32_t lo = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
